@@ -1,0 +1,174 @@
+"""ctypes wrapper of the CPU oracle (``moe_oracle.c``).
+
+TEST INFRASTRUCTURE: imported only by ``tests/``, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py``.  The HIP library never imports,
+links or calls anything here.
+
+All arrays are numpy, host memory.  bf16 tensors are ``uint16`` bit arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
+_lib = None
+
+GATE_SOFTMAX = 0
+GATE_SIGMOID = 1
+
+
+class OrcLayer(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int64), ("d", ctypes.c_int64), ("F", ctypes.c_int64), ("E", ctypes.c_int64),
+        ("K", ctypes.c_int64), ("gate", ctypes.c_int32), ("renorm", ctypes.c_int32),
+        ("residual", ctypes.c_int32), ("bf16", ctypes.c_int32), ("capacity_factor", ctypes.c_double),
+        ("n_shared", ctypes.c_int64), ("Fs", ctypes.c_int64),
+    ]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc: -O2, OpenMP, no fast-math, no FMA contraction."""
+    src = os.path.join(_HERE, "moe_oracle.c")
+    stale = not os.path.exists(_LIB_PATH) or os.path.getmtime(src) > os.path.getmtime(_LIB_PATH)
+    if force or stale:
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC",
+                               src, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        P = ctypes.POINTER(OrcLayer)
+        lib.orc_logits.argtypes = [P, vp, vp, vp, vp]
+        lib.orc_select.argtypes = [P, vp, vp, vp, vp, vp]
+        lib.orc_capacity.argtypes = [P]
+        lib.orc_capacity.restype = i64
+        lib.orc_permute.argtypes = [P, vp, vp, vp, vp, vp, vp]
+        lib.orc_swiglu.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp, i32]
+        lib.orc_forward_rows.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]
+        lib.orc_expert_choice.argtypes = [P, vp, i64, vp, vp]
+        for fn in (lib.orc_logits, lib.orc_select, lib.orc_permute, lib.orc_swiglu, lib.orc_forward_rows,
+                   lib.orc_expert_choice):
+            fn.restype = None
+        _lib = lib
+    return _lib
+
+
+def _p(a):
+    if a is None:
+        return None
+    assert isinstance(a, np.ndarray) and a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous numpy"
+    return a.ctypes.data
+
+
+def layer(T, d, F, E, K, gate=GATE_SOFTMAX, renorm=True, residual=False, bf16=False, capacity_factor=0.0,
+          n_shared=0, Fs=0) -> OrcLayer:
+    return OrcLayer(T, d, F, E, K, gate, int(renorm), int(residual), int(bf16), float(capacity_factor),
+                    n_shared, Fs)
+
+
+def layer_of(wl, residual=False) -> OrcLayer:
+    """OrcLayer for a ``moe_synth`` workload."""
+    return layer(wl.T, wl.d, wl.F, wl.E, wl.K, gate=wl.gate, renorm=wl.renorm, residual=residual,
+                 bf16=(wl.dtype == "bf16"), capacity_factor=wl.capacity_factor, n_shared=wl.n_shared, Fs=wl.Fs)
+
+
+def logits(L: OrcLayer, x, Wg, logit_bias=None) -> np.ndarray:
+    out = np.empty((L.T, L.E), dtype=np.float32)
+    _load().orc_logits(ctypes.byref(L), _p(x), _p(Wg), _p(logit_bias), _p(out))
+    return out
+
+
+def select(L: OrcLayer, lg, sel_bias=None):
+    """-> (idx int32 [T,K], w float64 [T,K], gap float64 [T])"""
+    idx = np.empty((L.T, L.K), dtype=np.int32)
+    w = np.empty((L.T, L.K), dtype=np.float64)
+    gap = np.empty((L.T,), dtype=np.float64)
+    _load().orc_select(ctypes.byref(L), _p(np.ascontiguousarray(lg, dtype=np.float32)), _p(sel_bias), _p(idx),
+                       _p(w), _p(gap))
+    return idx, w, gap
+
+
+def capacity(L: OrcLayer) -> int:
+    return int(_load().orc_capacity(ctypes.byref(L)))
+
+
+def permute(L: OrcLayer, idx):
+    """-> dict(counts [E], offsets [E+1], dest [T*K], row_src [T*K], dropped [T*K])"""
+    N = L.T * L.K
+    out = dict(counts=np.empty(L.E, np.int32), offsets=np.empty(L.E + 1, np.int32), dest=np.empty(N, np.int32),
+               row_src=np.empty(N, np.int32), dropped=np.empty(N, np.uint8))
+    _load().orc_permute(ctypes.byref(L), _p(np.ascontiguousarray(idx, dtype=np.int32)), _p(out["counts"]),
+                        _p(out["offsets"]), _p(out["dest"]), _p(out["row_src"]), _p(out["dropped"]))
+    return out
+
+
+def swiglu(W1, W3, W2, x, bf16: bool, threads: int = 1) -> np.ndarray:
+    """One expert on one row: W1, W3 [F, d], W2 [d, F]; x float64 [d]."""
+    F, d = W1.shape
+    out = np.empty(d, dtype=np.float64)
+    _load().orc_swiglu(d, F, int(bf16), _p(np.ascontiguousarray(W1)), _p(np.ascontiguousarray(W3)),
+                       _p(np.ascontiguousarray(W2)), _p(np.ascontiguousarray(x, dtype=np.float64)), _p(out),
+                       threads)
+    return out
+
+
+def forward_rows(L: OrcLayer, x, idx, w, dest, W1e, W3e, W2e, Ws1=None, Ws3=None, Ws2=None, tokens=None):
+    """y (float64 [n, d]) for the listed tokens (all tokens if None).
+
+    W1e/W3e/W2e: either stacked arrays [E, ...] or lists of per-expert arrays
+    (None for experts no listed token uses)."""
+    if tokens is None:
+        tokens = np.arange(L.T, dtype=np.int64)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int64)
+
+    def ptrs(W):
+        arr = (ctypes.c_void_p * L.E)()
+        keep = []
+        for e in range(L.E):
+            a = W[e] if W is not None else None
+            if a is not None:
+                a = np.ascontiguousarray(a)
+                keep.append(a)
+                arr[e] = a.ctypes.data
+        return arr, keep
+
+    p1, k1 = ptrs(W1e)
+    p3, k3 = ptrs(W3e)
+    p2, k2 = ptrs(W2e)
+    y = np.empty((len(tokens), L.d), dtype=np.float64)
+    _load().orc_forward_rows(ctypes.byref(L), _p(x), _p(np.ascontiguousarray(idx, dtype=np.int32)),
+                             _p(np.ascontiguousarray(w, dtype=np.float64)),
+                             _p(None if dest is None else np.ascontiguousarray(dest, dtype=np.int32)),
+                             ctypes.cast(p1, ctypes.c_void_p), ctypes.cast(p3, ctypes.c_void_p),
+                             ctypes.cast(p2, ctypes.c_void_p), _p(Ws1), _p(Ws3), _p(Ws2), _p(tokens), len(tokens),
+                             _p(y))
+    del k1, k3, k2
+    return y
+
+
+def expert_choice(L: OrcLayer, lg, cap: int):
+    """-> (tok int32 [E, cap], g float64 [E, cap])"""
+    tok = np.empty((L.E, cap), dtype=np.int32)
+    g = np.empty((L.E, cap), dtype=np.float64)
+    _load().orc_expert_choice(ctypes.byref(L), _p(np.ascontiguousarray(lg, dtype=np.float32)), cap, _p(tok), _p(g))
+    return tok, g
+
+
+def route(L: OrcLayer, x, Wg, logit_bias=None, sel_bias=None):
+    """a1-a4 in order: logits, selection, permutation."""
+    lg = logits(L, x, Wg, logit_bias)
+    idx, w, gap = select(L, lg, sel_bias)
+    perm = permute(L, idx)
+    return dict(logits=lg, idx=idx, w=w, gap=gap, **perm)

@@ -1,0 +1,260 @@
+/*
+ * moe_oracle.c -- CPU reference of one sparsely-gated MoE FFN layer forward.
+ *
+ * TEST INFRASTRUCTURE ONLY (see moe_oracle.h).  Written from the pages'
+ * definitions, step by step; no blocking, fusion or reordering beyond what a
+ * definition states.  Reductions are in double, in ascending index order.
+ */
+#include "moe_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---- element access ----------------------------------------------------- */
+
+static inline double bf16_bits_to_double(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* element i of a bf16 or fp32 array, widened exactly to double */
+static inline double elem(const void* p, int32_t bf16, int64_t i) {
+  return bf16 ? bf16_bits_to_double(((const uint16_t*)p)[i]) : (double)((const float*)p)[i];
+}
+
+/* ---- a1: router logits  [TD §3.1 step 1; BD §3.2] ------------------------ */
+
+void orc_logits(const orc_layer* L, const void* x, const float* Wg, const float* logit_bias, float* logits) {
+  const int64_t T = L->T, d = L->d, E = L->E;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int64_t i = 0; i < d; ++i) acc += elem(x, L->bf16, t * d + i) * (double)Wg[e * d + i];
+      if (logit_bias) acc += (double)logit_bias[e];
+      logits[t * E + e] = (float)acc;
+    }
+  }
+}
+
+/* ---- a2 + a3: gate, key, Top-K, weights ----------------------------------- */
+
+/* "a ranks before b": larger key first, ties to the lower expert index.  Keys
+ * are compared as IEEE values, so -0 and +0 are equal. */
+static inline int ranks_before(float ka, int64_t ea, float kb, int64_t eb) {
+  if (ka != kb) return ka > kb;
+  return ea < eb;
+}
+
+void orc_select(const orc_layer* L, const float* logits, const float* sel_bias, int32_t* idx, double* w,
+                double* gap) {
+  const int64_t T = L->T, E = L->E, K = L->K;
+#pragma omp parallel
+  {
+    float* key = (float*)malloc(sizeof(float) * (size_t)E);
+    double* score = (double*)malloc(sizeof(double) * (size_t)E);
+    int64_t* order = (int64_t*)malloc(sizeof(int64_t) * (size_t)E);
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t t = 0; t < T; ++t) {
+      const float* l = logits + t * E;
+      if (L->gate == ORC_GATE_SOFTMAX) {
+        /* p_i = e^{l_i} / sum_j e^{l_j}  [TD §3.2], evaluated with the max
+         * subtracted; softmax is monotone, so the key is the logit itself. */
+        double m = -INFINITY;
+        for (int64_t e = 0; e < E; ++e) m = fmax(m, (double)l[e]);
+        double z = 0.0;
+        for (int64_t e = 0; e < E; ++e) z += exp((double)l[e] - m);
+        for (int64_t e = 0; e < E; ++e) {
+          score[e] = exp((double)l[e] - m) / z;
+          key[e] = l[e];
+        }
+      } else {
+        /* s = Sigmoid(u^T e_i)  [TD §3.5]; selection on s + b_i, weights on s
+         * alone  [TD §4.3; §9.2].  The key is formed in fp32. */
+        for (int64_t e = 0; e < E; ++e) {
+          double s = 1.0 / (1.0 + exp(-(double)l[e]));
+          float sf = (float)s;
+          float b = sel_bias ? sel_bias[e] : 0.0f;
+          score[e] = s;
+          key[e] = sf + b;
+        }
+      }
+      /* Top-K: selection by repeated maximum under the total order above
+       * [TD §3.1 KeepTopK]. */
+      for (int64_t e = 0; e < E; ++e) order[e] = e;
+      for (int64_t k = 0; k < K && k < E; ++k) {
+        int64_t best = k;
+        for (int64_t j = k + 1; j < E; ++j)
+          if (ranks_before(key[order[j]], order[j], key[order[best]], order[best])) best = j;
+        int64_t tmp = order[k];
+        order[k] = order[best];
+        order[best] = tmp;
+      }
+      double sum = 0.0;
+      for (int64_t k = 0; k < K; ++k) sum += score[order[k]];
+      for (int64_t k = 0; k < K; ++k) {
+        idx[t * K + k] = (int32_t)order[k];
+        /* renormalised Top-K weights  [TD §9.1] */
+        w[t * K + k] = L->renorm ? score[order[k]] / sum : score[order[k]];
+      }
+      if (gap) {
+        if (K >= E) {
+          gap[t] = INFINITY;
+        } else {
+          /* the (K+1)-th key is the largest among the unselected ones */
+          float next = key[order[K]];
+          for (int64_t j = K + 1; j < E; ++j)
+            if (key[order[j]] > next) next = key[order[j]];
+          gap[t] = (double)key[order[K - 1]] - (double)next;
+        }
+      }
+    }
+    free(key);
+    free(score);
+    free(order);
+  }
+}
+
+/* ---- a4: capacity, histogram, stable permutation  [TD §3.2] -------------- */
+
+int64_t orc_capacity(const orc_layer* L) {
+  if (!(L->capacity_factor > 0.0)) return -1;
+  /* K_max = floor(C * N_tokens / N_experts), with N_tokens counted in
+   * (token, choice) assignments so the formula also covers K > 1. */
+  return (int64_t)floor(L->capacity_factor * (double)(L->T * L->K) / (double)L->E);
+}
+
+void orc_permute(const orc_layer* L, const int32_t* idx, int32_t* counts, int32_t* offsets, int32_t* dest,
+                 int32_t* row_src, uint8_t* dropped) {
+  const int64_t E = L->E, N = L->T * L->K;
+  const int64_t cap = orc_capacity(L);
+  int64_t* pos = (int64_t*)malloc(sizeof(int64_t) * (size_t)(N > 0 ? N : 1));
+  for (int64_t e = 0; e < E; ++e) counts[e] = 0;
+  /* pos(f): arrivals in flat order; the first `cap` arrivals are kept and
+   * the rest overflow and are dropped. */
+  for (int64_t f = 0; f < N; ++f) pos[f] = counts[idx[f]]++;
+  offsets[0] = 0;
+  for (int64_t e = 0; e < E; ++e) {
+    int64_t kept = counts[e];
+    if (cap >= 0 && kept > cap) kept = cap;
+    offsets[e + 1] = offsets[e] + (int32_t)kept;
+  }
+  for (int64_t r = 0; r < N; ++r) row_src[r] = -1;
+  for (int64_t f = 0; f < N; ++f) {
+    int keep = (cap < 0) || (pos[f] < cap);
+    dest[f] = keep ? (int32_t)(offsets[idx[f]] + pos[f]) : -1;
+    dropped[f] = (uint8_t)!keep;
+    if (keep) row_src[dest[f]] = (int32_t)f;
+  }
+  free(pos);
+}
+
+/* ---- a6 + a7: one SwiGLU expert on one row  [LN §2.2] -------------------- */
+
+void orc_swiglu(int64_t d, int64_t F, int32_t bf16, const void* W1, const void* W3, const void* W2,
+                const double* x, double* out, int32_t threads) {
+  double* h = (double*)malloc(sizeof(double) * (size_t)F);
+  int nt = threads > 1 ? threads : 1;
+#pragma omp parallel for schedule(static) num_threads(nt) if (nt > 1)
+  for (int64_t j = 0; j < F; ++j) {
+    double a = 0.0, b = 0.0;
+    for (int64_t i = 0; i < d; ++i) {
+      a += elem(W1, bf16, j * d + i) * x[i];
+      b += elem(W3, bf16, j * d + i) * x[i];
+    }
+    double silu = a / (1.0 + exp(-a));
+    h[j] = silu * b;
+  }
+#pragma omp parallel for schedule(static) num_threads(nt) if (nt > 1)
+  for (int64_t m = 0; m < d; ++m) {
+    double o = 0.0;
+    for (int64_t j = 0; j < F; ++j) o += elem(W2, bf16, m * F + j) * h[j];
+    out[m] = o;
+  }
+  free(h);
+}
+
+/* ---- a6-a9: routed experts, shared experts, weighted combine ------------- */
+
+void orc_forward_rows(const orc_layer* L, const void* x, const int32_t* idx, const double* w, const int32_t* dest,
+                      const void* const* W1e, const void* const* W3e, const void* const* W2e, const void* Ws1,
+                      const void* Ws3, const void* Ws2, const int64_t* tokens, int64_t n_tokens, double* y) {
+  const int64_t d = L->d, K = L->K, F = L->F, Fs = L->Fs;
+  const size_t esz = L->bf16 ? 2 : 4;
+  int max_threads = 1;
+#ifdef _OPENMP
+  max_threads = omp_get_max_threads();
+#endif
+  /* Few tokens: split each expert's output loops across threads instead. */
+  const int inner = (n_tokens < 2 * max_threads) ? max_threads : 1;
+#pragma omp parallel for schedule(dynamic, 1) if (inner == 1)
+  for (int64_t j = 0; j < n_tokens; ++j) {
+    const int64_t t = tokens[j];
+    double* xt = (double*)malloc(sizeof(double) * (size_t)d);
+    double* o = (double*)malloc(sizeof(double) * (size_t)d);
+    double* acc = y + j * d;
+    for (int64_t i = 0; i < d; ++i) {
+      xt[i] = elem(x, L->bf16, t * d + i);
+      acc[i] = 0.0;
+    }
+    /* y = sum_i G_i E_i(x) over the chosen experts  [TD §3.1 step 4]; an
+     * assignment dropped for capacity contributes nothing  [TD §3.2]. */
+    for (int64_t k = 0; k < K; ++k) {
+      if (dest && dest[t * K + k] < 0) continue;
+      const int32_t e = idx[t * K + k];
+      orc_swiglu(d, F, L->bf16, W1e[e], W3e[e], W2e[e], xt, o, inner);
+      for (int64_t i = 0; i < d; ++i) acc[i] += w[t * K + k] * o[i];
+    }
+    /* always-active shared experts, added unweighted  [TD §3.4; §9.1] */
+    for (int64_t s = 0; s < L->n_shared; ++s) {
+      const char* p1 = (const char*)Ws1 + (size_t)(s * Fs * d) * esz;
+      const char* p3 = (const char*)Ws3 + (size_t)(s * Fs * d) * esz;
+      const char* p2 = (const char*)Ws2 + (size_t)(s * d * Fs) * esz;
+      orc_swiglu(d, Fs, L->bf16, p1, p3, p2, xt, o, inner);
+      for (int64_t i = 0; i < d; ++i) acc[i] += o[i];
+    }
+    /* residual Add of the MoE block  [TD §2.1] */
+    if (L->residual)
+      for (int64_t i = 0; i < d; ++i) acc[i] += xt[i];
+    free(xt);
+    free(o);
+  }
+}
+
+/* ---- expert-choice routing  [TD §3.3] ------------------------------------ */
+
+void orc_expert_choice(const orc_layer* L, const float* logits, int64_t cap, int32_t* tok, double* g) {
+  const int64_t T = L->T, E = L->E;
+#pragma omp parallel
+  {
+    int64_t* order = (int64_t*)malloc(sizeof(int64_t) * (size_t)(T > 0 ? T : 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t e = 0; e < E; ++e) {
+      for (int64_t t = 0; t < T; ++t) order[t] = t;
+      for (int64_t c = 0; c < cap && c < T; ++c) {
+        int64_t best = c;
+        for (int64_t j = c + 1; j < T; ++j) {
+          float a = logits[order[j] * E + e], b = logits[order[best] * E + e];
+          if (a > b || (a == b && order[j] < order[best])) best = j;
+        }
+        int64_t tmp = order[c];
+        order[c] = order[best];
+        order[best] = tmp;
+        const int64_t t = order[c];
+        const float* l = logits + t * E;
+        double m = -INFINITY, z = 0.0;
+        for (int64_t q = 0; q < E; ++q) m = fmax(m, (double)l[q]);
+        for (int64_t q = 0; q < E; ++q) z += exp((double)l[q] - m);
+        tok[e * cap + c] = (int32_t)t;
+        g[e * cap + c] = exp((double)l[e] - m) / z;
+      }
+    }
+    free(order);
+  }
+}

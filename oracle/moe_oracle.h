@@ -1,0 +1,114 @@
+/*
+ * moe_oracle.h -- plain, slow, obviously-correct CPU reference of one
+ * sparsely-gated Mixture-of-Experts FFN layer forward.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The product path (the
+ * HIP library under mixture_experts_sparse_route_amd/) never calls it, and the
+ * two share no code, header, table or constant.
+ *
+ * Conventions
+ *   - All pointers are host pointers, row-major, caller-owned.
+ *   - "bf16" tensors are raw bf16 bit patterns (uint16); they are widened to
+ *     fp32 exactly, then to double.
+ *   - Every floating-point reduction runs in double, in ascending index order,
+ *     one accumulator per output, so results do not depend on the thread count.
+ *
+ * Sources (pages of the reference set, cited by title and section):
+ *   [TD]  "技术日报 2026-04-14" (jsqmd.com): §2.1 MoE block, §3.1 Top-K
+ *         routing (Shazeer), §3.2 Switch top-1 and capacity factor, §3.4
+ *         shared experts, §3.5 sigmoid gate, §4.3 selection-only bias, §9.1
+ *         MoELayer code, §9.2 AuxFreeRouter code.
+ *   [BD]  "MoE稀疏架构：定义、原理与工程实践" (cloud.baidu.com): §3.2 gating
+ *         network, §4 six-step forward workflow.
+ *   [LN]  lnwmold.com article on GPT-4-class sparse activation: §2.2 expert
+ *         FFN with W1/W2/W3, §3.2 capacity example, §5.5 toy MoE layer.
+ *
+ * Parity pins: every function here is pinned by the CPU test suite against
+ * library routines, brute force, closed forms or the pages' worked numbers;
+ * none is "parity unpinned".
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_GATE_SOFTMAX = 0, ORC_GATE_SIGMOID = 1 };
+
+typedef struct orc_layer {
+  int64_t T;        /* tokens */
+  int64_t d;        /* d_model */
+  int64_t F;        /* routed expert d_ff */
+  int64_t E;        /* routed experts */
+  int64_t K;        /* experts per token */
+  int32_t gate;     /* ORC_GATE_* */
+  int32_t renorm;   /* renormalise the K selected weights */
+  int32_t residual; /* add x to the output (the block's residual Add) */
+  int32_t bf16;     /* 1: x, expert weights and y are bf16; 0: fp32 */
+  double capacity_factor; /* <= 0: no capacity limit */
+  int64_t n_shared; /* always-active shared experts */
+  int64_t Fs;       /* shared expert d_ff */
+} orc_layer;
+
+/* a1. logits[t][e] = fp32( sum_i x[t][i] * Wg[e][i] + logit_bias[e] )  [TD §3.1 step 1]
+ * logit_bias may be NULL. */
+void orc_logits(const orc_layer* L, const void* x, const float* Wg, const float* logit_bias, float* logits);
+
+/* a2 + a3.  Gate, selection key, Top-K and weights for every token.
+ *   softmax gate: key = logit; p = softmax over all E logits (double)
+ *   sigmoid gate: s = fp32(sigmoid(logit)); key = fp32(s + sel_bias[e])
+ *   Top-K = the K largest keys, ties to the lower expert, in key-descending order.
+ *   w[t][k] = p (or s) of the chosen expert; renormalised to sum 1 if L->renorm.
+ *   gap[t] = key of the K-th choice minus key of the (K+1)-th (+inf if K == E).
+ * sel_bias may be NULL (treated as 0); it never enters w.  gap may be NULL. */
+void orc_select(const orc_layer* L, const float* logits, const float* sel_bias, int32_t* idx, double* w,
+                double* gap);
+
+/* Per-expert capacity: floor(cf * T * K / E) when cf > 0, else -1 (no limit).  [TD §3.2] */
+int64_t orc_capacity(const orc_layer* L);
+
+/* a4.  Histogram, capacity and stable permutation of the T*K assignments
+ * f = t*K + k.  pos(f) = number of earlier f' (in f order) with the same
+ * expert; kept iff pos < capacity.  counts[e] = demand; offsets = exclusive
+ * scan of min(counts, capacity) with offsets[E] = R; dest[f] = offsets[e] +
+ * pos(f) or -1 when dropped; row_src[dest[f]] = f for kept f (entries >= R
+ * are set to -1); dropped[f] = (dest[f] < 0). */
+void orc_permute(const orc_layer* L, const int32_t* idx, int32_t* counts, int32_t* offsets, int32_t* dest,
+                 int32_t* row_src, uint8_t* dropped);
+
+/* a6 + a7 for one row and one expert:
+ *   out[m] = sum_j W2[m][j] * h_j,   h_j = SiLU(a_j) * b_j,  SiLU(z) = z / (1 + e^-z),
+ *   a_j = sum_i W1[j][i] x[i],  b_j = sum_i W3[j][i] x[i].          [LN §2.2]
+ * W1, W3: [F][d]; W2: [d][F]; bf16 or fp32 per `bf16`; x, out in double.
+ * If `threads` > 1 the output loops are split across OpenMP threads. */
+void orc_swiglu(int64_t d, int64_t F, int32_t bf16, const void* W1, const void* W3, const void* W2,
+                const double* x, double* out, int32_t threads);
+
+/* a6-a9 for the listed tokens:
+ *   y[j] = sum_{k ascending, dest[t][k] >= 0} w[t][k] * E_{idx[t][k]}(x_t)
+ *        + sum_s Shared_s(x_t)  (+ x_t if L->residual),   t = tokens[j].
+ * [TD §3.1 step 4, §3.4, §9.1; BD §4]
+ * W1e/W3e/W2e: E pointers, one per expert ([F][d], [F][d], [d][F]); entries
+ * for experts no listed token uses may be NULL.  Ws1/Ws3/Ws2: the shared
+ * experts, [S][Fs][d], [S][Fs][d], [S][d][Fs] (NULL when n_shared == 0).
+ * dest may be NULL (every assignment kept).  y: [n_tokens][d] double. */
+void orc_forward_rows(const orc_layer* L, const void* x, const int32_t* idx, const double* w, const int32_t* dest,
+                      const void* const* W1e, const void* const* W3e, const void* const* W2e, const void* Ws1,
+                      const void* Ws3, const void* Ws2, const int64_t* tokens, int64_t n_tokens, double* y);
+
+/* Expert-choice routing [TD §3.3]: the affinity matrix is S = logits [T][E];
+ * each expert e takes the `cap` tokens with the largest S[:, e] (ties to the
+ * lower token), in descending-affinity order.  tok[e][c] = chosen token;
+ * g[e][c] = the softmax-over-experts probability of that token for e (double;
+ * the page names no combine weight, the token-choice softmax gate of §3.2 is
+ * used).  Requires cap <= T. */
+void orc_expert_choice(const orc_layer* L, const float* logits, int64_t cap, int32_t* tok, double* g);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
