@@ -1,0 +1,209 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse Mixture-of-Experts FFN layer.
+ *
+ * One sparsely-gated MoE FFN layer forward on one GPU, in the order the
+ * pages give it:
+ *   router logits -> softmax or sigmoid gate -> per-token Top-K (optionally
+ *   with a per-expert capacity; overflow assignments are dropped) ->
+ *   dispatch (permute tokens into expert-contiguous rows) -> each expert's
+ *   SwiGLU FFN -> gate-weighted combine back to token order.
+ *
+ * Sources, cited by page title and section:
+ *   [TD] "技术日报 2026-04-14" (jsqmd.com)
+ *   [BD] "MoE稀疏架构：定义、原理与工程实践" (cloud.baidu.com)
+ *   [LN] lnwmold.com article on GPT-4-class sparse activation
+ *
+ * General rules for every entry point
+ *   - Pointers named as device pointers must be device memory of the current
+ *     HIP device (or be NULL where a parameter says "nullable").  Every array
+ *     is dense row-major; the caller owns all memory.  The library never
+ *     allocates device memory: scratch lives in the caller's workspace
+ *     (size from moe_workspace_size), 256-byte aligned.
+ *   - Configs and routing descriptors are host structs, read during the call.
+ *   - All GPU work is enqueued on `stream` (NULL = the default stream) and is
+ *     asynchronous.  Argument validation is synchronous, happens on the host
+ *     before any launch, and returns MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED /
+ *     MOE_ERR_WORKSPACE without touching the GPU.  A failed launch returns
+ *     MOE_ERR_HIP.  moe_last_error() gives a thread-local detail string.
+ *   - The number of kept rows R is computed on the device and never read
+ *     back, so no call synchronises with the host.
+ *   - Calls are stateless; calls sharing a workspace must be stream-ordered.
+ *   - Results are deterministic: no floating-point atomics; every reduction
+ *     has a fixed order.  Behaviour on non-finite inputs is undefined.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t. */
+typedef struct ihipStream_t* moe_stream_t;
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* a size, pointer or enum is out of range */
+  MOE_ERR_UNSUPPORTED = 2, /* valid, but this build does not implement it */
+  MOE_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than moe_workspace_size */
+  MOE_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+} moe_status;
+
+/* Element types.  Router weights and logits are always fp32. */
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Gate [TD §3.2 softmax; TD §3.5 sigmoid]. */
+typedef enum moe_gate { MOE_GATE_SOFTMAX = 0, MOE_GATE_SIGMOID = 1 } moe_gate;
+
+/* Flags (moe_config.flags). */
+enum {
+  /* Renormalise the K selected gate values to sum to 1 [TD §9.1]. */
+  MOE_F_RENORM = 1u,
+  /* Add x to y: the MoE block's residual Add [TD §2.1].  Dropped
+   * assignments then pass x through unchanged [TD §3.2]. */
+  MOE_F_RESIDUAL = 2u,
+  /* moe_route / moe_forward read the caller's fp32 logits from
+   * routing->logits instead of computing x . Wg. */
+  MOE_F_LOGITS_IN = 4u,
+  /* moe_route / moe_forward read the caller's Top-K choice from
+   * routing->topk_idx and routing->topk_w and skip logits and gate. */
+  MOE_F_TOPK_IN = 8u
+};
+
+/* Layer description.  T = tokens, d = d_model, F = d_ff, E = n_experts,
+ * K = top_k. */
+typedef struct moe_config {
+  int64_t tokens;          /* T >= 0; T == 0 makes every call a no-op */
+  int64_t d_model;         /* d >= 1; bf16: multiple of 64 */
+  int64_t d_ff;            /* F >= 1; bf16: multiple of 64 */
+  int64_t n_experts;       /* 1 <= E <= 1024 */
+  int64_t top_k;           /* 1 <= K <= min(E, 32) */
+  int32_t gate;            /* moe_gate */
+  uint32_t flags;          /* MOE_F_* */
+  /* Capacity factor C [TD §3.2].  C > 0: each expert keeps at most
+   * K_max = floor(C * T * K / E) assignments (T*K counts (token, choice)
+   * pairs, which is T for top-1); the first K_max in flat order f = t*K + k
+   * are kept and the rest dropped.  C <= 0: no limit. */
+  double capacity_factor;
+  int64_t n_shared;        /* always-active shared experts, 0 or 1 [TD §3.4] */
+  int64_t d_ff_shared;     /* shared expert d_ff; bf16: multiple of 64 */
+  int32_t act_dtype;       /* moe_dtype of x and the expert activations (xp, h) */
+  int32_t w_dtype;         /* moe_dtype of the expert weights; must equal act_dtype */
+  /* moe_dtype of y: act_dtype, or MOE_F32 for a bf16 layer (the fp32 sum
+   * before its final rounding; the bf16 output is exactly its
+   * round-to-nearest-even image). */
+  int32_t out_dtype;
+} moe_config;
+
+/* Routing arrays, all DEVICE pointers.  Sizes are in elements. */
+typedef struct moe_routing {
+  float* logits;     /* [T, E]  fp32 router logits (input with MOE_F_LOGITS_IN) */
+  int32_t* topk_idx; /* [T, K]  chosen experts, key-descending, ties to the lower index */
+  float* topk_w;     /* [T, K]  gate weights of the chosen experts */
+  int32_t* counts;   /* [E]     assignments per expert before capacity (demand) */
+  int32_t* offsets;  /* [E+1]   exclusive scan of kept counts; offsets[E] = R */
+  int32_t* dest;     /* [T*K]   row of assignment f = t*K + k in xp / yp, or -1 if dropped */
+  int32_t* row_src;  /* [T*K]   assignment f held by row r (r < R); rows >= R are not written */
+  uint8_t* dropped;  /* [T*K]   1 if assignment f was dropped for capacity */
+} moe_routing;
+
+/* Bytes of workspace any entry point needs for `cfg` (the same figure is
+ * enough for all of them).  Host only. */
+moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
+
+/* Upper bound of the kept-row count R for `cfg`: min(T*K, E*K_max), or T*K
+ * without capacity.  Host only; size xp / yp with it. */
+moe_status moe_max_rows(const moe_config* cfg, int64_t* rows);
+
+/* a1-a4: router logits, gate, Top-K and weights, per-expert histogram,
+ * capacity and stable permutation.
+ *   logits[t][e] = x[t] . Wg[e] (+ logit_bias[e])                  [TD §3.1]
+ *   softmax gate: key = logit; p = softmax over all E logits        [TD §3.2]
+ *   sigmoid gate: s = sigmoid(logit) (fp32); key = s + sel_bias[e]  [TD §3.5, §4.3]
+ *   topk_idx = the K largest keys, ties to the lower expert index (keys are
+ *   compared as IEEE values, -0 equal to +0), in key-descending order;
+ *   topk_w = p (or s) of each choice, divided by their sum with MOE_F_RENORM.
+ *   counts / offsets / dest / row_src / dropped as described in moe_routing,
+ *   with the first-come (flat order) capacity rule.            [TD §3.2]
+ * x:          device, [T, d] act_dtype
+ * Wg:         device, [E, d] fp32 (unused with MOE_F_LOGITS_IN / MOE_F_TOPK_IN)
+ * logit_bias: device, [E] fp32, nullable; added to the logits (enters both
+ *             selection and weights)
+ * sel_bias:   device, [E] fp32, nullable; sigmoid gate only; enters the
+ *             selection key, never the weights
+ * r:          every pointer required.  With MOE_F_TOPK_IN, r->logits is not
+ *             touched and topk_idx / topk_w are inputs (idx in [0, E),
+ *             distinct per token, not checked on the device).
+ */
+moe_status moe_route(const moe_config* cfg, const void* x, const float* Wg, const float* logit_bias,
+                     const float* sel_bias, const moe_routing* r, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* a5: dispatch.  xp[row][:] = x[row_src[row] / K][:] for every kept row
+ * (R = offsets[E] rows, read on the device) [BD §4 step 3; TD §9.1].
+ * x: device [T, d]; xp: device [max_rows, d], act_dtype.  Uses r->row_src and
+ * r->offsets only. */
+moe_status moe_dispatch(const moe_config* cfg, const void* x, const moe_routing* r, void* xp, moe_stream_t stream);
+
+/* a6-a7: grouped SwiGLU experts [LN §2.2]. For each group g < n_groups, rows
+ * offsets[g] .. offsets[g+1]-1 of xp go through expert g:
+ *   yp[row] = W2[g] . ( SiLU(W1[g] . xp[row]) * (W3[g] . xp[row]) ),  SiLU(z) = z / (1 + e^-z)
+ * xp:      device [max_rows, d] act_dtype
+ * offsets: device [n_groups + 1] int32, offsets[0] = 0, non-decreasing,
+ *          offsets[n_groups] <= max_rows (not checked on the device)
+ * W1, W3:  device [n_groups, F, d] w_dtype (nn.Linear out x in layout)
+ * W2:      device [n_groups, d, F] w_dtype
+ * yp:      device [max_rows, d] fp32
+ * The intermediate h = SiLU(.) * (.) is kept in act_dtype in the workspace.
+ * max_rows: host upper bound on offsets[n_groups].  n_groups <= 65536. */
+moe_status moe_expert_ffn(const moe_config* cfg, const void* xp, const int32_t* offsets, int64_t n_groups,
+                          int64_t max_rows, const void* W1, const void* W3, const void* W2, float* yp, void* ws,
+                          size_t ws_bytes, moe_stream_t stream);
+
+/* a9: weighted combine [TD §3.1 step 4; BD §4 step 5]:
+ *   y[t] = sum_{k ascending, dest[t*K+k] >= 0} topk_w[t][k] * yp[dest[t*K+k]]
+ *          + shared_out[t] + (x[t] if MOE_F_RESIDUAL)
+ * accumulated in fp32 in that order and rounded once to out_dtype.
+ * yp: device [max_rows, d] fp32; shared_out: device [T, d] fp32, nullable;
+ * x_residual: device [T, d] act_dtype, required iff MOE_F_RESIDUAL;
+ * y: device [T, d] out_dtype.  Uses r->topk_w and r->dest. */
+moe_status moe_combine(const moe_config* cfg, const float* yp, const moe_routing* r, const float* shared_out,
+                       const void* x_residual, void* y, moe_stream_t stream);
+
+/* The whole layer: moe_route, moe_dispatch, moe_expert_ffn, the shared
+ * expert (a SwiGLU over all T rows with Ws1, Ws3 [1, Fs, d], Ws2 [1, d, Fs],
+ * added unweighted [TD §3.4, §9.1]) and moe_combine, in one stream-ordered
+ * sequence with no host synchronisation.
+ * r: nullable; when NULL the routing arrays live in the workspace.  When
+ * given, the routing results are written there (and MOE_F_LOGITS_IN /
+ * MOE_F_TOPK_IN inputs read from there).
+ * Ws1/Ws3/Ws2: required iff n_shared == 1.  y: device [T, d] out_dtype. */
+moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, const float* logit_bias,
+                       const float* sel_bias, const void* W1, const void* W3, const void* W2, const void* Ws1,
+                       const void* Ws3, const void* Ws2, void* y, const moe_routing* r, void* ws, size_t ws_bytes,
+                       moe_stream_t stream);
+
+/* Static string for a status code. */
+const char* moe_status_string(moe_status s);
+
+/* Detail of the calling thread's last failed call ("" if none). */
+const char* moe_last_error(void);
+
+/* ---- Per-kernel timing (diagnostics) --------------------------------------
+ * When enabled, every kernel the library launches is bracketed by a pair of
+ * HIP events recorded on the launch stream.  moe_profile_read synchronises
+ * on the recorded events and returns, per kernel id, the summed duration in
+ * milliseconds and the launch count since the last reset.  Not thread-safe
+ * across concurrent callers; intended for benchmarks. */
+moe_status moe_profile_enable(int enable);
+moe_status moe_profile_reset(void);
+moe_status moe_profile_read(int kernel_id, double* total_ms, int64_t* launches);
+/* Name of kernel id `kernel_id` (NULL past the last id). */
+const char* moe_kernel_name(int kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,261 @@
+"""Python binding of the MI355X sparse-MoE layer library (``libmoe.so``).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current stream.  The
+functions carry the C-ABI names (``moe_route``, ``moe_dispatch``,
+``moe_expert_ffn``, ``moe_combine``, ``moe_forward``); see ``include/moe.h``
+for argument meaning, layouts and error behaviour.
+
+There is no fallback: if ``libmoe.so`` is missing, importing the library
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+MOE_GATE_SOFTMAX, MOE_GATE_SIGMOID = 0, 1
+MOE_F_RENORM, MOE_F_RESIDUAL, MOE_F_LOGITS_IN, MOE_F_TOPK_IN = 1, 2, 4, 8
+
+KERNEL_NAMES = ["router_logits", "router_topk", "route_scan", "route_scatter", "dispatch", "ffn_tiles",
+                "gemm_gate_up", "gemm_down", "combine"]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, fn: str, detail: str):
+        super().__init__(f"{fn}: {_status_name(status)}: {detail}")
+        self.status = status
+
+
+class MoeConfig(ctypes.Structure):
+    _fields_ = [
+        ("tokens", ctypes.c_int64), ("d_model", ctypes.c_int64), ("d_ff", ctypes.c_int64),
+        ("n_experts", ctypes.c_int64), ("top_k", ctypes.c_int64), ("gate", ctypes.c_int32),
+        ("flags", ctypes.c_uint32), ("capacity_factor", ctypes.c_double), ("n_shared", ctypes.c_int64),
+        ("d_ff_shared", ctypes.c_int64), ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+    ]
+
+
+class MoeRouting(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("logits", "topk_idx", "topk_w", "counts", "offsets", "dest", "row_src", "dropped")]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load ``libmoe.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with mixture_experts_sparse_route_amd/build.py")
+    lib = ctypes.CDLL(path)
+    vp, sz, i64, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64, ctypes.c_int
+    C, R = ctypes.POINTER(MoeConfig), ctypes.POINTER(MoeRouting)
+    sigs = {
+        "moe_workspace_size": [C, ctypes.POINTER(sz)],
+        "moe_max_rows": [C, ctypes.POINTER(i64)],
+        "moe_route": [C, vp, vp, vp, vp, R, vp, sz, vp],
+        "moe_dispatch": [C, vp, R, vp, vp],
+        "moe_expert_ffn": [C, vp, vp, i64, i64, vp, vp, vp, vp, vp, sz, vp],
+        "moe_combine": [C, vp, R, vp, vp, vp, vp],
+        "moe_forward": [C, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, R, vp, sz, vp],
+        "moe_profile_enable": [i32],
+        "moe_profile_reset": [],
+        "moe_profile_read": [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)],
+    }
+    for name, args in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_last_error.argtypes = []
+    lib.moe_last_error.restype = ctypes.c_char_p
+    lib.moe_kernel_name.argtypes = [ctypes.c_int]
+    lib.moe_kernel_name.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _status_name(s: int) -> str:
+    try:
+        return load_library().moe_status_string(s).decode()
+    except Exception:  # pragma: no cover - only when the library is absent
+        return str(s)
+
+
+def _check(status: int, fn: str):
+    if status != MOE_OK:
+        raise MoeError(status, fn, load_library().moe_last_error().decode())
+
+
+# ------------------------------------------------------------------ config --
+
+@dataclass
+class LayerSpec:
+    """Layer description, mirrors ``moe_config``."""
+    tokens: int
+    d_model: int
+    d_ff: int
+    n_experts: int
+    top_k: int
+    gate: int = MOE_GATE_SOFTMAX
+    renorm: bool = True
+    residual: bool = False
+    capacity_factor: float = 0.0
+    n_shared: int = 0
+    d_ff_shared: int = 0
+    dtype: str = "bf16"            # "bf16" or "f32" (activations and expert weights)
+    out_dtype: Optional[str] = None  # dtype of y; None = dtype ("f32" allowed for a bf16 layer)
+    logits_in: bool = False
+    topk_in: bool = False
+
+    def config(self) -> MoeConfig:
+        flags = ((MOE_F_RENORM if self.renorm else 0) | (MOE_F_RESIDUAL if self.residual else 0)
+                 | (MOE_F_LOGITS_IN if self.logits_in else 0) | (MOE_F_TOPK_IN if self.topk_in else 0))
+        dt = MOE_BF16 if self.dtype == "bf16" else MOE_F32
+        ot = dt if self.out_dtype is None else (MOE_BF16 if self.out_dtype == "bf16" else MOE_F32)
+        return MoeConfig(self.tokens, self.d_model, self.d_ff, self.n_experts, self.top_k, self.gate, flags,
+                         float(self.capacity_factor), self.n_shared, self.d_ff_shared, dt, dt, ot)
+
+
+def _cfg(spec_or_cfg) -> MoeConfig:
+    return spec_or_cfg.config() if isinstance(spec_or_cfg, LayerSpec) else spec_or_cfg
+
+
+def workspace_size(spec) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().moe_workspace_size(ctypes.byref(_cfg(spec)), ctypes.byref(n)), "moe_workspace_size")
+    return n.value
+
+
+def max_rows(spec) -> int:
+    n = ctypes.c_int64()
+    _check(load_library().moe_max_rows(ctypes.byref(_cfg(spec)), ctypes.byref(n)), "moe_max_rows")
+    return n.value
+
+
+# ----------------------------------------------------------- torch plumbing --
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the MoE library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+class Routing:
+    """Device routing arrays (``moe_routing``) for one config."""
+
+    def __init__(self, spec, device="cuda"):
+        torch = _torch()
+        c = _cfg(spec)
+        T, E, K = c.tokens, c.n_experts, c.top_k
+        self.logits = torch.empty((T, E), dtype=torch.float32, device=device)
+        self.topk_idx = torch.empty((T, K), dtype=torch.int32, device=device)
+        self.topk_w = torch.empty((T, K), dtype=torch.float32, device=device)
+        self.counts = torch.empty((E,), dtype=torch.int32, device=device)
+        self.offsets = torch.empty((E + 1,), dtype=torch.int32, device=device)
+        self.dest = torch.empty((T * K,), dtype=torch.int32, device=device)
+        self.row_src = torch.empty((max(T * K, 1),), dtype=torch.int32, device=device)
+        self.dropped = torch.empty((T * K,), dtype=torch.uint8, device=device)
+
+    def struct(self) -> MoeRouting:
+        return MoeRouting(*(_ptr(getattr(self, n)) for n in
+                            ("logits", "topk_idx", "topk_w", "counts", "offsets", "dest", "row_src", "dropped")))
+
+
+def alloc_workspace(spec, device="cuda"):
+    """A 256-byte aligned device workspace of ``moe_workspace_size`` bytes."""
+    torch = _torch()
+    n = workspace_size(spec)
+    return torch.empty((max(n, 1) + 256,), dtype=torch.uint8, device=device), n
+
+
+def _ws_ptr(ws) -> int:
+    p = ws.data_ptr()
+    return (p + 255) // 256 * 256
+
+
+def _ws_bytes(ws) -> int:
+    return ws.numel() - (_ws_ptr(ws) - ws.data_ptr())
+
+
+# -------------------------------------------------------------- entry points --
+
+def moe_route(spec, x, Wg, logit_bias, sel_bias, routing: Routing, ws, stream=None):
+    r = routing.struct()
+    _check(load_library().moe_route(ctypes.byref(_cfg(spec)), _ptr(x), _ptr(Wg), _ptr(logit_bias), _ptr(sel_bias),
+                                    ctypes.byref(r), _ws_ptr(ws), _ws_bytes(ws), _stream(stream)), "moe_route")
+
+
+def moe_dispatch(spec, x, routing: Routing, xp, stream=None):
+    r = routing.struct()
+    _check(load_library().moe_dispatch(ctypes.byref(_cfg(spec)), _ptr(x), ctypes.byref(r), _ptr(xp),
+                                       _stream(stream)), "moe_dispatch")
+
+
+def moe_expert_ffn(spec, xp, offsets, n_groups, max_rows_, W1, W3, W2, yp, ws, stream=None):
+    _check(load_library().moe_expert_ffn(ctypes.byref(_cfg(spec)), _ptr(xp), _ptr(offsets), n_groups, max_rows_,
+                                         _ptr(W1), _ptr(W3), _ptr(W2), _ptr(yp), _ws_ptr(ws), _ws_bytes(ws),
+                                         _stream(stream)), "moe_expert_ffn")
+
+
+def moe_combine(spec, yp, routing: Routing, shared_out, x_residual, y, stream=None):
+    r = routing.struct()
+    _check(load_library().moe_combine(ctypes.byref(_cfg(spec)), _ptr(yp), ctypes.byref(r), _ptr(shared_out),
+                                      _ptr(x_residual), _ptr(y), _stream(stream)), "moe_combine")
+
+
+def moe_forward(spec, x, Wg, logit_bias, sel_bias, W1, W3, W2, Ws1, Ws3, Ws2, y, routing: Optional[Routing], ws,
+                stream=None):
+    r = routing.struct() if routing is not None else None
+    _check(load_library().moe_forward(ctypes.byref(_cfg(spec)), _ptr(x), _ptr(Wg), _ptr(logit_bias), _ptr(sel_bias),
+                                      _ptr(W1), _ptr(W3), _ptr(W2), _ptr(Ws1), _ptr(Ws3), _ptr(Ws2), _ptr(y),
+                                      ctypes.byref(r) if r is not None else None, _ws_ptr(ws), _ws_bytes(ws),
+                                      _stream(stream)), "moe_forward")
+
+
+# ---------------------------------------------------------------- profiling --
+
+def profile_enable(on: bool = True):
+    _check(load_library().moe_profile_enable(1 if on else 0), "moe_profile_enable")
+
+
+def profile_reset():
+    _check(load_library().moe_profile_reset(), "moe_profile_reset")
+
+
+def profile_read() -> dict:
+    """{kernel name: (total ms, launches)} since the last reset."""
+    lib = load_library()
+    out = {}
+    for i, name in enumerate(KERNEL_NAMES):
+        ms, n = ctypes.c_double(), ctypes.c_int64()
+        _check(lib.moe_profile_read(i, ctypes.byref(ms), ctypes.byref(n)), "moe_profile_read")
+        out[name] = (ms.value, n.value)
+    return out

@@ -1,0 +1,448 @@
+// C-ABI layer of the MoE layer: argument validation (host only, before any
+// HIP call), workspace layout, and the stream-ordered launch sequence.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+#include "moe.h"
+
+namespace moe {
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+moe_status hip_fail(hipError_t e, const char* where) {
+  return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+#define MOE_HIP(call)                                       \
+  do {                                                      \
+    hipError_t e_ = (call);                                 \
+    if (e_ != hipSuccess) return hip_fail(e_, #call);      \
+  } while (0)
+
+constexpr uint32_t kKnownFlags = MOE_F_RENORM | MOE_F_RESIDUAL | MOE_F_LOGITS_IN | MOE_F_TOPK_IN;
+
+// Everything the launches need, derived from a validated config.
+struct Shape {
+  bool bf16;
+  bool out_bf16;
+  int64_t T, d, F, E, K, S, Fs;
+  int64_t cap;       // -1: no limit
+  int64_t max_rows;  // upper bound of kept rows R
+  int64_t n_chunks;  // router_topk workgroups / histogram chunks
+  size_t esz;
+};
+
+moe_status validate(const moe_config* c, Shape* sh) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "config is NULL");
+  if (c->tokens < 0) return fail(MOE_ERR_INVALID_ARG, "tokens = %lld < 0", (long long)c->tokens);
+  if (c->d_model < 1 || c->d_ff < 1) return fail(MOE_ERR_INVALID_ARG, "d_model and d_ff must be >= 1");
+  if (c->n_experts < 1 || c->n_experts > 1024)
+    return fail(MOE_ERR_INVALID_ARG, "n_experts = %lld outside [1, 1024]", (long long)c->n_experts);
+  if (c->top_k < 1 || c->top_k > c->n_experts || c->top_k > 32)
+    return fail(MOE_ERR_INVALID_ARG, "top_k = %lld outside [1, min(n_experts, 32)]", (long long)c->top_k);
+  if (c->gate != MOE_GATE_SOFTMAX && c->gate != MOE_GATE_SIGMOID)
+    return fail(MOE_ERR_INVALID_ARG, "unknown gate %d", (int)c->gate);
+  if (c->flags & ~kKnownFlags) return fail(MOE_ERR_INVALID_ARG, "unknown flag bits 0x%x", c->flags & ~kKnownFlags);
+  if (!std::isfinite(c->capacity_factor)) return fail(MOE_ERR_INVALID_ARG, "capacity_factor is not finite");
+  if (c->n_shared < 0 || c->n_shared > 1) return fail(MOE_ERR_INVALID_ARG, "n_shared must be 0 or 1");
+  if (c->n_shared == 1 && c->d_ff_shared < 1) return fail(MOE_ERR_INVALID_ARG, "d_ff_shared must be >= 1");
+  if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "unknown act_dtype %d", (int)c->act_dtype);
+  if (c->w_dtype != MOE_F32 && c->w_dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "unknown w_dtype %d", (int)c->w_dtype);
+  if (c->w_dtype != c->act_dtype) return fail(MOE_ERR_UNSUPPORTED, "w_dtype must equal act_dtype");
+  if (c->out_dtype != MOE_F32 && c->out_dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "unknown out_dtype %d", (int)c->out_dtype);
+  if (c->act_dtype == MOE_F32 && c->out_dtype != MOE_F32)
+    return fail(MOE_ERR_UNSUPPORTED, "an fp32 layer has an fp32 output");
+  const bool bf16 = c->act_dtype == MOE_BF16;
+  if (bf16) {
+    if (c->d_model % 64 || c->d_ff % 64 || (c->n_shared && c->d_ff_shared % 64))
+      return fail(MOE_ERR_UNSUPPORTED, "bf16 needs d_model, d_ff and d_ff_shared to be multiples of 64");
+  }
+  const int64_t T = c->tokens, d = c->d_model, F = c->d_ff, E = c->n_experts, K = c->top_k;
+  const int64_t Fs = c->n_shared ? c->d_ff_shared : 0;
+  if (T > (int64_t)INT32_MAX / K) return fail(MOE_ERR_UNSUPPORTED, "tokens * top_k exceeds 2^31 - 1");
+  if (T > (int64_t)INT32_MAX / E) return fail(MOE_ERR_UNSUPPORTED, "tokens * n_experts exceeds 2^31 - 1");
+  if (F > (int64_t)INT32_MAX / d || Fs > (int64_t)INT32_MAX / d)
+    return fail(MOE_ERR_UNSUPPORTED, "d_ff * d_model exceeds 2^31 - 1");
+  int64_t cap = -1;
+  if (c->capacity_factor > 0.0) {
+    // K_max = floor(C * N_tokens / N_experts) with N_tokens = T * K assignments
+    const double v = std::floor(c->capacity_factor * (double)(T * K) / (double)E);
+    cap = v > (double)(T * K) ? T * K : (int64_t)v;
+  }
+  sh->bf16 = bf16;
+  sh->out_bf16 = c->out_dtype == MOE_BF16;
+  sh->T = T;
+  sh->d = d;
+  sh->F = F;
+  sh->E = E;
+  sh->K = K;
+  sh->S = c->n_shared;
+  sh->Fs = Fs;
+  sh->cap = cap;
+  sh->max_rows = cap >= 0 ? std::min(T * K, E * cap) : T * K;
+  sh->n_chunks = (T + kTopkTokens - 1) / kTopkTokens;
+  sh->esz = bf16 ? 2 : 4;
+  return MOE_OK;
+}
+
+// ---- workspace layout ----
+struct Layout {
+  size_t blk_count, blk_base, gtile_up, gtile_down, sh_range, sh_gtile_up, sh_gtile_down;
+  size_t h, xp, yp, sh_h, sh_out;
+  size_t r_logits, r_idx, r_w, r_counts, r_offsets, r_dest, r_row_src, r_dropped;
+  size_t total;
+};
+
+Layout layout(const Shape& s) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += (bytes + 255) / 256 * 256;
+    return at;
+  };
+  const size_t TK = (size_t)(s.T * s.K);
+  L.blk_count = take((size_t)(s.n_chunks * s.E) * 4);
+  L.blk_base = take((size_t)(s.n_chunks * s.E) * 4);
+  L.gtile_up = take((size_t)(s.E + 1) * 4);
+  L.gtile_down = take((size_t)(s.E + 1) * 4);
+  L.sh_range = take(2 * 4);
+  L.sh_gtile_up = take(2 * 4);
+  L.sh_gtile_down = take(2 * 4);
+  L.h = take((size_t)s.max_rows * s.F * s.esz);
+  L.xp = take((size_t)s.max_rows * s.d * s.esz);
+  L.yp = take((size_t)s.max_rows * s.d * 4);
+  L.sh_h = take((size_t)(s.S ? s.T * s.Fs : 0) * s.esz);
+  L.sh_out = take((size_t)(s.S ? s.T * s.d : 0) * 4);
+  L.r_logits = take((size_t)(s.T * s.E) * 4);
+  L.r_idx = take(TK * 4);
+  L.r_w = take(TK * 4);
+  L.r_counts = take((size_t)s.E * 4);
+  L.r_offsets = take((size_t)(s.E + 1) * 4);
+  L.r_dest = take(TK * 4);
+  L.r_row_src = take(TK * 4);
+  L.r_dropped = take(TK);
+  L.total = off;
+  return L;
+}
+
+moe_status check_ws(const Shape& s, const void* ws, size_t ws_bytes, Layout* L) {
+  *L = layout(s);
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+  if ((uintptr_t)ws % 256) return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < L->total)
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, L->total);
+  return MOE_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return (T*)((char*)ws + off);
+}
+
+moe_status check_routing(const moe_routing* r, bool need_logits) {
+  if (!r) return fail(MOE_ERR_INVALID_ARG, "routing is NULL");
+  if ((need_logits && !r->logits) || !r->topk_idx || !r->topk_w || !r->counts || !r->offsets || !r->dest ||
+      !r->row_src || !r->dropped)
+    return fail(MOE_ERR_INVALID_ARG, "a routing pointer is NULL");
+  return MOE_OK;
+}
+
+// a1-a4 on a validated shape.
+moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const void* x, const float* Wg,
+                    const float* logit_bias, const float* sel_bias, const moe_routing& r, void* ws, hipStream_t st) {
+  int32_t* blk_count = at<int32_t>(ws, L.blk_count);
+  int32_t* blk_base = at<int32_t>(ws, L.blk_base);
+  const bool topk_in = c->flags & MOE_F_TOPK_IN;
+  if (!topk_in) {
+    if (!(c->flags & MOE_F_LOGITS_IN))
+      MOE_HIP(launch_router_logits(s.bf16, x, Wg, logit_bias, r.logits, s.T, s.d, s.E, st));
+    MOE_HIP(launch_router_topk(r.logits, c->gate == MOE_GATE_SIGMOID ? sel_bias : nullptr, r.topk_idx, r.topk_w,
+                               blk_count, s.T, s.E, s.K, c->gate, c->flags & MOE_F_RENORM, false, st));
+  } else {
+    MOE_HIP(launch_router_topk(nullptr, nullptr, r.topk_idx, nullptr, blk_count, s.T, s.E, s.K, c->gate, false, true,
+                               st));
+  }
+  MOE_HIP(launch_route_scan(blk_count, blk_base, r.counts, r.offsets, s.n_chunks, s.E, s.cap, st));
+  MOE_HIP(launch_route_scatter(r.topk_idx, blk_base, r.offsets, r.dest, r.row_src, r.dropped, s.T, s.K, s.E, s.cap,
+                               st));
+  return MOE_OK;
+}
+
+moe_status do_ffn(const Shape& s, const void* A, const int32_t* offsets, int64_t n_groups, int64_t max_rows,
+                  const void* W1, const void* W3, const void* W2, void* h, float* yp, int32_t* gt_up,
+                  int32_t* gt_down, int64_t F, hipStream_t st) {
+  const FfnPlan plan = ffn_plan(s.bf16, max_rows, n_groups);
+  MOE_HIP(launch_ffn_tiles(plan, offsets, n_groups, F, s.d, gt_up, gt_down, st));
+  MOE_HIP(launch_gemm_gate_up(s.bf16, plan, A, offsets, gt_up, n_groups, max_rows, W1, W3, h, F, s.d, st));
+  MOE_HIP(launch_gemm_down(s.bf16, plan, h, offsets, gt_down, n_groups, max_rows, W2, yp, F, s.d, st));
+  return MOE_OK;
+}
+
+// ---- per-kernel timing ----
+struct ProfRec {
+  int id;
+  hipEvent_t a, b;
+};
+bool g_prof = false;
+std::mutex g_prof_mu;
+std::vector<ProfRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+hipEvent_t g_open = nullptr;
+double g_ms[K_COUNT];
+int64_t g_n[K_COUNT];
+
+hipEvent_t get_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+moe_status resolve_records() {
+  for (const ProfRec& r : g_recs) {
+    MOE_HIP(hipEventSynchronize(r.b));
+    float ms = 0.f;
+    MOE_HIP(hipEventElapsedTime(&ms, r.a, r.b));
+    g_ms[r.id] += ms;
+    g_n[r.id] += 1;
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_recs.clear();
+  return MOE_OK;
+}
+
+const char* const kNames[K_COUNT] = {"router_logits", "router_topk", "route_scan",    "route_scatter", "dispatch",
+                                     "ffn_tiles",     "gemm_gate_up", "gemm_down",    "combine"};
+
+}  // namespace
+
+const char* kernel_name(int id) { return (id >= 0 && id < K_COUNT) ? kNames[id] : nullptr; }
+
+void prof_begin(int id, hipStream_t s) {
+  (void)id;
+  if (!g_prof) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_open = get_event();
+  if (g_open) (void)hipEventRecord(g_open, s);
+}
+
+void prof_end(int id, hipStream_t s) {
+  if (!g_prof) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_open) return;
+  hipEvent_t b = get_event();
+  if (!b) return;
+  (void)hipEventRecord(b, s);
+  g_recs.push_back(ProfRec{id, g_open, b});
+  g_open = nullptr;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes) {
+  Shape s;
+  moe_status st = validate(cfg, &s);
+  if (st != MOE_OK) return st;
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = layout(s).total;
+  return MOE_OK;
+}
+
+moe_status moe_max_rows(const moe_config* cfg, int64_t* rows) {
+  Shape s;
+  moe_status st = validate(cfg, &s);
+  if (st != MOE_OK) return st;
+  if (!rows) return fail(MOE_ERR_INVALID_ARG, "rows is NULL");
+  *rows = s.max_rows;
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_config* cfg, const void* x, const float* Wg, const float* logit_bias,
+                     const float* sel_bias, const moe_routing* r, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  Shape s;
+  moe_status st = validate(cfg, &s);
+  if (st != MOE_OK) return st;
+  const bool topk_in = cfg->flags & MOE_F_TOPK_IN;
+  const bool logits_in = cfg->flags & MOE_F_LOGITS_IN;
+  if ((st = check_routing(r, !topk_in)) != MOE_OK) return st;
+  if (!topk_in && !logits_in && (!x || !Wg)) return fail(MOE_ERR_INVALID_ARG, "x and Wg are required");
+  Layout L;
+  if ((st = check_ws(s, ws, ws_bytes, &L)) != MOE_OK) return st;
+  if (s.T == 0) return MOE_OK;
+  return do_route(cfg, s, L, x, Wg, logit_bias, sel_bias, *r, ws, (hipStream_t)stream);
+}
+
+moe_status moe_dispatch(const moe_config* cfg, const void* x, const moe_routing* r, void* xp, moe_stream_t stream) {
+  Shape s;
+  moe_status st = validate(cfg, &s);
+  if (st != MOE_OK) return st;
+  if (!r || !r->row_src || !r->offsets) return fail(MOE_ERR_INVALID_ARG, "routing row_src / offsets required");
+  if (!x || !xp) return fail(MOE_ERR_INVALID_ARG, "x and xp are required");
+  if (s.T == 0) return MOE_OK;
+  MOE_HIP(launch_dispatch(x, r->row_src, r->offsets + s.E, xp, s.max_rows, s.K, s.d * (int64_t)s.esz,
+                          (hipStream_t)stream));
+  return MOE_OK;
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, const void* xp, const int32_t* offsets, int64_t n_groups,
+                          int64_t max_rows, const void* W1, const void* W3, const void* W2, float* yp, void* ws,
+                          size_t ws_bytes, moe_stream_t stream) {
+  Shape s;
+  moe_status st = validate(cfg, &s);
+  if (st != MOE_OK) return st;
+  if (n_groups < 1 || n_groups > s.E) return fail(MOE_ERR_INVALID_ARG, "n_groups must be in [1, n_experts]");
+  if (max_rows < 0 || max_rows > s.max_rows)
+    return fail(MOE_ERR_INVALID_ARG, "max_rows = %lld outside [0, %lld]", (long long)max_rows,
+                (long long)s.max_rows);
+  if (!xp || !offsets || !W1 || !W3 || !W2 || !yp) return fail(MOE_ERR_INVALID_ARG, "a required pointer is NULL");
+  Layout L;
+  if ((st = check_ws(s, ws, ws_bytes, &L)) != MOE_OK) return st;
+  if (max_rows == 0) return MOE_OK;
+  return do_ffn(s, xp, offsets, n_groups, max_rows, W1, W3, W2, at<void>(ws, L.h), yp, at<int32_t>(ws, L.gtile_up),
+                at<int32_t>(ws, L.gtile_down), s.F, (hipStream_t)stream);
+}
+
+moe_status moe_combine(const moe_config* cfg, const float* yp, const moe_routing* r, const float* shared_out,
+                       const void* x_residual, void* y, moe_stream_t stream) {
+  Shape s;
+  moe_status st = validate(cfg, &s);
+  if (st != MOE_OK) return st;
+  if (!r || !r->topk_w || !r->dest) return fail(MOE_ERR_INVALID_ARG, "routing topk_w / dest required");
+  if (!yp || !y) return fail(MOE_ERR_INVALID_ARG, "yp and y are required");
+  const bool residual = cfg->flags & MOE_F_RESIDUAL;
+  if (residual && !x_residual) return fail(MOE_ERR_INVALID_ARG, "MOE_F_RESIDUAL needs x_residual");
+  if (s.T == 0) return MOE_OK;
+  MOE_HIP(launch_combine(s.bf16, s.out_bf16, yp, r->topk_w, r->dest, shared_out, residual ? x_residual : nullptr, y, s.T, s.d,
+                         s.K, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, const float* logit_bias,
+                       const float* sel_bias, const void* W1, const void* W3, const void* W2, const void* Ws1,
+                       const void* Ws3, const void* Ws2, void* y, const moe_routing* r, void* ws, size_t ws_bytes,
+                       moe_stream_t stream) {
+  Shape s;
+  moe_status st = validate(cfg, &s);
+  if (st != MOE_OK) return st;
+  const bool topk_in = cfg->flags & MOE_F_TOPK_IN;
+  const bool logits_in = cfg->flags & MOE_F_LOGITS_IN;
+  if (!x || !y || !W1 || !W3 || !W2) return fail(MOE_ERR_INVALID_ARG, "x, y, W1, W3, W2 are required");
+  if (!topk_in && !logits_in && !Wg) return fail(MOE_ERR_INVALID_ARG, "Wg is required");
+  if (s.S && (!Ws1 || !Ws3 || !Ws2)) return fail(MOE_ERR_INVALID_ARG, "shared expert weights are required");
+  if ((topk_in || logits_in) && !r) return fail(MOE_ERR_INVALID_ARG, "MOE_F_*_IN needs the routing arrays");
+  if (r && (st = check_routing(r, !topk_in)) != MOE_OK) return st;
+  Layout L;
+  if ((st = check_ws(s, ws, ws_bytes, &L)) != MOE_OK) return st;
+  if (s.T == 0) return MOE_OK;
+  hipStream_t hs = (hipStream_t)stream;
+  moe_routing rr;
+  if (r) {
+    rr = *r;
+  } else {
+    rr.logits = at<float>(ws, L.r_logits);
+    rr.topk_idx = at<int32_t>(ws, L.r_idx);
+    rr.topk_w = at<float>(ws, L.r_w);
+    rr.counts = at<int32_t>(ws, L.r_counts);
+    rr.offsets = at<int32_t>(ws, L.r_offsets);
+    rr.dest = at<int32_t>(ws, L.r_dest);
+    rr.row_src = at<int32_t>(ws, L.r_row_src);
+    rr.dropped = at<uint8_t>(ws, L.r_dropped);
+  }
+  if ((st = do_route(cfg, s, L, x, Wg, logit_bias, sel_bias, rr, ws, hs)) != MOE_OK) return st;
+  void* xp = at<void>(ws, L.xp);
+  float* yp = at<float>(ws, L.yp);
+  if (s.max_rows > 0) {
+    MOE_HIP(launch_dispatch(x, rr.row_src, rr.offsets + s.E, xp, s.max_rows, s.K, s.d * (int64_t)s.esz, hs));
+    if ((st = do_ffn(s, xp, rr.offsets, s.E, s.max_rows, W1, W3, W2, at<void>(ws, L.h), yp,
+                     at<int32_t>(ws, L.gtile_up), at<int32_t>(ws, L.gtile_down), s.F, hs)) != MOE_OK)
+      return st;
+  }
+  float* sh_out = nullptr;
+  if (s.S) {
+    int32_t* range = at<int32_t>(ws, L.sh_range);
+    MOE_HIP(launch_set_range(range, s.T, hs));
+    sh_out = at<float>(ws, L.sh_out);
+    if ((st = do_ffn(s, x, range, 1, s.T, Ws1, Ws3, Ws2, at<void>(ws, L.sh_h), sh_out,
+                     at<int32_t>(ws, L.sh_gtile_up), at<int32_t>(ws, L.sh_gtile_down), s.Fs, hs)) != MOE_OK)
+      return st;
+  }
+  MOE_HIP(launch_combine(s.bf16, s.out_bf16, yp, rr.topk_w, rr.dest, sh_out, (cfg->flags & MOE_F_RESIDUAL) ? x : nullptr, y, s.T,
+                         s.d, s.K, hs));
+  return MOE_OK;
+}
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+moe_status moe_profile_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof = enable != 0;
+  return MOE_OK;
+}
+
+moe_status moe_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  moe_status st = resolve_records();
+  for (int i = 0; i < K_COUNT; ++i) {
+    g_ms[i] = 0.0;
+    g_n[i] = 0;
+  }
+  return st;
+}
+
+moe_status moe_profile_read(int kernel_id, double* total_ms, int64_t* launches) {
+  if (kernel_id < 0 || kernel_id >= K_COUNT || !total_ms || !launches)
+    return fail(MOE_ERR_INVALID_ARG, "bad kernel id or NULL output");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  moe_status st = resolve_records();
+  if (st != MOE_OK) return st;
+  *total_ms = g_ms[kernel_id];
+  *launches = g_n[kernel_id];
+  return MOE_OK;
+}
+
+const char* moe_kernel_name(int kernel_id) { return kernel_name(kernel_id); }
+
+}  // extern "C"

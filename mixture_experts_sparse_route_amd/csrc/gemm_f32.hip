@@ -1,0 +1,144 @@
+// fp32 grouped expert GEMMs (the fp32 layer), the FFN tile plan, and the
+// dispatch between the fp32 and bf16 paths.
+//
+// Same SwiGLU expert as the bf16 path (lnwmold.com article, §2.2): vector
+// FMA, 32 x 32 output tiles, k-tiles of 32 staged through LDS, any sizes.
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int FB = 32;  // rows, columns and k per fp32 tile
+
+struct F32Args {
+  const float* A;
+  const float* B0;
+  const float* B1;
+  float* C;
+  const int32_t* offsets;
+  const int32_t* gtile;
+  int n_groups, N, Kdim;
+};
+
+template <bool GATE_UP>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(const F32Args p) {
+  __shared__ float as[FB][FB + 1];
+  __shared__ float b0s[FB][FB + 1];
+  __shared__ float b1s[GATE_UP ? FB : 1][FB + 1];
+  const int total = p.gtile[p.n_groups];
+  const int64_t L = xcd_tile(blockIdx.x, total);
+  if (L < 0) return;
+  int lo = 0, hi = p.n_groups;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.gtile[mid] <= L) lo = mid; else hi = mid;
+  }
+  const int g = lo;
+  const int row0 = p.offsets[g];
+  const int rows_g = p.offsets[g + 1] - row0;
+  const int mtiles = (rows_g + FB - 1) / FB;
+  const int r = (int)(L - p.gtile[g]);
+  const int nt = r / mtiles, mt = r % mtiles;
+  const int m0 = mt * FB, n0 = nt * FB;
+  const int rows = min(FB, rows_g - m0);
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int64_t gb = (int64_t)g * p.N * p.Kdim;
+  float a00 = 0, a01 = 0, a10 = 0, a11 = 0;
+  float c00 = 0, c01 = 0, c10 = 0, c11 = 0;
+  for (int k0 = 0; k0 < p.Kdim; k0 += FB) {
+    for (int q = threadIdx.x; q < FB * FB; q += 256) {
+      const int rr = q / FB, kk = q % FB, k = k0 + kk;
+      as[rr][kk] = (rr < rows && k < p.Kdim) ? p.A[(int64_t)(row0 + m0 + rr) * p.Kdim + k] : 0.f;
+      const int col = n0 + rr;
+      const bool ok = col < p.N && k < p.Kdim;
+      b0s[rr][kk] = ok ? p.B0[gb + (int64_t)col * p.Kdim + k] : 0.f;
+      if (GATE_UP) b1s[rr][kk] = ok ? p.B1[gb + (int64_t)col * p.Kdim + k] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < FB; ++kk) {
+      const float x0 = as[ty * 2][kk], x1 = as[ty * 2 + 1][kk];
+      const float w0 = b0s[tx * 2][kk], w1 = b0s[tx * 2 + 1][kk];
+      a00 = fmaf(x0, w0, a00);
+      a01 = fmaf(x0, w1, a01);
+      a10 = fmaf(x1, w0, a10);
+      a11 = fmaf(x1, w1, a11);
+      if (GATE_UP) {
+        const float u0 = b1s[tx * 2][kk], u1 = b1s[tx * 2 + 1][kk];
+        c00 = fmaf(x0, u0, c00);
+        c01 = fmaf(x0, u1, c01);
+        c10 = fmaf(x1, u0, c10);
+        c11 = fmaf(x1, u1, c11);
+      }
+    }
+    __syncthreads();
+  }
+  const float av[2][2] = {{a00, a01}, {a10, a11}};
+  const float cv[2][2] = {{c00, c01}, {c10, c11}};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rr = ty * 2 + i;
+    if (rr >= rows) continue;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + tx * 2 + j;
+      if (col >= p.N) continue;
+      const float v = GATE_UP ? silu(av[i][j]) * cv[i][j] : av[i][j];
+      p.C[(int64_t)(row0 + m0 + rr) * p.N + col] = v;
+    }
+  }
+}
+
+}  // namespace
+
+FfnPlan ffn_plan(bool bf16, int64_t max_rows, int64_t n_groups) {
+  (void)max_rows;
+  (void)n_groups;
+  if (bf16) return FfnPlan{256, 128, 256};
+  return FfnPlan{FB, FB, FB};
+}
+
+int64_t ffn_max_mtiles(const FfnPlan& p, int64_t max_rows, int64_t n_groups) {
+  // sum over groups of ceil(rows_g / bm) <= floor(max_rows / bm) + n_groups
+  return max_rows / p.bm + n_groups;
+}
+
+hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const void* A, const int32_t* offsets,
+                               const int32_t* gtile, int64_t n_groups, int64_t max_rows, const void* W1,
+                               const void* W3, void* h, int64_t F, int64_t d, hipStream_t s) {
+  prof_begin(K_GEMM_GATE_UP, s);
+  hipError_t err;
+  if (bf16) {
+    err = gemm_bf16_gate_up(p, A, offsets, gtile, n_groups, max_rows, W1, W3, h, F, d, s);
+  } else {
+    F32Args a{(const float*)A, (const float*)W1, (const float*)W3, (float*)h, offsets, gtile, (int)n_groups, (int)F,
+              (int)d};
+    const int64_t tiles = ffn_max_mtiles(p, max_rows, n_groups) * ((F + FB - 1) / FB);
+    const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
+    if (grid > 0) gemm_f32_kernel<true><<<(unsigned)grid, 256, 0, s>>>(a);
+    err = hipGetLastError();
+  }
+  prof_end(K_GEMM_GATE_UP, s);
+  return err;
+}
+
+hipError_t launch_gemm_down(bool bf16, const FfnPlan& p, const void* h, const int32_t* offsets, const int32_t* gtile,
+                            int64_t n_groups, int64_t max_rows, const void* W2, float* yp, int64_t F, int64_t d,
+                            hipStream_t s) {
+  prof_begin(K_GEMM_DOWN, s);
+  hipError_t err;
+  if (bf16) {
+    err = gemm_bf16_down(p, h, offsets, gtile, n_groups, max_rows, W2, yp, F, d, s);
+  } else {
+    F32Args a{(const float*)h, (const float*)W2, nullptr, yp, offsets, gtile, (int)n_groups, (int)d, (int)F};
+    const int64_t tiles = ffn_max_mtiles(p, max_rows, n_groups) * ((d + FB - 1) / FB);
+    const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
+    if (grid > 0) gemm_f32_kernel<false><<<(unsigned)grid, 256, 0, s>>>(a);
+    err = hipGetLastError();
+  }
+  prof_end(K_GEMM_DOWN, s);
+  return err;
+}
+
+}  // namespace moe

@@ -1,0 +1,80 @@
+// Host-side interface between the C-ABI layer (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Kernel ids for the per-kernel timing facility (order = moe_kernel_name).
+enum KernelId {
+  K_ROUTER_LOGITS = 0,
+  K_ROUTER_TOPK,
+  K_ROUTE_SCAN,
+  K_ROUTE_SCATTER,
+  K_DISPATCH,
+  K_FFN_TILES,
+  K_GEMM_GATE_UP,    // grouped GEMM1 + SiLU*gate epilogue
+  K_GEMM_DOWN,       // grouped GEMM2
+  K_COMBINE,
+  K_COUNT
+};
+const char* kernel_name(int id);
+
+// Records a timing event pair around a launch when profiling is on.
+void prof_begin(int id, hipStream_t s);
+void prof_end(int id, hipStream_t s);
+
+// Tokens per router_topk workgroup; also the histogram chunk (in tokens).
+constexpr int kTopkTokens = 32;
+
+// ---- router (a1-a3) ----
+hipError_t launch_router_logits(bool bf16, const void* x, const float* Wg, const float* bias, float* logits, int64_t T,
+                                int64_t d, int64_t E, hipStream_t s);
+// topk_in: idx is an input; only the per-chunk histogram is produced.
+hipError_t launch_router_topk(const float* logits, const float* sel_bias, int32_t* idx, float* w, int32_t* blk_count,
+                              int64_t T, int64_t E, int64_t K, int gate, bool renorm, bool topk_in, hipStream_t s);
+
+// ---- permutation (a4) and dispatch (a5) ----
+hipError_t launch_route_scan(const int32_t* blk_count, int32_t* blk_base, int32_t* counts, int32_t* offsets,
+                             int64_t n_chunks, int64_t E, int64_t cap, hipStream_t s);
+hipError_t launch_route_scatter(const int32_t* idx, const int32_t* blk_base, const int32_t* offsets, int32_t* dest,
+                                int32_t* row_src, uint8_t* dropped, int64_t T, int64_t K, int64_t E, int64_t cap,
+                                hipStream_t s);
+hipError_t launch_dispatch(const void* x, const int32_t* row_src, const int32_t* R_ptr, void* xp, int64_t max_rows,
+                           int64_t K, int64_t row_bytes, hipStream_t s);
+
+// ---- grouped expert FFN (a6-a7) ----
+struct FfnPlan {
+  int bm;           // rows per m-tile
+  int bn_out_up;    // h columns per GEMM1 tile
+  int bn_out_down;  // yp columns per GEMM2 tile
+};
+FfnPlan ffn_plan(bool bf16, int64_t max_rows, int64_t n_groups);
+// Worst-case tile-list entries for the plan.
+int64_t ffn_max_mtiles(const FfnPlan& p, int64_t max_rows, int64_t n_groups);
+// gtile_up / gtile_down: [n_groups + 1] int32 cumulative tile counts.
+hipError_t launch_ffn_tiles(const FfnPlan& p, const int32_t* offsets, int64_t n_groups, int64_t F, int64_t d,
+                            int32_t* gtile_up, int32_t* gtile_down, hipStream_t s);
+// bf16 MFMA path (gemm_bf16.hip); called through the launchers below.
+hipError_t gemm_bf16_gate_up(const FfnPlan& p, const void* A, const int32_t* offsets, const int32_t* gtile,
+                             int64_t n_groups, int64_t max_rows, const void* W1, const void* W3, void* h, int64_t F,
+                             int64_t d, hipStream_t s);
+hipError_t gemm_bf16_down(const FfnPlan& p, const void* h, const int32_t* offsets, const int32_t* gtile,
+                          int64_t n_groups, int64_t max_rows, const void* W2, float* yp, int64_t F, int64_t d,
+                          hipStream_t s);
+hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const void* A, const int32_t* offsets,
+                               const int32_t* gtile, int64_t n_groups, int64_t max_rows, const void* W1,
+                               const void* W3, void* h, int64_t F, int64_t d, hipStream_t s);
+hipError_t launch_gemm_down(bool bf16, const FfnPlan& p, const void* h, const int32_t* offsets, const int32_t* gtile,
+                            int64_t n_groups, int64_t max_rows, const void* W2, float* yp, int64_t F, int64_t d,
+                            hipStream_t s);
+
+// dst[0] = 0, dst[1] = n (row range of the shared expert).
+hipError_t launch_set_range(int32_t* dst, int64_t n, hipStream_t s);
+
+// ---- combine (a9) ----
+hipError_t launch_combine(bool x_bf16, bool y_bf16, const float* yp, const float* w, const int32_t* dest, const float* shared,
+                          const void* xres, void* y, int64_t T, int64_t d, int64_t K, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,232 @@
+// Capacity and stable permutation (a4), dispatch gather (a5), and the tile
+// list of the grouped expert GEMMs.
+//
+// Capacity rule: "技术日报 2026-04-14" (jsqmd.com) §3.2 -- each expert keeps at
+// most K_max = floor(C * N_tokens / N_experts) assignments; overflow is dropped.
+// The first K_max arrivals in flat (token, choice) order are kept.
+#include <limits.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+// ------------------------------------------------------------ a4: scan
+// One workgroup.  For every expert e: blk_base[b][e] = sum of blk_count[b'][e]
+// over chunks b' < b; counts[e] = total demand; offsets = exclusive scan of
+// min(counts, cap) with offsets[E] = R.  S threads share each expert's chunk
+// range.
+__global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restrict__ blk_count,
+                                                          int32_t* __restrict__ blk_base, int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ offsets, int NB, int E, int Epad,
+                                                          int cap) {
+  __shared__ int part[1024];
+  __shared__ int kept[1024];
+  const int S = 1024 / Epad;
+  const int e = threadIdx.x % Epad, sub = threadIdx.x / Epad;
+  const int per = (NB + S - 1) / S;
+  const int b0 = min(NB, sub * per), b1 = min(NB, b0 + per);
+  int sum = 0;
+  if (e < E)
+    for (int b = b0; b < b1; ++b) sum += blk_count[(int64_t)b * E + e];
+  part[sub * Epad + e] = sum;
+  __syncthreads();
+  if (e < E) {
+    int run = 0;
+    for (int q = 0; q < sub; ++q) run += part[q * Epad + e];
+    for (int b = b0; b < b1; ++b) {
+      blk_base[(int64_t)b * E + e] = run;
+      run += blk_count[(int64_t)b * E + e];
+    }
+    if (sub == S - 1) {
+      counts[e] = run;
+      kept[e] = min(run, cap);
+    }
+  } else if (sub == S - 1) {
+    kept[e] = 0;
+  }
+  __syncthreads();
+  // inclusive Hillis-Steele scan of kept[0 .. Epad) with the first Epad threads
+  for (int off = 1; off < Epad; off <<= 1) {
+    int v = 0;
+    if (threadIdx.x < Epad && threadIdx.x >= off) v = kept[threadIdx.x - off];
+    __syncthreads();
+    if (threadIdx.x < Epad) kept[threadIdx.x] += v;
+    __syncthreads();
+  }
+  if (threadIdx.x < E) offsets[threadIdx.x + 1] = kept[threadIdx.x];
+  if (threadIdx.x == 0) offsets[0] = 0;
+}
+
+// ------------------------------------------------------------ a4: scatter
+// Chunk b (kTopkTokens tokens = kTopkTokens*K assignments) is ranked in passes
+// of 256 assignments.  Within a wave, lanes holding the same expert find each
+// other with one ballot per expert-id bit; a lane's rank is the number of
+// lower lanes in its peer set.  Per-wave counts are then scanned across the
+// four waves in LDS, and a running per-expert count carries across passes.
+// pos(f) = blk_base[b][e] + (earlier passes) + (earlier waves) + rank, which
+// is the number of assignments before f in flat order with the same expert.
+__global__ __launch_bounds__(256) void route_scatter_kernel(const int32_t* __restrict__ idx,
+                                                            const int32_t* __restrict__ blk_base,
+                                                            const int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ dest, int32_t* __restrict__ row_src,
+                                                            uint8_t* __restrict__ dropped, int T, int K, int E,
+                                                            int nbits, int cap) {
+  __shared__ int running[1024];
+  __shared__ int wcnt[4][1024];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t f_begin = (int64_t)blockIdx.x * kTopkTokens * K;
+  const int64_t f_end = min((int64_t)T * K, f_begin + (int64_t)kTopkTokens * K);
+  for (int e = threadIdx.x; e < E; e += 256) running[e] = blk_base[(int64_t)blockIdx.x * E + e];
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t pass = f_begin; pass < f_end; pass += 256) {
+    for (int q = threadIdx.x; q < 4 * E; q += 256) wcnt[q / E][q % E] = 0;
+    __syncthreads();
+    const int64_t f = pass + threadIdx.x;
+    int e = f < f_end ? idx[f] : -1;
+    const bool valid = e >= 0 && e < E;  // out-of-range choices are dropped
+    if (!valid) e = 0;
+    uint64_t peers = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool mine = (e >> bit) & 1;
+      const uint64_t bal = __ballot(mine);
+      peers &= mine ? bal : ~bal;
+    }
+    const int rank = __popcll(peers & lt_mask);
+    // the highest lane of each peer set publishes the set size
+    if (valid && (peers >> lane) == 1ull) wcnt[wave][e] = __popcll(peers);
+    __syncthreads();
+    int pos = 0;
+    if (valid) {
+      pos = running[e] + rank;
+      for (int q = 0; q < wave; ++q) pos += wcnt[q][e];
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < E; q += 256) running[q] += wcnt[0][q] + wcnt[1][q] + wcnt[2][q] + wcnt[3][q];
+    if (f < f_end) {
+      const bool keep = valid && pos < cap;
+      const int32_t d = keep ? offsets[e] + pos : -1;
+      dest[f] = d;
+      dropped[f] = keep ? 0 : 1;
+      if (keep) row_src[d] = (int32_t)f;
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------ a5: dispatch
+// xp[r] = x[row_src[r] / K] for r < R; R = offsets[E] read on the device.
+template <typename V>
+__global__ __launch_bounds__(256) void dispatch_kernel(const V* __restrict__ x, const int32_t* __restrict__ row_src,
+                                                       const int32_t* __restrict__ R_ptr, V* __restrict__ xp, int K,
+                                                       int row_vecs, int rows_per_block) {
+  const int R = *R_ptr;
+  const int r0 = blockIdx.x * rows_per_block;
+  for (int rr = 0; rr < rows_per_block; ++rr) {
+    const int r = r0 + rr;
+    if (r >= R) return;
+    const int64_t t = row_src[r] / K;
+    const V* src = x + t * row_vecs;
+    V* dst = xp + (int64_t)r * row_vecs;
+    for (int c = threadIdx.x; c < row_vecs; c += 256) dst[c] = src[c];
+  }
+}
+
+// ------------------------------------------------------------ FFN tiles
+// gtile[g] = sum over g' < g of ceil(rows(g') / bm) * n_ntiles, for both GEMMs.
+__global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t* __restrict__ offsets, int G, int bm,
+                                                         int nt_up, int nt_down, int32_t* __restrict__ gtile_up,
+                                                         int32_t* __restrict__ gtile_down) {
+  __shared__ int carry;
+  __shared__ int buf[1024];
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int g0 = 0; g0 < G; g0 += 1024) {
+    const int g = g0 + threadIdx.x;
+    int mt = 0;
+    if (g < G) {
+      const int rows = offsets[g + 1] - offsets[g];
+      mt = rows > 0 ? (rows + bm - 1) / bm : 0;
+    }
+    buf[threadIdx.x] = mt;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int v = threadIdx.x >= off ? buf[threadIdx.x - off] : 0;
+      __syncthreads();
+      buf[threadIdx.x] += v;
+      __syncthreads();
+    }
+    if (g < G) {
+      const int excl = carry + buf[threadIdx.x] - mt;
+      gtile_up[g] = excl * nt_up;
+      gtile_down[g] = excl * nt_down;
+    }
+    __syncthreads();
+    if (threadIdx.x == 1023) carry += buf[1023];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    gtile_up[G] = carry * nt_up;
+    gtile_down[G] = carry * nt_down;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_route_scan(const int32_t* blk_count, int32_t* blk_base, int32_t* counts, int32_t* offsets,
+                             int64_t n_chunks, int64_t E, int64_t cap, hipStream_t s) {
+  int Epad = 1;
+  while (Epad < E) Epad <<= 1;
+  const int capi = cap < 0 || cap > INT_MAX ? INT_MAX : (int)cap;
+  prof_begin(K_ROUTE_SCAN, s);
+  route_scan_kernel<<<1, 1024, 0, s>>>(blk_count, blk_base, counts, offsets, (int)n_chunks, (int)E, Epad, capi);
+  prof_end(K_ROUTE_SCAN, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_scatter(const int32_t* idx, const int32_t* blk_base, const int32_t* offsets, int32_t* dest,
+                                int32_t* row_src, uint8_t* dropped, int64_t T, int64_t K, int64_t E, int64_t cap,
+                                hipStream_t s) {
+  int nbits = 0;
+  while ((1ll << nbits) < E) ++nbits;
+  const int capi = cap < 0 || cap > INT_MAX ? INT_MAX : (int)cap;
+  const unsigned nb = (unsigned)((T + kTopkTokens - 1) / kTopkTokens);
+  prof_begin(K_ROUTE_SCATTER, s);
+  route_scatter_kernel<<<nb, 256, 0, s>>>(idx, blk_base, offsets, dest, row_src, dropped, (int)T, (int)K, (int)E,
+                                          nbits, capi);
+  prof_end(K_ROUTE_SCATTER, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch(const void* x, const int32_t* row_src, const int32_t* R_ptr, void* xp, int64_t max_rows,
+                           int64_t K, int64_t row_bytes, hipStream_t s) {
+  int rpb = row_bytes >= 4096 ? 1 : (int)(4096 / row_bytes);
+  if (rpb > 64) rpb = 64;
+  const unsigned nb = (unsigned)((max_rows + rpb - 1) / rpb);
+  if (nb == 0) return hipSuccess;
+  prof_begin(K_DISPATCH, s);
+  if (row_bytes % 16 == 0)
+    dispatch_kernel<uint4><<<nb, 256, 0, s>>>((const uint4*)x, row_src, R_ptr, (uint4*)xp, (int)K,
+                                              (int)(row_bytes / 16), rpb);
+  else if (row_bytes % 4 == 0)
+    dispatch_kernel<uint32_t><<<nb, 256, 0, s>>>((const uint32_t*)x, row_src, R_ptr, (uint32_t*)xp, (int)K,
+                                                 (int)(row_bytes / 4), rpb);
+  else
+    dispatch_kernel<uint16_t><<<nb, 256, 0, s>>>((const uint16_t*)x, row_src, R_ptr, (uint16_t*)xp, (int)K,
+                                                 (int)(row_bytes / 2), rpb);
+  prof_end(K_DISPATCH, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_tiles(const FfnPlan& p, const int32_t* offsets, int64_t n_groups, int64_t F, int64_t d,
+                            int32_t* gtile_up, int32_t* gtile_down, hipStream_t s) {
+  const int nt_up = (int)((F + p.bn_out_up - 1) / p.bn_out_up);
+  const int nt_down = (int)((d + p.bn_out_down - 1) / p.bn_out_down);
+  prof_begin(K_FFN_TILES, s);
+  ffn_tiles_kernel<<<1, 1024, 0, s>>>(offsets, (int)n_groups, p.bm, nt_up, nt_down, gtile_up, gtile_down);
+  prof_end(K_FFN_TILES, s);
+  return hipGetLastError();
+}
+
+}  // namespace moe

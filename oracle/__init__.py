@@ -58,6 +58,8 @@ def _load():
         lib.orc_swiglu.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp, i32]
         lib.orc_forward_rows.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]
         lib.orc_expert_choice.argtypes = [P, vp, i64, vp, vp]
+        lib.orc_combine.argtypes = [P, vp, vp, vp, vp, vp, vp]
+        lib.orc_combine.restype = None
         for fn in (lib.orc_logits, lib.orc_select, lib.orc_permute, lib.orc_swiglu, lib.orc_forward_rows,
                    lib.orc_expert_choice):
             fn.restype = None
@@ -155,6 +157,16 @@ def forward_rows(L: OrcLayer, x, idx, w, dest, W1e, W3e, W2e, Ws1=None, Ws3=None
                              ctypes.cast(p2, ctypes.c_void_p), _p(Ws1), _p(Ws3), _p(Ws2), _p(tokens), len(tokens),
                              _p(y))
     del k1, k3, k2
+    return y
+
+
+def combine(L: OrcLayer, yp, w, dest, shared=None, x=None) -> np.ndarray:
+    """a9 alone: y float64 [T, d] from fp32 expert rows yp [R, d]."""
+    y = np.empty((L.T, L.d), dtype=np.float64)
+    _load().orc_combine(ctypes.byref(L), _p(np.ascontiguousarray(yp, dtype=np.float32)),
+                        _p(np.ascontiguousarray(w, dtype=np.float64)), _p(np.ascontiguousarray(dest, dtype=np.int32)),
+                        _p(None if shared is None else np.ascontiguousarray(shared, dtype=np.float32)),
+                        _p(x), _p(y))
     return y
 
 

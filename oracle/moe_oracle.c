@@ -227,6 +227,27 @@ void orc_forward_rows(const orc_layer* L, const void* x, const int32_t* idx, con
   }
 }
 
+/* ---- a9 alone ------------------------------------------------------------ */
+
+void orc_combine(const orc_layer* L, const float* yp, const double* w, const int32_t* dest, const float* shared,
+                 const void* x, double* y) {
+  const int64_t T = L->T, d = L->d, K = L->K;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    double* acc = y + t * d;
+    for (int64_t i = 0; i < d; ++i) acc[i] = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      const int32_t r = dest[t * K + k];
+      if (r < 0) continue;
+      for (int64_t i = 0; i < d; ++i) acc[i] += w[t * K + k] * (double)yp[(int64_t)r * d + i];
+    }
+    if (shared)
+      for (int64_t i = 0; i < d; ++i) acc[i] += (double)shared[t * d + i];
+    if (L->residual)
+      for (int64_t i = 0; i < d; ++i) acc[i] += elem(x, L->bf16, t * d + i);
+  }
+}
+
 /* ---- expert-choice routing  [TD §3.3] ------------------------------------ */
 
 void orc_expert_choice(const orc_layer* L, const float* logits, int64_t cap, int32_t* tok, double* g) {

@@ -100,6 +100,13 @@ void orc_forward_rows(const orc_layer* L, const void* x, const int32_t* idx, con
                       const void* const* W1e, const void* const* W3e, const void* const* W2e, const void* Ws1,
                       const void* Ws3, const void* Ws2, const int64_t* tokens, int64_t n_tokens, double* y);
 
+/* a9 alone: y[t] = sum_{k ascending, dest[t][k] >= 0} w[t][k] * yp[dest[t][k]]
+ *                 + shared[t]  (+ x[t] if L->residual)            [TD §3.1 step 4]
+ * yp: [R][d] fp32 expert-output rows; w: [T][K] double; shared: [T][d] fp32,
+ * may be NULL; y: [T][d] double. */
+void orc_combine(const orc_layer* L, const float* yp, const double* w, const int32_t* dest, const float* shared,
+                 const void* x, double* y);
+
 /* Expert-choice routing [TD §3.3]: the affinity matrix is S = logits [T][E];
  * each expert e takes the `cap` tokens with the largest S[:, e] (ties to the
  * lower token), in descending-affinity order.  tok[e][c] = chosen token;

@@ -421,3 +421,23 @@ def test_expert_choice_vs_brute_force():
         order = sorted(range(T), key=lambda t: (-float(lg[t, e]), t))[:cap]
         assert tok[e].tolist() == order
         np.testing.assert_allclose(g[e], p[order, e], rtol=1e-14)
+
+
+def test_combine_vs_direct_sum():
+    r = rng(14)
+    T, d, K, R = 30, 12, 3, 70
+    yp = r.standard_normal((R, d)).astype(np.float32)
+    w = r.uniform(0, 1, (T, K))
+    dest = r.integers(-1, R, size=(T * K,)).astype(np.int32)
+    sh = r.standard_normal((T, d)).astype(np.float32)
+    x = r.standard_normal((T, d)).astype(np.float32)
+    L = oracle.layer(T, d, 4, 8, K, residual=True)
+    got = oracle.combine(L, yp, w, dest, sh, x)
+    want = sh.astype(np.float64) + x
+    for t in range(T):
+        for k in range(K):
+            if dest[t * K + k] >= 0:
+                want[t] += w[t, k] * yp[dest[t * K + k]].astype(np.float64)
+    np.testing.assert_allclose(got, want, rtol=1e-14, atol=1e-14)
+    L0 = oracle.layer(T, d, 4, 8, K)
+    assert np.all(oracle.combine(L0, yp, w, np.full(T * K, -1, np.int32)) == 0)

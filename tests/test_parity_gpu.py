@@ -1,0 +1,218 @@
+"""GPU parity: the HIP library (through the C-ABI) against the CPU oracle on
+the same seeded inputs.
+
+Three paths per case, each checked end to end:
+  free      the library computes its own logits; logits within the fp32
+            forward-error bound, indices equal except near-ties (counted),
+            weights, permutation and outputs checked when no choice flipped;
+  logits_in both sides route the oracle's fp32 logits: indices, counts,
+            offsets, dest, row_src and drop mask bit-exact, outputs within
+            tolerance;
+  topk_in   both sides use the oracle's Top-K choice: permutation bit-exact,
+            outputs within tolerance.
+Small cases (several tiles and a ragged tail) compare every output; the five
+full-size workloads compare routing over all tokens and outputs on a sample of
+tokens the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+import oracle
+import mixture_experts_sparse_route_amd as moe
+from moe_synth import workload
+from parity_lib import (NEAR_TIE, Case, assert_permutation_equal, assert_weights_close, assert_y_close, dev,
+                        host_f64, kept_tokens, routing_host, spec_of)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU parity tests need a GPU"
+    moe.load_library()
+    moe_synth.build(force=False)
+    oracle.build(force=False)
+
+
+def sample_tokens(case: Case, n=24, seed=0):
+    T = case.wl.T
+    r = np.random.default_rng(seed)
+    picks = {0, T - 1} | set(r.choice(T, size=min(n, T), replace=False).tolist())
+    orc = case.oracle_route()
+    if case.wl.capacity_factor > 0:
+        dropped = np.nonzero(orc["dropped"].reshape(T, -1).all(1))[0]
+        picks |= set(dropped[:4].tolist()) | set(dropped[-4:].tolist())
+    return np.array(sorted(picks), dtype=np.int64)
+
+
+def check_case(case: Case, tokens=None, residual=False):
+    wl = case.wl
+    T, K = wl.T, wl.K
+    orc = case.oracle_route()
+    rows = np.arange(T) if tokens is None else tokens
+    y_ref = case.oracle_y(orc["idx"], orc["w"], orc["dest"], tokens=rows, residual=residual)
+    live = kept_tokens(orc["dest"], K, wl.n_shared)[rows]
+    dead = ~live
+    report = {}
+
+    # ---- free-running path (fp32 output; for a bf16 layer the bf16 output is
+    # checked to be exactly its round-to-nearest-even image)
+    y, r = case.gpu_forward(residual=residual, out_dtype="f32")
+    g = routing_host(r)
+    if wl.dtype == "bf16":
+        yb, _ = case.gpu_forward(residual=residual, out_dtype="bf16")
+        assert torch.equal(yb.view(torch.int16), y.to(torch.bfloat16).view(torch.int16)), \
+            "bf16 output is not the rounded fp32 output"
+    bound = (wl.d + 2) * 2.0 ** -24 * case.logit_bound() + 2.0 ** -24 * np.abs(orc["logits"])
+    if case.h["logit_bias"] is not None:
+        bound += 2.0 ** -24 * np.abs(case.h["logit_bias"])[None, :]
+    lerr = np.abs(g["logits"].astype(np.float64) - orc["logits"])
+    assert np.all(lerr <= bound), f"logits outside the forward-error bound: {np.max(lerr / bound):.3g}x"
+    near = orc["gap"] < NEAR_TIE
+    flip = (g["idx"] != orc["idx"]).any(1)
+    assert not np.any(flip & ~near), f"{int(np.sum(flip & ~near))} tokens changed experts without a near-tie"
+    report["near_ties"] = int(near.sum())
+    report["flips"] = int(flip.sum())
+    if not flip.any():
+        assert_weights_close(g["w"], orc["w"], "free")
+        assert_permutation_equal(g, orc, "free")
+        yg = host_f64(y)[rows]
+        report["err_free"] = assert_y_close(yg, y_ref, wl.dtype, rows=live, label="free")
+        if dead.any():
+            xf = case.h["x"] if wl.dtype == "f32" else moe_synth.bf16_to_f32(case.h["x"])
+            want = xf.astype(np.float64)[rows][dead] if residual else 0.0
+            assert np.array_equal(yg[dead], np.broadcast_to(want, yg[dead].shape)), "dropped rows are not pass-through"
+
+    # ---- logits_in: identical fp32 logits on both sides
+    y2, r2 = case.gpu_forward(residual=residual, logits_in=orc["logits"], out_dtype="f32")
+    g2 = routing_host(r2)
+    assert np.array_equal(g2["idx"], orc["idx"]), \
+        f"indices differ given identical logits on {int((g2['idx'] != orc['idx']).any(1).sum())} tokens"
+    assert_weights_close(g2["w"], orc["w"], "logits_in")
+    assert_permutation_equal(g2, orc, "logits_in")
+    yg2 = host_f64(y2)[rows]
+    report["err_logits_in"] = assert_y_close(yg2, y_ref, wl.dtype, rows=live, label="logits_in")
+
+    # ---- topk_in: identical Top-K choice on both sides
+    y3, r3 = case.gpu_forward(residual=residual, topk_in=(orc["idx"], orc["w"].astype(np.float32)),
+                              out_dtype="f32")
+    g3 = routing_host(r3)
+    assert_permutation_equal(g3, orc, "topk_in")
+    report["err_topk_in"] = assert_y_close(host_f64(y3)[rows], y_ref, wl.dtype, rows=live, label="topk_in")
+    return report
+
+
+# ------------------------------------------------------------ small cases --
+
+SMALL = {
+    "tiny_top2_fp32": workload("tiny_top2_fp32"),
+    "switch_capacity_small": workload("switch_top1_capacity", T=1000, d=256, F=512, E=16),
+    "mixtral_small": workload("mixtral_prefill", T=300, d=512, F=1024),
+    "mixtral_two_mtiles": workload("mixtral_prefill", T=1100, d=256, F=384),
+    "deepseek_small": workload("deepseek_v3_fine", T=200, d=512, F=256, E=64, Fs=256),
+    "decode_small": workload("mixtral_decode", T=5, d=512, F=1024),
+    "dense_k_equals_e": workload("mixtral_prefill", T=100, d=128, F=128, E=4, K=4, renorm=False),
+    "fp32_ragged": workload("tiny_top2_fp32", T=50, d=100, F=37, E=5),
+    "single_expert": workload("mixtral_prefill", T=77, d=128, F=128, E=1, K=1),
+    "sigmoid_unnormalised": workload("deepseek_v3_fine", T=64, d=256, F=128, E=32, K=4, renorm=False, n_shared=0,
+                                     Fs=0),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_case(name):
+    rep = check_case(Case(SMALL[name]))
+    print(name, rep)
+
+
+def test_residual_pass_through_with_capacity():
+    rep = check_case(Case(SMALL["switch_capacity_small"]), residual=True)
+    print(rep)
+
+
+def test_everything_dropped():
+    # floor(1.0 * 10 / 64) = 0: every assignment overflows
+    wl = workload("switch_top1_capacity", T=10, d=128, F=128, E=64, capacity_factor=1.0)
+    case = Case(wl)
+    y, r = case.gpu_forward()
+    assert torch.all(y == 0)
+    assert int(r.offsets[-1]) == 0 and torch.all(r.dropped == 1) and torch.all(r.dest == -1)
+    y2, _ = case.gpu_forward(residual=True)
+    assert torch.equal(y2.view(torch.int16), case.d["x"].view(torch.int16))
+
+
+def test_single_token():
+    rep = check_case(Case(workload("deepseek_v3_fine", T=1, d=256, F=128, E=16, K=3, Fs=128)))
+    print(rep)
+
+
+def test_run_twice_bitwise_identical():
+    case = Case(SMALL["deepseek_small"])
+    y1, r1 = case.gpu_forward()
+    y2, r2 = case.gpu_forward()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(r1.topk_idx, r2.topk_idx) and torch.equal(r1.topk_w, r2.topk_w)
+
+
+def test_entry_points_in_isolation():
+    """moe_route, moe_dispatch, moe_expert_ffn and moe_combine called one by
+    one, each checked against the oracle's version of that step."""
+    wl = SMALL["mixtral_two_mtiles"]
+    case = Case(wl)
+    orc = case.oracle_route()
+    spec = spec_of(wl)
+    ws, _ = moe.alloc_workspace(spec)
+    r = moe.Routing(spec)
+    moe.moe_route(spec, case.d["x"], case.d["Wg"], None, None, r, ws)
+    torch.cuda.synchronize()
+    g = routing_host(r)
+    assert np.array_equal(g["idx"], orc["idx"])
+    assert_permutation_equal(g, orc, "moe_route")
+
+    R = int(orc["offsets"][-1])
+    mr = moe.max_rows(spec)
+    xp = torch.empty((mr, wl.d), dtype=torch.bfloat16, device="cuda")
+    moe.moe_dispatch(spec, case.d["x"], r, xp)
+    torch.cuda.synchronize()
+    xp_h = xp[:R].view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(xp_h, case.h["x"][orc["row_src"][:R] // wl.K])
+
+    yp = torch.empty((mr, wl.d), dtype=torch.float32, device="cuda")
+    moe.moe_expert_ffn(spec, xp, r.offsets, wl.E, mr, case.d["W1"], case.d["W3"], case.d["W2"], yp, ws)
+    torch.cuda.synchronize()
+    yp_h = yp[:R].cpu().numpy().astype(np.float64)
+    xrows = moe_synth.bf16_to_f32(case.h["x"][orc["row_src"][:R] // wl.K]).astype(np.float64)
+    grp = np.searchsorted(orc["offsets"], np.arange(R), side="right") - 1
+    pick = np.unique(np.concatenate([np.arange(0, R, 37), [R - 1], orc["offsets"][1:-1] - 1]))
+    ref = np.stack([oracle.swiglu(case.h["W1"][grp[i]], case.h["W3"][grp[i]], case.h["W2"][grp[i]], xrows[i],
+                                  bf16=True, threads=4) for i in pick])
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert np.max(np.abs(yp_h[pick] - ref)) <= 2e-2 * rms
+
+    # combine on the oracle's routing with seeded expert rows (fp32 output)
+    ypr = moe_synth.normal(0, 99, (R, wl.d), 1.0, "f32")
+    y = torch.empty((wl.T, wl.d), dtype=torch.float32, device="cuda")
+    rr = moe.Routing(spec)
+    rr.topk_w.copy_(torch.from_numpy(orc["w"].astype(np.float32)))
+    rr.dest.copy_(torch.from_numpy(orc["dest"]))
+    moe.moe_combine(spec_of(wl, out_dtype="f32"), dev(ypr), rr, None, None, y)
+    torch.cuda.synchronize()
+    ref_c = oracle.combine(oracle.layer_of(wl), ypr, orc["w"].astype(np.float32).astype(np.float64), orc["dest"])
+    # fp32 accumulation of K terms in the same order: a few fp32 ulps
+    assert np.max(np.abs(host_f64(y) - ref_c) / np.maximum(np.abs(ref_c), np.sqrt(np.mean(ref_c ** 2)))) <= 1e-5
+
+
+# -------------------------------------------------------- full-size cases --
+
+FULL = ["tiny_top2_fp32", "switch_top1_capacity", "mixtral_prefill", "mixtral_decode", "deepseek_v3_fine"]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", FULL)
+def test_full_size(name):
+    case = Case(workload(name))
+    toks = None if case.wl.T <= 64 else sample_tokens(case)
+    rep = check_case(case, tokens=toks)
+    print(name, "sampled" if toks is not None else "all", rep)
