@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark of one sparse-MoE FFN layer forward on one MI355X.
+
+A step is one whole-layer forward (router logits, gate, Top-K, histogram /
+capacity / permutation, dispatch, grouped SwiGLU experts, combine) through
+``moe_forward`` of the C-ABI library, on seeded synthetic inputs already
+resident in HBM.  Default workload: Switch-style top-1 with capacity factor
+1.25 (T=8192, d_model=1024, 64 experts, d_ff=4096, bf16, fp32 router).
+
+Prints one JSON line: tokens/s, the dominant kernel's roofline position
+(measured with HIP events on the launch stream inside the timed region), and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/sec; achieved MFMA TFLOP/s (prefill) and HBM GB/s (decode)"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3     # MI355X fp32
+RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+DEFAULT_WORKLOAD = "switch_top1_capacity"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown", action="store_true", help="also time every kernel in an untimed extra pass")
+    return ap.parse_args()
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def kernel_accounting(wl, R: int, touched: int):
+    """Algorithmic flops and bytes per launch of each kernel of one step.
+
+    gemm_gate_up: reads W1, W3 of every touched expert once, the R dispatched
+    rows, writes h; 4 d F flops per row.  gemm_down: reads W2 of every touched
+    expert, h; writes fp32 rows; 2 d F flops per row.  The shared expert, when
+    present, is one more launch of each with T rows.
+    """
+    esz = 2 if wl.dtype == "bf16" else 4
+    d, F = wl.d, wl.F
+    acc = {
+        "gemm_gate_up": dict(flops=4.0 * d * F * R, bytes=touched * 2.0 * F * d * esz + R * d * esz + R * F * esz),
+        "gemm_down": dict(flops=2.0 * d * F * R, bytes=touched * 1.0 * F * d * esz + R * F * esz + R * d * 4.0),
+    }
+    if wl.n_shared:
+        Fs, T = wl.Fs, wl.T
+        acc["gemm_gate_up"]["flops_shared"] = 4.0 * d * Fs * T
+        acc["gemm_gate_up"]["bytes_shared"] = 2.0 * Fs * d * esz + T * d * esz + T * Fs * esz
+        acc["gemm_down"]["flops_shared"] = 2.0 * d * Fs * T
+        acc["gemm_down"]["bytes_shared"] = 1.0 * Fs * d * esz + T * Fs * esz + T * d * 4.0
+    layer_flops = 6.0 * d * F * R + 2.0 * wl.T * d * wl.E + (6.0 * d * wl.Fs * wl.T if wl.n_shared else 0.0)
+    layer_bytes = (touched * 3.0 * F * d * esz + (3.0 * wl.Fs * d * esz if wl.n_shared else 0.0)
+                   + 2.0 * wl.T * d * esz + wl.E * d * 4.0)
+    return acc, layer_flops, layer_bytes
+
+
+def cpu_baseline(wl, h, budget_s: float):
+    """The oracle as it stands on a bounded sample: routing of all T tokens
+    (capacity needs every token), then tokens in blocks of 64 through the
+    experts and combine until the budget is spent; the whole-layer time is
+    extrapolated from the per-token rate."""
+    import numpy as np
+    import oracle
+
+    oracle.build(force=False)
+    L = oracle.layer_of(wl)
+    t0 = time.perf_counter()
+    rt = oracle.route(L, h["x"], h["Wg"], h["logit_bias"], h["sel_bias"])
+    t_route = time.perf_counter() - t0
+    done = 0
+    t_rows = 0.0
+    while done < wl.T and t_rows < budget_s:
+        toks = np.arange(done, min(wl.T, done + 64), dtype=np.int64)
+        t1 = time.perf_counter()
+        oracle.forward_rows(L, h["x"], rt["idx"], rt["w"], rt["dest"], h["W1"], h["W3"], h["W2"], h["Ws1"],
+                            h["Ws3"], h["Ws2"], tokens=toks)
+        t_rows += time.perf_counter() - t1
+        done += len(toks)
+    t_layer = t_route + t_rows * wl.T / done
+    return {"value": wl.T / t_layer, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"routing of all {wl.T} tokens ({t_route:.2f} s) + experts and combine for the first "
+                      f"{done} tokens ({t_rows:.2f} s), extrapolated to {wl.T} tokens",
+            "seconds_measured": round(t_route + t_rows, 2)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "expert parallelism across GPUs is not part of it.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_sparse_route_amd as moe
+    from moe_synth import workload
+
+    wl = workload(args.workload)
+    lib = moe.load_library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    t_gen = time.perf_counter()
+    h = wl.gen_all()
+
+    def dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    d = {k: dev(v) for k, v in h.items()}
+    t_gen = time.perf_counter() - t_gen
+    spec = moe.LayerSpec(tokens=wl.T, d_model=wl.d, d_ff=wl.F, n_experts=wl.E, top_k=wl.K, gate=wl.gate,
+                         renorm=wl.renorm, capacity_factor=wl.capacity_factor, n_shared=wl.n_shared,
+                         d_ff_shared=wl.Fs, dtype=wl.dtype)
+    ws, _ = moe.alloc_workspace(spec)
+    r = moe.Routing(spec)
+    y = torch.empty((wl.T, wl.d), dtype=torch.bfloat16 if wl.dtype == "bf16" else torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        moe.moe_forward(spec, d["x"], d["Wg"], d["logit_bias"], d["sel_bias"], d["W1"], d["W3"], d["W2"], d["Ws1"],
+                        d["Ws3"], d["Ws2"], y, r, ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` steps; the dominant kernel is bracketed
+    # by HIP events on the launch stream
+    dominant = "gemm_gate_up"
+    moe.profile_enable([])
+    moe.profile_reset()
+    moe.profile_enable([dominant])
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    moe.profile_enable([])
+    prof = moe.profile_read()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    dom_ms, dom_n = prof[dominant]
+    dom_avg_ms = dom_ms / max(dom_n, 1)
+
+    breakdown = None
+    if args.breakdown:
+        moe.profile_reset()
+        moe.profile_enable(None)
+        for _ in range(5):
+            step()
+        torch.cuda.synchronize()
+        moe.profile_enable([])
+        breakdown = {k: round(v[0] / v[1] * 1000.0, 2) for k, v in moe.profile_read().items() if v[1]}
+
+    offsets = r.offsets.cpu().numpy()
+    R = int(offsets[-1])
+    touched = int(np.count_nonzero(np.diff(offsets)))
+    acc, layer_flops, layer_bytes = kernel_accounting(wl, R, touched)
+    a = acc[dominant]
+    n_dom_per_step = dom_n / args.steps  # routed (+ shared) launches per step
+    dom_bytes = a["bytes"] + (a.get("bytes_shared", 0.0) if n_dom_per_step > 1 else 0.0)
+    dom_flops = a["flops"] + (a.get("flops_shared", 0.0) if n_dom_per_step > 1 else 0.0)
+    # bytes and flops per launch (routed and shared launches averaged)
+    per_launch_bytes = dom_bytes / n_dom_per_step
+    per_launch_flops = dom_flops / n_dom_per_step
+    intensity = per_launch_flops / per_launch_bytes
+    if intensity < RIDGE:
+        achieved = per_launch_bytes / (dom_avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = per_launch_flops / (dom_avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+    roof["kernel"] = dominant
+    roof["avg_launch_ms"] = round(dom_avg_ms, 4)
+    roof["algorithmic_bytes_per_launch"] = per_launch_bytes
+    roof["algorithmic_flops_per_launch"] = per_launch_flops
+    # HBM traffic from rocprofv3 counters, valid only for the kernel source it was taken on
+    roof["traffic"] = None
+    tpath = os.path.join(ROOT, "profiles", f"traffic_{dominant}_{wl.name}.json")
+    if os.path.exists(tpath):
+        t = json.load(open(tpath))
+        src = os.path.join(ROOT, "mixture_experts_sparse_route_amd", "csrc", "gemm_bf16.hip")
+        if t.get("source_sha256_16") == source_hash(src):
+            roof["traffic"] = t["bytes_per_launch"]
+
+    line = {
+        "metric": METRIC,
+        "value": round(wl.T / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": wl.T, "d_model": wl.d, "d_ff": wl.F, "n_experts": wl.E,
+                   "top_k": wl.K, "gate": "sigmoid" if wl.gate else "softmax", "renorm": wl.renorm,
+                   "capacity_factor": wl.capacity_factor, "n_shared": wl.n_shared, "d_ff_shared": wl.Fs,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "layer": {"tflops": round(layer_flops / (ms_per_step * 1e-3) / 1e12, 2),
+                  "algorithmic_gbps": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+                  "mfma_frac": round(layer_flops / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                  "hbm_frac": round(layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "kept_rows": R, "touched_experts": touched, "host_wall_s": round(wall, 3)},
+    }
+    if breakdown:
+        line["kernels_us"] = breakdown
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, h, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    del lib
+
+
+if __name__ == "__main__":
+    main()

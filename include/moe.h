@@ -192,12 +192,13 @@ const char* moe_status_string(moe_status s);
 const char* moe_last_error(void);
 
 /* ---- Per-kernel timing (diagnostics) --------------------------------------
- * When enabled, every kernel the library launches is bracketed by a pair of
- * HIP events recorded on the launch stream.  moe_profile_read synchronises
- * on the recorded events and returns, per kernel id, the summed duration in
- * milliseconds and the launch count since the last reset.  Not thread-safe
- * across concurrent callers; intended for benchmarks. */
-moe_status moe_profile_enable(int enable);
+ * When enabled for a kernel (bit `kernel_id` of `kernel_mask`), every launch
+ * of that kernel is bracketed by a pair of HIP events recorded on the launch
+ * stream.  moe_profile_read synchronises on the recorded events and returns
+ * the summed duration in milliseconds and the launch count since the last
+ * reset.  kernel_mask = 0 turns timing off.  Not thread-safe across
+ * concurrent callers; intended for benchmarks. */
+moe_status moe_profile_enable(uint32_t kernel_mask);
 moe_status moe_profile_reset(void);
 moe_status moe_profile_read(int kernel_id, double* total_ms, int64_t* launches);
 /* Name of kernel id `kernel_id` (NULL past the last id). */

@@ -70,7 +70,7 @@ def load_library(path: str = LIB_PATH):
         "moe_expert_ffn": [C, vp, vp, i64, i64, vp, vp, vp, vp, vp, sz, vp],
         "moe_combine": [C, vp, R, vp, vp, vp, vp],
         "moe_forward": [C, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, R, vp, sz, vp],
-        "moe_profile_enable": [i32],
+        "moe_profile_enable": [ctypes.c_uint32],
         "moe_profile_reset": [],
         "moe_profile_read": [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)],
     }
@@ -242,8 +242,15 @@ def moe_forward(spec, x, Wg, logit_bias, sel_bias, W1, W3, W2, Ws1, Ws3, Ws2, y,
 
 # ---------------------------------------------------------------- profiling --
 
-def profile_enable(on: bool = True):
-    _check(load_library().moe_profile_enable(1 if on else 0), "moe_profile_enable")
+def profile_enable(kernels=None):
+    """Time the named kernels (all if None; [] turns timing off)."""
+    if kernels is None:
+        mask = (1 << len(KERNEL_NAMES)) - 1
+    else:
+        mask = 0
+        for k in kernels:
+            mask |= 1 << KERNEL_NAMES.index(k)
+    _check(load_library().moe_profile_enable(mask), "moe_profile_enable")
 
 
 def profile_reset():

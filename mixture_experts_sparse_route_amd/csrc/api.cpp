@@ -206,7 +206,7 @@ struct ProfRec {
   int id;
   hipEvent_t a, b;
 };
-bool g_prof = false;
+uint32_t g_prof = 0;  // bit k: time kernel id k
 std::mutex g_prof_mu;
 std::vector<ProfRec> g_recs;
 std::vector<hipEvent_t> g_pool;
@@ -247,15 +247,14 @@ const char* const kNames[K_COUNT] = {"router_logits", "router_topk", "route_scan
 const char* kernel_name(int id) { return (id >= 0 && id < K_COUNT) ? kNames[id] : nullptr; }
 
 void prof_begin(int id, hipStream_t s) {
-  (void)id;
-  if (!g_prof) return;
+  if (!(g_prof >> id & 1u)) return;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_open = get_event();
   if (g_open) (void)hipEventRecord(g_open, s);
 }
 
 void prof_end(int id, hipStream_t s) {
-  if (!g_prof) return;
+  if (!(g_prof >> id & 1u)) return;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   if (!g_open) return;
   hipEvent_t b = get_event();
@@ -416,9 +415,9 @@ const char* moe_status_string(moe_status s) {
 
 const char* moe_last_error(void) { return g_err.c_str(); }
 
-moe_status moe_profile_enable(int enable) {
+moe_status moe_profile_enable(uint32_t kernel_mask) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  g_prof = enable != 0;
+  g_prof = kernel_mask;
   return MOE_OK;
 }
 

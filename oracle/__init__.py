@@ -58,6 +58,8 @@ def _load():
         lib.orc_swiglu.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp, i32]
         lib.orc_forward_rows.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]
         lib.orc_expert_choice.argtypes = [P, vp, i64, vp, vp]
+        lib.orc_threads.argtypes = []
+        lib.orc_threads.restype = i32
         lib.orc_combine.argtypes = [P, vp, vp, vp, vp, vp, vp]
         lib.orc_combine.restype = None
         for fn in (lib.orc_logits, lib.orc_select, lib.orc_permute, lib.orc_swiglu, lib.orc_forward_rows,
@@ -84,6 +86,11 @@ def layer_of(wl, residual=False) -> OrcLayer:
     """OrcLayer for a ``moe_synth`` workload."""
     return layer(wl.T, wl.d, wl.F, wl.E, wl.K, gate=wl.gate, renorm=wl.renorm, residual=residual,
                  bf16=(wl.dtype == "bf16"), capacity_factor=wl.capacity_factor, n_shared=wl.n_shared, Fs=wl.Fs)
+
+
+def threads() -> int:
+    """OpenMP threads the oracle uses."""
+    return int(_load().orc_threads())
 
 
 def logits(L: OrcLayer, x, Wg, logit_bias=None) -> np.ndarray:

@@ -279,3 +279,11 @@ void orc_expert_choice(const orc_layer* L, const float* logits, int64_t cap, int
     free(order);
   }
 }
+
+int32_t orc_threads(void) {
+#ifdef _OPENMP
+  return (int32_t)omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

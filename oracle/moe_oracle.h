@@ -115,6 +115,9 @@ void orc_combine(const orc_layer* L, const float* yp, const double* w, const int
  * used).  Requires cap <= T. */
 void orc_expert_choice(const orc_layer* L, const float* logits, int64_t cap, int32_t* tok, double* g);
 
+/* Number of OpenMP threads the oracle's parallel loops use. */
+int32_t orc_threads(void);
+
 #ifdef __cplusplus
 }
 #endif
