@@ -109,7 +109,7 @@ moe_status validate(const moe_config* c, Shape* sh) {
 
 // ---- workspace layout ----
 struct Layout {
-  size_t blk_count, blk_base, gtile_up, gtile_down, sh_range, sh_gtile_up, sh_gtile_down;
+  size_t router_part, blk_count, blk_base, gtile_up, gtile_down, sh_range, sh_gtile_up, sh_gtile_down;
   size_t h, xp, yp, sh_h, sh_out;
   size_t r_logits, r_idx, r_w, r_counts, r_offsets, r_dest, r_row_src, r_dropped;
   size_t total;
@@ -124,6 +124,8 @@ Layout layout(const Shape& s) {
     return at;
   };
   const size_t TK = (size_t)(s.T * s.K);
+  const int S = router_splits(s.T, s.d, s.E, s.bf16);
+  L.router_part = take(S > 1 ? (size_t)S * s.T * s.E * 4 : 0);
   L.blk_count = take((size_t)(s.n_chunks * s.E) * 4);
   L.blk_base = take((size_t)(s.n_chunks * s.E) * 4);
   L.gtile_up = take((size_t)(s.E + 1) * 4);
@@ -176,14 +178,19 @@ moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const 
   int32_t* blk_count = at<int32_t>(ws, L.blk_count);
   int32_t* blk_base = at<int32_t>(ws, L.blk_base);
   const bool topk_in = c->flags & MOE_F_TOPK_IN;
+  const float* sb = c->gate == MOE_GATE_SIGMOID ? sel_bias : nullptr;
   if (!topk_in) {
-    if (!(c->flags & MOE_F_LOGITS_IN))
-      MOE_HIP(launch_router_logits(s.bf16, x, Wg, logit_bias, r.logits, s.T, s.d, s.E, st));
-    MOE_HIP(launch_router_topk(r.logits, c->gate == MOE_GATE_SIGMOID ? sel_bias : nullptr, r.topk_idx, r.topk_w,
-                               blk_count, s.T, s.E, s.K, c->gate, c->flags & MOE_F_RENORM, false, st));
+    int S = 1;
+    float* part = at<float>(ws, L.router_part);
+    if (!(c->flags & MOE_F_LOGITS_IN)) {
+      S = router_splits(s.T, s.d, s.E, s.bf16);
+      MOE_HIP(launch_router_logits(s.bf16, x, Wg, logit_bias, r.logits, part, s.T, s.d, s.E, st));
+    }
+    MOE_HIP(launch_router_topk(r.logits, part, S, logit_bias, sb, r.topk_idx, r.topk_w, blk_count, s.T, s.E, s.K,
+                               c->gate, c->flags & MOE_F_RENORM, false, st));
   } else {
-    MOE_HIP(launch_router_topk(nullptr, nullptr, r.topk_idx, nullptr, blk_count, s.T, s.E, s.K, c->gate, false, true,
-                               st));
+    MOE_HIP(launch_router_topk(nullptr, nullptr, 1, nullptr, nullptr, r.topk_idx, nullptr, blk_count, s.T, s.E, s.K,
+                               c->gate, false, true, st));
   }
   MOE_HIP(launch_route_scan(blk_count, blk_base, r.counts, r.offsets, s.n_chunks, s.E, s.cap, st));
   MOE_HIP(launch_route_scatter(r.topk_idx, blk_base, r.offsets, r.dest, r.row_src, r.dropped, s.T, s.K, s.E, s.cap,

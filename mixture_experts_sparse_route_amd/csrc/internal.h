@@ -29,11 +29,17 @@ void prof_end(int id, hipStream_t s);
 constexpr int kTopkTokens = 32;
 
 // ---- router (a1-a3) ----
-hipError_t launch_router_logits(bool bf16, const void* x, const float* Wg, const float* bias, float* logits, int64_t T,
-                                int64_t d, int64_t E, hipStream_t s);
+// Number of d-slices the logits GEMM is cut into (1 = logits written directly).
+int router_splits(int64_t T, int64_t d, int64_t E, bool bf16);
+// part: [S, T, E] fp32 partial sums (unused when S == 1).
+hipError_t launch_router_logits(bool bf16, const void* x, const float* Wg, const float* bias, float* logits,
+                                float* part, int64_t T, int64_t d, int64_t E, hipStream_t s);
+// S > 1: logits = sum of the S slices of `part` (in order) + bias, written to
+// `logits` before selection; S == 1: `logits` is read as is.
 // topk_in: idx is an input; only the per-chunk histogram is produced.
-hipError_t launch_router_topk(const float* logits, const float* sel_bias, int32_t* idx, float* w, int32_t* blk_count,
-                              int64_t T, int64_t E, int64_t K, int gate, bool renorm, bool topk_in, hipStream_t s);
+hipError_t launch_router_topk(float* logits, const float* part, int S, const float* bias, const float* sel_bias,
+                              int32_t* idx, float* w, int32_t* blk_count, int64_t T, int64_t E, int64_t K, int gate,
+                              bool renorm, bool topk_in, hipStream_t s);
 
 // ---- permutation (a4) and dispatch (a5) ----
 hipError_t launch_route_scan(const int32_t* blk_count, int32_t* blk_base, int32_t* counts, int32_t* offsets,

@@ -11,45 +11,173 @@ namespace moe {
 namespace {
 
 // ---------------------------------------------------------------- a1 logits
-// logits[t][e] = sum_i x[t][i] * Wg[e][i] (+ bias[e]); fp32 FMA in ascending i.
-// 64 tokens x 64 experts per workgroup, k-tiles of 32 staged through LDS.
-constexpr int LG_T = 64, LG_E = 64, LG_K = 32;
+// logits[t][e] = sum_i x[t][i] * Wg[e][i] (+ bias[e]).
+//
+// bf16 x: bf16 MFMA.  Each fp32 router weight is split exactly into three
+// bf16 parts, w = hi + mid + lo (hi = bf16(w), mid = bf16(w - hi),
+// lo = w - hi - mid, each difference exact in fp32), so every product
+// x * part is exact in fp32 and the fp32 MFMA accumulation gives an fp32 dot
+// product of the unrounded operands.  Work is cut into 64-token x EW-expert
+// tiles and S slices of d; slice s writes its partial sums to part[s] and the
+// Top-K kernel adds the S slices in order.  With S == 1 the tile writes the
+// logits (plus bias) directly.
+// fp32 x: the same tiling with fp32 FMA.
+constexpr int LG_T = 64, LG_K = 32;
 
-template <typename XT>
-__global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict__ x, const float* __restrict__ Wg,
-                                                            const float* __restrict__ bias, float* __restrict__ logits,
-                                                            int T, int d, int E) {
+__device__ __forceinline__ int lg_pos(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
+
+__device__ __forceinline__ void split3(float w, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+  hi = f32_to_bf16(w);
+  const float r1 = w - bf16_to_f32(hi);
+  mid = f32_to_bf16(r1);
+  const float r2 = r1 - bf16_to_f32(mid);
+  lo = f32_to_bf16(r2);
+}
+
+template <int EW>
+__global__ __launch_bounds__(256) void router_logits_mfma_kernel(const uint16_t* __restrict__ x,
+                                                                 const float* __restrict__ Wg,
+                                                                 const float* __restrict__ bias, float* __restrict__ out,
+                                                                 int T, int d, int E, int S) {
+  constexpr int WE = EW == 64 ? 2 : 1;     // waves along experts
+  constexpr int WT = 4 / WE;               // waves along tokens
+  constexpr int TB = LG_T / WT / 16;       // 16-token blocks per wave
+  constexpr int EB = EW / WE / 16;         // 16-expert blocks per wave
+  __shared__ __attribute__((aligned(16))) char xs[2][LG_T * 64];
+  __shared__ __attribute__((aligned(16))) char ws[2][3][EW * 64];
+
+  const int ne = (E + EW - 1) / EW, nt = (T + LG_T - 1) / LG_T;
+  const int b = blockIdx.x;
+  const int s = b / (ne * nt);
+  const int et = (b / nt) % ne, tt = b % nt;
+  const int t0 = tt * LG_T, e0 = et * EW;
+  const int kr = d / S, kbeg = s * kr;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+
+  // staging: one 16-byte chunk of x per thread; EW*8 float4 chunks of Wg
+  const int xr = tid >> 2, xc = tid & 3;
+  const bool x_ok = t0 + xr < T;
+  const uint16_t* xsrc = x + (int64_t)(x_ok ? t0 + xr : 0) * d + kbeg + xc * 8;
+  constexpr int WL = EW * 8 / 256 > 0 ? EW * 8 / 256 : 1;  // float4 loads per thread
+  uint4 xreg;
+  float4 wreg[WL];
+  auto gload = [&](int k0) {
+    xreg = x_ok ? *(const uint4*)(xsrc + k0) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < WL; ++i) {
+      const int q = tid + 256 * i;
+      const int er = q >> 3, c4 = q & 7;
+      wreg[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (q < EW * 8 && e0 + er < E) wreg[i] = *(const float4*)(Wg + (int64_t)(e0 + er) * d + kbeg + k0 + c4 * 4);
+    }
+  };
+  auto lstore = [&](int st) {
+    *(uint4*)(xs[st] + lg_pos(xr, xc)) = xreg;
+#pragma unroll
+    for (int i = 0; i < WL; ++i) {
+      const int q = tid + 256 * i;
+      if (q >= EW * 8) continue;
+      const int er = q >> 3, c4 = q & 7;
+      const float f[4] = {wreg[i].x, wreg[i].y, wreg[i].z, wreg[i].w};
+      uint16_t hi[4], mi[4], lo[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) split3(f[u], hi[u], mi[u], lo[u]);
+      const int off = lg_pos(er, c4 >> 1) + (c4 & 1) * 8;
+      *(uint2*)(ws[st][0] + off) = make_uint2(hi[0] | (uint32_t)hi[1] << 16, hi[2] | (uint32_t)hi[3] << 16);
+      *(uint2*)(ws[st][1] + off) = make_uint2(mi[0] | (uint32_t)mi[1] << 16, mi[2] | (uint32_t)mi[3] << 16);
+      *(uint2*)(ws[st][2] + off) = make_uint2(lo[0] | (uint32_t)lo[1] << 16, lo[2] | (uint32_t)lo[3] << 16);
+    }
+  };
+
+  const int wt = wave / WE, we = wave % WE;
+  const int lr = lane & 15, lk = lane >> 4;
+  f32x4_t acc[TB][EB];
+#pragma unroll
+  for (int i = 0; i < TB; ++i)
+#pragma unroll
+    for (int j = 0; j < EB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = kr / LG_K;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * LG_K);
+    bf16x8_t af[TB];
+#pragma unroll
+    for (int i = 0; i < TB; ++i) af[i] = *(const bf16x8_t*)(xs[cur] + lg_pos((wt * TB + i) * 16 + lr, lk));
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+#pragma unroll
+      for (int j = 0; j < EB; ++j) {
+        const bf16x8_t bfr = *(const bf16x8_t*)(ws[cur][p] + lg_pos((we * EB + j) * 16 + lr, lk));
+#pragma unroll
+        for (int i = 0; i < TB; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr, acc[i][j], 0, 0, 0);
+      }
+    }
+    if (kt + 1 < nk) lstore(cur ^ 1);
+    __syncthreads();
+  }
+  // lane holds tokens (block*16 + lk*4 + v), expert (block*16 + lr)
+#pragma unroll
+  for (int i = 0; i < TB; ++i)
+#pragma unroll
+    for (int j = 0; j < EB; ++j) {
+      const int e = e0 + (we * EB + j) * 16 + lr;
+      if (e >= E) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = t0 + (wt * TB + i) * 16 + lk * 4 + v;
+        if (t >= T) continue;
+        if (S == 1)
+          out[(int64_t)t * E + e] = acc[i][j][v] + (bias ? bias[e] : 0.0f);
+        else
+          out[((int64_t)s * T + t) * E + e] = acc[i][j][v];
+      }
+    }
+}
+
+// fp32 x: 64 tokens x 64 experts per workgroup, fp32 FMA, same slices.
+__global__ __launch_bounds__(256) void router_logits_f32_kernel(const float* __restrict__ x,
+                                                                const float* __restrict__ Wg,
+                                                                const float* __restrict__ bias, float* __restrict__ out,
+                                                                int T, int d, int E, int S) {
+  constexpr int LE = 64;
   __shared__ float xs[LG_K][LG_T + 4];
-  __shared__ float ws[LG_K][LG_E + 4];
-  const int ne = (E + LG_E - 1) / LG_E;
-  const int t0 = (blockIdx.x / ne) * LG_T, e0 = (blockIdx.x % ne) * LG_E;
+  __shared__ float wsh[LG_K][LE + 4];
+  const int ne = (E + LE - 1) / LE, nt = (T + LG_T - 1) / LG_T;
+  const int b = blockIdx.x;
+  const int s = b / (ne * nt);
+  const int et = (b / nt) % ne, tt = b % nt;
+  const int t0 = tt * LG_T, e0 = et * LE;
+  const int kr = (d + S - 1) / S, kbeg = s * kr, kend = min(d, kbeg + kr);
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   float acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
-
-  for (int k0 = 0; k0 < d; k0 += LG_K) {
+  for (int k0 = kbeg; k0 < kend; k0 += LG_K) {
     for (int q = threadIdx.x; q < LG_T * LG_K; q += 256) {
       const int r = q / LG_K, c = q % LG_K;
       const int t = t0 + r, k = k0 + c;
-      xs[c][r] = (t < T && k < d) ? load_act(x, (int64_t)t * d + k) : 0.0f;
+      xs[c][r] = (t < T && k < kend) ? x[(int64_t)t * d + k] : 0.0f;
       const int e = e0 + r;
-      ws[c][r] = (e < E && k < d) ? Wg[(int64_t)e * d + k] : 0.0f;
+      wsh[c][r] = (e < E && k < kend) ? Wg[(int64_t)e * d + k] : 0.0f;
     }
     __syncthreads();
 #pragma unroll 8
     for (int c = 0; c < LG_K; ++c) {
-      float a[4], b[4];
+      float a[4], bb[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) a[i] = xs[c][ty * 4 + i];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = ws[c][tx * 4 + j];
+      for (int j = 0; j < 4; ++j) bb[j] = wsh[c][tx * 4 + j];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], bb[j], acc[i][j]);
     }
     __syncthreads();
   }
@@ -60,7 +188,11 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = e0 + tx * 4 + j;
-      if (e < E) logits[(int64_t)t * E + e] = acc[i][j] + (bias ? bias[e] : 0.0f);
+      if (e >= E) continue;
+      if (S == 1)
+        out[(int64_t)t * E + e] = acc[i][j] + (bias ? bias[e] : 0.0f);
+      else
+        out[((int64_t)s * T + t) * E + e] = acc[i][j];
     }
   }
 }
@@ -93,7 +225,8 @@ __device__ __forceinline__ float group_sum(float v, int L) {
 }
 
 template <int P>
-__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits,
+__global__ __launch_bounds__(256) void router_topk_kernel(float* __restrict__ logits, const float* __restrict__ part,
+                                                          int S, const float* __restrict__ bias,
                                                           const float* __restrict__ sel_bias, int32_t* __restrict__ idx,
                                                           float* __restrict__ w, int32_t* __restrict__ blk_count, int T,
                                                           int E, int K, int L, int gate, int renorm, int topk_in) {
@@ -124,7 +257,16 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
         pk[p] = 0;
         lv[p] = -INFINITY;
         if (valid && e < E) {
-          const float l = lt[e];
+          float l;
+          if (S > 1) {
+            // logits = the d-slices' partial sums added in slice order, then the bias
+            l = part[(int64_t)t * E + e];
+            for (int q = 1; q < S; ++q) l += part[((int64_t)q * T + t) * E + e];
+            if (bias) l += bias[e];
+            logits[(int64_t)t * E + e] = l;
+          } else {
+            l = lt[e];
+          }
           lv[p] = l;
           float key;
           if (gate == 0) {
@@ -137,8 +279,10 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
           pk[p] = pack_key(key, e);
         }
       }
-      // K rounds of group max; lane ll == k keeps choice k.
+      // K rounds of group max; lane ll == k keeps choice k and its logit,
+      // fetched from the lane that holds that expert.
       int my_e = -1;
+      float my_l = -INFINITY;
       for (int k = 0; k < K; ++k) {
         uint64_t m = 0;
 #pragma unroll
@@ -148,25 +292,34 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
 #pragma unroll
         for (int p = 0; p < P; ++p)
           if (pk[p] == m) pk[p] = 0;
-        if (ll == k) my_e = e;
+        const int pe = e >= 0 ? e / L : 0, oe = e >= 0 ? e % L : 0;
+        float v = lv[0];
+#pragma unroll
+        for (int p = 1; p < P; ++p)
+          if (p == pe) v = lv[p];
+        const float le = __shfl(v, slot * L + oe, 64);
+        if (ll == k) {
+          my_e = e;
+          my_l = le;
+        }
       }
       // weights
       float contrib = 0.0f, mine = 0.0f;
       if (gate == 0) {
         // p_e = exp(l_e - m) / sum; m = the largest logit = the first choice
-        const float top = __shfl(my_e >= 0 ? lt[my_e] : -INFINITY, slot * L, 64);
+        const float top = __shfl(my_l, slot * L, 64);
         float zs = 0.0f;
 #pragma unroll
         for (int p = 0; p < P; ++p) zs += (lv[p] == -INFINITY) ? 0.0f : expf(lv[p] - top);
         const float z_all = group_sum(zs, L);
-        if (my_e >= 0) mine = expf(lt[my_e] - top);
+        if (my_e >= 0) mine = expf(my_l - top);
         contrib = mine;
         const float z_sel = group_sum(contrib, L);
         if (valid && my_e >= 0) {
           w[(int64_t)t * K + ll] = mine / (renorm ? z_sel : z_all);
         }
       } else {
-        if (my_e >= 0) mine = (float)(1.0 / (1.0 + exp(-(double)lt[my_e])));
+        if (my_e >= 0) mine = (float)(1.0 / (1.0 + exp(-(double)my_l)));
         contrib = mine;
         const float z_sel = group_sum(contrib, L);
         if (valid && my_e >= 0) w[(int64_t)t * K + ll] = renorm ? mine / z_sel : mine;
@@ -183,28 +336,46 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
 
 }  // namespace
 
-hipError_t launch_router_logits(bool bf16, const void* x, const float* Wg, const float* bias, float* logits, int64_t T,
-                                int64_t d, int64_t E, hipStream_t s) {
-  const unsigned grid = (unsigned)(((E + LG_E - 1) / LG_E) * ((T + LG_T - 1) / LG_T));
+int router_splits(int64_t T, int64_t d, int64_t E, bool bf16) {
+  const int64_t ew = (!bf16 || E > 16) ? 64 : 16;
+  const int64_t tiles = ((T + LG_T - 1) / LG_T) * ((E + ew - 1) / ew);
+  int S = 1;
+  while (tiles * S < 512 && S < 64 && d % ((int64_t)S * 2 * LG_K) == 0) S *= 2;
+  return S;
+}
+
+hipError_t launch_router_logits(bool bf16, const void* x, const float* Wg, const float* bias, float* logits,
+                                float* part, int64_t T, int64_t d, int64_t E, hipStream_t s) {
+  const int S = router_splits(T, d, E, bf16);
+  float* out = S == 1 ? logits : part;
   prof_begin(K_ROUTER_LOGITS, s);
-  if (bf16)
-    router_logits_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)x, Wg, bias, logits, (int)T, (int)d, (int)E);
-  else
-    router_logits_kernel<float><<<grid, 256, 0, s>>>((const float*)x, Wg, bias, logits, (int)T, (int)d, (int)E);
+  if (bf16) {
+    if (E <= 16) {
+      const unsigned grid = (unsigned)(((T + LG_T - 1) / LG_T) * S);
+      router_logits_mfma_kernel<16><<<grid, 256, 0, s>>>((const uint16_t*)x, Wg, bias, out, (int)T, (int)d, (int)E, S);
+    } else {
+      const unsigned grid = (unsigned)(((T + LG_T - 1) / LG_T) * ((E + 63) / 64) * S);
+      router_logits_mfma_kernel<64><<<grid, 256, 0, s>>>((const uint16_t*)x, Wg, bias, out, (int)T, (int)d, (int)E, S);
+    }
+  } else {
+    const unsigned grid = (unsigned)(((T + LG_T - 1) / LG_T) * ((E + 63) / 64) * S);
+    router_logits_f32_kernel<<<grid, 256, 0, s>>>((const float*)x, Wg, bias, out, (int)T, (int)d, (int)E, S);
+  }
   prof_end(K_ROUTER_LOGITS, s);
   return hipGetLastError();
 }
 
-hipError_t launch_router_topk(const float* logits, const float* sel_bias, int32_t* idx, float* w, int32_t* blk_count,
-                              int64_t T, int64_t E, int64_t K, int gate, bool renorm, bool topk_in, hipStream_t s) {
+hipError_t launch_router_topk(float* logits, const float* part, int S, const float* bias, const float* sel_bias,
+                              int32_t* idx, float* w, int32_t* blk_count, int64_t T, int64_t E, int64_t K, int gate,
+                              bool renorm, bool topk_in, hipStream_t s) {
   int L = 1;
   while (L < E && L < 64) L <<= 1;
   const int P = (int)((E + L - 1) / L);
   const unsigned nb = (unsigned)((T + kTopkTokens - 1) / kTopkTokens);
   prof_begin(K_ROUTER_TOPK, s);
 #define MOE_TOPK(PP)                                                                                          \
-  router_topk_kernel<PP><<<nb, 256, 0, s>>>(logits, sel_bias, idx, w, blk_count, (int)T, (int)E, (int)K, L, gate, \
-                                            renorm ? 1 : 0, topk_in ? 1 : 0)
+  router_topk_kernel<PP><<<nb, 256, 0, s>>>(logits, part, S, bias, sel_bias, idx, w, blk_count, (int)T, (int)E,     \
+                                            (int)K, L, gate, renorm ? 1 : 0, topk_in ? 1 : 0)
   if (P <= 1)
     MOE_TOPK(1);
   else if (P <= 2)

@@ -10,8 +10,11 @@ Tolerances (one place, used by every parity test):
                output must then equal the round-to-nearest-even image of that
                result bit for bit.  (Rounding the exact result to bf16 alone
                can already cost 2e-2 x RMS when max|y| / RMS exceeds about 5.)
-  router logits: |l_gpu - l_ref| <= (d + 2) * 2^-24 * sum_i |x_i w_i| + 2^-24 |l_ref|
-               (the forward-error bound of an fp32 dot product of length d)
+  router logits: |l_gpu - l_ref| <= (3d + 2) * 2^-24 * sum_i |x_i w_i| + 2^-24 |l_ref|
+               (the forward-error bound of an fp32 sum of 3d exact products:
+               the bf16 path splits each fp32 router weight into three bf16
+               parts), and the RMS of (l_gpu - l_ref) / sum_i |x_i w_i| below
+               4 * sqrt(3d) * 2^-24, which a dropped or misplaced term breaks
   Top-K weights: |w_gpu - w_ref| <= 1e-5 * |w_ref| + 1e-6
   Integer routing (indices, counts, offsets, dest, row_src, drop mask): exact.
 A token whose K-th / (K+1)-th key gap is below 1e-4 is a near-tie: its choice

@@ -65,11 +65,15 @@ def check_case(case: Case, tokens=None, residual=False):
         yb, _ = case.gpu_forward(residual=residual, out_dtype="bf16")
         assert torch.equal(yb.view(torch.int16), y.to(torch.bfloat16).view(torch.int16)), \
             "bf16 output is not the rounded fp32 output"
-    bound = (wl.d + 2) * 2.0 ** -24 * case.logit_bound() + 2.0 ** -24 * np.abs(orc["logits"])
+    sxw = case.logit_bound()
+    bound = (3 * wl.d + 2) * 2.0 ** -24 * sxw + 2.0 ** -24 * np.abs(orc["logits"])
     if case.h["logit_bias"] is not None:
         bound += 2.0 ** -24 * np.abs(case.h["logit_bias"])[None, :]
     lerr = np.abs(g["logits"].astype(np.float64) - orc["logits"])
     assert np.all(lerr <= bound), f"logits outside the forward-error bound: {np.max(lerr / bound):.3g}x"
+    rel_rms = float(np.sqrt(np.mean((lerr / sxw) ** 2)))
+    assert rel_rms <= 4 * np.sqrt(3 * wl.d) * 2.0 ** -24, f"logit error RMS {rel_rms:.3g} is not rounding noise"
+    report["logit_rel_rms"] = rel_rms
     near = orc["gap"] < NEAR_TIE
     flip = (g["idx"] != orc["idx"]).any(1)
     assert not np.any(flip & ~near), f"{int(np.sum(flip & ~near))} tokens changed experts without a near-tie"
