@@ -157,7 +157,8 @@ moe_status moe_dispatch(const moe_config* cfg, const void* x, const moe_routing*
  * W2:      device [n_groups, d, F] w_dtype
  * yp:      device [max_rows, d] fp32
  * The intermediate h = SiLU(.) * (.) is kept in act_dtype in the workspace.
- * max_rows: host upper bound on offsets[n_groups].  n_groups <= 65536. */
+ * max_rows: host upper bound on offsets[n_groups], at most moe_max_rows(cfg);
+ * 1 <= n_groups <= n_experts. */
 moe_status moe_expert_ffn(const moe_config* cfg, const void* xp, const int32_t* offsets, int64_t n_groups,
                           int64_t max_rows, const void* W1, const void* W3, const void* W2, float* yp, void* ws,
                           size_t ws_bytes, moe_stream_t stream);

@@ -109,7 +109,7 @@ moe_status validate(const moe_config* c, Shape* sh) {
 
 // ---- workspace layout ----
 struct Layout {
-  size_t router_part, blk_count, blk_base, gtile_up, gtile_down, sh_range, sh_gtile_up, sh_gtile_down;
+  size_t router_part, blk_count, blk_base, tab_up, tab_down, counts, sh_range, sh_tab_up, sh_tab_down, sh_counts;
   size_t h, xp, yp, sh_h, sh_out;
   size_t r_logits, r_idx, r_w, r_counts, r_offsets, r_dest, r_row_src, r_dropped;
   size_t total;
@@ -128,11 +128,13 @@ Layout layout(const Shape& s) {
   L.router_part = take(S > 1 ? (size_t)S * s.T * s.E * 4 : 0);
   L.blk_count = take((size_t)(s.n_chunks * s.E) * 4);
   L.blk_base = take((size_t)(s.n_chunks * s.E) * 4);
-  L.gtile_up = take((size_t)(s.E + 1) * 4);
-  L.gtile_down = take((size_t)(s.E + 1) * 4);
+  L.tab_up = take((size_t)ffn_table_entries(s.bf16, s.max_rows, s.E, s.F, true) * 16);
+  L.tab_down = take((size_t)ffn_table_entries(s.bf16, s.max_rows, s.E, s.d, false) * 16);
+  L.counts = take(2 * 4);
   L.sh_range = take(2 * 4);
-  L.sh_gtile_up = take(2 * 4);
-  L.sh_gtile_down = take(2 * 4);
+  L.sh_tab_up = take(s.S ? (size_t)ffn_table_entries(s.bf16, s.T, 1, s.Fs, true) * 16 : 0);
+  L.sh_tab_down = take(s.S ? (size_t)ffn_table_entries(s.bf16, s.T, 1, s.d, false) * 16 : 0);
+  L.sh_counts = take(2 * 4);
   L.h = take((size_t)s.max_rows * s.F * s.esz);
   L.xp = take((size_t)s.max_rows * s.d * s.esz);
   L.yp = take((size_t)s.max_rows * s.d * 4);
@@ -199,12 +201,12 @@ moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const 
 }
 
 moe_status do_ffn(const Shape& s, const void* A, const int32_t* offsets, int64_t n_groups, int64_t max_rows,
-                  const void* W1, const void* W3, const void* W2, void* h, float* yp, int32_t* gt_up,
-                  int32_t* gt_down, int64_t F, hipStream_t st) {
+                  const void* W1, const void* W3, const void* W2, void* h, float* yp, int4* tab_up, int4* tab_down,
+                  int32_t* counts, int64_t F, hipStream_t st) {
   const FfnPlan plan = ffn_plan(s.bf16, max_rows, n_groups);
-  MOE_HIP(launch_ffn_tiles(plan, offsets, n_groups, F, s.d, gt_up, gt_down, st));
-  MOE_HIP(launch_gemm_gate_up(s.bf16, plan, A, offsets, gt_up, n_groups, max_rows, W1, W3, h, F, s.d, st));
-  MOE_HIP(launch_gemm_down(s.bf16, plan, h, offsets, gt_down, n_groups, max_rows, W2, yp, F, s.d, st));
+  MOE_HIP(launch_ffn_tiles(plan, offsets, n_groups, F, s.d, tab_up, tab_down, counts, st));
+  MOE_HIP(launch_gemm_gate_up(s.bf16, plan, A, tab_up, counts, n_groups, max_rows, W1, W3, h, F, s.d, st));
+  MOE_HIP(launch_gemm_down(s.bf16, plan, h, tab_down, counts + 1, n_groups, max_rows, W2, yp, F, s.d, st));
   return MOE_OK;
 }
 
@@ -336,8 +338,8 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* xp, const int32_t* 
   Layout L;
   if ((st = check_ws(s, ws, ws_bytes, &L)) != MOE_OK) return st;
   if (max_rows == 0) return MOE_OK;
-  return do_ffn(s, xp, offsets, n_groups, max_rows, W1, W3, W2, at<void>(ws, L.h), yp, at<int32_t>(ws, L.gtile_up),
-                at<int32_t>(ws, L.gtile_down), s.F, (hipStream_t)stream);
+  return do_ffn(s, xp, offsets, n_groups, max_rows, W1, W3, W2, at<void>(ws, L.h), yp, at<int4>(ws, L.tab_up),
+                at<int4>(ws, L.tab_down), at<int32_t>(ws, L.counts), s.F, (hipStream_t)stream);
 }
 
 moe_status moe_combine(const moe_config* cfg, const float* yp, const moe_routing* r, const float* shared_out,
@@ -391,8 +393,8 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, co
   float* yp = at<float>(ws, L.yp);
   if (s.max_rows > 0) {
     MOE_HIP(launch_dispatch(x, rr.row_src, rr.offsets + s.E, xp, s.max_rows, s.K, s.d * (int64_t)s.esz, hs));
-    if ((st = do_ffn(s, xp, rr.offsets, s.E, s.max_rows, W1, W3, W2, at<void>(ws, L.h), yp,
-                     at<int32_t>(ws, L.gtile_up), at<int32_t>(ws, L.gtile_down), s.F, hs)) != MOE_OK)
+    if ((st = do_ffn(s, xp, rr.offsets, s.E, s.max_rows, W1, W3, W2, at<void>(ws, L.h), yp, at<int4>(ws, L.tab_up),
+                     at<int4>(ws, L.tab_down), at<int32_t>(ws, L.counts), s.F, hs)) != MOE_OK)
       return st;
   }
   float* sh_out = nullptr;
@@ -400,8 +402,8 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, co
     int32_t* range = at<int32_t>(ws, L.sh_range);
     MOE_HIP(launch_set_range(range, s.T, hs));
     sh_out = at<float>(ws, L.sh_out);
-    if ((st = do_ffn(s, x, range, 1, s.T, Ws1, Ws3, Ws2, at<void>(ws, L.sh_h), sh_out,
-                     at<int32_t>(ws, L.sh_gtile_up), at<int32_t>(ws, L.sh_gtile_down), s.Fs, hs)) != MOE_OK)
+    if ((st = do_ffn(s, x, range, 1, s.T, Ws1, Ws3, Ws2, at<void>(ws, L.sh_h), sh_out, at<int4>(ws, L.sh_tab_up),
+                     at<int4>(ws, L.sh_tab_down), at<int32_t>(ws, L.sh_counts), s.Fs, hs)) != MOE_OK)
       return st;
   }
   MOE_HIP(launch_combine(s.bf16, s.out_bf16, yp, rr.topk_w, rr.dest, sh_out, (cfg->flags & MOE_F_RESIDUAL) ? x : nullptr, y, s.T,

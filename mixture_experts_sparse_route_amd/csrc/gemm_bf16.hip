@@ -35,7 +35,7 @@ namespace {
 constexpr int BKS = 32;   // k per stage
 constexpr int RB = 64;    // LDS bytes per tile row
 constexpr int BNB = 256;  // weight rows per tile
-constexpr int NS = 4;     // LDS stages
+constexpr int LDS_BYTES = 160 * 1024;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -44,12 +44,33 @@ struct GemmArgs {
   const uint16_t* B0;      // [groups, N, Kdim]  W1 or W2
   const uint16_t* B1;      // [groups, N, Kdim]  W3 (gate_up only)
   void* C;                 // gate_up: bf16 [rows, N]; down: fp32 [rows, N]
-  const int32_t* offsets;  // [groups + 1]
-  const int32_t* gtile;    // [groups + 1]
-  int n_groups, N, Kdim;
+  const int4* tab;         // tile table {group, first row, rows, first column}
+  const int32_t* count;    // entries in tab
+  int N, Kdim;
 };
 
 __device__ __forceinline__ int lds_pos(int row, int chunk) { return row * RB + ((chunk ^ ((row >> 2) & 3)) << 4); }
+
+// s_waitcnt vmcnt(N) with N an immediate.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most min(ahead, MAXA) stages of LPS loads each are still
+// outstanding (loads complete in issue order).
+template <int LPS, int MAXA>
+__device__ __forceinline__ void vm_wait_stages(int ahead) {
+  if constexpr (MAXA > 0) {
+    if (ahead >= MAXA) {
+      vm_wait<MAXA * LPS>();
+      return;
+    }
+    vm_wait_stages<LPS, MAXA - 1>(ahead);
+  } else {
+    vm_wait<0>();
+  }
+}
 
 // Per-tile state handed from the kernel's set-up to the k-loop.
 struct TileCtx {
@@ -62,11 +83,12 @@ struct TileCtx {
 };
 
 // k-loop and epilogue for a wave that owns NBW active 16-row blocks.
-template <int BM, bool GATE_UP, int NBW>
+template <int BM, int NS, bool GATE_UP, int NBW>
 __device__ __forceinline__ void gemm_tile(const TileCtx& t) {
   constexpr int AG = BM / 16 / 4;   // A 16-row groups loaded per wave per stage
   constexpr int BG = BNB / 16 / 4;  // B 16-row groups loaded per wave per stage
   constexpr int LPS = AG + BG;      // loads per wave per stage
+  static_assert((NS - 2) * LPS <= 63, "vmcnt counts at most 63 outstanding loads");
   constexpr int STAGE = (BM + BNB) * RB;
   const int wave = t.wave, lane = t.lane;
   const int wm = wave & 1, wn = wave >> 1;
@@ -98,13 +120,7 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& t) {
 
   for (int kt = 0; kt < nk; ++kt) {
     // stage kt has landed once at most min(NS-2, nk-1-kt) later stages are outstanding
-    const int ahead = min(NS - 2, nk - 1 - kt);
-    if (ahead >= 2)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPS) : "memory");
-    else if (ahead == 1)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPS) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    vm_wait_stages<LPS, NS - 2>(nk - 1 - kt);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 
@@ -160,40 +176,30 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& t) {
   }
 }
 
-template <int BM, bool GATE_UP>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const GemmArgs p) {
+template <int BM, int NS, bool GATE_UP>
+__global__ __launch_bounds__(256, NS*(BM + BNB) * RB <= LDS_BYTES / 2 ? 2 : 1) void gemm_bf16_kernel(const GemmArgs p) {
   constexpr int MI = BM / 32;        // MFMA row blocks per M-wave
   constexpr int AG = BM / 16 / 4;
   constexpr int BG = BNB / 16 / 4;
   static_assert(AG <= 4 && BG <= 4, "TileCtx holds at most 4 source rows per wave");
   constexpr int STAGE = (BM + BNB) * RB;
+  static_assert(NS * STAGE <= LDS_BYTES, "LDS stages exceed 160 KB");
   __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
 
-  // ---- which tile
-  const int total = p.gtile[p.n_groups];
-  const int64_t L = xcd_tile(blockIdx.x, total);
+  // ---- which tile: one table entry
+  const int64_t L = xcd_tile(blockIdx.x, *p.count);
   if (L < 0) return;
-  int lo = 0, hi = p.n_groups;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (p.gtile[mid] <= L) lo = mid; else hi = mid;
-  }
-  const int g = lo;
-  const int row0 = p.offsets[g];
-  const int rows_g = p.offsets[g + 1] - row0;
-  const int mtiles = (rows_g + BM - 1) / BM;
-  const int r = (int)(L - p.gtile[g]);
-  const int nt = r / mtiles, mt = r % mtiles;
-  const int m0 = mt * BM;
+  const int4 te = p.tab[L];
+  const int g = te.x, row_first = te.y;
 
   TileCtx t;
   t.lds = lds;
-  t.rows = min(BM, rows_g - m0);
-  t.n0 = nt * (GATE_UP ? 128 : 256);
+  t.rows = te.z;
+  t.n0 = te.w;
   t.N = p.N;
   t.nk = p.Kdim / BKS;
   t.C = p.C;
-  t.out_row0 = (int64_t)row0 + m0;
+  t.out_row0 = row_first;
   t.wave = threadIdx.x >> 6;
   t.lane = threadIdx.x & 63;
   const int64_t Kd = p.Kdim;
@@ -204,7 +210,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const GemmArgs p) {
 #pragma unroll
   for (int j = 0; j < AG; ++j) {
     const int row = min((t.wave + 4 * j) * 16 + r_l, t.rows - 1);
-    t.a_src[j] = p.A + (int64_t)(row0 + m0 + row) * Kd + c_l * 8;
+    t.a_src[j] = p.A + (int64_t)(row_first + row) * Kd + c_l * 8;
   }
   const int64_t gbase = (int64_t)g * p.N * Kd;
 #pragma unroll
@@ -229,43 +235,56 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const GemmArgs p) {
   switch (nbw) {
 #define GG_CASE(n) \
   case n:          \
-    if constexpr (n <= MI) gemm_tile<BM, GATE_UP, n>(t); \
+    if constexpr (n <= MI) gemm_tile<BM, NS, GATE_UP, n>(t); \
     break;
     GG_CASE(1) GG_CASE(2) GG_CASE(3) GG_CASE(4) GG_CASE(5) GG_CASE(6) GG_CASE(7) GG_CASE(8)
 #undef GG_CASE
     default:
       // no rows in this M half: still take part in the barriers and loads
-      gemm_tile<BM, GATE_UP, 0>(t);
+      gemm_tile<BM, NS, GATE_UP, 0>(t);
       break;
   }
 }
 
-int64_t grid_for(const FfnPlan& pl, int64_t max_rows, int64_t n_groups, int64_t ntiles) {
-  const int64_t tiles = ffn_max_mtiles(pl, max_rows, n_groups) * ntiles;
-  return (tiles + kXcds - 1) / kXcds * kXcds;
-}
-
 }  // namespace
 
-hipError_t gemm_bf16_gate_up(const FfnPlan& pl, const void* A, const int32_t* offsets, const int32_t* gtile,
-                             int64_t n_groups, int64_t max_rows, const void* W1, const void* W3, void* h, int64_t F,
-                             int64_t d, hipStream_t s) {
-  GemmArgs a{(const uint16_t*)A, (const uint16_t*)W1, (const uint16_t*)W3, h, offsets, gtile, (int)n_groups, (int)F,
-             (int)d};
-  const int64_t grid = grid_for(pl, max_rows, n_groups, (F + 127) / 128);
-  if (grid == 0) return hipSuccess;
-  gemm_bf16_kernel<256, true><<<(unsigned)grid, 256, 0, s>>>(a);
-  return hipGetLastError();
+// (bm, stages) pairs compiled below
+#define MOE_GEMM_CONFIGS(X) X(256, 5) X(256, 4) X(128, 6) X(128, 3) X(64, 8) X(64, 4)
+
+int gemm_bf16_default_stages(int bm) { return bm == 256 ? 5 : bm == 128 ? 3 : 4; }
+
+bool gemm_bf16_has_config(int bm, int ns) {
+#define MOE_HAS(B, N) \
+  if (bm == B && ns == N) return true;
+  MOE_GEMM_CONFIGS(MOE_HAS)
+#undef MOE_HAS
+  return false;
 }
 
-hipError_t gemm_bf16_down(const FfnPlan& pl, const void* h, const int32_t* offsets, const int32_t* gtile,
-                          int64_t n_groups, int64_t max_rows, const void* W2, float* yp, int64_t F, int64_t d,
-                          hipStream_t s) {
-  GemmArgs a{(const uint16_t*)h, (const uint16_t*)W2, nullptr, yp, offsets, gtile, (int)n_groups, (int)d, (int)F};
-  const int64_t grid = grid_for(pl, max_rows, n_groups, (d + 255) / 256);
-  if (grid == 0) return hipSuccess;
-  gemm_bf16_kernel<256, false><<<(unsigned)grid, 256, 0, s>>>(a);
-  return hipGetLastError();
+hipError_t gemm_bf16_gate_up(const FfnPlan& pl, const void* A, const int4* tab, const int32_t* count, int64_t grid,
+                             const void* W1, const void* W3, void* h, int64_t F, int64_t d, hipStream_t s) {
+  GemmArgs a{(const uint16_t*)A, (const uint16_t*)W1, (const uint16_t*)W3, h, tab, count, (int)F, (int)d};
+#define MOE_LAUNCH(B, N)                                                                     \
+  if (pl.bm == B && pl.ns == N) {                                                            \
+    gemm_bf16_kernel<B, N, true><<<(unsigned)grid, 256, 0, s>>>(a);                          \
+    return hipGetLastError();                                                                \
+  }
+  MOE_GEMM_CONFIGS(MOE_LAUNCH)
+#undef MOE_LAUNCH
+  return hipErrorInvalidValue;
+}
+
+hipError_t gemm_bf16_down(const FfnPlan& pl, const void* h, const int4* tab, const int32_t* count, int64_t grid,
+                          const void* W2, float* yp, int64_t F, int64_t d, hipStream_t s) {
+  GemmArgs a{(const uint16_t*)h, (const uint16_t*)W2, nullptr, yp, tab, count, (int)d, (int)F};
+#define MOE_LAUNCH(B, N)                                                                     \
+  if (pl.bm == B && pl.ns == N) {                                                            \
+    gemm_bf16_kernel<B, N, false><<<(unsigned)grid, 256, 0, s>>>(a);                         \
+    return hipGetLastError();                                                                \
+  }
+  MOE_GEMM_CONFIGS(MOE_LAUNCH)
+#undef MOE_LAUNCH
+  return hipErrorInvalidValue;
 }
 
 }  // namespace moe

@@ -3,6 +3,8 @@
 //
 // Same SwiGLU expert as the bf16 path (lnwmold.com article, §2.2): vector
 // FMA, 32 x 32 output tiles, k-tiles of 32 staged through LDS, any sizes.
+#include <stdlib.h>
+
 #include "common.h"
 #include "internal.h"
 
@@ -16,9 +18,9 @@ struct F32Args {
   const float* B0;
   const float* B1;
   float* C;
-  const int32_t* offsets;
-  const int32_t* gtile;
-  int n_groups, N, Kdim;
+  const int4* tab;       // {group, first row, rows, first column}
+  const int32_t* count;  // entries in tab
+  int N, Kdim;
 };
 
 template <bool GATE_UP>
@@ -26,22 +28,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const F32Args p) {
   __shared__ float as[FB][FB + 1];
   __shared__ float b0s[FB][FB + 1];
   __shared__ float b1s[GATE_UP ? FB : 1][FB + 1];
-  const int total = p.gtile[p.n_groups];
-  const int64_t L = xcd_tile(blockIdx.x, total);
+  const int64_t L = xcd_tile(blockIdx.x, *p.count);
   if (L < 0) return;
-  int lo = 0, hi = p.n_groups;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (p.gtile[mid] <= L) lo = mid; else hi = mid;
-  }
-  const int g = lo;
-  const int row0 = p.offsets[g];
-  const int rows_g = p.offsets[g + 1] - row0;
-  const int mtiles = (rows_g + FB - 1) / FB;
-  const int r = (int)(L - p.gtile[g]);
-  const int nt = r / mtiles, mt = r % mtiles;
-  const int m0 = mt * FB, n0 = nt * FB;
-  const int rows = min(FB, rows_g - m0);
+  const int4 te = p.tab[L];
+  const int g = te.x, row0 = te.y, rows = te.z, n0 = te.w;
+  const int m0 = 0;
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const int64_t gb = (int64_t)g * p.N * p.Kdim;
   float a00 = 0, a01 = 0, a10 = 0, a11 = 0;
@@ -93,48 +84,72 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const F32Args p) {
 }  // namespace
 
 FfnPlan ffn_plan(bool bf16, int64_t max_rows, int64_t n_groups) {
+  if (!bf16) return FfnPlan{FB, 1, FB, FB};
+  // 128-row m-tiles with 3 LDS stages (72 KB): two workgroups per CU, so one
+  // tile's pipeline fill and epilogue overlap the other's main loop.  Measured
+  // best on all four bf16 workloads on MI355X (prefill included).
+  FfnPlan p{128, 3, 128, 256};
+  // tile overrides for tuning: MOE_GEMM_BM in {64, 128, 256}, MOE_GEMM_NS stages
+  if (const char* e = getenv("MOE_GEMM_BM")) {
+    const int v = atoi(e);
+    if (v == 64 || v == 128 || v == 256) p.bm = v;
+  }
+  if (getenv("MOE_GEMM_BM")) p.ns = gemm_bf16_default_stages(p.bm);
+  if (const char* e = getenv("MOE_GEMM_NS")) {
+    const int v = atoi(e);
+    if (gemm_bf16_has_config(p.bm, v)) p.ns = v;
+  }
   (void)max_rows;
   (void)n_groups;
-  if (bf16) return FfnPlan{256, 128, 256};
-  return FfnPlan{FB, FB, FB};
+  return p;
 }
 
-int64_t ffn_max_mtiles(const FfnPlan& p, int64_t max_rows, int64_t n_groups) {
+int64_t ffn_max_mtiles(int bm, int64_t max_rows, int64_t n_groups) {
   // sum over groups of ceil(rows_g / bm) <= floor(max_rows / bm) + n_groups
-  return max_rows / p.bm + n_groups;
+  return max_rows / bm + n_groups;
 }
 
-hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const void* A, const int32_t* offsets,
-                               const int32_t* gtile, int64_t n_groups, int64_t max_rows, const void* W1,
-                               const void* W3, void* h, int64_t F, int64_t d, hipStream_t s) {
+int64_t ffn_table_entries(bool bf16, int64_t max_rows, int64_t n_groups, int64_t n_cols, bool gate_up) {
+  const int bm = bf16 ? 64 : FB;  // the smallest m-tile any plan uses
+  const int bn = bf16 ? (gate_up ? 128 : 256) : FB;
+  return ffn_max_mtiles(bm, max_rows, n_groups) * ((n_cols + bn - 1) / bn);
+}
+
+static int64_t grid_of(const FfnPlan& p, int64_t max_rows, int64_t n_groups, int64_t n_cols, int bn) {
+  const int64_t tiles = ffn_max_mtiles(p.bm, max_rows, n_groups) * ((n_cols + bn - 1) / bn);
+  return (tiles + kXcds - 1) / kXcds * kXcds;
+}
+
+hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const void* A, const int4* tab, const int32_t* count,
+                               int64_t n_groups, int64_t max_rows, const void* W1, const void* W3, void* h, int64_t F,
+                               int64_t d, hipStream_t s) {
+  const int64_t grid = grid_of(p, max_rows, n_groups, F, p.bn_out_up);
+  if (grid == 0) return hipSuccess;
   prof_begin(K_GEMM_GATE_UP, s);
   hipError_t err;
   if (bf16) {
-    err = gemm_bf16_gate_up(p, A, offsets, gtile, n_groups, max_rows, W1, W3, h, F, d, s);
+    err = gemm_bf16_gate_up(p, A, tab, count, grid, W1, W3, h, F, d, s);
   } else {
-    F32Args a{(const float*)A, (const float*)W1, (const float*)W3, (float*)h, offsets, gtile, (int)n_groups, (int)F,
-              (int)d};
-    const int64_t tiles = ffn_max_mtiles(p, max_rows, n_groups) * ((F + FB - 1) / FB);
-    const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
-    if (grid > 0) gemm_f32_kernel<true><<<(unsigned)grid, 256, 0, s>>>(a);
+    F32Args a{(const float*)A, (const float*)W1, (const float*)W3, (float*)h, tab, count, (int)F, (int)d};
+    gemm_f32_kernel<true><<<(unsigned)grid, 256, 0, s>>>(a);
     err = hipGetLastError();
   }
   prof_end(K_GEMM_GATE_UP, s);
   return err;
 }
 
-hipError_t launch_gemm_down(bool bf16, const FfnPlan& p, const void* h, const int32_t* offsets, const int32_t* gtile,
+hipError_t launch_gemm_down(bool bf16, const FfnPlan& p, const void* h, const int4* tab, const int32_t* count,
                             int64_t n_groups, int64_t max_rows, const void* W2, float* yp, int64_t F, int64_t d,
                             hipStream_t s) {
+  const int64_t grid = grid_of(p, max_rows, n_groups, d, p.bn_out_down);
+  if (grid == 0) return hipSuccess;
   prof_begin(K_GEMM_DOWN, s);
   hipError_t err;
   if (bf16) {
-    err = gemm_bf16_down(p, h, offsets, gtile, n_groups, max_rows, W2, yp, F, d, s);
+    err = gemm_bf16_down(p, h, tab, count, grid, W2, yp, F, d, s);
   } else {
-    F32Args a{(const float*)h, (const float*)W2, nullptr, yp, offsets, gtile, (int)n_groups, (int)d, (int)F};
-    const int64_t tiles = ffn_max_mtiles(p, max_rows, n_groups) * ((d + FB - 1) / FB);
-    const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
-    if (grid > 0) gemm_f32_kernel<false><<<(unsigned)grid, 256, 0, s>>>(a);
+    F32Args a{(const float*)h, (const float*)W2, nullptr, yp, tab, count, (int)d, (int)F};
+    gemm_f32_kernel<false><<<(unsigned)grid, 256, 0, s>>>(a);
     err = hipGetLastError();
   }
   prof_end(K_GEMM_DOWN, s);

@@ -53,26 +53,32 @@ hipError_t launch_dispatch(const void* x, const int32_t* row_src, const int32_t*
 // ---- grouped expert FFN (a6-a7) ----
 struct FfnPlan {
   int bm;           // rows per m-tile
+  int ns;           // LDS stages (bf16 path)
   int bn_out_up;    // h columns per GEMM1 tile
   int bn_out_down;  // yp columns per GEMM2 tile
 };
 FfnPlan ffn_plan(bool bf16, int64_t max_rows, int64_t n_groups);
-// Worst-case tile-list entries for the plan.
-int64_t ffn_max_mtiles(const FfnPlan& p, int64_t max_rows, int64_t n_groups);
-// gtile_up / gtile_down: [n_groups + 1] int32 cumulative tile counts.
+// bf16 GEMM instantiations: default LDS stages for an m-tile size, and
+// whether (bm, ns) is compiled.
+int gemm_bf16_default_stages(int bm);
+bool gemm_bf16_has_config(int bm, int ns);
+// Worst-case m-tiles for `bm`-row tiles.
+int64_t ffn_max_mtiles(int bm, int64_t max_rows, int64_t n_groups);
+// Entries the tile tables need for any plan of this dtype.
+int64_t ffn_table_entries(bool bf16, int64_t max_rows, int64_t n_groups, int64_t n_cols, bool gate_up);
+// Builds both GEMMs' tile tables (int4 {group, first row, rows, first column})
+// and their entry counts counts[0] (gate_up) and counts[1] (down).
 hipError_t launch_ffn_tiles(const FfnPlan& p, const int32_t* offsets, int64_t n_groups, int64_t F, int64_t d,
-                            int32_t* gtile_up, int32_t* gtile_down, hipStream_t s);
+                            int4* tab_up, int4* tab_down, int32_t* counts, hipStream_t s);
 // bf16 MFMA path (gemm_bf16.hip); called through the launchers below.
-hipError_t gemm_bf16_gate_up(const FfnPlan& p, const void* A, const int32_t* offsets, const int32_t* gtile,
-                             int64_t n_groups, int64_t max_rows, const void* W1, const void* W3, void* h, int64_t F,
-                             int64_t d, hipStream_t s);
-hipError_t gemm_bf16_down(const FfnPlan& p, const void* h, const int32_t* offsets, const int32_t* gtile,
-                          int64_t n_groups, int64_t max_rows, const void* W2, float* yp, int64_t F, int64_t d,
-                          hipStream_t s);
-hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const void* A, const int32_t* offsets,
-                               const int32_t* gtile, int64_t n_groups, int64_t max_rows, const void* W1,
-                               const void* W3, void* h, int64_t F, int64_t d, hipStream_t s);
-hipError_t launch_gemm_down(bool bf16, const FfnPlan& p, const void* h, const int32_t* offsets, const int32_t* gtile,
+hipError_t gemm_bf16_gate_up(const FfnPlan& p, const void* A, const int4* tab, const int32_t* count, int64_t grid,
+                             const void* W1, const void* W3, void* h, int64_t F, int64_t d, hipStream_t s);
+hipError_t gemm_bf16_down(const FfnPlan& p, const void* h, const int4* tab, const int32_t* count, int64_t grid,
+                          const void* W2, float* yp, int64_t F, int64_t d, hipStream_t s);
+hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const void* A, const int4* tab, const int32_t* count,
+                               int64_t n_groups, int64_t max_rows, const void* W1, const void* W3, void* h, int64_t F,
+                               int64_t d, hipStream_t s);
+hipError_t launch_gemm_down(bool bf16, const FfnPlan& p, const void* h, const int4* tab, const int32_t* count,
                             int64_t n_groups, int64_t max_rows, const void* W2, float* yp, int64_t F, int64_t d,
                             hipStream_t s);
 

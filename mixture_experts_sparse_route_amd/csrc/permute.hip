@@ -134,41 +134,59 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const V* __restrict__ x, 
 }
 
 // ------------------------------------------------------------ FFN tiles
-// gtile[g] = sum over g' < g of ceil(rows(g') / bm) * n_ntiles, for both GEMMs.
+// One workgroup.  Tile list of both expert GEMMs: for group g with rows(g)
+// rows, ceil(rows(g) / bm) m-tiles times the GEMM's n-tiles, in the order
+// (group, n-tile, m-tile) with the m-tile fastest, so the m-tiles of one
+// weight tile are neighbours.  Entry L = {group, first row, rows, first
+// column}; count[0] = number of entries.
 __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t* __restrict__ offsets, int G, int bm,
-                                                         int nt_up, int nt_down, int32_t* __restrict__ gtile_up,
-                                                         int32_t* __restrict__ gtile_down) {
-  __shared__ int carry;
+                                                         int nt_up, int bn_up, int nt_down, int bn_down,
+                                                         int4* __restrict__ tab_up, int4* __restrict__ tab_down,
+                                                         int32_t* __restrict__ counts) {
+  __shared__ int mstart[1025];  // exclusive scan of m-tiles per group (G <= 1024)
   __shared__ int buf[1024];
-  if (threadIdx.x == 0) carry = 0;
+  const int g = threadIdx.x;
+  int mt = 0;
+  if (g < G) {
+    const int rows = offsets[g + 1] - offsets[g];
+    mt = rows > 0 ? (rows + bm - 1) / bm : 0;
+  }
+  buf[g] = mt;
   __syncthreads();
-  for (int g0 = 0; g0 < G; g0 += 1024) {
-    const int g = g0 + threadIdx.x;
-    int mt = 0;
-    if (g < G) {
-      const int rows = offsets[g + 1] - offsets[g];
-      mt = rows > 0 ? (rows + bm - 1) / bm : 0;
-    }
-    buf[threadIdx.x] = mt;
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = g >= off ? buf[g - off] : 0;
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int v = threadIdx.x >= off ? buf[threadIdx.x - off] : 0;
-      __syncthreads();
-      buf[threadIdx.x] += v;
-      __syncthreads();
-    }
-    if (g < G) {
-      const int excl = carry + buf[threadIdx.x] - mt;
-      gtile_up[g] = excl * nt_up;
-      gtile_down[g] = excl * nt_down;
-    }
-    __syncthreads();
-    if (threadIdx.x == 1023) carry += buf[1023];
+    buf[g] += v;
     __syncthreads();
   }
-  if (threadIdx.x == 0) {
-    gtile_up[G] = carry * nt_up;
-    gtile_down[G] = carry * nt_down;
+  if (g < G) mstart[g] = buf[g] - mt;
+  if (g == 0) mstart[G] = buf[1023];
+  __syncthreads();
+  const int total_m = mstart[G];
+  const int tot_up = total_m * nt_up, tot_down = total_m * nt_down;
+  if (g == 0) {
+    counts[0] = tot_up;
+    counts[1] = tot_down;
+  }
+  for (int pass = 0; pass < 2; ++pass) {
+    const int nt = pass == 0 ? nt_up : nt_down;
+    const int bn = pass == 0 ? bn_up : bn_down;
+    const int tot = pass == 0 ? tot_up : tot_down;
+    int4* tab = pass == 0 ? tab_up : tab_down;
+    for (int L = threadIdx.x; L < tot; L += 1024) {
+      // group of entry L: largest gg with mstart[gg] * nt <= L
+      int lo = 0, hi = G;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (mstart[mid] * nt <= L) lo = mid; else hi = mid;
+      }
+      const int mtiles = mstart[lo + 1] - mstart[lo];
+      const int r = L - mstart[lo] * nt;
+      const int n = r / mtiles, m = r % mtiles;
+      const int row0 = offsets[lo] + m * bm;
+      const int rows = min(bm, offsets[lo + 1] - row0);
+      tab[L] = make_int4(lo, row0, rows, n * bn);
+    }
   }
 }
 
@@ -220,11 +238,12 @@ hipError_t launch_dispatch(const void* x, const int32_t* row_src, const int32_t*
 }
 
 hipError_t launch_ffn_tiles(const FfnPlan& p, const int32_t* offsets, int64_t n_groups, int64_t F, int64_t d,
-                            int32_t* gtile_up, int32_t* gtile_down, hipStream_t s) {
+                            int4* tab_up, int4* tab_down, int32_t* counts, hipStream_t s) {
   const int nt_up = (int)((F + p.bn_out_up - 1) / p.bn_out_up);
   const int nt_down = (int)((d + p.bn_out_down - 1) / p.bn_out_down);
   prof_begin(K_FFN_TILES, s);
-  ffn_tiles_kernel<<<1, 1024, 0, s>>>(offsets, (int)n_groups, p.bm, nt_up, nt_down, gtile_up, gtile_down);
+  ffn_tiles_kernel<<<1, 1024, 0, s>>>(offsets, (int)n_groups, p.bm, nt_up, p.bn_out_up, nt_down, p.bn_out_down,
+                                      tab_up, tab_down, counts);
   prof_end(K_FFN_TILES, s);
   return hipGetLastError();
 }
