@@ -34,7 +34,6 @@ namespace {
 
 constexpr int BKS = 32;   // k per stage
 constexpr int RB = 64;    // LDS bytes per tile row
-constexpr int BNB = 256;  // weight rows per tile
 constexpr int LDS_BYTES = 160 * 1024;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -72,202 +71,252 @@ __device__ __forceinline__ void vm_wait_stages(int ahead) {
   }
 }
 
-// Per-tile state handed from the kernel's set-up to the k-loop.
-struct TileCtx {
-  char* lds;
-  const uint16_t* a_src[4];
-  const uint16_t* b_src[4];
-  void* C;
-  int64_t out_row0;
-  int rows, n0, N, nk, wave, lane;
+// DMA issue state of one workgroup: the table entry of the tile whose
+// k-steps are being issued, and of the tile after it.
+struct TileRef {
+  int g, row_first, rows, n0;  // group, first row, rows, first column
 };
 
-// k-loop and epilogue for a wave that owns NBW active 16-row blocks.
-template <int BM, int NS, bool GATE_UP, int NBW>
-__device__ __forceinline__ void gemm_tile(const TileCtx& t) {
-  constexpr int AG = BM / 16 / 4;   // A 16-row groups loaded per wave per stage
-  constexpr int BG = BNB / 16 / 4;  // B 16-row groups loaded per wave per stage
-  constexpr int LPS = AG + BG;      // loads per wave per stage
+__device__ __forceinline__ TileRef load_tile(const int4* tab, int64_t L) {
+  const int4 v = tab[L];
+  return TileRef{v.x, v.y, v.z, v.w};
+}
+
+struct IssueState {
+  TileRef cur;   // tile whose k-steps are being issued
+  TileRef next;  // the following tile
+  int tile;      // position of `cur` in this workgroup's tile sequence
+};
+
+// Per-workgroup constants of the tile sequence.
+struct Seq {
+  int64_t lbase;    // table index of the first tile
+  int lstride;      // table stride between consecutive tiles of this workgroup
+  int n_tiles;      // tiles of this workgroup
+  int nk;           // k-steps per tile
+  int total_steps;  // n_tiles * nk
+};
+
+// Issues the DMA of global step s (tile s / nk, k-step s % nk) into stage s % NS.
+// Lane -> (row r_l of a 16-row group, chunk c_l), chunk swizzled as in
+// lds_pos; A rows past the tile's end are loaded clamped to its last row
+// (their results are never stored).
+template <int BM, int BNB, int NS, bool GATE_UP>
+__device__ __forceinline__ void issue_step(IssueState& is, const GemmArgs& p, const Seq& q, char* lds, int s, int wave,
+                                           int lane) {
+  constexpr int AG = BM / 16 / 4;
+  constexpr int BG = BNB / 16 / 4;
+  constexpr int HALF = BNB / 4;  // gate_up: rows of one matrix in each quarter of the weight tile
+  constexpr int STAGE = (BM + BNB) * RB;
+  const int ti = s / q.nk, kt = s - ti * q.nk;
+  if (ti != is.tile) {  // crossed into the next tile of the sequence
+    is.tile = ti;
+    is.cur = is.next;
+    if (ti + 1 < q.n_tiles) is.next = load_tile(p.tab, q.lbase + (int64_t)(ti + 1) * q.lstride);
+  }
+  const int64_t Kd = p.Kdim;
+  const int r_l = lane >> 2;
+  const int c_l = (lane & 3) ^ ((r_l >> 2) & 3);
+  const int g = is.cur.g, row_first = is.cur.row_first, rows = is.cur.rows, n0 = is.cur.n0;
+  const int64_t ko = (int64_t)kt * BKS + c_l * 8;
+  char* const st = lds + (s % NS) * STAGE;
+#pragma unroll
+  for (int j = 0; j < AG; ++j) {
+    const int row = min((wave + 4 * j) * 16 + r_l, rows - 1);
+    __builtin_amdgcn_global_load_lds(p.A + (int64_t)(row_first + row) * Kd + ko,
+                                     (lds_ptr_t)(st + (wave + 4 * j) * 16 * RB), 16, 0, 0);
+  }
+  const int64_t gbase = (int64_t)g * p.N * Kd + ko;
+#pragma unroll
+  for (int j = 0; j < BG; ++j) {
+    const int q16 = wave + 4 * j;
+    int col;
+    const uint16_t* base = p.B0;
+    if (GATE_UP) {
+      // quarters of the weight tile: W1 half 0, W3 half 0, W1 half 1, W3 half 1
+      const int qb = (q16 * 16) / HALF;
+      if (qb & 1) base = p.B1;
+      col = n0 + (qb >> 1) * HALF + (q16 * 16) % HALF + r_l;
+    } else {
+      col = n0 + q16 * 16 + r_l;
+    }
+    col = min(col, p.N - 1);
+    __builtin_amdgcn_global_load_lds(base + gbase + (int64_t)col * Kd,
+                                     (lds_ptr_t)(st + BM * RB + (wave + 4 * j) * 16 * RB), 16, 0, 0);
+  }
+}
+
+// k-loop and epilogue of one tile for a wave that owns NBW active 16-row
+// blocks.  `step` is the global step of the tile's first k-step.
+template <int BM, int BNB, int NS, bool GATE_UP, int NBW>
+__device__ __forceinline__ void gemm_tile(IssueState& is, const GemmArgs& p, const Seq& q, char* lds, const TileRef te,
+                                          const int step0, const int wave, const int lane) {
+  constexpr int AG = BM / 16 / 4;
+  constexpr int BG = BNB / 16 / 4;
+  constexpr int CB = BNB / 32;  // 16-column MFMA blocks per N-wave
+  constexpr int LPS = AG + BG;  // loads per wave per stage
   static_assert((NS - 2) * LPS <= 63, "vmcnt counts at most 63 outstanding loads");
   constexpr int STAGE = (BM + BNB) * RB;
-  const int wave = t.wave, lane = t.lane;
   const int wm = wave & 1, wn = wave >> 1;
   const int lr = lane & 15, lk = lane >> 4;
-  char* const lds_wave_a = t.lds + wave * 16 * RB;
-  char* const lds_wave_b = t.lds + BM * RB + wave * 16 * RB;
-
-#define GG_ISSUE(kt_)                                                                                   \
-  do {                                                                                                  \
-    const int st_ = (kt_) % NS;                                                                         \
-    const int64_t ko_ = (int64_t)(kt_) * BKS;                                                           \
-    _Pragma("unroll") for (int j = 0; j < AG; ++j) __builtin_amdgcn_global_load_lds(                   \
-        t.a_src[j] + ko_, (lds_ptr_t)(lds_wave_a + st_ * STAGE + j * 4 * 16 * RB), 16, 0, 0);           \
-    _Pragma("unroll") for (int j = 0; j < BG; ++j) __builtin_amdgcn_global_load_lds(                   \
-        t.b_src[j] + ko_, (lds_ptr_t)(lds_wave_b + st_ * STAGE + j * 4 * 16 * RB), 16, 0, 0);           \
-  } while (0)
 
   constexpr int NA = NBW > 0 ? NBW : 1;  // array extent (NBW may be 0)
-  f32x4_t acc[NA][8];
+  f32x4_t acc[NA][CB];
 #pragma unroll
   for (int i = 0; i < NBW; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < CB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = t.nk;
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) GG_ISSUE(s);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt has landed once at most min(NS-2, nk-1-kt) later stages are outstanding
-    vm_wait_stages<LPS, NS - 2>(nk - 1 - kt);
+  for (int kt = 0; kt < q.nk; ++kt) {
+    const int s = step0 + kt;
+    // stage s has landed once at most min(NS-2, total_steps-1-s) later stages are outstanding
+    vm_wait_stages<LPS, NS - 2>(q.total_steps - 1 - s);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-
-    const char* st = t.lds + (kt % NS) * STAGE;
-    bf16x8_t bfr[8];
+    const char* st = lds + (s % NS) * STAGE;
+    bf16x8_t bfr[CB];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      bfr[j] = *(const bf16x8_t*)(st + BM * RB + lds_pos(wn * 128 + j * 16 + lr, lk));
+    for (int j = 0; j < CB; ++j)
+      bfr[j] = *(const bf16x8_t*)(st + BM * RB + lds_pos(wn * (BNB / 2) + j * 16 + lr, lk));
     bf16x8_t afr[NA];
 #pragma unroll
     for (int i = 0; i < NBW; ++i) afr[i] = *(const bf16x8_t*)(st + lds_pos((2 * i + wm) * 16 + lr, lk));
     asm volatile("" ::: "memory");
-    // refill the stage consumed in the previous iteration (every wave has
-    // passed this iteration's barrier, so nobody reads it any more)
-    if (kt + NS - 1 < nk) GG_ISSUE(kt + NS - 1);
+    // refill the stage consumed in the previous step (every wave has passed
+    // this step's barrier, so nobody reads it any more); near the end of a
+    // tile this already fetches the next tile's first k-steps
+    if (s + NS - 1 < q.total_steps) issue_step<BM, BNB, NS, GATE_UP>(is, p, q, lds, s + NS - 1, wave, lane);
 #pragma unroll
     for (int i = 0; i < NBW; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < CB; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[i], bfr[j], acc[i][j], 0, 0, 0);
   }
-#undef GG_ISSUE
 
   // ---- epilogue: lane holds rows (2i+wm)*16 + lk*4 + v, column block j, column lr
+  const int rows = te.rows, n0 = te.n0;
+  const int64_t out_row0 = te.row_first;
 #pragma unroll
   for (int i = 0; i < NBW; ++i) {
     const int rb_ = (2 * i + wm) * 16 + lk * 4;
     if (GATE_UP) {
-      uint16_t* C = (uint16_t*)t.C;
+      // column blocks j < CB/2 hold W1 results, j + CB/2 the W3 results of the same h columns
+      uint16_t* C = (uint16_t*)p.C;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = t.n0 + wn * 64 + j * 16 + lr;
-        if (col >= t.N) continue;
+      for (int j = 0; j < CB / 2; ++j) {
+        const int col = n0 + wn * (BNB / 4) + j * 16 + lr;
+        if (col >= p.N) continue;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int rr = rb_ + v;
-          if (rr < t.rows) C[(t.out_row0 + rr) * t.N + col] = f32_to_bf16(silu(acc[i][j][v]) * acc[i][j + 4][v]);
+          if (rr < rows) C[(out_row0 + rr) * p.N + col] = f32_to_bf16(silu(acc[i][j][v]) * acc[i][j + CB / 2][v]);
         }
       }
     } else {
-      float* C = (float*)t.C;
+      float* C = (float*)p.C;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int col = t.n0 + wn * 128 + j * 16 + lr;
-        if (col >= t.N) continue;
+      for (int j = 0; j < CB; ++j) {
+        const int col = n0 + wn * (BNB / 2) + j * 16 + lr;
+        if (col >= p.N) continue;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int rr = rb_ + v;
-          if (rr < t.rows) C[(t.out_row0 + rr) * t.N + col] = acc[i][j][v];
+          if (rr < rows) C[(out_row0 + rr) * p.N + col] = acc[i][j][v];
         }
       }
     }
   }
 }
 
-template <int BM, int NS, bool GATE_UP>
+// Persistent grouped GEMM.  The tiles of the table are cut into 8 contiguous
+// ranges, one per XCD; the G workgroups of an XCD take its tiles round-robin,
+// so the tiles in flight on an XCD at any time are neighbours (same weight
+// tile, same rows).  A workgroup's tiles form one stream of k-steps for the
+// LDS ring, so the next tile's first stages load while the current tile
+// finishes and writes its output.  With one workgroup per tile this is the
+// plain one-tile-per-workgroup GEMM.
+template <int BM, int BNB, int NS, bool GATE_UP>
 __global__ __launch_bounds__(256, NS*(BM + BNB) * RB <= LDS_BYTES / 2 ? 2 : 1) void gemm_bf16_kernel(const GemmArgs p) {
-  constexpr int MI = BM / 32;        // MFMA row blocks per M-wave
-  constexpr int AG = BM / 16 / 4;
-  constexpr int BG = BNB / 16 / 4;
-  static_assert(AG <= 4 && BG <= 4, "TileCtx holds at most 4 source rows per wave");
+  constexpr int MI = BM / 32;  // MFMA row blocks per M-wave
   constexpr int STAGE = (BM + BNB) * RB;
   static_assert(NS * STAGE <= LDS_BYTES, "LDS stages exceed 160 KB");
   __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
 
-  // ---- which tile: one table entry
-  const int64_t L = xcd_tile(blockIdx.x, *p.count);
-  if (L < 0) return;
-  const int4 te = p.tab[L];
-  const int g = te.x, row_first = te.y;
+  const int total = *p.count;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int g8 = gridDim.x / kXcds;
+  const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+  const int begin = xcd * per_xcd, end = min(total, begin + per_xcd);
+  if (begin + j >= end) return;
+  Seq q;
+  q.lbase = begin + j;
+  q.lstride = g8;
+  q.n_tiles = (end - begin - j + g8 - 1) / g8;
+  q.nk = p.Kdim / BKS;
+  q.total_steps = q.n_tiles * q.nk;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 
-  TileCtx t;
-  t.lds = lds;
-  t.rows = te.z;
-  t.n0 = te.w;
-  t.N = p.N;
-  t.nk = p.Kdim / BKS;
-  t.C = p.C;
-  t.out_row0 = row_first;
-  t.wave = threadIdx.x >> 6;
-  t.lane = threadIdx.x & 63;
-  const int64_t Kd = p.Kdim;
-
-  // ---- DMA sources: lane -> (row r_l of a 16-row group, chunk c_l)
-  const int r_l = t.lane >> 2;
-  const int c_l = (t.lane & 3) ^ ((r_l >> 2) & 3);
+  IssueState is;
+  is.tile = 0;
+  is.cur = load_tile(p.tab, q.lbase);
+  is.next = q.n_tiles > 1 ? load_tile(p.tab, q.lbase + q.lstride) : is.cur;
 #pragma unroll
-  for (int j = 0; j < AG; ++j) {
-    const int row = min((t.wave + 4 * j) * 16 + r_l, t.rows - 1);
-    t.a_src[j] = p.A + (int64_t)(row_first + row) * Kd + c_l * 8;
-  }
-  const int64_t gbase = (int64_t)g * p.N * Kd;
-#pragma unroll
-  for (int j = 0; j < BG; ++j) {
-    const int q16 = t.wave + 4 * j;
-    int col;
-    const uint16_t* base = p.B0;
-    if (GATE_UP) {
-      const int qb = q16 >> 2;
-      if (qb & 1) base = p.B1;
-      col = t.n0 + (qb >> 1) * 64 + (q16 & 3) * 16 + r_l;
-    } else {
-      col = t.n0 + q16 * 16 + r_l;
-    }
-    col = min(col, p.N - 1);
-    t.b_src[j] = base + gbase + (int64_t)col * Kd + c_l * 8;
-  }
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < q.total_steps) issue_step<BM, BNB, NS, GATE_UP>(is, p, q, lds, s, wave, lane);
 
-  // active 16-row blocks of this wave's M half: blocks 2i + wm
-  const int nbm = (t.rows + 15) >> 4;
-  const int nbw = min(MI, (nbm - (t.wave & 1) + 1) >> 1);
-  switch (nbw) {
-#define GG_CASE(n) \
-  case n:          \
-    if constexpr (n <= MI) gemm_tile<BM, NS, GATE_UP, n>(t); \
+  for (int t = 0; t < q.n_tiles; ++t) {
+    // k-steps issued so far end inside tile t (nk >= NS - 1), so the issue
+    // state's current entry is tile t's
+    const TileRef te = is.cur;
+    const int nbm = (te.rows + 15) >> 4;
+    const int nbw = min(MI, (nbm - (wave & 1) + 1) >> 1);
+    switch (nbw) {
+#define GG_CASE(n)                                                                        \
+  case n:                                                                                 \
+    if constexpr (n <= MI) gemm_tile<BM, BNB, NS, GATE_UP, n>(is, p, q, lds, te, t * q.nk, wave, lane); \
     break;
-    GG_CASE(1) GG_CASE(2) GG_CASE(3) GG_CASE(4) GG_CASE(5) GG_CASE(6) GG_CASE(7) GG_CASE(8)
+      GG_CASE(1) GG_CASE(2) GG_CASE(3) GG_CASE(4) GG_CASE(5) GG_CASE(6) GG_CASE(7) GG_CASE(8)
 #undef GG_CASE
-    default:
-      // no rows in this M half: still take part in the barriers and loads
-      gemm_tile<BM, NS, GATE_UP, 0>(t);
-      break;
+      default:
+        // no rows in this M half: still take part in the barriers and loads
+        gemm_tile<BM, BNB, NS, GATE_UP, 0>(is, p, q, lds, te, t * q.nk, wave, lane);
+        break;
+    }
   }
 }
 
 }  // namespace
 
-// (bm, stages) pairs compiled below
-#define MOE_GEMM_CONFIGS(X) X(256, 5) X(256, 4) X(128, 6) X(128, 3) X(64, 8) X(64, 4)
+// (m-tile rows, weight-tile rows, LDS stages) compiled below.  The k-loop
+// needs K >= 32 * (NS - 1); the launchers check it.
+#define MOE_GEMM_CONFIGS(X) X(256, 256, 5) X(256, 256, 4) X(128, 256, 3) X(128, 256, 6) X(64, 256, 4) \
+  X(128, 128, 4) X(64, 128, 8) X(64, 128, 6)
 
-int gemm_bf16_default_stages(int bm) { return bm == 256 ? 5 : bm == 128 ? 3 : 4; }
-
-bool gemm_bf16_has_config(int bm, int ns) {
-#define MOE_HAS(B, N) \
-  if (bm == B && ns == N) return true;
+bool gemm_bf16_has_config(int bm, int bnb, int ns) {
+#define MOE_HAS(B, W, N) \
+  if (bm == B && bnb == W && ns == N) return true;
   MOE_GEMM_CONFIGS(MOE_HAS)
 #undef MOE_HAS
   return false;
 }
 
+// Workgroups to launch: one per tile (upper bound `grid`), or with
+// pl.wg_per_cu > 0 a persistent grid of wg_per_cu workgroups per CU.
+static int64_t launch_grid(const FfnPlan& pl, int64_t grid) {
+  if (pl.wg_per_cu <= 0) return grid;
+  const int64_t pg = (int64_t)device_cus() * pl.wg_per_cu / kXcds * kXcds;
+  return pg < grid ? pg : grid;
+}
+
 hipError_t gemm_bf16_gate_up(const FfnPlan& pl, const void* A, const int4* tab, const int32_t* count, int64_t grid,
                              const void* W1, const void* W3, void* h, int64_t F, int64_t d, hipStream_t s) {
   GemmArgs a{(const uint16_t*)A, (const uint16_t*)W1, (const uint16_t*)W3, h, tab, count, (int)F, (int)d};
-#define MOE_LAUNCH(B, N)                                                                     \
-  if (pl.bm == B && pl.ns == N) {                                                            \
-    gemm_bf16_kernel<B, N, true><<<(unsigned)grid, 256, 0, s>>>(a);                          \
-    return hipGetLastError();                                                                \
+  if (d / BKS < pl.ns_up - 1) return hipErrorInvalidValue;
+  const unsigned g = (unsigned)launch_grid(pl, grid);
+#define MOE_LAUNCH(B, W, N)                                           \
+  if (pl.bm == B && pl.bnb_up == W && pl.ns_up == N) {                \
+    gemm_bf16_kernel<B, W, N, true><<<g, 256, 0, s>>>(a);             \
+    return hipGetLastError();                                         \
   }
   MOE_GEMM_CONFIGS(MOE_LAUNCH)
 #undef MOE_LAUNCH
@@ -277,10 +326,12 @@ hipError_t gemm_bf16_gate_up(const FfnPlan& pl, const void* A, const int4* tab, 
 hipError_t gemm_bf16_down(const FfnPlan& pl, const void* h, const int4* tab, const int32_t* count, int64_t grid,
                           const void* W2, float* yp, int64_t F, int64_t d, hipStream_t s) {
   GemmArgs a{(const uint16_t*)h, (const uint16_t*)W2, nullptr, yp, tab, count, (int)d, (int)F};
-#define MOE_LAUNCH(B, N)                                                                     \
-  if (pl.bm == B && pl.ns == N) {                                                            \
-    gemm_bf16_kernel<B, N, false><<<(unsigned)grid, 256, 0, s>>>(a);                         \
-    return hipGetLastError();                                                                \
+  if (F / BKS < pl.ns_down - 1) return hipErrorInvalidValue;
+  const unsigned g = (unsigned)launch_grid(pl, grid);
+#define MOE_LAUNCH(B, W, N)                                           \
+  if (pl.bm == B && pl.bnb_down == W && pl.ns_down == N) {            \
+    gemm_bf16_kernel<B, W, N, false><<<g, 256, 0, s>>>(a);            \
+    return hipGetLastError();                                         \
   }
   MOE_GEMM_CONFIGS(MOE_LAUNCH)
 #undef MOE_LAUNCH

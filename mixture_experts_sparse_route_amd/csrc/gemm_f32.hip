@@ -83,24 +83,61 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const F32Args p) {
 
 }  // namespace
 
-FfnPlan ffn_plan(bool bf16, int64_t max_rows, int64_t n_groups) {
-  if (!bf16) return FfnPlan{FB, 1, FB, FB};
-  // 128-row m-tiles with 3 LDS stages (72 KB): two workgroups per CU, so one
-  // tile's pipeline fill and epilogue overlap the other's main loop.  Measured
-  // best on all four bf16 workloads on MI355X (prefill included).
-  FfnPlan p{128, 3, 128, 256};
-  // tile overrides for tuning: MOE_GEMM_BM in {64, 128, 256}, MOE_GEMM_NS stages
-  if (const char* e = getenv("MOE_GEMM_BM")) {
-    const int v = atoi(e);
-    if (v == 64 || v == 128 || v == 256) p.bm = v;
+int device_cus() {
+  static int n_cu = 0;
+  if (n_cu == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n_cu = v;
+    else
+      n_cu = 256;
   }
-  if (getenv("MOE_GEMM_BM")) p.ns = gemm_bf16_default_stages(p.bm);
-  if (const char* e = getenv("MOE_GEMM_NS")) {
-    const int v = atoi(e);
-    if (gemm_bf16_has_config(p.bm, v)) p.ns = v;
+  return n_cu;
+}
+
+static int env_int(const char* name, int def) {
+  const char* e = getenv(name);
+  return e ? atoi(e) : def;
+}
+
+FfnPlan ffn_plan(bool bf16, int64_t max_rows, int64_t n_groups, int64_t F, int64_t d) {
+  if (!bf16) return FfnPlan{FB, 0, 1, 0, 1, 0, FB, FB};
+  // 128-row m-tiles with a 3-stage ring of 256-row weight tiles (72 KB of
+  // LDS): two workgroups per CU, so one tile's pipeline fill and epilogue
+  // overlap the other's main loop.  A GEMM that would have fewer than two
+  // such tiles per CU uses 128-row weight tiles (4 stages, 64 KB) instead.
+  // Few rows per expert (decode-sized batches): 64-row m-tiles and a 6-stage
+  // ring of 128-row weight tiles, the deepest weight stream that still fits
+  // two workgroups per CU.
+  FfnPlan p{128, 256, 3, 256, 3, 0, 128, 256};
+  if (n_groups > 0 && max_rows / n_groups <= 64) {
+    p = FfnPlan{64, 128, 6, 128, 6, 0, 64, 128};
+  } else {
+    const int64_t mtiles = max_rows / 128 > n_groups ? max_rows / 128 : n_groups;  // rough m-tile count
+    const int64_t want = 2 * (int64_t)device_cus();
+    if (mtiles * ((F + 127) / 128) < want) {
+      p.bnb_up = 128;
+      p.ns_up = 4;
+    }
+    if (mtiles * ((d + 255) / 256) < want) {
+      p.bnb_down = 128;
+      p.ns_down = 4;
+    }
   }
-  (void)max_rows;
-  (void)n_groups;
+  // overrides for tuning: MOE_GEMM_BM, MOE_GEMM_{BNB,NS}_{UP,DOWN}, MOE_GEMM_WGS
+  const FfnPlan def = p;
+  p.bm = env_int("MOE_GEMM_BM", p.bm);
+  p.bnb_up = env_int("MOE_GEMM_BNB_UP", p.bnb_up);
+  p.ns_up = env_int("MOE_GEMM_NS_UP", p.ns_up);
+  p.bnb_down = env_int("MOE_GEMM_BNB_DOWN", p.bnb_down);
+  p.ns_down = env_int("MOE_GEMM_NS_DOWN", p.ns_down);
+  p.wg_per_cu = env_int("MOE_GEMM_WGS", p.wg_per_cu);
+  if (!gemm_bf16_has_config(p.bm, p.bnb_up, p.ns_up) || !gemm_bf16_has_config(p.bm, p.bnb_down, p.ns_down) ||
+      d / 32 < p.ns_up - 1 || F / 32 < p.ns_down - 1)
+    p = def;
+  p.bn_out_up = p.bnb_up / 2;
+  p.bn_out_down = p.bnb_down;
   return p;
 }
 
@@ -111,7 +148,7 @@ int64_t ffn_max_mtiles(int bm, int64_t max_rows, int64_t n_groups) {
 
 int64_t ffn_table_entries(bool bf16, int64_t max_rows, int64_t n_groups, int64_t n_cols, bool gate_up) {
   const int bm = bf16 ? 64 : FB;  // the smallest m-tile any plan uses
-  const int bn = bf16 ? (gate_up ? 128 : 256) : FB;
+  const int bn = bf16 ? (gate_up ? 64 : 128) : FB;  // the narrowest tiles any plan uses
   return ffn_max_mtiles(bm, max_rows, n_groups) * ((n_cols + bn - 1) / bn);
 }
 

@@ -53,15 +53,19 @@ hipError_t launch_dispatch(const void* x, const int32_t* row_src, const int32_t*
 // ---- grouped expert FFN (a6-a7) ----
 struct FfnPlan {
   int bm;           // rows per m-tile
-  int ns;           // LDS stages (bf16 path)
+  int bnb_up;       // bf16: weight rows per GEMM1 tile (W1 and W3 rows together)
+  int ns_up;        // bf16: LDS stages of GEMM1
+  int bnb_down;     // bf16: weight rows per GEMM2 tile
+  int ns_down;      // bf16: LDS stages of GEMM2
+  int wg_per_cu;    // bf16: persistent workgroups per CU (0 = one workgroup per tile)
   int bn_out_up;    // h columns per GEMM1 tile
   int bn_out_down;  // yp columns per GEMM2 tile
 };
-FfnPlan ffn_plan(bool bf16, int64_t max_rows, int64_t n_groups);
-// bf16 GEMM instantiations: default LDS stages for an m-tile size, and
-// whether (bm, ns) is compiled.
-int gemm_bf16_default_stages(int bm);
-bool gemm_bf16_has_config(int bm, int ns);
+// Compute units of the current device (queried once).
+int device_cus();
+FfnPlan ffn_plan(bool bf16, int64_t max_rows, int64_t n_groups, int64_t F, int64_t d);
+// Whether the bf16 GEMM is compiled for (m-tile rows, weight-tile rows, stages).
+bool gemm_bf16_has_config(int bm, int bnb, int ns);
 // Worst-case m-tiles for `bm`-row tiles.
 int64_t ffn_max_mtiles(int bm, int64_t max_rows, int64_t n_groups);
 // Entries the tile tables need for any plan of this dtype.
