@@ -206,14 +206,19 @@ def main():
     roof["avg_launch_ms"] = round(dom_avg_ms, 4)
     roof["algorithmic_bytes_per_launch"] = per_launch_bytes
     roof["algorithmic_flops_per_launch"] = per_launch_flops
-    # HBM traffic from rocprofv3 counters, valid only for the kernel source it was taken on
+    # HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    # summary, valid only for the kernel source the counters were taken on
     roof["traffic"] = None
-    tpath = os.path.join(ROOT, "profiles", f"traffic_{dominant}_{wl.name}.json")
+    tpath = os.path.join(ROOT, "profiles", f"traffic__{dominant}__{wl.name}.txt")
     if os.path.exists(tpath):
-        t = json.load(open(tpath))
+        kv = {}
+        for ln in open(tpath):
+            if "=" in ln and not ln.lstrip().startswith("#"):
+                k, v = ln.split("=", 1)
+                kv[k.strip()] = v.strip()
         src = os.path.join(ROOT, "mixture_experts_sparse_route_amd", "csrc", "gemm_bf16.hip")
-        if t.get("source_sha256_16") == source_hash(src):
-            roof["traffic"] = t["bytes_per_launch"]
+        if kv.get("source_sha256_16") == source_hash(src):
+            roof["traffic"] = float(kv["bytes_per_launch"])
 
     line = {
         "metric": METRIC,
