@@ -58,6 +58,8 @@ def _load():
         lib.orc_swiglu.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp, i32]
         lib.orc_forward_rows.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]
         lib.orc_expert_choice.argtypes = [P, vp, i64, vp, vp]
+        lib.orc_router_stats.argtypes = [P, vp, vp, vp]
+        lib.orc_router_stats.restype = None
         lib.orc_threads.argtypes = []
         lib.orc_threads.restype = i32
         lib.orc_combine.argtypes = [P, vp, vp, vp, vp, vp, vp]
@@ -165,6 +167,20 @@ def forward_rows(L: OrcLayer, x, idx, w, dest, W1e, W3e, W2e, Ws1=None, Ws3=None
                              _p(y))
     del k1, k3, k2
     return y
+
+
+STAT_NAMES = ["balance", "z_loss", "lif", "cv", "entropy_p", "entropy_f"]
+
+
+def router_stats(L: OrcLayer, lg, idx) -> dict:
+    """{'P': [E], 'balance', 'z_loss', 'lif', 'cv', 'entropy_p', 'entropy_f'} (float64)."""
+    out = np.empty(L.E + len(STAT_NAMES), dtype=np.float64)
+    _load().orc_router_stats(ctypes.byref(L), _p(np.ascontiguousarray(lg, dtype=np.float32)),
+                             _p(np.ascontiguousarray(idx, dtype=np.int32)), _p(out))
+    d = {"P": out[:L.E].copy()}
+    for i, n in enumerate(STAT_NAMES):
+        d[n] = float(out[L.E + i])
+    return d
 
 
 def combine(L: OrcLayer, yp, w, dest, shared=None, x=None) -> np.ndarray:

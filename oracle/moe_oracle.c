@@ -248,6 +248,55 @@ void orc_combine(const orc_layer* L, const float* yp, const double* w, const int
   }
 }
 
+/* ---- router statistics  [TD §4.2, §4.4, §9.1] ---------------------------- */
+
+void orc_router_stats(const orc_layer* L, const float* logits, const int32_t* idx, double* out) {
+  const int64_t T = L->T, E = L->E, K = L->K;
+  double* P = (double*)calloc((size_t)E, sizeof(double));
+  double* f = (double*)calloc((size_t)E, sizeof(double));
+  double z = 0.0;
+  for (int64_t t = 0; t < T; ++t) {
+    const float* l = logits + t * E;
+    double m = -INFINITY;
+    for (int64_t e = 0; e < E; ++e) m = fmax(m, (double)l[e]);
+    double se = 0.0;
+    for (int64_t e = 0; e < E; ++e) se += exp((double)l[e] - m);
+    const double lse = m + log(se);
+    z += lse * lse;
+    if (L->gate == ORC_GATE_SOFTMAX) {
+      for (int64_t e = 0; e < E; ++e) P[e] += exp((double)l[e] - m) / se;
+    } else {
+      double ss = 0.0;
+      for (int64_t e = 0; e < E; ++e) ss += 1.0 / (1.0 + exp(-(double)l[e]));
+      for (int64_t e = 0; e < E; ++e) P[e] += (1.0 / (1.0 + exp(-(double)l[e]))) / ss;
+    }
+  }
+  for (int64_t q = 0; q < T * K; ++q) f[idx[q]] += 1.0;
+  double bal = 0.0, fmaxv = 0.0, fmean = 0.0, hP = 0.0, hf = 0.0;
+  for (int64_t e = 0; e < E; ++e) {
+    P[e] /= (double)T;
+    f[e] /= (double)(T * K);
+    bal += f[e] * P[e];
+    fmaxv = fmax(fmaxv, f[e]);
+    fmean += f[e];
+    if (P[e] > 0) hP -= P[e] * log(P[e]);
+    if (f[e] > 0) hf -= f[e] * log(f[e]);
+  }
+  fmean /= (double)E;
+  double var = 0.0;
+  for (int64_t e = 0; e < E; ++e) var += (f[e] - fmean) * (f[e] - fmean);
+  var /= (double)E;
+  for (int64_t e = 0; e < E; ++e) out[e] = P[e];
+  out[E + 0] = (double)E * bal;
+  out[E + 1] = z / (double)T;
+  out[E + 2] = (double)E * fmaxv;
+  out[E + 3] = sqrt(var) / fmean;
+  out[E + 4] = hP;
+  out[E + 5] = hf;
+  free(P);
+  free(f);
+}
+
 /* ---- expert-choice routing  [TD §3.3] ------------------------------------ */
 
 void orc_expert_choice(const orc_layer* L, const float* logits, int64_t cap, int32_t* tok, double* g) {

@@ -115,6 +115,18 @@ void orc_combine(const orc_layer* L, const float* yp, const double* w, const int
  * used).  Requires cap <= T. */
 void orc_expert_choice(const orc_layer* L, const float* logits, int64_t cap, int32_t* tok, double* g);
 
+/* Router statistics  [TD §4.2 auxiliary losses; §4.4 load diagnostics; §9.1].
+ * Router distribution p[t][e]: softmax gate -> softmax of the logits;
+ * sigmoid gate -> sigmoid scores normalised over all E experts.
+ * f_e = counts_e / (T*K) (demand before capacity), P_e = mean_t p[t][e],
+ * lse_t = log sum_e exp(l[t][e]).
+ * out[e] = P_e (e < E), then out[E+0] = E * sum_e f_e P_e (Switch balance term
+ * without alpha), out[E+1] = mean_t lse_t^2 (router z-loss),
+ * out[E+2] = E * max_e f_e (load imbalance factor), out[E+3] = std(f)/mean(f)
+ * (population std), out[E+4] = -sum_e P_e ln P_e, out[E+5] = -sum_e f_e ln f_e
+ * (0 ln 0 = 0).  All in double. */
+void orc_router_stats(const orc_layer* L, const float* logits, const int32_t* idx, double* out);
+
 /* Number of OpenMP threads the oracle's parallel loops use. */
 int32_t orc_threads(void);
 

@@ -441,3 +441,47 @@ def test_combine_vs_direct_sum():
     np.testing.assert_allclose(got, want, rtol=1e-14, atol=1e-14)
     L0 = oracle.layer(T, d, 4, 8, K)
     assert np.all(oracle.combine(L0, yp, w, np.full(T * K, -1, np.int32)) == 0)
+
+
+# ---------------------------------------------------------- router statistics --
+
+def test_router_stats_vs_numpy():
+    """[TD §4.2, §4.4, §9.1] definitions recomputed with numpy / scipy."""
+    import scipy.stats
+    r = rng(15)
+    for gate, K in ((oracle.GATE_SOFTMAX, 2), (oracle.GATE_SIGMOID, 3)):
+        T, E = 200, 12
+        lg = (2 * r.standard_normal((T, E))).astype(np.float32)
+        L = oracle.layer(T, 4, 4, E, K, gate=gate)
+        idx, _, _ = oracle.select(L, lg)
+        st = oracle.router_stats(L, lg, idx)
+        l64 = lg.astype(np.float64)
+        if gate == oracle.GATE_SOFTMAX:
+            p = scipy.special.softmax(l64, axis=1)
+        else:
+            s = scipy.special.expit(l64)
+            p = s / s.sum(1, keepdims=True)
+        P = p.mean(0)
+        f = np.bincount(idx.reshape(-1), minlength=E) / (T * K)
+        np.testing.assert_allclose(st["P"], P, rtol=1e-12)
+        assert abs(st["balance"] - E * np.sum(f * P)) < 1e-12
+        assert abs(st["z_loss"] - np.mean(scipy.special.logsumexp(l64, axis=1) ** 2)) < 1e-10
+        assert abs(st["lif"] - E * f.max()) < 1e-12
+        assert abs(st["cv"] - f.std() / f.mean()) < 1e-12
+        assert abs(st["entropy_p"] - scipy.stats.entropy(P)) < 1e-12
+        assert abs(st["entropy_f"] - scipy.stats.entropy(f)) < 1e-12
+
+
+def test_router_stats_balanced_optimum():
+    """Equal logits: P_i = f_i = 1/N is the balanced optimum of the Switch
+    loss ([TD §4.2]); the balance term is then exactly 1, LIF = 1, CV = 0 and
+    both entropies are ln N."""
+    T, E, K = 64, 8, 1
+    lg = np.zeros((T, E), np.float32)
+    L = oracle.layer(T, 4, 4, E, K)
+    idx = (np.arange(T) % E).astype(np.int32).reshape(T, 1)  # a balanced assignment
+    st = oracle.router_stats(L, lg, idx)
+    np.testing.assert_allclose(st["P"], 1 / E, rtol=1e-15)
+    assert abs(st["balance"] - 1) < 1e-14 and abs(st["lif"] - 1) < 1e-14 and abs(st["cv"]) < 1e-14
+    assert abs(st["entropy_p"] - math.log(E)) < 1e-14 and abs(st["entropy_f"] - math.log(E)) < 1e-14
+    assert abs(st["z_loss"] - math.log(E) ** 2) < 1e-12
