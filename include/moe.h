@@ -70,7 +70,35 @@ enum {
   MOE_F_LOGITS_IN = 4u,
   /* moe_route / moe_forward read the caller's Top-K choice from
    * routing->topk_idx and routing->topk_w and skip logits and gate. */
-  MOE_F_TOPK_IN = 8u
+  MOE_F_TOPK_IN = 8u,
+  /* moe_route / moe_forward also write the router statistics to
+   * routing->stats (see below); not with MOE_F_TOPK_IN. */
+  MOE_F_STATS = 16u
+};
+
+/* Router statistics, written to routing->stats (E + MOE_N_STATS doubles)
+ * with MOE_F_STATS [TD §4.2 auxiliary losses; TD §4.4 load diagnostics].
+ * p[t][e] is the router distribution: the softmax of the logits (softmax
+ * gate) or the sigmoid scores normalised over all E experts (sigmoid gate).
+ * f_e = counts[e] / (T*K), the share of assignments each expert is asked to
+ * take before capacity (for K = 1 the argmax fraction of the Switch loss;
+ * E * f_e is DeepSeek's N'/(K'T) count).  lse_t = log sum_e exp(logit[t][e]).
+ *   stats[e], e < E       P_e = (1/T) sum_t p[t][e]
+ *   stats[E + BALANCE]    E * sum_e f_e P_e   (Switch / expert-balance term without alpha)
+ *   stats[E + Z_LOSS]     (1/T) sum_t lse_t^2 (router z-loss)
+ *   stats[E + LIF]        E * max_e f_e       (load imbalance factor, 1 = balanced)
+ *   stats[E + CV]         std(f) / mean(f)    (population std; 0 = balanced)
+ *   stats[E + ENTROPY_P]  -sum_e P_e ln P_e   (router entropy)
+ *   stats[E + ENTROPY_F]  -sum_e f_e ln f_e   (entropy of the load)
+ * Sums are taken in double in a fixed order.  Nothing is written for T = 0. */
+enum {
+  MOE_STAT_BALANCE = 0,
+  MOE_STAT_Z_LOSS = 1,
+  MOE_STAT_LIF = 2,
+  MOE_STAT_CV = 3,
+  MOE_STAT_ENTROPY_P = 4,
+  MOE_STAT_ENTROPY_F = 5,
+  MOE_N_STATS = 6
 };
 
 /* Layer description.  T = tokens, d = d_model, F = d_ff, E = n_experts,
@@ -108,6 +136,7 @@ typedef struct moe_routing {
   int32_t* dest;     /* [T*K]   row of assignment f = t*K + k in xp / yp, or -1 if dropped */
   int32_t* row_src;  /* [T*K]   assignment f held by row r (r < R); rows >= R are not written */
   uint8_t* dropped;  /* [T*K]   1 if assignment f was dropped for capacity */
+  double* stats;     /* [E + MOE_N_STATS] router statistics; used only with MOE_F_STATS */
 } moe_routing;
 
 /* Bytes of workspace any entry point needs for `cfg` (the same figure is
@@ -134,9 +163,10 @@ moe_status moe_max_rows(const moe_config* cfg, int64_t* rows);
  *             selection and weights)
  * sel_bias:   device, [E] fp32, nullable; sigmoid gate only; enters the
  *             selection key, never the weights
- * r:          every pointer required.  With MOE_F_TOPK_IN, r->logits is not
- *             touched and topk_idx / topk_w are inputs (idx in [0, E),
- *             distinct per token, not checked on the device).
+ * r:          every pointer required (r->stats only with MOE_F_STATS).  With
+ *             MOE_F_TOPK_IN, r->logits is not touched and topk_idx / topk_w
+ *             are inputs (idx in [0, E), distinct per token, not checked on
+ *             the device).
  */
 moe_status moe_route(const moe_config* cfg, const void* x, const float* Wg, const float* logit_bias,
                      const float* sel_bias, const moe_routing* r, void* ws, size_t ws_bytes, moe_stream_t stream);
@@ -179,7 +209,8 @@ moe_status moe_combine(const moe_config* cfg, const float* yp, const moe_routing
  * sequence with no host synchronisation.
  * r: nullable; when NULL the routing arrays live in the workspace.  When
  * given, the routing results are written there (and MOE_F_LOGITS_IN /
- * MOE_F_TOPK_IN inputs read from there).
+ * MOE_F_TOPK_IN inputs read from there).  Required with MOE_F_*_IN and
+ * MOE_F_STATS.
  * Ws1/Ws3/Ws2: required iff n_shared == 1.  y: device [T, d] out_dtype. */
 moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, const float* logit_bias,
                        const float* sel_bias, const void* W1, const void* W3, const void* W2, const void* Ws1,

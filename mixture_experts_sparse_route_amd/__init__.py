@@ -22,7 +22,9 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_GATE_SOFTMAX, MOE_GATE_SIGMOID = 0, 1
-MOE_F_RENORM, MOE_F_RESIDUAL, MOE_F_LOGITS_IN, MOE_F_TOPK_IN = 1, 2, 4, 8
+MOE_F_RENORM, MOE_F_RESIDUAL, MOE_F_LOGITS_IN, MOE_F_TOPK_IN, MOE_F_STATS = 1, 2, 4, 8, 16
+# router statistics after the E per-expert mean probabilities (moe.h, MOE_STAT_*)
+STAT_NAMES = ("balance", "z_loss", "lif", "cv", "entropy_p", "entropy_f")
 
 KERNEL_NAMES = ["router_logits", "router_topk", "route_scan", "route_scatter", "dispatch", "ffn_tiles",
                 "gemm_gate_up", "gemm_down", "combine"]
@@ -46,7 +48,7 @@ class MoeConfig(ctypes.Structure):
 
 class MoeRouting(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("logits", "topk_idx", "topk_w", "counts", "offsets", "dest", "row_src", "dropped")]
+                ("logits", "topk_idx", "topk_w", "counts", "offsets", "dest", "row_src", "dropped", "stats")]
 
 
 _lib = None
@@ -120,10 +122,12 @@ class LayerSpec:
     out_dtype: Optional[str] = None  # dtype of y; None = dtype ("f32" allowed for a bf16 layer)
     logits_in: bool = False
     topk_in: bool = False
+    stats: bool = False
 
     def config(self) -> MoeConfig:
         flags = ((MOE_F_RENORM if self.renorm else 0) | (MOE_F_RESIDUAL if self.residual else 0)
-                 | (MOE_F_LOGITS_IN if self.logits_in else 0) | (MOE_F_TOPK_IN if self.topk_in else 0))
+                 | (MOE_F_LOGITS_IN if self.logits_in else 0) | (MOE_F_TOPK_IN if self.topk_in else 0)
+                 | (MOE_F_STATS if self.stats else 0))
         dt = MOE_BF16 if self.dtype == "bf16" else MOE_F32
         ot = dt if self.out_dtype is None else (MOE_BF16 if self.out_dtype == "bf16" else MOE_F32)
         return MoeConfig(self.tokens, self.d_model, self.d_ff, self.n_experts, self.top_k, self.gate, flags,
@@ -183,10 +187,23 @@ class Routing:
         self.dest = torch.empty((T * K,), dtype=torch.int32, device=device)
         self.row_src = torch.empty((max(T * K, 1),), dtype=torch.int32, device=device)
         self.dropped = torch.empty((T * K,), dtype=torch.uint8, device=device)
+        self.stats = torch.empty((E + len(STAT_NAMES),), dtype=torch.float64, device=device)
 
     def struct(self) -> MoeRouting:
         return MoeRouting(*(_ptr(getattr(self, n)) for n in
-                            ("logits", "topk_idx", "topk_w", "counts", "offsets", "dest", "row_src", "dropped")))
+                            ("logits", "topk_idx", "topk_w", "counts", "offsets", "dest", "row_src", "dropped",
+                             "stats")))
+
+    def statistics(self) -> dict:
+        """The router statistics written with MOE_F_STATS, as host floats:
+        {'P': per-expert mean probability [E], 'balance', 'z_loss', 'lif',
+        'cv', 'entropy_p', 'entropy_f'}."""
+        v = self.stats.cpu().numpy()
+        E = v.shape[0] - len(STAT_NAMES)
+        d = {"P": v[:E].copy()}
+        for i, n in enumerate(STAT_NAMES):
+            d[n] = float(v[E + i])
+        return d
 
 
 def alloc_workspace(spec, device="cuda"):

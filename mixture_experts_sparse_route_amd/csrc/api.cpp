@@ -38,12 +38,13 @@ moe_status hip_fail(hipError_t e, const char* where) {
     if (e_ != hipSuccess) return hip_fail(e_, #call);      \
   } while (0)
 
-constexpr uint32_t kKnownFlags = MOE_F_RENORM | MOE_F_RESIDUAL | MOE_F_LOGITS_IN | MOE_F_TOPK_IN;
+constexpr uint32_t kKnownFlags = MOE_F_RENORM | MOE_F_RESIDUAL | MOE_F_LOGITS_IN | MOE_F_TOPK_IN | MOE_F_STATS;
 
 // Everything the launches need, derived from a validated config.
 struct Shape {
   bool bf16;
   bool out_bf16;
+  bool stats;  // router statistics requested
   int64_t T, d, F, E, K, S, Fs;
   int64_t cap;       // -1: no limit
   int64_t max_rows;  // upper bound of kept rows R
@@ -62,6 +63,8 @@ moe_status validate(const moe_config* c, Shape* sh) {
   if (c->gate != MOE_GATE_SOFTMAX && c->gate != MOE_GATE_SIGMOID)
     return fail(MOE_ERR_INVALID_ARG, "unknown gate %d", (int)c->gate);
   if (c->flags & ~kKnownFlags) return fail(MOE_ERR_INVALID_ARG, "unknown flag bits 0x%x", c->flags & ~kKnownFlags);
+  if ((c->flags & MOE_F_STATS) && (c->flags & MOE_F_TOPK_IN))
+    return fail(MOE_ERR_INVALID_ARG, "MOE_F_STATS needs logits; it cannot be combined with MOE_F_TOPK_IN");
   if (!std::isfinite(c->capacity_factor)) return fail(MOE_ERR_INVALID_ARG, "capacity_factor is not finite");
   if (c->n_shared < 0 || c->n_shared > 1) return fail(MOE_ERR_INVALID_ARG, "n_shared must be 0 or 1");
   if (c->n_shared == 1 && c->d_ff_shared < 1) return fail(MOE_ERR_INVALID_ARG, "d_ff_shared must be >= 1");
@@ -93,6 +96,7 @@ moe_status validate(const moe_config* c, Shape* sh) {
   }
   sh->bf16 = bf16;
   sh->out_bf16 = c->out_dtype == MOE_BF16;
+  sh->stats = c->flags & MOE_F_STATS;
   sh->T = T;
   sh->d = d;
   sh->F = F;
@@ -109,7 +113,7 @@ moe_status validate(const moe_config* c, Shape* sh) {
 
 // ---- workspace layout ----
 struct Layout {
-  size_t router_part, blk_count, blk_base, tab_up, tab_down, counts, sh_range, sh_tab_up, sh_tab_down, sh_counts;
+  size_t router_part, blk_count, blk_base, blk_P, blk_z, tab_up, tab_down, counts, sh_range, sh_tab_up, sh_tab_down, sh_counts;
   size_t h, xp, yp, sh_h, sh_out;
   size_t r_logits, r_idx, r_w, r_counts, r_offsets, r_dest, r_row_src, r_dropped;
   size_t total;
@@ -128,6 +132,8 @@ Layout layout(const Shape& s) {
   L.router_part = take(S > 1 ? (size_t)S * s.T * s.E * 4 : 0);
   L.blk_count = take((size_t)(s.n_chunks * s.E) * 4);
   L.blk_base = take((size_t)(s.n_chunks * s.E) * 4);
+  L.blk_P = take(s.stats ? (size_t)(s.n_chunks * s.E) * 4 : 0);
+  L.blk_z = take(s.stats ? (size_t)s.n_chunks * 4 : 0);
   L.tab_up = take((size_t)ffn_table_entries(s.bf16, s.max_rows, s.E, s.F, true) * 16);
   L.tab_down = take((size_t)ffn_table_entries(s.bf16, s.max_rows, s.E, s.d, false) * 16);
   L.counts = take(2 * 4);
@@ -166,11 +172,12 @@ T* at(void* ws, size_t off) {
   return (T*)((char*)ws + off);
 }
 
-moe_status check_routing(const moe_routing* r, bool need_logits) {
+moe_status check_routing(const moe_routing* r, bool need_logits, bool need_stats) {
   if (!r) return fail(MOE_ERR_INVALID_ARG, "routing is NULL");
   if ((need_logits && !r->logits) || !r->topk_idx || !r->topk_w || !r->counts || !r->offsets || !r->dest ||
       !r->row_src || !r->dropped)
     return fail(MOE_ERR_INVALID_ARG, "a routing pointer is NULL");
+  if (need_stats && !r->stats) return fail(MOE_ERR_INVALID_ARG, "MOE_F_STATS needs routing->stats");
   return MOE_OK;
 }
 
@@ -181,6 +188,8 @@ moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const 
   int32_t* blk_base = at<int32_t>(ws, L.blk_base);
   const bool topk_in = c->flags & MOE_F_TOPK_IN;
   const float* sb = c->gate == MOE_GATE_SIGMOID ? sel_bias : nullptr;
+  float* blk_P = s.stats ? at<float>(ws, L.blk_P) : nullptr;
+  float* blk_z = s.stats ? at<float>(ws, L.blk_z) : nullptr;
   if (!topk_in) {
     int S = 1;
     float* part = at<float>(ws, L.router_part);
@@ -188,13 +197,14 @@ moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const 
       S = router_splits(s.T, s.d, s.E, s.bf16);
       MOE_HIP(launch_router_logits(s.bf16, x, Wg, logit_bias, r.logits, part, s.T, s.d, s.E, st));
     }
-    MOE_HIP(launch_router_topk(r.logits, part, S, logit_bias, sb, r.topk_idx, r.topk_w, blk_count, s.T, s.E, s.K,
-                               c->gate, c->flags & MOE_F_RENORM, false, st));
+    MOE_HIP(launch_router_topk(r.logits, part, S, logit_bias, sb, r.topk_idx, r.topk_w, blk_count, blk_P, blk_z,
+                               s.T, s.E, s.K, c->gate, c->flags & MOE_F_RENORM, false, st));
   } else {
-    MOE_HIP(launch_router_topk(nullptr, nullptr, 1, nullptr, nullptr, r.topk_idx, nullptr, blk_count, s.T, s.E, s.K,
-                               c->gate, false, true, st));
+    MOE_HIP(launch_router_topk(nullptr, nullptr, 1, nullptr, nullptr, r.topk_idx, nullptr, blk_count, nullptr,
+                               nullptr, s.T, s.E, s.K, c->gate, false, true, st));
   }
-  MOE_HIP(launch_route_scan(blk_count, blk_base, r.counts, r.offsets, s.n_chunks, s.E, s.cap, st));
+  MOE_HIP(launch_route_scan(blk_count, blk_base, r.counts, r.offsets, s.n_chunks, s.E, s.cap, blk_P, blk_z,
+                            s.stats ? r.stats : nullptr, s.T, s.K, st));
   MOE_HIP(launch_route_scatter(r.topk_idx, blk_base, r.offsets, r.dest, r.row_src, r.dropped, s.T, s.K, s.E, s.cap,
                                st));
   return MOE_OK;
@@ -304,7 +314,7 @@ moe_status moe_route(const moe_config* cfg, const void* x, const float* Wg, cons
   if (st != MOE_OK) return st;
   const bool topk_in = cfg->flags & MOE_F_TOPK_IN;
   const bool logits_in = cfg->flags & MOE_F_LOGITS_IN;
-  if ((st = check_routing(r, !topk_in)) != MOE_OK) return st;
+  if ((st = check_routing(r, !topk_in, s.stats)) != MOE_OK) return st;
   if (!topk_in && !logits_in && (!x || !Wg)) return fail(MOE_ERR_INVALID_ARG, "x and Wg are required");
   Layout L;
   if ((st = check_ws(s, ws, ws_bytes, &L)) != MOE_OK) return st;
@@ -369,8 +379,9 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, co
   if (!x || !y || !W1 || !W3 || !W2) return fail(MOE_ERR_INVALID_ARG, "x, y, W1, W3, W2 are required");
   if (!topk_in && !logits_in && !Wg) return fail(MOE_ERR_INVALID_ARG, "Wg is required");
   if (s.S && (!Ws1 || !Ws3 || !Ws2)) return fail(MOE_ERR_INVALID_ARG, "shared expert weights are required");
-  if ((topk_in || logits_in) && !r) return fail(MOE_ERR_INVALID_ARG, "MOE_F_*_IN needs the routing arrays");
-  if (r && (st = check_routing(r, !topk_in)) != MOE_OK) return st;
+  if ((topk_in || logits_in || s.stats) && !r)
+    return fail(MOE_ERR_INVALID_ARG, "MOE_F_*_IN and MOE_F_STATS need the routing arrays");
+  if (r && (st = check_routing(r, !topk_in, s.stats)) != MOE_OK) return st;
   Layout L;
   if ((st = check_ws(s, ws, ws_bytes, &L)) != MOE_OK) return st;
   if (s.T == 0) return MOE_OK;
@@ -387,6 +398,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, co
     rr.dest = at<int32_t>(ws, L.r_dest);
     rr.row_src = at<int32_t>(ws, L.r_row_src);
     rr.dropped = at<uint8_t>(ws, L.r_dropped);
+    rr.stats = nullptr;
   }
   if ((st = do_route(cfg, s, L, x, Wg, logit_bias, sel_bias, rr, ws, hs)) != MOE_OK) return st;
   void* xp = at<void>(ws, L.xp);

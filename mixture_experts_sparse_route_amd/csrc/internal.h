@@ -37,13 +37,18 @@ hipError_t launch_router_logits(bool bf16, const void* x, const float* Wg, const
 // S > 1: logits = sum of the S slices of `part` (in order) + bias, written to
 // `logits` before selection; S == 1: `logits` is read as is.
 // topk_in: idx is an input; only the per-chunk histogram is produced.
+// blk_P / blk_z non-null (never with topk_in): per-chunk router-distribution
+// sums [n_chunks, E] and logsumexp^2 sums [n_chunks] for the statistics.
 hipError_t launch_router_topk(float* logits, const float* part, int S, const float* bias, const float* sel_bias,
-                              int32_t* idx, float* w, int32_t* blk_count, int64_t T, int64_t E, int64_t K, int gate,
-                              bool renorm, bool topk_in, hipStream_t s);
+                              int32_t* idx, float* w, int32_t* blk_count, float* blk_P, float* blk_z, int64_t T,
+                              int64_t E, int64_t K, int gate, bool renorm, bool topk_in, hipStream_t s);
 
 // ---- permutation (a4) and dispatch (a5) ----
+// stats non-null: also folds blk_P / blk_z into the router statistics
+// (E + 6 doubles).
 hipError_t launch_route_scan(const int32_t* blk_count, int32_t* blk_base, int32_t* counts, int32_t* offsets,
-                             int64_t n_chunks, int64_t E, int64_t cap, hipStream_t s);
+                             int64_t n_chunks, int64_t E, int64_t cap, const float* blk_P, const float* blk_z,
+                             double* stats, int64_t T, int64_t K, hipStream_t s);
 hipError_t launch_route_scatter(const int32_t* idx, const int32_t* blk_base, const int32_t* offsets, int32_t* dest,
                                 int32_t* row_src, uint8_t* dropped, int64_t T, int64_t K, int64_t E, int64_t cap,
                                 hipStream_t s);

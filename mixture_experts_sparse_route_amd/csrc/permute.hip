@@ -17,20 +17,57 @@ namespace {
 // over chunks b' < b; counts[e] = total demand; offsets = exclusive scan of
 // min(counts, cap) with offsets[E] = R.  S threads share each expert's chunk
 // range.
+//
+// With `stats` (router statistics, [TD §4.2 auxiliary losses, §4.4 load
+// diagnostics]) the kernel also folds the Top-K kernel's per-chunk sums,
+// in double and in chunk order, into
+//   stats[e]   = P_e = (1/T) sum_t p[t][e]
+//   stats[E+0] = E * sum_e f_e P_e        (Switch balance term, no alpha)
+//   stats[E+1] = (1/T) sum_t lse_t^2      (router z-loss)
+//   stats[E+2] = E * max_e f_e            (load imbalance factor)
+//   stats[E+3] = std(f) / mean(f)         (population std; mean f = 1/E)
+//   stats[E+4] = -sum_e P_e ln P_e        (router entropy)
+//   stats[E+5] = -sum_e f_e ln f_e
+// where f_e = counts[e] / (T*K) is the demand before capacity.
+__device__ __forceinline__ double wave_sum(double v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ double wave_max(double v) {
+  for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
 __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restrict__ blk_count,
                                                           int32_t* __restrict__ blk_base, int32_t* __restrict__ counts,
                                                           int32_t* __restrict__ offsets, int NB, int E, int Epad,
-                                                          int cap) {
+                                                          int cap, const float* __restrict__ blk_P,
+                                                          const float* __restrict__ blk_z, double* __restrict__ stats,
+                                                          int T, int K) {
   __shared__ int part[1024];
   __shared__ int kept[1024];
+  __shared__ int total[1024];
+  __shared__ double dpart[1024];
+  __shared__ double red[7][16];
   const int S = 1024 / Epad;
   const int e = threadIdx.x % Epad, sub = threadIdx.x / Epad;
   const int per = (NB + S - 1) / S;
   const int b0 = min(NB, sub * per), b1 = min(NB, b0 + per);
   int sum = 0;
-  if (e < E)
-    for (int b = b0; b < b1; ++b) sum += blk_count[(int64_t)b * E + e];
+  double psum = 0.0;
+  if (e < E) {
+    if (stats) {
+      for (int b = b0; b < b1; ++b) {
+        sum += blk_count[(int64_t)b * E + e];
+        psum += (double)blk_P[(int64_t)b * E + e];
+      }
+    } else {
+      for (int b = b0; b < b1; ++b) sum += blk_count[(int64_t)b * E + e];
+    }
+  }
   part[sub * Epad + e] = sum;
+  dpart[sub * Epad + e] = psum;
   __syncthreads();
   if (e < E) {
     int run = 0;
@@ -42,11 +79,51 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
     if (sub == S - 1) {
       counts[e] = run;
       kept[e] = min(run, cap);
+      total[e] = run;
     }
   } else if (sub == S - 1) {
     kept[e] = 0;
   }
   __syncthreads();
+  if (stats) {
+    // thread i < E: expert i; every thread adds the chunks' z sums i, i+1024, ...
+    const int i = threadIdx.x, wave = i >> 6, lane = i & 63;
+    double z = 0.0;
+    for (int b = i; b < NB; b += 1024) z += (double)blk_z[b];
+    double v[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    if (i < E) {
+      double P = 0.0;
+      for (int q = 0; q < S; ++q) P += dpart[q * Epad + i];
+      P /= (double)T;
+      const double f = (double)total[i] / ((double)T * (double)K);
+      const double df = f - 1.0 / (double)E;
+      stats[i] = P;
+      v[0] = f * P;
+      v[1] = f;
+      v[2] = df * df;
+      v[3] = P > 0.0 ? -P * log(P) : 0.0;
+      v[4] = f > 0.0 ? -f * log(f) : 0.0;
+    }
+    v[5] = z;
+#pragma unroll
+    for (int q = 0; q < 6; ++q) {
+      const double r = q == 1 ? wave_max(v[q]) : wave_sum(v[q]);
+      if (lane == 0) red[q][wave] = r;
+    }
+    __syncthreads();
+    if (i == 0) {
+      double a[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+      for (int w = 0; w < 16; ++w)
+        for (int q = 0; q < 6; ++q) a[q] = q == 1 ? fmax(a[q], red[q][w]) : a[q] + red[q][w];
+      const double En = (double)E;
+      stats[E + 0] = En * a[0];
+      stats[E + 1] = a[5] / (double)T;
+      stats[E + 2] = En * a[1];
+      stats[E + 3] = sqrt(a[2] / En) * En;
+      stats[E + 4] = a[3];
+      stats[E + 5] = a[4];
+    }
+  }
   // inclusive Hillis-Steele scan of kept[0 .. Epad) with the first Epad threads
   for (int off = 1; off < Epad; off <<= 1) {
     int v = 0;
@@ -193,12 +270,14 @@ __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t* __restri
 }  // namespace
 
 hipError_t launch_route_scan(const int32_t* blk_count, int32_t* blk_base, int32_t* counts, int32_t* offsets,
-                             int64_t n_chunks, int64_t E, int64_t cap, hipStream_t s) {
+                             int64_t n_chunks, int64_t E, int64_t cap, const float* blk_P, const float* blk_z,
+                             double* stats, int64_t T, int64_t K, hipStream_t s) {
   int Epad = 1;
   while (Epad < E) Epad <<= 1;
   const int capi = cap < 0 || cap > INT_MAX ? INT_MAX : (int)cap;
   prof_begin(K_ROUTE_SCAN, s);
-  route_scan_kernel<<<1, 1024, 0, s>>>(blk_count, blk_base, counts, offsets, (int)n_chunks, (int)E, Epad, capi);
+  route_scan_kernel<<<1, 1024, 0, s>>>(blk_count, blk_base, counts, offsets, (int)n_chunks, (int)E, Epad, capi,
+                                       blk_P, blk_z, stats, (int)T, (int)K);
   prof_end(K_ROUTE_SCAN, s);
   return hipGetLastError();
 }

@@ -224,15 +224,35 @@ __device__ __forceinline__ float group_sum(float v, int L) {
   return v;
 }
 
-template <int P>
+__device__ __forceinline__ float group_maxf(float v, int L) {
+  for (int off = L >> 1; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// With STATS the kernel also writes, per workgroup b, the router distribution
+// summed over its tokens, blk_P[b][e] = sum_t p[t][e], and blk_z[b] =
+// sum_t lse_t^2 with lse_t = log sum_e exp(logit[t][e])  ([TD §4.2] P_i and
+// the z-loss).  p is the softmax over all E logits (softmax gate) or the
+// sigmoid scores normalised over all E experts (sigmoid gate).  Each lane
+// keeps its running sums in registers; the tokens of a wave are then added
+// by a butterfly and the four waves in wave order, so the sums have a fixed
+// order.
+template <int P, bool STATS>
 __global__ __launch_bounds__(256) void router_topk_kernel(float* __restrict__ logits, const float* __restrict__ part,
                                                           int S, const float* __restrict__ bias,
                                                           const float* __restrict__ sel_bias, int32_t* __restrict__ idx,
-                                                          float* __restrict__ w, int32_t* __restrict__ blk_count, int T,
+                                                          float* __restrict__ w, int32_t* __restrict__ blk_count,
+                                                          float* __restrict__ blk_P, float* __restrict__ blk_z, int T,
                                                           int E, int K, int L, int gate, int renorm, int topk_in) {
   __shared__ int hist[1024];
+  __shared__ float wsum[STATS ? 4 : 1][STATS ? 1024 : 1];
+  __shared__ float wz[4];
   for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
   __syncthreads();
+  float pacc[P];
+  float zacc = 0.0f;
+#pragma unroll
+  for (int p = 0; p < P; ++p) pacc[p] = 0.0f;
 
   const int t_begin = blockIdx.x * kTopkTokens;
   const int t_end = min(T, t_begin + kTopkTokens);
@@ -250,12 +270,13 @@ __global__ __launch_bounds__(256) void router_topk_kernel(float* __restrict__ lo
       const bool valid = t < t_end;
       const float* lt = logits + (int64_t)(valid ? t : t_begin) * E;
       uint64_t pk[P];
-      float lv[P];
+      float lv[P], sv[P];
 #pragma unroll
       for (int p = 0; p < P; ++p) {
         const int e = ll + L * p;
         pk[p] = 0;
         lv[p] = -INFINITY;
+        sv[p] = 0.0f;
         if (valid && e < E) {
           float l;
           if (S > 1) {
@@ -274,6 +295,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(float* __restrict__ lo
           } else {
             // sigmoid formed in double and rounded once, then the selection bias
             const float s = (float)(1.0 / (1.0 + exp(-(double)l)));
+            sv[p] = s;
             key = s + (sel_bias ? sel_bias[e] : 0.0f);
           }
           pk[p] = pack_key(key, e);
@@ -305,13 +327,18 @@ __global__ __launch_bounds__(256) void router_topk_kernel(float* __restrict__ lo
       }
       // weights
       float contrib = 0.0f, mine = 0.0f;
+      float top = 0.0f, z_all = 1.0f;
+      float ez[P];
       if (gate == 0) {
         // p_e = exp(l_e - m) / sum; m = the largest logit = the first choice
-        const float top = __shfl(my_l, slot * L, 64);
+        top = __shfl(my_l, slot * L, 64);
         float zs = 0.0f;
 #pragma unroll
-        for (int p = 0; p < P; ++p) zs += (lv[p] == -INFINITY) ? 0.0f : expf(lv[p] - top);
-        const float z_all = group_sum(zs, L);
+        for (int p = 0; p < P; ++p) {
+          ez[p] = (lv[p] == -INFINITY) ? 0.0f : expf(lv[p] - top);
+          zs += ez[p];
+        }
+        z_all = group_sum(zs, L);
         if (my_e >= 0) mine = expf(my_l - top);
         contrib = mine;
         const float z_sel = group_sum(contrib, L);
@@ -328,10 +355,59 @@ __global__ __launch_bounds__(256) void router_topk_kernel(float* __restrict__ lo
         idx[(int64_t)t * K + ll] = my_e;
         atomicAdd(&hist[my_e], 1);
       }
+      if constexpr (STATS) {
+        float lse;
+        if (gate == 0) {
+          lse = top + logf(z_all);
+#pragma unroll
+          for (int p = 0; p < P; ++p) ez[p] = ez[p] / z_all;
+        } else {
+          float ss = 0.0f, mx = -INFINITY;
+#pragma unroll
+          for (int p = 0; p < P; ++p) {
+            ss += sv[p];
+            mx = fmaxf(mx, lv[p]);
+          }
+          ss = group_sum(ss, L);
+          mx = group_maxf(mx, L);
+          float es = 0.0f;
+#pragma unroll
+          for (int p = 0; p < P; ++p) es += (lv[p] == -INFINITY) ? 0.0f : expf(lv[p] - mx);
+          lse = mx + logf(group_sum(es, L));
+#pragma unroll
+          for (int p = 0; p < P; ++p) ez[p] = sv[p] / ss;
+        }
+        if (valid) {
+#pragma unroll
+          for (int p = 0; p < P; ++p)
+            if (ll + L * p < E) pacc[p] += ez[p];
+          if (ll == 0) zacc += lse * lse;
+        }
+      }
     }
   }
+  if constexpr (STATS) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // add the wave's token slots (lanes with equal ll) and its z terms
+    for (int off = 64 >> 1; off > 0; off >>= 1) zacc += __shfl_xor(zacc, off, 64);
+    for (int off = L; off < 64; off <<= 1) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) pacc[p] += __shfl_xor(pacc[p], off, 64);
+    }
+    if (lane < L) {
+#pragma unroll
+      for (int p = 0; p < P; ++p)
+        if (lane + L * p < E) wsum[wave][lane + L * p] = pacc[p];
+    }
+    if (lane == 0) wz[wave] = zacc;
+  }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) blk_count[(int64_t)blockIdx.x * E + e] = hist[e];
+  for (int e = threadIdx.x; e < E; e += 256) {
+    blk_count[(int64_t)blockIdx.x * E + e] = hist[e];
+    if constexpr (STATS) blk_P[(int64_t)blockIdx.x * E + e] = ((wsum[0][e] + wsum[1][e]) + wsum[2][e]) + wsum[3][e];
+  }
+  if constexpr (STATS)
+    if (threadIdx.x == 0) blk_z[blockIdx.x] = ((wz[0] + wz[1]) + wz[2]) + wz[3];
 }
 
 }  // namespace
@@ -366,16 +442,24 @@ hipError_t launch_router_logits(bool bf16, const void* x, const float* Wg, const
 }
 
 hipError_t launch_router_topk(float* logits, const float* part, int S, const float* bias, const float* sel_bias,
-                              int32_t* idx, float* w, int32_t* blk_count, int64_t T, int64_t E, int64_t K, int gate,
-                              bool renorm, bool topk_in, hipStream_t s) {
+                              int32_t* idx, float* w, int32_t* blk_count, float* blk_P, float* blk_z, int64_t T,
+                              int64_t E, int64_t K, int gate, bool renorm, bool topk_in, hipStream_t s) {
   int L = 1;
   while (L < E && L < 64) L <<= 1;
   const int P = (int)((E + L - 1) / L);
   const unsigned nb = (unsigned)((T + kTopkTokens - 1) / kTopkTokens);
   prof_begin(K_ROUTER_TOPK, s);
-#define MOE_TOPK(PP)                                                                                          \
-  router_topk_kernel<PP><<<nb, 256, 0, s>>>(logits, part, S, bias, sel_bias, idx, w, blk_count, (int)T, (int)E,     \
-                                            (int)K, L, gate, renorm ? 1 : 0, topk_in ? 1 : 0)
+#define MOE_TOPK(PP)                                                                                             \
+  do {                                                                                                           \
+    if (blk_P)                                                                                                   \
+      router_topk_kernel<PP, true><<<nb, 256, 0, s>>>(logits, part, S, bias, sel_bias, idx, w, blk_count, blk_P,  \
+                                                      blk_z, (int)T, (int)E, (int)K, L, gate, renorm ? 1 : 0,     \
+                                                      topk_in ? 1 : 0);                                           \
+    else                                                                                                         \
+      router_topk_kernel<PP, false><<<nb, 256, 0, s>>>(logits, part, S, bias, sel_bias, idx, w, blk_count,        \
+                                                       nullptr, nullptr, (int)T, (int)E, (int)K, L, gate,         \
+                                                       renorm ? 1 : 0, topk_in ? 1 : 0);                          \
+  } while (0)
   if (P <= 1)
     MOE_TOPK(1);
   else if (P <= 2)

@@ -69,13 +69,14 @@ class Case:
         self._route = None
 
     # ---------------------------------------------------------- GPU side --
-    def gpu_forward(self, residual=False, logits_in=None, topk_in=None, out_dtype=None):
+    def gpu_forward(self, residual=False, logits_in=None, topk_in=None, out_dtype=None, stats=False):
         """moe_forward through the C-ABI.  logits_in: fp32 [T, E] host array;
         topk_in: (idx int32 [T, K], w fp32 [T, K]) host arrays; out_dtype:
-        "f32" or "bf16" (default: the layer's dtype)."""
+        "f32" or "bf16" (default: the layer's dtype); stats: also write the
+        router statistics (Routing.statistics())."""
         wl = self.wl
         spec = spec_of(wl, residual=residual, logits_in=logits_in is not None, topk_in=topk_in is not None,
-                       out_dtype=out_dtype)
+                       out_dtype=out_dtype, stats=stats)
         r = moe.Routing(spec)
         if logits_in is not None:
             r.logits.copy_(torch.from_numpy(np.ascontiguousarray(logits_in, dtype=np.float32)))

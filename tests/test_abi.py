@@ -148,3 +148,30 @@ def test_zero_tokens_is_a_no_op(lib):
     assert lib.moe_combine(ctypes.byref(c), 8, ctypes.byref(r), None, None, 8, None) == moe.MOE_OK
     assert lib.moe_forward(ctypes.byref(c), 8, 8, None, None, 8, 8, 8, None, None, None, 8, None, 256, n,
                            None) == moe.MOE_OK
+
+
+def test_statistics_flag_validation(lib):
+    """MOE_F_STATS: needs logits (rejected with MOE_F_TOPK_IN), needs
+    routing->stats, and adds its per-chunk partial sums to the workspace."""
+    n = ctypes.c_size_t()
+    c = spec(stats=True, topk_in=True).config()
+    assert lib.moe_workspace_size(ctypes.byref(c), ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
+    assert b"MOE_F_STATS" in lib.moe_last_error()
+    assert moe.workspace_size(spec(stats=True, tokens=4096)) > moe.workspace_size(spec(tokens=4096))
+    c = spec(stats=True).config()
+    r = moe.MoeRouting(*([256] * 8), None)   # stats pointer missing
+    assert lib.moe_route(ctypes.byref(c), 8, 8, None, None, ctypes.byref(r), 256, 1 << 30, None) \
+        == moe.MOE_ERR_INVALID_ARG
+    assert b"stats" in lib.moe_last_error()
+    # moe_forward with statistics needs caller routing arrays
+    assert lib.moe_forward(ctypes.byref(c), 8, 8, None, None, 8, 8, 8, None, None, None, 8, None, 256, 1 << 30,
+                           None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_routing_struct_matches_the_header():
+    """moe_routing in moe.h: eight array pointers, then the statistics pointer."""
+    src = open(HEADER).read()
+    body = re.search(r"typedef struct moe_routing \{(.*?)\} moe_routing;", src, re.S).group(1)
+    names = re.findall(r"\*\s*(\w+);", body)
+    assert names == [f[0] for f in moe.MoeRouting._fields_]
+    assert ctypes.sizeof(moe.MoeRouting) == 8 * len(names)
