@@ -41,6 +41,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel in an untimed extra pass")
+    ap.add_argument("--stats", action="store_true", help="also compute the fused router statistics every step")
     return ap.parse_args()
 
 
@@ -137,7 +138,7 @@ def main():
     t_gen = time.perf_counter() - t_gen
     spec = moe.LayerSpec(tokens=wl.T, d_model=wl.d, d_ff=wl.F, n_experts=wl.E, top_k=wl.K, gate=wl.gate,
                          renorm=wl.renorm, capacity_factor=wl.capacity_factor, n_shared=wl.n_shared,
-                         d_ff_shared=wl.Fs, dtype=wl.dtype)
+                         d_ff_shared=wl.Fs, dtype=wl.dtype, stats=args.stats)
     ws, _ = moe.alloc_workspace(spec)
     r = moe.Routing(spec)
     y = torch.empty((wl.T, wl.d), dtype=torch.bfloat16 if wl.dtype == "bf16" else torch.float32, device="cuda")
@@ -236,7 +237,7 @@ def main():
         "config": {"workload": wl.name, "tokens": wl.T, "d_model": wl.d, "d_ff": wl.F, "n_experts": wl.E,
                    "top_k": wl.K, "gate": "sigmoid" if wl.gate else "softmax", "renorm": wl.renorm,
                    "capacity_factor": wl.capacity_factor, "n_shared": wl.n_shared, "d_ff_shared": wl.Fs,
-                   "parallelism": "single GPU"},
+                   "router_stats": args.stats, "parallelism": "single GPU"},
         "roofline": roof,
         "layer": {"tflops": round(layer_flops / (ms_per_step * 1e-3) / 1e12, 2),
                   "algorithmic_gbps": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),

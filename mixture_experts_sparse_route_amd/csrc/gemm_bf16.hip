@@ -290,7 +290,7 @@ __global__ __launch_bounds__(256, NS*(BM + BNB) * RB <= LDS_BYTES / 2 ? 2 : 1) v
 // (m-tile rows, weight-tile rows, LDS stages) compiled below.  The k-loop
 // needs K >= 32 * (NS - 1); the launchers check it.
 #define MOE_GEMM_CONFIGS(X) X(256, 256, 5) X(256, 256, 4) X(128, 256, 3) X(128, 256, 6) X(64, 256, 4) \
-  X(128, 128, 4) X(64, 128, 8) X(64, 128, 6)
+  X(128, 128, 4) X(128, 128, 3) X(64, 128, 8) X(64, 128, 6) X(64, 128, 3)
 
 bool gemm_bf16_has_config(int bm, int bnb, int ns) {
 #define MOE_HAS(B, W, N) \

@@ -125,6 +125,11 @@ FfnPlan ffn_plan(bool bf16, int64_t max_rows, int64_t n_groups, int64_t F, int64
       p.ns_down = 4;
     }
   }
+  // A ring deeper than the reduction dimension's k-steps + 1 cannot be
+  // filled: short reductions (d or F of 64 .. 160) take the 3-stage variant
+  // of the same tile shape (every bf16 size is at least 2 k-steps).
+  if (d / 32 < p.ns_up - 1) p.ns_up = 3;
+  if (F / 32 < p.ns_down - 1) p.ns_down = 3;
   // overrides for tuning: MOE_GEMM_BM, MOE_GEMM_{BNB,NS}_{UP,DOWN}, MOE_GEMM_WGS
   const FfnPlan def = p;
   p.bm = env_int("MOE_GEMM_BM", p.bm);

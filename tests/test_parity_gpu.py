@@ -122,6 +122,9 @@ SMALL = {
     "single_expert": workload("mixtral_prefill", T=77, d=128, F=128, E=1, K=1),
     "sigmoid_unnormalised": workload("deepseek_v3_fine", T=64, d=256, F=128, E=32, K=4, renorm=False, n_shared=0,
                                      Fs=0),
+    # reductions of 2 k-steps (d = F = 64): the shallowest weight rings
+    "short_reduction_decode": workload("mixtral_decode", T=6, d=64, F=64),
+    "short_reduction_prefill": workload("mixtral_prefill", T=700, d=64, F=128),
 }
 
 
