@@ -58,6 +58,12 @@ def _load():
         lib.orc_swiglu.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp, i32]
         lib.orc_forward_rows.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]
         lib.orc_expert_choice.argtypes = [P, vp, i64, vp, vp]
+        lib.orc_select_ranked.argtypes = [P, vp, vp, i64, vp, vp]
+        lib.orc_select_ranked.restype = None
+        lib.orc_permute_affinity.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+        lib.orc_permute_affinity.restype = None
+        lib.orc_permute_reroute.argtypes = [P, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp]
+        lib.orc_permute_reroute.restype = None
         lib.orc_router_stats.argtypes = [P, vp, vp, vp]
         lib.orc_router_stats.restype = None
         lib.orc_threads.argtypes = []
@@ -123,6 +129,53 @@ def permute(L: OrcLayer, idx):
     _load().orc_permute(ctypes.byref(L), _p(np.ascontiguousarray(idx, dtype=np.int32)), _p(out["counts"]),
                         _p(out["offsets"]), _p(out["dest"]), _p(out["row_src"]), _p(out["dropped"]))
     return out
+
+
+def select_ranked(L: OrcLayer, lg, n: int, sel_bias=None):
+    """The n best experts per token -> (idx int32 [T, n], w float64 [T, n])."""
+    idx = np.empty((L.T, n), dtype=np.int32)
+    w = np.empty((L.T, n), dtype=np.float64)
+    _load().orc_select_ranked(ctypes.byref(L), _p(np.ascontiguousarray(lg, dtype=np.float32)), _p(sel_bias), n,
+                              _p(idx), _p(w))
+    return idx, w
+
+
+def _perm_out(L: OrcLayer):
+    N = L.T * L.K
+    return dict(counts=np.empty(L.E, np.int32), offsets=np.empty(L.E + 1, np.int32), dest=np.empty(N, np.int32),
+                row_src=np.empty(N, np.int32), dropped=np.empty(N, np.uint8))
+
+
+def permute_affinity(L: OrcLayer, idx, aff):
+    """a4, affinity-descending drop; aff: fp32 [T, K] affinities."""
+    out = _perm_out(L)
+    _load().orc_permute_affinity(ctypes.byref(L), _p(np.ascontiguousarray(idx, dtype=np.int32)),
+                                 _p(np.ascontiguousarray(aff, dtype=np.float32)), _p(out["counts"]),
+                                 _p(out["offsets"]), _p(out["dest"]), _p(out["row_src"]), _p(out["dropped"]))
+    return out
+
+
+def permute_reroute(L: OrcLayer, idx, w, alt_idx, alt_w):
+    """a4, overflow re-routing.  alt_idx int32 [T, n_alt], alt_w float64 [T, n_alt].
+    Adds 'idx' and 'w' (final expert and weight per assignment) to the result."""
+    out = _perm_out(L)
+    n_alt = alt_idx.shape[1] if alt_idx.ndim == 2 else 0
+    out["idx"] = np.empty((L.T, L.K), np.int32)
+    out["w"] = np.empty((L.T, L.K), np.float64)
+    _load().orc_permute_reroute(ctypes.byref(L), _p(np.ascontiguousarray(idx, dtype=np.int32)),
+                                _p(np.ascontiguousarray(w, dtype=np.float64)),
+                                _p(np.ascontiguousarray(alt_idx, dtype=np.int32)),
+                                _p(np.ascontiguousarray(alt_w, dtype=np.float64)), n_alt, _p(out["counts"]),
+                                _p(out["offsets"]), _p(out["dest"]), _p(out["row_src"]), _p(out["dropped"]),
+                                _p(out["idx"]), _p(out["w"]))
+    return out
+
+
+def alternates(L: OrcLayer, lg, sel_bias=None):
+    """Re-routing candidates: ranks K .. min(2K, E)-1 of every token."""
+    n = min(2 * L.K, L.E)
+    ridx, rw = select_ranked(L, lg, n, sel_bias)
+    return np.ascontiguousarray(ridx[:, L.K:]), np.ascontiguousarray(rw[:, L.K:])
 
 
 def swiglu(W1, W3, W2, x, bf16: bool, threads: int = 1) -> np.ndarray:
@@ -201,9 +254,31 @@ def expert_choice(L: OrcLayer, lg, cap: int):
     return tok, g
 
 
-def route(L: OrcLayer, x, Wg, logit_bias=None, sel_bias=None):
-    """a1-a4 in order: logits, selection, permutation."""
-    lg = logits(L, x, Wg, logit_bias)
+POLICIES = ("first_come", "affinity", "reroute")
+
+
+def route(L: OrcLayer, x, Wg, logit_bias=None, sel_bias=None, policy: str = "first_come", lg=None):
+    """a1-a4 in order: logits, selection, permutation under a drop policy.
+
+    first_come: the first K_max arrivals in flat order are kept [TD §3.2];
+    affinity:   the K_max highest-affinity assignments are kept, the
+                affinity being the fp32 gate weight [TD §5.2];
+    reroute:    overflow goes to the next-best expert [LN §3.2]; 'idx' and 'w'
+                are then the final assignment, 'idx_first' / 'w_first' the
+                Top-K choice.
+    lg: fp32 logits to route instead of computing them."""
+    if lg is None:
+        lg = logits(L, x, Wg, logit_bias)
     idx, w, gap = select(L, lg, sel_bias)
-    perm = permute(L, idx)
+    if policy == "first_come":
+        perm = permute(L, idx)
+    elif policy == "affinity":
+        perm = permute_affinity(L, idx, w.astype(np.float32))
+    elif policy == "reroute":
+        ai, aw = alternates(L, lg, sel_bias)
+        perm = permute_reroute(L, idx, w, ai, aw)
+        perm["idx_first"], perm["w_first"] = idx, w
+        idx, w = perm.pop("idx"), perm.pop("w")
+    else:
+        raise ValueError(policy)
     return dict(logits=lg, idx=idx, w=w, gap=gap, **perm)

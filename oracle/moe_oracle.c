@@ -52,6 +52,47 @@ static inline int ranks_before(float ka, int64_t ea, float kb, int64_t eb) {
   return ea < eb;
 }
 
+/* Selection key and gate score of every expert for one token's logits. */
+static void token_scores(const orc_layer* L, const float* l, const float* sel_bias, float* key, double* score) {
+  const int64_t E = L->E;
+  if (L->gate == ORC_GATE_SOFTMAX) {
+    /* p_i = e^{l_i} / sum_j e^{l_j}  [TD §3.2], evaluated with the max
+     * subtracted; softmax is monotone, so the key is the logit itself. */
+    double m = -INFINITY;
+    for (int64_t e = 0; e < E; ++e) m = fmax(m, (double)l[e]);
+    double z = 0.0;
+    for (int64_t e = 0; e < E; ++e) z += exp((double)l[e] - m);
+    for (int64_t e = 0; e < E; ++e) {
+      score[e] = exp((double)l[e] - m) / z;
+      key[e] = l[e];
+    }
+  } else {
+    /* s = Sigmoid(u^T e_i)  [TD §3.5]; selection on s + b_i, weights on s
+     * alone  [TD §4.3; §9.2].  The key is formed in fp32. */
+    for (int64_t e = 0; e < E; ++e) {
+      double s = 1.0 / (1.0 + exp(-(double)l[e]));
+      float sf = (float)s;
+      float b = sel_bias ? sel_bias[e] : 0.0f;
+      score[e] = s;
+      key[e] = sf + b;
+    }
+  }
+}
+
+/* order[0 .. n) = the n best experts by repeated maximum under the total
+ * order above [TD §3.1 KeepTopK]; order[n ..) holds the rest. */
+static void top_n(const float* key, int64_t E, int64_t n, int64_t* order) {
+  for (int64_t e = 0; e < E; ++e) order[e] = e;
+  for (int64_t k = 0; k < n && k < E; ++k) {
+    int64_t best = k;
+    for (int64_t j = k + 1; j < E; ++j)
+      if (ranks_before(key[order[j]], order[j], key[order[best]], order[best])) best = j;
+    int64_t tmp = order[k];
+    order[k] = order[best];
+    order[best] = tmp;
+  }
+}
+
 void orc_select(const orc_layer* L, const float* logits, const float* sel_bias, int32_t* idx, double* w,
                 double* gap) {
   const int64_t T = L->T, E = L->E, K = L->K;
@@ -62,40 +103,8 @@ void orc_select(const orc_layer* L, const float* logits, const float* sel_bias, 
     int64_t* order = (int64_t*)malloc(sizeof(int64_t) * (size_t)E);
 #pragma omp for schedule(dynamic, 16)
     for (int64_t t = 0; t < T; ++t) {
-      const float* l = logits + t * E;
-      if (L->gate == ORC_GATE_SOFTMAX) {
-        /* p_i = e^{l_i} / sum_j e^{l_j}  [TD §3.2], evaluated with the max
-         * subtracted; softmax is monotone, so the key is the logit itself. */
-        double m = -INFINITY;
-        for (int64_t e = 0; e < E; ++e) m = fmax(m, (double)l[e]);
-        double z = 0.0;
-        for (int64_t e = 0; e < E; ++e) z += exp((double)l[e] - m);
-        for (int64_t e = 0; e < E; ++e) {
-          score[e] = exp((double)l[e] - m) / z;
-          key[e] = l[e];
-        }
-      } else {
-        /* s = Sigmoid(u^T e_i)  [TD §3.5]; selection on s + b_i, weights on s
-         * alone  [TD §4.3; §9.2].  The key is formed in fp32. */
-        for (int64_t e = 0; e < E; ++e) {
-          double s = 1.0 / (1.0 + exp(-(double)l[e]));
-          float sf = (float)s;
-          float b = sel_bias ? sel_bias[e] : 0.0f;
-          score[e] = s;
-          key[e] = sf + b;
-        }
-      }
-      /* Top-K: selection by repeated maximum under the total order above
-       * [TD §3.1 KeepTopK]. */
-      for (int64_t e = 0; e < E; ++e) order[e] = e;
-      for (int64_t k = 0; k < K && k < E; ++k) {
-        int64_t best = k;
-        for (int64_t j = k + 1; j < E; ++j)
-          if (ranks_before(key[order[j]], order[j], key[order[best]], order[best])) best = j;
-        int64_t tmp = order[k];
-        order[k] = order[best];
-        order[best] = tmp;
-      }
+      token_scores(L, logits + t * E, sel_bias, key, score);
+      top_n(key, E, K, order);
       double sum = 0.0;
       for (int64_t k = 0; k < K; ++k) sum += score[order[k]];
       for (int64_t k = 0; k < K; ++k) {
@@ -113,6 +122,31 @@ void orc_select(const orc_layer* L, const float* logits, const float* sel_bias, 
             if (key[order[j]] > next) next = key[order[j]];
           gap[t] = (double)key[order[K - 1]] - (double)next;
         }
+      }
+    }
+    free(key);
+    free(score);
+    free(order);
+  }
+}
+
+void orc_select_ranked(const orc_layer* L, const float* logits, const float* sel_bias, int64_t n, int32_t* idx,
+                       double* w) {
+  const int64_t T = L->T, E = L->E, K = L->K;
+#pragma omp parallel
+  {
+    float* key = (float*)malloc(sizeof(float) * (size_t)E);
+    double* score = (double*)malloc(sizeof(double) * (size_t)E);
+    int64_t* order = (int64_t*)malloc(sizeof(int64_t) * (size_t)E);
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t t = 0; t < T; ++t) {
+      token_scores(L, logits + t * E, sel_bias, key, score);
+      top_n(key, E, n, order);
+      double sum = 0.0;
+      for (int64_t k = 0; k < K; ++k) sum += score[order[k]];
+      for (int64_t r = 0; r < n; ++r) {
+        idx[t * n + r] = (int32_t)order[r];
+        w[t * n + r] = L->renorm ? score[order[r]] / sum : score[order[r]];
       }
     }
     free(key);
@@ -152,6 +186,126 @@ void orc_permute(const orc_layer* L, const int32_t* idx, int32_t* counts, int32_
     dropped[f] = (uint8_t)!keep;
     if (keep) row_src[dest[f]] = (int32_t)f;
   }
+  free(pos);
+}
+
+/* ---- a4 variants: which overflow assignments drop ----------------------- */
+
+typedef struct aff_item {
+  float a;
+  int64_t f;
+} aff_item;
+
+/* higher affinity first, then the lower flat index */
+static int aff_cmp(const void* pa, const void* pb) {
+  const aff_item* x = (const aff_item*)pa;
+  const aff_item* y = (const aff_item*)pb;
+  if (x->a != y->a) return x->a > y->a ? -1 : 1;
+  return x->f < y->f ? -1 : (x->f > y->f ? 1 : 0);
+}
+
+void orc_permute_affinity(const orc_layer* L, const int32_t* idx, const float* aff, int32_t* counts,
+                          int32_t* offsets, int32_t* dest, int32_t* row_src, uint8_t* dropped) {
+  const int64_t E = L->E, N = L->T * L->K;
+  const int64_t cap = orc_capacity(L);
+  uint8_t* keep = (uint8_t*)malloc((size_t)(N > 0 ? N : 1));
+  aff_item* items = (aff_item*)malloc(sizeof(aff_item) * (size_t)(N > 0 ? N : 1));
+  for (int64_t e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t f = 0; f < N; ++f) counts[idx[f]]++;
+  /* each expert over capacity keeps its `cap` highest-affinity assignments
+   * and drops the rest, in descending-affinity order  [TD §5.2, V2 token
+   * dropping]; ties go to the earlier assignment */
+  for (int64_t e = 0; e < E; ++e) {
+    int64_t n = 0;
+    for (int64_t f = 0; f < N; ++f)
+      if (idx[f] == e) {
+        items[n].a = aff[f];
+        items[n].f = f;
+        ++n;
+      }
+    if (n > 1) qsort(items, (size_t)n, sizeof(aff_item), aff_cmp);
+    for (int64_t i = 0; i < n; ++i) keep[items[i].f] = (uint8_t)(cap < 0 || i < cap);
+  }
+  offsets[0] = 0;
+  for (int64_t e = 0; e < E; ++e) {
+    int64_t kept = counts[e];
+    if (cap >= 0 && kept > cap) kept = cap;
+    offsets[e + 1] = offsets[e] + (int32_t)kept;
+  }
+  /* kept rows of an expert stay in flat order */
+  int32_t* run = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+  for (int64_t r = 0; r < N; ++r) row_src[r] = -1;
+  for (int64_t f = 0; f < N; ++f) {
+    const int32_t e = idx[f];
+    dest[f] = keep[f] ? offsets[e] + run[e]++ : -1;
+    dropped[f] = (uint8_t)!keep[f];
+    if (keep[f]) row_src[dest[f]] = (int32_t)f;
+  }
+  free(run);
+  free(items);
+  free(keep);
+}
+
+void orc_permute_reroute(const orc_layer* L, const int32_t* idx, const double* w, const int32_t* alt_idx,
+                         const double* alt_w, int64_t n_alt, int32_t* counts, int32_t* offsets, int32_t* dest,
+                         int32_t* row_src, uint8_t* dropped, int32_t* idx_out, double* w_out) {
+  const int64_t E = L->E, T = L->T, K = L->K, N = T * K;
+  const int64_t cap = orc_capacity(L);
+  int64_t* pos = (int64_t*)malloc(sizeof(int64_t) * (size_t)(N > 0 ? N : 1));
+  int32_t* cand = (int32_t*)malloc(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
+  int64_t* first = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+  int64_t* second = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+  /* first pass: the first-come rule of orc_permute */
+  for (int64_t e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t f = 0; f < N; ++f) pos[f] = counts[idx[f]]++;
+  for (int64_t e = 0; e < E; ++e) first[e] = (cap >= 0 && counts[e] > cap) ? cap : counts[e];
+  /* an overflowing assignment is sent to the token's next-best expert
+   * [LN §3.2]: the j-th overflowing choice of token t (in k order) takes the
+   * token's rank K + j expert, if there is one */
+  for (int64_t t = 0; t < T; ++t) {
+    int64_t j = 0;
+    for (int64_t k = 0; k < K; ++k) {
+      const int64_t f = t * K + k;
+      idx_out[f] = idx[f];
+      w_out[f] = w[f];
+      cand[f] = -1;
+      if (cap >= 0 && pos[f] >= cap) {
+        if (j < n_alt && alt_idx[t * n_alt + j] >= 0) {
+          cand[f] = alt_idx[t * n_alt + j];
+          idx_out[f] = cand[f];
+          w_out[f] = alt_w[t * n_alt + j];
+        }
+        ++j;
+      }
+    }
+  }
+  /* second pass: re-routed assignments, in flat order, take what capacity
+   * their new expert has left after the first pass */
+  for (int64_t f = 0; f < N; ++f)
+    if (cand[f] >= 0) pos[f] = second[cand[f]]++;
+  offsets[0] = 0;
+  for (int64_t e = 0; e < E; ++e) {
+    int64_t room = cap - first[e];
+    int64_t extra = second[e] < room ? second[e] : room;
+    offsets[e + 1] = offsets[e] + (int32_t)(first[e] + extra);
+  }
+  /* rows of an expert: its first-pass assignments, then its re-routed ones,
+   * each in flat order */
+  for (int64_t r = 0; r < N; ++r) row_src[r] = -1;
+  for (int64_t f = 0; f < N; ++f) {
+    int64_t row = -1;
+    if (cap < 0 || (cand[f] < 0 && pos[f] < cap)) {
+      row = offsets[idx[f]] + pos[f];
+    } else if (cand[f] >= 0 && pos[f] < cap - first[cand[f]]) {
+      row = offsets[cand[f]] + first[cand[f]] + pos[f];
+    }
+    dest[f] = (int32_t)row;
+    dropped[f] = (uint8_t)(row < 0);
+    if (row >= 0) row_src[row] = (int32_t)f;
+  }
+  free(second);
+  free(first);
+  free(cand);
   free(pos);
 }
 

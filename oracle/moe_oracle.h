@@ -22,7 +22,9 @@
  *   [BD]  "MoE稀疏架构：定义、原理与工程实践" (cloud.baidu.com): §3.2 gating
  *         network, §4 six-step forward workflow.
  *   [LN]  lnwmold.com article on GPT-4-class sparse activation: §2.2 expert
- *         FFN with W1/W2/W3, §3.2 capacity example, §5.5 toy MoE layer.
+ *         FFN with W1/W2/W3, §3.2 capacity example and re-routing, §5.5 toy
+ *         MoE layer.
+ *   [TD]  §5.2 also gives DeepSeek-V2's affinity-ordered token dropping.
  *
  * Parity pins: every function here is pinned by the CPU test suite against
  * library routines, brute force, closed forms or the pages' worked numbers;
@@ -79,6 +81,34 @@ int64_t orc_capacity(const orc_layer* L);
  * are set to -1); dropped[f] = (dest[f] < 0). */
 void orc_permute(const orc_layer* L, const int32_t* idx, int32_t* counts, int32_t* offsets, int32_t* dest,
                  int32_t* row_src, uint8_t* dropped);
+
+/* The n best experts of every token (n <= E), ranked as orc_select ranks
+ * them; weights normalised as orc_select normalises the first K (with
+ * renorm, every rank is divided by the sum over the K selected).
+ * idx, w: [T][n]. */
+void orc_select_ranked(const orc_layer* L, const float* logits, const float* sel_bias, int64_t n, int32_t* idx,
+                       double* w);
+
+/* a4 with the affinity-descending drop rule [TD §5.2, DeepSeek-V2 token
+ * dropping]: an expert over capacity keeps its `capacity` assignments of
+ * highest affinity aff[f] (ties to the lower f) and drops the others; the
+ * kept rows of each expert are in flat order.  Outputs as orc_permute. */
+void orc_permute_affinity(const orc_layer* L, const int32_t* idx, const float* aff, int32_t* counts,
+                          int32_t* offsets, int32_t* dest, int32_t* row_src, uint8_t* dropped);
+
+/* a4 with overflow re-routing [LN §3.2: over-capacity tokens go to the
+ * next-best expert].  First pass: the first-come rule of orc_permute
+ * (counts = this pass's demand).  The j-th overflowing choice of token t (in
+ * k order) is re-routed to alt_idx[t][j] (the token's rank-(K+j) expert)
+ * with weight alt_w[t][j], when j < n_alt and alt_idx[t][j] >= 0; otherwise
+ * it is dropped.  Second pass: re-routed assignments, in flat order, are kept
+ * while their new expert has room left (capacity minus its first-pass kept
+ * count).  Rows of an expert: first-pass kept, then re-routed kept, each in
+ * flat order.  idx_out / w_out: the final expert and weight of every
+ * assignment (the new expert and weight when re-routed). */
+void orc_permute_reroute(const orc_layer* L, const int32_t* idx, const double* w, const int32_t* alt_idx,
+                         const double* alt_w, int64_t n_alt, int32_t* counts, int32_t* offsets, int32_t* dest,
+                         int32_t* row_src, uint8_t* dropped, int32_t* idx_out, double* w_out);
 
 /* a6 + a7 for one row and one expert:
  *   out[m] = sum_j W2[m][j] * h_j,   h_j = SiLU(a_j) * b_j,  SiLU(z) = z / (1 + e^-z),

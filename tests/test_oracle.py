@@ -485,3 +485,163 @@ def test_router_stats_balanced_optimum():
     assert abs(st["balance"] - 1) < 1e-14 and abs(st["lif"] - 1) < 1e-14 and abs(st["cv"]) < 1e-14
     assert abs(st["entropy_p"] - math.log(E)) < 1e-14 and abs(st["entropy_f"] - math.log(E)) < 1e-14
     assert abs(st["z_loss"] - math.log(E) ** 2) < 1e-12
+
+
+# ------------------------------------------------------------ drop policies --
+
+def _perm_consistent(L, idx_final, p):
+    """dest / row_src / dropped / offsets agree with each other and rows of an
+    expert lie in its offsets range."""
+    N = L.T * L.K
+    dest, rs, dr, off = p["dest"], p["row_src"], p["dropped"], p["offsets"]
+    R = off[-1]
+    assert np.array_equal(dr, (dest < 0).astype(np.uint8))
+    kept = np.nonzero(dest >= 0)[0]
+    assert len(kept) == R and np.array_equal(np.sort(dest[kept]), np.arange(R))
+    assert np.array_equal(rs[dest[kept]], kept) and np.all(rs[R:N] == -1)
+    e = idx_final.reshape(-1)[kept]
+    assert np.all(dest[kept] >= off[e]) and np.all(dest[kept] < off[e + 1])
+
+
+def test_select_ranked_brute_force():
+    """Ranks = a stable sort of the keys (descending, ties to the lower
+    expert); weights use the first K's normaliser."""
+    r = rng(21)
+    T, E, K = 40, 9, 2
+    lg = np.round(r.standard_normal((T, E)), 1).astype(np.float32)  # many exact ties
+    L = oracle.layer(T, 4, 4, E, K, renorm=True)
+    idx, w = oracle.select_ranked(L, lg, E)
+    p = scipy.special.softmax(lg.astype(np.float64), axis=1)
+    for t in range(T):
+        order = np.lexsort((np.arange(E), -lg[t].astype(np.float64)))
+        assert np.array_equal(idx[t], order)
+        np.testing.assert_allclose(w[t], p[t, order] / p[t, order[:K]].sum(), rtol=1e-13)
+    i2, w2, _ = oracle.select(L, lg)
+    assert np.array_equal(i2, idx[:, :K]) and np.allclose(w2, w[:, :K], rtol=0, atol=0)
+
+
+def test_affinity_drop_golden():
+    g = json.load(open(os.path.join(GOLDEN, "affinity_drop_small.json")))
+    L = oracle.layer(g["T"], 4, 4, g["E"], g["K"], capacity_factor=g["capacity_factor"])
+    assert oracle.capacity(L) == g["capacity"]
+    p = oracle.permute_affinity(L, np.array(g["idx"], np.int32).reshape(-1, 1),
+                                np.array(g["aff"], np.float32).reshape(-1, 1))
+    for k, v in g["expect"].items():
+        assert p[k].tolist() == v, k
+
+
+def test_affinity_drop_invariants_and_special_cases():
+    r = rng(22)
+    T, E, K = 500, 8, 2
+    lg = (r.standard_normal((T, E)) + np.linspace(0, 2, E)).astype(np.float32)
+    L = oracle.layer(T, 4, 4, E, K, capacity_factor=0.9)
+    cap = oracle.capacity(L)
+    idx, w, _ = oracle.select(L, lg)
+    aff = w.astype(np.float32)
+    p = oracle.permute_affinity(L, idx, aff)
+    _perm_consistent(L, idx, p)
+    fi, a, dest = idx.reshape(-1), aff.reshape(-1), p["dest"]
+    assert np.array_equal(p["counts"], np.bincount(fi, minlength=E))
+    for e in range(E):
+        fs = np.nonzero(fi == e)[0]
+        kept, drop = fs[dest[fs] >= 0], fs[dest[fs] < 0]
+        assert len(kept) == min(len(fs), cap)
+        assert np.all(np.diff(dest[kept]) == 1)          # kept rows in flat order
+        if len(drop):
+            lo = a[kept].min()
+            assert lo >= a[drop].max()
+            tie = kept[a[kept] == lo]
+            assert np.all(a[drop] < lo) or tie.max() < drop[a[drop] == lo].min()
+    assert p["dropped"].sum() > 0
+    # equal affinities: the first-come rule
+    same = oracle.permute_affinity(L, idx, np.full_like(aff, 0.5))
+    fc = oracle.permute(L, idx)
+    for k in fc:
+        assert np.array_equal(same[k], fc[k]), k
+    # no capacity pressure: nothing dropped, the first-come permutation
+    L2 = oracle.layer(T, 4, 4, E, K, capacity_factor=8.0)
+    a2, f2 = oracle.permute_affinity(L2, idx, aff), oracle.permute(L2, idx)
+    assert a2["dropped"].sum() == 0 and all(np.array_equal(a2[k], f2[k]) for k in f2)
+
+
+def _reroute_logits(g):
+    T, E = g["T"], g["E"]
+    lg = np.zeros((T, E), np.float32)
+    hot = [g["hot_tokens_stride"] * i for i in range(g["hot_tokens"])]
+    j = 0
+    for t in range(T):
+        if t in hot:
+            i = hot.index(t)
+            lg[t, g["hot_expert"]] = 10.0
+            lg[t, 1 + i % 5] = 5.0
+        else:
+            lg[t, 1 + j % 127] = 10.0
+            lg[t, 1 + (j + 1) % 127] = 5.0
+            j += 1
+    return lg
+
+
+def test_reroute_page_example():
+    """[LN §3.2]: capacity 10 at C = 1.25, batch 1024, 128 experts; an expert
+    chosen 15 times keeps 10 and its 5 excess tokens go to their next-best
+    expert."""
+    g = json.load(open(os.path.join(GOLDEN, "reroute_page_example.json")))
+    L = oracle.layer(g["T"], 4, 4, g["E"], g["K"], renorm=False, capacity_factor=g["capacity_factor"])
+    assert oracle.capacity(L) == g["capacity"]
+    rt = oracle.route(L, None, None, policy="reroute", lg=_reroute_logits(g))
+    ex = g["expect"]
+    assert rt["counts"][g["hot_expert"]] == ex["counts_hot"]
+    on_hot = np.nonzero((rt["idx"][:, 0] == g["hot_expert"]) & (rt["dest"] >= 0))[0]
+    assert on_hot.tolist() == ex["kept_on_hot"]
+    for t, e in ex["rerouted"].items():
+        assert rt["idx"][int(t), 0] == e and rt["dest"][int(t)] >= 0
+        assert rt["idx_first"][int(t), 0] == g["hot_expert"]
+    assert int(rt["dropped"].sum()) == ex["dropped"]
+    kept = np.bincount(rt["idx"][:, 0][rt["dest"] >= 0], minlength=g["E"])
+    assert kept.max() <= g["capacity"]
+    _perm_consistent(L, rt["idx"], rt)
+
+
+def test_reroute_invariants_and_special_cases():
+    r = rng(23)
+    for K in (1, 2, 3):
+        T, E = 400, 8
+        lg = (r.standard_normal((T, E)) + np.linspace(0, 3, E)).astype(np.float32)
+        L = oracle.layer(T, 4, 4, E, K, renorm=(K > 1), capacity_factor=1.0)
+        cap = oracle.capacity(L)
+        rt = oracle.route(L, None, None, policy="reroute", lg=lg)
+        fc = oracle.route(L, None, None, policy="first_come", lg=lg)
+        _perm_consistent(L, rt["idx"], rt)
+        ranked, rw = oracle.select_ranked(L, lg, min(2 * K, E))
+        first_kept = fc["dest"] >= 0
+        # the first pass is the first-come rule
+        assert np.array_equal(rt["counts"], fc["counts"])
+        assert np.array_equal(rt["idx"].reshape(-1)[first_kept], fc["idx"].reshape(-1)[first_kept])
+        assert np.all(rt["dest"][first_kept] >= 0)
+        fin = rt["idx"].reshape(-1)
+        kept_per = np.bincount(fin[rt["dest"] >= 0], minlength=E)
+        assert kept_per.max() <= cap
+        moved = np.nonzero(~first_kept)[0]
+        assert len(moved) > 0
+        for f in moved:
+            t, k = divmod(f, K)
+            j = int(np.sum(~first_kept[t * K:f]))          # earlier overflowing choices of t
+            if K + j < min(2 * K, E):
+                assert fin[f] == ranked[t, K + j] and rt["w"][t, k] == rw[t, K + j]
+                if rt["dest"][f] < 0:
+                    assert kept_per[fin[f]] == cap        # dropped only when the new expert is full
+            else:
+                assert rt["dest"][f] < 0 and fin[f] == fc["idx"].reshape(-1)[f]
+        # flat-order priority among re-routed assignments of one expert
+        for e in range(E):
+            mv = moved[fin[moved] == e]
+            k_ = mv[rt["dest"][mv] >= 0]
+            d_ = mv[rt["dest"][mv] < 0]
+            if len(k_) and len(d_):
+                assert k_.max() < d_.min()
+    # K == E: no alternates, so re-routing drops exactly what first-come drops
+    L = oracle.layer(50, 4, 4, 3, 3, capacity_factor=0.5)
+    lg = r.standard_normal((50, 3)).astype(np.float32)
+    a, b = oracle.route(L, None, None, policy="reroute", lg=lg), oracle.route(L, None, None, lg=lg)
+    for k in ("dest", "row_src", "dropped", "offsets", "idx"):
+        assert np.array_equal(a[k], b[k]), k
