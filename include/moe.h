@@ -58,6 +58,27 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 /* Gate [TD §3.2 softmax; TD §3.5 sigmoid]. */
 typedef enum moe_gate { MOE_GATE_SOFTMAX = 0, MOE_GATE_SIGMOID = 1 } moe_gate;
 
+/* Which assignments an expert over capacity drops (moe_config.drop_policy;
+ * only used when capacity_factor > 0). */
+typedef enum moe_drop_policy {
+  /* the first K_max arrivals in flat order f = t*K + k are kept [TD §3.2] */
+  MOE_DROP_FIRST_COME = 0,
+  /* the K_max assignments of highest affinity are kept, the rest dropped
+   * in descending-affinity order [TD §5.2, DeepSeek-V2]; the affinity is
+   * the assignment's gate weight topk_w, ties to the lower f */
+  MOE_DROP_AFFINITY = 1,
+  /* overflow goes to the token's next-best expert [LN §3.2]: after a
+   * first-come pass, the j-th overflowing choice of a token (in k order) is
+   * re-routed to its rank-(K+j) expert (the best ones it did not choose),
+   * with that expert's gate weight normalised like the token's other
+   * weights; re-routed assignments, in flat order, take what capacity their
+   * new expert has left and are dropped when it is full.  Rows of an expert
+   * hold its first-pass assignments, then its re-routed ones.  topk_idx /
+   * topk_w then give the final expert and weight of each assignment;
+   * counts stays the first-pass demand. */
+  MOE_DROP_REROUTE = 2
+} moe_drop_policy;
+
 /* Flags (moe_config.flags). */
 enum {
   /* Renormalise the K selected gate values to sum to 1 [TD §9.1]. */
@@ -113,8 +134,8 @@ typedef struct moe_config {
   uint32_t flags;          /* MOE_F_* */
   /* Capacity factor C [TD §3.2].  C > 0: each expert keeps at most
    * K_max = floor(C * T * K / E) assignments (T*K counts (token, choice)
-   * pairs, which is T for top-1); the first K_max in flat order f = t*K + k
-   * are kept and the rest dropped.  C <= 0: no limit. */
+   * pairs, which is T for top-1); drop_policy says which are kept (by
+   * default the first K_max in flat order f = t*K + k).  C <= 0: no limit. */
   double capacity_factor;
   int64_t n_shared;        /* always-active shared experts, 0 or 1 [TD §3.4] */
   int64_t d_ff_shared;     /* shared expert d_ff; bf16: multiple of 64 */
@@ -124,6 +145,7 @@ typedef struct moe_config {
    * before its final rounding; the bf16 output is exactly its
    * round-to-nearest-even image). */
   int32_t out_dtype;
+  int32_t drop_policy;     /* moe_drop_policy; MOE_DROP_REROUTE needs the logits (not MOE_F_TOPK_IN) */
 } moe_config;
 
 /* Routing arrays, all DEVICE pointers.  Sizes are in elements. */
@@ -156,7 +178,7 @@ moe_status moe_max_rows(const moe_config* cfg, int64_t* rows);
  *   compared as IEEE values, -0 equal to +0), in key-descending order;
  *   topk_w = p (or s) of each choice, divided by their sum with MOE_F_RENORM.
  *   counts / offsets / dest / row_src / dropped as described in moe_routing,
- *   with the first-come (flat order) capacity rule.            [TD §3.2]
+ *   with the capacity rule of cfg->drop_policy.          [TD §3.2, §5.2; LN §3.2]
  * x:          device, [T, d] act_dtype
  * Wg:         device, [E, d] fp32 (unused with MOE_F_LOGITS_IN / MOE_F_TOPK_IN)
  * logit_bias: device, [E] fp32, nullable; added to the logits (enters both

@@ -23,6 +23,8 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16 = 0, 1
 MOE_GATE_SOFTMAX, MOE_GATE_SIGMOID = 0, 1
 MOE_F_RENORM, MOE_F_RESIDUAL, MOE_F_LOGITS_IN, MOE_F_TOPK_IN, MOE_F_STATS = 1, 2, 4, 8, 16
+# moe_drop_policy: which assignments an expert over capacity drops
+DROP_POLICIES = {"first_come": 0, "affinity": 1, "reroute": 2}
 # router statistics after the E per-expert mean probabilities (moe.h, MOE_STAT_*)
 STAT_NAMES = ("balance", "z_loss", "lif", "cv", "entropy_p", "entropy_f")
 
@@ -42,7 +44,7 @@ class MoeConfig(ctypes.Structure):
         ("n_experts", ctypes.c_int64), ("top_k", ctypes.c_int64), ("gate", ctypes.c_int32),
         ("flags", ctypes.c_uint32), ("capacity_factor", ctypes.c_double), ("n_shared", ctypes.c_int64),
         ("d_ff_shared", ctypes.c_int64), ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
-        ("out_dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32), ("drop_policy", ctypes.c_int32),
     ]
 
 
@@ -123,6 +125,7 @@ class LayerSpec:
     logits_in: bool = False
     topk_in: bool = False
     stats: bool = False
+    drop_policy: str = "first_come"   # a key of DROP_POLICIES
 
     def config(self) -> MoeConfig:
         flags = ((MOE_F_RENORM if self.renorm else 0) | (MOE_F_RESIDUAL if self.residual else 0)
@@ -131,7 +134,8 @@ class LayerSpec:
         dt = MOE_BF16 if self.dtype == "bf16" else MOE_F32
         ot = dt if self.out_dtype is None else (MOE_BF16 if self.out_dtype == "bf16" else MOE_F32)
         return MoeConfig(self.tokens, self.d_model, self.d_ff, self.n_experts, self.top_k, self.gate, flags,
-                         float(self.capacity_factor), self.n_shared, self.d_ff_shared, dt, dt, ot)
+                         float(self.capacity_factor), self.n_shared, self.d_ff_shared, dt, dt, ot,
+                         DROP_POLICIES[self.drop_policy])
 
 
 def _cfg(spec_or_cfg) -> MoeConfig:

@@ -45,6 +45,8 @@ struct Shape {
   bool bf16;
   bool out_bf16;
   bool stats;  // router statistics requested
+  int policy;  // moe_drop_policy in effect (first-come when there is no capacity)
+  int64_t K2;  // re-routing alternates per token
   int64_t T, d, F, E, K, S, Fs;
   int64_t cap;       // -1: no limit
   int64_t max_rows;  // upper bound of kept rows R
@@ -65,6 +67,10 @@ moe_status validate(const moe_config* c, Shape* sh) {
   if (c->flags & ~kKnownFlags) return fail(MOE_ERR_INVALID_ARG, "unknown flag bits 0x%x", c->flags & ~kKnownFlags);
   if ((c->flags & MOE_F_STATS) && (c->flags & MOE_F_TOPK_IN))
     return fail(MOE_ERR_INVALID_ARG, "MOE_F_STATS needs logits; it cannot be combined with MOE_F_TOPK_IN");
+  if (c->drop_policy < MOE_DROP_FIRST_COME || c->drop_policy > MOE_DROP_REROUTE)
+    return fail(MOE_ERR_INVALID_ARG, "unknown drop_policy %d", (int)c->drop_policy);
+  if (c->drop_policy == MOE_DROP_REROUTE && (c->flags & MOE_F_TOPK_IN))
+    return fail(MOE_ERR_INVALID_ARG, "MOE_DROP_REROUTE ranks experts from the logits; not with MOE_F_TOPK_IN");
   if (!std::isfinite(c->capacity_factor)) return fail(MOE_ERR_INVALID_ARG, "capacity_factor is not finite");
   if (c->n_shared < 0 || c->n_shared > 1) return fail(MOE_ERR_INVALID_ARG, "n_shared must be 0 or 1");
   if (c->n_shared == 1 && c->d_ff_shared < 1) return fail(MOE_ERR_INVALID_ARG, "d_ff_shared must be >= 1");
@@ -97,6 +103,8 @@ moe_status validate(const moe_config* c, Shape* sh) {
   sh->bf16 = bf16;
   sh->out_bf16 = c->out_dtype == MOE_BF16;
   sh->stats = c->flags & MOE_F_STATS;
+  sh->policy = cap >= 0 ? c->drop_policy : MOE_DROP_FIRST_COME;
+  sh->K2 = sh->policy == MOE_DROP_REROUTE ? std::min(K, E - K) : 0;
   sh->T = T;
   sh->d = d;
   sh->F = F;
@@ -113,7 +121,8 @@ moe_status validate(const moe_config* c, Shape* sh) {
 
 // ---- workspace layout ----
 struct Layout {
-  size_t router_part, blk_count, blk_base, blk_P, blk_z, tab_up, tab_down, counts, sh_range, sh_tab_up, sh_tab_down, sh_counts;
+  size_t router_part, blk_count, blk_base, blk_P, blk_z, dem_off, seg, alt_idx, alt_w, pos1, cand, cand_w,
+      blk_count2, blk_base2, counts2, tab_up, tab_down, counts, sh_range, sh_tab_up, sh_tab_down, sh_counts;
   size_t h, xp, yp, sh_h, sh_out;
   size_t r_logits, r_idx, r_w, r_counts, r_offsets, r_dest, r_row_src, r_dropped;
   size_t total;
@@ -134,6 +143,17 @@ Layout layout(const Shape& s) {
   L.blk_base = take((size_t)(s.n_chunks * s.E) * 4);
   L.blk_P = take(s.stats ? (size_t)(s.n_chunks * s.E) * 4 : 0);
   L.blk_z = take(s.stats ? (size_t)s.n_chunks * 4 : 0);
+  const bool aff = s.policy == MOE_DROP_AFFINITY, rr = s.policy == MOE_DROP_REROUTE;
+  L.dem_off = take(aff ? (size_t)(s.E + 1) * 4 : 0);
+  L.seg = take(aff ? TK * 8 : 0);
+  L.alt_idx = take(rr ? (size_t)(s.T * s.K2) * 4 : 0);
+  L.alt_w = take(rr ? (size_t)(s.T * s.K2) * 4 : 0);
+  L.pos1 = take(rr ? TK * 4 : 0);
+  L.cand = take(rr ? TK * 4 : 0);
+  L.cand_w = take(rr ? TK * 4 : 0);
+  L.blk_count2 = take(rr ? (size_t)(s.n_chunks * s.E) * 4 : 0);
+  L.blk_base2 = take(rr ? (size_t)(s.n_chunks * s.E) * 4 : 0);
+  L.counts2 = take(rr ? (size_t)s.E * 4 : 0);
   L.tab_up = take((size_t)ffn_table_entries(s.bf16, s.max_rows, s.E, s.F, true) * 16);
   L.tab_down = take((size_t)ffn_table_entries(s.bf16, s.max_rows, s.E, s.d, false) * 16);
   L.counts = take(2 * 4);
@@ -190,6 +210,9 @@ moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const 
   const float* sb = c->gate == MOE_GATE_SIGMOID ? sel_bias : nullptr;
   float* blk_P = s.stats ? at<float>(ws, L.blk_P) : nullptr;
   float* blk_z = s.stats ? at<float>(ws, L.blk_z) : nullptr;
+  const bool rr = s.policy == MOE_DROP_REROUTE, aff = s.policy == MOE_DROP_AFFINITY;
+  int32_t* alt_idx = rr ? at<int32_t>(ws, L.alt_idx) : nullptr;
+  float* alt_w = rr ? at<float>(ws, L.alt_w) : nullptr;
   if (!topk_in) {
     int S = 1;
     float* part = at<float>(ws, L.router_part);
@@ -198,15 +221,56 @@ moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const 
       MOE_HIP(launch_router_logits(s.bf16, x, Wg, logit_bias, r.logits, part, s.T, s.d, s.E, st));
     }
     MOE_HIP(launch_router_topk(r.logits, part, S, logit_bias, sb, r.topk_idx, r.topk_w, blk_count, blk_P, blk_z,
-                               s.T, s.E, s.K, c->gate, c->flags & MOE_F_RENORM, false, st));
+                               alt_idx, alt_w, s.K2, s.T, s.E, s.K, c->gate, c->flags & MOE_F_RENORM, false, st));
   } else {
     MOE_HIP(launch_router_topk(nullptr, nullptr, 1, nullptr, nullptr, r.topk_idx, nullptr, blk_count, nullptr,
-                               nullptr, s.T, s.E, s.K, c->gate, false, true, st));
+                               nullptr, nullptr, nullptr, 0, s.T, s.E, s.K, c->gate, false, true, st));
   }
+  int32_t* dem_off = aff ? at<int32_t>(ws, L.dem_off) : nullptr;
   MOE_HIP(launch_route_scan(blk_count, blk_base, r.counts, r.offsets, s.n_chunks, s.E, s.cap, blk_P, blk_z,
-                            s.stats ? r.stats : nullptr, s.T, s.K, st));
-  MOE_HIP(launch_route_scatter(r.topk_idx, blk_base, r.offsets, r.dest, r.row_src, r.dropped, s.T, s.K, s.E, s.cap,
-                               st));
+                            s.stats ? r.stats : nullptr, s.T, s.K, nullptr, dem_off, st));
+  RouteScatter sc{};
+  sc.idx = r.topk_idx;
+  sc.blk_base = blk_base;
+  sc.offsets = r.offsets;
+  sc.dest = r.dest;
+  sc.row_src = r.row_src;
+  sc.dropped = r.dropped;
+  if (aff) {
+    uint64_t* seg = at<uint64_t>(ws, L.seg);
+    sc.mode = kAffinity;
+    sc.counts = r.counts;
+    sc.dem_off = dem_off;
+    sc.aff = r.topk_w;
+    sc.seg = seg;
+    MOE_HIP(launch_route_scatter(sc, s.T, s.K, s.E, s.cap, st));
+    MOE_HIP(launch_route_affinity(seg, r.counts, dem_off, r.offsets, r.dest, r.row_src, r.dropped, s.E, s.cap, st));
+  } else if (rr) {
+    int32_t* blk_count2 = at<int32_t>(ws, L.blk_count2);
+    int32_t* blk_base2 = at<int32_t>(ws, L.blk_base2);
+    sc.mode = kReroute1;
+    sc.alt_idx = alt_idx;
+    sc.alt_w = alt_w;
+    sc.K2 = (int)s.K2;
+    sc.pos1 = at<int32_t>(ws, L.pos1);
+    sc.cand = at<int32_t>(ws, L.cand);
+    sc.cand_w = at<float>(ws, L.cand_w);
+    sc.blk_count2 = blk_count2;
+    MOE_HIP(launch_route_scatter(sc, s.T, s.K, s.E, s.cap, st));
+    // second pass: final offsets from the first-pass kept and the candidates that fit
+    MOE_HIP(launch_route_scan(blk_count2, blk_base2, at<int32_t>(ws, L.counts2), r.offsets, s.n_chunks, s.E, s.cap,
+                              nullptr, nullptr, nullptr, s.T, s.K, r.counts, nullptr, st));
+    sc.mode = kReroute2;
+    sc.idx = sc.cand;
+    sc.blk_base = blk_base2;
+    sc.first_counts = r.counts;
+    sc.topk_idx = r.topk_idx;
+    sc.topk_w = r.topk_w;
+    MOE_HIP(launch_route_scatter(sc, s.T, s.K, s.E, s.cap, st));
+  } else {
+    sc.mode = kFirstCome;
+    MOE_HIP(launch_route_scatter(sc, s.T, s.K, s.E, s.cap, st));
+  }
   return MOE_OK;
 }
 

@@ -39,19 +39,55 @@ hipError_t launch_router_logits(bool bf16, const void* x, const float* Wg, const
 // topk_in: idx is an input; only the per-chunk histogram is produced.
 // blk_P / blk_z non-null (never with topk_in): per-chunk router-distribution
 // sums [n_chunks, E] and logsumexp^2 sums [n_chunks] for the statistics.
+// K2 > 0: also the ranks K .. K+K2-1 of every token (alt_idx / alt_w [T, K2],
+// weights normalised like the first K) for re-routing.
 hipError_t launch_router_topk(float* logits, const float* part, int S, const float* bias, const float* sel_bias,
-                              int32_t* idx, float* w, int32_t* blk_count, float* blk_P, float* blk_z, int64_t T,
-                              int64_t E, int64_t K, int gate, bool renorm, bool topk_in, hipStream_t s);
+                              int32_t* idx, float* w, int32_t* blk_count, float* blk_P, float* blk_z, int32_t* alt_idx,
+                              float* alt_w, int64_t K2, int64_t T, int64_t E, int64_t K, int gate, bool renorm,
+                              bool topk_in, hipStream_t s);
 
 // ---- permutation (a4) and dispatch (a5) ----
 // stats non-null: also folds blk_P / blk_z into the router statistics
 // (E + 6 doubles).
+// first_counts non-null: second scan of re-routing (kept = first-pass kept +
+// what fits of this pass's demand).  dem_off non-null: also the exclusive
+// scan of the demand (segments of the affinity drop).
 hipError_t launch_route_scan(const int32_t* blk_count, int32_t* blk_base, int32_t* counts, int32_t* offsets,
                              int64_t n_chunks, int64_t E, int64_t cap, const float* blk_P, const float* blk_z,
-                             double* stats, int64_t T, int64_t K, hipStream_t s);
-hipError_t launch_route_scatter(const int32_t* idx, const int32_t* blk_base, const int32_t* offsets, int32_t* dest,
-                                int32_t* row_src, uint8_t* dropped, int64_t T, int64_t K, int64_t E, int64_t cap,
-                                hipStream_t s);
+                             double* stats, int64_t T, int64_t K, const int32_t* first_counts, int32_t* dem_off,
+                             hipStream_t s);
+
+// Capacity drop policy of the scatter (kernel comments give each mode).
+enum ScatterMode { kFirstCome = 0, kAffinity = 1, kReroute1 = 2, kReroute2 = 3 };
+
+// Arrays of one scatter launch; unused ones may be null.
+struct RouteScatter {
+  int mode;                 // ScatterMode
+  const int32_t* idx;       // the expert ranked for each assignment (-1 or >= E: none)
+  const int32_t* blk_base;  // [chunks, E] rank base of each chunk
+  const int32_t* offsets;   // [E + 1] final row offsets (unused by kReroute1)
+  int32_t* dest;
+  int32_t* row_src;
+  uint8_t* dropped;
+  const int32_t* counts;    // kAffinity: demand per expert
+  const int32_t* dem_off;   // kAffinity: exclusive scan of the demand
+  const float* aff;         // kAffinity: affinity of each assignment (its gate weight)
+  uint64_t* seg;            // kAffinity: [T*K] keys, expert e's segment at dem_off[e]
+  const int32_t* alt_idx;   // kReroute1: [T, K2] rank-(K+j) expert of each token
+  const float* alt_w;       // kReroute1: [T, K2] its weight
+  int K2;
+  int32_t* pos1;            // first-pass rank of kept assignments, -1 when overflowing
+  int32_t* cand;            // re-routing candidate expert of each assignment or -1
+  float* cand_w;            // its weight
+  int32_t* blk_count2;      // kReroute1: [chunks, E] candidates per chunk
+  const int32_t* first_counts;  // kReroute2: first-pass demand
+  int32_t* topk_idx;        // kReroute2: re-routed assignments get their new expert
+  float* topk_w;            //            and weight
+};
+hipError_t launch_route_scatter(const RouteScatter& r, int64_t T, int64_t K, int64_t E, int64_t cap, hipStream_t s);
+hipError_t launch_route_affinity(const uint64_t* seg, const int32_t* counts, const int32_t* dem_off,
+                                 const int32_t* offsets, int32_t* dest, int32_t* row_src, uint8_t* dropped, int64_t E,
+                                 int64_t cap, hipStream_t s);
 hipError_t launch_dispatch(const void* x, const int32_t* row_src, const int32_t* R_ptr, void* xp, int64_t max_rows,
                            int64_t K, int64_t row_bytes, hipStream_t s);
 

@@ -44,9 +44,11 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ offsets, int NB, int E, int Epad,
                                                           int cap, const float* __restrict__ blk_P,
                                                           const float* __restrict__ blk_z, double* __restrict__ stats,
-                                                          int T, int K) {
+                                                          int T, int K, const int32_t* __restrict__ first_counts,
+                                                          int32_t* __restrict__ dem_off) {
   __shared__ int part[1024];
   __shared__ int kept[1024];
+  __shared__ int dem[1024];
   __shared__ int total[1024];
   __shared__ double dpart[1024];
   __shared__ double red[7][16];
@@ -78,11 +80,19 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
     }
     if (sub == S - 1) {
       counts[e] = run;
-      kept[e] = min(run, cap);
+      if (first_counts) {
+        // second pass of re-routing: room left after the first pass
+        const int k1 = min(first_counts[e], cap);
+        kept[e] = k1 + min(run, cap - k1);
+      } else {
+        kept[e] = min(run, cap);
+      }
       total[e] = run;
+      dem[e] = run;
     }
   } else if (sub == S - 1) {
     kept[e] = 0;
+    dem[e] = 0;
   }
   __syncthreads();
   if (stats) {
@@ -124,16 +134,27 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
       stats[E + 5] = a[4];
     }
   }
-  // inclusive Hillis-Steele scan of kept[0 .. Epad) with the first Epad threads
+  // inclusive Hillis-Steele scans of kept[0 .. Epad) (and of the demand for
+  // dem_off) with the first Epad threads
   for (int off = 1; off < Epad; off <<= 1) {
-    int v = 0;
-    if (threadIdx.x < Epad && threadIdx.x >= off) v = kept[threadIdx.x - off];
+    int v = 0, w = 0;
+    if (threadIdx.x < Epad && threadIdx.x >= off) {
+      v = kept[threadIdx.x - off];
+      w = dem[threadIdx.x - off];
+    }
     __syncthreads();
-    if (threadIdx.x < Epad) kept[threadIdx.x] += v;
+    if (threadIdx.x < Epad) {
+      kept[threadIdx.x] += v;
+      dem[threadIdx.x] += w;
+    }
     __syncthreads();
   }
   if (threadIdx.x < E) offsets[threadIdx.x + 1] = kept[threadIdx.x];
   if (threadIdx.x == 0) offsets[0] = 0;
+  if (dem_off) {
+    if (threadIdx.x < E) dem_off[threadIdx.x + 1] = dem[threadIdx.x];
+    if (threadIdx.x == 0) dem_off[0] = 0;
+  }
 }
 
 // ------------------------------------------------------------ a4: scatter
@@ -144,24 +165,45 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
 // four waves in LDS, and a running per-expert count carries across passes.
 // pos(f) = blk_base[b][e] + (earlier passes) + (earlier waves) + rank, which
 // is the number of assignments before f in flat order with the same expert.
-__global__ __launch_bounds__(256) void route_scatter_kernel(const int32_t* __restrict__ idx,
-                                                            const int32_t* __restrict__ blk_base,
-                                                            const int32_t* __restrict__ offsets,
-                                                            int32_t* __restrict__ dest, int32_t* __restrict__ row_src,
-                                                            uint8_t* __restrict__ dropped, int T, int K, int E,
-                                                            int nbits, int cap) {
+//
+// What happens to an assignment past its expert's capacity depends on MODE:
+//   kFirstCome   it is dropped [TD §3.2];
+//   kAffinity    an expert over capacity has all its assignments written,
+//                in flat order, to its segment of `seg` as 64-bit keys
+//                (affinity, then the earlier assignment); route_affinity
+//                decides them [TD §5.2];
+//   kReroute1    first pass of re-routing [LN §3.2]: within-expert ranks of
+//                the kept ones go to pos1; the j-th overflowing choice of a
+//                token becomes a candidate for the token's rank-(K+j) expert
+//                (cand, cand_w), counted per chunk in blk_count2;
+//   kReroute2    second pass: candidates (idx = cand) ranked the same way
+//                take the room their expert has left; every dest is final.
+__device__ __forceinline__ uint64_t affinity_key(float a, int64_t f) {
+  uint32_t u = __float_as_uint(a + 0.0f);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)f);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void route_scatter_kernel(const RouteScatter a, const int T, const int K,
+                                                            const int E, const int nbits, const int cap) {
   __shared__ int running[1024];
   __shared__ int wcnt[4][1024];
+  __shared__ uint8_t ovf[MODE == kReroute1 ? kTopkTokens * 32 : 1];
+  __shared__ int hist2[MODE == kReroute1 ? 1024 : 1];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t f_begin = (int64_t)blockIdx.x * kTopkTokens * K;
   const int64_t f_end = min((int64_t)T * K, f_begin + (int64_t)kTopkTokens * K);
-  for (int e = threadIdx.x; e < E; e += 256) running[e] = blk_base[(int64_t)blockIdx.x * E + e];
+  for (int e = threadIdx.x; e < E; e += 256) {
+    running[e] = a.blk_base[(int64_t)blockIdx.x * E + e];
+    if constexpr (MODE == kReroute1) hist2[e] = 0;
+  }
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int64_t pass = f_begin; pass < f_end; pass += 256) {
     for (int q = threadIdx.x; q < 4 * E; q += 256) wcnt[q / E][q % E] = 0;
     __syncthreads();
     const int64_t f = pass + threadIdx.x;
-    int e = f < f_end ? idx[f] : -1;
+    int e = f < f_end ? a.idx[f] : -1;
     const bool valid = e >= 0 && e < E;  // out-of-range choices are dropped
     if (!valid) e = 0;
     uint64_t peers = __ballot(valid);
@@ -182,12 +224,164 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(const int32_t* __res
     __syncthreads();
     for (int q = threadIdx.x; q < E; q += 256) running[q] += wcnt[0][q] + wcnt[1][q] + wcnt[2][q] + wcnt[3][q];
     if (f < f_end) {
-      const bool keep = valid && pos < cap;
-      const int32_t d = keep ? offsets[e] + pos : -1;
-      dest[f] = d;
-      dropped[f] = keep ? 0 : 1;
-      if (keep) row_src[d] = (int32_t)f;
+      if constexpr (MODE == kFirstCome) {
+        const bool keep = valid && pos < cap;
+        const int32_t d = keep ? a.offsets[e] + pos : -1;
+        a.dest[f] = d;
+        a.dropped[f] = keep ? 0 : 1;
+        if (keep) a.row_src[d] = (int32_t)f;
+      } else if constexpr (MODE == kAffinity) {
+        if (valid && a.counts[e] > cap) {
+          a.seg[a.dem_off[e] + pos] = affinity_key(a.aff[f], f);
+        } else {
+          const int32_t d = valid ? a.offsets[e] + pos : -1;
+          a.dest[f] = d;
+          a.dropped[f] = valid ? 0 : 1;
+          if (valid) a.row_src[d] = (int32_t)f;
+        }
+      } else if constexpr (MODE == kReroute1) {
+        const bool keep = valid && pos < cap;
+        a.pos1[f] = keep ? pos : -1;
+        ovf[f - f_begin] = keep ? 0 : 1;
+      } else {
+        const int32_t p1 = a.pos1[f];
+        int32_t d = -1;
+        if (p1 >= 0) {
+          d = a.offsets[a.topk_idx[f]] + p1;
+        } else if (valid) {
+          const int k1 = min(a.first_counts[e], cap);
+          if (pos < cap - k1) d = a.offsets[e] + k1 + pos;
+          a.topk_idx[f] = e;
+          a.topk_w[f] = a.cand_w[f];
+        }
+        a.dest[f] = d;
+        a.dropped[f] = d >= 0 ? 0 : 1;
+        if (d >= 0) a.row_src[d] = (int32_t)f;
+      }
     }
+    __syncthreads();
+  }
+  if constexpr (MODE == kReroute1) {
+    // the j-th overflowing choice of token t (in k order) is offered to the
+    // token's rank-(K+j) expert
+    for (int64_t f = f_begin + threadIdx.x; f < f_end; f += 256) {
+      int32_t c = -1;
+      float cw = 0.0f;
+      if (ovf[f - f_begin]) {
+        const int64_t t = f / K;
+        int j = 0;
+        for (int64_t q = t * K; q < f; ++q) j += ovf[q - f_begin];
+        if (j < a.K2) {
+          c = a.alt_idx[t * a.K2 + j];
+          cw = a.alt_w[t * a.K2 + j];
+        }
+        if (c >= 0 && c < E) atomicAdd(&hist2[c], 1);
+        else c = -1;
+      }
+      a.cand[f] = c;
+      a.cand_w[f] = cw;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) a.blk_count2[(int64_t)blockIdx.x * E + e] = hist2[e];
+  }
+}
+
+// ------------------------------------------------------- a4: affinity drop
+// One workgroup per expert.  An expert over capacity keeps its `cap`
+// largest keys (affinity, then the earlier assignment) [TD §5.2]: a
+// most-significant-digit radix select (8 passes of 8 bits over the
+// expert's segment) finds the cap-th largest key, then one ordered pass
+// gives the kept assignments consecutive rows in flat order.  Experts within
+// capacity were finished by the scatter.
+__global__ __launch_bounds__(256) void route_affinity_kernel(const uint64_t* __restrict__ seg,
+                                                             const int32_t* __restrict__ counts,
+                                                             const int32_t* __restrict__ dem_off,
+                                                             const int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ dest, int32_t* __restrict__ row_src,
+                                                             uint8_t* __restrict__ dropped, int cap) {
+  __shared__ int hist[256];
+  __shared__ int sel_bin, sel_want;
+  __shared__ int wtot[4];
+  const int e = blockIdx.x;
+  const int n = counts[e];
+  if (n <= cap) return;
+  const uint64_t* s = seg + dem_off[e];
+  uint64_t thr = ~0ull;  // keep iff key >= thr (cap == 0 keeps none: keys never reach ~0)
+  if (cap > 0) {
+    uint64_t prefix = 0, pmask = 0;
+    int want = cap;  // rank (1 = largest) of the wanted key among keys matching the prefix
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      hist[threadIdx.x] = 0;
+      __syncthreads();
+      for (int i = threadIdx.x; i < n; i += 256) {
+        const uint64_t k = s[i];
+        if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255], 1);
+      }
+      __syncthreads();
+      if (threadIdx.x < 64) {
+        // lane l holds bins 4l .. 4l+3; suffix sums over the lanes above it
+        const int l = threadIdx.x;
+        const int c0 = hist[4 * l], c1 = hist[4 * l + 1], c2 = hist[4 * l + 2], c3 = hist[4 * l + 3];
+        const int local = c0 + c1 + c2 + c3;
+        int suf = local;
+        for (int off = 1; off < 64; off <<= 1) {
+          const int v = __shfl_down(suf, off, 64);
+          if (l + off < 64) suf += v;
+        }
+        const int above = suf - local;  // keys in bins above 4l+3
+        if (above < want && want <= suf) {
+          int acc = above, b;
+          if (acc + c3 >= want) {
+            b = 4 * l + 3;
+          } else {
+            acc += c3;
+            if (acc + c2 >= want) {
+              b = 4 * l + 2;
+            } else {
+              acc += c2;
+              if (acc + c1 >= want) {
+                b = 4 * l + 1;
+              } else {
+                acc += c1;
+                b = 4 * l;
+              }
+            }
+          }
+          sel_bin = b;
+          sel_want = want - acc;
+        }
+      }
+      __syncthreads();
+      prefix |= (uint64_t)sel_bin << shift;
+      pmask |= 0xFFull << shift;
+      want = sel_want;
+      __syncthreads();
+    }
+    thr = prefix;  // the cap-th largest key (keys are distinct)
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int base = offsets[e];
+  int run = 0;
+  for (int i0 = 0; i0 < n; i0 += 256) {
+    const int i = i0 + threadIdx.x;
+    const bool in = i < n;
+    const uint64_t k = in ? s[i] : 0ull;
+    const bool keep = in && cap > 0 && k >= thr;
+    const uint64_t bal = __ballot(keep);
+    if (lane == 0) wtot[wave] = __popcll(bal);
+    __syncthreads();
+    int before = run;
+    for (int q = 0; q < wave; ++q) before += wtot[q];
+    const int tot = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+    if (in) {
+      const int32_t f = (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+      const int32_t row = keep ? base + before + __popcll(bal & lt_mask) : -1;
+      dest[f] = row;
+      dropped[f] = keep ? 0 : 1;
+      if (keep) row_src[row] = f;
+    }
+    run += tot;
     __syncthreads();
   }
 }
@@ -271,27 +465,41 @@ __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t* __restri
 
 hipError_t launch_route_scan(const int32_t* blk_count, int32_t* blk_base, int32_t* counts, int32_t* offsets,
                              int64_t n_chunks, int64_t E, int64_t cap, const float* blk_P, const float* blk_z,
-                             double* stats, int64_t T, int64_t K, hipStream_t s) {
+                             double* stats, int64_t T, int64_t K, const int32_t* first_counts, int32_t* dem_off,
+                             hipStream_t s) {
   int Epad = 1;
   while (Epad < E) Epad <<= 1;
   const int capi = cap < 0 || cap > INT_MAX ? INT_MAX : (int)cap;
   prof_begin(K_ROUTE_SCAN, s);
   route_scan_kernel<<<1, 1024, 0, s>>>(blk_count, blk_base, counts, offsets, (int)n_chunks, (int)E, Epad, capi,
-                                       blk_P, blk_z, stats, (int)T, (int)K);
+                                       blk_P, blk_z, stats, (int)T, (int)K, first_counts, dem_off);
   prof_end(K_ROUTE_SCAN, s);
   return hipGetLastError();
 }
 
-hipError_t launch_route_scatter(const int32_t* idx, const int32_t* blk_base, const int32_t* offsets, int32_t* dest,
-                                int32_t* row_src, uint8_t* dropped, int64_t T, int64_t K, int64_t E, int64_t cap,
-                                hipStream_t s) {
+hipError_t launch_route_scatter(const RouteScatter& r, int64_t T, int64_t K, int64_t E, int64_t cap, hipStream_t s) {
   int nbits = 0;
   while ((1ll << nbits) < E) ++nbits;
   const int capi = cap < 0 || cap > INT_MAX ? INT_MAX : (int)cap;
   const unsigned nb = (unsigned)((T + kTopkTokens - 1) / kTopkTokens);
+  const int Ti = (int)T, Ki = (int)K, Ei = (int)E;
   prof_begin(K_ROUTE_SCATTER, s);
-  route_scatter_kernel<<<nb, 256, 0, s>>>(idx, blk_base, offsets, dest, row_src, dropped, (int)T, (int)K, (int)E,
-                                          nbits, capi);
+  switch (r.mode) {
+    case kFirstCome: route_scatter_kernel<kFirstCome><<<nb, 256, 0, s>>>(r, Ti, Ki, Ei, nbits, capi); break;
+    case kAffinity: route_scatter_kernel<kAffinity><<<nb, 256, 0, s>>>(r, Ti, Ki, Ei, nbits, capi); break;
+    case kReroute1: route_scatter_kernel<kReroute1><<<nb, 256, 0, s>>>(r, Ti, Ki, Ei, nbits, capi); break;
+    default: route_scatter_kernel<kReroute2><<<nb, 256, 0, s>>>(r, Ti, Ki, Ei, nbits, capi); break;
+  }
+  prof_end(K_ROUTE_SCATTER, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_affinity(const uint64_t* seg, const int32_t* counts, const int32_t* dem_off,
+                                 const int32_t* offsets, int32_t* dest, int32_t* row_src, uint8_t* dropped, int64_t E,
+                                 int64_t cap, hipStream_t s) {
+  const int capi = cap < 0 || cap > INT_MAX ? INT_MAX : (int)cap;
+  prof_begin(K_ROUTE_SCATTER, s);
+  route_affinity_kernel<<<(unsigned)E, 256, 0, s>>>(seg, counts, dem_off, offsets, dest, row_src, dropped, capi);
   prof_end(K_ROUTE_SCATTER, s);
   return hipGetLastError();
 }

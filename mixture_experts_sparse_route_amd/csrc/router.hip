@@ -242,8 +242,10 @@ __global__ __launch_bounds__(256) void router_topk_kernel(float* __restrict__ lo
                                                           int S, const float* __restrict__ bias,
                                                           const float* __restrict__ sel_bias, int32_t* __restrict__ idx,
                                                           float* __restrict__ w, int32_t* __restrict__ blk_count,
-                                                          float* __restrict__ blk_P, float* __restrict__ blk_z, int T,
-                                                          int E, int K, int L, int gate, int renorm, int topk_in) {
+                                                          float* __restrict__ blk_P, float* __restrict__ blk_z,
+                                                          int32_t* __restrict__ alt_idx, float* __restrict__ alt_w,
+                                                          int K2, int T, int E, int K, int L, int gate, int renorm,
+                                                          int topk_in) {
   __shared__ int hist[1024];
   __shared__ float wsum[STATS ? 4 : 1][STATS ? 1024 : 1];
   __shared__ float wz[4];
@@ -302,10 +304,11 @@ __global__ __launch_bounds__(256) void router_topk_kernel(float* __restrict__ lo
         }
       }
       // K rounds of group max; lane ll == k keeps choice k and its logit,
-      // fetched from the lane that holds that expert.
-      int my_e = -1;
-      float my_l = -INFINITY;
-      for (int k = 0; k < K; ++k) {
+      // fetched from the lane that holds that expert.  K2 more rounds give
+      // the re-routing alternates (ranks K .. K+K2-1), kept by lane k - K.
+      int my_e = -1, alt_e = -1;
+      float my_l = -INFINITY, alt_l = -INFINITY;
+      for (int k = 0; k < K + K2; ++k) {
         uint64_t m = 0;
 #pragma unroll
         for (int p = 0; p < P; ++p) m = pk[p] > m ? pk[p] : m;
@@ -323,6 +326,10 @@ __global__ __launch_bounds__(256) void router_topk_kernel(float* __restrict__ lo
         if (ll == k) {
           my_e = e;
           my_l = le;
+        }
+        if (ll == k - K) {
+          alt_e = e;
+          alt_l = le;
         }
       }
       // weights
@@ -345,11 +352,20 @@ __global__ __launch_bounds__(256) void router_topk_kernel(float* __restrict__ lo
         if (valid && my_e >= 0) {
           w[(int64_t)t * K + ll] = mine / (renorm ? z_sel : z_all);
         }
+        if (valid && alt_e >= 0) {
+          alt_idx[(int64_t)t * K2 + ll] = alt_e;
+          alt_w[(int64_t)t * K2 + ll] = expf(alt_l - top) / (renorm ? z_sel : z_all);
+        }
       } else {
         if (my_e >= 0) mine = (float)(1.0 / (1.0 + exp(-(double)my_l)));
         contrib = mine;
         const float z_sel = group_sum(contrib, L);
         if (valid && my_e >= 0) w[(int64_t)t * K + ll] = renorm ? mine / z_sel : mine;
+        if (valid && alt_e >= 0) {
+          const float sa = (float)(1.0 / (1.0 + exp(-(double)alt_l)));
+          alt_idx[(int64_t)t * K2 + ll] = alt_e;
+          alt_w[(int64_t)t * K2 + ll] = renorm ? sa / z_sel : sa;
+        }
       }
       if (valid && my_e >= 0) {
         idx[(int64_t)t * K + ll] = my_e;
@@ -442,8 +458,9 @@ hipError_t launch_router_logits(bool bf16, const void* x, const float* Wg, const
 }
 
 hipError_t launch_router_topk(float* logits, const float* part, int S, const float* bias, const float* sel_bias,
-                              int32_t* idx, float* w, int32_t* blk_count, float* blk_P, float* blk_z, int64_t T,
-                              int64_t E, int64_t K, int gate, bool renorm, bool topk_in, hipStream_t s) {
+                              int32_t* idx, float* w, int32_t* blk_count, float* blk_P, float* blk_z, int32_t* alt_idx,
+                              float* alt_w, int64_t K2, int64_t T, int64_t E, int64_t K, int gate, bool renorm,
+                              bool topk_in, hipStream_t s) {
   int L = 1;
   while (L < E && L < 64) L <<= 1;
   const int P = (int)((E + L - 1) / L);
@@ -453,12 +470,12 @@ hipError_t launch_router_topk(float* logits, const float* part, int S, const flo
   do {                                                                                                           \
     if (blk_P)                                                                                                   \
       router_topk_kernel<PP, true><<<nb, 256, 0, s>>>(logits, part, S, bias, sel_bias, idx, w, blk_count, blk_P,  \
-                                                      blk_z, (int)T, (int)E, (int)K, L, gate, renorm ? 1 : 0,     \
-                                                      topk_in ? 1 : 0);                                           \
+                                                      blk_z, alt_idx, alt_w, (int)K2, (int)T, (int)E, (int)K, L,  \
+                                                      gate, renorm ? 1 : 0, topk_in ? 1 : 0);                     \
     else                                                                                                         \
       router_topk_kernel<PP, false><<<nb, 256, 0, s>>>(logits, part, S, bias, sel_bias, idx, w, blk_count,        \
-                                                       nullptr, nullptr, (int)T, (int)E, (int)K, L, gate,         \
-                                                       renorm ? 1 : 0, topk_in ? 1 : 0);                          \
+                                                       nullptr, nullptr, alt_idx, alt_w, (int)K2, (int)T, (int)E, \
+                                                       (int)K, L, gate, renorm ? 1 : 0, topk_in ? 1 : 0);         \
   } while (0)
   if (P <= 1)
     MOE_TOPK(1);

@@ -69,14 +69,16 @@ class Case:
         self._route = None
 
     # ---------------------------------------------------------- GPU side --
-    def gpu_forward(self, residual=False, logits_in=None, topk_in=None, out_dtype=None, stats=False):
+    def gpu_forward(self, residual=False, logits_in=None, topk_in=None, out_dtype=None, stats=False,
+                    drop_policy="first_come"):
         """moe_forward through the C-ABI.  logits_in: fp32 [T, E] host array;
         topk_in: (idx int32 [T, K], w fp32 [T, K]) host arrays; out_dtype:
         "f32" or "bf16" (default: the layer's dtype); stats: also write the
-        router statistics (Routing.statistics())."""
+        router statistics (Routing.statistics()); drop_policy: a key of
+        moe.DROP_POLICIES."""
         wl = self.wl
         spec = spec_of(wl, residual=residual, logits_in=logits_in is not None, topk_in=topk_in is not None,
-                       out_dtype=out_dtype, stats=stats)
+                       out_dtype=out_dtype, stats=stats, drop_policy=drop_policy)
         r = moe.Routing(spec)
         if logits_in is not None:
             r.logits.copy_(torch.from_numpy(np.ascontiguousarray(logits_in, dtype=np.float32)))

@@ -175,3 +175,20 @@ def test_routing_struct_matches_the_header():
     names = re.findall(r"\*\s*(\w+);", body)
     assert names == [f[0] for f in moe.MoeRouting._fields_]
     assert ctypes.sizeof(moe.MoeRouting) == 8 * len(names)
+
+
+def test_drop_policy_validation(lib):
+    """drop_policy: known values only; re-routing needs logits; the policies'
+    scratch arrays enlarge the workspace only when capacity is on."""
+    n = ctypes.c_size_t()
+    c = spec(capacity_factor=1.0).config()
+    c.drop_policy = 3
+    assert lib.moe_workspace_size(ctypes.byref(c), ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
+    c = spec(capacity_factor=1.0, drop_policy="reroute", topk_in=True).config()
+    assert lib.moe_workspace_size(ctypes.byref(c), ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
+    assert b"MOE_DROP_REROUTE" in lib.moe_last_error()
+    base = moe.workspace_size(spec(tokens=4096, capacity_factor=1.0))
+    for p in ("affinity", "reroute"):
+        assert moe.workspace_size(spec(tokens=4096, capacity_factor=1.0, drop_policy=p)) > base
+        assert moe.workspace_size(spec(tokens=4096, drop_policy=p)) == moe.workspace_size(spec(tokens=4096))
+    assert moe.workspace_size(spec(capacity_factor=1.0, drop_policy="affinity", topk_in=True)) > 0

@@ -1,0 +1,179 @@
+"""GPU parity of the capacity drop policies against the oracle.
+
+  affinity  an expert over capacity keeps its highest-affinity assignments
+            (DeepSeek-V2 token dropping, Tech Daily 2026-04-14 §5.2);
+  reroute   overflow goes to the token's next-best expert (lnwmold.com
+            article, §3.2).
+
+With identical fp32 logits (logits_in) the Top-K choice, the re-routing
+alternates and the first-come passes are decided on identical values, so the
+re-routed routing (final experts, counts, offsets, dest, row_src, drop mask)
+must be bit-exact.  The affinity drop ranks fp32 gate weights that the two
+sides compute independently (to a few ulps), so with logits_in it must be
+bit-exact on every expert whose cut is not a near-tie (the cap-th and next
+affinities closer than 1e-5 relative; counted and reported); with topk_in
+both sides rank the same caller weights and everything must be bit-exact.
+Outputs are held to the layer's tolerance against the oracle's forward on
+the oracle's routing.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+import oracle
+import mixture_experts_sparse_route_amd as moe
+from moe_synth import workload
+from parity_lib import (Case, assert_permutation_equal, assert_weights_close, assert_y_close, dev, host_f64,
+                        kept_tokens, routing_host, spec_of)
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU parity tests need a GPU"
+    moe.load_library()
+    moe_synth.build(force=False)
+    oracle.build(force=False)
+
+
+CASES = {
+    "switch_small": workload("switch_top1_capacity", T=1000, d=256, F=128, E=16),
+    "switch_tight": workload("switch_top1_capacity", T=700, d=128, F=64, E=8, capacity_factor=0.6),
+    "mixtral_capacity": workload("mixtral_prefill", T=400, d=256, F=128, capacity_factor=1.0),
+    "deepseek_capacity": workload("deepseek_v3_fine", T=150, d=256, F=64, E=64, Fs=64, capacity_factor=1.0),
+    "fp32_capacity": workload("tiny_top2_fp32", T=90, d=40, F=24, E=6, capacity_factor=0.8),
+    "k6_of_12": workload("mixtral_prefill", T=160, d=128, F=64, E=12, K=6, capacity_factor=0.9),
+}
+
+
+def near_tie_experts(o_idx, aff32, cap, E):
+    """Experts over capacity whose cap-th and (cap+1)-th affinities are within
+    1e-5 relative: the cut there is a rounding-level decision."""
+    fi, a = o_idx.reshape(-1), aff32.reshape(-1).astype(np.float64)
+    amb = []
+    for e in range(E):
+        v = np.sort(a[fi == e])[::-1]
+        if len(v) > cap and cap > 0 and v[cap - 1] - v[cap] <= 1e-5 * abs(v[cap - 1]):
+            amb.append(e)
+    return amb
+
+
+def check_policy(case: Case, policy: str):
+    wl = case.wl
+    T, K, E = wl.T, wl.K, wl.E
+    lg = case.oracle_route()["logits"]
+    orc = oracle.route(case.L, None, None, sel_bias=case.h["sel_bias"], policy=policy, lg=lg)
+    cap = oracle.capacity(case.L)
+    assert orc["dropped"].sum() > 0 or policy == "reroute", "case exercises no capacity drop"
+    report = {"dropped": int(orc["dropped"].sum())}
+    y, r = case.gpu_forward(logits_in=lg, out_dtype="f32", drop_policy=policy)
+    g = routing_host(r)
+    assert np.array_equal(g["idx"], orc["idx"]), "final experts differ"
+    assert_weights_close(g["w"], orc["w"], policy)
+    rows = None
+    if policy == "reroute":
+        report["rerouted"] = int(np.sum(orc["idx"] != orc["idx_first"]))
+        assert_permutation_equal(g, orc, policy)
+    else:
+        amb = near_tie_experts(orc["idx"], orc["w"].astype(np.float32), cap, E)
+        report["near_tie_experts"] = len(amb)
+        ok = ~np.isin(orc["idx"].reshape(-1), amb)
+        assert np.array_equal(g["counts"], orc["counts"]) and np.array_equal(g["offsets"], orc["offsets"])
+        assert np.array_equal(g["dest"][ok], orc["dest"][ok]), "affinity drop differs"
+        if amb:
+            rows = ~np.isin(np.arange(T), np.nonzero(~ok)[0] // K)   # compare tokens away from the near-ties
+    live = kept_tokens(orc["dest"], K, wl.n_shared)
+    if rows is not None:
+        live &= rows
+    y_ref = case.oracle_y(orc["idx"], orc["w"], orc["dest"])
+    report["err"] = assert_y_close(host_f64(y), y_ref, wl.dtype, rows=live, label=policy)
+    if policy == "affinity":
+        # the caller's weights as affinities: identical values on both sides
+        w32 = orc["w"].astype(np.float32)
+        o2 = oracle.permute_affinity(case.L, orc["idx"], w32)
+        _, r2 = case.gpu_forward(topk_in=(orc["idx"], w32), out_dtype="f32", drop_policy=policy)
+        assert_permutation_equal(routing_host(r2), o2, "affinity topk_in")
+    return report
+
+
+@pytest.mark.parametrize("policy", ["affinity", "reroute"])
+@pytest.mark.parametrize("name", list(CASES))
+def test_policy_small(name, policy):
+    print(name, policy, check_policy(Case(CASES[name]), policy))
+
+
+def test_reroute_page_example():
+    """Capacity 10 at C = 1.25, 1024 tokens, 128 experts; the expert chosen 15
+    times keeps the first 10 and the other 5 move to their second choice."""
+    g = json.load(open(os.path.join(GOLDEN, "reroute_page_example.json")))
+    wl = workload("switch_top1_capacity", T=g["T"], d=64, F=64, E=g["E"], capacity_factor=g["capacity_factor"],
+                  dtype="f32", logit_bias=None)
+    from test_oracle import _reroute_logits
+    lg = _reroute_logits(g)
+    case = Case(wl)
+    _, r = case.gpu_forward(logits_in=lg, out_dtype="f32", drop_policy="reroute")
+    h = routing_host(r)
+    orc = oracle.route(case.L, None, None, policy="reroute", lg=lg)
+    assert_permutation_equal(h, orc, "page example")
+    assert np.array_equal(h["idx"], orc["idx"])
+    for t, e in g["expect"]["rerouted"].items():
+        assert h["idx"][int(t), 0] == e and h["dest"][int(t)] >= 0
+    assert h["counts"][g["hot_expert"]] == g["expect"]["counts_hot"] and h["dropped"].sum() == 0
+
+
+def test_affinity_golden_through_moe_route():
+    g = json.load(open(os.path.join(GOLDEN, "affinity_drop_small.json")))
+    spec = moe.LayerSpec(tokens=g["T"], d_model=8, d_ff=8, n_experts=g["E"], top_k=g["K"],
+                         capacity_factor=g["capacity_factor"], dtype="f32", topk_in=True, drop_policy="affinity")
+    r = moe.Routing(spec)
+    r.topk_idx.copy_(torch.tensor(g["idx"], dtype=torch.int32).view(-1, 1))
+    r.topk_w.copy_(torch.tensor(g["aff"], dtype=torch.float32).view(-1, 1))
+    ws, _ = moe.alloc_workspace(spec)
+    moe.moe_route(spec, None, None, None, None, r, ws)
+    torch.cuda.synchronize()
+    h = routing_host(r)
+    for k, v in g["expect"].items():
+        got = h[k][: len(v)] if k == "row_src" else h[k]
+        want = v[: int(h["offsets"][-1])] if k == "row_src" else v
+        assert got[: len(want)].tolist() == want, k
+
+
+@pytest.mark.parametrize("policy", ["affinity", "reroute"])
+def test_policy_without_pressure_is_first_come(policy):
+    """A capacity no expert reaches: both policies give the first-come routing."""
+    case = Case(workload("mixtral_prefill", T=200, d=128, F=64, capacity_factor=8.0))
+    lg = case.oracle_route()["logits"]
+    _, r0 = case.gpu_forward(logits_in=lg, out_dtype="f32")
+    _, r1 = case.gpu_forward(logits_in=lg, out_dtype="f32", drop_policy=policy)
+    a, b = routing_host(r0), routing_host(r1)
+    for k in ("idx", "w", "counts", "offsets", "dest", "dropped"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("policy", ["affinity", "reroute"])
+def test_policy_full_size_switch(policy):
+    """The Switch workload (T=8192, E=64, C=1.25, Zipf-skewed router): routing
+    over all tokens, outputs on a sample."""
+    case = Case(workload("switch_top1_capacity"))
+    wl = case.wl
+    lg = case.oracle_route()["logits"]
+    orc = oracle.route(case.L, None, None, policy=policy, lg=lg)
+    _, r = case.gpu_forward(logits_in=lg, out_dtype="f32", drop_policy=policy)
+    g = routing_host(r)
+    assert np.array_equal(g["idx"], orc["idx"])
+    if policy == "reroute":
+        assert_permutation_equal(g, orc, policy)
+    else:
+        cap = oracle.capacity(case.L)
+        amb = near_tie_experts(orc["idx"], orc["w"].astype(np.float32), cap, wl.E)
+        ok = ~np.isin(orc["idx"].reshape(-1), amb)
+        assert np.array_equal(g["dest"][ok], orc["dest"][ok])
+        print("near-tie experts", len(amb))
+    print(policy, "dropped", int(orc["dropped"].sum()), "of", wl.T * wl.K)
