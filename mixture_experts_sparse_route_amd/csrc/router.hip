@@ -323,11 +323,12 @@ __global__ __launch_bounds__(256) void router_topk_kernel(float* __restrict__ lo
         for (int p = 1; p < P; ++p)
           if (p == pe) v = lv[p];
         const float le = __shfl(v, slot * L + oe, 64);
-        if (ll == k) {
-          my_e = e;
-          my_l = le;
-        }
-        if (ll == k - K) {
+        if (k < K) {
+          if (ll == k) {
+            my_e = e;
+            my_l = le;
+          }
+        } else if (ll == k - K) {
           alt_e = e;
           alt_l = le;
         }
