@@ -27,7 +27,7 @@ class OrcLayer(ctypes.Structure):
         ("T", ctypes.c_int64), ("d", ctypes.c_int64), ("F", ctypes.c_int64), ("E", ctypes.c_int64),
         ("K", ctypes.c_int64), ("gate", ctypes.c_int32), ("renorm", ctypes.c_int32),
         ("residual", ctypes.c_int32), ("bf16", ctypes.c_int32), ("capacity_factor", ctypes.c_double),
-        ("n_shared", ctypes.c_int64), ("Fs", ctypes.c_int64),
+        ("n_shared", ctypes.c_int64), ("Fs", ctypes.c_int64), ("round_h", ctypes.c_int32),
     ]
 
 
@@ -55,7 +55,9 @@ def _load():
         lib.orc_capacity.argtypes = [P]
         lib.orc_capacity.restype = i64
         lib.orc_permute.argtypes = [P, vp, vp, vp, vp, vp, vp]
-        lib.orc_swiglu.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp, i32]
+        lib.orc_swiglu.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, vp, i32]
+        lib.orc_bf16_round.argtypes = [ctypes.c_double]
+        lib.orc_bf16_round.restype = ctypes.c_double
         lib.orc_forward_rows.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]
         lib.orc_expert_choice.argtypes = [P, vp, i64, vp, vp]
         lib.orc_select_ranked.argtypes = [P, vp, vp, i64, vp, vp]
@@ -85,15 +87,23 @@ def _p(a):
 
 
 def layer(T, d, F, E, K, gate=GATE_SOFTMAX, renorm=True, residual=False, bf16=False, capacity_factor=0.0,
-          n_shared=0, Fs=0) -> OrcLayer:
+          n_shared=0, Fs=0, round_h=None) -> OrcLayer:
+    """round_h: store the SwiGLU output h in bf16 (default: for bf16 layers)."""
+    rh = bf16 if round_h is None else round_h
     return OrcLayer(T, d, F, E, K, gate, int(renorm), int(residual), int(bf16), float(capacity_factor),
-                    n_shared, Fs)
+                    n_shared, Fs, int(rh))
 
 
-def layer_of(wl, residual=False) -> OrcLayer:
+def layer_of(wl, residual=False, round_h=None) -> OrcLayer:
     """OrcLayer for a ``moe_synth`` workload."""
     return layer(wl.T, wl.d, wl.F, wl.E, wl.K, gate=wl.gate, renorm=wl.renorm, residual=residual,
-                 bf16=(wl.dtype == "bf16"), capacity_factor=wl.capacity_factor, n_shared=wl.n_shared, Fs=wl.Fs)
+                 bf16=(wl.dtype == "bf16"), capacity_factor=wl.capacity_factor, n_shared=wl.n_shared, Fs=wl.Fs,
+                 round_h=round_h)
+
+
+def bf16_round(v: float) -> float:
+    """v rounded to the nearest bf16 value, ties to even."""
+    return float(_load().orc_bf16_round(float(v)))
 
 
 def threads() -> int:
@@ -178,11 +188,11 @@ def alternates(L: OrcLayer, lg, sel_bias=None):
     return np.ascontiguousarray(ridx[:, L.K:]), np.ascontiguousarray(rw[:, L.K:])
 
 
-def swiglu(W1, W3, W2, x, bf16: bool, threads: int = 1) -> np.ndarray:
+def swiglu(W1, W3, W2, x, bf16: bool, threads: int = 1, round_h: bool = False) -> np.ndarray:
     """One expert on one row: W1, W3 [F, d], W2 [d, F]; x float64 [d]."""
     F, d = W1.shape
     out = np.empty(d, dtype=np.float64)
-    _load().orc_swiglu(d, F, int(bf16), _p(np.ascontiguousarray(W1)), _p(np.ascontiguousarray(W3)),
+    _load().orc_swiglu(d, F, int(bf16), int(round_h), _p(np.ascontiguousarray(W1)), _p(np.ascontiguousarray(W3)),
                        _p(np.ascontiguousarray(W2)), _p(np.ascontiguousarray(x, dtype=np.float64)), _p(out),
                        threads)
     return out

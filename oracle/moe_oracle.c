@@ -311,8 +311,19 @@ void orc_permute_reroute(const orc_layer* L, const int32_t* idx, const double* w
 
 /* ---- a6 + a7: one SwiGLU expert on one row  [LN §2.2] -------------------- */
 
-void orc_swiglu(int64_t d, int64_t F, int32_t bf16, const void* W1, const void* W3, const void* W2,
-                const double* x, double* out, int32_t threads) {
+double orc_bf16_round(double v) {
+  /* bf16 keeps 8 significant bits and fp32's exponent range: round v to
+   * that grid, ties to even (the default rounding mode of nearbyint). */
+  if (v == 0.0 || !isfinite(v)) return v;
+  const double min_normal = ldexp(1.0, -126);
+  if (fabs(v) < min_normal) return ldexp(nearbyint(ldexp(v, 133)), -133); /* subnormal spacing 2^-133 */
+  int e;
+  const double m = frexp(v, &e); /* v = m * 2^e, 0.5 <= |m| < 1 */
+  return ldexp(nearbyint(ldexp(m, 8)), e - 8);
+}
+
+void orc_swiglu(int64_t d, int64_t F, int32_t bf16, int32_t round_h, const void* W1, const void* W3,
+                const void* W2, const double* x, double* out, int32_t threads) {
   double* h = (double*)malloc(sizeof(double) * (size_t)F);
   int nt = threads > 1 ? threads : 1;
 #pragma omp parallel for schedule(static) num_threads(nt) if (nt > 1)
@@ -324,6 +335,8 @@ void orc_swiglu(int64_t d, int64_t F, int32_t bf16, const void* W1, const void* 
     }
     double silu = a / (1.0 + exp(-a));
     h[j] = silu * b;
+    /* a bf16 layer holds its activations, h included, in bf16 */
+    if (round_h) h[j] = orc_bf16_round(h[j]);
   }
 #pragma omp parallel for schedule(static) num_threads(nt) if (nt > 1)
   for (int64_t m = 0; m < d; ++m) {
@@ -362,7 +375,7 @@ void orc_forward_rows(const orc_layer* L, const void* x, const int32_t* idx, con
     for (int64_t k = 0; k < K; ++k) {
       if (dest && dest[t * K + k] < 0) continue;
       const int32_t e = idx[t * K + k];
-      orc_swiglu(d, F, L->bf16, W1e[e], W3e[e], W2e[e], xt, o, inner);
+      orc_swiglu(d, F, L->bf16, L->round_h, W1e[e], W3e[e], W2e[e], xt, o, inner);
       for (int64_t i = 0; i < d; ++i) acc[i] += w[t * K + k] * o[i];
     }
     /* always-active shared experts, added unweighted  [TD §3.4; §9.1] */
@@ -370,7 +383,7 @@ void orc_forward_rows(const orc_layer* L, const void* x, const int32_t* idx, con
       const char* p1 = (const char*)Ws1 + (size_t)(s * Fs * d) * esz;
       const char* p3 = (const char*)Ws3 + (size_t)(s * Fs * d) * esz;
       const char* p2 = (const char*)Ws2 + (size_t)(s * d * Fs) * esz;
-      orc_swiglu(d, Fs, L->bf16, p1, p3, p2, xt, o, inner);
+      orc_swiglu(d, Fs, L->bf16, L->round_h, p1, p3, p2, xt, o, inner);
       for (int64_t i = 0; i < d; ++i) acc[i] += o[i];
     }
     /* residual Add of the MoE block  [TD §2.1] */

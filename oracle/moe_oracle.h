@@ -54,6 +54,10 @@ typedef struct orc_layer {
   double capacity_factor; /* <= 0: no capacity limit */
   int64_t n_shared; /* always-active shared experts */
   int64_t Fs;       /* shared expert d_ff */
+  /* 1: the SwiGLU output h is stored in bf16 (rounded to nearest even) before
+   * the down projection, as a bf16 layer stores its activations; 0: h stays
+   * in double */
+  int32_t round_h;
 } orc_layer;
 
 /* a1. logits[t][e] = fp32( sum_i x[t][i] * Wg[e][i] + logit_bias[e] )  [TD §3.1 step 1]
@@ -110,13 +114,18 @@ void orc_permute_reroute(const orc_layer* L, const int32_t* idx, const double* w
                          const double* alt_w, int64_t n_alt, int32_t* counts, int32_t* offsets, int32_t* dest,
                          int32_t* row_src, uint8_t* dropped, int32_t* idx_out, double* w_out);
 
+/* v rounded to the nearest bf16 value (8 significant bits, fp32 exponent
+ * range), ties to even. */
+double orc_bf16_round(double v);
+
 /* a6 + a7 for one row and one expert:
  *   out[m] = sum_j W2[m][j] * h_j,   h_j = SiLU(a_j) * b_j,  SiLU(z) = z / (1 + e^-z),
  *   a_j = sum_i W1[j][i] x[i],  b_j = sum_i W3[j][i] x[i].          [LN §2.2]
- * W1, W3: [F][d]; W2: [d][F]; bf16 or fp32 per `bf16`; x, out in double.
+ * W1, W3: [F][d]; W2: [d][F]; bf16 or fp32 per `bf16`; x, out in double;
+ * h_j replaced by orc_bf16_round(h_j) when round_h.
  * If `threads` > 1 the output loops are split across OpenMP threads. */
-void orc_swiglu(int64_t d, int64_t F, int32_t bf16, const void* W1, const void* W3, const void* W2,
-                const double* x, double* out, int32_t threads);
+void orc_swiglu(int64_t d, int64_t F, int32_t bf16, int32_t round_h, const void* W1, const void* W3,
+                const void* W2, const double* x, double* out, int32_t threads);
 
 /* a6-a9 for the listed tokens:
  *   y[j] = sum_{k ascending, dest[t][k] >= 0} w[t][k] * E_{idx[t][k]}(x_t)

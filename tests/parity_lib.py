@@ -32,7 +32,12 @@ import mixture_experts_sparse_route_amd as moe
 
 NEAR_TIE = 1e-4
 F32_TOL = 1e-4
+# bf16 layers: max |y - r| <= 2e-2 * RMS(r) is the stated bound; against the
+# oracle that stores h in bf16 as the layer does, the remaining differences
+# are fp32 accumulation and rare one-ulp differences in h's rounding, so the
+# tests hold the tighter 5e-3.
 BF16_TOL = 2e-2
+BF16_H_TOL = 5e-3
 
 
 def dev(a: np.ndarray | None):
@@ -101,9 +106,10 @@ class Case:
             self._route = oracle.route(self.L, h["x"], h["Wg"], h["logit_bias"], h["sel_bias"])
         return self._route
 
-    def oracle_y(self, idx, w, dest, tokens=None, residual=False):
+    def oracle_y(self, idx, w, dest, tokens=None, residual=False, round_h=None):
+        """round_h=False: h kept in double (no bf16 storage of the SwiGLU output)."""
         h = self.h
-        L = oracle.layer_of(self.wl, residual=residual)
+        L = oracle.layer_of(self.wl, residual=residual, round_h=round_h)
         return oracle.forward_rows(L, h["x"], idx, w, dest, h["W1"], h["W3"], h["W2"], h["Ws1"], h["Ws3"], h["Ws2"],
                                    tokens=tokens)
 
@@ -147,7 +153,7 @@ def y_error(y_gpu: np.ndarray, y_ref: np.ndarray, dtype: str, rows=None):
     if dtype == "f32":
         den = np.maximum(np.abs(y_ref), rms)
         return float(np.max(np.abs(y_gpu - y_ref) / den)), F32_TOL
-    return float(np.max(np.abs(y_gpu - y_ref))) / rms, BF16_TOL
+    return float(np.max(np.abs(y_gpu - y_ref))) / rms, min(BF16_TOL, BF16_H_TOL)
 
 
 def assert_y_close(y_gpu: np.ndarray, y_ref: np.ndarray, dtype: str, rows=None, label=""):

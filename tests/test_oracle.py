@@ -277,6 +277,41 @@ def test_swiglu_vs_torch(bf16):
         np.testing.assert_allclose(got, torch_swiglu(*Wf, x), rtol=1e-12, atol=1e-14)
 
 
+def test_bf16_round():
+    """Against the integer round-to-nearest-even of fp32 bit patterns (values
+    that are exact in fp32, normal and subnormal) and at exact ties."""
+    r = rng(31)
+    f = np.concatenate([r.standard_normal(20000) * 10.0 ** r.integers(-30, 30, 20000),
+                        r.standard_normal(2000) * 1e-39]).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    want = (((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16).astype(np.uint32).view(np.float32)
+    got = np.array([oracle.bf16_round(float(v)) for v in f])
+    assert np.array_equal(got, want.astype(np.float64))
+    one_ulp = 2.0 ** -7
+    assert oracle.bf16_round(1 + one_ulp / 2) == 1.0                   # tie to the even 1.0
+    assert oracle.bf16_round(1 + 3 * one_ulp / 2) == 1 + 2 * one_ulp    # tie to the even mantissa
+    assert oracle.bf16_round(-(1 + one_ulp / 2)) == -1.0
+    assert oracle.bf16_round(1 + one_ulp / 2 + 2.0 ** -40) == 1 + one_ulp  # above the tie (not fp32-exact)
+    assert oracle.bf16_round(0.0) == 0.0
+
+
+def test_swiglu_round_h_vs_torch():
+    """round_h: h stored as bf16 before W2 (torch's bf16 cast of the fp32 h;
+    the fp32 step rounds twice only inside a 2^-29-wide window that random
+    data does not hit)."""
+    r = rng(32)
+    d, F = 48, 80
+    W = [moe_synth.f32_to_bf16(r.standard_normal(s).astype(np.float32) / 5) for s in ((F, d), (F, d), (d, F))]
+    Wf = [torch.from_numpy(moe_synth.bf16_to_f32(a).astype(np.float64)) for a in W]
+    x = r.standard_normal(d)
+    xt = torch.from_numpy(x)
+    hh = torch.nn.functional.silu(Wf[0] @ xt) * (Wf[1] @ xt)
+    want = (Wf[2] @ hh.float().bfloat16().double()).numpy()
+    got = oracle.swiglu(*W, x, bf16=True, round_h=True)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14)
+    assert not np.allclose(got, oracle.swiglu(*W, x, bf16=True), rtol=1e-6, atol=0)
+
+
 def test_swiglu_closed_forms():
     r = rng(10)
     d, F = 16, 24

@@ -23,7 +23,7 @@ import oracle
 import mixture_experts_sparse_route_amd as moe
 from moe_synth import workload
 from parity_lib import (NEAR_TIE, Case, assert_permutation_equal, assert_weights_close, assert_y_close, dev,
-                        host_f64, kept_tokens, routing_host, spec_of)
+                        host_f64, kept_tokens, routing_host, spec_of, y_error)
 
 pytestmark = pytest.mark.gpu
 
@@ -84,6 +84,10 @@ def check_case(case: Case, tokens=None, residual=False):
         assert_permutation_equal(g, orc, "free")
         yg = host_f64(y)[rows]
         report["err_free"] = assert_y_close(yg, y_ref, wl.dtype, rows=live, label="free")
+        if wl.dtype == "bf16":
+            # for information: against h kept in double (the cost of bf16 storage included)
+            y64 = case.oracle_y(orc["idx"], orc["w"], orc["dest"], tokens=rows, residual=residual, round_h=False)
+            report["err_vs_unrounded_h"] = y_error(yg, y64, wl.dtype, rows=live)[0]
         if dead.any():
             xf = case.h["x"] if wl.dtype == "f32" else moe_synth.bf16_to_f32(case.h["x"])
             want = xf.astype(np.float64)[rows][dead] if residual else 0.0
