@@ -264,6 +264,49 @@ def expert_choice(L: OrcLayer, lg, cap: int):
     return tok, g
 
 
+def ec_capacity(L: OrcLayer) -> int:
+    """Tokens each expert takes under expert choice: floor(C * T * K / E) with
+    C = capacity_factor (1 when C <= 0), at most T -- the token-choice
+    capacity formula [TD §3.2], so both routings process about C*T*K
+    (token, expert) pairs."""
+    c = L.capacity_factor if L.capacity_factor > 0 else 1.0
+    return min(int(np.floor(c * L.T * L.K / L.E)), L.T)
+
+
+def ec_layer(L: OrcLayer) -> OrcLayer:
+    """The layer seen as K = E token choice with a drop mask: assignment
+    (t, e) is expert e, kept iff expert e chose token t."""
+    return OrcLayer(L.T, L.d, L.F, L.E, L.E, L.gate, 0, L.residual, L.bf16, 0.0, L.n_shared, L.Fs, L.round_h)
+
+
+def route_expert_choice(L: OrcLayer, x=None, Wg=None, logit_bias=None, lg=None):
+    """Expert-choice routing [TD §3.3]: S = the logits [T, E]; expert e takes
+    the ec_capacity(L) tokens with the largest S[:, e] (ties to the lower
+    token).  Returned in the K = E form of ec_layer(L): idx[t][e] = e,
+    w[t][e] = g (the token's softmax-over-experts probability of e) where e
+    chose t (NaN elsewhere), dest[t*E + e] = e * cap + (rank of t among the
+    tokens e chose, ascending t), or -1.  counts[e] = cap; offsets = e * cap."""
+    if lg is None:
+        lg = logits(L, x, Wg, logit_bias)
+    T, E = L.T, L.E
+    cap = ec_capacity(L)
+    tok, g = expert_choice(L, lg, cap)
+    idx = np.tile(np.arange(E, dtype=np.int32), (T, 1))
+    w = np.full((T, E), np.nan)
+    dest = np.full(T * E, -1, np.int32)
+    row_src = np.full(T * E, -1, np.int32)
+    for e in range(E):
+        order = np.argsort(tok[e], kind="stable")
+        for rank, c in enumerate(order):
+            t = int(tok[e, c])
+            w[t, e] = g[e, c]
+            dest[t * E + e] = e * cap + rank
+            row_src[e * cap + rank] = t * E + e
+    return dict(logits=lg, idx=idx, w=w, dest=dest, row_src=row_src, dropped=(dest < 0).astype(np.uint8),
+                counts=np.full(E, cap, np.int32), offsets=(np.arange(E + 1) * cap).astype(np.int32), cap=cap,
+                tok=tok, g=g)
+
+
 POLICIES = ("first_come", "affinity", "reroute")
 
 

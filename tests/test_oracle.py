@@ -680,3 +680,40 @@ def test_reroute_invariants_and_special_cases():
     a, b = oracle.route(L, None, None, policy="reroute", lg=lg), oracle.route(L, None, None, lg=lg)
     for k in ("dest", "row_src", "dropped", "offsets", "idx"):
         assert np.array_equal(a[k], b[k]), k
+
+
+def test_expert_choice_route_and_forward():
+    """Expert choice in the K = E form: every expert holds exactly cap rows,
+    rows list the chosen tokens in ascending order, and the layer output
+    equals the direct sum over chosen (token, expert) pairs of g * E_e(x_t)
+    [TD §3.3]; a token no expert chose gets zero (plus its shared expert)."""
+    r = rng(24)
+    T, d, F, E, K = 30, 8, 6, 5, 1
+    L = oracle.layer(T, d, F, E, K, capacity_factor=1.4, n_shared=1, Fs=4)
+    cap = oracle.ec_capacity(L)
+    assert cap == int(np.floor(1.4 * T * K / E)) == 8
+    assert oracle.ec_capacity(oracle.layer(T, d, F, E, 2)) == 12
+    assert oracle.ec_capacity(oracle.layer(4, d, F, 2, 2, capacity_factor=9.0)) == 4   # at most T
+    lg = r.standard_normal((T, E)).astype(np.float32)
+    rt = oracle.route_expert_choice(L, lg=lg)
+    dest = rt["dest"].reshape(T, E)
+    for e in range(E):
+        chosen = sorted(rt["tok"][e].tolist())
+        assert np.nonzero(dest[:, e] >= 0)[0].tolist() == chosen
+        assert dest[chosen, e].tolist() == list(range(e * cap, (e + 1) * cap))
+    assert np.array_equal(rt["row_src"][dest[dest >= 0]], np.nonzero(rt["dest"] >= 0)[0])
+    x = r.standard_normal((T, d)).astype(np.float32)
+    W1, W3 = (r.standard_normal((E, F, d)).astype(np.float32) / 3 for _ in range(2))
+    W2 = r.standard_normal((E, d, F)).astype(np.float32) / 3
+    Ws1, Ws3 = (r.standard_normal((1, 4, d)).astype(np.float32) / 3 for _ in range(2))
+    Ws2 = r.standard_normal((1, d, 4)).astype(np.float32) / 3
+    y = oracle.forward_rows(oracle.ec_layer(L), x, rt["idx"], np.nan_to_num(rt["w"]), rt["dest"], W1, W3, W2,
+                            Ws1, Ws3, Ws2)
+    p = scipy.special.softmax(lg.astype(np.float64), axis=1)
+    for t in range(T):
+        want = torch_swiglu(Ws1[0], Ws3[0], Ws2[0], x[t].astype(np.float64))
+        for e in range(E):
+            if dest[t, e] >= 0:
+                want = want + p[t, e] * torch_swiglu(W1[e], W3[e], W2[e], x[t].astype(np.float64))
+        np.testing.assert_allclose(y[t], want, rtol=1e-12, atol=1e-13)
+    assert (dest < 0).all(1).any()          # some token was chosen by no expert
