@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel in an untimed extra pass")
     ap.add_argument("--stats", action="store_true", help="also compute the fused router statistics every step")
+    ap.add_argument("--drop-policy", default="first_come", choices=["first_come", "affinity", "reroute"],
+                    help="which assignments an expert over capacity drops")
+    ap.add_argument("--expert-choice", action="store_true", help="expert-choice routing instead of token choice")
     return ap.parse_args()
 
 
@@ -76,7 +79,7 @@ def kernel_accounting(wl, R: int, touched: int):
     return acc, layer_flops, layer_bytes
 
 
-def cpu_baseline(wl, h, budget_s: float):
+def cpu_baseline(wl, h, budget_s: float, policy: str = "first_come", expert_choice: bool = False):
     """The oracle as it stands on a bounded sample: routing of all T tokens
     (capacity needs every token), then tokens in blocks of 64 through the
     experts and combine until the budget is spent; the whole-layer time is
@@ -87,7 +90,13 @@ def cpu_baseline(wl, h, budget_s: float):
     oracle.build(force=False)
     L = oracle.layer_of(wl)
     t0 = time.perf_counter()
-    rt = oracle.route(L, h["x"], h["Wg"], h["logit_bias"], h["sel_bias"])
+    if expert_choice:
+        L.renorm = 0
+        rt = oracle.route_expert_choice(L, h["x"], h["Wg"], h["logit_bias"])
+        rt["w"] = np.nan_to_num(rt["w"])
+        L = oracle.ec_layer(L)
+    else:
+        rt = oracle.route(L, h["x"], h["Wg"], h["logit_bias"], h["sel_bias"], policy=policy)
     t_route = time.perf_counter() - t0
     done = 0
     t_rows = 0.0
@@ -137,8 +146,9 @@ def main():
     d = {k: dev(v) for k, v in h.items()}
     t_gen = time.perf_counter() - t_gen
     spec = moe.LayerSpec(tokens=wl.T, d_model=wl.d, d_ff=wl.F, n_experts=wl.E, top_k=wl.K, gate=wl.gate,
-                         renorm=wl.renorm, capacity_factor=wl.capacity_factor, n_shared=wl.n_shared,
-                         d_ff_shared=wl.Fs, dtype=wl.dtype, stats=args.stats)
+                         capacity_factor=wl.capacity_factor, n_shared=wl.n_shared,
+                         d_ff_shared=wl.Fs, dtype=wl.dtype, stats=args.stats, drop_policy=args.drop_policy,
+                         expert_choice=args.expert_choice, renorm=wl.renorm and not args.expert_choice)
     ws, _ = moe.alloc_workspace(spec)
     r = moe.Routing(spec)
     y = torch.empty((wl.T, wl.d), dtype=torch.bfloat16 if wl.dtype == "bf16" else torch.float32, device="cuda")
@@ -237,7 +247,9 @@ def main():
         "config": {"workload": wl.name, "tokens": wl.T, "d_model": wl.d, "d_ff": wl.F, "n_experts": wl.E,
                    "top_k": wl.K, "gate": "sigmoid" if wl.gate else "softmax", "renorm": wl.renorm,
                    "capacity_factor": wl.capacity_factor, "n_shared": wl.n_shared, "d_ff_shared": wl.Fs,
-                   "router_stats": args.stats, "parallelism": "single GPU"},
+                   "router_stats": args.stats, "drop_policy": args.drop_policy,
+                   "routing": "expert_choice" if args.expert_choice else "token_choice",
+                   "parallelism": "single GPU"},
         "roofline": roof,
         "layer": {"tflops": round(layer_flops / (ms_per_step * 1e-3) / 1e12, 2),
                   "algorithmic_gbps": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
@@ -248,7 +260,7 @@ def main():
     if breakdown:
         line["kernels_us"] = breakdown
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, h, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(wl, h, args.cpu_seconds, args.drop_policy, args.expert_choice)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

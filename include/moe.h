@@ -94,7 +94,19 @@ enum {
   MOE_F_TOPK_IN = 8u,
   /* moe_route / moe_forward also write the router statistics to
    * routing->stats (see below); not with MOE_F_TOPK_IN. */
-  MOE_F_STATS = 16u
+  MOE_F_STATS = 16u,
+  /* Expert-choice routing [TD §3.3]: the affinity matrix is the logits
+   * S [T, E]; expert e takes the cap = min(floor(C * T * top_k / E), T)
+   * tokens with the largest S[:, e] (C = capacity_factor, 1 when <= 0; ties
+   * to the lower token), so each expert processes exactly cap rows and a
+   * token may be taken by 0 .. E experts.  The routing arrays then have the
+   * K = E form: topk_idx / topk_w / dest / row_src / dropped are [T, E],
+   * entry (t, e) = expert e with weight p = the token's softmax over all E
+   * logits [TD §3.2], dest = e * cap + (rank of t among the tokens e took,
+   * ascending t) or -1; counts[e] = cap, offsets[e] = e * cap; every other
+   * entry point then takes K = E.  Softmax gate only; not with
+   * MOE_F_TOPK_IN, MOE_F_STATS or MOE_F_RENORM. */
+  MOE_F_EXPERT_CHOICE = 32u
 };
 
 /* Router statistics, written to routing->stats (E + MOE_N_STATS doubles)

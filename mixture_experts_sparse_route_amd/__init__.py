@@ -23,6 +23,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16 = 0, 1
 MOE_GATE_SOFTMAX, MOE_GATE_SIGMOID = 0, 1
 MOE_F_RENORM, MOE_F_RESIDUAL, MOE_F_LOGITS_IN, MOE_F_TOPK_IN, MOE_F_STATS = 1, 2, 4, 8, 16
+MOE_F_EXPERT_CHOICE = 32
 # moe_drop_policy: which assignments an expert over capacity drops
 DROP_POLICIES = {"first_come": 0, "affinity": 1, "reroute": 2}
 # router statistics after the E per-expert mean probabilities (moe.h, MOE_STAT_*)
@@ -126,11 +127,12 @@ class LayerSpec:
     topk_in: bool = False
     stats: bool = False
     drop_policy: str = "first_come"   # a key of DROP_POLICIES
+    expert_choice: bool = False       # expert-choice routing (routing arrays in the K = E form)
 
     def config(self) -> MoeConfig:
         flags = ((MOE_F_RENORM if self.renorm else 0) | (MOE_F_RESIDUAL if self.residual else 0)
                  | (MOE_F_LOGITS_IN if self.logits_in else 0) | (MOE_F_TOPK_IN if self.topk_in else 0)
-                 | (MOE_F_STATS if self.stats else 0))
+                 | (MOE_F_STATS if self.stats else 0) | (MOE_F_EXPERT_CHOICE if self.expert_choice else 0))
         dt = MOE_BF16 if self.dtype == "bf16" else MOE_F32
         ot = dt if self.out_dtype is None else (MOE_BF16 if self.out_dtype == "bf16" else MOE_F32)
         return MoeConfig(self.tokens, self.d_model, self.d_ff, self.n_experts, self.top_k, self.gate, flags,
@@ -182,7 +184,8 @@ class Routing:
     def __init__(self, spec, device="cuda"):
         torch = _torch()
         c = _cfg(spec)
-        T, E, K = c.tokens, c.n_experts, c.top_k
+        T, E = c.tokens, c.n_experts
+        K = E if c.flags & MOE_F_EXPERT_CHOICE else c.top_k   # expert choice: the K = E form
         self.logits = torch.empty((T, E), dtype=torch.float32, device=device)
         self.topk_idx = torch.empty((T, K), dtype=torch.int32, device=device)
         self.topk_w = torch.empty((T, K), dtype=torch.float32, device=device)

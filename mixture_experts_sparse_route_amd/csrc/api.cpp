@@ -38,7 +38,8 @@ moe_status hip_fail(hipError_t e, const char* where) {
     if (e_ != hipSuccess) return hip_fail(e_, #call);      \
   } while (0)
 
-constexpr uint32_t kKnownFlags = MOE_F_RENORM | MOE_F_RESIDUAL | MOE_F_LOGITS_IN | MOE_F_TOPK_IN | MOE_F_STATS;
+constexpr uint32_t kKnownFlags =
+    MOE_F_RENORM | MOE_F_RESIDUAL | MOE_F_LOGITS_IN | MOE_F_TOPK_IN | MOE_F_STATS | MOE_F_EXPERT_CHOICE;
 
 // Everything the launches need, derived from a validated config.
 struct Shape {
@@ -47,6 +48,7 @@ struct Shape {
   bool stats;  // router statistics requested
   int policy;  // moe_drop_policy in effect (first-come when there is no capacity)
   int64_t K2;  // re-routing alternates per token
+  bool ec;     // expert-choice routing: K is E (the K = E form), cap the tokens per expert
   int64_t T, d, F, E, K, S, Fs;
   int64_t cap;       // -1: no limit
   int64_t max_rows;  // upper bound of kept rows R
@@ -71,6 +73,11 @@ moe_status validate(const moe_config* c, Shape* sh) {
     return fail(MOE_ERR_INVALID_ARG, "unknown drop_policy %d", (int)c->drop_policy);
   if (c->drop_policy == MOE_DROP_REROUTE && (c->flags & MOE_F_TOPK_IN))
     return fail(MOE_ERR_INVALID_ARG, "MOE_DROP_REROUTE ranks experts from the logits; not with MOE_F_TOPK_IN");
+  const bool ec = c->flags & MOE_F_EXPERT_CHOICE;
+  if (ec && (c->flags & (MOE_F_TOPK_IN | MOE_F_STATS | MOE_F_RENORM)))
+    return fail(MOE_ERR_INVALID_ARG, "MOE_F_EXPERT_CHOICE excludes MOE_F_TOPK_IN, MOE_F_STATS and MOE_F_RENORM");
+  if (ec && c->gate != MOE_GATE_SOFTMAX)
+    return fail(MOE_ERR_UNSUPPORTED, "expert-choice routing is implemented for the softmax gate");
   if (!std::isfinite(c->capacity_factor)) return fail(MOE_ERR_INVALID_ARG, "capacity_factor is not finite");
   if (c->n_shared < 0 || c->n_shared > 1) return fail(MOE_ERR_INVALID_ARG, "n_shared must be 0 or 1");
   if (c->n_shared == 1 && c->d_ff_shared < 1) return fail(MOE_ERR_INVALID_ARG, "d_ff_shared must be >= 1");
@@ -88,14 +95,20 @@ moe_status validate(const moe_config* c, Shape* sh) {
     if (c->d_model % 64 || c->d_ff % 64 || (c->n_shared && c->d_ff_shared % 64))
       return fail(MOE_ERR_UNSUPPORTED, "bf16 needs d_model, d_ff and d_ff_shared to be multiples of 64");
   }
-  const int64_t T = c->tokens, d = c->d_model, F = c->d_ff, E = c->n_experts, K = c->top_k;
+  const int64_t T = c->tokens, d = c->d_model, F = c->d_ff, E = c->n_experts;
+  const int64_t K = ec ? c->n_experts : c->top_k;  // expert choice: the K = E form
   const int64_t Fs = c->n_shared ? c->d_ff_shared : 0;
   if (T > (int64_t)INT32_MAX / K) return fail(MOE_ERR_UNSUPPORTED, "tokens * top_k exceeds 2^31 - 1");
   if (T > (int64_t)INT32_MAX / E) return fail(MOE_ERR_UNSUPPORTED, "tokens * n_experts exceeds 2^31 - 1");
   if (F > (int64_t)INT32_MAX / d || Fs > (int64_t)INT32_MAX / d)
     return fail(MOE_ERR_UNSUPPORTED, "d_ff * d_model exceeds 2^31 - 1");
   int64_t cap = -1;
-  if (c->capacity_factor > 0.0) {
+  if (ec) {
+    // tokens per expert: floor(C * T * top_k / E), C = 1 when not given, at most T
+    const double C = c->capacity_factor > 0.0 ? c->capacity_factor : 1.0;
+    const double v = std::floor(C * (double)(T * c->top_k) / (double)E);
+    cap = v > (double)T ? T : (int64_t)v;
+  } else if (c->capacity_factor > 0.0) {
     // K_max = floor(C * N_tokens / N_experts) with N_tokens = T * K assignments
     const double v = std::floor(c->capacity_factor * (double)(T * K) / (double)E);
     cap = v > (double)(T * K) ? T * K : (int64_t)v;
@@ -114,6 +127,7 @@ moe_status validate(const moe_config* c, Shape* sh) {
   sh->Fs = Fs;
   sh->cap = cap;
   sh->max_rows = cap >= 0 ? std::min(T * K, E * cap) : T * K;
+  sh->ec = ec;
   sh->n_chunks = (T + kTopkTokens - 1) / kTopkTokens;
   sh->esz = bf16 ? 2 : 4;
   return MOE_OK;
@@ -145,7 +159,7 @@ Layout layout(const Shape& s) {
   L.blk_z = take(s.stats ? (size_t)s.n_chunks * 4 : 0);
   const bool aff = s.policy == MOE_DROP_AFFINITY, rr = s.policy == MOE_DROP_REROUTE;
   L.dem_off = take(aff ? (size_t)(s.E + 1) * 4 : 0);
-  L.seg = take(aff ? TK * 8 : 0);
+  L.seg = take(aff || s.ec ? TK * 8 : 0);
   L.alt_idx = take(rr ? (size_t)(s.T * s.K2) * 4 : 0);
   L.alt_w = take(rr ? (size_t)(s.T * s.K2) * 4 : 0);
   L.pos1 = take(rr ? TK * 4 : 0);
@@ -213,6 +227,17 @@ moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const 
   const bool rr = s.policy == MOE_DROP_REROUTE, aff = s.policy == MOE_DROP_AFFINITY;
   int32_t* alt_idx = rr ? at<int32_t>(ws, L.alt_idx) : nullptr;
   float* alt_w = rr ? at<float>(ws, L.alt_w) : nullptr;
+  if (s.ec) {
+    int S = 1;
+    float* part = at<float>(ws, L.router_part);
+    if (!(c->flags & MOE_F_LOGITS_IN)) {
+      S = router_splits(s.T, s.d, s.E, s.bf16);
+      MOE_HIP(launch_router_logits(s.bf16, x, Wg, logit_bias, r.logits, part, s.T, s.d, s.E, st));
+    }
+    MOE_HIP(launch_expert_choice(r.logits, part, S, logit_bias, r.topk_idx, r.topk_w, at<uint64_t>(ws, L.seg),
+                                 r.counts, r.offsets, r.dest, r.row_src, r.dropped, s.T, s.E, s.cap, st));
+    return MOE_OK;
+  }
   if (!topk_in) {
     int S = 1;
     float* part = at<float>(ws, L.router_part);

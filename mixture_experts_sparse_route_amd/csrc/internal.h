@@ -88,6 +88,12 @@ hipError_t launch_route_scatter(const RouteScatter& r, int64_t T, int64_t K, int
 hipError_t launch_route_affinity(const uint64_t* seg, const int32_t* counts, const int32_t* dem_off,
                                  const int32_t* offsets, int32_t* dest, int32_t* row_src, uint8_t* dropped, int64_t E,
                                  int64_t cap, hipStream_t s);
+// Expert-choice routing in the K = E form: w / idx / dest / dropped are
+// [T, E]; seg: [E, T] key scratch; cap tokens per expert (0 <= cap <= T).
+// S > 1: logits = sum of the router's d-slices in `part` (+ bias), written.
+hipError_t launch_expert_choice(float* logits, const float* part, int S, const float* bias, int32_t* idx, float* w,
+                                uint64_t* seg, int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* row_src,
+                                uint8_t* dropped, int64_t T, int64_t E, int64_t cap, hipStream_t s);
 hipError_t launch_dispatch(const void* x, const int32_t* row_src, const int32_t* R_ptr, void* xp, int64_t max_rows,
                            int64_t K, int64_t row_bytes, hipStream_t s);
 

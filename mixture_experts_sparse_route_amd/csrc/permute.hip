@@ -8,6 +8,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "radix_select.h"
 
 namespace moe {
 namespace {
@@ -300,67 +301,14 @@ __global__ __launch_bounds__(256) void route_affinity_kernel(const uint64_t* __r
                                                              int32_t* __restrict__ dest, int32_t* __restrict__ row_src,
                                                              uint8_t* __restrict__ dropped, int cap) {
   __shared__ int hist[256];
-  __shared__ int sel_bin, sel_want;
+  __shared__ int sel[2];
   __shared__ int wtot[4];
   const int e = blockIdx.x;
   const int n = counts[e];
   if (n <= cap) return;
   const uint64_t* s = seg + dem_off[e];
-  uint64_t thr = ~0ull;  // keep iff key >= thr (cap == 0 keeps none: keys never reach ~0)
-  if (cap > 0) {
-    uint64_t prefix = 0, pmask = 0;
-    int want = cap;  // rank (1 = largest) of the wanted key among keys matching the prefix
-    for (int shift = 56; shift >= 0; shift -= 8) {
-      hist[threadIdx.x] = 0;
-      __syncthreads();
-      for (int i = threadIdx.x; i < n; i += 256) {
-        const uint64_t k = s[i];
-        if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255], 1);
-      }
-      __syncthreads();
-      if (threadIdx.x < 64) {
-        // lane l holds bins 4l .. 4l+3; suffix sums over the lanes above it
-        const int l = threadIdx.x;
-        const int c0 = hist[4 * l], c1 = hist[4 * l + 1], c2 = hist[4 * l + 2], c3 = hist[4 * l + 3];
-        const int local = c0 + c1 + c2 + c3;
-        int suf = local;
-        for (int off = 1; off < 64; off <<= 1) {
-          const int v = __shfl_down(suf, off, 64);
-          if (l + off < 64) suf += v;
-        }
-        const int above = suf - local;  // keys in bins above 4l+3
-        if (above < want && want <= suf) {
-          int acc = above, b;
-          if (acc + c3 >= want) {
-            b = 4 * l + 3;
-          } else {
-            acc += c3;
-            if (acc + c2 >= want) {
-              b = 4 * l + 2;
-            } else {
-              acc += c2;
-              if (acc + c1 >= want) {
-                b = 4 * l + 1;
-              } else {
-                acc += c1;
-                b = 4 * l;
-              }
-            }
-          }
-          sel_bin = b;
-          sel_want = want - acc;
-        }
-      }
-      __syncthreads();
-      prefix |= (uint64_t)sel_bin << shift;
-      pmask |= 0xFFull << shift;
-      want = sel_want;
-      __syncthreads();
-    }
-    thr = prefix;  // the cap-th largest key (keys are distinct)
-  }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // keep iff key >= thr; cap == 0 keeps none
+  const uint64_t thr = cap > 0 ? radix_select_desc<256>(s, n, cap, hist, sel) : 0ull;
   const int base = offsets[e];
   int run = 0;
   for (int i0 = 0; i0 < n; i0 += 256) {
@@ -368,21 +316,16 @@ __global__ __launch_bounds__(256) void route_affinity_kernel(const uint64_t* __r
     const bool in = i < n;
     const uint64_t k = in ? s[i] : 0ull;
     const bool keep = in && cap > 0 && k >= thr;
-    const uint64_t bal = __ballot(keep);
-    if (lane == 0) wtot[wave] = __popcll(bal);
-    __syncthreads();
-    int before = run;
-    for (int q = 0; q < wave; ++q) before += wtot[q];
-    const int tot = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+    int tot;
+    const int rank = block_rank<256>(keep, wtot, &tot);
     if (in) {
       const int32_t f = (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
-      const int32_t row = keep ? base + before + __popcll(bal & lt_mask) : -1;
+      const int32_t row = keep ? base + run + rank : -1;
       dest[f] = row;
       dropped[f] = keep ? 0 : 1;
       if (keep) row_src[row] = f;
     }
     run += tot;
-    __syncthreads();
   }
 }
 

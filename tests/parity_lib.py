@@ -75,7 +75,7 @@ class Case:
 
     # ---------------------------------------------------------- GPU side --
     def gpu_forward(self, residual=False, logits_in=None, topk_in=None, out_dtype=None, stats=False,
-                    drop_policy="first_come"):
+                    drop_policy="first_come", expert_choice=False):
         """moe_forward through the C-ABI.  logits_in: fp32 [T, E] host array;
         topk_in: (idx int32 [T, K], w fp32 [T, K]) host arrays; out_dtype:
         "f32" or "bf16" (default: the layer's dtype); stats: also write the
@@ -83,7 +83,7 @@ class Case:
         moe.DROP_POLICIES."""
         wl = self.wl
         spec = spec_of(wl, residual=residual, logits_in=logits_in is not None, topk_in=topk_in is not None,
-                       out_dtype=out_dtype, stats=stats, drop_policy=drop_policy)
+                       out_dtype=out_dtype, stats=stats, drop_policy=drop_policy, expert_choice=expert_choice)
         r = moe.Routing(spec)
         if logits_in is not None:
             r.logits.copy_(torch.from_numpy(np.ascontiguousarray(logits_in, dtype=np.float32)))

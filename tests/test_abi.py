@@ -192,3 +192,19 @@ def test_drop_policy_validation(lib):
         assert moe.workspace_size(spec(tokens=4096, capacity_factor=1.0, drop_policy=p)) > base
         assert moe.workspace_size(spec(tokens=4096, drop_policy=p)) == moe.workspace_size(spec(tokens=4096))
     assert moe.workspace_size(spec(capacity_factor=1.0, drop_policy="affinity", topk_in=True)) > 0
+
+
+def test_expert_choice_validation(lib):
+    n = ctypes.c_size_t()
+    for kw, st in ((dict(gate=moe.MOE_GATE_SIGMOID), moe.MOE_ERR_UNSUPPORTED), (dict(topk_in=True), moe.MOE_ERR_INVALID_ARG),
+                   (dict(stats=True), moe.MOE_ERR_INVALID_ARG), (dict(renorm=True), moe.MOE_ERR_INVALID_ARG)):
+        base = dict(expert_choice=True, renorm=False)
+        base.update(kw)
+        c = spec(**base).config()
+        assert lib.moe_workspace_size(ctypes.byref(c), ctypes.byref(n)) == st, kw
+    # cap = floor(C*T*K/E), at most T; rows = E * cap
+    assert moe.max_rows(spec(expert_choice=True, renorm=False, tokens=100, n_experts=8, top_k=2,
+                             capacity_factor=1.25)) == 8 * 31
+    assert moe.max_rows(spec(expert_choice=True, renorm=False, tokens=100, n_experts=8, top_k=2)) == 8 * 25
+    assert moe.max_rows(spec(expert_choice=True, renorm=False, tokens=10, n_experts=2, top_k=2,
+                             capacity_factor=3.0)) == 2 * 10
