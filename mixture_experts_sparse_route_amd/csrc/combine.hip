@@ -18,16 +18,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       OUT* __restrict__ y, int T, int d, int K) {
   const int vecs = d / VEC;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= (int64_t)T * vecs) return;
+  // vecs % 64 == 0: all 64 lanes of a wave serve one token (the grid is a
+  // whole number of waves, so such a wave never straddles the end)
+  const bool wave_token = vecs % 64 == 0;
+  if (!wave_token && gid >= (int64_t)T * vecs) return;
   const int t = (int)(gid / vecs);
   const int c = (int)(gid % vecs) * VEC;
   float acc[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
-  for (int k = 0; k < K; ++k) {
-    const int r = dest[(int64_t)t * K + k];
-    if (r < 0) continue;
-    const float wk = w[(int64_t)t * K + k];
+  auto add_row = [&](int r, float wk) {
     const float* src = yp + (int64_t)r * d + c;
     if (VEC == 4) {
       const float4 q = *(const float4*)src;
@@ -38,6 +38,29 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     } else {
 #pragma unroll
       for (int v = 0; v < VEC; ++v) acc[v] = fmaf(wk, src[v], acc[v]);
+    }
+  };
+  if (wave_token) {
+    if (t >= T) return;
+    // the wave loads the token's K (row, weight) pairs, one per lane, and
+    // visits the kept ones in ascending k
+    const int lane = threadIdx.x & 63;
+    for (int k0 = 0; k0 < K; k0 += 64) {
+      const int k = k0 + lane;
+      const int r = k < K ? dest[(int64_t)t * K + k] : -1;
+      const float wk = k < K ? w[(int64_t)t * K + k] : 0.f;
+      uint64_t kept = __ballot(r >= 0);
+      while (kept) {
+        const int j = __ffsll((unsigned long long)kept) - 1;
+        kept &= kept - 1;
+        add_row(__shfl(r, j, 64), __shfl(wk, j, 64));
+      }
+    }
+  } else {
+    for (int k = 0; k < K; ++k) {
+      const int r = dest[(int64_t)t * K + k];
+      if (r < 0) continue;
+      add_row(r, w[(int64_t)t * K + k]);
     }
   }
   const int64_t o = (int64_t)t * d + c;

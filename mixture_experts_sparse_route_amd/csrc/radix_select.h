@@ -8,11 +8,13 @@
 
 namespace moe {
 
-// The want-th largest (1 = the largest) of the n distinct keys s[0 .. n),
-// 1 <= want <= n.  Most-significant-digit radix select: 8 passes, each
-// histogramming the next 8 bits of the keys that share the prefix found so
-// far and keeping the bin that holds the wanted rank.  Every thread of the
-// NT-thread block calls it.  hist: 256 ints of LDS; sel: 2 ints of LDS.
+// A threshold thr such that exactly `want` of the n distinct keys s[0 .. n)
+// are >= thr, 1 <= want <= n.  Most-significant-digit radix select: up to 8
+// passes, each histogramming the next 8 bits of the keys that share the
+// prefix found so far and keeping the bin that holds the want-th largest
+// key; it stops early once every key of that bin is wanted (thr is then the
+// prefix with its lower bits zero).  Every thread of the NT-thread block
+// calls it.  hist: 256 ints of LDS; sel: 2 ints of LDS.
 template <int NT>
 __device__ uint64_t radix_select_desc(const uint64_t* __restrict__ s, int n, int want, int* hist, int* sel) {
   uint64_t prefix = 0, pmask = 0;
@@ -61,7 +63,11 @@ __device__ uint64_t radix_select_desc(const uint64_t* __restrict__ s, int n, int
     prefix |= (uint64_t)sel[0] << shift;
     pmask |= 0xFFull << shift;
     want = sel[1];
+    // every key of the chosen bin is wanted: the keys >= prefix (lower bits
+    // zero) are exactly the wanted ones, whatever their lower bits hold
+    const bool whole_bin = want == hist[sel[0]];
     __syncthreads();
+    if (whole_bin) break;
   }
   return prefix;
 }
