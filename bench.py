@@ -98,13 +98,14 @@ def cpu_baseline(wl, h, budget_s: float, policy: str = "first_come", expert_choi
     else:
         rt = oracle.route(L, h["x"], h["Wg"], h["logit_bias"], h["sel_bias"], policy=policy)
     t_route = time.perf_counter() - t0
+    scales = {k: h.get(k) for k in ("S1", "S3", "S2", "Ss1", "Ss3", "Ss2")}
     done = 0
     t_rows = 0.0
     while done < wl.T and t_rows < budget_s:
         toks = np.arange(done, min(wl.T, done + 64), dtype=np.int64)
         t1 = time.perf_counter()
         oracle.forward_rows(L, h["x"], rt["idx"], rt["w"], rt["dest"], h["W1"], h["W3"], h["W2"], h["Ws1"],
-                            h["Ws3"], h["Ws2"], tokens=toks)
+                            h["Ws3"], h["Ws2"], tokens=toks, **scales)
         t_rows += time.perf_counter() - t1
         done += len(toks)
     t_layer = t_route + t_rows * wl.T / done

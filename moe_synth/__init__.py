@@ -23,6 +23,8 @@ _lib = None
 
 # tensor ids of the counter-based streams
 TID_X, TID_WG, TID_W1, TID_W3, TID_W2, TID_WS1, TID_WS3, TID_WS2, TID_SEL_BIAS = range(9)
+# per-row scales of FP8 expert weights
+TID_S1, TID_S3, TID_S2, TID_SS1, TID_SS3, TID_SS2 = range(9, 15)
 
 
 def build(force: bool = True) -> str:
@@ -49,6 +51,8 @@ def _load():
         lib.synth_uniform_f32.argtypes = [u64, u64, u64, u64, dbl, dbl, vp]
         lib.synth_uniform_f32.restype = None
         lib.synth_bits.argtypes = [u64, u64, u64, u64, vp]
+        lib.synth_fp8_codes.argtypes = [u64, u64, u64, u64, vp]
+        lib.synth_fp8_codes.restype = None
         lib.synth_bits.restype = None
         lib.synth_splitmix64.argtypes = [u64, u64, vp]
         lib.synth_splitmix64.restype = None
@@ -94,6 +98,15 @@ def bits(seed: int, tid: int, count: int, offset: int = 0) -> np.ndarray:
     lib = _load()
     out = np.empty((count,), dtype=np.uint64)
     lib.synth_bits(seed, tid, offset, count, _ptr(out))
+    return out
+
+
+def fp8_codes(seed: int, tid: int, shape, offset: int = 0) -> np.ndarray:
+    """Random FP8 E4M3 codes (uint8) of elements ``offset ..`` of stream
+    (seed, tid): random sign and mantissa, exponent field 3 + Binomial(8, 1/2)."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    out = np.empty(shape, dtype=np.uint8)
+    _load().synth_fp8_codes(seed, tid, offset, n, _ptr(out))
     return out
 
 

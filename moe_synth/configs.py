@@ -14,6 +14,11 @@ Input recipe (every workload, seed 0 unless a caller says otherwise):
   selection bias [E] ~ U(-0.1, 0.1), fp32      tensor id 8
   logit bias [E] (Switch workload only): 2.0 * (e + 1)^-1.1, a Zipf(s = 1.1)
       profile over expert rank scaled so the first expert gets 2.0.
+FP8 expert weights (wdtype "fp8"; activations stay bf16): E4M3 codes from
+  random bits (moe_synth.fp8_codes, same tensor ids as the bf16 weights; the
+  decoded codes have standard deviation about 3.6) and per-row fp32 scales
+  ~ U(0.5, 1.5) / (4 sqrt(fan-in)) (W1, W3 rows: d; W2 rows: F), tensor ids
+  9 .. 14.
 """
 from __future__ import annotations
 
@@ -41,6 +46,7 @@ class Workload:
     n_shared: int = 0
     Fs: int = 0       # shared-expert d_ff
     dtype: str = "bf16"            # activations and expert weights: "f32" or "bf16"
+    wdtype: str = ""               # "fp8": expert weights are E4M3 codes with per-row scales
     logit_bias: Optional[str] = None   # None or "zipf1.1x2"
     sel_bias: Optional[str] = None     # None or "u0.1"
     seed: int = 0
@@ -77,19 +83,45 @@ class Workload:
 
     def gen_expert(self, e0: int = 0, ne: Optional[int] = None):
         """W1, W3 [ne, F, d] and W2 [ne, d, F] for experts e0 .. e0+ne-1."""
-        from . import TID_W1, TID_W2, TID_W3, normal
+        from . import TID_W1, TID_W2, TID_W3, fp8_codes, normal
         ne = self.E - e0 if ne is None else ne
         fd = self.F * self.d
+        if self.wdtype == "fp8":
+            return (fp8_codes(self.seed, TID_W1, (ne, self.F, self.d), offset=e0 * fd),
+                    fp8_codes(self.seed, TID_W3, (ne, self.F, self.d), offset=e0 * fd),
+                    fp8_codes(self.seed, TID_W2, (ne, self.d, self.F), offset=e0 * fd))
         w1 = normal(self.seed, TID_W1, (ne, self.F, self.d), 1.0 / np.sqrt(self.d), self.dtype, offset=e0 * fd)
         w3 = normal(self.seed, TID_W3, (ne, self.F, self.d), 1.0 / np.sqrt(self.d), self.dtype, offset=e0 * fd)
         w2 = normal(self.seed, TID_W2, (ne, self.d, self.F), 1.0 / np.sqrt(self.F), self.dtype, offset=e0 * fd)
         return w1, w3, w2
 
+    def gen_scales(self):
+        """Per-row scales of FP8 weights: S1, S3 [E, F], S2 [E, d], Ss1, Ss3
+        [S, Fs], Ss2 [S, d] (None when the weights are not FP8)."""
+        from . import TID_S1, TID_S2, TID_S3, TID_SS1, TID_SS2, TID_SS3, uniform
+        if self.wdtype != "fp8":
+            return dict(S1=None, S3=None, S2=None, Ss1=None, Ss3=None, Ss2=None)
+        E, F, d, S, Fs = self.E, self.F, self.d, self.n_shared, self.Fs
+        rd, rf = 0.25 / np.sqrt(d), 0.25 / np.sqrt(F)   # codes have std about 3.6
+        out = dict(S1=uniform(self.seed, TID_S1, (E, F), 0.5 * rd, 1.5 * rd),
+                   S3=uniform(self.seed, TID_S3, (E, F), 0.5 * rd, 1.5 * rd),
+                   S2=uniform(self.seed, TID_S2, (E, d), 0.5 * rf, 1.5 * rf),
+                   Ss1=None, Ss3=None, Ss2=None)
+        if S:
+            rs = 0.25 / np.sqrt(Fs)
+            out.update(Ss1=uniform(self.seed, TID_SS1, (S, Fs), 0.5 * rd, 1.5 * rd),
+                       Ss3=uniform(self.seed, TID_SS3, (S, Fs), 0.5 * rd, 1.5 * rd),
+                       Ss2=uniform(self.seed, TID_SS2, (S, d), 0.5 * rs, 1.5 * rs))
+        return out
+
     def gen_shared(self):
-        from . import TID_WS1, TID_WS2, TID_WS3, normal
+        from . import TID_WS1, TID_WS2, TID_WS3, fp8_codes, normal
         if self.n_shared == 0:
             return None, None, None
         s, fs, d = self.n_shared, self.Fs, self.d
+        if self.wdtype == "fp8":
+            return (fp8_codes(self.seed, TID_WS1, (s, fs, d)), fp8_codes(self.seed, TID_WS3, (s, fs, d)),
+                    fp8_codes(self.seed, TID_WS2, (s, d, fs)))
         ws1 = normal(self.seed, TID_WS1, (s, fs, d), 1.0 / np.sqrt(d), self.dtype)
         ws3 = normal(self.seed, TID_WS3, (s, fs, d), 1.0 / np.sqrt(d), self.dtype)
         ws2 = normal(self.seed, TID_WS2, (s, d, fs), 1.0 / np.sqrt(fs), self.dtype)
@@ -99,7 +131,8 @@ class Workload:
         w1, w3, w2 = self.gen_expert()
         ws1, ws3, ws2 = self.gen_shared()
         return dict(x=self.gen_x(), Wg=self.gen_wg(), logit_bias=self.gen_logit_bias(),
-                    sel_bias=self.gen_sel_bias(), W1=w1, W3=w3, W2=w2, Ws1=ws1, Ws3=ws3, Ws2=ws2)
+                    sel_bias=self.gen_sel_bias(), W1=w1, W3=w3, W2=w2, Ws1=ws1, Ws3=ws3, Ws2=ws2,
+                    **self.gen_scales())
 
 
 WORKLOADS = {

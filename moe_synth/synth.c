@@ -88,6 +88,20 @@ void synth_bits(uint64_t seed, uint64_t tid, uint64_t offset, uint64_t count, ui
   for (uint64_t j = 0; j < count; ++j) out[j] = mix64(key + (offset + j + 1ULL) * 0x9E3779B97F4A7C15ULL);
 }
 
+/* Random FP8 E4M3 weight codes built from raw draws alone (no rounding of
+ * real values): sign = bit 63, mantissa field = bits 60..62, exponent field
+ * = 3 + (number of set bits among bits 0..7), i.e. a binomial spread of
+ * magnitudes 2^-4 .. 2^4 around 1 (the exponent never reaches the NaN field). */
+void synth_fp8_codes(uint64_t seed, uint64_t tid, uint64_t offset, uint64_t count, uint8_t* out) {
+  uint64_t key = stream_key(seed, tid);
+#pragma omp parallel for schedule(static, 65536)
+  for (int64_t j = 0; j < (int64_t)count; ++j) {
+    const uint64_t r = mix64(key + (offset + (uint64_t)j + 1ULL) * 0x9E3779B97F4A7C15ULL);
+    const uint32_t e = 3u + (uint32_t)__builtin_popcountll(r & 0xFFull);
+    out[j] = (uint8_t)(((r >> 63) << 7) | (e << 3) | ((r >> 60) & 7u));
+  }
+}
+
 /* bf16 bits -> fp32, and fp32 -> bf16 bits (round to nearest even); helpers
  * for callers that hold bf16 as uint16 arrays. */
 void synth_f32_to_bf16(const float* in, uint16_t* out, uint64_t n) {

@@ -28,6 +28,7 @@ class OrcLayer(ctypes.Structure):
         ("K", ctypes.c_int64), ("gate", ctypes.c_int32), ("renorm", ctypes.c_int32),
         ("residual", ctypes.c_int32), ("bf16", ctypes.c_int32), ("capacity_factor", ctypes.c_double),
         ("n_shared", ctypes.c_int64), ("Fs", ctypes.c_int64), ("round_h", ctypes.c_int32),
+        ("w_fp8", ctypes.c_int32),
     ]
 
 
@@ -55,10 +56,13 @@ def _load():
         lib.orc_capacity.argtypes = [P]
         lib.orc_capacity.restype = i64
         lib.orc_permute.argtypes = [P, vp, vp, vp, vp, vp, vp]
-        lib.orc_swiglu.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, vp, i32]
+        lib.orc_swiglu.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32]
+        lib.orc_fp8_e4m3.argtypes = [ctypes.c_uint8]
+        lib.orc_fp8_e4m3.restype = ctypes.c_double
         lib.orc_bf16_round.argtypes = [ctypes.c_double]
         lib.orc_bf16_round.restype = ctypes.c_double
-        lib.orc_forward_rows.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]
+        lib.orc_forward_rows.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         i64, vp]
         lib.orc_expert_choice.argtypes = [P, vp, i64, vp, vp]
         lib.orc_select_ranked.argtypes = [P, vp, vp, i64, vp, vp]
         lib.orc_select_ranked.restype = None
@@ -87,18 +91,24 @@ def _p(a):
 
 
 def layer(T, d, F, E, K, gate=GATE_SOFTMAX, renorm=True, residual=False, bf16=False, capacity_factor=0.0,
-          n_shared=0, Fs=0, round_h=None) -> OrcLayer:
-    """round_h: store the SwiGLU output h in bf16 (default: for bf16 layers)."""
+          n_shared=0, Fs=0, round_h=None, w_fp8=False) -> OrcLayer:
+    """round_h: store the SwiGLU output h in bf16 (default: for bf16 layers).
+    w_fp8: expert weights are FP8 E4M3 codes with per-row scales."""
     rh = bf16 if round_h is None else round_h
     return OrcLayer(T, d, F, E, K, gate, int(renorm), int(residual), int(bf16), float(capacity_factor),
-                    n_shared, Fs, int(rh))
+                    n_shared, Fs, int(rh), int(w_fp8))
 
 
 def layer_of(wl, residual=False, round_h=None) -> OrcLayer:
     """OrcLayer for a ``moe_synth`` workload."""
     return layer(wl.T, wl.d, wl.F, wl.E, wl.K, gate=wl.gate, renorm=wl.renorm, residual=residual,
                  bf16=(wl.dtype == "bf16"), capacity_factor=wl.capacity_factor, n_shared=wl.n_shared, Fs=wl.Fs,
-                 round_h=round_h)
+                 round_h=round_h, w_fp8=(getattr(wl, "wdtype", "") == "fp8"))
+
+
+def fp8_e4m3(code: int) -> float:
+    """The value of an OCP FP8 E4M3 code."""
+    return float(_load().orc_fp8_e4m3(int(code)))
 
 
 def bf16_round(v: float) -> float:
@@ -188,21 +198,28 @@ def alternates(L: OrcLayer, lg, sel_bias=None):
     return np.ascontiguousarray(ridx[:, L.K:]), np.ascontiguousarray(rw[:, L.K:])
 
 
-def swiglu(W1, W3, W2, x, bf16: bool, threads: int = 1, round_h: bool = False) -> np.ndarray:
-    """One expert on one row: W1, W3 [F, d], W2 [d, F]; x float64 [d]."""
+def swiglu(W1, W3, W2, x, bf16: bool, threads: int = 1, round_h: bool = False, scales=None) -> np.ndarray:
+    """One expert on one row: W1, W3 [F, d], W2 [d, F]; x float64 [d].
+    uint8 weights are FP8 E4M3 codes; scales = (s1 [F], s3 [F], s2 [d])."""
     F, d = W1.shape
     out = np.empty(d, dtype=np.float64)
-    _load().orc_swiglu(d, F, int(bf16), int(round_h), _p(np.ascontiguousarray(W1)), _p(np.ascontiguousarray(W3)),
-                       _p(np.ascontiguousarray(W2)), _p(np.ascontiguousarray(x, dtype=np.float64)), _p(out),
-                       threads)
+    wdt = 2 if W1.dtype == np.uint8 else int(bf16)
+    s1, s3, s2 = (None, None, None) if scales is None else (np.ascontiguousarray(a, dtype=np.float32)
+                                                             for a in scales)
+    _load().orc_swiglu(d, F, wdt, int(round_h), _p(np.ascontiguousarray(W1)), _p(np.ascontiguousarray(W3)),
+                       _p(np.ascontiguousarray(W2)), _p(s1), _p(s3), _p(s2),
+                       _p(np.ascontiguousarray(x, dtype=np.float64)), _p(out), threads)
     return out
 
 
-def forward_rows(L: OrcLayer, x, idx, w, dest, W1e, W3e, W2e, Ws1=None, Ws3=None, Ws2=None, tokens=None):
+def forward_rows(L: OrcLayer, x, idx, w, dest, W1e, W3e, W2e, Ws1=None, Ws3=None, Ws2=None, tokens=None,
+                 S1=None, S3=None, S2=None, Ss1=None, Ss3=None, Ss2=None):
     """y (float64 [n, d]) for the listed tokens (all tokens if None).
 
     W1e/W3e/W2e: either stacked arrays [E, ...] or lists of per-expert arrays
-    (None for experts no listed token uses)."""
+    (None for experts no listed token uses).  FP8 layers (L.w_fp8): S1/S3
+    [E, F] and S2 [E, d] row scales (stacked or per-expert lists), Ss1/Ss3
+    [S, Fs] and Ss2 [S, d]."""
     if tokens is None:
         tokens = np.arange(L.T, dtype=np.int64)
     tokens = np.ascontiguousarray(tokens, dtype=np.int64)
@@ -221,14 +238,21 @@ def forward_rows(L: OrcLayer, x, idx, w, dest, W1e, W3e, W2e, Ws1=None, Ws3=None
     p1, k1 = ptrs(W1e)
     p3, k3 = ptrs(W3e)
     p2, k2 = ptrs(W2e)
+    q1, kq1 = ptrs(S1)
+    q3, kq3 = ptrs(S3)
+    q2, kq2 = ptrs(S2)
+    sh = [None if a is None else np.ascontiguousarray(a, dtype=np.float32) for a in (Ss1, Ss3, Ss2)]
     y = np.empty((len(tokens), L.d), dtype=np.float64)
     _load().orc_forward_rows(ctypes.byref(L), _p(x), _p(np.ascontiguousarray(idx, dtype=np.int32)),
                              _p(np.ascontiguousarray(w, dtype=np.float64)),
                              _p(None if dest is None else np.ascontiguousarray(dest, dtype=np.int32)),
                              ctypes.cast(p1, ctypes.c_void_p), ctypes.cast(p3, ctypes.c_void_p),
-                             ctypes.cast(p2, ctypes.c_void_p), _p(Ws1), _p(Ws3), _p(Ws2), _p(tokens), len(tokens),
-                             _p(y))
-    del k1, k3, k2
+                             ctypes.cast(p2, ctypes.c_void_p), _p(Ws1), _p(Ws3), _p(Ws2),
+                             None if S1 is None else ctypes.cast(q1, ctypes.c_void_p),
+                             None if S3 is None else ctypes.cast(q3, ctypes.c_void_p),
+                             None if S2 is None else ctypes.cast(q2, ctypes.c_void_p),
+                             _p(sh[0]), _p(sh[1]), _p(sh[2]), _p(tokens), len(tokens), _p(y))
+    del k1, k3, k2, kq1, kq3, kq2
     return y
 
 
@@ -276,7 +300,8 @@ def ec_capacity(L: OrcLayer) -> int:
 def ec_layer(L: OrcLayer) -> OrcLayer:
     """The layer seen as K = E token choice with a drop mask: assignment
     (t, e) is expert e, kept iff expert e chose token t."""
-    return OrcLayer(L.T, L.d, L.F, L.E, L.E, L.gate, 0, L.residual, L.bf16, 0.0, L.n_shared, L.Fs, L.round_h)
+    return OrcLayer(L.T, L.d, L.F, L.E, L.E, L.gate, 0, L.residual, L.bf16, 0.0, L.n_shared, L.Fs, L.round_h,
+                    L.w_fp8)
 
 
 def route_expert_choice(L: OrcLayer, x=None, Wg=None, logit_bias=None, lg=None):

@@ -28,6 +28,22 @@ static inline double elem(const void* p, int32_t bf16, int64_t i) {
   return bf16 ? bf16_bits_to_double(((const uint16_t*)p)[i]) : (double)((const float*)p)[i];
 }
 
+double orc_fp8_e4m3(uint8_t c) {
+  /* OCP FP8 E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent
+   * field 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN; no infinities. */
+  const int sgn = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double v = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sgn ? -v : v;
+}
+
+/* element i of an expert weight: wdt 0 fp32, 1 bf16, 2 FP8 E4M3 code times
+ * the per-row scale scale[i / row_len] */
+static inline double welem(const void* p, int32_t wdt, int64_t i, const float* scale, int64_t row_len) {
+  if (wdt == 2) return orc_fp8_e4m3(((const uint8_t*)p)[i]) * (double)scale[i / row_len];
+  return elem(p, wdt, i);
+}
+
 /* ---- a1: router logits  [TD §3.1 step 1; BD §3.2] ------------------------ */
 
 void orc_logits(const orc_layer* L, const void* x, const float* Wg, const float* logit_bias, float* logits) {
@@ -322,16 +338,17 @@ double orc_bf16_round(double v) {
   return ldexp(nearbyint(ldexp(m, 8)), e - 8);
 }
 
-void orc_swiglu(int64_t d, int64_t F, int32_t bf16, int32_t round_h, const void* W1, const void* W3,
-                const void* W2, const double* x, double* out, int32_t threads) {
+void orc_swiglu(int64_t d, int64_t F, int32_t wdt, int32_t round_h, const void* W1, const void* W3,
+                const void* W2, const float* s1, const float* s3, const float* s2, const double* x, double* out,
+                int32_t threads) {
   double* h = (double*)malloc(sizeof(double) * (size_t)F);
   int nt = threads > 1 ? threads : 1;
 #pragma omp parallel for schedule(static) num_threads(nt) if (nt > 1)
   for (int64_t j = 0; j < F; ++j) {
     double a = 0.0, b = 0.0;
     for (int64_t i = 0; i < d; ++i) {
-      a += elem(W1, bf16, j * d + i) * x[i];
-      b += elem(W3, bf16, j * d + i) * x[i];
+      a += welem(W1, wdt, j * d + i, s1, d) * x[i];
+      b += welem(W3, wdt, j * d + i, s3, d) * x[i];
     }
     double silu = a / (1.0 + exp(-a));
     h[j] = silu * b;
@@ -341,7 +358,7 @@ void orc_swiglu(int64_t d, int64_t F, int32_t bf16, int32_t round_h, const void*
 #pragma omp parallel for schedule(static) num_threads(nt) if (nt > 1)
   for (int64_t m = 0; m < d; ++m) {
     double o = 0.0;
-    for (int64_t j = 0; j < F; ++j) o += elem(W2, bf16, m * F + j) * h[j];
+    for (int64_t j = 0; j < F; ++j) o += welem(W2, wdt, m * F + j, s2, F) * h[j];
     out[m] = o;
   }
   free(h);
@@ -351,9 +368,12 @@ void orc_swiglu(int64_t d, int64_t F, int32_t bf16, int32_t round_h, const void*
 
 void orc_forward_rows(const orc_layer* L, const void* x, const int32_t* idx, const double* w, const int32_t* dest,
                       const void* const* W1e, const void* const* W3e, const void* const* W2e, const void* Ws1,
-                      const void* Ws3, const void* Ws2, const int64_t* tokens, int64_t n_tokens, double* y) {
+                      const void* Ws3, const void* Ws2, const float* const* S1e, const float* const* S3e,
+                      const float* const* S2e, const float* Ss1, const float* Ss3, const float* Ss2,
+                      const int64_t* tokens, int64_t n_tokens, double* y) {
   const int64_t d = L->d, K = L->K, F = L->F, Fs = L->Fs;
-  const size_t esz = L->bf16 ? 2 : 4;
+  const int32_t wdt = L->w_fp8 ? 2 : L->bf16;
+  const size_t esz = L->w_fp8 ? 1 : (L->bf16 ? 2 : 4);
   int max_threads = 1;
 #ifdef _OPENMP
   max_threads = omp_get_max_threads();
@@ -375,7 +395,8 @@ void orc_forward_rows(const orc_layer* L, const void* x, const int32_t* idx, con
     for (int64_t k = 0; k < K; ++k) {
       if (dest && dest[t * K + k] < 0) continue;
       const int32_t e = idx[t * K + k];
-      orc_swiglu(d, F, L->bf16, L->round_h, W1e[e], W3e[e], W2e[e], xt, o, inner);
+      orc_swiglu(d, F, wdt, L->round_h, W1e[e], W3e[e], W2e[e], S1e ? S1e[e] : NULL, S3e ? S3e[e] : NULL,
+                 S2e ? S2e[e] : NULL, xt, o, inner);
       for (int64_t i = 0; i < d; ++i) acc[i] += w[t * K + k] * o[i];
     }
     /* always-active shared experts, added unweighted  [TD §3.4; §9.1] */
@@ -383,7 +404,8 @@ void orc_forward_rows(const orc_layer* L, const void* x, const int32_t* idx, con
       const char* p1 = (const char*)Ws1 + (size_t)(s * Fs * d) * esz;
       const char* p3 = (const char*)Ws3 + (size_t)(s * Fs * d) * esz;
       const char* p2 = (const char*)Ws2 + (size_t)(s * d * Fs) * esz;
-      orc_swiglu(d, Fs, L->bf16, L->round_h, p1, p3, p2, xt, o, inner);
+      orc_swiglu(d, Fs, wdt, L->round_h, p1, p3, p2, Ss1 ? Ss1 + s * Fs : NULL, Ss3 ? Ss3 + s * Fs : NULL,
+                 Ss2 ? Ss2 + s * d : NULL, xt, o, inner);
       for (int64_t i = 0; i < d; ++i) acc[i] += o[i];
     }
     /* residual Add of the MoE block  [TD §2.1] */

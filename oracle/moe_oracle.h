@@ -58,6 +58,10 @@ typedef struct orc_layer {
    * the down projection, as a bf16 layer stores its activations; 0: h stays
    * in double */
   int32_t round_h;
+  /* 1: the expert weights (routed and shared) are OCP FP8 E4M3 codes, each
+   * row with an fp32 scale (weight = decoded code * scale of its row); x
+   * and y keep the `bf16` setting */
+  int32_t w_fp8;
 } orc_layer;
 
 /* a1. logits[t][e] = fp32( sum_i x[t][i] * Wg[e][i] + logit_bias[e] )  [TD §3.1 step 1]
@@ -118,14 +122,19 @@ void orc_permute_reroute(const orc_layer* L, const int32_t* idx, const double* w
  * range), ties to even. */
 double orc_bf16_round(double v);
 
+/* The value of an OCP FP8 E4M3 code (NaN for the two NaN codes). */
+double orc_fp8_e4m3(uint8_t c);
+
 /* a6 + a7 for one row and one expert:
  *   out[m] = sum_j W2[m][j] * h_j,   h_j = SiLU(a_j) * b_j,  SiLU(z) = z / (1 + e^-z),
  *   a_j = sum_i W1[j][i] x[i],  b_j = sum_i W3[j][i] x[i].          [LN §2.2]
- * W1, W3: [F][d]; W2: [d][F]; bf16 or fp32 per `bf16`; x, out in double;
+ * W1, W3: [F][d]; W2: [d][F]; wdt 0 fp32, 1 bf16, 2 FP8 E4M3 codes with
+ * row scales s1, s3 [F] and s2 [d] (ignored otherwise); x, out in double;
  * h_j replaced by orc_bf16_round(h_j) when round_h.
  * If `threads` > 1 the output loops are split across OpenMP threads. */
-void orc_swiglu(int64_t d, int64_t F, int32_t bf16, int32_t round_h, const void* W1, const void* W3,
-                const void* W2, const double* x, double* out, int32_t threads);
+void orc_swiglu(int64_t d, int64_t F, int32_t wdt, int32_t round_h, const void* W1, const void* W3,
+                const void* W2, const float* s1, const float* s3, const float* s2, const double* x, double* out,
+                int32_t threads);
 
 /* a6-a9 for the listed tokens:
  *   y[j] = sum_{k ascending, dest[t][k] >= 0} w[t][k] * E_{idx[t][k]}(x_t)
@@ -134,10 +143,14 @@ void orc_swiglu(int64_t d, int64_t F, int32_t bf16, int32_t round_h, const void*
  * W1e/W3e/W2e: E pointers, one per expert ([F][d], [F][d], [d][F]); entries
  * for experts no listed token uses may be NULL.  Ws1/Ws3/Ws2: the shared
  * experts, [S][Fs][d], [S][Fs][d], [S][d][Fs] (NULL when n_shared == 0).
- * dest may be NULL (every assignment kept).  y: [n_tokens][d] double. */
+ * dest may be NULL (every assignment kept).  y: [n_tokens][d] double.
+ * With L->w_fp8: S1e/S3e [F] and S2e [d] per expert, Ss1/Ss3 [S][Fs] and
+ * Ss2 [S][d] are the row scales (NULL otherwise). */
 void orc_forward_rows(const orc_layer* L, const void* x, const int32_t* idx, const double* w, const int32_t* dest,
                       const void* const* W1e, const void* const* W3e, const void* const* W2e, const void* Ws1,
-                      const void* Ws3, const void* Ws2, const int64_t* tokens, int64_t n_tokens, double* y);
+                      const void* Ws3, const void* Ws2, const float* const* S1e, const float* const* S3e,
+                      const float* const* S2e, const float* Ss1, const float* Ss3, const float* Ss2,
+                      const int64_t* tokens, int64_t n_tokens, double* y);
 
 /* a9 alone: y[t] = sum_{k ascending, dest[t][k] >= 0} w[t][k] * yp[dest[t][k]]
  *                 + shared[t]  (+ x[t] if L->residual)            [TD §3.1 step 4]

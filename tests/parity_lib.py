@@ -40,6 +40,11 @@ BF16_TOL = 2e-2
 BF16_H_TOL = 5e-3
 
 
+def scales_of(h: dict) -> dict:
+    """The FP8 row scales of a generated input set (all None for bf16 / fp32)."""
+    return {k: h.get(k) for k in ("S1", "S3", "S2", "Ss1", "Ss3", "Ss2")}
+
+
 def dev(a: np.ndarray | None):
     if a is None:
         return None
@@ -111,7 +116,7 @@ class Case:
         h = self.h
         L = oracle.layer_of(self.wl, residual=residual, round_h=round_h)
         return oracle.forward_rows(L, h["x"], idx, w, dest, h["W1"], h["W3"], h["W2"], h["Ws1"], h["Ws3"], h["Ws2"],
-                                   tokens=tokens)
+                                   tokens=tokens, **scales_of(h))
 
     def logit_bound(self):
         x = self.h["x"]

@@ -17,7 +17,8 @@ import moe_synth
 import oracle
 import mixture_experts_sparse_route_amd as moe
 from moe_synth import workload
-from parity_lib import (NEAR_TIE, Case, assert_permutation_equal, assert_y_close, host_f64, routing_host)
+from parity_lib import (NEAR_TIE, Case, assert_permutation_equal, assert_y_close, host_f64, routing_host,
+                        scales_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -63,7 +64,7 @@ def check_ec(case: Case, residual=False, tokens=None):
     h = case.h
     L_res = oracle.ec_layer(oracle.layer_of(wl, residual=residual))
     y_ref = oracle.forward_rows(L_res, h["x"], orc["idx"], np.nan_to_num(orc["w"]), orc["dest"], h["W1"], h["W3"],
-                                h["W2"], h["Ws1"], h["Ws3"], h["Ws2"], tokens=rows)
+                                h["W2"], h["Ws1"], h["Ws3"], h["Ws2"], tokens=rows, **scales_of(h))
     live = np.ones(len(rows), bool) if (wl.n_shared or residual) else chosen.reshape(T, E)[rows].any(1)
     report = {"cap": orc["cap"], "unchosen_tokens": int((~chosen.reshape(T, E).any(1)).sum())}
     # identical logits

@@ -717,3 +717,66 @@ def test_expert_choice_route_and_forward():
                 want = want + p[t, e] * torch_swiglu(W1[e], W3[e], W2[e], x[t].astype(np.float64))
         np.testing.assert_allclose(y[t], want, rtol=1e-12, atol=1e-13)
     assert (dest < 0).all(1).any()          # some token was chosen by no expert
+
+
+# ---------------------------------------------------------- FP8 E4M3 weights --
+
+def test_fp8_e4m3_decode():
+    """Every code against torch's float8_e4m3fn, plus the format's landmarks."""
+    codes = torch.arange(256, dtype=torch.uint8)
+    want = codes.view(torch.float8_e4m3fn).double().numpy()
+    got = np.array([oracle.fp8_e4m3(c) for c in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(want)) and np.array_equal(got[~np.isnan(got)], want[~np.isnan(want)])
+    assert oracle.fp8_e4m3(0x38) == 1.0 and oracle.fp8_e4m3(0x7E) == 448.0 and oracle.fp8_e4m3(0xFE) == -448.0
+    assert oracle.fp8_e4m3(0x01) == 2.0 ** -9 and oracle.fp8_e4m3(0x08) == 2.0 ** -6
+    assert np.isnan(oracle.fp8_e4m3(0x7F)) and np.isnan(oracle.fp8_e4m3(0xFF))
+
+
+def _fp8_values(codes, scale_rows):
+    return codes_to_f64(codes) * scale_rows.astype(np.float64)[..., None]
+
+
+def codes_to_f64(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def test_swiglu_fp8_vs_torch():
+    """Weight = decoded code * row scale, then the SwiGLU expert (torch on the
+    dequantised weights)."""
+    r = rng(33)
+    d, F = 48, 80
+    codes = [moe_synth.fp8_codes(7, t, s) for t, s in ((2, (F, d)), (3, (F, d)), (4, (d, F)))]
+    sc = [r.uniform(0.01, 0.05, n).astype(np.float32) for n in (F, F, d)]
+    x = r.standard_normal(d)
+    want = torch_swiglu(*(_fp8_values(c, s) for c, s in zip(codes, sc)), x)
+    got = oracle.swiglu(*codes, x, bf16=True, scales=sc)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14)
+
+
+def test_forward_rows_fp8_layer():
+    """A whole FP8-weight layer (routed + shared expert) against the same
+    layer with the dequantised weights given as fp32 (exact when the product
+    code * scale is representable in fp32, which holds for these scales: 3
+    mantissa bits times an fp32 value with few significant bits)."""
+    r = rng(34)
+    T, d, F, E, K, Fs = 12, 16, 8, 4, 2, 8
+    wl = moe_synth.workload("mixtral_prefill", T=T, d=d, F=F, E=E, K=K, n_shared=1, Fs=Fs, wdtype="fp8")
+    h = wl.gen_all()
+    # scales with 8 significant bits: every code * scale is exact in fp32
+    for k in ("S1", "S3", "S2", "Ss1", "Ss3", "Ss2"):
+        h[k] = (np.round(h[k] * 2.0 ** 14) / 2.0 ** 14).astype(np.float32)
+    assert oracle.layer_of(wl).w_fp8 == 1
+    x = r.standard_normal((T, d)).astype(np.float32)
+    L8 = oracle.layer(T, d, F, E, K, n_shared=1, Fs=Fs, w_fp8=True)
+    rt = oracle.route(L8, x, h["Wg"])
+    y8 = oracle.forward_rows(L8, x, rt["idx"], rt["w"], rt["dest"], h["W1"], h["W3"], h["W2"], h["Ws1"], h["Ws3"],
+                             h["Ws2"], **{k: h[k] for k in ("S1", "S3", "S2", "Ss1", "Ss3", "Ss2")})
+    deq = lambda c, s: _fp8_values(c, s).astype(np.float32)
+    W1f = np.stack([deq(h["W1"][e], h["S1"][e]) for e in range(E)])
+    W3f = np.stack([deq(h["W3"][e], h["S3"][e]) for e in range(E)])
+    W2f = np.stack([deq(h["W2"][e], h["S2"][e]) for e in range(E)])
+    Ws = [deq(h[a][0], h[b][0])[None] for a, b in (("Ws1", "Ss1"), ("Ws3", "Ss3"), ("Ws2", "Ss2"))]
+    assert np.array_equal(W1f.astype(np.float64), np.stack([_fp8_values(h["W1"][e], h["S1"][e]) for e in range(E)]))
+    Lf = oracle.layer(T, d, F, E, K, n_shared=1, Fs=Fs)
+    yf = oracle.forward_rows(Lf, x, rt["idx"], rt["w"], rt["dest"], W1f, W3f, W2f, *Ws)
+    np.testing.assert_allclose(y8, yf, rtol=1e-13, atol=1e-13)
