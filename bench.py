@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--drop-policy", default="first_come", choices=["first_come", "affinity", "reroute"],
                     help="which assignments an expert over capacity drops")
     ap.add_argument("--expert-choice", action="store_true", help="expert-choice routing instead of token choice")
+    ap.add_argument("--fp8", action="store_true", help="FP8 E4M3 expert weights with per-row scales")
     return ap.parse_args()
 
 
@@ -61,20 +62,25 @@ def kernel_accounting(wl, R: int, touched: int):
     expert, h; writes fp32 rows; 2 d F flops per row.  The shared expert, when
     present, is one more launch of each with T rows.
     """
-    esz = 2 if wl.dtype == "bf16" else 4
+    esz = 2 if wl.dtype == "bf16" else 4           # activations
+    fp8 = wl.wdtype == "fp8"
+    wsz = 1 if fp8 else esz                         # expert weights
     d, F = wl.d, wl.F
+    sc_up = 2.0 * F * 4 if fp8 else 0.0             # fp32 row scales of W1, W3
+    sc_dn = d * 4.0 if fp8 else 0.0                 # of W2
     acc = {
-        "gemm_gate_up": dict(flops=4.0 * d * F * R, bytes=touched * 2.0 * F * d * esz + R * d * esz + R * F * esz),
-        "gemm_down": dict(flops=2.0 * d * F * R, bytes=touched * 1.0 * F * d * esz + R * F * esz + R * d * 4.0),
+        "gemm_gate_up": dict(flops=4.0 * d * F * R,
+                             bytes=touched * (2.0 * F * d * wsz + sc_up) + R * d * esz + R * F * esz),
+        "gemm_down": dict(flops=2.0 * d * F * R, bytes=touched * (1.0 * F * d * wsz + sc_dn) + R * F * esz + R * d * 4.0),
     }
     if wl.n_shared:
         Fs, T = wl.Fs, wl.T
         acc["gemm_gate_up"]["flops_shared"] = 4.0 * d * Fs * T
-        acc["gemm_gate_up"]["bytes_shared"] = 2.0 * Fs * d * esz + T * d * esz + T * Fs * esz
+        acc["gemm_gate_up"]["bytes_shared"] = 2.0 * Fs * d * wsz + T * d * esz + T * Fs * esz
         acc["gemm_down"]["flops_shared"] = 2.0 * d * Fs * T
-        acc["gemm_down"]["bytes_shared"] = 1.0 * Fs * d * esz + T * Fs * esz + T * d * 4.0
+        acc["gemm_down"]["bytes_shared"] = 1.0 * Fs * d * wsz + T * Fs * esz + T * d * 4.0
     layer_flops = 6.0 * d * F * R + 2.0 * wl.T * d * wl.E + (6.0 * d * wl.Fs * wl.T if wl.n_shared else 0.0)
-    layer_bytes = (touched * 3.0 * F * d * esz + (3.0 * wl.Fs * d * esz if wl.n_shared else 0.0)
+    layer_bytes = (touched * 3.0 * F * d * wsz + (3.0 * wl.Fs * d * wsz if wl.n_shared else 0.0)
                    + 2.0 * wl.T * d * esz + wl.E * d * 4.0)
     return acc, layer_flops, layer_bytes
 
@@ -129,7 +135,7 @@ def main():
     import mixture_experts_sparse_route_amd as moe
     from moe_synth import workload
 
-    wl = workload(args.workload)
+    wl = workload(args.workload, **({"wdtype": "fp8"} if args.fp8 else {}))
     lib = moe.load_library()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
@@ -149,7 +155,11 @@ def main():
     spec = moe.LayerSpec(tokens=wl.T, d_model=wl.d, d_ff=wl.F, n_experts=wl.E, top_k=wl.K, gate=wl.gate,
                          capacity_factor=wl.capacity_factor, n_shared=wl.n_shared,
                          d_ff_shared=wl.Fs, dtype=wl.dtype, stats=args.stats, drop_policy=args.drop_policy,
-                         expert_choice=args.expert_choice, renorm=wl.renorm and not args.expert_choice)
+                         expert_choice=args.expert_choice, renorm=wl.renorm and not args.expert_choice,
+                         wdtype=wl.wdtype)
+    scales = None
+    if args.fp8:
+        scales = dict(w1=d["S1"], w3=d["S3"], w2=d["S2"], ws1=d["Ss1"], ws3=d["Ss3"], ws2=d["Ss2"])
     ws, _ = moe.alloc_workspace(spec)
     r = moe.Routing(spec)
     y = torch.empty((wl.T, wl.d), dtype=torch.bfloat16 if wl.dtype == "bf16" else torch.float32, device="cuda")
@@ -157,7 +167,7 @@ def main():
 
     def step():
         moe.moe_forward(spec, d["x"], d["Wg"], d["logit_bias"], d["sel_bias"], d["W1"], d["W3"], d["W2"], d["Ws1"],
-                        d["Ws3"], d["Ws2"], y, r, ws, stream)
+                        d["Ws3"], d["Ws2"], y, r, ws, stream, scales=scales)
 
     for _ in range(args.warmup):
         step()
@@ -248,6 +258,7 @@ def main():
         "config": {"workload": wl.name, "tokens": wl.T, "d_model": wl.d, "d_ff": wl.F, "n_experts": wl.E,
                    "top_k": wl.K, "gate": "sigmoid" if wl.gate else "softmax", "renorm": wl.renorm,
                    "capacity_factor": wl.capacity_factor, "n_shared": wl.n_shared, "d_ff_shared": wl.Fs,
+                   "expert_weights": "fp8_e4m3" if args.fp8 else wl.dtype,
                    "router_stats": args.stats, "drop_policy": args.drop_policy,
                    "routing": "expert_choice" if args.expert_choice else "token_choice",
                    "parallelism": "single GPU"},

@@ -52,8 +52,26 @@ typedef enum moe_status {
   MOE_ERR_HIP = 4          /* a HIP launch or runtime call failed */
 } moe_status;
 
-/* Element types.  Router weights and logits are always fp32. */
-typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+/* Element types.  Router weights and logits are always fp32.
+ * MOE_FP8_E4M3 (expert weights only, with bf16 activations): OCP FP8 E4M3
+ * codes, one byte per weight, each weight row with an fp32 scale
+ * (moe_scales): weight[row][k] = E4M3(code[row][k]) * scale[row]
+ * [TD §7.4 FP8 expert GEMMs; LN §4.2 E4M3]. */
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+
+/* Per-row fp32 scales of MOE_FP8_E4M3 expert weights (device pointers): a
+ * scale per output channel, i.e. per row of W1, W3 ([E, F] each), W2
+ * ([E, d]) and of the shared Ws1, Ws3 ([n_shared, d_ff_shared]) and Ws2
+ * ([n_shared, d]).  Ignored for bf16 / fp32 weights (the pointer to the
+ * struct may then be NULL). */
+typedef struct moe_scales {
+  const float* w1;
+  const float* w3;
+  const float* w2;
+  const float* ws1;
+  const float* ws3;
+  const float* ws2;
+} moe_scales;
 
 /* Gate [TD §3.2 softmax; TD §3.5 sigmoid]. */
 typedef enum moe_gate { MOE_GATE_SOFTMAX = 0, MOE_GATE_SIGMOID = 1 } moe_gate;
@@ -152,7 +170,7 @@ typedef struct moe_config {
   int64_t n_shared;        /* always-active shared experts, 0 or 1 [TD §3.4] */
   int64_t d_ff_shared;     /* shared expert d_ff; bf16: multiple of 64 */
   int32_t act_dtype;       /* moe_dtype of x and the expert activations (xp, h) */
-  int32_t w_dtype;         /* moe_dtype of the expert weights; must equal act_dtype */
+  int32_t w_dtype;         /* moe_dtype of the expert weights: act_dtype, or MOE_FP8_E4M3 with bf16 act_dtype */
   /* moe_dtype of y: act_dtype, or MOE_F32 for a bf16 layer (the fp32 sum
    * before its final rounding; the bf16 output is exactly its
    * round-to-nearest-even image). */
@@ -219,13 +237,15 @@ moe_status moe_dispatch(const moe_config* cfg, const void* x, const moe_routing*
  *          offsets[n_groups] <= max_rows (not checked on the device)
  * W1, W3:  device [n_groups, F, d] w_dtype (nn.Linear out x in layout)
  * W2:      device [n_groups, d, F] w_dtype
+ * scales:  host struct of device pointers; required (w1, w3, w2) for
+ *          MOE_FP8_E4M3 weights, else nullable
  * yp:      device [max_rows, d] fp32
  * The intermediate h = SiLU(.) * (.) is kept in act_dtype in the workspace.
  * max_rows: host upper bound on offsets[n_groups], at most moe_max_rows(cfg);
  * 1 <= n_groups <= n_experts. */
 moe_status moe_expert_ffn(const moe_config* cfg, const void* xp, const int32_t* offsets, int64_t n_groups,
-                          int64_t max_rows, const void* W1, const void* W3, const void* W2, float* yp, void* ws,
-                          size_t ws_bytes, moe_stream_t stream);
+                          int64_t max_rows, const void* W1, const void* W3, const void* W2, const moe_scales* scales,
+                          float* yp, void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* a9: weighted combine [TD §3.1 step 4; BD §4 step 5]:
  *   y[t] = sum_{k ascending, dest[t*K+k] >= 0} topk_w[t][k] * yp[dest[t*K+k]]
@@ -245,11 +265,12 @@ moe_status moe_combine(const moe_config* cfg, const float* yp, const moe_routing
  * given, the routing results are written there (and MOE_F_LOGITS_IN /
  * MOE_F_TOPK_IN inputs read from there).  Required with MOE_F_*_IN and
  * MOE_F_STATS.
- * Ws1/Ws3/Ws2: required iff n_shared == 1.  y: device [T, d] out_dtype. */
+ * Ws1/Ws3/Ws2: required iff n_shared == 1.  scales: as for moe_expert_ffn,
+ * plus ws1, ws3, ws2 when n_shared == 1.  y: device [T, d] out_dtype. */
 moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, const float* logit_bias,
                        const float* sel_bias, const void* W1, const void* W3, const void* W2, const void* Ws1,
-                       const void* Ws3, const void* Ws2, void* y, const moe_routing* r, void* ws, size_t ws_bytes,
-                       moe_stream_t stream);
+                       const void* Ws3, const void* Ws2, const moe_scales* scales, void* y, const moe_routing* r,
+                       void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* Static string for a status code. */
 const char* moe_status_string(moe_status s);

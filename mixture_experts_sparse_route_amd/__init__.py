@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16 = 0, 1
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_GATE_SOFTMAX, MOE_GATE_SIGMOID = 0, 1
 MOE_F_RENORM, MOE_F_RESIDUAL, MOE_F_LOGITS_IN, MOE_F_TOPK_IN, MOE_F_STATS = 1, 2, 4, 8, 16
 MOE_F_EXPERT_CHOICE = 32
@@ -49,6 +49,11 @@ class MoeConfig(ctypes.Structure):
     ]
 
 
+class MoeScales(ctypes.Structure):
+    """Per-row fp32 scales of FP8 E4M3 expert weights (device pointers)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w1", "w3", "w2", "ws1", "ws3", "ws2")]
+
+
 class MoeRouting(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("logits", "topk_idx", "topk_w", "counts", "offsets", "dest", "row_src", "dropped", "stats")]
@@ -72,9 +77,9 @@ def load_library(path: str = LIB_PATH):
         "moe_max_rows": [C, ctypes.POINTER(i64)],
         "moe_route": [C, vp, vp, vp, vp, R, vp, sz, vp],
         "moe_dispatch": [C, vp, R, vp, vp],
-        "moe_expert_ffn": [C, vp, vp, i64, i64, vp, vp, vp, vp, vp, sz, vp],
+        "moe_expert_ffn": [C, vp, vp, i64, i64, vp, vp, vp, ctypes.POINTER(MoeScales), vp, vp, sz, vp],
         "moe_combine": [C, vp, R, vp, vp, vp, vp],
-        "moe_forward": [C, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, R, vp, sz, vp],
+        "moe_forward": [C, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(MoeScales), vp, R, vp, sz, vp],
         "moe_profile_enable": [ctypes.c_uint32],
         "moe_profile_reset": [],
         "moe_profile_read": [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)],
@@ -122,6 +127,7 @@ class LayerSpec:
     n_shared: int = 0
     d_ff_shared: int = 0
     dtype: str = "bf16"            # "bf16" or "f32" (activations and expert weights)
+    wdtype: str = ""               # "fp8": expert weights are E4M3 codes with per-row scales (bf16 layer)
     out_dtype: Optional[str] = None  # dtype of y; None = dtype ("f32" allowed for a bf16 layer)
     logits_in: bool = False
     topk_in: bool = False
@@ -136,7 +142,8 @@ class LayerSpec:
         dt = MOE_BF16 if self.dtype == "bf16" else MOE_F32
         ot = dt if self.out_dtype is None else (MOE_BF16 if self.out_dtype == "bf16" else MOE_F32)
         return MoeConfig(self.tokens, self.d_model, self.d_ff, self.n_experts, self.top_k, self.gate, flags,
-                         float(self.capacity_factor), self.n_shared, self.d_ff_shared, dt, dt, ot,
+                         float(self.capacity_factor), self.n_shared, self.d_ff_shared, dt,
+                         MOE_FP8_E4M3 if self.wdtype == "fp8" else dt, ot,
                          DROP_POLICIES[self.drop_policy])
 
 
@@ -243,10 +250,18 @@ def moe_dispatch(spec, x, routing: Routing, xp, stream=None):
                                        _stream(stream)), "moe_dispatch")
 
 
-def moe_expert_ffn(spec, xp, offsets, n_groups, max_rows_, W1, W3, W2, yp, ws, stream=None):
+def _scales(scales):
+    """MoeScales from a dict of device tensors (keys w1, w3, w2, ws1, ws3, ws2)."""
+    if scales is None:
+        return None
+    return ctypes.byref(MoeScales(*(_ptr(scales.get(k)) for k in ("w1", "w3", "w2", "ws1", "ws3", "ws2"))))
+
+
+def moe_expert_ffn(spec, xp, offsets, n_groups, max_rows_, W1, W3, W2, yp, ws, stream=None, scales=None):
+    """scales: dict of device fp32 row-scale tensors for FP8 E4M3 weights."""
     _check(load_library().moe_expert_ffn(ctypes.byref(_cfg(spec)), _ptr(xp), _ptr(offsets), n_groups, max_rows_,
-                                         _ptr(W1), _ptr(W3), _ptr(W2), _ptr(yp), _ws_ptr(ws), _ws_bytes(ws),
-                                         _stream(stream)), "moe_expert_ffn")
+                                         _ptr(W1), _ptr(W3), _ptr(W2), _scales(scales), _ptr(yp), _ws_ptr(ws),
+                                         _ws_bytes(ws), _stream(stream)), "moe_expert_ffn")
 
 
 def moe_combine(spec, yp, routing: Routing, shared_out, x_residual, y, stream=None):
@@ -256,10 +271,12 @@ def moe_combine(spec, yp, routing: Routing, shared_out, x_residual, y, stream=No
 
 
 def moe_forward(spec, x, Wg, logit_bias, sel_bias, W1, W3, W2, Ws1, Ws3, Ws2, y, routing: Optional[Routing], ws,
-                stream=None):
+                stream=None, scales=None):
+    """scales: dict of device fp32 row-scale tensors for FP8 E4M3 weights."""
     r = routing.struct() if routing is not None else None
     _check(load_library().moe_forward(ctypes.byref(_cfg(spec)), _ptr(x), _ptr(Wg), _ptr(logit_bias), _ptr(sel_bias),
-                                      _ptr(W1), _ptr(W3), _ptr(W2), _ptr(Ws1), _ptr(Ws3), _ptr(Ws2), _ptr(y),
+                                      _ptr(W1), _ptr(W3), _ptr(W2), _ptr(Ws1), _ptr(Ws3), _ptr(Ws2),
+                                      _scales(scales), _ptr(y),
                                       ctypes.byref(r) if r is not None else None, _ws_ptr(ws), _ws_bytes(ws),
                                       _stream(stream)), "moe_forward")
 

@@ -46,6 +46,7 @@ struct Shape {
   bool bf16;
   bool out_bf16;
   bool stats;  // router statistics requested
+  bool w8;     // expert weights are E4M3 bytes with per-row scales
   int policy;  // moe_drop_policy in effect (first-come when there is no capacity)
   int64_t K2;  // re-routing alternates per token
   bool ec;     // expert-choice routing: K is E (the K = E form), cap the tokens per expert
@@ -83,9 +84,10 @@ moe_status validate(const moe_config* c, Shape* sh) {
   if (c->n_shared == 1 && c->d_ff_shared < 1) return fail(MOE_ERR_INVALID_ARG, "d_ff_shared must be >= 1");
   if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16)
     return fail(MOE_ERR_INVALID_ARG, "unknown act_dtype %d", (int)c->act_dtype);
-  if (c->w_dtype != MOE_F32 && c->w_dtype != MOE_BF16)
+  if (c->w_dtype != MOE_F32 && c->w_dtype != MOE_BF16 && c->w_dtype != MOE_FP8_E4M3)
     return fail(MOE_ERR_INVALID_ARG, "unknown w_dtype %d", (int)c->w_dtype);
-  if (c->w_dtype != c->act_dtype) return fail(MOE_ERR_UNSUPPORTED, "w_dtype must equal act_dtype");
+  if (c->w_dtype == MOE_FP8_E4M3 ? c->act_dtype != MOE_BF16 : c->w_dtype != c->act_dtype)
+    return fail(MOE_ERR_UNSUPPORTED, "w_dtype must equal act_dtype, or be MOE_FP8_E4M3 with bf16 activations");
   if (c->out_dtype != MOE_F32 && c->out_dtype != MOE_BF16)
     return fail(MOE_ERR_INVALID_ARG, "unknown out_dtype %d", (int)c->out_dtype);
   if (c->act_dtype == MOE_F32 && c->out_dtype != MOE_F32)
@@ -116,6 +118,7 @@ moe_status validate(const moe_config* c, Shape* sh) {
   sh->bf16 = bf16;
   sh->out_bf16 = c->out_dtype == MOE_BF16;
   sh->stats = c->flags & MOE_F_STATS;
+  sh->w8 = c->w_dtype == MOE_FP8_E4M3;
   sh->policy = cap >= 0 ? c->drop_policy : MOE_DROP_FIRST_COME;
   sh->K2 = sh->policy == MOE_DROP_REROUTE ? std::min(K, E - K) : 0;
   sh->T = T;
@@ -299,13 +302,14 @@ moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const 
   return MOE_OK;
 }
 
+// s1 / s3 / s2: row scales of E4M3 weights (s.w8), else unused.
 moe_status do_ffn(const Shape& s, const void* A, const int32_t* offsets, int64_t n_groups, int64_t max_rows,
-                  const void* W1, const void* W3, const void* W2, void* h, float* yp, int4* tab_up, int4* tab_down,
-                  int32_t* counts, int64_t F, hipStream_t st) {
-  const FfnPlan plan = ffn_plan(s.bf16, max_rows, n_groups, F, s.d);
+                  const void* W1, const void* W3, const void* W2, const float* s1, const float* s3, const float* s2,
+                  void* h, float* yp, int4* tab_up, int4* tab_down, int32_t* counts, int64_t F, hipStream_t st) {
+  const FfnPlan plan = ffn_plan(s.bf16, s.w8, max_rows, n_groups, F, s.d);
   MOE_HIP(launch_ffn_tiles(plan, offsets, n_groups, F, s.d, tab_up, tab_down, counts, st));
-  MOE_HIP(launch_gemm_gate_up(s.bf16, plan, A, tab_up, counts, n_groups, max_rows, W1, W3, h, F, s.d, st));
-  MOE_HIP(launch_gemm_down(s.bf16, plan, h, tab_down, counts + 1, n_groups, max_rows, W2, yp, F, s.d, st));
+  MOE_HIP(launch_gemm_gate_up(s.bf16, plan, A, tab_up, counts, n_groups, max_rows, W1, W3, s1, s3, h, F, s.d, st));
+  MOE_HIP(launch_gemm_down(s.bf16, plan, h, tab_down, counts + 1, n_groups, max_rows, W2, s2, yp, F, s.d, st));
   return MOE_OK;
 }
 
@@ -424,8 +428,8 @@ moe_status moe_dispatch(const moe_config* cfg, const void* x, const moe_routing*
 }
 
 moe_status moe_expert_ffn(const moe_config* cfg, const void* xp, const int32_t* offsets, int64_t n_groups,
-                          int64_t max_rows, const void* W1, const void* W3, const void* W2, float* yp, void* ws,
-                          size_t ws_bytes, moe_stream_t stream) {
+                          int64_t max_rows, const void* W1, const void* W3, const void* W2, const moe_scales* scales,
+                          float* yp, void* ws, size_t ws_bytes, moe_stream_t stream) {
   Shape s;
   moe_status st = validate(cfg, &s);
   if (st != MOE_OK) return st;
@@ -434,11 +438,16 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* xp, const int32_t* 
     return fail(MOE_ERR_INVALID_ARG, "max_rows = %lld outside [0, %lld]", (long long)max_rows,
                 (long long)s.max_rows);
   if (!xp || !offsets || !W1 || !W3 || !W2 || !yp) return fail(MOE_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (s.w8 && (!scales || !scales->w1 || !scales->w3 || !scales->w2))
+    return fail(MOE_ERR_INVALID_ARG, "MOE_FP8_E4M3 weights need scales->w1, w3, w2");
   Layout L;
   if ((st = check_ws(s, ws, ws_bytes, &L)) != MOE_OK) return st;
   if (max_rows == 0) return MOE_OK;
-  return do_ffn(s, xp, offsets, n_groups, max_rows, W1, W3, W2, at<void>(ws, L.h), yp, at<int4>(ws, L.tab_up),
-                at<int4>(ws, L.tab_down), at<int32_t>(ws, L.counts), s.F, (hipStream_t)stream);
+  const moe_scales none{};
+  const moe_scales& sc = s.w8 ? *scales : none;
+  return do_ffn(s, xp, offsets, n_groups, max_rows, W1, W3, W2, sc.w1, sc.w3, sc.w2, at<void>(ws, L.h), yp,
+                at<int4>(ws, L.tab_up), at<int4>(ws, L.tab_down), at<int32_t>(ws, L.counts), s.F,
+                (hipStream_t)stream);
 }
 
 moe_status moe_combine(const moe_config* cfg, const float* yp, const moe_routing* r, const float* shared_out,
@@ -458,8 +467,8 @@ moe_status moe_combine(const moe_config* cfg, const float* yp, const moe_routing
 
 moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, const float* logit_bias,
                        const float* sel_bias, const void* W1, const void* W3, const void* W2, const void* Ws1,
-                       const void* Ws3, const void* Ws2, void* y, const moe_routing* r, void* ws, size_t ws_bytes,
-                       moe_stream_t stream) {
+                       const void* Ws3, const void* Ws2, const moe_scales* scales, void* y, const moe_routing* r,
+                       void* ws, size_t ws_bytes, moe_stream_t stream) {
   Shape s;
   moe_status st = validate(cfg, &s);
   if (st != MOE_OK) return st;
@@ -468,6 +477,11 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, co
   if (!x || !y || !W1 || !W3 || !W2) return fail(MOE_ERR_INVALID_ARG, "x, y, W1, W3, W2 are required");
   if (!topk_in && !logits_in && !Wg) return fail(MOE_ERR_INVALID_ARG, "Wg is required");
   if (s.S && (!Ws1 || !Ws3 || !Ws2)) return fail(MOE_ERR_INVALID_ARG, "shared expert weights are required");
+  if (s.w8 && (!scales || !scales->w1 || !scales->w3 || !scales->w2 ||
+               (s.S && (!scales->ws1 || !scales->ws3 || !scales->ws2))))
+    return fail(MOE_ERR_INVALID_ARG, "MOE_FP8_E4M3 weights need their scales");
+  const moe_scales none{};
+  const moe_scales& sc = s.w8 ? *scales : none;
   if ((topk_in || logits_in || s.stats) && !r)
     return fail(MOE_ERR_INVALID_ARG, "MOE_F_*_IN and MOE_F_STATS need the routing arrays");
   if (r && (st = check_routing(r, !topk_in, s.stats)) != MOE_OK) return st;
@@ -494,8 +508,8 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, co
   float* yp = at<float>(ws, L.yp);
   if (s.max_rows > 0) {
     MOE_HIP(launch_dispatch(x, rr.row_src, rr.offsets + s.E, xp, s.max_rows, s.K, s.d * (int64_t)s.esz, hs));
-    if ((st = do_ffn(s, xp, rr.offsets, s.E, s.max_rows, W1, W3, W2, at<void>(ws, L.h), yp, at<int4>(ws, L.tab_up),
-                     at<int4>(ws, L.tab_down), at<int32_t>(ws, L.counts), s.F, hs)) != MOE_OK)
+    if ((st = do_ffn(s, xp, rr.offsets, s.E, s.max_rows, W1, W3, W2, sc.w1, sc.w3, sc.w2, at<void>(ws, L.h), yp,
+                     at<int4>(ws, L.tab_up), at<int4>(ws, L.tab_down), at<int32_t>(ws, L.counts), s.F, hs)) != MOE_OK)
       return st;
   }
   float* sh_out = nullptr;
@@ -503,8 +517,9 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, co
     int32_t* range = at<int32_t>(ws, L.sh_range);
     MOE_HIP(launch_set_range(range, s.T, hs));
     sh_out = at<float>(ws, L.sh_out);
-    if ((st = do_ffn(s, x, range, 1, s.T, Ws1, Ws3, Ws2, at<void>(ws, L.sh_h), sh_out, at<int4>(ws, L.sh_tab_up),
-                     at<int4>(ws, L.sh_tab_down), at<int32_t>(ws, L.sh_counts), s.Fs, hs)) != MOE_OK)
+    if ((st = do_ffn(s, x, range, 1, s.T, Ws1, Ws3, Ws2, sc.ws1, sc.ws3, sc.ws2, at<void>(ws, L.sh_h), sh_out,
+                     at<int4>(ws, L.sh_tab_up), at<int4>(ws, L.sh_tab_down), at<int32_t>(ws, L.sh_counts), s.Fs,
+                     hs)) != MOE_OK)
       return st;
   }
   MOE_HIP(launch_combine(s.bf16, s.out_bf16, yp, rr.topk_w, rr.dest, sh_out, (cfg->flags & MOE_F_RESIDUAL) ? x : nullptr, y, s.T,

@@ -21,6 +21,13 @@
 // position c ^ ((r >> 2) & 3), which makes both the DMA writes (1 KB
 // contiguous per wave) and the MFMA fragment reads bank-conflict free.
 //
+// FP8 weights (W8): the weight tile is staged as OCP E4M3 bytes (32-byte
+// LDS rows per k-step, 16-byte chunk c of row r at c ^ ((r >> 2) & 1)); each
+// 8-byte fragment is converted exactly to bf16 when read (E4M3 values are
+// bf16 values), the MFMAs are the bf16 ones, and the per-row weight scale
+// multiplies the fp32 sums in the epilogue (weight = code * scale[row], so
+// sum_k a_k w_k = scale * sum_k a_k code_k).
+//
 // Compute: 4 waves, 2 (M) x 2 (N); each wave owns 128 weight rows (8 MFMA
 // column blocks) and the 16-row MFMA row blocks 2i + wm of the m-tile.  Row
 // blocks past the group's last row are skipped, so a part-filled m-tile costs
@@ -40,8 +47,10 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 struct GemmArgs {
   const uint16_t* A;       // [rows, Kdim]
-  const uint16_t* B0;      // [groups, N, Kdim]  W1 or W2
-  const uint16_t* B1;      // [groups, N, Kdim]  W3 (gate_up only)
+  const void* B0;          // [groups, N, Kdim]  W1 or W2 (bf16, or E4M3 bytes)
+  const void* B1;          // [groups, N, Kdim]  W3 (gate_up only)
+  const float* S0;         // E4M3 weights: [groups, N] row scales of B0
+  const float* S1;         // E4M3 weights: [groups, N] row scales of B1
   void* C;                 // gate_up: bf16 [rows, N]; down: fp32 [rows, N]
   const int4* tab;         // tile table {group, first row, rows, first column}
   const int32_t* count;    // entries in tab
@@ -49,6 +58,35 @@ struct GemmArgs {
 };
 
 __device__ __forceinline__ int lds_pos(int row, int chunk) { return row * RB + ((chunk ^ ((row >> 2) & 3)) << 4); }
+
+// byte offset of E4M3 bytes k = 8*lk .. 8*lk+7 of weight-tile row `row`
+__device__ __forceinline__ int lds_pos8(int row, int lk) {
+  return row * 32 + ((((lk >> 1) ^ ((row >> 2) & 1))) << 4) + (lk & 1) * 8;
+}
+
+// 8 E4M3 bytes (k order, little-endian in lo, hi) -> 8 bf16, exactly
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  bf16x8_t r;
+  r[0] = a.x;
+  r[1] = a.y;
+  r[2] = b.x;
+  r[3] = b.y;
+  r[4] = c.x;
+  r[5] = c.y;
+  r[6] = d.x;
+  r[7] = d.y;
+  return r;
+}
+
+template <bool W8>
+constexpr int stage_bytes(int bm, int bnb) {
+  return bm * RB + bnb * (W8 ? 32 : RB);
+}
 
 // s_waitcnt vmcnt(N) with N an immediate.
 template <int N>
@@ -101,13 +139,13 @@ struct Seq {
 // Lane -> (row r_l of a 16-row group, chunk c_l), chunk swizzled as in
 // lds_pos; A rows past the tile's end are loaded clamped to its last row
 // (their results are never stored).
-template <int BM, int BNB, int NS, bool GATE_UP>
+template <int BM, int BNB, int NS, bool GATE_UP, bool W8>
 __device__ __forceinline__ void issue_step(IssueState& is, const GemmArgs& p, const Seq& q, char* lds, int s, int wave,
                                            int lane) {
   constexpr int AG = BM / 16 / 4;
   constexpr int BG = BNB / 16 / 4;
   constexpr int HALF = BNB / 4;  // gate_up: rows of one matrix in each quarter of the weight tile
-  constexpr int STAGE = (BM + BNB) * RB;
+  constexpr int STAGE = stage_bytes<W8>(BM, BNB);
   const int ti = s / q.nk, kt = s - ti * q.nk;
   if (ti != is.tile) {  // crossed into the next tile of the sequence
     is.tile = ti;
@@ -126,37 +164,62 @@ __device__ __forceinline__ void issue_step(IssueState& is, const GemmArgs& p, co
     __builtin_amdgcn_global_load_lds(p.A + (int64_t)(row_first + row) * Kd + ko,
                                      (lds_ptr_t)(st + (wave + 4 * j) * 16 * RB), 16, 0, 0);
   }
-  const int64_t gbase = (int64_t)g * p.N * Kd + ko;
+  if constexpr (!W8) {
+    const int64_t gbase = (int64_t)g * p.N * Kd + ko;
 #pragma unroll
-  for (int j = 0; j < BG; ++j) {
-    const int q16 = wave + 4 * j;
-    int col;
-    const uint16_t* base = p.B0;
-    if (GATE_UP) {
-      // quarters of the weight tile: W1 half 0, W3 half 0, W1 half 1, W3 half 1
-      const int qb = (q16 * 16) / HALF;
-      if (qb & 1) base = p.B1;
-      col = n0 + (qb >> 1) * HALF + (q16 * 16) % HALF + r_l;
-    } else {
-      col = n0 + q16 * 16 + r_l;
+    for (int j = 0; j < BG; ++j) {
+      const int q16 = wave + 4 * j;
+      int col;
+      const uint16_t* base = (const uint16_t*)p.B0;
+      if (GATE_UP) {
+        // quarters of the weight tile: W1 half 0, W3 half 0, W1 half 1, W3 half 1
+        const int qb = (q16 * 16) / HALF;
+        if (qb & 1) base = (const uint16_t*)p.B1;
+        col = n0 + (qb >> 1) * HALF + (q16 * 16) % HALF + r_l;
+      } else {
+        col = n0 + q16 * 16 + r_l;
+      }
+      col = min(col, p.N - 1);
+      __builtin_amdgcn_global_load_lds(base + gbase + (int64_t)col * Kd,
+                                       (lds_ptr_t)(st + BM * RB + (wave + 4 * j) * 16 * RB), 16, 0, 0);
     }
-    col = min(col, p.N - 1);
-    __builtin_amdgcn_global_load_lds(base + gbase + (int64_t)col * Kd,
-                                     (lds_ptr_t)(st + BM * RB + (wave + 4 * j) * 16 * RB), 16, 0, 0);
+  } else {
+    // E4M3 rows: 32 bytes per k-step, two lanes per row, 32 rows per load
+    constexpr int BG8 = BNB / 32 / 4;
+    const int r8 = lane >> 1;
+    const int c8 = (lane & 1) ^ ((r8 >> 2) & 1);  // the chunk that lands in this lane's LDS slot
+    const int64_t gbase8 = (int64_t)g * p.N * Kd + (int64_t)kt * BKS + c8 * 16;
+#pragma unroll
+    for (int j = 0; j < BG8; ++j) {
+      const int q32 = wave + 4 * j;
+      const int rt = q32 * 32 + r8;
+      int col;
+      const uint8_t* base = (const uint8_t*)p.B0;
+      if (GATE_UP) {
+        const int qb = rt / HALF;
+        if (qb & 1) base = (const uint8_t*)p.B1;
+        col = n0 + (qb >> 1) * HALF + rt % HALF;
+      } else {
+        col = n0 + rt;
+      }
+      col = min(col, p.N - 1);
+      __builtin_amdgcn_global_load_lds(base + gbase8 + (int64_t)col * Kd,
+                                       (lds_ptr_t)(st + BM * RB + q32 * 32 * 32), 16, 0, 0);
+    }
   }
 }
 
 // k-loop and epilogue of one tile for a wave that owns NBW active 16-row
 // blocks.  `step` is the global step of the tile's first k-step.
-template <int BM, int BNB, int NS, bool GATE_UP, int NBW>
+template <int BM, int BNB, int NS, bool GATE_UP, bool W8, int NBW>
 __device__ __forceinline__ void gemm_tile(IssueState& is, const GemmArgs& p, const Seq& q, char* lds, const TileRef te,
                                           const int step0, const int wave, const int lane) {
   constexpr int AG = BM / 16 / 4;
-  constexpr int BG = BNB / 16 / 4;
+  constexpr int BG = W8 ? BNB / 32 / 4 : BNB / 16 / 4;
   constexpr int CB = BNB / 32;  // 16-column MFMA blocks per N-wave
   constexpr int LPS = AG + BG;  // loads per wave per stage
   static_assert((NS - 2) * LPS <= 63, "vmcnt counts at most 63 outstanding loads");
-  constexpr int STAGE = (BM + BNB) * RB;
+  constexpr int STAGE = stage_bytes<W8>(BM, BNB);
   const int wm = wave & 1, wn = wave >> 1;
   const int lr = lane & 15, lk = lane >> 4;
 
@@ -175,9 +238,17 @@ __device__ __forceinline__ void gemm_tile(IssueState& is, const GemmArgs& p, con
     asm volatile("" ::: "memory");
     const char* st = lds + (s % NS) * STAGE;
     bf16x8_t bfr[CB];
+    if constexpr (W8) {
 #pragma unroll
-    for (int j = 0; j < CB; ++j)
-      bfr[j] = *(const bf16x8_t*)(st + BM * RB + lds_pos(wn * (BNB / 2) + j * 16 + lr, lk));
+      for (int j = 0; j < CB; ++j) {
+        const uint2 raw = *(const uint2*)(st + BM * RB + lds_pos8(wn * (BNB / 2) + j * 16 + lr, lk));
+        bfr[j] = fp8x8_to_bf16(raw.x, raw.y);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < CB; ++j)
+        bfr[j] = *(const bf16x8_t*)(st + BM * RB + lds_pos(wn * (BNB / 2) + j * 16 + lr, lk));
+    }
     bf16x8_t afr[NA];
 #pragma unroll
     for (int i = 0; i < NBW; ++i) afr[i] = *(const bf16x8_t*)(st + lds_pos((2 * i + wm) * 16 + lr, lk));
@@ -185,7 +256,7 @@ __device__ __forceinline__ void gemm_tile(IssueState& is, const GemmArgs& p, con
     // refill the stage consumed in the previous step (every wave has passed
     // this step's barrier, so nobody reads it any more); near the end of a
     // tile this already fetches the next tile's first k-steps
-    if (s + NS - 1 < q.total_steps) issue_step<BM, BNB, NS, GATE_UP>(is, p, q, lds, s + NS - 1, wave, lane);
+    if (s + NS - 1 < q.total_steps) issue_step<BM, BNB, NS, GATE_UP, W8>(is, p, q, lds, s + NS - 1, wave, lane);
 #pragma unroll
     for (int i = 0; i < NBW; ++i)
 #pragma unroll
@@ -206,10 +277,20 @@ __device__ __forceinline__ void gemm_tile(IssueState& is, const GemmArgs& p, con
       for (int j = 0; j < CB / 2; ++j) {
         const int col = n0 + wn * (BNB / 4) + j * 16 + lr;
         if (col >= p.N) continue;
+        if constexpr (W8) {
+          const float s1 = p.S0[(int64_t)te.g * p.N + col], s3 = p.S1[(int64_t)te.g * p.N + col];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int rr = rb_ + v;
-          if (rr < rows) C[(out_row0 + rr) * p.N + col] = f32_to_bf16(silu(acc[i][j][v]) * acc[i][j + CB / 2][v]);
+          for (int v = 0; v < 4; ++v) {
+            const int rr = rb_ + v;
+            if (rr < rows)
+              C[(out_row0 + rr) * p.N + col] = f32_to_bf16(silu(acc[i][j][v] * s1) * (acc[i][j + CB / 2][v] * s3));
+          }
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int rr = rb_ + v;
+            if (rr < rows) C[(out_row0 + rr) * p.N + col] = f32_to_bf16(silu(acc[i][j][v]) * acc[i][j + CB / 2][v]);
+          }
         }
       }
     } else {
@@ -218,10 +299,11 @@ __device__ __forceinline__ void gemm_tile(IssueState& is, const GemmArgs& p, con
       for (int j = 0; j < CB; ++j) {
         const int col = n0 + wn * (BNB / 2) + j * 16 + lr;
         if (col >= p.N) continue;
+        const float s2 = W8 ? p.S0[(int64_t)te.g * p.N + col] : 1.0f;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int rr = rb_ + v;
-          if (rr < rows) C[(out_row0 + rr) * p.N + col] = acc[i][j][v];
+          if (rr < rows) C[(out_row0 + rr) * p.N + col] = W8 ? acc[i][j][v] * s2 : acc[i][j][v];
         }
       }
     }
@@ -235,10 +317,11 @@ __device__ __forceinline__ void gemm_tile(IssueState& is, const GemmArgs& p, con
 // LDS ring, so the next tile's first stages load while the current tile
 // finishes and writes its output.  With one workgroup per tile this is the
 // plain one-tile-per-workgroup GEMM.
-template <int BM, int BNB, int NS, bool GATE_UP>
-__global__ __launch_bounds__(256, NS*(BM + BNB) * RB <= LDS_BYTES / 2 ? 2 : 1) void gemm_bf16_kernel(const GemmArgs p) {
+template <int BM, int BNB, int NS, bool GATE_UP, bool W8>
+__global__ __launch_bounds__(256, NS* stage_bytes<W8>(BM, BNB) <= LDS_BYTES / 2 ? 2 : 1) void gemm_bf16_kernel(
+    const GemmArgs p) {
   constexpr int MI = BM / 32;  // MFMA row blocks per M-wave
-  constexpr int STAGE = (BM + BNB) * RB;
+  constexpr int STAGE = stage_bytes<W8>(BM, BNB);
   static_assert(NS * STAGE <= LDS_BYTES, "LDS stages exceed 160 KB");
   __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
 
@@ -262,7 +345,7 @@ __global__ __launch_bounds__(256, NS*(BM + BNB) * RB <= LDS_BYTES / 2 ? 2 : 1) v
   is.next = q.n_tiles > 1 ? load_tile(p.tab, q.lbase + q.lstride) : is.cur;
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    if (s < q.total_steps) issue_step<BM, BNB, NS, GATE_UP>(is, p, q, lds, s, wave, lane);
+    if (s < q.total_steps) issue_step<BM, BNB, NS, GATE_UP, W8>(is, p, q, lds, s, wave, lane);
 
   for (int t = 0; t < q.n_tiles; ++t) {
     // k-steps issued so far end inside tile t (nk >= NS - 1), so the issue
@@ -273,13 +356,13 @@ __global__ __launch_bounds__(256, NS*(BM + BNB) * RB <= LDS_BYTES / 2 ? 2 : 1) v
     switch (nbw) {
 #define GG_CASE(n)                                                                        \
   case n:                                                                                 \
-    if constexpr (n <= MI) gemm_tile<BM, BNB, NS, GATE_UP, n>(is, p, q, lds, te, t * q.nk, wave, lane); \
+    if constexpr (n <= MI) gemm_tile<BM, BNB, NS, GATE_UP, W8, n>(is, p, q, lds, te, t * q.nk, wave, lane); \
     break;
       GG_CASE(1) GG_CASE(2) GG_CASE(3) GG_CASE(4) GG_CASE(5) GG_CASE(6) GG_CASE(7) GG_CASE(8)
 #undef GG_CASE
       default:
         // no rows in this M half: still take part in the barriers and loads
-        gemm_tile<BM, BNB, NS, GATE_UP, 0>(is, p, q, lds, te, t * q.nk, wave, lane);
+        gemm_tile<BM, BNB, NS, GATE_UP, W8, 0>(is, p, q, lds, te, t * q.nk, wave, lane);
         break;
     }
   }
@@ -287,15 +370,21 @@ __global__ __launch_bounds__(256, NS*(BM + BNB) * RB <= LDS_BYTES / 2 ? 2 : 1) v
 
 }  // namespace
 
-// (m-tile rows, weight-tile rows, LDS stages) compiled below.  The k-loop
-// needs K >= 32 * (NS - 1); the launchers check it.
+// (m-tile rows, weight-tile rows, LDS stages) compiled below, for bf16 and for
+// E4M3 weights.  The k-loop needs K >= 32 * (NS - 1); the launchers check it.
 #define MOE_GEMM_CONFIGS(X) X(256, 256, 5) X(256, 256, 4) X(128, 256, 3) X(128, 256, 6) X(64, 256, 4) \
   X(128, 128, 4) X(128, 128, 3) X(64, 128, 8) X(64, 128, 6) X(64, 128, 3)
+#define MOE_GEMM8_CONFIGS(X) X(128, 256, 5) X(128, 256, 3) X(128, 128, 6) X(128, 128, 3) X(64, 128, 10) \
+  X(64, 128, 3)
 
-bool gemm_bf16_has_config(int bm, int bnb, int ns) {
+bool gemm_bf16_has_config(bool w8, int bm, int bnb, int ns) {
 #define MOE_HAS(B, W, N) \
   if (bm == B && bnb == W && ns == N) return true;
-  MOE_GEMM_CONFIGS(MOE_HAS)
+  if (w8) {
+    MOE_GEMM8_CONFIGS(MOE_HAS)
+  } else {
+    MOE_GEMM_CONFIGS(MOE_HAS)
+  }
 #undef MOE_HAS
   return false;
 }
@@ -309,31 +398,48 @@ static int64_t launch_grid(const FfnPlan& pl, int64_t grid) {
 }
 
 hipError_t gemm_bf16_gate_up(const FfnPlan& pl, const void* A, const int4* tab, const int32_t* count, int64_t grid,
-                             const void* W1, const void* W3, void* h, int64_t F, int64_t d, hipStream_t s) {
-  GemmArgs a{(const uint16_t*)A, (const uint16_t*)W1, (const uint16_t*)W3, h, tab, count, (int)F, (int)d};
+                             const void* W1, const void* W3, const float* s1, const float* s3, void* h, int64_t F,
+                             int64_t d, hipStream_t s) {
+  GemmArgs a{(const uint16_t*)A, W1, W3, s1, s3, h, tab, count, (int)F, (int)d};
   if (d / BKS < pl.ns_up - 1) return hipErrorInvalidValue;
   const unsigned g = (unsigned)launch_grid(pl, grid);
 #define MOE_LAUNCH(B, W, N)                                           \
   if (pl.bm == B && pl.bnb_up == W && pl.ns_up == N) {                \
-    gemm_bf16_kernel<B, W, N, true><<<g, 256, 0, s>>>(a);             \
+    gemm_bf16_kernel<B, W, N, true, W8V><<<g, 256, 0, s>>>(a);        \
     return hipGetLastError();                                         \
   }
-  MOE_GEMM_CONFIGS(MOE_LAUNCH)
+  if (pl.w8) {
+#define W8V true
+    MOE_GEMM8_CONFIGS(MOE_LAUNCH)
+#undef W8V
+  } else {
+#define W8V false
+    MOE_GEMM_CONFIGS(MOE_LAUNCH)
+#undef W8V
+  }
 #undef MOE_LAUNCH
   return hipErrorInvalidValue;
 }
 
 hipError_t gemm_bf16_down(const FfnPlan& pl, const void* h, const int4* tab, const int32_t* count, int64_t grid,
-                          const void* W2, float* yp, int64_t F, int64_t d, hipStream_t s) {
-  GemmArgs a{(const uint16_t*)h, (const uint16_t*)W2, nullptr, yp, tab, count, (int)d, (int)F};
+                          const void* W2, const float* s2, float* yp, int64_t F, int64_t d, hipStream_t s) {
+  GemmArgs a{(const uint16_t*)h, W2, nullptr, s2, nullptr, yp, tab, count, (int)d, (int)F};
   if (F / BKS < pl.ns_down - 1) return hipErrorInvalidValue;
   const unsigned g = (unsigned)launch_grid(pl, grid);
 #define MOE_LAUNCH(B, W, N)                                           \
   if (pl.bm == B && pl.bnb_down == W && pl.ns_down == N) {            \
-    gemm_bf16_kernel<B, W, N, false><<<g, 256, 0, s>>>(a);            \
+    gemm_bf16_kernel<B, W, N, false, W8V><<<g, 256, 0, s>>>(a);       \
     return hipGetLastError();                                         \
   }
-  MOE_GEMM_CONFIGS(MOE_LAUNCH)
+  if (pl.w8) {
+#define W8V true
+    MOE_GEMM8_CONFIGS(MOE_LAUNCH)
+#undef W8V
+  } else {
+#define W8V false
+    MOE_GEMM_CONFIGS(MOE_LAUNCH)
+#undef W8V
+  }
 #undef MOE_LAUNCH
   return hipErrorInvalidValue;
 }

@@ -101,8 +101,8 @@ static int env_int(const char* name, int def) {
   return e ? atoi(e) : def;
 }
 
-FfnPlan ffn_plan(bool bf16, int64_t max_rows, int64_t n_groups, int64_t F, int64_t d) {
-  if (!bf16) return FfnPlan{FB, 0, 1, 0, 1, 0, FB, FB};
+FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t n_groups, int64_t F, int64_t d) {
+  if (!bf16) return FfnPlan{FB, 0, 1, 0, 1, 0, FB, FB, false};
   // 128-row m-tiles with a 3-stage ring of 256-row weight tiles (72 KB of
   // LDS): two workgroups per CU, so one tile's pipeline fill and epilogue
   // overlap the other's main loop.  A GEMM that would have fewer than two
@@ -110,24 +110,28 @@ FfnPlan ffn_plan(bool bf16, int64_t max_rows, int64_t n_groups, int64_t F, int64
   // Few rows per expert (decode-sized batches): 64-row m-tiles and a 6-stage
   // ring of 128-row weight tiles, the deepest weight stream that still fits
   // two workgroups per CU.
-  FfnPlan p{128, 256, 3, 256, 3, 0, 128, 256};
+  // E4M3 weights halve the weight-tile bytes, so the same LDS holds deeper
+  // rings: 5 stages of 128 x 256 tiles, 6 of 128 x 128, 10 of 64 x 128.
+  const int ns_main = w8 ? 5 : 3, ns_narrow = w8 ? 6 : 4, ns_decode = w8 ? 10 : 6;
+  FfnPlan p{128, 256, ns_main, 256, ns_main, 0, 128, 256, w8};
   if (n_groups > 0 && max_rows / n_groups <= 64) {
-    p = FfnPlan{64, 128, 6, 128, 6, 0, 64, 128};
+    p = FfnPlan{64, 128, ns_decode, 128, ns_decode, 0, 64, 128, w8};
   } else {
     const int64_t mtiles = max_rows / 128 > n_groups ? max_rows / 128 : n_groups;  // rough m-tile count
     const int64_t want = 2 * (int64_t)device_cus();
     if (mtiles * ((F + 127) / 128) < want) {
       p.bnb_up = 128;
-      p.ns_up = 4;
+      p.ns_up = ns_narrow;
     }
     if (mtiles * ((d + 255) / 256) < want) {
       p.bnb_down = 128;
-      p.ns_down = 4;
+      p.ns_down = ns_narrow;
     }
   }
   // A ring deeper than the reduction dimension's k-steps + 1 cannot be
-  // filled: short reductions (d or F of 64 .. 160) take the 3-stage variant
-  // of the same tile shape (every bf16 size is at least 2 k-steps).
+  // filled: a reduction (d or F) of fewer than NS - 1 k-steps of 32 takes the
+  // 3-stage variant of the same tile shape (every bf16 size is at least 2
+  // k-steps).
   if (d / 32 < p.ns_up - 1) p.ns_up = 3;
   if (F / 32 < p.ns_down - 1) p.ns_down = 3;
   // overrides for tuning: MOE_GEMM_BM, MOE_GEMM_{BNB,NS}_{UP,DOWN}, MOE_GEMM_WGS
@@ -138,7 +142,7 @@ FfnPlan ffn_plan(bool bf16, int64_t max_rows, int64_t n_groups, int64_t F, int64
   p.bnb_down = env_int("MOE_GEMM_BNB_DOWN", p.bnb_down);
   p.ns_down = env_int("MOE_GEMM_NS_DOWN", p.ns_down);
   p.wg_per_cu = env_int("MOE_GEMM_WGS", p.wg_per_cu);
-  if (!gemm_bf16_has_config(p.bm, p.bnb_up, p.ns_up) || !gemm_bf16_has_config(p.bm, p.bnb_down, p.ns_down) ||
+  if (!gemm_bf16_has_config(w8, p.bm, p.bnb_up, p.ns_up) || !gemm_bf16_has_config(w8, p.bm, p.bnb_down, p.ns_down) ||
       d / 32 < p.ns_up - 1 || F / 32 < p.ns_down - 1)
     p = def;
   p.bn_out_up = p.bnb_up / 2;
@@ -163,14 +167,14 @@ static int64_t grid_of(const FfnPlan& p, int64_t max_rows, int64_t n_groups, int
 }
 
 hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const void* A, const int4* tab, const int32_t* count,
-                               int64_t n_groups, int64_t max_rows, const void* W1, const void* W3, void* h, int64_t F,
-                               int64_t d, hipStream_t s) {
+                               int64_t n_groups, int64_t max_rows, const void* W1, const void* W3, const float* s1,
+                               const float* s3, void* h, int64_t F, int64_t d, hipStream_t s) {
   const int64_t grid = grid_of(p, max_rows, n_groups, F, p.bn_out_up);
   if (grid == 0) return hipSuccess;
   prof_begin(K_GEMM_GATE_UP, s);
   hipError_t err;
   if (bf16) {
-    err = gemm_bf16_gate_up(p, A, tab, count, grid, W1, W3, h, F, d, s);
+    err = gemm_bf16_gate_up(p, A, tab, count, grid, W1, W3, s1, s3, h, F, d, s);
   } else {
     F32Args a{(const float*)A, (const float*)W1, (const float*)W3, (float*)h, tab, count, (int)F, (int)d};
     gemm_f32_kernel<true><<<(unsigned)grid, 256, 0, s>>>(a);
@@ -181,14 +185,14 @@ hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const void* A, const
 }
 
 hipError_t launch_gemm_down(bool bf16, const FfnPlan& p, const void* h, const int4* tab, const int32_t* count,
-                            int64_t n_groups, int64_t max_rows, const void* W2, float* yp, int64_t F, int64_t d,
-                            hipStream_t s) {
+                            int64_t n_groups, int64_t max_rows, const void* W2, const float* s2, float* yp, int64_t F,
+                            int64_t d, hipStream_t s) {
   const int64_t grid = grid_of(p, max_rows, n_groups, d, p.bn_out_down);
   if (grid == 0) return hipSuccess;
   prof_begin(K_GEMM_DOWN, s);
   hipError_t err;
   if (bf16) {
-    err = gemm_bf16_down(p, h, tab, count, grid, W2, yp, F, d, s);
+    err = gemm_bf16_down(p, h, tab, count, grid, W2, s2, yp, F, d, s);
   } else {
     F32Args a{(const float*)h, (const float*)W2, nullptr, yp, tab, count, (int)d, (int)F};
     gemm_f32_kernel<false><<<(unsigned)grid, 256, 0, s>>>(a);

@@ -107,12 +107,14 @@ struct FfnPlan {
   int wg_per_cu;    // bf16: persistent workgroups per CU (0 = one workgroup per tile)
   int bn_out_up;    // h columns per GEMM1 tile
   int bn_out_down;  // yp columns per GEMM2 tile
+  bool w8;          // expert weights are E4M3 bytes with per-row scales
 };
 // Compute units of the current device (queried once).
 int device_cus();
-FfnPlan ffn_plan(bool bf16, int64_t max_rows, int64_t n_groups, int64_t F, int64_t d);
-// Whether the bf16 GEMM is compiled for (m-tile rows, weight-tile rows, stages).
-bool gemm_bf16_has_config(int bm, int bnb, int ns);
+FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t n_groups, int64_t F, int64_t d);
+// Whether the bf16-activation GEMM is compiled for (m-tile rows, weight-tile
+// rows, stages), with bf16 (w8 false) or E4M3 (w8 true) weights.
+bool gemm_bf16_has_config(bool w8, int bm, int bnb, int ns);
 // Worst-case m-tiles for `bm`-row tiles.
 int64_t ffn_max_mtiles(int bm, int64_t max_rows, int64_t n_groups);
 // Entries the tile tables need for any plan of this dtype.
@@ -122,16 +124,18 @@ int64_t ffn_table_entries(bool bf16, int64_t max_rows, int64_t n_groups, int64_t
 hipError_t launch_ffn_tiles(const FfnPlan& p, const int32_t* offsets, int64_t n_groups, int64_t F, int64_t d,
                             int4* tab_up, int4* tab_down, int32_t* counts, hipStream_t s);
 // bf16 MFMA path (gemm_bf16.hip); called through the launchers below.
+// s1 / s3 / s2: [groups, N] row scales of E4M3 weights (p.w8), else unused.
 hipError_t gemm_bf16_gate_up(const FfnPlan& p, const void* A, const int4* tab, const int32_t* count, int64_t grid,
-                             const void* W1, const void* W3, void* h, int64_t F, int64_t d, hipStream_t s);
+                             const void* W1, const void* W3, const float* s1, const float* s3, void* h, int64_t F,
+                             int64_t d, hipStream_t s);
 hipError_t gemm_bf16_down(const FfnPlan& p, const void* h, const int4* tab, const int32_t* count, int64_t grid,
-                          const void* W2, float* yp, int64_t F, int64_t d, hipStream_t s);
+                          const void* W2, const float* s2, float* yp, int64_t F, int64_t d, hipStream_t s);
 hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const void* A, const int4* tab, const int32_t* count,
-                               int64_t n_groups, int64_t max_rows, const void* W1, const void* W3, void* h, int64_t F,
-                               int64_t d, hipStream_t s);
+                               int64_t n_groups, int64_t max_rows, const void* W1, const void* W3, const float* s1,
+                               const float* s3, void* h, int64_t F, int64_t d, hipStream_t s);
 hipError_t launch_gemm_down(bool bf16, const FfnPlan& p, const void* h, const int4* tab, const int32_t* count,
-                            int64_t n_groups, int64_t max_rows, const void* W2, float* yp, int64_t F, int64_t d,
-                            hipStream_t s);
+                            int64_t n_groups, int64_t max_rows, const void* W2, const float* s2, float* yp, int64_t F,
+                            int64_t d, hipStream_t s);
 
 // dst[0] = 0, dst[1] = n (row range of the shared expert).
 hipError_t launch_set_range(int32_t* dst, int64_t n, hipStream_t s);

@@ -65,7 +65,14 @@ def host_bits(t: torch.Tensor) -> np.ndarray:
 def spec_of(wl, **kw) -> moe.LayerSpec:
     return moe.LayerSpec(tokens=wl.T, d_model=wl.d, d_ff=wl.F, n_experts=wl.E, top_k=wl.K, gate=wl.gate,
                          renorm=wl.renorm, capacity_factor=wl.capacity_factor, n_shared=wl.n_shared,
-                         d_ff_shared=wl.Fs, dtype=wl.dtype, **kw)
+                         d_ff_shared=wl.Fs, dtype=wl.dtype, wdtype=wl.wdtype, **kw)
+
+
+def device_scales(d: dict):
+    """The library's scales dict from device input tensors (None without FP8 weights)."""
+    if d.get("S1") is None:
+        return None
+    return dict(w1=d["S1"], w3=d["S3"], w2=d["S2"], ws1=d.get("Ss1"), ws3=d.get("Ss3"), ws2=d.get("Ss2"))
 
 
 class Case:
@@ -100,7 +107,7 @@ class Case:
         y = torch.empty((wl.T, wl.d), dtype=ydt, device="cuda")
         d = self.d
         moe.moe_forward(spec, d["x"], d["Wg"], d["logit_bias"], d["sel_bias"], d["W1"], d["W3"], d["W2"],
-                        d["Ws1"], d["Ws3"], d["Ws2"], y, r, ws)
+                        d["Ws1"], d["Ws3"], d["Ws2"], y, r, ws, scales=device_scales(d))
         torch.cuda.synchronize()
         return y, r
 

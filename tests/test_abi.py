@@ -123,19 +123,19 @@ def test_entry_points_reject_null_and_small_workspace_without_launching(lib):
     assert lib.moe_route(ctypes.byref(c), None, None, None, None, ctypes.byref(r), 256, 1 << 30, None) \
         == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_dispatch(ctypes.byref(c), None, ctypes.byref(r), 8, None) == moe.MOE_ERR_INVALID_ARG
-    assert lib.moe_expert_ffn(ctypes.byref(c), 8, 8, 0, 16, 8, 8, 8, 8, 256, 1 << 30, None) \
+    assert lib.moe_expert_ffn(ctypes.byref(c), 8, 8, 0, 16, 8, 8, 8, None, 8, 256, 1 << 30, None) \
         == moe.MOE_ERR_INVALID_ARG  # n_groups = 0
-    assert lib.moe_expert_ffn(ctypes.byref(c), 8, 8, 8, 1 << 20, 8, 8, 8, 8, 256, 1 << 30, None) \
+    assert lib.moe_expert_ffn(ctypes.byref(c), 8, 8, 8, 1 << 20, 8, 8, 8, None, 8, 256, 1 << 30, None) \
         == moe.MOE_ERR_INVALID_ARG  # max_rows above the config's bound
     cr = spec(residual=True).config()
     assert lib.moe_combine(ctypes.byref(cr), 8, ctypes.byref(r), None, None, 8, None) == moe.MOE_ERR_INVALID_ARG
     # shared expert weights required
     cs = spec(n_shared=1, d_ff_shared=256).config()
-    assert lib.moe_forward(ctypes.byref(cs), 8, 8, None, None, 8, 8, 8, None, None, None, 8, None, 256, 1 << 30,
+    assert lib.moe_forward(ctypes.byref(cs), 8, 8, None, None, 8, 8, 8, None, None, None, None, 8, None, 256, 1 << 30,
                            None) == moe.MOE_ERR_INVALID_ARG
     # *_IN flags need the routing arrays
     ci = spec(logits_in=True).config()
-    assert lib.moe_forward(ctypes.byref(ci), 8, 8, None, None, 8, 8, 8, None, None, None, 8, None, 256, 1 << 30,
+    assert lib.moe_forward(ctypes.byref(ci), 8, 8, None, None, 8, 8, 8, None, None, None, None, 8, None, 256, 1 << 30,
                            None) == moe.MOE_ERR_INVALID_ARG
 
 
@@ -146,7 +146,7 @@ def test_zero_tokens_is_a_no_op(lib):
     assert lib.moe_route(ctypes.byref(c), 8, 8, None, None, ctypes.byref(r), 256, n, None) == moe.MOE_OK
     assert lib.moe_dispatch(ctypes.byref(c), 8, ctypes.byref(r), 8, None) == moe.MOE_OK
     assert lib.moe_combine(ctypes.byref(c), 8, ctypes.byref(r), None, None, 8, None) == moe.MOE_OK
-    assert lib.moe_forward(ctypes.byref(c), 8, 8, None, None, 8, 8, 8, None, None, None, 8, None, 256, n,
+    assert lib.moe_forward(ctypes.byref(c), 8, 8, None, None, 8, 8, 8, None, None, None, None, 8, None, 256, n,
                            None) == moe.MOE_OK
 
 
@@ -164,7 +164,7 @@ def test_statistics_flag_validation(lib):
         == moe.MOE_ERR_INVALID_ARG
     assert b"stats" in lib.moe_last_error()
     # moe_forward with statistics needs caller routing arrays
-    assert lib.moe_forward(ctypes.byref(c), 8, 8, None, None, 8, 8, 8, None, None, None, 8, None, 256, 1 << 30,
+    assert lib.moe_forward(ctypes.byref(c), 8, 8, None, None, 8, 8, 8, None, None, None, None, 8, None, 256, 1 << 30,
                            None) == moe.MOE_ERR_INVALID_ARG
 
 
@@ -208,3 +208,26 @@ def test_expert_choice_validation(lib):
     assert moe.max_rows(spec(expert_choice=True, renorm=False, tokens=100, n_experts=8, top_k=2)) == 8 * 25
     assert moe.max_rows(spec(expert_choice=True, renorm=False, tokens=10, n_experts=2, top_k=2,
                              capacity_factor=3.0)) == 2 * 10
+
+
+def test_fp8_weight_validation(lib):
+    """MOE_FP8_E4M3 expert weights: only with bf16 activations, and the scales
+    are required by moe_expert_ffn and moe_forward."""
+    n = ctypes.c_size_t()
+    c = spec(dtype="f32", wdtype="fp8").config()
+    assert lib.moe_workspace_size(ctypes.byref(c), ctypes.byref(n)) == moe.MOE_ERR_UNSUPPORTED
+    c = spec(wdtype="fp8").config()
+    assert c.w_dtype == moe.MOE_FP8_E4M3 and c.act_dtype == moe.MOE_BF16
+    assert lib.moe_workspace_size(ctypes.byref(c), ctypes.byref(n)) == moe.MOE_OK
+    assert lib.moe_expert_ffn(ctypes.byref(c), 8, 8, 8, 16, 8, 8, 8, None, 8, 256, 1 << 30, None) \
+        == moe.MOE_ERR_INVALID_ARG
+    assert b"scales" in lib.moe_last_error()
+    half = moe.MoeScales(8, 8, None, None, None, None)
+    assert lib.moe_expert_ffn(ctypes.byref(c), 8, 8, 8, 16, 8, 8, 8, ctypes.byref(half), 8, 256, 1 << 30, None) \
+        == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward(ctypes.byref(c), 8, 8, None, None, 8, 8, 8, None, None, None, None, 8, None, 256, 1 << 30,
+                           None) == moe.MOE_ERR_INVALID_ARG
+    cs = spec(wdtype="fp8", n_shared=1, d_ff_shared=128).config()
+    full = moe.MoeScales(8, 8, 8, None, None, None)      # shared-expert scales missing
+    assert lib.moe_forward(ctypes.byref(cs), 8, 8, None, None, 8, 8, 8, 8, 8, 8, ctypes.byref(full), 8, None, 256,
+                           1 << 30, None) == moe.MOE_ERR_INVALID_ARG

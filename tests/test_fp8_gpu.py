@@ -1,0 +1,116 @@
+"""GPU parity of FP8 E4M3 expert weights (per-row fp32 scales) against the
+oracle (Tech Daily 2026-04-14, §7.4: expert GEMMs in FP8; lnwmold.com
+article, §4.2: E4M3).
+
+The kernels stage the E4M3 bytes, convert them exactly to bf16 for the bf16
+MFMA and multiply the fp32 sums by the row scale; the oracle decodes each
+code by the format's definition, multiplies by the row scale and computes
+in double (storing h in bf16, as the bf16 layer does).  The routing is the
+bf16 layer's, so the tolerance is the bf16 one (checked on the fp32
+result); every case also checks that the bf16 output is the rounded fp32
+one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+import oracle
+import mixture_experts_sparse_route_amd as moe
+from moe_synth import workload
+from parity_lib import Case, assert_permutation_equal, assert_y_close, host_f64, kept_tokens, routing_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU parity tests need a GPU"
+    moe.load_library()
+    moe_synth.build(force=False)
+    oracle.build(force=False)
+
+
+CASES = {
+    "mixtral_small": workload("mixtral_prefill", T=300, d=512, F=1024, wdtype="fp8"),
+    "mixtral_two_mtiles": workload("mixtral_prefill", T=1100, d=256, F=384, wdtype="fp8"),
+    "decode_small": workload("mixtral_decode", T=5, d=512, F=1024, wdtype="fp8"),
+    "switch_capacity": workload("switch_top1_capacity", T=1000, d=256, F=512, E=16, wdtype="fp8"),
+    "deepseek_shared": workload("deepseek_v3_fine", T=200, d=512, F=256, E=64, Fs=256, wdtype="fp8"),
+    "short_reduction": workload("mixtral_decode", T=6, d=64, F=64, wdtype="fp8"),
+    "short_reduction_prefill": workload("mixtral_prefill", T=700, d=64, F=128, wdtype="fp8"),
+}
+
+
+def check_fp8(case: Case, tokens=None, expert_choice=False):
+    wl = case.wl
+    T, K = wl.T, wl.K
+    orc = case.oracle_route()
+    lg = orc["logits"]
+    y, r = case.gpu_forward(logits_in=lg, out_dtype="f32", expert_choice=expert_choice)
+    g = routing_host(r)
+    if expert_choice:
+        orc = oracle.route_expert_choice(case.L, lg=lg)
+        L = oracle.ec_layer(case.L)
+        w = np.nan_to_num(orc["w"])
+        live = np.ones(T, bool) if wl.n_shared else (orc["dest"].reshape(T, -1) >= 0).any(1)
+    else:
+        L, w = case.L, orc["w"]
+        live = kept_tokens(orc["dest"], K, wl.n_shared)
+    assert_permutation_equal(g, orc, "fp8")
+    rows = np.arange(T) if tokens is None else tokens
+    h = case.h
+    y_ref = oracle.forward_rows(L, h["x"], orc["idx"], w, orc["dest"], h["W1"], h["W3"], h["W2"], h["Ws1"], h["Ws3"],
+                                h["Ws2"], tokens=rows,
+                                **{k: h[k] for k in ("S1", "S3", "S2", "Ss1", "Ss3", "Ss2")})
+    err = assert_y_close(host_f64(y)[rows], y_ref, "bf16", rows=live[rows], label="fp8")
+    yb, _ = case.gpu_forward(logits_in=lg, out_dtype="bf16", expert_choice=expert_choice)
+    assert torch.equal(yb.view(torch.int16), y.to(torch.bfloat16).view(torch.int16)), "bf16 output != rounded fp32"
+    return err
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_fp8_small(name):
+    print(name, check_fp8(Case(CASES[name])))
+
+
+def test_fp8_expert_choice():
+    wl = workload("mixtral_prefill", T=300, d=256, F=128, renorm=False, wdtype="fp8")
+    print(check_fp8(Case(wl), expert_choice=True))
+
+
+def test_fp8_matches_dequantised_bf16_weights():
+    """Where code * scale is exactly a bf16 value (scales that are powers of
+    two), the FP8 layer must equal, bit for bit, the bf16 layer given the
+    dequantised weights: the same MFMAs see the same bf16 operands, and a
+    power-of-two scale commutes exactly with the fp32 sums."""
+    wl = workload("mixtral_prefill", T=200, d=256, F=256, wdtype="fp8")
+    case = Case(wl)
+    h = case.h
+    for k in ("S1", "S3", "S2"):
+        e = np.round(np.log2(h[k]))
+        case.d[k].copy_(torch.from_numpy((2.0 ** e).astype(np.float32)))
+    lg = case.oracle_route()["logits"]
+    y8, _ = case.gpu_forward(logits_in=lg, out_dtype="f32")
+    # the same layer in bf16 with W = code * scale (exact in bf16)
+    deq = {}
+    for k, sk in (("W1", "S1"), ("W3", "S3"), ("W2", "S2")):
+        v = torch.from_numpy(h[k]).view(torch.float8_e4m3fn).float() * case.d[sk].cpu().float()[..., None]
+        deq[k] = v.to(torch.bfloat16)
+        assert torch.equal(deq[k].float(), v), "dequantised weight not exact in bf16"
+    wlb = wl.with_(wdtype="")
+    cb = Case(wlb)
+    for k in ("W1", "W3", "W2"):
+        cb.d[k] = deq[k].cuda()
+    yb, _ = cb.gpu_forward(logits_in=lg, out_dtype="f32")
+    assert torch.equal(y8, yb)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["mixtral_decode", "switch_top1_capacity"])
+def test_fp8_full_size(name):
+    case = Case(workload(name, wdtype="fp8"))
+    T = case.wl.T
+    r = np.random.default_rng(0)
+    toks = None if T <= 64 else np.array(sorted({0, T - 1} | set(r.choice(T, 24, replace=False).tolist())))
+    print(name, check_fp8(case, tokens=toks))

@@ -23,7 +23,7 @@ import oracle
 import mixture_experts_sparse_route_amd as moe
 from moe_synth import workload
 from parity_lib import (NEAR_TIE, Case, assert_permutation_equal, assert_weights_close, assert_y_close, dev,
-                        host_f64, kept_tokens, routing_host, spec_of, y_error)
+                        device_scales, host_f64, kept_tokens, routing_host, spec_of, y_error)
 
 pytestmark = pytest.mark.gpu
 
@@ -191,7 +191,8 @@ def test_entry_points_in_isolation():
     assert np.array_equal(xp_h, case.h["x"][orc["row_src"][:R] // wl.K])
 
     yp = torch.empty((mr, wl.d), dtype=torch.float32, device="cuda")
-    moe.moe_expert_ffn(spec, xp, r.offsets, wl.E, mr, case.d["W1"], case.d["W3"], case.d["W2"], yp, ws)
+    moe.moe_expert_ffn(spec, xp, r.offsets, wl.E, mr, case.d["W1"], case.d["W3"], case.d["W2"], yp, ws,
+                       scales=device_scales(case.d))
     torch.cuda.synchronize()
     yp_h = yp[:R].cpu().numpy().astype(np.float64)
     xrows = moe_synth.bf16_to_f32(case.h["x"][orc["row_src"][:R] // wl.K]).astype(np.float64)
