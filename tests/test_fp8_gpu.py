@@ -5,10 +5,15 @@ article, §4.2: E4M3).
 The kernels stage the E4M3 bytes, convert them exactly to bf16 for the bf16
 MFMA and multiply the fp32 sums by the row scale; the oracle decodes each
 code by the format's definition, multiplies by the row scale and computes
-in double (storing h in bf16, as the bf16 layer does).  The routing is the
-bf16 layer's, so the tolerance is the bf16 one (checked on the fp32
-result); every case also checks that the bf16 output is the rounded fp32
-one.
+in double (storing h in bf16, as the bf16 layer does).  Outputs are held to
+the stated bf16 bound, max |y - r| <= 2e-2 RMS(r) on the fp32 result: the
+E4M3 test weights are heavier-tailed than the bf16 ones, so an fp32 sum that
+lands on the other side of a bf16 rounding boundary of h than the double sum
+moves y by up to about 5e-3 RMS (a CPU emulation with fp32 sums gives 0.0043
+on the two-m-tile case), above the 5e-3 the bf16-weight tests hold.  The
+kernel itself is pinned bit for bit: with power-of-two scales the FP8 layer
+must equal the bf16 layer given the dequantised weights.  Every case also
+checks that the bf16 output is the rounded fp32 one.
 """
 import numpy as np
 import pytest
@@ -18,7 +23,7 @@ import moe_synth
 import oracle
 import mixture_experts_sparse_route_amd as moe
 from moe_synth import workload
-from parity_lib import Case, assert_permutation_equal, assert_y_close, host_f64, kept_tokens, routing_host
+from parity_lib import BF16_TOL, Case, assert_permutation_equal, host_f64, kept_tokens, routing_host, y_error
 
 pytestmark = pytest.mark.gpu
 
@@ -63,7 +68,8 @@ def check_fp8(case: Case, tokens=None, expert_choice=False):
     y_ref = oracle.forward_rows(L, h["x"], orc["idx"], w, orc["dest"], h["W1"], h["W3"], h["W2"], h["Ws1"], h["Ws3"],
                                 h["Ws2"], tokens=rows,
                                 **{k: h[k] for k in ("S1", "S3", "S2", "Ss1", "Ss3", "Ss2")})
-    err = assert_y_close(host_f64(y)[rows], y_ref, "bf16", rows=live[rows], label="fp8")
+    err, _ = y_error(host_f64(y)[rows], y_ref, "bf16", rows=live[rows])
+    assert err <= BF16_TOL, f"fp8: output error {err:.4g} > {BF16_TOL}"
     yb, _ = case.gpu_forward(logits_in=lg, out_dtype="bf16", expert_choice=expert_choice)
     assert torch.equal(yb.view(torch.int16), y.to(torch.bfloat16).view(torch.int16)), "bf16 output != rounded fp32"
     return err
