@@ -307,7 +307,7 @@ moe_status do_ffn(const Shape& s, const void* A, const int32_t* offsets, int64_t
                   const void* W1, const void* W3, const void* W2, const float* s1, const float* s3, const float* s2,
                   void* h, float* yp, int4* tab_up, int4* tab_down, int32_t* counts, int64_t F, hipStream_t st) {
   const FfnPlan plan = ffn_plan(s.bf16, s.w8, max_rows, n_groups, F, s.d);
-  MOE_HIP(launch_ffn_tiles(plan, offsets, n_groups, F, s.d, tab_up, tab_down, counts, st));
+  MOE_HIP(launch_ffn_tiles(plan, offsets, n_groups, max_rows, F, s.d, tab_up, tab_down, counts, st));
   MOE_HIP(launch_gemm_gate_up(s.bf16, plan, A, tab_up, counts, n_groups, max_rows, W1, W3, s1, s3, h, F, s.d, st));
   MOE_HIP(launch_gemm_down(s.bf16, plan, h, tab_down, counts + 1, n_groups, max_rows, W2, s2, yp, F, s.d, st));
   return MOE_OK;

@@ -31,8 +31,17 @@ __global__ __launch_bounds__(256) void ec_weights_kernel(float* __restrict__ log
   for (int e = lane; e < E; e += 64) {
     float l;
     if (S > 1) {
+      // the d-slices' partial sums in slice order, loads issued together
       l = part[(int64_t)t * E + e];
-      for (int q = 1; q < S; ++q) l += part[((int64_t)q * T + t) * E + e];
+      int q = 1;
+      for (; q + 8 <= S; q += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = part[((int64_t)(q + u) * T + t) * E + e];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) l += v[u];
+      }
+      for (; q < S; ++q) l += part[((int64_t)q * T + t) * E + e];
       if (bias) l += bias[e];
       lt[e] = l;
     } else {

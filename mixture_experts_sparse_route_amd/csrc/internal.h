@@ -121,8 +121,8 @@ int64_t ffn_max_mtiles(int bm, int64_t max_rows, int64_t n_groups);
 int64_t ffn_table_entries(bool bf16, int64_t max_rows, int64_t n_groups, int64_t n_cols, bool gate_up);
 // Builds both GEMMs' tile tables (int4 {group, first row, rows, first column})
 // and their entry counts counts[0] (gate_up) and counts[1] (down).
-hipError_t launch_ffn_tiles(const FfnPlan& p, const int32_t* offsets, int64_t n_groups, int64_t F, int64_t d,
-                            int4* tab_up, int4* tab_down, int32_t* counts, hipStream_t s);
+hipError_t launch_ffn_tiles(const FfnPlan& p, const int32_t* offsets, int64_t n_groups, int64_t max_rows, int64_t F,
+                            int64_t d, int4* tab_up, int4* tab_down, int32_t* counts, hipStream_t s);
 // bf16 MFMA path (gemm_bf16.hip); called through the launchers below.
 // s1 / s3 / s2: [groups, N] row scales of E4M3 weights (p.w8), else unused.
 hipError_t gemm_bf16_gate_up(const FfnPlan& p, const void* A, const int4* tab, const int32_t* count, int64_t grid,

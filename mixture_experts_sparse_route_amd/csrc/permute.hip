@@ -6,6 +6,8 @@
 // The first K_max arrivals in flat (token, choice) order are kept.
 #include <limits.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 #include "radix_select.h"
@@ -61,11 +63,13 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
   double psum = 0.0;
   if (e < E) {
     if (stats) {
+#pragma unroll 8
       for (int b = b0; b < b1; ++b) {
         sum += blk_count[(int64_t)b * E + e];
         psum += (double)blk_P[(int64_t)b * E + e];
       }
     } else {
+#pragma unroll 8
       for (int b = b0; b < b1; ++b) sum += blk_count[(int64_t)b * E + e];
     }
   }
@@ -75,6 +79,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
   if (e < E) {
     int run = 0;
     for (int q = 0; q < sub; ++q) run += part[q * Epad + e];
+#pragma unroll 8
     for (int b = b0; b < b1; ++b) {
       blk_base[(int64_t)b * E + e] = run;
       run += blk_count[(int64_t)b * E + e];
@@ -348,11 +353,12 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const V* __restrict__ x, 
 }
 
 // ------------------------------------------------------------ FFN tiles
-// One workgroup.  Tile list of both expert GEMMs: for group g with rows(g)
+// Tile list of both expert GEMMs (each workgroup scans the m-tile counts and
+// writes its share of the entries): for group g with rows(g)
 // rows, ceil(rows(g) / bm) m-tiles times the GEMM's n-tiles, in the order
 // (group, n-tile, m-tile) with the m-tile fastest, so the m-tiles of one
 // weight tile are neighbours.  Entry L = {group, first row, rows, first
-// column}; count[0] = number of entries.
+// column}; counts[0] / counts[1] = entries of the gate_up / down tables.
 __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t* __restrict__ offsets, int G, int bm,
                                                          int nt_up, int bn_up, int nt_down, int bn_down,
                                                          int4* __restrict__ tab_up, int4* __restrict__ tab_down,
@@ -378,16 +384,18 @@ __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t* __restri
   __syncthreads();
   const int total_m = mstart[G];
   const int tot_up = total_m * nt_up, tot_down = total_m * nt_down;
-  if (g == 0) {
+  if (g == 0 && blockIdx.x == 0) {
     counts[0] = tot_up;
     counts[1] = tot_down;
   }
+  // every workgroup computes the scan; workgroup b writes entries b*1024 + i
+  // (+ multiples of the grid's threads)
   for (int pass = 0; pass < 2; ++pass) {
     const int nt = pass == 0 ? nt_up : nt_down;
     const int bn = pass == 0 ? bn_up : bn_down;
     const int tot = pass == 0 ? tot_up : tot_down;
     int4* tab = pass == 0 ? tab_up : tab_down;
-    for (int L = threadIdx.x; L < tot; L += 1024) {
+    for (int L = blockIdx.x * 1024 + threadIdx.x; L < tot; L += gridDim.x * 1024) {
       // group of entry L: largest gg with mstart[gg] * nt <= L
       int lo = 0, hi = G;
       while (hi - lo > 1) {
@@ -467,13 +475,16 @@ hipError_t launch_dispatch(const void* x, const int32_t* row_src, const int32_t*
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_tiles(const FfnPlan& p, const int32_t* offsets, int64_t n_groups, int64_t F, int64_t d,
-                            int4* tab_up, int4* tab_down, int32_t* counts, hipStream_t s) {
+hipError_t launch_ffn_tiles(const FfnPlan& p, const int32_t* offsets, int64_t n_groups, int64_t max_rows, int64_t F,
+                            int64_t d, int4* tab_up, int4* tab_down, int32_t* counts, hipStream_t s) {
   const int nt_up = (int)((F + p.bn_out_up - 1) / p.bn_out_up);
   const int nt_down = (int)((d + p.bn_out_down - 1) / p.bn_out_down);
+  // enough workgroups for the largest table this plan can produce, at most 32
+  const int64_t most = ffn_max_mtiles(p.bm, max_rows, n_groups) * (nt_up > nt_down ? nt_up : nt_down);
+  const unsigned grid = (unsigned)std::min<int64_t>(32, std::max<int64_t>(1, (most + 1023) / 1024));
   prof_begin(K_FFN_TILES, s);
-  ffn_tiles_kernel<<<1, 1024, 0, s>>>(offsets, (int)n_groups, p.bm, nt_up, p.bn_out_up, nt_down, p.bn_out_down,
-                                      tab_up, tab_down, counts);
+  ffn_tiles_kernel<<<grid, 1024, 0, s>>>(offsets, (int)n_groups, p.bm, nt_up, p.bn_out_up, nt_down, p.bn_out_down,
+                                         tab_up, tab_down, counts);
   prof_end(K_FFN_TILES, s);
   return hipGetLastError();
 }

@@ -4,6 +4,8 @@
 // Gate and selection follow "技术日报 2026-04-14" (jsqmd.com): §3.1 Top-K
 // (KeepTopK), §3.2 softmax gate, §3.5 sigmoid gate, §4.3 and §9.2 selection-only
 // bias, §9.1 renormalised Top-K weights.
+#include <stdlib.h>
+
 #include "common.h"
 #include "internal.h"
 
@@ -224,6 +226,23 @@ __device__ __forceinline__ float group_sum(float v, int L) {
   return v;
 }
 
+// part[0][i] + part[1][i] + ... + part[S-1][i], added in slice order; the
+// loads are issued eight at a time so they overlap instead of forming one
+// dependent chain of S loads.
+__device__ __forceinline__ float sum_slices(const float* __restrict__ part, int S, int64_t stride, int64_t i) {
+  float l = part[i];
+  int q = 1;
+  for (; q + 8 <= S; q += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(q + u) * stride + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) l += v[u];
+  }
+  for (; q < S; ++q) l += part[(int64_t)q * stride + i];
+  return l;
+}
+
 __device__ __forceinline__ float group_maxf(float v, int L) {
   for (int off = L >> 1; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
   return v;
@@ -258,6 +277,21 @@ __global__ __launch_bounds__(256) void router_topk_kernel(float* __restrict__ lo
 
   const int t_begin = blockIdx.x * kTopkTokens;
   const int t_end = min(T, t_begin + kTopkTokens);
+  // Many d-slices (small T): the chunk's logits first, all threads over its
+  // (token, expert) pairs, so the long slice sums run in parallel; with few
+  // slices each lane sums its own experts' slices in the selection loop.
+  const bool presum = !topk_in && S >= 8;
+  if (presum) {
+    // the d-slices' partial sums in slice order, then the bias
+    const int n = (t_end - t_begin) * E;
+    for (int i = threadIdx.x; i < n; i += 256) {
+      const int64_t te = (int64_t)t_begin * E + i;
+      float l = sum_slices(part, S, (int64_t)T * E, te);
+      if (bias) l += bias[i % E];
+      logits[te] = l;
+    }
+    __syncthreads();  // the selection below reads them back (same workgroup)
+  }
   if (topk_in) {
     for (int f = t_begin * K + threadIdx.x; f < t_end * K; f += 256) {
       const int e = idx[f];
@@ -281,10 +315,9 @@ __global__ __launch_bounds__(256) void router_topk_kernel(float* __restrict__ lo
         sv[p] = 0.0f;
         if (valid && e < E) {
           float l;
-          if (S > 1) {
+          if (S > 1 && !presum) {
             // logits = the d-slices' partial sums added in slice order, then the bias
-            l = part[(int64_t)t * E + e];
-            for (int q = 1; q < S; ++q) l += part[((int64_t)q * T + t) * E + e];
+            l = sum_slices(part, S, (int64_t)T * E, (int64_t)t * E + e);
             if (bias) l += bias[e];
             logits[(int64_t)t * E + e] = l;
           } else {
@@ -432,8 +465,14 @@ __global__ __launch_bounds__(256) void router_topk_kernel(float* __restrict__ lo
 int router_splits(int64_t T, int64_t d, int64_t E, bool bf16) {
   const int64_t ew = (!bf16 || E > 16) ? 64 : 16;
   const int64_t tiles = ((T + LG_T - 1) / LG_T) * ((E + ew - 1) / ew);
+  // split d until there are `want` workgroups (tuning override: MOE_ROUTER_WGS)
+  static const int64_t want = [] {
+    const char* v = getenv("MOE_ROUTER_WGS");
+    const long n = v ? atol(v) : 0;
+    return n > 0 ? (int64_t)n : (int64_t)512;
+  }();
   int S = 1;
-  while (tiles * S < 512 && S < 64 && d % ((int64_t)S * 2 * LG_K) == 0) S *= 2;
+  while (tiles * S < want && S < 64 && d % ((int64_t)S * 2 * LG_K) == 0) S *= 2;
   return S;
 }
 
@@ -462,8 +501,11 @@ hipError_t launch_router_topk(float* logits, const float* part, int S, const flo
                               int32_t* idx, float* w, int32_t* blk_count, float* blk_P, float* blk_z, int32_t* alt_idx,
                               float* alt_w, int64_t K2, int64_t T, int64_t E, int64_t K, int gate, bool renorm,
                               bool topk_in, hipStream_t s) {
+  // lanes per token: a power of two with at most 4 experts per lane and at
+  // least K lanes (lane k keeps choice k, and re-routing alternate k, K2 <= K);
+  // fewer lanes per token = more tokens per wave pass
   int L = 1;
-  while (L < E && L < 64) L <<= 1;
+  while (L < 64 && (L * 4 < E || L < K)) L <<= 1;
   const int P = (int)((E + L - 1) / L);
   const unsigned nb = (unsigned)((T + kTopkTokens - 1) / kTopkTokens);
   prof_begin(K_ROUTER_TOPK, s);
