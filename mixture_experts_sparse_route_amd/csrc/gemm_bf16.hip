@@ -372,7 +372,7 @@ __global__ __launch_bounds__(256, NS* stage_bytes<W8>(BM, BNB) <= LDS_BYTES / 2 
 
 // (m-tile rows, weight-tile rows, LDS stages) compiled below, for bf16 and for
 // E4M3 weights.  The k-loop needs K >= 32 * (NS - 1); the launchers check it.
-#define MOE_GEMM_CONFIGS(X) X(256, 256, 5) X(256, 256, 4) X(128, 256, 3) X(128, 256, 6) X(64, 256, 4) \
+#define MOE_GEMM_CONFIGS(X) X(128, 256, 3) X(128, 256, 6) X(64, 256, 4) \
   X(128, 128, 4) X(128, 128, 3) X(64, 128, 8) X(64, 128, 6) X(64, 128, 3)
 #define MOE_GEMM8_CONFIGS(X) X(128, 256, 5) X(128, 256, 3) X(128, 128, 6) X(128, 128, 3) X(64, 128, 10) \
   X(64, 128, 3)

@@ -61,26 +61,35 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const uint16_t*
   const bool x_ok = t0 + xr < T;
   const uint16_t* xsrc = x + (int64_t)(x_ok ? t0 + xr : 0) * d + kbeg + xc * 8;
   constexpr int WL = EW * 8 / 256 > 0 ? EW * 8 / 256 : 1;  // float4 loads per thread
-  uint4 xreg;
-  float4 wreg[WL];
-  auto gload = [&](int k0) {
-    xreg = x_ok ? *(const uint4*)(xsrc + k0) : make_uint4(0, 0, 0, 0);
+  // two register sets: k-step kt+2 loads while kt+1 waits to be staged
+  uint4 xregA, xregB;
+  float4 wregA[WL], wregB[WL];
+  // Loads are unconditional (rows past T or E are clamped and zeroed when
+  // staged): straight-line loads let the compiler wait for exactly the
+  // register set being staged instead of draining every load in flight.
+  const float* wsrc[WL];
+  bool w_ok[WL];
 #pragma unroll
-    for (int i = 0; i < WL; ++i) {
-      const int q = tid + 256 * i;
-      const int er = q >> 3, c4 = q & 7;
-      wreg[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (q < EW * 8 && e0 + er < E) wreg[i] = *(const float4*)(Wg + (int64_t)(e0 + er) * d + kbeg + k0 + c4 * 4);
-    }
+  for (int i = 0; i < WL; ++i) {
+    const int q = (tid + 256 * i) % (EW * 8);
+    const int er = q >> 3, c4 = q & 7;
+    w_ok[i] = tid + 256 * i < EW * 8 && e0 + er < E;
+    wsrc[i] = Wg + (int64_t)min(e0 + er, E - 1) * d + kbeg + c4 * 4;
+  }
+  auto gload = [&](uint4& xreg, float4 (&wreg)[WL], int k0) {
+    xreg = *(const uint4*)(xsrc + k0);
+#pragma unroll
+    for (int i = 0; i < WL; ++i) wreg[i] = *(const float4*)(wsrc[i] + k0);
   };
-  auto lstore = [&](int st) {
-    *(uint4*)(xs[st] + lg_pos(xr, xc)) = xreg;
+  auto lstore = [&](const uint4& xreg, const float4 (&wreg)[WL], int st) {
+    *(uint4*)(xs[st] + lg_pos(xr, xc)) = x_ok ? xreg : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < WL; ++i) {
       const int q = tid + 256 * i;
       if (q >= EW * 8) continue;
       const int er = q >> 3, c4 = q & 7;
-      const float f[4] = {wreg[i].x, wreg[i].y, wreg[i].z, wreg[i].w};
+      const float4 wv = w_ok[i] ? wreg[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float f[4] = {wv.x, wv.y, wv.z, wv.w};
       uint16_t hi[4], mi[4], lo[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) split3(f[u], hi[u], mi[u], lo[u]);
@@ -99,13 +108,7 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const uint16_t*
 #pragma unroll
     for (int j = 0; j < EB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = kr / LG_K;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * LG_K);
+  auto compute = [&](int cur) {
     bf16x8_t af[TB];
 #pragma unroll
     for (int i = 0; i < TB; ++i) af[i] = *(const bf16x8_t*)(xs[cur] + lg_pos((wt * TB + i) * 16 + lr, lk));
@@ -118,8 +121,35 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const uint16_t*
         for (int i = 0; i < TB; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr, acc[i][j], 0, 0, 0);
       }
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
+  };
+
+  // LDS buffer kt % 2 holds k-step kt; register set A holds even k-steps,
+  // B odd ones, loaded two k-steps before they are staged.  The barriers
+  // wait only for this thread's LDS traffic (lgkmcnt), not for the global
+  // loads in flight (a plain __syncthreads would drain those every k-step);
+  // a register set is waited for where lstore reads it.
+  auto lds_barrier = [] {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // Every load is issued (k-steps past the end reload the last one and are
+  // never multiplied), so the loop has no branch around a load.
+  const int nk = kr / LG_K;
+  auto kofs = [&](int kt) { return min(kt, nk - 1) * LG_K; };
+  gload(xregA, wregA, 0);
+  gload(xregB, wregB, kofs(1));
+  lstore(xregA, wregA, 0);
+  lds_barrier();
+  for (int kt = 0; kt < nk; kt += 2) {
+    gload(xregA, wregA, kofs(kt + 2));
+    compute(0);
+    lstore(xregB, wregB, 1);
+    lds_barrier();
+    if (kt + 1 < nk) compute(1);
+    gload(xregB, wregB, kofs(kt + 3));
+    lstore(xregA, wregA, 0);
+    lds_barrier();
   }
   // lane holds tokens (block*16 + lk*4 + v), expert (block*16 + lr)
 #pragma unroll
