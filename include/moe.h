@@ -19,6 +19,10 @@
  *     is dense row-major; the caller owns all memory.  The library never
  *     allocates device memory: scratch lives in the caller's workspace
  *     (size from moe_workspace_size), 256-byte aligned.
+ *   - Activation, weight, scale and output arrays (x, Wg, W*, Ws*, scales,
+ *     xp, yp, shared_out, x_residual, y) must be 16-byte aligned (hipMalloc
+ *     and torch allocations are); others return MOE_ERR_INVALID_ARG.  Bias
+ *     and routing arrays need only their element alignment.
  *   - Configs and routing descriptors are host structs, read during the call.
  *   - All GPU work is enqueued on `stream` (NULL = the default stream) and is
  *     asynchronous.  Argument validation is synchronous, happens on the host

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -204,6 +205,14 @@ moe_status check_ws(const Shape& s, const void* ws, size_t ws_bytes, Layout* L) 
   return MOE_OK;
 }
 
+// Activation, weight, scale and output arrays are read and written with
+// 16-byte vector accesses.
+moe_status check_aligned(std::initializer_list<const void*> ptrs) {
+  for (const void* q : ptrs)
+    if ((uintptr_t)q % 16) return fail(MOE_ERR_INVALID_ARG, "activation, weight, scale and output arrays must be 16-byte aligned");
+  return MOE_OK;
+}
+
 template <typename T>
 T* at(void* ws, size_t off) {
   return (T*)((char*)ws + off);
@@ -303,10 +312,12 @@ moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const 
 }
 
 // s1 / s3 / s2: row scales of E4M3 weights (s.w8), else unused.
+// group_max: bound of any group's rows.
 moe_status do_ffn(const Shape& s, const void* A, const int32_t* offsets, int64_t n_groups, int64_t max_rows,
+                  int64_t group_max,
                   const void* W1, const void* W3, const void* W2, const float* s1, const float* s3, const float* s2,
                   void* h, float* yp, int4* tab_up, int4* tab_down, int32_t* counts, int64_t F, hipStream_t st) {
-  const FfnPlan plan = ffn_plan(s.bf16, s.w8, max_rows, n_groups, F, s.d);
+  const FfnPlan plan = ffn_plan(s.bf16, s.w8, max_rows, group_max, n_groups, F, s.d);
   MOE_HIP(launch_ffn_tiles(plan, offsets, n_groups, max_rows, F, s.d, tab_up, tab_down, counts, st));
   MOE_HIP(launch_gemm_gate_up(s.bf16, plan, A, tab_up, counts, n_groups, max_rows, W1, W3, s1, s3, h, F, s.d, st));
   MOE_HIP(launch_gemm_down(s.bf16, plan, h, tab_down, counts + 1, n_groups, max_rows, W2, s2, yp, F, s.d, st));
@@ -332,8 +343,11 @@ hipEvent_t get_event() {
     g_pool.pop_back();
     return e;
   }
+  // timing-only events: no system-scope fence (cache writeback and
+  // invalidate) when recorded, so the bracketed kernel and its neighbours run
+  // as they would unobserved
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
@@ -409,6 +423,7 @@ moe_status moe_route(const moe_config* cfg, const void* x, const float* Wg, cons
   const bool logits_in = cfg->flags & MOE_F_LOGITS_IN;
   if ((st = check_routing(r, !topk_in, s.stats)) != MOE_OK) return st;
   if (!topk_in && !logits_in && (!x || !Wg)) return fail(MOE_ERR_INVALID_ARG, "x and Wg are required");
+  if ((st = check_aligned({x, Wg})) != MOE_OK) return st;
   Layout L;
   if ((st = check_ws(s, ws, ws_bytes, &L)) != MOE_OK) return st;
   if (s.T == 0) return MOE_OK;
@@ -421,6 +436,7 @@ moe_status moe_dispatch(const moe_config* cfg, const void* x, const moe_routing*
   if (st != MOE_OK) return st;
   if (!r || !r->row_src || !r->offsets) return fail(MOE_ERR_INVALID_ARG, "routing row_src / offsets required");
   if (!x || !xp) return fail(MOE_ERR_INVALID_ARG, "x and xp are required");
+  if ((st = check_aligned({x, xp})) != MOE_OK) return st;
   if (s.T == 0) return MOE_OK;
   MOE_HIP(launch_dispatch(x, r->row_src, r->offsets + s.E, xp, s.max_rows, s.K, s.d * (int64_t)s.esz,
                           (hipStream_t)stream));
@@ -440,12 +456,16 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* xp, const int32_t* 
   if (!xp || !offsets || !W1 || !W3 || !W2 || !yp) return fail(MOE_ERR_INVALID_ARG, "a required pointer is NULL");
   if (s.w8 && (!scales || !scales->w1 || !scales->w3 || !scales->w2))
     return fail(MOE_ERR_INVALID_ARG, "MOE_FP8_E4M3 weights need scales->w1, w3, w2");
+  if ((st = check_aligned({xp, W1, W3, W2, yp})) != MOE_OK) return st;
+  if (s.w8 && (st = check_aligned({scales->w1, scales->w3, scales->w2})) != MOE_OK) return st;
   Layout L;
   if ((st = check_ws(s, ws, ws_bytes, &L)) != MOE_OK) return st;
   if (max_rows == 0) return MOE_OK;
   const moe_scales none{};
   const moe_scales& sc = s.w8 ? *scales : none;
-  return do_ffn(s, xp, offsets, n_groups, max_rows, W1, W3, W2, sc.w1, sc.w3, sc.w2, at<void>(ws, L.h), yp,
+  // the plan assumes the routed bound of a group's rows (any rows stay correct)
+  const int64_t group_max = s.cap >= 0 ? std::min(s.T, s.cap) : s.T;
+  return do_ffn(s, xp, offsets, n_groups, max_rows, group_max, W1, W3, W2, sc.w1, sc.w3, sc.w2, at<void>(ws, L.h), yp,
                 at<int4>(ws, L.tab_up), at<int4>(ws, L.tab_down), at<int32_t>(ws, L.counts), s.F,
                 (hipStream_t)stream);
 }
@@ -459,6 +479,7 @@ moe_status moe_combine(const moe_config* cfg, const float* yp, const moe_routing
   if (!yp || !y) return fail(MOE_ERR_INVALID_ARG, "yp and y are required");
   const bool residual = cfg->flags & MOE_F_RESIDUAL;
   if (residual && !x_residual) return fail(MOE_ERR_INVALID_ARG, "MOE_F_RESIDUAL needs x_residual");
+  if ((st = check_aligned({yp, y, shared_out, residual ? x_residual : nullptr})) != MOE_OK) return st;
   if (s.T == 0) return MOE_OK;
   MOE_HIP(launch_combine(s.bf16, s.out_bf16, yp, r->topk_w, r->dest, shared_out, residual ? x_residual : nullptr, y, s.T, s.d,
                          s.K, (hipStream_t)stream));
@@ -480,6 +501,9 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, co
   if (s.w8 && (!scales || !scales->w1 || !scales->w3 || !scales->w2 ||
                (s.S && (!scales->ws1 || !scales->ws3 || !scales->ws2))))
     return fail(MOE_ERR_INVALID_ARG, "MOE_FP8_E4M3 weights need their scales");
+  if ((st = check_aligned({x, Wg, W1, W3, W2, Ws1, Ws3, Ws2, y})) != MOE_OK) return st;
+  if (s.w8 && (st = check_aligned({scales->w1, scales->w3, scales->w2, scales->ws1, scales->ws3, scales->ws2})) != MOE_OK)
+    return st;
   const moe_scales none{};
   const moe_scales& sc = s.w8 ? *scales : none;
   if ((topk_in || logits_in || s.stats) && !r)
@@ -508,7 +532,9 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, co
   float* yp = at<float>(ws, L.yp);
   if (s.max_rows > 0) {
     MOE_HIP(launch_dispatch(x, rr.row_src, rr.offsets + s.E, xp, s.max_rows, s.K, s.d * (int64_t)s.esz, hs));
-    if ((st = do_ffn(s, xp, rr.offsets, s.E, s.max_rows, W1, W3, W2, sc.w1, sc.w3, sc.w2, at<void>(ws, L.h), yp,
+    // an expert holds at most one row per token, and at most its capacity
+    const int64_t group_max = s.cap >= 0 ? std::min(s.T, s.cap) : s.T;
+    if ((st = do_ffn(s, xp, rr.offsets, s.E, s.max_rows, group_max, W1, W3, W2, sc.w1, sc.w3, sc.w2, at<void>(ws, L.h), yp,
                      at<int4>(ws, L.tab_up), at<int4>(ws, L.tab_down), at<int32_t>(ws, L.counts), s.F, hs)) != MOE_OK)
       return st;
   }
@@ -517,7 +543,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, co
     int32_t* range = at<int32_t>(ws, L.sh_range);
     MOE_HIP(launch_set_range(range, s.T, hs));
     sh_out = at<float>(ws, L.sh_out);
-    if ((st = do_ffn(s, x, range, 1, s.T, Ws1, Ws3, Ws2, sc.ws1, sc.ws3, sc.ws2, at<void>(ws, L.sh_h), sh_out,
+    if ((st = do_ffn(s, x, range, 1, s.T, s.T, Ws1, Ws3, Ws2, sc.ws1, sc.ws3, sc.ws2, at<void>(ws, L.sh_h), sh_out,
                      at<int4>(ws, L.sh_tab_up), at<int4>(ws, L.sh_tab_down), at<int32_t>(ws, L.sh_counts), s.Fs,
                      hs)) != MOE_OK)
       return st;

@@ -36,7 +36,8 @@ __device__ __forceinline__ void store_act<float>(float* p, int64_t i, float v) {
 template <>
 __device__ __forceinline__ void store_act<uint16_t>(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
 
-__device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
+// SiLU(a) = a * sigmoid(a); the reciprocal is the hardware one (1 ulp)
+__device__ __forceinline__ float silu(float a) { return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
 
 // MI355X has 8 XCDs; the dispatcher hands workgroup b to XCD (b mod 8).
 constexpr int kXcds = 8;

@@ -28,8 +28,11 @@
 // multiplies the fp32 sums in the epilogue (weight = code * scale[row], so
 // sum_k a_k w_k = scale * sum_k a_k code_k).
 //
-// Compute: 4 waves, 2 (M) x 2 (N); each wave owns 128 weight rows (8 MFMA
-// column blocks) and the 16-row MFMA row blocks 2i + wm of the m-tile.  Row
+// Compute: 4 waves, 2 (M) x 2 (N); each wave owns BNB/2 weight rows (MFMA
+// column blocks of 16) and the 16-row MFMA row blocks 2i + wm of the m-tile.
+// The weight fragment is the MFMA's first operand and the row fragment its
+// second, so the accumulator of a lane runs along the output columns (four
+// consecutive ones), which makes the output stores 8 or 16 bytes wide.  Row
 // blocks past the group's last row are skipped, so a part-filled m-tile costs
 // in proportion to its rows.  A rows past the end are loaded clamped to the
 // last row (their results are never stored).
@@ -58,6 +61,13 @@ struct GemmArgs {
 };
 
 __device__ __forceinline__ int lds_pos(int row, int chunk) { return row * RB + ((chunk ^ ((row >> 2) & 3)) << 4); }
+
+// two floats -> two bf16 (round to nearest even), lo in the low half
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 // byte offset of E4M3 bytes k = 8*lk .. 8*lk+7 of weight-tile row `row`
 __device__ __forceinline__ int lds_pos8(int row, int lk) {
@@ -261,50 +271,45 @@ __device__ __forceinline__ void gemm_tile(IssueState& is, const GemmArgs& p, con
     for (int i = 0; i < NBW; ++i)
 #pragma unroll
       for (int j = 0; j < CB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[i], bfr[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], afr[i], acc[i][j], 0, 0, 0);
   }
 
-  // ---- epilogue: lane holds rows (2i+wm)*16 + lk*4 + v, column block j, column lr
+  // ---- epilogue.  The weight fragment is the MFMA's first operand, so for
+  // row block i and column block j lane (lr, lk) holds row (2i+wm)*16 + lr
+  // and the four consecutive weight rows lk*4 .. lk*4+3 of block j: one
+  // 8-byte store of bf16 h, or one 16-byte store of fp32 yp.
   const int rows = te.rows, n0 = te.n0;
-  const int64_t out_row0 = te.row_first;
 #pragma unroll
   for (int i = 0; i < NBW; ++i) {
-    const int rb_ = (2 * i + wm) * 16 + lk * 4;
+    const int r = (2 * i + wm) * 16 + lr;
+    if (r >= rows) continue;
+    const int64_t orow = (int64_t)(te.row_first + r) * p.N;
     if (GATE_UP) {
       // column blocks j < CB/2 hold W1 results, j + CB/2 the W3 results of the same h columns
-      uint16_t* C = (uint16_t*)p.C;
+      uint16_t* C = (uint16_t*)p.C + orow;
 #pragma unroll
       for (int j = 0; j < CB / 2; ++j) {
-        const int col = n0 + wn * (BNB / 4) + j * 16 + lr;
+        const int col = n0 + wn * (BNB / 4) + j * 16 + lk * 4;
         if (col >= p.N) continue;
+        f32x4_t g = acc[i][j], u = acc[i][j + CB / 2];
         if constexpr (W8) {
-          const float s1 = p.S0[(int64_t)te.g * p.N + col], s3 = p.S1[(int64_t)te.g * p.N + col];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int rr = rb_ + v;
-            if (rr < rows)
-              C[(out_row0 + rr) * p.N + col] = f32_to_bf16(silu(acc[i][j][v] * s1) * (acc[i][j + CB / 2][v] * s3));
-          }
-        } else {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int rr = rb_ + v;
-            if (rr < rows) C[(out_row0 + rr) * p.N + col] = f32_to_bf16(silu(acc[i][j][v]) * acc[i][j + CB / 2][v]);
-          }
+          g *= *(const f32x4_t*)(p.S0 + (int64_t)te.g * p.N + col);
+          u *= *(const f32x4_t*)(p.S1 + (int64_t)te.g * p.N + col);
         }
+        uint2 o;
+        o.x = pack_bf16x2(silu(g[0]) * u[0], silu(g[1]) * u[1]);
+        o.y = pack_bf16x2(silu(g[2]) * u[2], silu(g[3]) * u[3]);
+        *(uint2*)(C + col) = o;
       }
     } else {
-      float* C = (float*)p.C;
+      float* C = (float*)p.C + orow;
 #pragma unroll
       for (int j = 0; j < CB; ++j) {
-        const int col = n0 + wn * (BNB / 2) + j * 16 + lr;
+        const int col = n0 + wn * (BNB / 2) + j * 16 + lk * 4;
         if (col >= p.N) continue;
-        const float s2 = W8 ? p.S0[(int64_t)te.g * p.N + col] : 1.0f;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int rr = rb_ + v;
-          if (rr < rows) C[(out_row0 + rr) * p.N + col] = W8 ? acc[i][j][v] * s2 : acc[i][j][v];
-        }
+        f32x4_t o = acc[i][j];
+        if constexpr (W8) o *= *(const f32x4_t*)(p.S0 + (int64_t)te.g * p.N + col);
+        *(f32x4_t*)(C + col) = o;
       }
     }
   }
@@ -373,7 +378,7 @@ __global__ __launch_bounds__(256, NS* stage_bytes<W8>(BM, BNB) <= LDS_BYTES / 2 
 // (m-tile rows, weight-tile rows, LDS stages) compiled below, for bf16 and for
 // E4M3 weights.  The k-loop needs K >= 32 * (NS - 1); the launchers check it.
 #define MOE_GEMM_CONFIGS(X) X(128, 256, 3) X(128, 256, 6) X(64, 256, 4) \
-  X(128, 128, 4) X(128, 128, 3) X(64, 128, 8) X(64, 128, 6) X(64, 128, 3)
+  X(128, 128, 4) X(128, 128, 3) X(64, 128, 8) X(64, 128, 6) X(64, 128, 3) X(192, 128, 4) X(192, 128, 3) X(192, 256, 3)
 #define MOE_GEMM8_CONFIGS(X) X(128, 256, 5) X(128, 256, 3) X(128, 128, 6) X(128, 128, 3) X(64, 128, 10) \
   X(64, 128, 3)
 
@@ -427,7 +432,7 @@ hipError_t gemm_bf16_down(const FfnPlan& pl, const void* h, const int4* tab, con
   if (F / BKS < pl.ns_down - 1) return hipErrorInvalidValue;
   const unsigned g = (unsigned)launch_grid(pl, grid);
 #define MOE_LAUNCH(B, W, N)                                           \
-  if (pl.bm == B && pl.bnb_down == W && pl.ns_down == N) {            \
+  if (pl.bm_down == B && pl.bnb_down == W && pl.ns_down == N) {       \
     gemm_bf16_kernel<B, W, N, false, W8V><<<g, 256, 0, s>>>(a);       \
     return hipGetLastError();                                         \
   }

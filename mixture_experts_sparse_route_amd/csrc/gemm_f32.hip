@@ -101,8 +101,8 @@ static int env_int(const char* name, int def) {
   return e ? atoi(e) : def;
 }
 
-FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t n_groups, int64_t F, int64_t d) {
-  if (!bf16) return FfnPlan{FB, 0, 1, 0, 1, 0, FB, FB, false};
+FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_t n_groups, int64_t F, int64_t d) {
+  if (!bf16) return FfnPlan{FB, 0, 1, 0, 1, 0, FB, FB, false, FB};
   // 128-row m-tiles with a 3-stage ring of 256-row weight tiles (72 KB of
   // LDS): two workgroups per CU, so one tile's pipeline fill and epilogue
   // overlap the other's main loop.  A GEMM that would have fewer than two
@@ -113,9 +113,9 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t n_groups, int64_t
   // E4M3 weights halve the weight-tile bytes, so the same LDS holds deeper
   // rings: 5 stages of 128 x 256 tiles, 6 of 128 x 128, 10 of 64 x 128.
   const int ns_main = w8 ? 5 : 3, ns_narrow = w8 ? 6 : 4, ns_decode = w8 ? 10 : 6;
-  FfnPlan p{128, 256, ns_main, 256, ns_main, 0, 128, 256, w8};
+  FfnPlan p{128, 256, ns_main, 256, ns_main, 0, 128, 256, w8, 128};
   if (n_groups > 0 && max_rows / n_groups <= 64) {
-    p = FfnPlan{64, 128, ns_decode, 128, ns_decode, 0, 64, 128, w8};
+    p = FfnPlan{64, 128, ns_decode, 128, ns_decode, 0, 64, 128, w8, 64};
   } else {
     const int64_t mtiles = max_rows / 128 > n_groups ? max_rows / 128 : n_groups;  // rough m-tile count
     const int64_t want = 2 * (int64_t)device_cus();
@@ -128,21 +128,38 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t n_groups, int64_t
       p.ns_down = ns_narrow;
     }
   }
+  // GEMM2 m-tiles of 192 rows (bf16 weights): when no group can exceed 192
+  // rows but some may exceed 128 (an expert capacity in (128, 192]), every
+  // group is one m-tile, so each W2 tile is streamed once and the tile count
+  // is E * d / 128; when groups average 512 rows or more (MFMA-bound) the
+  // taller tile reuses each weight fragment over more rows.
+  if (!w8 && p.bm == 128) {
+    if (group_max > 128 && group_max <= 192) {
+      p.bm_down = 192;
+      p.bnb_down = 128;
+      p.ns_down = 4;
+    } else if (n_groups > 0 && max_rows / n_groups >= 512) {
+      p.bm_down = 192;
+      p.bnb_down = 128;
+      p.ns_down = 3;
+    }
+  }
   // A ring deeper than the reduction dimension's k-steps + 1 cannot be
   // filled: a reduction (d or F) of fewer than NS - 1 k-steps of 32 takes the
   // 3-stage variant of the same tile shape (every bf16 size is at least 2
   // k-steps).
   if (d / 32 < p.ns_up - 1) p.ns_up = 3;
   if (F / 32 < p.ns_down - 1) p.ns_down = 3;
-  // overrides for tuning: MOE_GEMM_BM, MOE_GEMM_{BNB,NS}_{UP,DOWN}, MOE_GEMM_WGS
+  // overrides for tuning: MOE_GEMM_BM, MOE_GEMM_BM_DOWN, MOE_GEMM_{BNB,NS}_{UP,DOWN}, MOE_GEMM_WGS
   const FfnPlan def = p;
   p.bm = env_int("MOE_GEMM_BM", p.bm);
+  p.bm_down = env_int("MOE_GEMM_BM_DOWN", p.bm_down == def.bm ? p.bm : p.bm_down);
   p.bnb_up = env_int("MOE_GEMM_BNB_UP", p.bnb_up);
   p.ns_up = env_int("MOE_GEMM_NS_UP", p.ns_up);
   p.bnb_down = env_int("MOE_GEMM_BNB_DOWN", p.bnb_down);
   p.ns_down = env_int("MOE_GEMM_NS_DOWN", p.ns_down);
   p.wg_per_cu = env_int("MOE_GEMM_WGS", p.wg_per_cu);
-  if (!gemm_bf16_has_config(w8, p.bm, p.bnb_up, p.ns_up) || !gemm_bf16_has_config(w8, p.bm, p.bnb_down, p.ns_down) ||
+  if (!gemm_bf16_has_config(w8, p.bm, p.bnb_up, p.ns_up) || !gemm_bf16_has_config(w8, p.bm_down, p.bnb_down, p.ns_down) ||
       d / 32 < p.ns_up - 1 || F / 32 < p.ns_down - 1)
     p = def;
   p.bn_out_up = p.bnb_up / 2;
@@ -161,15 +178,15 @@ int64_t ffn_table_entries(bool bf16, int64_t max_rows, int64_t n_groups, int64_t
   return ffn_max_mtiles(bm, max_rows, n_groups) * ((n_cols + bn - 1) / bn);
 }
 
-static int64_t grid_of(const FfnPlan& p, int64_t max_rows, int64_t n_groups, int64_t n_cols, int bn) {
-  const int64_t tiles = ffn_max_mtiles(p.bm, max_rows, n_groups) * ((n_cols + bn - 1) / bn);
+static int64_t grid_of(int bm, int64_t max_rows, int64_t n_groups, int64_t n_cols, int bn) {
+  const int64_t tiles = ffn_max_mtiles(bm, max_rows, n_groups) * ((n_cols + bn - 1) / bn);
   return (tiles + kXcds - 1) / kXcds * kXcds;
 }
 
 hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const void* A, const int4* tab, const int32_t* count,
                                int64_t n_groups, int64_t max_rows, const void* W1, const void* W3, const float* s1,
                                const float* s3, void* h, int64_t F, int64_t d, hipStream_t s) {
-  const int64_t grid = grid_of(p, max_rows, n_groups, F, p.bn_out_up);
+  const int64_t grid = grid_of(p.bm, max_rows, n_groups, F, p.bn_out_up);
   if (grid == 0) return hipSuccess;
   prof_begin(K_GEMM_GATE_UP, s);
   hipError_t err;
@@ -187,7 +204,7 @@ hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const void* A, const
 hipError_t launch_gemm_down(bool bf16, const FfnPlan& p, const void* h, const int4* tab, const int32_t* count,
                             int64_t n_groups, int64_t max_rows, const void* W2, const float* s2, float* yp, int64_t F,
                             int64_t d, hipStream_t s) {
-  const int64_t grid = grid_of(p, max_rows, n_groups, d, p.bn_out_down);
+  const int64_t grid = grid_of(p.bm_down, max_rows, n_groups, d, p.bn_out_down);
   if (grid == 0) return hipSuccess;
   prof_begin(K_GEMM_DOWN, s);
   hipError_t err;

@@ -108,10 +108,13 @@ struct FfnPlan {
   int bn_out_up;    // h columns per GEMM1 tile
   int bn_out_down;  // yp columns per GEMM2 tile
   bool w8;          // expert weights are E4M3 bytes with per-row scales
+  int bm_down;      // rows per m-tile of GEMM2 (bm: GEMM1)
 };
 // Compute units of the current device (queried once).
 int device_cus();
-FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t n_groups, int64_t F, int64_t d);
+// group_max: upper bound of any group's rows (the expert capacity when there
+// is one); max_rows: of all groups together.
+FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_t n_groups, int64_t F, int64_t d);
 // Whether the bf16-activation GEMM is compiled for (m-tile rows, weight-tile
 // rows, stages), with bf16 (w8 false) or E4M3 (w8 true) weights.
 bool gemm_bf16_has_config(bool w8, int bm, int bnb, int ns);
@@ -119,7 +122,8 @@ bool gemm_bf16_has_config(bool w8, int bm, int bnb, int ns);
 int64_t ffn_max_mtiles(int bm, int64_t max_rows, int64_t n_groups);
 // Entries the tile tables need for any plan of this dtype.
 int64_t ffn_table_entries(bool bf16, int64_t max_rows, int64_t n_groups, int64_t n_cols, bool gate_up);
-// Builds both GEMMs' tile tables (int4 {group, first row, rows, first column})
+// Builds both GEMMs' tile tables (int4 {group, first row, rows, first column};
+// m-tiles of p.bm rows for gate_up, p.bm_down for down)
 // and their entry counts counts[0] (gate_up) and counts[1] (down).
 hipError_t launch_ffn_tiles(const FfnPlan& p, const int32_t* offsets, int64_t n_groups, int64_t max_rows, int64_t F,
                             int64_t d, int4* tab_up, int4* tab_down, int32_t* counts, hipStream_t s);

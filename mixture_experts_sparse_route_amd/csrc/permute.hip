@@ -354,36 +354,46 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const V* __restrict__ x, 
 
 // ------------------------------------------------------------ FFN tiles
 // Tile list of both expert GEMMs (each workgroup scans the m-tile counts and
-// writes its share of the entries): for group g with rows(g)
-// rows, ceil(rows(g) / bm) m-tiles times the GEMM's n-tiles, in the order
+// writes its share of the entries): for group g with rows(g) rows,
+// ceil(rows(g) / bm) m-tiles (bm of that GEMM) times its n-tiles, in the order
 // (group, n-tile, m-tile) with the m-tile fastest, so the m-tiles of one
 // weight tile are neighbours.  Entry L = {group, first row, rows, first
 // column}; counts[0] / counts[1] = entries of the gate_up / down tables.
-__global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t* __restrict__ offsets, int G, int bm,
-                                                         int nt_up, int bn_up, int nt_down, int bn_down,
+__global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t* __restrict__ offsets, int G, int bm_up,
+                                                         int nt_up, int bn_up, int bm_down, int nt_down, int bn_down,
                                                          int4* __restrict__ tab_up, int4* __restrict__ tab_down,
                                                          int32_t* __restrict__ counts) {
-  __shared__ int mstart[1025];  // exclusive scan of m-tiles per group (G <= 1024)
-  __shared__ int buf[1024];
-  const int g = threadIdx.x;
-  int mt = 0;
+  __shared__ int mstart[2][1025];  // exclusive scans of m-tiles per group (G <= 1024), per GEMM
+  __shared__ int2 wsum[16];
+  const int g = threadIdx.x, lane = g & 63, wave = g >> 6;
+  const int rows = g < G ? offsets[g + 1] - offsets[g] : 0;
+  const int2 mt = rows > 0 ? make_int2((rows + bm_up - 1) / bm_up, (rows + bm_down - 1) / bm_down) : make_int2(0, 0);
+  // both inclusive scans at once: within the wave, then over the wave totals
+  int2 v = mt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int ux = __shfl_up(v.x, o), uy = __shfl_up(v.y, o);
+    if (lane >= o) {
+      v.x += ux;
+      v.y += uy;
+    }
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) {
+    v.x += wsum[w].x;
+    v.y += wsum[w].y;
+  }
   if (g < G) {
-    const int rows = offsets[g + 1] - offsets[g];
-    mt = rows > 0 ? (rows + bm - 1) / bm : 0;
+    mstart[0][g] = v.x - mt.x;
+    mstart[1][g] = v.y - mt.y;
   }
-  buf[g] = mt;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = g >= off ? buf[g - off] : 0;
-    __syncthreads();
-    buf[g] += v;
-    __syncthreads();
+  if (g == 1023) {  // threads past G add nothing: the last inclusive value is the total
+    mstart[0][G] = v.x;
+    mstart[1][G] = v.y;
   }
-  if (g < G) mstart[g] = buf[g] - mt;
-  if (g == 0) mstart[G] = buf[1023];
   __syncthreads();
-  const int total_m = mstart[G];
-  const int tot_up = total_m * nt_up, tot_down = total_m * nt_down;
+  const int tot_up = mstart[0][G] * nt_up, tot_down = mstart[1][G] * nt_down;
   if (g == 0 && blockIdx.x == 0) {
     counts[0] = tot_up;
     counts[1] = tot_down;
@@ -394,20 +404,21 @@ __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t* __restri
     const int nt = pass == 0 ? nt_up : nt_down;
     const int bn = pass == 0 ? bn_up : bn_down;
     const int tot = pass == 0 ? tot_up : tot_down;
+    const int bm = pass == 0 ? bm_up : bm_down;
+    const int* ms = mstart[pass];
     int4* tab = pass == 0 ? tab_up : tab_down;
     for (int L = blockIdx.x * 1024 + threadIdx.x; L < tot; L += gridDim.x * 1024) {
       // group of entry L: largest gg with mstart[gg] * nt <= L
       int lo = 0, hi = G;
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (mstart[mid] * nt <= L) lo = mid; else hi = mid;
+        if (ms[mid] * nt <= L) lo = mid; else hi = mid;
       }
-      const int mtiles = mstart[lo + 1] - mstart[lo];
-      const int r = L - mstart[lo] * nt;
+      const int mtiles = ms[lo + 1] - ms[lo];
+      const int r = L - ms[lo] * nt;
       const int n = r / mtiles, m = r % mtiles;
       const int row0 = offsets[lo] + m * bm;
-      const int rows = min(bm, offsets[lo + 1] - row0);
-      tab[L] = make_int4(lo, row0, rows, n * bn);
+      tab[L] = make_int4(lo, row0, min(bm, offsets[lo + 1] - row0), n * bn);
     }
   }
 }
@@ -480,11 +491,12 @@ hipError_t launch_ffn_tiles(const FfnPlan& p, const int32_t* offsets, int64_t n_
   const int nt_up = (int)((F + p.bn_out_up - 1) / p.bn_out_up);
   const int nt_down = (int)((d + p.bn_out_down - 1) / p.bn_out_down);
   // enough workgroups for the largest table this plan can produce, at most 32
-  const int64_t most = ffn_max_mtiles(p.bm, max_rows, n_groups) * (nt_up > nt_down ? nt_up : nt_down);
+  const int64_t most = std::max(ffn_max_mtiles(p.bm, max_rows, n_groups) * nt_up,
+                                ffn_max_mtiles(p.bm_down, max_rows, n_groups) * nt_down);
   const unsigned grid = (unsigned)std::min<int64_t>(32, std::max<int64_t>(1, (most + 1023) / 1024));
   prof_begin(K_FFN_TILES, s);
-  ffn_tiles_kernel<<<grid, 1024, 0, s>>>(offsets, (int)n_groups, p.bm, nt_up, p.bn_out_up, nt_down, p.bn_out_down,
-                                         tab_up, tab_down, counts);
+  ffn_tiles_kernel<<<grid, 1024, 0, s>>>(offsets, (int)n_groups, p.bm, nt_up, p.bn_out_up, p.bm_down, nt_down,
+                                         p.bn_out_down, tab_up, tab_down, counts);
   prof_end(K_FFN_TILES, s);
   return hipGetLastError();
 }

@@ -111,31 +111,31 @@ def test_entry_points_reject_null_and_small_workspace_without_launching(lib):
     c = spec().config()
     r = moe.MoeRouting()
     # routing arrays missing
-    assert lib.moe_route(ctypes.byref(c), 8, 8, None, None, ctypes.byref(r), 256, 1 << 30, None) \
+    assert lib.moe_route(ctypes.byref(c), 256, 256, None, None, ctypes.byref(r), 256, 1 << 30, None) \
         == moe.MOE_ERR_INVALID_ARG
     r = moe.MoeRouting(*([256] * 8))
     # workspace NULL, misaligned, too small
-    assert lib.moe_route(ctypes.byref(c), 8, 8, None, None, ctypes.byref(r), None, 0, None) == moe.MOE_ERR_WORKSPACE
-    assert lib.moe_route(ctypes.byref(c), 8, 8, None, None, ctypes.byref(r), 257, 1 << 30, None) \
+    assert lib.moe_route(ctypes.byref(c), 256, 256, None, None, ctypes.byref(r), None, 0, None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_route(ctypes.byref(c), 256, 256, None, None, ctypes.byref(r), 257, 1 << 30, None) \
         == moe.MOE_ERR_WORKSPACE
-    assert lib.moe_route(ctypes.byref(c), 8, 8, None, None, ctypes.byref(r), 256, 16, None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_route(ctypes.byref(c), 256, 256, None, None, ctypes.byref(r), 256, 16, None) == moe.MOE_ERR_WORKSPACE
     # x / Wg missing
     assert lib.moe_route(ctypes.byref(c), None, None, None, None, ctypes.byref(r), 256, 1 << 30, None) \
         == moe.MOE_ERR_INVALID_ARG
-    assert lib.moe_dispatch(ctypes.byref(c), None, ctypes.byref(r), 8, None) == moe.MOE_ERR_INVALID_ARG
-    assert lib.moe_expert_ffn(ctypes.byref(c), 8, 8, 0, 16, 8, 8, 8, None, 8, 256, 1 << 30, None) \
+    assert lib.moe_dispatch(ctypes.byref(c), None, ctypes.byref(r), 256, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_ffn(ctypes.byref(c), 256, 256, 0, 16, 256, 256, 256, None, 256, 256, 1 << 30, None) \
         == moe.MOE_ERR_INVALID_ARG  # n_groups = 0
-    assert lib.moe_expert_ffn(ctypes.byref(c), 8, 8, 8, 1 << 20, 8, 8, 8, None, 8, 256, 1 << 30, None) \
+    assert lib.moe_expert_ffn(ctypes.byref(c), 256, 256, 8, 1 << 20, 256, 256, 256, None, 256, 256, 1 << 30, None) \
         == moe.MOE_ERR_INVALID_ARG  # max_rows above the config's bound
     cr = spec(residual=True).config()
-    assert lib.moe_combine(ctypes.byref(cr), 8, ctypes.byref(r), None, None, 8, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(ctypes.byref(cr), 256, ctypes.byref(r), None, None, 256, None) == moe.MOE_ERR_INVALID_ARG
     # shared expert weights required
     cs = spec(n_shared=1, d_ff_shared=256).config()
-    assert lib.moe_forward(ctypes.byref(cs), 8, 8, None, None, 8, 8, 8, None, None, None, None, 8, None, 256, 1 << 30,
+    assert lib.moe_forward(ctypes.byref(cs), 256, 256, None, None, 256, 256, 256, None, None, None, None, 256, None, 256, 1 << 30,
                            None) == moe.MOE_ERR_INVALID_ARG
     # *_IN flags need the routing arrays
     ci = spec(logits_in=True).config()
-    assert lib.moe_forward(ctypes.byref(ci), 8, 8, None, None, 8, 8, 8, None, None, None, None, 8, None, 256, 1 << 30,
+    assert lib.moe_forward(ctypes.byref(ci), 256, 256, None, None, 256, 256, 256, None, None, None, None, 256, None, 256, 1 << 30,
                            None) == moe.MOE_ERR_INVALID_ARG
 
 
@@ -143,10 +143,10 @@ def test_zero_tokens_is_a_no_op(lib):
     c = spec(tokens=0).config()
     r = moe.MoeRouting(*([256] * 8))
     n = moe.workspace_size(spec(tokens=0))
-    assert lib.moe_route(ctypes.byref(c), 8, 8, None, None, ctypes.byref(r), 256, n, None) == moe.MOE_OK
-    assert lib.moe_dispatch(ctypes.byref(c), 8, ctypes.byref(r), 8, None) == moe.MOE_OK
-    assert lib.moe_combine(ctypes.byref(c), 8, ctypes.byref(r), None, None, 8, None) == moe.MOE_OK
-    assert lib.moe_forward(ctypes.byref(c), 8, 8, None, None, 8, 8, 8, None, None, None, None, 8, None, 256, n,
+    assert lib.moe_route(ctypes.byref(c), 256, 256, None, None, ctypes.byref(r), 256, n, None) == moe.MOE_OK
+    assert lib.moe_dispatch(ctypes.byref(c), 256, ctypes.byref(r), 256, None) == moe.MOE_OK
+    assert lib.moe_combine(ctypes.byref(c), 256, ctypes.byref(r), None, None, 256, None) == moe.MOE_OK
+    assert lib.moe_forward(ctypes.byref(c), 256, 256, None, None, 256, 256, 256, None, None, None, None, 256, None, 256, n,
                            None) == moe.MOE_OK
 
 
@@ -160,11 +160,11 @@ def test_statistics_flag_validation(lib):
     assert moe.workspace_size(spec(stats=True, tokens=4096)) > moe.workspace_size(spec(tokens=4096))
     c = spec(stats=True).config()
     r = moe.MoeRouting(*([256] * 8), None)   # stats pointer missing
-    assert lib.moe_route(ctypes.byref(c), 8, 8, None, None, ctypes.byref(r), 256, 1 << 30, None) \
+    assert lib.moe_route(ctypes.byref(c), 256, 256, None, None, ctypes.byref(r), 256, 1 << 30, None) \
         == moe.MOE_ERR_INVALID_ARG
     assert b"stats" in lib.moe_last_error()
     # moe_forward with statistics needs caller routing arrays
-    assert lib.moe_forward(ctypes.byref(c), 8, 8, None, None, 8, 8, 8, None, None, None, None, 8, None, 256, 1 << 30,
+    assert lib.moe_forward(ctypes.byref(c), 256, 256, None, None, 256, 256, 256, None, None, None, None, 256, None, 256, 1 << 30,
                            None) == moe.MOE_ERR_INVALID_ARG
 
 
@@ -219,15 +219,32 @@ def test_fp8_weight_validation(lib):
     c = spec(wdtype="fp8").config()
     assert c.w_dtype == moe.MOE_FP8_E4M3 and c.act_dtype == moe.MOE_BF16
     assert lib.moe_workspace_size(ctypes.byref(c), ctypes.byref(n)) == moe.MOE_OK
-    assert lib.moe_expert_ffn(ctypes.byref(c), 8, 8, 8, 16, 8, 8, 8, None, 8, 256, 1 << 30, None) \
+    assert lib.moe_expert_ffn(ctypes.byref(c), 256, 256, 8, 16, 256, 256, 256, None, 256, 256, 1 << 30, None) \
         == moe.MOE_ERR_INVALID_ARG
     assert b"scales" in lib.moe_last_error()
-    half = moe.MoeScales(8, 8, None, None, None, None)
-    assert lib.moe_expert_ffn(ctypes.byref(c), 8, 8, 8, 16, 8, 8, 8, ctypes.byref(half), 8, 256, 1 << 30, None) \
+    half = moe.MoeScales(256, 256, None, None, None, None)
+    assert lib.moe_expert_ffn(ctypes.byref(c), 256, 256, 8, 16, 256, 256, 256, ctypes.byref(half), 256, 256, 1 << 30, None) \
         == moe.MOE_ERR_INVALID_ARG
-    assert lib.moe_forward(ctypes.byref(c), 8, 8, None, None, 8, 8, 8, None, None, None, None, 8, None, 256, 1 << 30,
+    assert lib.moe_forward(ctypes.byref(c), 256, 256, None, None, 256, 256, 256, None, None, None, None, 256, None, 256, 1 << 30,
                            None) == moe.MOE_ERR_INVALID_ARG
     cs = spec(wdtype="fp8", n_shared=1, d_ff_shared=128).config()
-    full = moe.MoeScales(8, 8, 8, None, None, None)      # shared-expert scales missing
-    assert lib.moe_forward(ctypes.byref(cs), 8, 8, None, None, 8, 8, 8, 8, 8, 8, ctypes.byref(full), 8, None, 256,
+    full = moe.MoeScales(256, 256, 256, None, None, None)      # shared-expert scales missing
+    assert lib.moe_forward(ctypes.byref(cs), 256, 256, None, None, 256, 256, 256, 256, 256, 256, ctypes.byref(full), 256, None, 256,
                            1 << 30, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_misaligned_arrays_are_rejected_without_launching(lib):
+    """Activation, weight, scale and output arrays are accessed 16 bytes at a
+    time: a pointer off a 16-byte boundary is an argument error."""
+    c = spec().config()
+    r = moe.MoeRouting(*([256] * 8))
+    assert lib.moe_route(ctypes.byref(c), 256 + 8, 256, None, None, ctypes.byref(r), 256, 1 << 30, None) \
+        == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch(ctypes.byref(c), 256, ctypes.byref(r), 256 + 4, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_ffn(ctypes.byref(c), 256, 256, 8, 16, 256, 256, 256, None, 256 + 8, 256, 1 << 30, None) \
+        == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(ctypes.byref(c), 256, ctypes.byref(r), None, None, 256 + 2, None) \
+        == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward(ctypes.byref(c), 256, 256, None, None, 256, 256 + 8, 256, None, None, None, None, 256, None,
+                           256, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
+    assert b"16-byte aligned" in lib.moe_last_error()

@@ -129,6 +129,11 @@ SMALL = {
     # reductions of 2 k-steps (d = F = 64): the shallowest weight rings
     "short_reduction_decode": workload("mixtral_decode", T=6, d=64, F=64),
     "short_reduction_prefill": workload("mixtral_prefill", T=700, d=64, F=128),
+    # expert capacity floor(1.25 * 2048 / 16) = 160: the down GEMM takes
+    # 192-row m-tiles, each expert one part-filled tile
+    "switch_capacity_160": workload("switch_top1_capacity", T=2048, d=256, F=512, E=16),
+    # about 550 rows per expert: 192-row down m-tiles with a ragged last one
+    "mixtral_550_rows_per_expert": workload("mixtral_prefill", T=2200, d=256, F=384),
 }
 
 
