@@ -312,14 +312,16 @@ moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const 
 }
 
 // s1 / s3 / s2: row scales of E4M3 weights (s.w8), else unused.
-// group_max: bound of any group's rows.
-moe_status do_ffn(const Shape& s, const void* A, const int32_t* offsets, int64_t n_groups, int64_t max_rows,
-                  int64_t group_max,
+// group_max: bound of any group's rows; a_blocked: A is k-blocked with
+// max_rows rows (the fused path's own dispatch output), else row-major.
+moe_status do_ffn(const Shape& s, const void* A, bool a_blocked, const int32_t* offsets, int64_t n_groups,
+                  int64_t max_rows, int64_t group_max,
                   const void* W1, const void* W3, const void* W2, const float* s1, const float* s3, const float* s2,
                   void* h, float* yp, int4* tab_up, int4* tab_down, int32_t* counts, int64_t F, hipStream_t st) {
   const FfnPlan plan = ffn_plan(s.bf16, s.w8, max_rows, group_max, n_groups, F, s.d);
   MOE_HIP(launch_ffn_tiles(plan, offsets, n_groups, max_rows, F, s.d, tab_up, tab_down, counts, st));
-  MOE_HIP(launch_gemm_gate_up(s.bf16, plan, A, tab_up, counts, n_groups, max_rows, W1, W3, s1, s3, h, F, s.d, st));
+  MOE_HIP(launch_gemm_gate_up(s.bf16, plan, A, a_blocked, tab_up, counts, n_groups, max_rows, W1, W3, s1, s3, h, F, s.d,
+                              st));
   MOE_HIP(launch_gemm_down(s.bf16, plan, h, tab_down, counts + 1, n_groups, max_rows, W2, s2, yp, F, s.d, st));
   return MOE_OK;
 }
@@ -438,7 +440,7 @@ moe_status moe_dispatch(const moe_config* cfg, const void* x, const moe_routing*
   if (!x || !xp) return fail(MOE_ERR_INVALID_ARG, "x and xp are required");
   if ((st = check_aligned({x, xp})) != MOE_OK) return st;
   if (s.T == 0) return MOE_OK;
-  MOE_HIP(launch_dispatch(x, r->row_src, r->offsets + s.E, xp, s.max_rows, s.K, s.d * (int64_t)s.esz,
+  MOE_HIP(launch_dispatch(x, r->row_src, r->offsets + s.E, xp, s.max_rows, s.K, s.d * (int64_t)s.esz, false,
                           (hipStream_t)stream));
   return MOE_OK;
 }
@@ -465,7 +467,7 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* xp, const int32_t* 
   const moe_scales& sc = s.w8 ? *scales : none;
   // the plan assumes the routed bound of a group's rows (any rows stay correct)
   const int64_t group_max = s.cap >= 0 ? std::min(s.T, s.cap) : s.T;
-  return do_ffn(s, xp, offsets, n_groups, max_rows, group_max, W1, W3, W2, sc.w1, sc.w3, sc.w2, at<void>(ws, L.h), yp,
+  return do_ffn(s, xp, false, offsets, n_groups, max_rows, group_max, W1, W3, W2, sc.w1, sc.w3, sc.w2, at<void>(ws, L.h), yp,
                 at<int4>(ws, L.tab_up), at<int4>(ws, L.tab_down), at<int32_t>(ws, L.counts), s.F,
                 (hipStream_t)stream);
 }
@@ -531,10 +533,12 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, co
   void* xp = at<void>(ws, L.xp);
   float* yp = at<float>(ws, L.yp);
   if (s.max_rows > 0) {
-    MOE_HIP(launch_dispatch(x, rr.row_src, rr.offsets + s.E, xp, s.max_rows, s.K, s.d * (int64_t)s.esz, hs));
+    // the fused path's xp is internal: k-blocked for bf16 (each k-step of a
+    // GEMM1 tile then reads one contiguous run)
+    MOE_HIP(launch_dispatch(x, rr.row_src, rr.offsets + s.E, xp, s.max_rows, s.K, s.d * (int64_t)s.esz, s.bf16, hs));
     // an expert holds at most one row per token, and at most its capacity
     const int64_t group_max = s.cap >= 0 ? std::min(s.T, s.cap) : s.T;
-    if ((st = do_ffn(s, xp, rr.offsets, s.E, s.max_rows, group_max, W1, W3, W2, sc.w1, sc.w3, sc.w2, at<void>(ws, L.h), yp,
+    if ((st = do_ffn(s, xp, s.bf16, rr.offsets, s.E, s.max_rows, group_max, W1, W3, W2, sc.w1, sc.w3, sc.w2, at<void>(ws, L.h), yp,
                      at<int4>(ws, L.tab_up), at<int4>(ws, L.tab_down), at<int32_t>(ws, L.counts), s.F, hs)) != MOE_OK)
       return st;
   }
@@ -543,7 +547,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, co
     int32_t* range = at<int32_t>(ws, L.sh_range);
     MOE_HIP(launch_set_range(range, s.T, hs));
     sh_out = at<float>(ws, L.sh_out);
-    if ((st = do_ffn(s, x, range, 1, s.T, s.T, Ws1, Ws3, Ws2, sc.ws1, sc.ws3, sc.ws2, at<void>(ws, L.sh_h), sh_out,
+    if ((st = do_ffn(s, x, false, range, 1, s.T, s.T, Ws1, Ws3, Ws2, sc.ws1, sc.ws3, sc.ws2, at<void>(ws, L.sh_h), sh_out,
                      at<int4>(ws, L.sh_tab_up), at<int4>(ws, L.sh_tab_down), at<int32_t>(ws, L.sh_counts), s.Fs,
                      hs)) != MOE_OK)
       return st;

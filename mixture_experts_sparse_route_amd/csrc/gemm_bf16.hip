@@ -58,6 +58,11 @@ struct GemmArgs {
   const int4* tab;         // tile table {group, first row, rows, first column}
   const int32_t* count;    // entries in tab
   int N, Kdim;
+  // element (row, k) of A at row * a_rs + (k / 32) * a_ks + k % 32, and
+  // element (row, n) of C at row * c_rs + (n / 32) * c_bs + n % 32: row-major
+  // (a_rs = Kdim, a_ks = 32) or k-blocked [Kdim/32][rows][32] (a_rs = 32,
+  // a_ks = 32 * rows), where a k-step's A tile is one contiguous run
+  int64_t a_rs, a_ks, c_rs, c_bs;
 };
 
 __device__ __forceinline__ int lds_pos(int row, int chunk) { return row * RB + ((chunk ^ ((row >> 2) & 3)) << 4); }
@@ -171,7 +176,7 @@ __device__ __forceinline__ void issue_step(IssueState& is, const GemmArgs& p, co
 #pragma unroll
   for (int j = 0; j < AG; ++j) {
     const int row = min((wave + 4 * j) * 16 + r_l, rows - 1);
-    __builtin_amdgcn_global_load_lds(p.A + (int64_t)(row_first + row) * Kd + ko,
+    __builtin_amdgcn_global_load_lds(p.A + (int64_t)(row_first + row) * p.a_rs + (int64_t)kt * p.a_ks + c_l * 8,
                                      (lds_ptr_t)(st + (wave + 4 * j) * 16 * RB), 16, 0, 0);
   }
   if constexpr (!W8) {
@@ -283,7 +288,7 @@ __device__ __forceinline__ void gemm_tile(IssueState& is, const GemmArgs& p, con
   for (int i = 0; i < NBW; ++i) {
     const int r = (2 * i + wm) * 16 + lr;
     if (r >= rows) continue;
-    const int64_t orow = (int64_t)(te.row_first + r) * p.N;
+    const int64_t orow = (int64_t)(te.row_first + r) * p.c_rs;
     if (GATE_UP) {
       // column blocks j < CB/2 hold W1 results, j + CB/2 the W3 results of the same h columns
       uint16_t* C = (uint16_t*)p.C + orow;
@@ -299,7 +304,7 @@ __device__ __forceinline__ void gemm_tile(IssueState& is, const GemmArgs& p, con
         uint2 o;
         o.x = pack_bf16x2(silu(g[0]) * u[0], silu(g[1]) * u[1]);
         o.y = pack_bf16x2(silu(g[2]) * u[2], silu(g[3]) * u[3]);
-        *(uint2*)(C + col) = o;
+        *(uint2*)(C + (int64_t)(col >> 5) * p.c_bs + (col & 31)) = o;
       }
     } else {
       float* C = (float*)p.C + orow;
@@ -309,7 +314,7 @@ __device__ __forceinline__ void gemm_tile(IssueState& is, const GemmArgs& p, con
         if (col >= p.N) continue;
         f32x4_t o = acc[i][j];
         if constexpr (W8) o *= *(const f32x4_t*)(p.S0 + (int64_t)te.g * p.N + col);
-        *(f32x4_t*)(C + col) = o;
+        *(f32x4_t*)(C + (int64_t)(col >> 5) * p.c_bs + (col & 31)) = o;
       }
     }
   }
@@ -402,10 +407,19 @@ static int64_t launch_grid(const FfnPlan& pl, int64_t grid) {
   return pg < grid ? pg : grid;
 }
 
-hipError_t gemm_bf16_gate_up(const FfnPlan& pl, const void* A, const int4* tab, const int32_t* count, int64_t grid,
-                             const void* W1, const void* W3, const float* s1, const float* s3, void* h, int64_t F,
-                             int64_t d, hipStream_t s) {
+// a_blk / c_blk: rows of a k-blocked A / h ([cols/32][rows][32]), 0 = row-major.
+static void set_layout(GemmArgs& a, int64_t a_blk, int64_t c_blk) {
+  a.a_rs = a_blk ? BKS : a.Kdim;
+  a.a_ks = a_blk ? BKS * a_blk : BKS;
+  a.c_rs = c_blk ? 32 : a.N;
+  a.c_bs = c_blk ? 32 * c_blk : 32;
+}
+
+hipError_t gemm_bf16_gate_up(const FfnPlan& pl, const void* A, int64_t a_blk, const int4* tab, const int32_t* count,
+                             int64_t grid, const void* W1, const void* W3, const float* s1, const float* s3, void* h,
+                             int64_t h_blk, int64_t F, int64_t d, hipStream_t s) {
   GemmArgs a{(const uint16_t*)A, W1, W3, s1, s3, h, tab, count, (int)F, (int)d};
+  set_layout(a, a_blk, h_blk);
   if (d / BKS < pl.ns_up - 1) return hipErrorInvalidValue;
   const unsigned g = (unsigned)launch_grid(pl, grid);
 #define MOE_LAUNCH(B, W, N)                                           \
@@ -426,9 +440,10 @@ hipError_t gemm_bf16_gate_up(const FfnPlan& pl, const void* A, const int4* tab, 
   return hipErrorInvalidValue;
 }
 
-hipError_t gemm_bf16_down(const FfnPlan& pl, const void* h, const int4* tab, const int32_t* count, int64_t grid,
-                          const void* W2, const float* s2, float* yp, int64_t F, int64_t d, hipStream_t s) {
+hipError_t gemm_bf16_down(const FfnPlan& pl, const void* h, int64_t h_blk, const int4* tab, const int32_t* count,
+                          int64_t grid, const void* W2, const float* s2, float* yp, int64_t F, int64_t d, hipStream_t s) {
   GemmArgs a{(const uint16_t*)h, W2, nullptr, s2, nullptr, yp, tab, count, (int)d, (int)F};
+  set_layout(a, h_blk, 0);
   if (F / BKS < pl.ns_down - 1) return hipErrorInvalidValue;
   const unsigned g = (unsigned)launch_grid(pl, grid);
 #define MOE_LAUNCH(B, W, N)                                           \

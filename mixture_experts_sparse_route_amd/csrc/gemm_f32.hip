@@ -183,15 +183,15 @@ static int64_t grid_of(int bm, int64_t max_rows, int64_t n_groups, int64_t n_col
   return (tiles + kXcds - 1) / kXcds * kXcds;
 }
 
-hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const void* A, const int4* tab, const int32_t* count,
-                               int64_t n_groups, int64_t max_rows, const void* W1, const void* W3, const float* s1,
-                               const float* s3, void* h, int64_t F, int64_t d, hipStream_t s) {
+hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const void* A, bool a_blocked, const int4* tab,
+                               const int32_t* count, int64_t n_groups, int64_t max_rows, const void* W1, const void* W3,
+                               const float* s1, const float* s3, void* h, int64_t F, int64_t d, hipStream_t s) {
   const int64_t grid = grid_of(p.bm, max_rows, n_groups, F, p.bn_out_up);
   if (grid == 0) return hipSuccess;
   prof_begin(K_GEMM_GATE_UP, s);
   hipError_t err;
   if (bf16) {
-    err = gemm_bf16_gate_up(p, A, tab, count, grid, W1, W3, s1, s3, h, F, d, s);
+    err = gemm_bf16_gate_up(p, A, a_blocked ? max_rows : 0, tab, count, grid, W1, W3, s1, s3, h, max_rows, F, d, s);
   } else {
     F32Args a{(const float*)A, (const float*)W1, (const float*)W3, (float*)h, tab, count, (int)F, (int)d};
     gemm_f32_kernel<true><<<(unsigned)grid, 256, 0, s>>>(a);
@@ -209,7 +209,7 @@ hipError_t launch_gemm_down(bool bf16, const FfnPlan& p, const void* h, const in
   prof_begin(K_GEMM_DOWN, s);
   hipError_t err;
   if (bf16) {
-    err = gemm_bf16_down(p, h, tab, count, grid, W2, s2, yp, F, d, s);
+    err = gemm_bf16_down(p, h, max_rows, tab, count, grid, W2, s2, yp, F, d, s);
   } else {
     F32Args a{(const float*)h, (const float*)W2, nullptr, yp, tab, count, (int)d, (int)F};
     gemm_f32_kernel<false><<<(unsigned)grid, 256, 0, s>>>(a);

@@ -94,8 +94,10 @@ hipError_t launch_route_affinity(const uint64_t* seg, const int32_t* counts, con
 hipError_t launch_expert_choice(float* logits, const float* part, int S, const float* bias, int32_t* idx, float* w,
                                 uint64_t* seg, int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* row_src,
                                 uint8_t* dropped, int64_t T, int64_t E, int64_t cap, hipStream_t s);
+// blocked: xp is k-blocked bf16 [d/32][max_rows][32] (row_bytes = 2 d), else
+// row-major.
 hipError_t launch_dispatch(const void* x, const int32_t* row_src, const int32_t* R_ptr, void* xp, int64_t max_rows,
-                           int64_t K, int64_t row_bytes, hipStream_t s);
+                           int64_t K, int64_t row_bytes, bool blocked, hipStream_t s);
 
 // ---- grouped expert FFN (a6-a7) ----
 struct FfnPlan {
@@ -129,14 +131,18 @@ hipError_t launch_ffn_tiles(const FfnPlan& p, const int32_t* offsets, int64_t n_
                             int64_t d, int4* tab_up, int4* tab_down, int32_t* counts, hipStream_t s);
 // bf16 MFMA path (gemm_bf16.hip); called through the launchers below.
 // s1 / s3 / s2: [groups, N] row scales of E4M3 weights (p.w8), else unused.
-hipError_t gemm_bf16_gate_up(const FfnPlan& p, const void* A, const int4* tab, const int32_t* count, int64_t grid,
-                             const void* W1, const void* W3, const float* s1, const float* s3, void* h, int64_t F,
-                             int64_t d, hipStream_t s);
-hipError_t gemm_bf16_down(const FfnPlan& p, const void* h, const int4* tab, const int32_t* count, int64_t grid,
-                          const void* W2, const float* s2, float* yp, int64_t F, int64_t d, hipStream_t s);
-hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const void* A, const int4* tab, const int32_t* count,
-                               int64_t n_groups, int64_t max_rows, const void* W1, const void* W3, const float* s1,
-                               const float* s3, void* h, int64_t F, int64_t d, hipStream_t s);
+// a_blk / h_blk: the row count R of a k-blocked operand ([cols/32][R][32]:
+// the 32 columns of a k-step of R rows are one contiguous run), 0 = row-major.
+hipError_t gemm_bf16_gate_up(const FfnPlan& p, const void* A, int64_t a_blk, const int4* tab, const int32_t* count,
+                             int64_t grid, const void* W1, const void* W3, const float* s1, const float* s3, void* h,
+                             int64_t h_blk, int64_t F, int64_t d, hipStream_t s);
+hipError_t gemm_bf16_down(const FfnPlan& p, const void* h, int64_t h_blk, const int4* tab, const int32_t* count,
+                          int64_t grid, const void* W2, const float* s2, float* yp, int64_t F, int64_t d, hipStream_t s);
+// bf16: h is k-blocked with max_rows rows, and so is A when a_blocked (else
+// row-major); fp32: everything row-major.
+hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const void* A, bool a_blocked, const int4* tab,
+                               const int32_t* count, int64_t n_groups, int64_t max_rows, const void* W1, const void* W3,
+                               const float* s1, const float* s3, void* h, int64_t F, int64_t d, hipStream_t s);
 hipError_t launch_gemm_down(bool bf16, const FfnPlan& p, const void* h, const int4* tab, const int32_t* count,
                             int64_t n_groups, int64_t max_rows, const void* W2, const float* s2, float* yp, int64_t F,
                             int64_t d, hipStream_t s);

@@ -352,6 +352,34 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const V* __restrict__ x, 
   }
 }
 
+// The same into a k-blocked xp (bf16, [d/32][blk_rows][32]): workgroup b
+// moves rows 16b .. 16b+15; in each instruction a wave writes one 64-byte
+// k-block of those 16 rows, 1 KB contiguous (lane: row lane/4, 16-byte chunk
+// lane%4), reading 64 bytes of each row's token.
+__global__ __launch_bounds__(256) void dispatch_blocked_kernel(const uint4* __restrict__ x,
+                                                               const int32_t* __restrict__ row_src,
+                                                               const int32_t* __restrict__ R_ptr,
+                                                               uint4* __restrict__ xp, int K, int n_kb,
+                                                               int64_t blk_rows) {
+  const int R = *R_ptr;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = blockIdx.x * 16 + (lane >> 2), c = lane & 3;
+  if (blockIdx.x * 16 >= R) return;
+  if (r >= R) return;
+  const uint4* src = x + (int64_t)(row_src[r] / K) * n_kb * 4 + c;
+  uint4* dst = xp + (int64_t)r * 4 + c;
+  const int64_t kb_stride = blk_rows * 4;
+  int kb = wave;
+  for (; kb + 12 < n_kb; kb += 16) {  // four k-blocks in flight per lane
+    const uint4 v0 = src[kb * 4], v1 = src[(kb + 4) * 4], v2 = src[(kb + 8) * 4], v3 = src[(kb + 12) * 4];
+    dst[kb * kb_stride] = v0;
+    dst[(kb + 4) * kb_stride] = v1;
+    dst[(kb + 8) * kb_stride] = v2;
+    dst[(kb + 12) * kb_stride] = v3;
+  }
+  for (; kb < n_kb; kb += 4) dst[kb * kb_stride] = src[kb * 4];
+}
+
 // ------------------------------------------------------------ FFN tiles
 // Tile list of both expert GEMMs (each workgroup scans the m-tile counts and
 // writes its share of the entries): for group g with rows(g) rows,
@@ -467,7 +495,17 @@ hipError_t launch_route_affinity(const uint64_t* seg, const int32_t* counts, con
 }
 
 hipError_t launch_dispatch(const void* x, const int32_t* row_src, const int32_t* R_ptr, void* xp, int64_t max_rows,
-                           int64_t K, int64_t row_bytes, hipStream_t s) {
+                           int64_t K, int64_t row_bytes, bool blocked, hipStream_t s) {
+  if (blocked) {
+    if (row_bytes % 64) return hipErrorInvalidValue;
+    const unsigned nb = (unsigned)((max_rows + 15) / 16);
+    if (nb == 0) return hipSuccess;
+    prof_begin(K_DISPATCH, s);
+    dispatch_blocked_kernel<<<nb, 256, 0, s>>>((const uint4*)x, row_src, R_ptr, (uint4*)xp, (int)K,
+                                               (int)(row_bytes / 64), max_rows);
+    prof_end(K_DISPATCH, s);
+    return hipGetLastError();
+  }
   int rpb = row_bytes >= 4096 ? 1 : (int)(4096 / row_bytes);
   if (rpb > 64) rpb = 64;
   const unsigned nb = (unsigned)((max_rows + rpb - 1) / rpb);
