@@ -21,10 +21,15 @@
 // position c ^ ((r >> 2) & 3), which makes both the DMA writes (1 KB
 // contiguous per wave) and the MFMA fragment reads bank-conflict free.
 //
-// FP8 weights (W8): the weight tile is staged as OCP E4M3 bytes (32-byte
-// LDS rows per k-step, 16-byte chunk c of row r at c ^ ((r >> 2) & 1)); each
-// 8-byte fragment is converted exactly to bf16 when read (E4M3 values are
-// bf16 values), the MFMAs are the bf16 ones, and the per-row weight scale
+// FP8 weights (E4M3, two stage widths).  Stages of 32 k: the weight tile is
+// staged as E4M3 bytes in 32-byte LDS rows (16-byte chunk c of row r at
+// c ^ ((r >> 2) & 1)), one MFMA k-step per stage.  Stages of 64 k: the weight
+// tile is staged as OCP E4M3
+// bytes in the 64-byte rows of the bf16 layout (so the weight loads are the
+// bf16 ones), the A tile as 128-byte rows (chunk c of row r at
+// c ^ (r & 7)).  Each stage is two MFMA k-steps in k order, the same sums as
+// two bf16 stages.  E4M3 values are bf16 values, so the conversion at
+// fragment read is exact; the MFMAs are the bf16 ones, and the per-row weight scale
 // multiplies the fp32 sums in the epilogue (weight = code * scale[row], so
 // sum_k a_k w_k = scale * sum_k a_k code_k).
 //
@@ -74,11 +79,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// byte offset of E4M3 bytes k = 8*lk .. 8*lk+7 of weight-tile row `row`
-__device__ __forceinline__ int lds_pos8(int row, int lk) {
-  return row * 32 + ((((lk >> 1) ^ ((row >> 2) & 1))) << 4) + (lk & 1) * 8;
-}
-
 // 8 E4M3 bytes (k order, little-endian in lo, hi) -> 8 bf16, exactly
 __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
   typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
@@ -98,10 +98,28 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
   return r;
 }
 
-template <bool W8>
+// Weight kinds: bf16 in stages of 32 k (64-byte A and weight rows); E4M3 in
+// stages of 32 k (64-byte A rows, 32-byte weight rows) or of 64 k (128-byte A
+// rows, 64-byte weight rows).
+enum { WK_BF16 = 0, WK_E4M3_32 = 1, WK_E4M3_64 = 2 };
+template <int WK>
 constexpr int stage_bytes(int bm, int bnb) {
-  return bm * RB + bnb * (W8 ? 32 : RB);
+  return WK == WK_E4M3_64 ? bm * 2 * RB + bnb * RB : (WK == WK_E4M3_32 ? bm * RB + bnb * 32 : bm * RB + bnb * RB);
 }
+template <int WK>
+constexpr int k_per_stage() {
+  return WK == WK_E4M3_64 ? 2 * BKS : BKS;
+}
+
+// byte offset of E4M3 bytes k = 8*lk .. 8*lk+7 of a 32-byte weight row
+// (stages of 32 k): chunk c of row r at c ^ ((r >> 2) & 1)
+__device__ __forceinline__ int lds_pos8(int row, int lk) {
+  return row * 32 + ((((lk >> 1) ^ ((row >> 2) & 1))) << 4) + (lk & 1) * 8;
+}
+
+// byte offset of the 16-byte chunk c (bf16 k = 8c .. 8c+7) of a 128-byte A
+// row of a 64-k stage: chunk c sits at position c ^ (row & 7)
+__device__ __forceinline__ int lds_pos128(int row, int chunk) { return row * 2 * RB + ((chunk ^ (row & 7)) << 4); }
 
 // s_waitcnt vmcnt(N) with N an immediate.
 template <int N>
@@ -154,13 +172,13 @@ struct Seq {
 // Lane -> (row r_l of a 16-row group, chunk c_l), chunk swizzled as in
 // lds_pos; A rows past the tile's end are loaded clamped to its last row
 // (their results are never stored).
-template <int BM, int BNB, int NS, bool GATE_UP, bool W8>
+template <int BM, int BNB, int NS, bool GATE_UP, int WK>
 __device__ __forceinline__ void issue_step(IssueState& is, const GemmArgs& p, const Seq& q, char* lds, int s, int wave,
                                            int lane) {
   constexpr int AG = BM / 16 / 4;
   constexpr int BG = BNB / 16 / 4;
   constexpr int HALF = BNB / 4;  // gate_up: rows of one matrix in each quarter of the weight tile
-  constexpr int STAGE = stage_bytes<W8>(BM, BNB);
+  constexpr int STAGE = stage_bytes<WK>(BM, BNB);
   const int ti = s / q.nk, kt = s - ti * q.nk;
   if (ti != is.tile) {  // crossed into the next tile of the sequence
     is.tile = ti;
@@ -171,35 +189,28 @@ __device__ __forceinline__ void issue_step(IssueState& is, const GemmArgs& p, co
   const int r_l = lane >> 2;
   const int c_l = (lane & 3) ^ ((r_l >> 2) & 3);
   const int g = is.cur.g, row_first = is.cur.row_first, rows = is.cur.rows, n0 = is.cur.n0;
-  const int64_t ko = (int64_t)kt * BKS + c_l * 8;
   char* const st = lds + (s % NS) * STAGE;
+  if constexpr (WK != WK_E4M3_64) {
 #pragma unroll
-  for (int j = 0; j < AG; ++j) {
-    const int row = min((wave + 4 * j) * 16 + r_l, rows - 1);
-    __builtin_amdgcn_global_load_lds(p.A + (int64_t)(row_first + row) * p.a_rs + (int64_t)kt * p.a_ks + c_l * 8,
-                                     (lds_ptr_t)(st + (wave + 4 * j) * 16 * RB), 16, 0, 0);
-  }
-  if constexpr (!W8) {
-    const int64_t gbase = (int64_t)g * p.N * Kd + ko;
-#pragma unroll
-    for (int j = 0; j < BG; ++j) {
-      const int q16 = wave + 4 * j;
-      int col;
-      const uint16_t* base = (const uint16_t*)p.B0;
-      if (GATE_UP) {
-        // quarters of the weight tile: W1 half 0, W3 half 0, W1 half 1, W3 half 1
-        const int qb = (q16 * 16) / HALF;
-        if (qb & 1) base = (const uint16_t*)p.B1;
-        col = n0 + (qb >> 1) * HALF + (q16 * 16) % HALF + r_l;
-      } else {
-        col = n0 + q16 * 16 + r_l;
-      }
-      col = min(col, p.N - 1);
-      __builtin_amdgcn_global_load_lds(base + gbase + (int64_t)col * Kd,
-                                       (lds_ptr_t)(st + BM * RB + (wave + 4 * j) * 16 * RB), 16, 0, 0);
+    for (int j = 0; j < AG; ++j) {
+      const int row = min((wave + 4 * j) * 16 + r_l, rows - 1);
+      __builtin_amdgcn_global_load_lds(p.A + (int64_t)(row_first + row) * p.a_rs + (int64_t)kt * p.a_ks + c_l * 8,
+                                       (lds_ptr_t)(st + (wave + 4 * j) * 16 * RB), 16, 0, 0);
     }
   } else {
-    // E4M3 rows: 32 bytes per k-step, two lanes per row, 32 rows per load
+    // 64-k stage: 128-byte A rows, 8 rows per load; lane -> row lane/8 of the
+    // group, LDS slot lane%8, which holds chunk (lane%8) ^ (row%8)
+    const int r8 = lane >> 3, ch = (lane & 7) ^ r8;
+#pragma unroll
+    for (int j = 0; j < BM / 32; ++j) {
+      const int row = min((wave + 4 * j) * 8 + r8, rows - 1);
+      __builtin_amdgcn_global_load_lds(p.A + (int64_t)(row_first + row) * p.a_rs +
+                                           (int64_t)(2 * kt + (ch >> 2)) * p.a_ks + (ch & 3) * 8,
+                                       (lds_ptr_t)(st + (wave + 4 * j) * 8 * 2 * RB), 16, 0, 0);
+    }
+  }
+  if constexpr (WK == WK_E4M3_32) {
+    // E4M3 rows of 32 bytes per stage: two lanes per row, 32 rows per load
     constexpr int BG8 = BNB / 32 / 4;
     const int r8 = lane >> 1;
     const int c8 = (lane & 1) ^ ((r8 >> 2) & 1);  // the chunk that lands in this lane's LDS slot
@@ -208,8 +219,8 @@ __device__ __forceinline__ void issue_step(IssueState& is, const GemmArgs& p, co
     for (int j = 0; j < BG8; ++j) {
       const int q32 = wave + 4 * j;
       const int rt = q32 * 32 + r8;
-      int col;
       const uint8_t* base = (const uint8_t*)p.B0;
+      int col;
       if (GATE_UP) {
         const int qb = rt / HALF;
         if (qb & 1) base = (const uint8_t*)p.B1;
@@ -221,20 +232,44 @@ __device__ __forceinline__ void issue_step(IssueState& is, const GemmArgs& p, co
       __builtin_amdgcn_global_load_lds(base + gbase8 + (int64_t)col * Kd,
                                        (lds_ptr_t)(st + BM * RB + q32 * 32 * 32), 16, 0, 0);
     }
+  } else {
+    // weight rows of 64 bytes per stage (32 bf16 or 64 E4M3 k): four lanes per
+    // row, 16 rows per load
+    constexpr int ESZ = WK == WK_BF16 ? 2 : 1;  // bytes per weight element
+    const int64_t gbase = ((int64_t)g * p.N * Kd + (int64_t)kt * (64 / ESZ) + c_l * (16 / ESZ)) * ESZ;
+#pragma unroll
+    for (int j = 0; j < BG; ++j) {
+      const int q16 = wave + 4 * j;
+      const char* base = (const char*)p.B0;
+      int col;
+      if (GATE_UP) {
+        // quarters of the weight tile: W1 half 0, W3 half 0, W1 half 1, W3 half 1
+        const int qb = (q16 * 16) / HALF;
+        if (qb & 1) base = (const char*)p.B1;
+        col = n0 + (qb >> 1) * HALF + (q16 * 16) % HALF + r_l;
+      } else {
+        col = n0 + q16 * 16 + r_l;
+      }
+      col = min(col, p.N - 1);
+      __builtin_amdgcn_global_load_lds(
+          base + gbase + (int64_t)col * Kd * ESZ,
+          (lds_ptr_t)(st + BM * (WK == WK_E4M3_64 ? 2 * RB : RB) + (wave + 4 * j) * 16 * RB), 16, 0, 0);
+    }
   }
 }
 
 // k-loop and epilogue of one tile for a wave that owns NBW active 16-row
 // blocks.  `step` is the global step of the tile's first k-step.
-template <int BM, int BNB, int NS, bool GATE_UP, bool W8, int NBW>
+template <int BM, int BNB, int NS, bool GATE_UP, int WK, int NBW>
 __device__ __forceinline__ void gemm_tile(IssueState& is, const GemmArgs& p, const Seq& q, char* lds, const TileRef te,
                                           const int step0, const int wave, const int lane) {
-  constexpr int AG = BM / 16 / 4;
-  constexpr int BG = W8 ? BNB / 32 / 4 : BNB / 16 / 4;
+  constexpr bool W8 = WK != WK_BF16;
+  constexpr int AG = WK == WK_E4M3_64 ? BM / 32 : BM / 16 / 4;    // A loads per wave per stage
+  constexpr int BG = WK == WK_E4M3_32 ? BNB / 32 / 4 : BNB / 16 / 4;  // weight loads per wave per stage
   constexpr int CB = BNB / 32;  // 16-column MFMA blocks per N-wave
   constexpr int LPS = AG + BG;  // loads per wave per stage
   static_assert((NS - 2) * LPS <= 63, "vmcnt counts at most 63 outstanding loads");
-  constexpr int STAGE = stage_bytes<W8>(BM, BNB);
+  constexpr int STAGE = stage_bytes<WK>(BM, BNB);
   const int wm = wave & 1, wn = wave >> 1;
   const int lr = lane & 15, lk = lane >> 4;
 
@@ -252,31 +287,62 @@ __device__ __forceinline__ void gemm_tile(IssueState& is, const GemmArgs& p, con
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     const char* st = lds + (s % NS) * STAGE;
-    bf16x8_t bfr[CB];
-    if constexpr (W8) {
+    if constexpr (WK == WK_E4M3_64) {
+      // 64-k stage, two MFMA k-steps in k order (those of two bf16 stages):
+      // in step u lane (lr, lk) takes k = 32 u + 8 lk + 0..7, i.e. bytes
+      // 32 u + 8 lk .. +7 of its 64-byte E4M3 row and chunk 4 u + lk of its
+      // 128-byte A row
+      bf16x8_t b0[CB], b1[CB];
 #pragma unroll
       for (int j = 0; j < CB; ++j) {
-        const uint2 raw = *(const uint2*)(st + BM * RB + lds_pos8(wn * (BNB / 2) + j * 16 + lr, lk));
-        bfr[j] = fp8x8_to_bf16(raw.x, raw.y);
+        const int row = wn * (BNB / 2) + j * 16 + lr;
+        const uint2 r0 = *(const uint2*)(st + BM * 2 * RB + lds_pos(row, lk >> 1) + (lk & 1) * 8);
+        const uint2 r1 = *(const uint2*)(st + BM * 2 * RB + lds_pos(row, 2 + (lk >> 1)) + (lk & 1) * 8);
+        b0[j] = fp8x8_to_bf16(r0.x, r0.y);
+        b1[j] = fp8x8_to_bf16(r1.x, r1.y);
       }
+      bf16x8_t a0[NA], a1[NA];
+#pragma unroll
+      for (int i = 0; i < NBW; ++i) {
+        a0[i] = *(const bf16x8_t*)(st + lds_pos128((2 * i + wm) * 16 + lr, lk));
+        a1[i] = *(const bf16x8_t*)(st + lds_pos128((2 * i + wm) * 16 + lr, 4 + lk));
+      }
+      asm volatile("" ::: "memory");
+      if (s + NS - 1 < q.total_steps) issue_step<BM, BNB, NS, GATE_UP, WK>(is, p, q, lds, s + NS - 1, wave, lane);
+#pragma unroll
+      for (int i = 0; i < NBW; ++i)
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0[j], a0[i], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1[j], a1[i], acc[i][j], 0, 0, 0);
+        }
     } else {
+      bf16x8_t bfr[CB];
+      if constexpr (WK == WK_E4M3_32) {
 #pragma unroll
-      for (int j = 0; j < CB; ++j)
-        bfr[j] = *(const bf16x8_t*)(st + BM * RB + lds_pos(wn * (BNB / 2) + j * 16 + lr, lk));
+        for (int j = 0; j < CB; ++j) {
+          const uint2 raw = *(const uint2*)(st + BM * RB + lds_pos8(wn * (BNB / 2) + j * 16 + lr, lk));
+          bfr[j] = fp8x8_to_bf16(raw.x, raw.y);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < CB; ++j)
+          bfr[j] = *(const bf16x8_t*)(st + BM * RB + lds_pos(wn * (BNB / 2) + j * 16 + lr, lk));
+      }
+      bf16x8_t afr[NA];
+#pragma unroll
+      for (int i = 0; i < NBW; ++i) afr[i] = *(const bf16x8_t*)(st + lds_pos((2 * i + wm) * 16 + lr, lk));
+      asm volatile("" ::: "memory");
+      // refill the stage consumed in the previous step (every wave has passed
+      // this step's barrier, so nobody reads it any more); near the end of a
+      // tile this already fetches the next tile's first k-steps
+      if (s + NS - 1 < q.total_steps) issue_step<BM, BNB, NS, GATE_UP, WK>(is, p, q, lds, s + NS - 1, wave, lane);
+#pragma unroll
+      for (int i = 0; i < NBW; ++i)
+#pragma unroll
+        for (int j = 0; j < CB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], afr[i], acc[i][j], 0, 0, 0);
     }
-    bf16x8_t afr[NA];
-#pragma unroll
-    for (int i = 0; i < NBW; ++i) afr[i] = *(const bf16x8_t*)(st + lds_pos((2 * i + wm) * 16 + lr, lk));
-    asm volatile("" ::: "memory");
-    // refill the stage consumed in the previous step (every wave has passed
-    // this step's barrier, so nobody reads it any more); near the end of a
-    // tile this already fetches the next tile's first k-steps
-    if (s + NS - 1 < q.total_steps) issue_step<BM, BNB, NS, GATE_UP, W8>(is, p, q, lds, s + NS - 1, wave, lane);
-#pragma unroll
-    for (int i = 0; i < NBW; ++i)
-#pragma unroll
-      for (int j = 0; j < CB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], afr[i], acc[i][j], 0, 0, 0);
   }
 
   // ---- epilogue.  The weight fragment is the MFMA's first operand, so for
@@ -327,11 +393,11 @@ __device__ __forceinline__ void gemm_tile(IssueState& is, const GemmArgs& p, con
 // LDS ring, so the next tile's first stages load while the current tile
 // finishes and writes its output.  With one workgroup per tile this is the
 // plain one-tile-per-workgroup GEMM.
-template <int BM, int BNB, int NS, bool GATE_UP, bool W8>
-__global__ __launch_bounds__(256, NS* stage_bytes<W8>(BM, BNB) <= LDS_BYTES / 2 ? 2 : 1) void gemm_bf16_kernel(
+template <int BM, int BNB, int NS, bool GATE_UP, int WK>
+__global__ __launch_bounds__(256, NS* stage_bytes<WK>(BM, BNB) <= LDS_BYTES / 2 ? 2 : 1) void gemm_bf16_kernel(
     const GemmArgs p) {
   constexpr int MI = BM / 32;  // MFMA row blocks per M-wave
-  constexpr int STAGE = stage_bytes<W8>(BM, BNB);
+  constexpr int STAGE = stage_bytes<WK>(BM, BNB);
   static_assert(NS * STAGE <= LDS_BYTES, "LDS stages exceed 160 KB");
   __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
 
@@ -345,7 +411,7 @@ __global__ __launch_bounds__(256, NS* stage_bytes<W8>(BM, BNB) <= LDS_BYTES / 2 
   q.lbase = begin + j;
   q.lstride = g8;
   q.n_tiles = (end - begin - j + g8 - 1) / g8;
-  q.nk = p.Kdim / BKS;
+  q.nk = p.Kdim / k_per_stage<WK>();
   q.total_steps = q.n_tiles * q.nk;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 
@@ -355,7 +421,7 @@ __global__ __launch_bounds__(256, NS* stage_bytes<W8>(BM, BNB) <= LDS_BYTES / 2 
   is.next = q.n_tiles > 1 ? load_tile(p.tab, q.lbase + q.lstride) : is.cur;
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    if (s < q.total_steps) issue_step<BM, BNB, NS, GATE_UP, W8>(is, p, q, lds, s, wave, lane);
+    if (s < q.total_steps) issue_step<BM, BNB, NS, GATE_UP, WK>(is, p, q, lds, s, wave, lane);
 
   for (int t = 0; t < q.n_tiles; ++t) {
     // k-steps issued so far end inside tile t (nk >= NS - 1), so the issue
@@ -366,13 +432,13 @@ __global__ __launch_bounds__(256, NS* stage_bytes<W8>(BM, BNB) <= LDS_BYTES / 2 
     switch (nbw) {
 #define GG_CASE(n)                                                                        \
   case n:                                                                                 \
-    if constexpr (n <= MI) gemm_tile<BM, BNB, NS, GATE_UP, W8, n>(is, p, q, lds, te, t * q.nk, wave, lane); \
+    if constexpr (n <= MI) gemm_tile<BM, BNB, NS, GATE_UP, WK, n>(is, p, q, lds, te, t * q.nk, wave, lane); \
     break;
       GG_CASE(1) GG_CASE(2) GG_CASE(3) GG_CASE(4) GG_CASE(5) GG_CASE(6) GG_CASE(7) GG_CASE(8)
 #undef GG_CASE
       default:
         // no rows in this M half: still take part in the barriers and loads
-        gemm_tile<BM, BNB, NS, GATE_UP, W8, 0>(is, p, q, lds, te, t * q.nk, wave, lane);
+        gemm_tile<BM, BNB, NS, GATE_UP, WK, 0>(is, p, q, lds, te, t * q.nk, wave, lane);
         break;
     }
   }
@@ -380,17 +446,21 @@ __global__ __launch_bounds__(256, NS* stage_bytes<W8>(BM, BNB) <= LDS_BYTES / 2 
 
 }  // namespace
 
-// (m-tile rows, weight-tile rows, LDS stages) compiled below, for bf16 and for
-// E4M3 weights.  The k-loop needs K >= 32 * (NS - 1); the launchers check it.
+// (m-tile rows, weight-tile rows, LDS stages) compiled below: bf16 weights,
+// E4M3 weights in stages of 32 k, E4M3 weights in stages of 64 k.  The k-loop
+// needs K >= (k per stage) * (NS - 1); the launchers check it.
 #define MOE_GEMM_CONFIGS(X) X(128, 256, 3) X(128, 256, 6) X(64, 256, 4) \
   X(128, 128, 4) X(128, 128, 3) X(64, 128, 8) X(64, 128, 6) X(64, 128, 3) X(192, 128, 4) X(192, 128, 3) X(192, 256, 3)
 #define MOE_GEMM8_CONFIGS(X) X(128, 256, 5) X(128, 256, 3) X(128, 128, 6) X(128, 128, 3) X(64, 128, 10) \
   X(64, 128, 3)
+#define MOE_GEMM8K64_CONFIGS(X) X(64, 256, 3) X(128, 128, 3) X(128, 128, 2) X(64, 128, 5) X(64, 128, 4) X(64, 128, 2)
 
-bool gemm_bf16_has_config(bool w8, int bm, int bnb, int ns) {
+bool gemm_bf16_has_config(bool w8, bool k64, int bm, int bnb, int ns) {
 #define MOE_HAS(B, W, N) \
   if (bm == B && bnb == W && ns == N) return true;
-  if (w8) {
+  if (w8 && k64) {
+    MOE_GEMM8K64_CONFIGS(MOE_HAS)
+  } else if (w8) {
     MOE_GEMM8_CONFIGS(MOE_HAS)
   } else {
     MOE_GEMM_CONFIGS(MOE_HAS)
@@ -415,27 +485,34 @@ static void set_layout(GemmArgs& a, int64_t a_blk, int64_t c_blk) {
   a.c_bs = c_blk ? 32 * c_blk : 32;
 }
 
+static int64_t plan_k_per_stage(const FfnPlan& pl) { return pl.w8 && pl.k64 ? 2 * BKS : BKS; }
+
+// the configuration list of the plan's weight kind, each entry expanded by LAUNCH
+#define MOE_DISPATCH_KIND(LAUNCH)      \
+  if (pl.w8 && pl.k64) {               \
+    constexpr int WKV = WK_E4M3_64;    \
+    MOE_GEMM8K64_CONFIGS(LAUNCH)       \
+  } else if (pl.w8) {                  \
+    constexpr int WKV = WK_E4M3_32;    \
+    MOE_GEMM8_CONFIGS(LAUNCH)          \
+  } else {                             \
+    constexpr int WKV = WK_BF16;       \
+    MOE_GEMM_CONFIGS(LAUNCH)           \
+  }
+
 hipError_t gemm_bf16_gate_up(const FfnPlan& pl, const void* A, int64_t a_blk, const int4* tab, const int32_t* count,
                              int64_t grid, const void* W1, const void* W3, const float* s1, const float* s3, void* h,
                              int64_t h_blk, int64_t F, int64_t d, hipStream_t s) {
   GemmArgs a{(const uint16_t*)A, W1, W3, s1, s3, h, tab, count, (int)F, (int)d};
   set_layout(a, a_blk, h_blk);
-  if (d / BKS < pl.ns_up - 1) return hipErrorInvalidValue;
+  if (d / plan_k_per_stage(pl) < pl.ns_up - 1) return hipErrorInvalidValue;
   const unsigned g = (unsigned)launch_grid(pl, grid);
-#define MOE_LAUNCH(B, W, N)                                           \
-  if (pl.bm == B && pl.bnb_up == W && pl.ns_up == N) {                \
-    gemm_bf16_kernel<B, W, N, true, W8V><<<g, 256, 0, s>>>(a);        \
-    return hipGetLastError();                                         \
+#define MOE_LAUNCH(B, W, N)                                    \
+  if (pl.bm == B && pl.bnb_up == W && pl.ns_up == N) {         \
+    gemm_bf16_kernel<B, W, N, true, WKV><<<g, 256, 0, s>>>(a); \
+    return hipGetLastError();                                  \
   }
-  if (pl.w8) {
-#define W8V true
-    MOE_GEMM8_CONFIGS(MOE_LAUNCH)
-#undef W8V
-  } else {
-#define W8V false
-    MOE_GEMM_CONFIGS(MOE_LAUNCH)
-#undef W8V
-  }
+  MOE_DISPATCH_KIND(MOE_LAUNCH)
 #undef MOE_LAUNCH
   return hipErrorInvalidValue;
 }
@@ -444,24 +521,18 @@ hipError_t gemm_bf16_down(const FfnPlan& pl, const void* h, int64_t h_blk, const
                           int64_t grid, const void* W2, const float* s2, float* yp, int64_t F, int64_t d, hipStream_t s) {
   GemmArgs a{(const uint16_t*)h, W2, nullptr, s2, nullptr, yp, tab, count, (int)d, (int)F};
   set_layout(a, h_blk, 0);
-  if (F / BKS < pl.ns_down - 1) return hipErrorInvalidValue;
+  if (F / plan_k_per_stage(pl) < pl.ns_down - 1) return hipErrorInvalidValue;
   const unsigned g = (unsigned)launch_grid(pl, grid);
-#define MOE_LAUNCH(B, W, N)                                           \
-  if (pl.bm_down == B && pl.bnb_down == W && pl.ns_down == N) {       \
-    gemm_bf16_kernel<B, W, N, false, W8V><<<g, 256, 0, s>>>(a);       \
-    return hipGetLastError();                                         \
+#define MOE_LAUNCH(B, W, N)                                     \
+  if (pl.bm_down == B && pl.bnb_down == W && pl.ns_down == N) { \
+    gemm_bf16_kernel<B, W, N, false, WKV><<<g, 256, 0, s>>>(a); \
+    return hipGetLastError();                                   \
   }
-  if (pl.w8) {
-#define W8V true
-    MOE_GEMM8_CONFIGS(MOE_LAUNCH)
-#undef W8V
-  } else {
-#define W8V false
-    MOE_GEMM_CONFIGS(MOE_LAUNCH)
-#undef W8V
-  }
+  MOE_DISPATCH_KIND(MOE_LAUNCH)
 #undef MOE_LAUNCH
   return hipErrorInvalidValue;
 }
+
+#undef MOE_DISPATCH_KIND
 
 }  // namespace moe

@@ -102,7 +102,7 @@ static int env_int(const char* name, int def) {
 }
 
 FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_t n_groups, int64_t F, int64_t d) {
-  if (!bf16) return FfnPlan{FB, 0, 1, 0, 1, 0, FB, FB, false, FB};
+  if (!bf16) return FfnPlan{FB, 0, 1, 0, 1, 0, FB, FB, false, FB, false};
   // 128-row m-tiles with a 3-stage ring of 256-row weight tiles (72 KB of
   // LDS): two workgroups per CU, so one tile's pipeline fill and epilogue
   // overlap the other's main loop.  A GEMM that would have fewer than two
@@ -110,12 +110,23 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_
   // Few rows per expert (decode-sized batches): 64-row m-tiles and a 6-stage
   // ring of 128-row weight tiles, the deepest weight stream that still fits
   // two workgroups per CU.
-  // E4M3 weights halve the weight-tile bytes, so the same LDS holds deeper
-  // rings: 5 stages of 128 x 256 tiles, 6 of 128 x 128, 10 of 64 x 128.
-  const int ns_main = w8 ? 5 : 3, ns_narrow = w8 ? 6 : 4, ns_decode = w8 ? 10 : 6;
-  FfnPlan p{128, 256, ns_main, 256, ns_main, 0, 128, 256, w8, 128};
-  if (n_groups > 0 && max_rows / n_groups <= 64) {
-    p = FfnPlan{64, 128, ns_decode, 128, ns_decode, 0, 64, 128, w8, 64};
+  // E4M3 weights: where groups are small (at most 96 rows on average, or an
+  // expert capacity of at most 192 rows), the
+  // weight stream dominates and stages of 64 k move the same weight bytes per
+  // stage as bf16 in half the stages: 64 x 256 tiles, 3 stages (72 KB), or
+  // 64 x 128 tiles, 5 stages, for decode-sized groups.  Larger groups keep
+  // stages of 32 k (half the LDS per stage, so deeper rings: 5 stages of
+  // 128 x 256 tiles, 6 of 128 x 128).
+  const bool small = n_groups > 0 && max_rows / n_groups <= 64;
+  bool k64 = w8 && n_groups > 0 && (max_rows / n_groups <= 96 || group_max <= 192);
+  if (w8) k64 = env_int("MOE_GEMM_K64", k64 ? 1 : 0) != 0;  // tuning override
+  const int ns_main = w8 ? 5 : 3, ns_narrow = w8 ? 6 : 4, ns_decode = k64 ? 5 : (w8 ? 10 : 6);
+  const int64_t ks = k64 ? 64 : 32;  // k per stage
+  FfnPlan p{128, 256, ns_main, 256, ns_main, 0, 128, 256, w8, 128, k64};
+  if (small) {
+    p = FfnPlan{64, 128, ns_decode, 128, ns_decode, 0, 64, 128, w8, 64, k64};
+  } else if (k64) {
+    p = FfnPlan{64, 256, 3, 256, 3, 0, 128, 256, w8, 64, k64};
   } else {
     const int64_t mtiles = max_rows / 128 > n_groups ? max_rows / 128 : n_groups;  // rough m-tile count
     const int64_t want = 2 * (int64_t)device_cus();
@@ -144,13 +155,22 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_
       p.ns_down = 3;
     }
   }
-  // A ring deeper than the reduction dimension's k-steps + 1 cannot be
-  // filled: a reduction (d or F) of fewer than NS - 1 k-steps of 32 takes the
-  // 3-stage variant of the same tile shape (every bf16 size is at least 2
-  // k-steps).
-  if (d / 32 < p.ns_up - 1) p.ns_up = 3;
-  if (F / 32 < p.ns_down - 1) p.ns_down = 3;
+  // A ring deeper than the reduction dimension's stages + 1 cannot be
+  // filled: a reduction (d or F) of fewer than NS - 1 stages takes the
+  // shallowest variant of the same tile shape (3 stages where a stage is 32 k:
+  // every size is at least 2 such stages; with stages of 64 k, at least 1
+  // stage: 2 stages of 128-row weight tiles).
+  const int ns_min = k64 ? 2 : 3;
+  if (d / ks < p.ns_up - 1) {
+    p.ns_up = ns_min;
+    if (k64) p.bnb_up = 128;
+  }
+  if (F / ks < p.ns_down - 1) {
+    p.ns_down = ns_min;
+    if (k64) p.bnb_down = 128;
+  }
   // overrides for tuning: MOE_GEMM_BM, MOE_GEMM_BM_DOWN, MOE_GEMM_{BNB,NS}_{UP,DOWN}, MOE_GEMM_WGS
+  // (and MOE_GEMM_K64 above)
   const FfnPlan def = p;
   p.bm = env_int("MOE_GEMM_BM", p.bm);
   p.bm_down = env_int("MOE_GEMM_BM_DOWN", p.bm_down == def.bm ? p.bm : p.bm_down);
@@ -159,8 +179,9 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_
   p.bnb_down = env_int("MOE_GEMM_BNB_DOWN", p.bnb_down);
   p.ns_down = env_int("MOE_GEMM_NS_DOWN", p.ns_down);
   p.wg_per_cu = env_int("MOE_GEMM_WGS", p.wg_per_cu);
-  if (!gemm_bf16_has_config(w8, p.bm, p.bnb_up, p.ns_up) || !gemm_bf16_has_config(w8, p.bm_down, p.bnb_down, p.ns_down) ||
-      d / 32 < p.ns_up - 1 || F / 32 < p.ns_down - 1)
+  if (!gemm_bf16_has_config(w8, k64, p.bm, p.bnb_up, p.ns_up) ||
+      !gemm_bf16_has_config(w8, k64, p.bm_down, p.bnb_down, p.ns_down) ||
+      d / ks < p.ns_up - 1 || F / ks < p.ns_down - 1)
     p = def;
   p.bn_out_up = p.bnb_up / 2;
   p.bn_out_down = p.bnb_down;

@@ -111,6 +111,7 @@ struct FfnPlan {
   int bn_out_down;  // yp columns per GEMM2 tile
   bool w8;          // expert weights are E4M3 bytes with per-row scales
   int bm_down;      // rows per m-tile of GEMM2 (bm: GEMM1)
+  bool k64;         // E4M3 weights: stages of 64 k (else 32)
 };
 // Compute units of the current device (queried once).
 int device_cus();
@@ -118,8 +119,9 @@ int device_cus();
 // is one); max_rows: of all groups together.
 FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_t n_groups, int64_t F, int64_t d);
 // Whether the bf16-activation GEMM is compiled for (m-tile rows, weight-tile
-// rows, stages), with bf16 (w8 false) or E4M3 (w8 true) weights.
-bool gemm_bf16_has_config(bool w8, int bm, int bnb, int ns);
+// rows, stages), with bf16 (w8 false) or E4M3 (w8 true) weights in stages of
+// 32 k or (k64) 64 k.
+bool gemm_bf16_has_config(bool w8, bool k64, int bm, int bnb, int ns);
 // Worst-case m-tiles for `bm`-row tiles.
 int64_t ffn_max_mtiles(int bm, int64_t max_rows, int64_t n_groups);
 // Entries the tile tables need for any plan of this dtype.
