@@ -101,14 +101,17 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
 // Weight kinds: bf16 in stages of 32 k (64-byte A and weight rows); E4M3 in
 // stages of 32 k (64-byte A rows, 32-byte weight rows) or of 64 k (128-byte A
 // rows, 64-byte weight rows).
-enum { WK_BF16 = 0, WK_E4M3_32 = 1, WK_E4M3_64 = 2 };
+// bf16 weights may also take stages of 64 k (128-byte A and weight rows).
+enum { WK_BF16 = 0, WK_E4M3_32 = 1, WK_E4M3_64 = 2, WK_BF16_64 = 3 };
 template <int WK>
 constexpr int stage_bytes(int bm, int bnb) {
-  return WK == WK_E4M3_64 ? bm * 2 * RB + bnb * RB : (WK == WK_E4M3_32 ? bm * RB + bnb * 32 : bm * RB + bnb * RB);
+  return WK == WK_BF16_64 ? (bm + bnb) * 2 * RB
+                          : (WK == WK_E4M3_64 ? bm * 2 * RB + bnb * RB
+                                              : (WK == WK_E4M3_32 ? bm * RB + bnb * 32 : bm * RB + bnb * RB));
 }
 template <int WK>
 constexpr int k_per_stage() {
-  return WK == WK_E4M3_64 ? 2 * BKS : BKS;
+  return WK == WK_E4M3_64 || WK == WK_BF16_64 ? 2 * BKS : BKS;
 }
 
 // byte offset of E4M3 bytes k = 8*lk .. 8*lk+7 of a 32-byte weight row
@@ -190,7 +193,7 @@ __device__ __forceinline__ void issue_step(IssueState& is, const GemmArgs& p, co
   const int c_l = (lane & 3) ^ ((r_l >> 2) & 3);
   const int g = is.cur.g, row_first = is.cur.row_first, rows = is.cur.rows, n0 = is.cur.n0;
   char* const st = lds + (s % NS) * STAGE;
-  if constexpr (WK != WK_E4M3_64) {
+  if constexpr (k_per_stage<WK>() == BKS) {
 #pragma unroll
     for (int j = 0; j < AG; ++j) {
       const int row = min((wave + 4 * j) * 16 + r_l, rows - 1);
@@ -209,7 +212,28 @@ __device__ __forceinline__ void issue_step(IssueState& is, const GemmArgs& p, co
                                        (lds_ptr_t)(st + (wave + 4 * j) * 8 * 2 * RB), 16, 0, 0);
     }
   }
-  if constexpr (WK == WK_E4M3_32) {
+  if constexpr (WK == WK_BF16_64) {
+    // bf16 rows of 128 bytes per stage, laid out as the A rows: eight lanes
+    // per row, 8 rows per load
+    const int r8 = lane >> 3, ch = (lane & 7) ^ r8;
+    const int64_t gbase = (int64_t)g * p.N * Kd + (int64_t)kt * 2 * BKS + ch * 8;
+#pragma unroll
+    for (int j = 0; j < BNB / 32; ++j) {
+      const int rt = (wave + 4 * j) * 8 + r8;
+      const uint16_t* base = (const uint16_t*)p.B0;
+      int col;
+      if (GATE_UP) {
+        const int qb = rt / HALF;
+        if (qb & 1) base = (const uint16_t*)p.B1;
+        col = n0 + (qb >> 1) * HALF + rt % HALF;
+      } else {
+        col = n0 + rt;
+      }
+      col = min(col, p.N - 1);
+      __builtin_amdgcn_global_load_lds(base + gbase + (int64_t)col * Kd,
+                                       (lds_ptr_t)(st + BM * 2 * RB + (wave + 4 * j) * 8 * 2 * RB), 16, 0, 0);
+    }
+  } else if constexpr (WK == WK_E4M3_32) {
     // E4M3 rows of 32 bytes per stage: two lanes per row, 32 rows per load
     constexpr int BG8 = BNB / 32 / 4;
     const int r8 = lane >> 1;
@@ -263,9 +287,10 @@ __device__ __forceinline__ void issue_step(IssueState& is, const GemmArgs& p, co
 template <int BM, int BNB, int NS, bool GATE_UP, int WK, int NBW>
 __device__ __forceinline__ void gemm_tile(IssueState& is, const GemmArgs& p, const Seq& q, char* lds, const TileRef te,
                                           const int step0, const int wave, const int lane) {
-  constexpr bool W8 = WK != WK_BF16;
-  constexpr int AG = WK == WK_E4M3_64 ? BM / 32 : BM / 16 / 4;    // A loads per wave per stage
-  constexpr int BG = WK == WK_E4M3_32 ? BNB / 32 / 4 : BNB / 16 / 4;  // weight loads per wave per stage
+  constexpr bool W8 = WK == WK_E4M3_32 || WK == WK_E4M3_64;  // E4M3 codes: row scales in the epilogue
+  constexpr bool K64 = k_per_stage<WK>() == 2 * BKS;
+  constexpr int AG = K64 ? BM / 32 : BM / 16 / 4;  // A loads per wave per stage
+  constexpr int BG = WK == WK_BF16_64 ? BNB / 32 : (WK == WK_E4M3_32 ? BNB / 32 / 4 : BNB / 16 / 4);  // weight loads
   constexpr int CB = BNB / 32;  // 16-column MFMA blocks per N-wave
   constexpr int LPS = AG + BG;  // loads per wave per stage
   static_assert((NS - 2) * LPS <= 63, "vmcnt counts at most 63 outstanding loads");
@@ -287,7 +312,7 @@ __device__ __forceinline__ void gemm_tile(IssueState& is, const GemmArgs& p, con
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     const char* st = lds + (s % NS) * STAGE;
-    if constexpr (WK == WK_E4M3_64) {
+    if constexpr (K64) {
       // 64-k stage, two MFMA k-steps in k order (those of two bf16 stages):
       // in step u lane (lr, lk) takes k = 32 u + 8 lk + 0..7, i.e. bytes
       // 32 u + 8 lk .. +7 of its 64-byte E4M3 row and chunk 4 u + lk of its
@@ -296,10 +321,15 @@ __device__ __forceinline__ void gemm_tile(IssueState& is, const GemmArgs& p, con
 #pragma unroll
       for (int j = 0; j < CB; ++j) {
         const int row = wn * (BNB / 2) + j * 16 + lr;
-        const uint2 r0 = *(const uint2*)(st + BM * 2 * RB + lds_pos(row, lk >> 1) + (lk & 1) * 8);
-        const uint2 r1 = *(const uint2*)(st + BM * 2 * RB + lds_pos(row, 2 + (lk >> 1)) + (lk & 1) * 8);
-        b0[j] = fp8x8_to_bf16(r0.x, r0.y);
-        b1[j] = fp8x8_to_bf16(r1.x, r1.y);
+        if constexpr (WK == WK_BF16_64) {
+          b0[j] = *(const bf16x8_t*)(st + BM * 2 * RB + lds_pos128(row, lk));
+          b1[j] = *(const bf16x8_t*)(st + BM * 2 * RB + lds_pos128(row, 4 + lk));
+        } else {
+          const uint2 r0 = *(const uint2*)(st + BM * 2 * RB + lds_pos(row, lk >> 1) + (lk & 1) * 8);
+          const uint2 r1 = *(const uint2*)(st + BM * 2 * RB + lds_pos(row, 2 + (lk >> 1)) + (lk & 1) * 8);
+          b0[j] = fp8x8_to_bf16(r0.x, r0.y);
+          b1[j] = fp8x8_to_bf16(r1.x, r1.y);
+        }
       }
       bf16x8_t a0[NA], a1[NA];
 #pragma unroll
@@ -454,12 +484,16 @@ __global__ __launch_bounds__(256, NS* stage_bytes<WK>(BM, BNB) <= LDS_BYTES / 2 
 #define MOE_GEMM8_CONFIGS(X) X(128, 256, 5) X(128, 256, 3) X(128, 128, 6) X(128, 128, 3) X(64, 128, 10) \
   X(64, 128, 3)
 #define MOE_GEMM8K64_CONFIGS(X) X(64, 256, 3) X(128, 128, 3) X(128, 128, 2) X(64, 128, 5) X(64, 128, 4) X(64, 128, 2)
+#define MOE_GEMM16K64_CONFIGS(X) X(192, 128, 3) X(192, 128, 2) X(128, 128, 3) X(128, 128, 2) X(64, 128, 3) \
+  X(64, 128, 2) X(64, 256, 3) X(128, 256, 2)
 
 bool gemm_bf16_has_config(bool w8, bool k64, int bm, int bnb, int ns) {
 #define MOE_HAS(B, W, N) \
   if (bm == B && bnb == W && ns == N) return true;
   if (w8 && k64) {
     MOE_GEMM8K64_CONFIGS(MOE_HAS)
+  } else if (k64) {
+    MOE_GEMM16K64_CONFIGS(MOE_HAS)
   } else if (w8) {
     MOE_GEMM8_CONFIGS(MOE_HAS)
   } else {
@@ -485,13 +519,14 @@ static void set_layout(GemmArgs& a, int64_t a_blk, int64_t c_blk) {
   a.c_bs = c_blk ? 32 * c_blk : 32;
 }
 
-static int64_t plan_k_per_stage(const FfnPlan& pl) { return pl.w8 && pl.k64 ? 2 * BKS : BKS; }
-
-// the configuration list of the plan's weight kind, each entry expanded by LAUNCH
-#define MOE_DISPATCH_KIND(LAUNCH)      \
-  if (pl.w8 && pl.k64) {               \
+// the configuration list of the weight kind (pl.w8, k64), each entry expanded by LAUNCH
+#define MOE_DISPATCH_KIND(k64, LAUNCH) \
+  if (pl.w8 && k64) {                  \
     constexpr int WKV = WK_E4M3_64;    \
     MOE_GEMM8K64_CONFIGS(LAUNCH)       \
+  } else if (k64) {                    \
+    constexpr int WKV = WK_BF16_64;    \
+    MOE_GEMM16K64_CONFIGS(LAUNCH)      \
   } else if (pl.w8) {                  \
     constexpr int WKV = WK_E4M3_32;    \
     MOE_GEMM8_CONFIGS(LAUNCH)          \
@@ -505,14 +540,14 @@ hipError_t gemm_bf16_gate_up(const FfnPlan& pl, const void* A, int64_t a_blk, co
                              int64_t h_blk, int64_t F, int64_t d, hipStream_t s) {
   GemmArgs a{(const uint16_t*)A, W1, W3, s1, s3, h, tab, count, (int)F, (int)d};
   set_layout(a, a_blk, h_blk);
-  if (d / plan_k_per_stage(pl) < pl.ns_up - 1) return hipErrorInvalidValue;
+  if (d / (pl.k64_up ? 2 * BKS : BKS) < pl.ns_up - 1) return hipErrorInvalidValue;
   const unsigned g = (unsigned)launch_grid(pl, grid);
 #define MOE_LAUNCH(B, W, N)                                    \
   if (pl.bm == B && pl.bnb_up == W && pl.ns_up == N) {         \
     gemm_bf16_kernel<B, W, N, true, WKV><<<g, 256, 0, s>>>(a); \
     return hipGetLastError();                                  \
   }
-  MOE_DISPATCH_KIND(MOE_LAUNCH)
+  MOE_DISPATCH_KIND(pl.k64_up, MOE_LAUNCH)
 #undef MOE_LAUNCH
   return hipErrorInvalidValue;
 }
@@ -521,14 +556,14 @@ hipError_t gemm_bf16_down(const FfnPlan& pl, const void* h, int64_t h_blk, const
                           int64_t grid, const void* W2, const float* s2, float* yp, int64_t F, int64_t d, hipStream_t s) {
   GemmArgs a{(const uint16_t*)h, W2, nullptr, s2, nullptr, yp, tab, count, (int)d, (int)F};
   set_layout(a, h_blk, 0);
-  if (F / plan_k_per_stage(pl) < pl.ns_down - 1) return hipErrorInvalidValue;
+  if (F / (pl.k64_down ? 2 * BKS : BKS) < pl.ns_down - 1) return hipErrorInvalidValue;
   const unsigned g = (unsigned)launch_grid(pl, grid);
 #define MOE_LAUNCH(B, W, N)                                     \
   if (pl.bm_down == B && pl.bnb_down == W && pl.ns_down == N) { \
     gemm_bf16_kernel<B, W, N, false, WKV><<<g, 256, 0, s>>>(a); \
     return hipGetLastError();                                   \
   }
-  MOE_DISPATCH_KIND(MOE_LAUNCH)
+  MOE_DISPATCH_KIND(pl.k64_down, MOE_LAUNCH)
 #undef MOE_LAUNCH
   return hipErrorInvalidValue;
 }

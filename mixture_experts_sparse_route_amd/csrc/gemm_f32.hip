@@ -102,32 +102,33 @@ static int env_int(const char* name, int def) {
 }
 
 FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_t n_groups, int64_t F, int64_t d) {
-  if (!bf16) return FfnPlan{FB, 0, 1, 0, 1, 0, FB, FB, false, FB, false};
-  // 128-row m-tiles with a 3-stage ring of 256-row weight tiles (72 KB of
-  // LDS): two workgroups per CU, so one tile's pipeline fill and epilogue
-  // overlap the other's main loop.  A GEMM that would have fewer than two
-  // such tiles per CU uses 128-row weight tiles (4 stages, 64 KB) instead.
-  // Few rows per expert (decode-sized batches): 64-row m-tiles and a 6-stage
-  // ring of 128-row weight tiles, the deepest weight stream that still fits
-  // two workgroups per CU.
+  if (!bf16) return FfnPlan{FB, 0, 1, 0, 1, 0, FB, FB, false, FB, false, false};
+  // Fields: bm, bnb_up, ns_up, bnb_down, ns_down, wg_per_cu, bn_out_up,
+  // bn_out_down, w8, bm_down, k64_up, k64_down.
+  //
+  // bf16 weights: 128-row m-tiles with a 3-stage ring of 256-row weight tiles
+  // in stages of 32 k (72 KB of LDS): two workgroups per CU, so one tile's
+  // pipeline fill and epilogue overlap the other's main loop.  A GEMM that
+  // would have fewer than two such tiles per CU uses 128-row weight tiles (4
+  // stages, 64 KB).  Decode-sized groups (at most 64 rows on average): 64-row
+  // m-tiles, 128-row weight tiles, 3 stages of 64 k (72 KB).
   // E4M3 weights: where groups are small (at most 96 rows on average, or an
-  // expert capacity of at most 192 rows), the
-  // weight stream dominates and stages of 64 k move the same weight bytes per
-  // stage as bf16 in half the stages: 64 x 256 tiles, 3 stages (72 KB), or
-  // 64 x 128 tiles, 5 stages, for decode-sized groups.  Larger groups keep
-  // stages of 32 k (half the LDS per stage, so deeper rings: 5 stages of
-  // 128 x 256 tiles, 6 of 128 x 128).
-  const bool small = n_groups > 0 && max_rows / n_groups <= 64;
-  bool k64 = w8 && n_groups > 0 && (max_rows / n_groups <= 96 || group_max <= 192);
-  if (w8) k64 = env_int("MOE_GEMM_K64", k64 ? 1 : 0) != 0;  // tuning override
-  const int ns_main = w8 ? 5 : 3, ns_narrow = w8 ? 6 : 4, ns_decode = k64 ? 5 : (w8 ? 10 : 6);
-  const int64_t ks = k64 ? 64 : 32;  // k per stage
-  FfnPlan p{128, 256, ns_main, 256, ns_main, 0, 128, 256, w8, 128, k64};
+  // expert capacity of at most 192 rows) the weight stream dominates, and
+  // stages of 64 k move the same weight bytes per stage as bf16 in half the
+  // stages: 64 x 256 tiles, 3 stages (72 KB), or 64 x 128 tiles, 5 stages,
+  // for decode-sized groups.  Larger groups keep stages of 32 k (half the LDS
+  // per stage, so deeper rings: 5 stages of 128 x 256 tiles, 6 of 128 x 128).
+  const int64_t avg = n_groups > 0 ? max_rows / n_groups : 0;
+  const bool small = n_groups > 0 && avg <= 64;
+  const bool w8k64 = w8 && n_groups > 0 && (avg <= 96 || group_max <= 192);
+  FfnPlan p{128, 256, w8 ? 5 : 3, 256, w8 ? 5 : 3, 0, 128, 256, w8, 128, false, false};
   if (small) {
-    p = FfnPlan{64, 128, ns_decode, 128, ns_decode, 0, 64, 128, w8, 64, k64};
-  } else if (k64) {
-    p = FfnPlan{64, 256, 3, 256, 3, 0, 128, 256, w8, 64, k64};
+    p = w8 ? FfnPlan{64, 128, 5, 128, 5, 0, 64, 128, true, 64, true, true}
+           : FfnPlan{64, 128, 3, 128, 3, 0, 64, 128, false, 64, true, true};
+  } else if (w8k64) {
+    p = FfnPlan{64, 256, 3, 256, 3, 0, 128, 256, true, 64, true, true};
   } else {
+    const int ns_narrow = w8 ? 6 : 4;
     const int64_t mtiles = max_rows / 128 > n_groups ? max_rows / 128 : n_groups;  // rough m-tile count
     const int64_t want = 2 * (int64_t)device_cus();
     if (mtiles * ((F + 127) / 128) < want) {
@@ -139,39 +140,51 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_
       p.ns_down = ns_narrow;
     }
   }
-  // GEMM2 m-tiles of 192 rows (bf16 weights): when no group can exceed 192
-  // rows but some may exceed 128 (an expert capacity in (128, 192]), every
-  // group is one m-tile, so each W2 tile is streamed once and the tile count
-  // is E * d / 128; when groups average 512 rows or more (MFMA-bound) the
-  // taller tile reuses each weight fragment over more rows.
+  // bf16 GEMM2 m-tiles of 192 rows: when no group can exceed 192 rows but
+  // some may exceed 128 (an expert capacity in (128, 192]), every group is
+  // one m-tile, so each W2 tile is streamed once and the tile count is
+  // E * d / 128 (stages of 32 k, 4 deep); when groups average 512 rows or
+  // more (MFMA-bound), stages of 64 k, 2 deep (80 KB): two MFMA k-steps per
+  // barrier and each weight fragment reused over 192 rows.
   if (!w8 && p.bm == 128) {
     if (group_max > 128 && group_max <= 192) {
       p.bm_down = 192;
       p.bnb_down = 128;
       p.ns_down = 4;
-    } else if (n_groups > 0 && max_rows / n_groups >= 512) {
+    } else if (avg >= 512) {
       p.bm_down = 192;
       p.bnb_down = 128;
-      p.ns_down = 3;
+      p.ns_down = 2;
+      p.k64_down = true;
     }
   }
   // A ring deeper than the reduction dimension's stages + 1 cannot be
-  // filled: a reduction (d or F) of fewer than NS - 1 stages takes the
-  // shallowest variant of the same tile shape (3 stages where a stage is 32 k:
-  // every size is at least 2 such stages; with stages of 64 k, at least 1
-  // stage: 2 stages of 128-row weight tiles).
-  const int ns_min = k64 ? 2 : 3;
-  if (d / ks < p.ns_up - 1) {
-    p.ns_up = ns_min;
-    if (k64) p.bnb_up = 128;
-  }
-  if (F / ks < p.ns_down - 1) {
-    p.ns_down = ns_min;
-    if (k64) p.bnb_down = 128;
-  }
-  // overrides for tuning: MOE_GEMM_BM, MOE_GEMM_BM_DOWN, MOE_GEMM_{BNB,NS}_{UP,DOWN}, MOE_GEMM_WGS
-  // (and MOE_GEMM_K64 above)
+  // filled.  bf16: such a GEMM takes stages of 32 k, 3 deep (every bf16 size
+  // is at least 2 of them); E4M3 in stages of 64 k: 2 stages of 128-row
+  // weight tiles (every size is at least 1 stage); E4M3 in stages of 32 k:
+  // 3 stages.
+  auto shallow = [&](int64_t K, bool& k64, int& ns, int& bnb) {
+    if (K / (k64 ? 64 : 32) >= ns - 1) return;
+    if (!w8 && k64) {
+      k64 = false;
+      ns = 3;
+    } else if (k64) {
+      ns = 2;
+      bnb = 128;
+    } else {
+      ns = 3;
+    }
+  };
+  shallow(d, p.k64_up, p.ns_up, p.bnb_up);
+  shallow(F, p.k64_down, p.ns_down, p.bnb_down);
+  // overrides for tuning: MOE_GEMM_K64 (both GEMMs in stages of 64 k, 0 or
+  // 1), MOE_GEMM_K64_DOWN, MOE_GEMM_BM, MOE_GEMM_BM_DOWN,
+  // MOE_GEMM_{BNB,NS}_{UP,DOWN}, MOE_GEMM_WGS; a set that names no compiled
+  // configuration leaves the plan as it was
   const FfnPlan def = p;
+  const int k64_env = env_int("MOE_GEMM_K64", -1);
+  if (k64_env >= 0) p.k64_up = p.k64_down = k64_env != 0;
+  p.k64_down = env_int("MOE_GEMM_K64_DOWN", p.k64_down ? 1 : 0) != 0;
   p.bm = env_int("MOE_GEMM_BM", p.bm);
   p.bm_down = env_int("MOE_GEMM_BM_DOWN", p.bm_down == def.bm ? p.bm : p.bm_down);
   p.bnb_up = env_int("MOE_GEMM_BNB_UP", p.bnb_up);
@@ -179,9 +192,9 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_
   p.bnb_down = env_int("MOE_GEMM_BNB_DOWN", p.bnb_down);
   p.ns_down = env_int("MOE_GEMM_NS_DOWN", p.ns_down);
   p.wg_per_cu = env_int("MOE_GEMM_WGS", p.wg_per_cu);
-  if (!gemm_bf16_has_config(w8, k64, p.bm, p.bnb_up, p.ns_up) ||
-      !gemm_bf16_has_config(w8, k64, p.bm_down, p.bnb_down, p.ns_down) ||
-      d / ks < p.ns_up - 1 || F / ks < p.ns_down - 1)
+  if (!gemm_bf16_has_config(w8, p.k64_up, p.bm, p.bnb_up, p.ns_up) ||
+      !gemm_bf16_has_config(w8, p.k64_down, p.bm_down, p.bnb_down, p.ns_down) ||
+      d / (p.k64_up ? 64 : 32) < p.ns_up - 1 || F / (p.k64_down ? 64 : 32) < p.ns_down - 1)
     p = def;
   p.bn_out_up = p.bnb_up / 2;
   p.bn_out_down = p.bnb_down;

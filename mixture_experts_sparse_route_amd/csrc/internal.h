@@ -111,7 +111,8 @@ struct FfnPlan {
   int bn_out_down;  // yp columns per GEMM2 tile
   bool w8;          // expert weights are E4M3 bytes with per-row scales
   int bm_down;      // rows per m-tile of GEMM2 (bm: GEMM1)
-  bool k64;         // E4M3 weights: stages of 64 k (else 32)
+  bool k64_up;      // GEMM1 in stages of 64 k (else 32)
+  bool k64_down;    // GEMM2 in stages of 64 k (else 32)
 };
 // Compute units of the current device (queried once).
 int device_cus();
