@@ -317,12 +317,13 @@ moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const 
 moe_status do_ffn(const Shape& s, const void* A, bool a_blocked, const int32_t* offsets, int64_t n_groups,
                   int64_t max_rows, int64_t group_max,
                   const void* W1, const void* W3, const void* W2, const float* s1, const float* s3, const float* s2,
-                  void* h, float* yp, int4* tab_up, int4* tab_down, int32_t* counts, int64_t F, hipStream_t st) {
+                  void* h, float* yp, int4* tab_up, int4* tab_down, int32_t* counts, int64_t F, hipStream_t st,
+                  const CombineFuse* fuse = nullptr) {
   const FfnPlan plan = ffn_plan(s.bf16, s.w8, max_rows, group_max, n_groups, F, s.d);
   MOE_HIP(launch_ffn_tiles(plan, offsets, n_groups, max_rows, F, s.d, tab_up, tab_down, counts, st));
   MOE_HIP(launch_gemm_gate_up(s.bf16, plan, A, a_blocked, tab_up, counts, n_groups, max_rows, W1, W3, s1, s3, h, F, s.d,
                               st));
-  MOE_HIP(launch_gemm_down(s.bf16, plan, h, tab_down, counts + 1, n_groups, max_rows, W2, s2, yp, F, s.d, st));
+  MOE_HIP(launch_gemm_down(s.bf16, plan, h, tab_down, counts + 1, n_groups, max_rows, W2, s2, yp, fuse, F, s.d, st));
   return MOE_OK;
 }
 
@@ -484,7 +485,7 @@ moe_status moe_combine(const moe_config* cfg, const float* yp, const moe_routing
   if ((st = check_aligned({yp, y, shared_out, residual ? x_residual : nullptr})) != MOE_OK) return st;
   if (s.T == 0) return MOE_OK;
   MOE_HIP(launch_combine(s.bf16, s.out_bf16, yp, r->topk_w, r->dest, shared_out, residual ? x_residual : nullptr, y, s.T, s.d,
-                         s.K, (hipStream_t)stream));
+                         s.K, false, (hipStream_t)stream));
   return MOE_OK;
 }
 
@@ -532,6 +533,11 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, co
   if ((st = do_route(cfg, s, L, x, Wg, logit_bias, sel_bias, rr, ws, hs)) != MOE_OK) return st;
   void* xp = at<void>(ws, L.xp);
   float* yp = at<float>(ws, L.yp);
+  const bool residual = cfg->flags & MOE_F_RESIDUAL;
+  // one assignment per token and no shared expert (bf16): GEMM2 writes the
+  // kept tokens' outputs itself and the combine only the dropped tokens
+  const bool fused = s.bf16 && s.K == 1 && s.S == 0 && !s.ec;
+  const CombineFuse fuse{rr.row_src, rr.topk_w, residual ? x : nullptr, y, s.bf16, s.out_bf16};
   if (s.max_rows > 0) {
     // the fused path's xp is internal: k-blocked for bf16 (each k-step of a
     // GEMM1 tile then reads one contiguous run)
@@ -539,7 +545,8 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, co
     // an expert holds at most one row per token, and at most its capacity
     const int64_t group_max = s.cap >= 0 ? std::min(s.T, s.cap) : s.T;
     if ((st = do_ffn(s, xp, s.bf16, rr.offsets, s.E, s.max_rows, group_max, W1, W3, W2, sc.w1, sc.w3, sc.w2, at<void>(ws, L.h), yp,
-                     at<int4>(ws, L.tab_up), at<int4>(ws, L.tab_down), at<int32_t>(ws, L.counts), s.F, hs)) != MOE_OK)
+                     at<int4>(ws, L.tab_up), at<int4>(ws, L.tab_down), at<int32_t>(ws, L.counts), s.F, hs,
+                     fused ? &fuse : nullptr)) != MOE_OK)
       return st;
   }
   float* sh_out = nullptr;
@@ -552,8 +559,8 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, co
                      hs)) != MOE_OK)
       return st;
   }
-  MOE_HIP(launch_combine(s.bf16, s.out_bf16, yp, rr.topk_w, rr.dest, sh_out, (cfg->flags & MOE_F_RESIDUAL) ? x : nullptr, y, s.T,
-                         s.d, s.K, hs));
+  MOE_HIP(launch_combine(s.bf16, s.out_bf16, yp, rr.topk_w, rr.dest, sh_out, residual ? x : nullptr, y, s.T, s.d, s.K,
+                         fused, hs));
   return MOE_OK;
 }
 

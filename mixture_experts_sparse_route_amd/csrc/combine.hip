@@ -15,7 +15,7 @@ template <typename XT, typename OUT, int VEC>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ yp, const float* __restrict__ w,
                                                       const int32_t* __restrict__ dest,
                                                       const float* __restrict__ shared, const XT* __restrict__ xres,
-                                                      OUT* __restrict__ y, int T, int d, int K) {
+                                                      OUT* __restrict__ y, int T, int d, int K, int only_dropped) {
   const int vecs = d / VEC;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   // vecs % 64 == 0: all 64 lanes of a wave serve one token (the grid is a
@@ -50,6 +50,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       const int r = k < K ? dest[(int64_t)t * K + k] : -1;
       const float wk = k < K ? w[(int64_t)t * K + k] : 0.f;
       uint64_t kept = __ballot(r >= 0);
+      if (only_dropped && kept) return;  // written by the fused GEMM2 epilogue (K <= 64 here)
       while (kept) {
         const int j = __ffsll((unsigned long long)kept) - 1;
         kept &= kept - 1;
@@ -60,6 +61,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     for (int k = 0; k < K; ++k) {
       const int r = dest[(int64_t)t * K + k];
       if (r < 0) continue;
+      if (only_dropped) return;  // written by the fused GEMM2 epilogue
       add_row(r, w[(int64_t)t * K + k]);
     }
   }
@@ -85,7 +87,8 @@ __global__ void set_range_kernel(int32_t* dst, int n) {
 
 hipError_t launch_combine(bool x_bf16, bool y_bf16, const float* yp, const float* w, const int32_t* dest,
                           const float* shared, const void* xres, void* y, int64_t T, int64_t d, int64_t K,
-                          hipStream_t s) {
+                          bool only_dropped, hipStream_t s) {
+  if (only_dropped && (K > 64 || shared)) return hipErrorInvalidValue;
   const int VEC = (d % 4 == 0) ? 4 : 1;
   const int64_t threads = T * (d / VEC);
   const unsigned nb = (unsigned)((threads + 255) / 256);
@@ -93,7 +96,7 @@ hipError_t launch_combine(bool x_bf16, bool y_bf16, const float* yp, const float
   prof_begin(K_COMBINE, s);
 #define MOE_COMBINE(XT, YT, V)                                                                                 \
   combine_kernel<XT, YT, V><<<nb, 256, 0, s>>>(yp, w, dest, shared, (const XT*)xres, (YT*)y, (int)T, (int)d, \
-                                               (int)K)
+                                               (int)K, only_dropped ? 1 : 0)
   if (x_bf16 && y_bf16) {
     if (VEC == 4) MOE_COMBINE(uint16_t, uint16_t, 4); else MOE_COMBINE(uint16_t, uint16_t, 1);
   } else if (x_bf16) {

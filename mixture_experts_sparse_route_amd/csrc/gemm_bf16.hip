@@ -68,6 +68,7 @@ struct GemmArgs {
   // (a_rs = Kdim, a_ks = 32) or k-blocked [Kdim/32][rows][32] (a_rs = 32,
   // a_ks = 32 * rows), where a k-step's A tile is one contiguous run
   int64_t a_rs, a_ks, c_rs, c_bs;
+  CombineFuse fuse;        // down: y written through it when fuse.y is set
 };
 
 __device__ __forceinline__ int lds_pos(int row, int chunk) { return row * RB + ((chunk ^ ((row >> 2) & 3)) << 4); }
@@ -402,6 +403,39 @@ __device__ __forceinline__ void gemm_tile(IssueState& is, const GemmArgs& p, con
         o.y = pack_bf16x2(silu(g[2]) * u[2], silu(g[3]) * u[3]);
         *(uint2*)(C + (int64_t)(col >> 5) * p.c_bs + (col & 31)) = o;
       }
+    } else if (p.fuse.y) {
+      // combine fused (one assignment per token): y[t] = w[t] * yp_row (+ x[t]),
+      // the combine's arithmetic (fmaf(w, yp, 0), then + x, one rounding)
+      const int64_t t = p.fuse.row_src[te.row_first + r];
+      const float wt = p.fuse.w[t];
+#pragma unroll
+      for (int j = 0; j < CB; ++j) {
+        const int col = n0 + wn * (BNB / 2) + j * 16 + lk * 4;
+        if (col >= p.N) continue;
+        f32x4_t o = acc[i][j];
+        if constexpr (W8) o *= *(const f32x4_t*)(p.S0 + (int64_t)te.g * p.N + col);
+        const int64_t yo = t * p.N + col;
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = fmaf(wt, o[u], 0.f);
+        if (p.fuse.xres) {
+          if (p.fuse.x_bf16) {
+            const uint2 xv = *(const uint2*)((const uint16_t*)p.fuse.xres + yo);
+            v[0] += bf16_to_f32((uint16_t)xv.x);
+            v[1] += bf16_to_f32((uint16_t)(xv.x >> 16));
+            v[2] += bf16_to_f32((uint16_t)xv.y);
+            v[3] += bf16_to_f32((uint16_t)(xv.y >> 16));
+          } else {
+            const f32x4_t xv = *(const f32x4_t*)((const float*)p.fuse.xres + yo);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] += xv[u];
+          }
+        }
+        if (p.fuse.y_bf16)
+          *(uint2*)((uint16_t*)p.fuse.y + yo) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        else
+          *(f32x4_t*)((float*)p.fuse.y + yo) = f32x4_t{v[0], v[1], v[2], v[3]};
+      }
     } else {
       float* C = (float*)p.C + orow;
 #pragma unroll
@@ -553,9 +587,11 @@ hipError_t gemm_bf16_gate_up(const FfnPlan& pl, const void* A, int64_t a_blk, co
 }
 
 hipError_t gemm_bf16_down(const FfnPlan& pl, const void* h, int64_t h_blk, const int4* tab, const int32_t* count,
-                          int64_t grid, const void* W2, const float* s2, float* yp, int64_t F, int64_t d, hipStream_t s) {
+                          int64_t grid, const void* W2, const float* s2, float* yp, const CombineFuse* fuse, int64_t F,
+                          int64_t d, hipStream_t s) {
   GemmArgs a{(const uint16_t*)h, W2, nullptr, s2, nullptr, yp, tab, count, (int)d, (int)F};
   set_layout(a, h_blk, 0);
+  if (fuse) a.fuse = *fuse;
   if (F / (pl.k64_down ? 2 * BKS : BKS) < pl.ns_down - 1) return hipErrorInvalidValue;
   const unsigned g = (unsigned)launch_grid(pl, grid);
 #define MOE_LAUNCH(B, W, N)                                     \

@@ -236,14 +236,15 @@ hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const void* A, bool 
 }
 
 hipError_t launch_gemm_down(bool bf16, const FfnPlan& p, const void* h, const int4* tab, const int32_t* count,
-                            int64_t n_groups, int64_t max_rows, const void* W2, const float* s2, float* yp, int64_t F,
-                            int64_t d, hipStream_t s) {
+                            int64_t n_groups, int64_t max_rows, const void* W2, const float* s2, float* yp,
+                            const CombineFuse* fuse, int64_t F, int64_t d, hipStream_t s) {
+  if (fuse && !bf16) return hipErrorInvalidValue;
   const int64_t grid = grid_of(p.bm_down, max_rows, n_groups, d, p.bn_out_down);
   if (grid == 0) return hipSuccess;
   prof_begin(K_GEMM_DOWN, s);
   hipError_t err;
   if (bf16) {
-    err = gemm_bf16_down(p, h, max_rows, tab, count, grid, W2, s2, yp, F, d, s);
+    err = gemm_bf16_down(p, h, max_rows, tab, count, grid, W2, s2, yp, fuse, F, d, s);
   } else {
     F32Args a{(const float*)h, (const float*)W2, nullptr, yp, tab, count, (int)d, (int)F};
     gemm_f32_kernel<false><<<(unsigned)grid, 256, 0, s>>>(a);

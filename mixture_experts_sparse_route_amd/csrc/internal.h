@@ -132,6 +132,18 @@ int64_t ffn_table_entries(bool bf16, int64_t max_rows, int64_t n_groups, int64_t
 // and their entry counts counts[0] (gate_up) and counts[1] (down).
 hipError_t launch_ffn_tiles(const FfnPlan& p, const int32_t* offsets, int64_t n_groups, int64_t max_rows, int64_t F,
                             int64_t d, int4* tab_up, int4* tab_down, int32_t* counts, hipStream_t s);
+// Combine fused into GEMM2 for one assignment per token (K == 1, no shared
+// expert): the epilogue writes y[t] = w[t] * yp_row (+ x[t]) for the token t
+// = row_src[row] of each kept row, in the combine's arithmetic; the combine
+// then only writes the dropped tokens.
+struct CombineFuse {
+  const int32_t* row_src;  // [R] flat assignment (= token) of each row
+  const float* w;          // [T] gate weight
+  const void* xres;        // residual x [T, d] or null
+  void* y;                 // [T, d] output
+  bool x_bf16, y_bf16;
+};
+
 // bf16 MFMA path (gemm_bf16.hip); called through the launchers below.
 // s1 / s3 / s2: [groups, N] row scales of E4M3 weights (p.w8), else unused.
 // a_blk / h_blk: the row count R of a k-blocked operand ([cols/32][R][32]:
@@ -140,21 +152,25 @@ hipError_t gemm_bf16_gate_up(const FfnPlan& p, const void* A, int64_t a_blk, con
                              int64_t grid, const void* W1, const void* W3, const float* s1, const float* s3, void* h,
                              int64_t h_blk, int64_t F, int64_t d, hipStream_t s);
 hipError_t gemm_bf16_down(const FfnPlan& p, const void* h, int64_t h_blk, const int4* tab, const int32_t* count,
-                          int64_t grid, const void* W2, const float* s2, float* yp, int64_t F, int64_t d, hipStream_t s);
+                          int64_t grid, const void* W2, const float* s2, float* yp, const CombineFuse* fuse, int64_t F,
+                          int64_t d, hipStream_t s);
 // bf16: h is k-blocked with max_rows rows, and so is A when a_blocked (else
 // row-major); fp32: everything row-major.
 hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const void* A, bool a_blocked, const int4* tab,
                                const int32_t* count, int64_t n_groups, int64_t max_rows, const void* W1, const void* W3,
                                const float* s1, const float* s3, void* h, int64_t F, int64_t d, hipStream_t s);
+// fuse (bf16 only, nullable): write y instead of yp.
 hipError_t launch_gemm_down(bool bf16, const FfnPlan& p, const void* h, const int4* tab, const int32_t* count,
-                            int64_t n_groups, int64_t max_rows, const void* W2, const float* s2, float* yp, int64_t F,
-                            int64_t d, hipStream_t s);
+                            int64_t n_groups, int64_t max_rows, const void* W2, const float* s2, float* yp,
+                            const CombineFuse* fuse, int64_t F, int64_t d, hipStream_t s);
 
 // dst[0] = 0, dst[1] = n (row range of the shared expert).
 hipError_t launch_set_range(int32_t* dst, int64_t n, hipStream_t s);
 
 // ---- combine (a9) ----
+// only_dropped: write only the tokens none of whose assignments was kept
+// (the others were written by a fused GEMM2 epilogue).
 hipError_t launch_combine(bool x_bf16, bool y_bf16, const float* yp, const float* w, const int32_t* dest, const float* shared,
-                          const void* xres, void* y, int64_t T, int64_t d, int64_t K, hipStream_t s);
+                          const void* xres, void* y, int64_t T, int64_t d, int64_t K, bool only_dropped, hipStream_t s);
 
 }  // namespace moe
