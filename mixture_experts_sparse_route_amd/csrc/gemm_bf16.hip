@@ -18,8 +18,11 @@
 // Each wave issues the same number of loads per stage, so "stage kt has
 // landed" is an exact vmcnt wait; NS-1 stages are in flight while one is
 // multiplied.  LDS rows are 64 bytes; the 16-byte chunk c of row r sits at
-// position c ^ ((r >> 2) & 3), which makes both the DMA writes (1 KB
-// contiguous per wave) and the MFMA fragment reads bank-conflict free.
+// position c ^ ((r >> 1) & 3): the DMA writes stay 1 KB contiguous per wave,
+// and the 8 rows that a 16-byte-per-lane fragment read covers in one LDS
+// cycle (rows 8m .. 8m+7, one chunk) fall on 8 distinct 16-byte bank groups
+// (with c ^ ((r >> 2) & 3), rows r and r + 2 collided: measured as half of
+// all LDS cycles lost to bank conflicts in the prefill GEMM).
 //
 // FP8 weights (E4M3, two stage widths).  Stages of 32 k: the weight tile is
 // staged as E4M3 bytes in 32-byte LDS rows (16-byte chunk c of row r at
@@ -71,7 +74,7 @@ struct GemmArgs {
   CombineFuse fuse;        // down: y written through it when fuse.y is set
 };
 
-__device__ __forceinline__ int lds_pos(int row, int chunk) { return row * RB + ((chunk ^ ((row >> 2) & 3)) << 4); }
+__device__ __forceinline__ int lds_pos(int row, int chunk) { return row * RB + ((chunk ^ ((row >> 1) & 3)) << 4); }
 
 // two floats -> two bf16 (round to nearest even), lo in the low half
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -191,7 +194,7 @@ __device__ __forceinline__ void issue_step(IssueState& is, const GemmArgs& p, co
   }
   const int64_t Kd = p.Kdim;
   const int r_l = lane >> 2;
-  const int c_l = (lane & 3) ^ ((r_l >> 2) & 3);
+  const int c_l = (lane & 3) ^ ((r_l >> 1) & 3);
   const int g = is.cur.g, row_first = is.cur.row_first, rows = is.cur.rows, n0 = is.cur.n0;
   char* const st = lds + (s % NS) * STAGE;
   if constexpr (k_per_stage<WK>() == BKS) {

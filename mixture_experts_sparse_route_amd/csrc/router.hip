@@ -26,7 +26,10 @@ namespace {
 // fp32 x: the same tiling with fp32 FMA.
 constexpr int LG_T = 64, LG_K = 32;
 
-__device__ __forceinline__ int lg_pos(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
+// 16-byte chunk c of 64-byte row r at c ^ ((r >> 1) & 3): the 8 rows a
+// 16-byte-per-lane read covers in one LDS cycle fall on 8 distinct 16-byte
+// bank groups
+__device__ __forceinline__ int lg_pos(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4); }
 
 __device__ __forceinline__ void split3(float w, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
   hi = f32_to_bf16(w);
