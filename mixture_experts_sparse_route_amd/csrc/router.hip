@@ -498,14 +498,18 @@ __global__ __launch_bounds__(256) void router_topk_kernel(float* __restrict__ lo
 int router_splits(int64_t T, int64_t d, int64_t E, bool bf16) {
   const int64_t ew = (!bf16 || E > 16) ? 64 : 16;
   const int64_t tiles = ((T + LG_T - 1) / LG_T) * ((E + ew - 1) / ew);
-  // split d until there are `want` workgroups (tuning override: MOE_ROUTER_WGS)
-  static const int64_t want = [] {
+  // split d until there is a workgroup per CU and no slice is longer than
+  // 4096 (a slice is one workgroup's serial chain of 32-wide k-steps; more
+  // slices cost the Top-K kernel their partial sums).  Tuning override:
+  // MOE_ROUTER_WGS, a workgroup count to reach instead.
+  static const int64_t want_env = [] {
     const char* v = getenv("MOE_ROUTER_WGS");
     const long n = v ? atol(v) : 0;
-    return n > 0 ? (int64_t)n : (int64_t)512;
+    return n > 0 ? (int64_t)n : (int64_t)0;
   }();
+  const int64_t want = want_env > 0 ? want_env : (int64_t)device_cus();
   int S = 1;
-  while (tiles * S < want && S < 64 && d % ((int64_t)S * 2 * LG_K) == 0) S *= 2;
+  while ((tiles * S < want || (want_env == 0 && d / S > 4096)) && S < 64 && d % ((int64_t)S * 2 * LG_K) == 0) S *= 2;
   return S;
 }
 
