@@ -155,16 +155,14 @@ struct TileRef {
   int g, row_first, rows, n0;  // group, first row, rows, first column
 };
 
+// The entry is uniform: it is moved to scalar registers at once, so the wait
+// for it happens here (at a tile's start) and no later copy of the issue
+// state waits on vector loads in flight (which would drain the DMA ring).
 __device__ __forceinline__ TileRef load_tile(const int4* tab, int64_t L) {
   const int4 v = tab[L];
-  return TileRef{v.x, v.y, v.z, v.w};
+  return TileRef{__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
+                 __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w)};
 }
-
-struct IssueState {
-  TileRef cur;   // tile whose k-steps are being issued
-  TileRef next;  // the following tile
-  int tile;      // position of `cur` in this workgroup's tile sequence
-};
 
 // Per-workgroup constants of the tile sequence.
 struct Seq {
@@ -175,121 +173,113 @@ struct Seq {
   int total_steps;  // n_tiles * nk
 };
 
-// Issues the DMA of global step s (tile s / nk, k-step s % nk) into stage s % NS.
-// Lane -> (row r_l of a 16-row group, chunk c_l), chunk swizzled as in
-// lds_pos; A rows past the tile's end are loaded clamped to its last row
-// (their results are never stored).
+// DMA issue state of one wave: the table entries of the tile whose k-steps
+// are being issued and of the tile after it, and this lane's source address
+// of every load of a stage, at k-step 0 of the current tile (set when the
+// issue crosses into a tile; a stage then only adds k-step x stride).
+//
+// Lane mapping (chunk swizzles as in lds_pos / lds_pos128 / lds_pos8):
+// 64-byte rows: lane -> (row lane/4 of a 16-row group, chunk (lane%4) ^
+// ((row >> 1) & 3)); 128-byte rows: (row lane/8 of an 8-row group, chunk
+// (lane%8) ^ row); 32-byte E4M3 rows: (row lane/2 of a 32-row group, chunk
+// (lane%2) ^ ((row >> 2) & 1)).  A rows past the tile's end are loaded
+// clamped to its last row (their results are never stored); weight rows past
+// N likewise.
 template <int BM, int BNB, int NS, bool GATE_UP, int WK>
-__device__ __forceinline__ void issue_step(IssueState& is, const GemmArgs& p, const Seq& q, char* lds, int s, int wave,
-                                           int lane) {
-  constexpr int AG = BM / 16 / 4;
-  constexpr int BG = BNB / 16 / 4;
-  constexpr int HALF = BNB / 4;  // gate_up: rows of one matrix in each quarter of the weight tile
-  constexpr int STAGE = stage_bytes<WK>(BM, BNB);
-  const int ti = s / q.nk, kt = s - ti * q.nk;
-  if (ti != is.tile) {  // crossed into the next tile of the sequence
-    is.tile = ti;
-    is.cur = is.next;
-    if (ti + 1 < q.n_tiles) is.next = load_tile(p.tab, q.lbase + (int64_t)(ti + 1) * q.lstride);
+struct Issuer {
+  static constexpr bool K64 = k_per_stage<WK>() == 2 * BKS;
+  static constexpr int NA = K64 ? BM / 32 : BM / 16 / 4;  // A loads per wave per stage
+  static constexpr int NB = WK == WK_BF16_64 ? BNB / 32 : (WK == WK_E4M3_32 ? BNB / 32 / 4 : BNB / 16 / 4);
+  static constexpr int HALF = BNB / 4;  // gate_up: rows of one matrix in each quarter of the weight tile
+  static constexpr int STAGE = stage_bytes<WK>(BM, BNB);
+  // weight bytes per stage and row
+  static constexpr int WKS = WK == WK_BF16_64 ? 2 * RB : (WK == WK_E4M3_32 ? 32 : RB);
+
+  TileRef cur;   // tile whose k-steps are being issued
+  TileRef next;  // the following tile
+  int tile;      // position of `cur` in this workgroup's tile sequence
+  int64_t aks;   // A bytes per stage along k
+  const char* ab[NA];
+  const char* wb[NB];
+
+  // weight row (table column) of tile-relative weight row rt, and its matrix
+  __device__ __forceinline__ const char* wrow(const GemmArgs& p, int rt, int64_t esz, int64_t off) const {
+    const char* base = (const char*)p.B0;
+    int col;
+    if (GATE_UP) {
+      // quarters of the weight tile: W1 half 0, W3 half 0, W1 half 1, W3 half 1
+      const int qb = rt / HALF;
+      if (qb & 1) base = (const char*)p.B1;
+      col = cur.n0 + (qb >> 1) * HALF + rt % HALF;
+    } else {
+      col = cur.n0 + rt;
+    }
+    col = min(col, p.N - 1);
+    return base + (((int64_t)cur.g * p.N + col) * p.Kdim) * esz + off;
   }
-  const int64_t Kd = p.Kdim;
-  const int r_l = lane >> 2;
-  const int c_l = (lane & 3) ^ ((r_l >> 1) & 3);
-  const int g = is.cur.g, row_first = is.cur.row_first, rows = is.cur.rows, n0 = is.cur.n0;
-  char* const st = lds + (s % NS) * STAGE;
-  if constexpr (k_per_stage<WK>() == BKS) {
+
+  __device__ __forceinline__ void setup(const GemmArgs& p, int wave, int lane) {
+    const int rows = cur.rows, row_first = cur.row_first;
+    if constexpr (!K64) {
+      const int r_l = lane >> 2, c_l = (lane & 3) ^ ((r_l >> 1) & 3);
+      aks = p.a_ks * 2;
 #pragma unroll
-    for (int j = 0; j < AG; ++j) {
-      const int row = min((wave + 4 * j) * 16 + r_l, rows - 1);
-      __builtin_amdgcn_global_load_lds(p.A + (int64_t)(row_first + row) * p.a_rs + (int64_t)kt * p.a_ks + c_l * 8,
-                                       (lds_ptr_t)(st + (wave + 4 * j) * 16 * RB), 16, 0, 0);
-    }
-  } else {
-    // 64-k stage: 128-byte A rows, 8 rows per load; lane -> row lane/8 of the
-    // group, LDS slot lane%8, which holds chunk (lane%8) ^ (row%8)
-    const int r8 = lane >> 3, ch = (lane & 7) ^ r8;
-#pragma unroll
-    for (int j = 0; j < BM / 32; ++j) {
-      const int row = min((wave + 4 * j) * 8 + r8, rows - 1);
-      __builtin_amdgcn_global_load_lds(p.A + (int64_t)(row_first + row) * p.a_rs +
-                                           (int64_t)(2 * kt + (ch >> 2)) * p.a_ks + (ch & 3) * 8,
-                                       (lds_ptr_t)(st + (wave + 4 * j) * 8 * 2 * RB), 16, 0, 0);
-    }
-  }
-  if constexpr (WK == WK_BF16_64) {
-    // bf16 rows of 128 bytes per stage, laid out as the A rows: eight lanes
-    // per row, 8 rows per load
-    const int r8 = lane >> 3, ch = (lane & 7) ^ r8;
-    const int64_t gbase = (int64_t)g * p.N * Kd + (int64_t)kt * 2 * BKS + ch * 8;
-#pragma unroll
-    for (int j = 0; j < BNB / 32; ++j) {
-      const int rt = (wave + 4 * j) * 8 + r8;
-      const uint16_t* base = (const uint16_t*)p.B0;
-      int col;
-      if (GATE_UP) {
-        const int qb = rt / HALF;
-        if (qb & 1) base = (const uint16_t*)p.B1;
-        col = n0 + (qb >> 1) * HALF + rt % HALF;
-      } else {
-        col = n0 + rt;
+      for (int j = 0; j < NA; ++j) {
+        const int row = min((wave + 4 * j) * 16 + r_l, rows - 1);
+        ab[j] = (const char*)(p.A + (int64_t)(row_first + row) * p.a_rs + c_l * 8);
       }
-      col = min(col, p.N - 1);
-      __builtin_amdgcn_global_load_lds(base + gbase + (int64_t)col * Kd,
-                                       (lds_ptr_t)(st + BM * 2 * RB + (wave + 4 * j) * 8 * 2 * RB), 16, 0, 0);
-    }
-  } else if constexpr (WK == WK_E4M3_32) {
-    // E4M3 rows of 32 bytes per stage: two lanes per row, 32 rows per load
-    constexpr int BG8 = BNB / 32 / 4;
-    const int r8 = lane >> 1;
-    const int c8 = (lane & 1) ^ ((r8 >> 2) & 1);  // the chunk that lands in this lane's LDS slot
-    const int64_t gbase8 = (int64_t)g * p.N * Kd + (int64_t)kt * BKS + c8 * 16;
+    } else {
+      const int r8 = lane >> 3, ch = (lane & 7) ^ r8;
+      aks = p.a_ks * 4;
 #pragma unroll
-    for (int j = 0; j < BG8; ++j) {
-      const int q32 = wave + 4 * j;
-      const int rt = q32 * 32 + r8;
-      const uint8_t* base = (const uint8_t*)p.B0;
-      int col;
-      if (GATE_UP) {
-        const int qb = rt / HALF;
-        if (qb & 1) base = (const uint8_t*)p.B1;
-        col = n0 + (qb >> 1) * HALF + rt % HALF;
-      } else {
-        col = n0 + rt;
+      for (int j = 0; j < NA; ++j) {
+        const int row = min((wave + 4 * j) * 8 + r8, rows - 1);
+        ab[j] = (const char*)(p.A + (int64_t)(row_first + row) * p.a_rs + (int64_t)(ch >> 2) * p.a_ks + (ch & 3) * 8);
       }
-      col = min(col, p.N - 1);
-      __builtin_amdgcn_global_load_lds(base + gbase8 + (int64_t)col * Kd,
-                                       (lds_ptr_t)(st + BM * RB + q32 * 32 * 32), 16, 0, 0);
     }
-  } else {
-    // weight rows of 64 bytes per stage (32 bf16 or 64 E4M3 k): four lanes per
-    // row, 16 rows per load
-    constexpr int ESZ = WK == WK_BF16 ? 2 : 1;  // bytes per weight element
-    const int64_t gbase = ((int64_t)g * p.N * Kd + (int64_t)kt * (64 / ESZ) + c_l * (16 / ESZ)) * ESZ;
+    if constexpr (WK == WK_BF16_64) {
+      const int r8 = lane >> 3, ch = (lane & 7) ^ r8;
 #pragma unroll
-    for (int j = 0; j < BG; ++j) {
-      const int q16 = wave + 4 * j;
-      const char* base = (const char*)p.B0;
-      int col;
-      if (GATE_UP) {
-        // quarters of the weight tile: W1 half 0, W3 half 0, W1 half 1, W3 half 1
-        const int qb = (q16 * 16) / HALF;
-        if (qb & 1) base = (const char*)p.B1;
-        col = n0 + (qb >> 1) * HALF + (q16 * 16) % HALF + r_l;
-      } else {
-        col = n0 + q16 * 16 + r_l;
-      }
-      col = min(col, p.N - 1);
-      __builtin_amdgcn_global_load_lds(
-          base + gbase + (int64_t)col * Kd * ESZ,
-          (lds_ptr_t)(st + BM * (WK == WK_E4M3_64 ? 2 * RB : RB) + (wave + 4 * j) * 16 * RB), 16, 0, 0);
+      for (int j = 0; j < NB; ++j) wb[j] = wrow(p, (wave + 4 * j) * 8 + r8, 2, ch * 16);
+    } else if constexpr (WK == WK_E4M3_32) {
+      const int r2 = lane >> 1, c8 = (lane & 1) ^ ((r2 >> 2) & 1);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) wb[j] = wrow(p, (wave + 4 * j) * 32 + r2, 1, c8 * 16);
+    } else {
+      const int r_l = lane >> 2, c_l = (lane & 3) ^ ((r_l >> 1) & 3);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) wb[j] = wrow(p, (wave + 4 * j) * 16 + r_l, WK == WK_BF16 ? 2 : 1, c_l * 16);
     }
   }
-}
+
+  // Issues the DMA of global step s (tile s / nk, k-step s % nk) into stage s % NS.
+  __device__ __forceinline__ void issue(const GemmArgs& p, const Seq& q, char* lds, int s, int wave, int lane) {
+    const int ti = s / q.nk, kt = s - ti * q.nk;
+    if (ti != tile) {  // crossed into the next tile of the sequence
+      tile = ti;
+      cur = next;
+      if (ti + 1 < q.n_tiles) next = load_tile(p.tab, q.lbase + (int64_t)(ti + 1) * q.lstride);
+      setup(p, wave, lane);
+    }
+    char* const st = lds + (s % NS) * STAGE;
+    const int64_t ao = (int64_t)kt * aks, wo = (int64_t)kt * WKS;
+#pragma unroll
+    for (int j = 0; j < NA; ++j)
+      __builtin_amdgcn_global_load_lds(ab[j] + ao, (lds_ptr_t)(st + (wave + 4 * j) * (K64 ? 8 * 2 * RB : 16 * RB)), 16,
+                                       0, 0);
+    constexpr int WOFF = BM * (K64 ? 2 * RB : RB);  // weight tile offset in the stage
+    constexpr int WLOAD = WK == WK_BF16_64 ? 8 * 2 * RB : (WK == WK_E4M3_32 ? 32 * 32 : 16 * RB);  // bytes per load
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      __builtin_amdgcn_global_load_lds(wb[j] + wo, (lds_ptr_t)(st + WOFF + (wave + 4 * j) * WLOAD), 16, 0, 0);
+  }
+};
 
 // k-loop and epilogue of one tile for a wave that owns NBW active 16-row
 // blocks.  `step` is the global step of the tile's first k-step.
 template <int BM, int BNB, int NS, bool GATE_UP, int WK, int NBW>
-__device__ __forceinline__ void gemm_tile(IssueState& is, const GemmArgs& p, const Seq& q, char* lds, const TileRef te,
+__device__ __forceinline__ void gemm_tile(Issuer<BM, BNB, NS, GATE_UP, WK>& is, const GemmArgs& p, const Seq& q,
+                                          char* lds, const TileRef te,
                                           const int step0, const int wave, const int lane) {
   constexpr bool W8 = WK == WK_E4M3_32 || WK == WK_E4M3_64;  // E4M3 codes: row scales in the epilogue
   constexpr bool K64 = k_per_stage<WK>() == 2 * BKS;
@@ -342,7 +332,7 @@ __device__ __forceinline__ void gemm_tile(IssueState& is, const GemmArgs& p, con
         a1[i] = *(const bf16x8_t*)(st + lds_pos128((2 * i + wm) * 16 + lr, 4 + lk));
       }
       asm volatile("" ::: "memory");
-      if (s + NS - 1 < q.total_steps) issue_step<BM, BNB, NS, GATE_UP, WK>(is, p, q, lds, s + NS - 1, wave, lane);
+      if (s + NS - 1 < q.total_steps) is.issue(p, q, lds, s + NS - 1, wave, lane);
 #pragma unroll
       for (int i = 0; i < NBW; ++i)
 #pragma unroll
@@ -370,7 +360,7 @@ __device__ __forceinline__ void gemm_tile(IssueState& is, const GemmArgs& p, con
       // refill the stage consumed in the previous step (every wave has passed
       // this step's barrier, so nobody reads it any more); near the end of a
       // tile this already fetches the next tile's first k-steps
-      if (s + NS - 1 < q.total_steps) issue_step<BM, BNB, NS, GATE_UP, WK>(is, p, q, lds, s + NS - 1, wave, lane);
+      if (s + NS - 1 < q.total_steps) is.issue(p, q, lds, s + NS - 1, wave, lane);
 #pragma unroll
       for (int i = 0; i < NBW; ++i)
 #pragma unroll
@@ -482,13 +472,14 @@ __global__ __launch_bounds__(256, NS* stage_bytes<WK>(BM, BNB) <= LDS_BYTES / 2 
   q.total_steps = q.n_tiles * q.nk;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 
-  IssueState is;
+  Issuer<BM, BNB, NS, GATE_UP, WK> is;
   is.tile = 0;
   is.cur = load_tile(p.tab, q.lbase);
   is.next = q.n_tiles > 1 ? load_tile(p.tab, q.lbase + q.lstride) : is.cur;
+  is.setup(p, wave, lane);
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    if (s < q.total_steps) issue_step<BM, BNB, NS, GATE_UP, WK>(is, p, q, lds, s, wave, lane);
+    if (s < q.total_steps) is.issue(p, q, lds, s, wave, lane);
 
   for (int t = 0; t < q.n_tiles; ++t) {
     // k-steps issued so far end inside tile t (nk >= NS - 1), so the issue
