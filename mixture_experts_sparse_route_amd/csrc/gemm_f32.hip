@@ -146,16 +146,27 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_
   // E * d / 128 (stages of 32 k, 4 deep); when groups average 512 rows or
   // more (MFMA-bound), stages of 64 k, 2 deep (80 KB): two MFMA k-steps per
   // barrier and each weight fragment reused over 192 rows.
+  // Otherwise (groups neither decode-sized nor bounded by such a capacity)
+  // GEMM1 takes 192 x 128 tiles in 2 stages of 64 k as well (same box:
+  // DeepSeek 6.79 -> 6.46 ms, prefill 3.03 -> 2.95 ms; Switch, whose groups
+  // the capacity bounds, is slower with them).
   if (!w8 && p.bm == 128) {
     if (group_max > 128 && group_max <= 192) {
       p.bm_down = 192;
       p.bnb_down = 128;
       p.ns_down = 4;
-    } else if (avg >= 512) {
-      p.bm_down = 192;
-      p.bnb_down = 128;
-      p.ns_down = 2;
-      p.k64_down = true;
+    } else {
+      p.bm_down = p.bm;
+      p.bm = 192;
+      p.bnb_up = 128;
+      p.ns_up = 2;
+      p.k64_up = true;
+      if (avg >= 512) {
+        p.bm_down = 192;
+        p.bnb_down = 128;
+        p.ns_down = 2;
+        p.k64_down = true;
+      }
     }
   }
   // A ring deeper than the reduction dimension's stages + 1 cannot be
