@@ -120,3 +120,22 @@ def test_fp8_full_size(name):
     r = np.random.default_rng(0)
     toks = None if T <= 64 else np.array(sorted({0, T - 1} | set(r.choice(T, 24, replace=False).tolist())))
     print(name, check_fp8(case, tokens=toks))
+
+
+# E4M3 weights in stages of 32 k (the plans take stages of 64 k; the tuning
+# overrides select the 32-k kernels: 128 x 256 and 128 x 128 tiles)
+K32_ENV = {"MOE_GEMM_K64": "0", "MOE_GEMM_BM": "128", "MOE_GEMM_BM_DOWN": "128", "MOE_GEMM_BNB_UP": "256",
+           "MOE_GEMM_NS_UP": "5", "MOE_GEMM_BNB_DOWN": "128", "MOE_GEMM_NS_DOWN": "6"}
+
+
+@pytest.mark.parametrize("name", ["mixtral_two_mtiles", "deepseek_shared"])
+def test_fp8_stages_of_32k(name, monkeypatch):
+    for k, v in K32_ENV.items():
+        monkeypatch.setenv(k, v)
+    print(name, check_fp8(Case(CASES[name])))
+
+
+def test_fp8_stages_of_32k_match_dequantised_bf16(monkeypatch):
+    for k, v in K32_ENV.items():
+        monkeypatch.setenv(k, v)
+    test_fp8_matches_dequantised_bf16_weights()
