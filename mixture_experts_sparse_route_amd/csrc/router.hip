@@ -260,11 +260,18 @@ __device__ __forceinline__ float group_sum(float v, int L) {
 }
 
 // part[0][i] + part[1][i] + ... + part[S-1][i], added in slice order; the
-// loads are issued eight at a time so they overlap instead of forming one
+// loads are issued 32 at a time so they overlap instead of forming one
 // dependent chain of S loads.
 __device__ __forceinline__ float sum_slices(const float* __restrict__ part, int S, int64_t stride, int64_t i) {
   float l = part[i];
   int q = 1;
+  for (; q + 32 <= S; q += 32) {
+    float v[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) v[u] = part[(int64_t)(q + u) * stride + i];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) l += v[u];
+  }
   for (; q + 8 <= S; q += 8) {
     float v[8];
 #pragma unroll
@@ -334,10 +341,65 @@ __global__ __launch_bounds__(256) void router_topk_kernel(float* __restrict__ lo
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int G = 64 / L;            // tokens per wave per pass
     const int slot = lane / L, ll = lane % L;
+    // This lane's logits of token t (its experts ll + L*p): with d-slices,
+    // their partial sums added in slice order, then the bias.  Every load of
+    // a block of slices (and the bias) is issued before the first add, so a
+    // pass waits for about one load latency rather than one per expert.
+    const bool sliced = S > 1 && !presum;
+    auto gather = [&](int t, bool valid, float (&l)[P]) {
+      int64_t off[P];
+      float b[P];
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const int e = ll + L * p;
+        const bool ok = valid && e < E;
+        off[p] = ok ? (int64_t)t * E + e : (int64_t)t_begin * E;  // unused lanes read an in-range element
+        b[p] = (sliced && bias) ? bias[ok ? e : 0] : 0.0f;
+      }
+      if (sliced) {
+        const int64_t stride = (int64_t)T * E;
+#pragma unroll
+        for (int p = 0; p < P; ++p) l[p] = part[off[p]];
+        int q = 1;
+        for (; q + 4 <= S; q += 4) {
+          float v[4][P];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int p = 0; p < P; ++p) v[u][p] = part[(int64_t)(q + u) * stride + off[p]];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int p = 0; p < P; ++p) l[p] += v[u][p];
+        }
+        for (; q < S; ++q) {
+          float v[P];
+#pragma unroll
+          for (int p = 0; p < P; ++p) v[p] = part[(int64_t)q * stride + off[p]];
+#pragma unroll
+          for (int p = 0; p < P; ++p) l[p] += v[p];
+        }
+        if (bias) {
+#pragma unroll
+          for (int p = 0; p < P; ++p) l[p] += b[p];
+        }
+      } else {
+#pragma unroll
+        for (int p = 0; p < P; ++p) l[p] = logits[off[p]];
+      }
+    };
+    // the next pass's logits load while this pass selects
+    float lcur[P], lnext[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) lnext[p] = 0.0f;
+    gather(t_begin + wave * G + slot, t_begin + wave * G + slot < t_end, lcur);
     for (int base = t_begin; base < t_end; base += 4 * G) {
       const int t = base + wave * G + slot;
       const bool valid = t < t_end;
-      const float* lt = logits + (int64_t)(valid ? t : t_begin) * E;
+      if (base + 4 * G < t_end) {
+        const int tn = t + 4 * G;
+        gather(tn, tn < t_end, lnext);
+      }
       uint64_t pk[P];
       float lv[P], sv[P];
 #pragma unroll
@@ -347,15 +409,8 @@ __global__ __launch_bounds__(256) void router_topk_kernel(float* __restrict__ lo
         lv[p] = -INFINITY;
         sv[p] = 0.0f;
         if (valid && e < E) {
-          float l;
-          if (S > 1 && !presum) {
-            // logits = the d-slices' partial sums added in slice order, then the bias
-            l = sum_slices(part, S, (int64_t)T * E, (int64_t)t * E + e);
-            if (bias) l += bias[e];
-            logits[(int64_t)t * E + e] = l;
-          } else {
-            l = lt[e];
-          }
+          const float l = lcur[p];
+          if (sliced) logits[(int64_t)t * E + e] = l;
           lv[p] = l;
           float key;
           if (gate == 0) {
@@ -467,6 +522,8 @@ __global__ __launch_bounds__(256) void router_topk_kernel(float* __restrict__ lo
           if (ll == 0) zacc += lse * lse;
         }
       }
+#pragma unroll
+      for (int p = 0; p < P; ++p) lcur[p] = lnext[p];
     }
   }
   if constexpr (STATS) {
