@@ -228,8 +228,13 @@ moe_status check_routing(const moe_routing* r, bool need_logits, bool need_stats
 }
 
 // a1-a4 on a validated shape.
+// drop_y non-null (first-come drops, one assignment per token, no shared
+// expert): the scatter also writes the dropped tokens' output rows (x or 0
+// when drop_x is null) and *drop_done says it did.
 moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const void* x, const float* Wg,
-                    const float* logit_bias, const float* sel_bias, const moe_routing& r, void* ws, hipStream_t st) {
+                    const float* logit_bias, const float* sel_bias, const moe_routing& r, void* ws, hipStream_t st,
+                    void* drop_y = nullptr, const void* drop_x = nullptr, bool* drop_done = nullptr) {
+  if (drop_done) *drop_done = false;
   int32_t* blk_count = at<int32_t>(ws, L.blk_count);
   int32_t* blk_base = at<int32_t>(ws, L.blk_base);
   const bool topk_in = c->flags & MOE_F_TOPK_IN;
@@ -306,7 +311,14 @@ moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const 
     MOE_HIP(launch_route_scatter(sc, s.T, s.K, s.E, s.cap, st));
   } else {
     sc.mode = kFirstCome;
+    if (drop_y && s.K == 1 && s.S == 0 && s.bf16) {
+      sc.drop_y = drop_y;
+      sc.drop_x = (const uint16_t*)drop_x;
+      sc.drop_y_bf16 = s.out_bf16;
+      sc.drop_d = (int)s.d;
+    }
     MOE_HIP(launch_route_scatter(sc, s.T, s.K, s.E, s.cap, st));
+    if (drop_done) *drop_done = sc.drop_y != nullptr;
   }
   return MOE_OK;
 }
@@ -530,13 +542,17 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, co
     rr.dropped = at<uint8_t>(ws, L.r_dropped);
     rr.stats = nullptr;
   }
-  if ((st = do_route(cfg, s, L, x, Wg, logit_bias, sel_bias, rr, ws, hs)) != MOE_OK) return st;
-  void* xp = at<void>(ws, L.xp);
-  float* yp = at<float>(ws, L.yp);
   const bool residual = cfg->flags & MOE_F_RESIDUAL;
   // one assignment per token and no shared expert (bf16): GEMM2 writes the
-  // kept tokens' outputs itself and the combine only the dropped tokens
+  // kept tokens' outputs itself, and the dropped tokens' rows are written by
+  // the capacity scatter (first-come drops) or else by the combine
   const bool fused = s.bf16 && s.K == 1 && s.S == 0 && !s.ec;
+  bool drop_done = false;
+  if ((st = do_route(cfg, s, L, x, Wg, logit_bias, sel_bias, rr, ws, hs, fused ? y : nullptr,
+                     residual ? x : nullptr, &drop_done)) != MOE_OK)
+    return st;
+  void* xp = at<void>(ws, L.xp);
+  float* yp = at<float>(ws, L.yp);
   const CombineFuse fuse{rr.row_src, rr.topk_w, residual ? x : nullptr, y, s.bf16, s.out_bf16};
   if (s.max_rows > 0) {
     // the fused path's xp is internal: k-blocked for bf16 (each k-step of a
@@ -559,8 +575,9 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, co
                      hs)) != MOE_OK)
       return st;
   }
-  MOE_HIP(launch_combine(s.bf16, s.out_bf16, yp, rr.topk_w, rr.dest, sh_out, residual ? x : nullptr, y, s.T, s.d, s.K,
-                         fused, hs));
+  if (!drop_done)
+    MOE_HIP(launch_combine(s.bf16, s.out_bf16, yp, rr.topk_w, rr.dest, sh_out, residual ? x : nullptr, y, s.T, s.d,
+                           s.K, fused, hs));
   return MOE_OK;
 }
 

@@ -83,6 +83,14 @@ struct RouteScatter {
   const int32_t* first_counts;  // kReroute2: first-pass demand
   int32_t* topk_idx;        // kReroute2: re-routed assignments get their new expert
   float* topk_w;            //            and weight
+  // kFirstCome with one assignment per token and no shared expert: the
+  // layer output rows of the dropped tokens, y[t] = 0 + x[t] (x nullable:
+  // 0), rounded once to y's type (the combine's arithmetic for such a row),
+  // are written here.  drop_y == nullptr: not written.
+  void* drop_y;
+  const uint16_t* drop_x;   // bf16 residual rows
+  bool drop_y_bf16;         // y is bf16, else fp32
+  int drop_d;               // row length
 };
 hipError_t launch_route_scatter(const RouteScatter& r, int64_t T, int64_t K, int64_t E, int64_t cap, hipStream_t s);
 hipError_t launch_route_affinity(const uint64_t* seg, const int32_t* counts, const int32_t* dem_off,
