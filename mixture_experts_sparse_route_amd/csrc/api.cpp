@@ -132,7 +132,7 @@ moe_status validate(const moe_config* c, Shape* sh) {
   sh->cap = cap;
   sh->max_rows = cap >= 0 ? std::min(T * K, E * cap) : T * K;
   sh->ec = ec;
-  sh->n_chunks = (T + kTopkTokens - 1) / kTopkTokens;
+  sh->n_chunks = (T + chunk_tokens(E, K) - 1) / chunk_tokens(E, K);
   sh->esz = bf16 ? 2 : 4;
   return MOE_OK;
 }

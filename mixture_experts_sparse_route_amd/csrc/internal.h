@@ -25,8 +25,12 @@ const char* kernel_name(int id);
 void prof_begin(int id, hipStream_t s);
 void prof_end(int id, hipStream_t s);
 
-// Tokens per router_topk workgroup; also the histogram chunk (in tokens).
+// Tokens per router_topk workgroup, which is also the histogram chunk of the
+// capacity scan and scatter: at most kTopkTokens.  Layers with a costly
+// selection (E * K >= 512) take chunks of 16 tokens, so the Top-K kernel has
+// twice the workgroups; the others 32 (fewer chunks for the scan).
 constexpr int kTopkTokens = 32;
+inline int chunk_tokens(int64_t E, int64_t K) { return E * K >= 512 ? 16 : 32; }
 
 // ---- router (a1-a3) ----
 // Number of d-slices the logits GEMM is cut into (1 = logits written directly).

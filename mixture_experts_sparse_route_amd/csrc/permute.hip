@@ -164,7 +164,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
 }
 
 // ------------------------------------------------------------ a4: scatter
-// Chunk b (kTopkTokens tokens = kTopkTokens*K assignments) is ranked in passes
+// Chunk b (ct <= kTopkTokens tokens = ct*K assignments) is ranked in passes
 // of 256 assignments.  Within a wave, lanes holding the same expert find each
 // other with one ballot per expert-id bit; a lane's rank is the number of
 // lower lanes in its peer set.  Per-wave counts are then scanned across the
@@ -192,15 +192,15 @@ __device__ __forceinline__ uint64_t affinity_key(float a, int64_t f) {
 
 template <int MODE>
 __global__ __launch_bounds__(256) void route_scatter_kernel(const RouteScatter a, const int T, const int K,
-                                                            const int E, const int nbits, const int cap) {
+                                                            const int E, const int nbits, const int cap, const int ct) {
   __shared__ int running[1024];
   __shared__ int wcnt[4][1024];
   __shared__ uint8_t ovf[MODE == kReroute1 ? kTopkTokens * 32 : 1];
   __shared__ int hist2[MODE == kReroute1 ? 1024 : 1];
   __shared__ uint8_t dropl[MODE == kFirstCome ? kTopkTokens : 1];  // K == 1: dropped tokens of the chunk
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t f_begin = (int64_t)blockIdx.x * kTopkTokens * K;
-  const int64_t f_end = min((int64_t)T * K, f_begin + (int64_t)kTopkTokens * K);
+  const int64_t f_begin = (int64_t)blockIdx.x * ct * K;
+  const int64_t f_end = min((int64_t)T * K, f_begin + (int64_t)ct * K);
   for (int e = threadIdx.x; e < E; e += 256) {
     running[e] = a.blk_base[(int64_t)blockIdx.x * E + e];
     if constexpr (MODE == kReroute1) hist2[e] = 0;
@@ -520,14 +520,15 @@ hipError_t launch_route_scatter(const RouteScatter& r, int64_t T, int64_t K, int
   int nbits = 0;
   while ((1ll << nbits) < E) ++nbits;
   const int capi = cap < 0 || cap > INT_MAX ? INT_MAX : (int)cap;
-  const unsigned nb = (unsigned)((T + kTopkTokens - 1) / kTopkTokens);
+  const int ct = chunk_tokens(E, K);
+  const unsigned nb = (unsigned)((T + ct - 1) / ct);
   const int Ti = (int)T, Ki = (int)K, Ei = (int)E;
   prof_begin(K_ROUTE_SCATTER, s);
   switch (r.mode) {
-    case kFirstCome: route_scatter_kernel<kFirstCome><<<nb, 256, 0, s>>>(r, Ti, Ki, Ei, nbits, capi); break;
-    case kAffinity: route_scatter_kernel<kAffinity><<<nb, 256, 0, s>>>(r, Ti, Ki, Ei, nbits, capi); break;
-    case kReroute1: route_scatter_kernel<kReroute1><<<nb, 256, 0, s>>>(r, Ti, Ki, Ei, nbits, capi); break;
-    default: route_scatter_kernel<kReroute2><<<nb, 256, 0, s>>>(r, Ti, Ki, Ei, nbits, capi); break;
+    case kFirstCome: route_scatter_kernel<kFirstCome><<<nb, 256, 0, s>>>(r, Ti, Ki, Ei, nbits, capi, ct); break;
+    case kAffinity: route_scatter_kernel<kAffinity><<<nb, 256, 0, s>>>(r, Ti, Ki, Ei, nbits, capi, ct); break;
+    case kReroute1: route_scatter_kernel<kReroute1><<<nb, 256, 0, s>>>(r, Ti, Ki, Ei, nbits, capi, ct); break;
+    default: route_scatter_kernel<kReroute2><<<nb, 256, 0, s>>>(r, Ti, Ki, Ei, nbits, capi, ct); break;
   }
   prof_end(K_ROUTE_SCATTER, s);
   return hipGetLastError();

@@ -238,7 +238,8 @@ __global__ __launch_bounds__(256) void router_logits_f32_kernel(const float* __r
 // rounds of a group-wide maximum over packed 64-bit keys select the experts:
 // high word = order-preserving image of the fp32 key, low word = ~expert, so
 // equal keys resolve to the lower expert.  Each workgroup covers
-// kTopkTokens consecutive tokens and also counts its assignments per expert.
+// ct <= kTopkTokens consecutive tokens and also counts its assignments per
+// expert.
 
 __device__ __forceinline__ uint64_t pack_key(float key, int e) {
   uint32_t u = __float_as_uint(key + 0.0f);  // -0 -> +0: signed zeros tie
@@ -304,7 +305,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(float* __restrict__ lo
                                                           float* __restrict__ blk_P, float* __restrict__ blk_z,
                                                           int32_t* __restrict__ alt_idx, float* __restrict__ alt_w,
                                                           int K2, int T, int E, int K, int L, int gate, int renorm,
-                                                          int topk_in) {
+                                                          int topk_in, int ct) {
   __shared__ int hist[1024];
   __shared__ float wsum[STATS ? 4 : 1][STATS ? 1024 : 1];
   __shared__ float wz[4];
@@ -315,8 +316,8 @@ __global__ __launch_bounds__(256) void router_topk_kernel(float* __restrict__ lo
 #pragma unroll
   for (int p = 0; p < P; ++p) pacc[p] = 0.0f;
 
-  const int t_begin = blockIdx.x * kTopkTokens;
-  const int t_end = min(T, t_begin + kTopkTokens);
+  const int t_begin = blockIdx.x * ct;
+  const int t_end = min(T, t_begin + ct);
   // Many d-slices (small T): the chunk's logits first, all threads over its
   // (token, expert) pairs, so the long slice sums run in parallel; with few
   // slices each lane sums its own experts' slices in the selection loop.
@@ -601,18 +602,19 @@ hipError_t launch_router_topk(float* logits, const float* part, int S, const flo
   int L = 1;
   while (L < 64 && (L * 4 < E || L < K)) L <<= 1;
   const int P = (int)((E + L - 1) / L);
-  const unsigned nb = (unsigned)((T + kTopkTokens - 1) / kTopkTokens);
+  const int ct = chunk_tokens(E, K);
+  const unsigned nb = (unsigned)((T + ct - 1) / ct);
   prof_begin(K_ROUTER_TOPK, s);
 #define MOE_TOPK(PP)                                                                                             \
   do {                                                                                                           \
     if (blk_P)                                                                                                   \
       router_topk_kernel<PP, true><<<nb, 256, 0, s>>>(logits, part, S, bias, sel_bias, idx, w, blk_count, blk_P,  \
                                                       blk_z, alt_idx, alt_w, (int)K2, (int)T, (int)E, (int)K, L,  \
-                                                      gate, renorm ? 1 : 0, topk_in ? 1 : 0);                     \
+                                                      gate, renorm ? 1 : 0, topk_in ? 1 : 0, ct);                 \
     else                                                                                                         \
       router_topk_kernel<PP, false><<<nb, 256, 0, s>>>(logits, part, S, bias, sel_bias, idx, w, blk_count,        \
                                                        nullptr, nullptr, alt_idx, alt_w, (int)K2, (int)T, (int)E, \
-                                                       (int)K, L, gate, renorm ? 1 : 0, topk_in ? 1 : 0);         \
+                                                       (int)K, L, gate, renorm ? 1 : 0, topk_in ? 1 : 0, ct);     \
   } while (0)
   if (P <= 1)
     MOE_TOPK(1);
