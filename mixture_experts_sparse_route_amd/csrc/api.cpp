@@ -380,6 +380,36 @@ moe_status resolve_records() {
   return MOE_OK;
 }
 
+// ---- side stream for the shared expert ----
+// The shared expert reads only x, so moe_forward runs it on a second stream
+// of the same device (default priority), forked from the caller's stream at
+// entry and joined before the combine: its GEMMs overlap the routing kernels
+// and the routed FFN.  One per device, created on first use; g_side_mu is
+// held while a call enqueues, so concurrent callers do not interleave their
+// fork / join records.
+struct Side {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+Side g_side[kMaxDevices];
+
+// The side stream of device `dev` (the current device), created on first use.
+moe_status side_of(int dev, Side** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device id %d out of range", dev);
+  Side& sd = g_side[dev];
+  if (!sd.s) {
+    // cross-stream ordering on one device needs no timing and no
+    // system-scope (host-visible) fence
+    MOE_HIP(hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming | hipEventDisableSystemFence));
+    MOE_HIP(hipEventCreateWithFlags(&sd.join, hipEventDisableTiming | hipEventDisableSystemFence));
+    MOE_HIP(hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking));
+  }
+  *out = &sd;
+  return MOE_OK;
+}
+
 const char* const kNames[K_COUNT] = {"router_logits", "router_topk", "route_scan",    "route_scatter", "dispatch",
                                      "ffn_tiles",     "gemm_gate_up", "gemm_down",    "combine"};
 
@@ -528,6 +558,17 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, co
   if ((st = check_ws(s, ws, ws_bytes, &L)) != MOE_OK) return st;
   if (s.T == 0) return MOE_OK;
   hipStream_t hs = (hipStream_t)stream;
+  // the shared expert on the device's side stream when the caller's stream
+  // belongs to the current device (else in order on the caller's stream)
+  std::unique_lock<std::mutex> side_lk;
+  Side* sd = nullptr;
+  if (s.S) {
+    int cur = -1, sdev = -2;
+    if (hipGetDevice(&cur) == hipSuccess && hipStreamGetDevice(hs, &sdev) == hipSuccess && sdev == cur) {
+      side_lk = std::unique_lock<std::mutex>(g_side_mu);
+      if ((st = side_of(cur, &sd)) != MOE_OK) return st;
+    }
+  }
   moe_routing rr;
   if (r) {
     rr = *r;
@@ -541,6 +582,20 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, co
     rr.row_src = at<int32_t>(ws, L.r_row_src);
     rr.dropped = at<uint8_t>(ws, L.r_dropped);
     rr.stats = nullptr;
+  }
+  // a8: the shared expert over all T rows of x
+  float* sh_out = s.S ? at<float>(ws, L.sh_out) : nullptr;
+  auto shared_ffn = [&](hipStream_t q) -> moe_status {
+    int32_t* range = at<int32_t>(ws, L.sh_range);
+    MOE_HIP(launch_set_range(range, s.T, q));
+    return do_ffn(s, x, false, range, 1, s.T, s.T, Ws1, Ws3, Ws2, sc.ws1, sc.ws3, sc.ws2, at<void>(ws, L.sh_h), sh_out,
+                  at<int4>(ws, L.sh_tab_up), at<int4>(ws, L.sh_tab_down), at<int32_t>(ws, L.sh_counts), s.Fs, q);
+  };
+  if (sd) {
+    MOE_HIP(hipEventRecord(sd->fork, hs));
+    MOE_HIP(hipStreamWaitEvent(sd->s, sd->fork, 0));
+    if ((st = shared_ffn(sd->s)) != MOE_OK) return st;
+    MOE_HIP(hipEventRecord(sd->join, sd->s));
   }
   const bool residual = cfg->flags & MOE_F_RESIDUAL;
   // one assignment per token and no shared expert (bf16): GEMM2 writes the
@@ -565,16 +620,8 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, co
                      fused ? &fuse : nullptr)) != MOE_OK)
       return st;
   }
-  float* sh_out = nullptr;
-  if (s.S) {
-    int32_t* range = at<int32_t>(ws, L.sh_range);
-    MOE_HIP(launch_set_range(range, s.T, hs));
-    sh_out = at<float>(ws, L.sh_out);
-    if ((st = do_ffn(s, x, false, range, 1, s.T, s.T, Ws1, Ws3, Ws2, sc.ws1, sc.ws3, sc.ws2, at<void>(ws, L.sh_h), sh_out,
-                     at<int4>(ws, L.sh_tab_up), at<int4>(ws, L.sh_tab_down), at<int32_t>(ws, L.sh_counts), s.Fs,
-                     hs)) != MOE_OK)
-      return st;
-  }
+  if (s.S && !sd && (st = shared_ffn(hs)) != MOE_OK) return st;
+  if (sd) MOE_HIP(hipStreamWaitEvent(hs, sd->join, 0));
   if (!drop_done)
     MOE_HIP(launch_combine(s.bf16, s.out_bf16, yp, rr.topk_w, rr.dest, sh_out, residual ? x : nullptr, y, s.T, s.d,
                            s.K, fused, hs));
