@@ -264,7 +264,12 @@ moe_status moe_combine(const moe_config* cfg, const float* yp, const moe_routing
 /* The whole layer: moe_route, moe_dispatch, moe_expert_ffn, the shared
  * expert (a SwiGLU over all T rows with Ws1, Ws3 [1, Fs, d], Ws2 [1, d, Fs],
  * added unweighted [TD §3.4, §9.1]) and moe_combine, in one stream-ordered
- * sequence with no host synchronisation.
+ * sequence with no host synchronisation.  With a shared expert, and `stream`
+ * on the current device, the shared expert runs on a second stream of that
+ * device that the library creates once (default priority) and orders with
+ * `stream` through events: it starts after the work enqueued on `stream`
+ * before the call, and the combine waits for it, so the call keeps plain
+ * stream semantics.
  * r: nullable; when NULL the routing arrays live in the workspace.  When
  * given, the routing results are written there (and MOE_F_LOGITS_IN /
  * MOE_F_TOPK_IN inputs read from there).  Required with MOE_F_*_IN and
