@@ -514,7 +514,7 @@ __global__ __launch_bounds__(256, NS* stage_bytes<WK>(BM, BNB) <= LDS_BYTES / 2 
 #define MOE_GEMM8K64_CONFIGS(X) X(64, 256, 3) X(128, 128, 3) X(128, 128, 2) X(64, 128, 5) X(64, 128, 4) X(64, 128, 2) \
   X(192, 128, 2) X(192, 128, 3)
 #define MOE_GEMM16K64_CONFIGS(X) X(192, 128, 3) X(192, 128, 2) X(128, 128, 3) X(128, 128, 2) X(64, 128, 3) \
-  X(64, 128, 2) X(64, 256, 3) X(128, 256, 2)
+  X(64, 128, 2) X(64, 256, 3) X(128, 256, 2) X(64, 128, 5)
 
 bool gemm_bf16_has_config(bool w8, bool k64, int bm, int bnb, int ns) {
 #define MOE_HAS(B, W, N) \
