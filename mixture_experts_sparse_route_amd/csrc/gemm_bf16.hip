@@ -516,6 +516,15 @@ __global__ __launch_bounds__(256, NS* stage_bytes<WK>(BM, BNB) <= LDS_BYTES / 2 
 #define MOE_GEMM16K64_CONFIGS(X) X(192, 128, 3) X(192, 128, 2) X(128, 128, 3) X(128, 128, 2) X(64, 128, 3) \
   X(64, 128, 2) X(64, 256, 3) X(128, 256, 2) X(64, 128, 5)
 
+// every configuration fits the tile tables' sizing
+#define MOE_FITS_TABLES(B, W, N) \
+  static_assert(B >= kMinTileRows && W >= kMinWeightTileRows, "tile tables are sized for larger tiles");
+MOE_GEMM_CONFIGS(MOE_FITS_TABLES)
+MOE_GEMM8_CONFIGS(MOE_FITS_TABLES)
+MOE_GEMM8K64_CONFIGS(MOE_FITS_TABLES)
+MOE_GEMM16K64_CONFIGS(MOE_FITS_TABLES)
+#undef MOE_FITS_TABLES
+
 bool gemm_bf16_has_config(bool w8, bool k64, int bm, int bnb, int ns) {
 #define MOE_HAS(B, W, N) \
   if (bm == B && bnb == W && ns == N) return true;

@@ -225,8 +225,9 @@ int64_t ffn_max_mtiles(int bm, int64_t max_rows, int64_t n_groups) {
 }
 
 int64_t ffn_table_entries(bool bf16, int64_t max_rows, int64_t n_groups, int64_t n_cols, bool gate_up) {
-  const int bm = bf16 ? 64 : FB;  // the smallest m-tile any plan uses
-  const int bn = bf16 ? (gate_up ? 64 : 128) : FB;  // the narrowest tiles any plan uses
+  const int bm = bf16 ? kMinTileRows : FB;  // the smallest m-tile any plan uses
+  // the narrowest output tiles any plan uses (GEMM1: half the weight rows)
+  const int bn = bf16 ? (gate_up ? kMinWeightTileRows / 2 : kMinWeightTileRows) : FB;
   return ffn_max_mtiles(bm, max_rows, n_groups) * ((n_cols + bn - 1) / bn);
 }
 

@@ -135,6 +135,11 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_
 // rows, stages), with bf16 (w8 false) or E4M3 (w8 true) weights in stages of
 // 32 k or (k64) 64 k.
 bool gemm_bf16_has_config(bool w8, bool k64, int bm, int bnb, int ns);
+// The smallest m-tile and weight tile (rows) of any compiled bf16 GEMM
+// configuration; the tile tables are sized for them (checked at compile time
+// against every configuration).
+constexpr int kMinTileRows = 64;
+constexpr int kMinWeightTileRows = 128;
 // Worst-case m-tiles for `bm`-row tiles.
 int64_t ffn_max_mtiles(int bm, int64_t max_rows, int64_t n_groups);
 // Entries the tile tables need for any plan of this dtype.
