@@ -311,7 +311,7 @@ moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const 
     MOE_HIP(launch_route_scatter(sc, s.T, s.K, s.E, s.cap, st));
   } else {
     sc.mode = kFirstCome;
-    if (drop_y && s.K == 1 && s.S == 0 && s.bf16) {
+    if (drop_y && s.K == 1 && s.S == 0 && s.bf16 && s.d % 8 == 0) {
       sc.drop_y = drop_y;
       sc.drop_x = (const uint16_t*)drop_x;
       sc.drop_y_bf16 = s.out_bf16;

@@ -94,7 +94,7 @@ struct RouteScatter {
   void* drop_y;
   const uint16_t* drop_x;   // bf16 residual rows
   bool drop_y_bf16;         // y is bf16, else fp32
-  int drop_d;               // row length
+  int drop_d;               // row length (a multiple of 8)
 };
 hipError_t launch_route_scatter(const RouteScatter& r, int64_t T, int64_t K, int64_t E, int64_t cap, hipStream_t s);
 hipError_t launch_route_affinity(const uint64_t* seg, const int32_t* counts, const int32_t* dem_off,

@@ -272,45 +272,34 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(const RouteScatter a
   if constexpr (MODE == kFirstCome) {
     if (a.drop_y && K == 1) {
       // one wave per dropped token of the chunk (token t = assignment f),
-      // 8 elements per lane and step when the row allows it
+      // 8 elements per lane and step (bf16 layers: d is a multiple of 64)
       const int n = (int)(f_end - f_begin), d = a.drop_d;
       for (int i = wave; i < n; i += 4) {
         if (!dropl[i]) continue;
         const int64_t o = (f_begin + i) * (int64_t)d;
-        if (d % 8 == 0) {
-          for (int c = lane * 8; c < d; c += 512) {
-            float v[8];
+        for (int c = lane * 8; c < d; c += 512) {
+          float v[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = 0.f;
-            if (a.drop_x) {
-              const uint4 xv = *(const uint4*)(a.drop_x + o + c);
-              const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+          for (int u = 0; u < 8; ++u) v[u] = 0.f;
+          if (a.drop_x) {
+            const uint4 xv = *(const uint4*)(a.drop_x + o + c);
+            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
-              for (int u = 0; u < 4; ++u) {
-                v[2 * u] += bf16_to_f32((uint16_t)xw[u]);
-                v[2 * u + 1] += bf16_to_f32((uint16_t)(xw[u] >> 16));
-              }
-            }
-            if (a.drop_y_bf16) {
-              uint32_t yw[4];
-#pragma unroll
-              for (int u = 0; u < 4; ++u)
-                yw[u] = (uint32_t)f32_to_bf16(v[2 * u]) | ((uint32_t)f32_to_bf16(v[2 * u + 1]) << 16);
-              *(uint4*)((uint16_t*)a.drop_y + o + c) = make_uint4(yw[0], yw[1], yw[2], yw[3]);
-            } else {
-              float* yr = (float*)a.drop_y + o + c;
-              *(float4*)yr = make_float4(v[0], v[1], v[2], v[3]);
-              *(float4*)(yr + 4) = make_float4(v[4], v[5], v[6], v[7]);
+            for (int u = 0; u < 4; ++u) {
+              v[2 * u] += bf16_to_f32((uint16_t)xw[u]);
+              v[2 * u + 1] += bf16_to_f32((uint16_t)(xw[u] >> 16));
             }
           }
-        } else {
-          for (int c = lane; c < d; c += 64) {
-            float v = 0.f;
-            if (a.drop_x) v += bf16_to_f32(a.drop_x[o + c]);
-            if (a.drop_y_bf16)
-              ((uint16_t*)a.drop_y)[o + c] = f32_to_bf16(v);
-            else
-              ((float*)a.drop_y)[o + c] = v;
+          if (a.drop_y_bf16) {
+            uint32_t yw[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              yw[u] = (uint32_t)f32_to_bf16(v[2 * u]) | ((uint32_t)f32_to_bf16(v[2 * u + 1]) << 16);
+            *(uint4*)((uint16_t*)a.drop_y + o + c) = make_uint4(yw[0], yw[1], yw[2], yw[3]);
+          } else {
+            float* yr = (float*)a.drop_y + o + c;
+            *(float4*)yr = make_float4(v[0], v[1], v[2], v[3]);
+            *(float4*)(yr + 4) = make_float4(v[4], v[5], v[6], v[7]);
           }
         }
       }
