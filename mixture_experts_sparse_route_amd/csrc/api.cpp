@@ -231,9 +231,13 @@ moe_status check_routing(const moe_routing* r, bool need_logits, bool need_stats
 // drop_y non-null (first-come drops, one assignment per token, no shared
 // expert): the scatter also writes the dropped tokens' output rows (x or 0
 // when drop_x is null) and *drop_done says it did.
+// disp_xp non-null (same layers, bf16): the scatter also copies the kept
+// tokens' rows of x to the k-blocked xp (disp_rows rows per k-block), the
+// dispatch's work, under the same *drop_done.
 moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const void* x, const float* Wg,
                     const float* logit_bias, const float* sel_bias, const moe_routing& r, void* ws, hipStream_t st,
-                    void* drop_y = nullptr, const void* drop_x = nullptr, bool* drop_done = nullptr) {
+                    void* drop_y = nullptr, const void* drop_x = nullptr, bool* drop_done = nullptr,
+                    void* disp_xp = nullptr, int64_t disp_rows = 0) {
   if (drop_done) *drop_done = false;
   int32_t* blk_count = at<int32_t>(ws, L.blk_count);
   int32_t* blk_base = at<int32_t>(ws, L.blk_base);
@@ -316,6 +320,12 @@ moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const 
       sc.drop_x = (const uint16_t*)drop_x;
       sc.drop_y_bf16 = s.out_bf16;
       sc.drop_d = (int)s.d;
+      if (disp_xp) {
+        sc.disp_xp = (uint4*)disp_xp;
+        sc.disp_x = (const uint4*)x;
+        sc.disp_n_kb = (int)(s.d / 32);
+        sc.disp_blk_rows = disp_rows;
+      }
     }
     MOE_HIP(launch_route_scatter(sc, s.T, s.K, s.E, s.cap, st));
     if (drop_done) *drop_done = sc.drop_y != nullptr;
@@ -603,16 +613,18 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, co
   // the capacity scatter (first-come drops) or else by the combine
   const bool fused = s.bf16 && s.K == 1 && s.S == 0 && !s.ec;
   bool drop_done = false;
-  if ((st = do_route(cfg, s, L, x, Wg, logit_bias, sel_bias, rr, ws, hs, fused ? y : nullptr,
-                     residual ? x : nullptr, &drop_done)) != MOE_OK)
-    return st;
   void* xp = at<void>(ws, L.xp);
+  // on the fused path the scatter also does the dispatch (one row per kept token)
+  if ((st = do_route(cfg, s, L, x, Wg, logit_bias, sel_bias, rr, ws, hs, fused ? y : nullptr,
+                     residual ? x : nullptr, &drop_done, fused && s.max_rows > 0 ? xp : nullptr, s.max_rows)) != MOE_OK)
+    return st;
   float* yp = at<float>(ws, L.yp);
   const CombineFuse fuse{rr.row_src, rr.topk_w, residual ? x : nullptr, y, s.bf16, s.out_bf16};
   if (s.max_rows > 0) {
     // the fused path's xp is internal: k-blocked for bf16 (each k-step of a
     // GEMM1 tile then reads one contiguous run)
-    MOE_HIP(launch_dispatch(x, rr.row_src, rr.offsets + s.E, xp, s.max_rows, s.K, s.d * (int64_t)s.esz, s.bf16, hs));
+    if (!drop_done)
+      MOE_HIP(launch_dispatch(x, rr.row_src, rr.offsets + s.E, xp, s.max_rows, s.K, s.d * (int64_t)s.esz, s.bf16, hs));
     // an expert holds at most one row per token, and at most its capacity
     const int64_t group_max = s.cap >= 0 ? std::min(s.T, s.cap) : s.T;
     if ((st = do_ffn(s, xp, s.bf16, rr.offsets, s.E, s.max_rows, group_max, W1, W3, W2, sc.w1, sc.w3, sc.w2, at<void>(ws, L.h), yp,

@@ -95,6 +95,14 @@ struct RouteScatter {
   const uint16_t* drop_x;   // bf16 residual rows
   bool drop_y_bf16;         // y is bf16, else fp32
   int drop_d;               // row length (a multiple of 8)
+  // kFirstCome with one assignment per token: the kept tokens' rows of x
+  // (bf16, disp_n_kb 64-byte k-blocks each) are also copied to their rows of
+  // the k-blocked xp ([n_kb][disp_blk_rows][32]), the dispatch's output.
+  // disp_xp == nullptr: not copied.
+  uint4* disp_xp;
+  const uint4* disp_x;
+  int disp_n_kb;
+  int64_t disp_blk_rows;
 };
 hipError_t launch_route_scatter(const RouteScatter& r, int64_t T, int64_t K, int64_t E, int64_t cap, hipStream_t s);
 hipError_t launch_route_affinity(const uint64_t* seg, const int32_t* counts, const int32_t* dem_off,

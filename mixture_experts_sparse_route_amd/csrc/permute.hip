@@ -198,6 +198,7 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(const RouteScatter a
   __shared__ uint8_t ovf[MODE == kReroute1 ? kTopkTokens * 32 : 1];
   __shared__ int hist2[MODE == kReroute1 ? 1024 : 1];
   __shared__ uint8_t dropl[MODE == kFirstCome ? kTopkTokens : 1];  // K == 1: dropped tokens of the chunk
+  __shared__ int32_t keptd[MODE == kFirstCome ? kTopkTokens : 1];  // K == 1: their rows (kept tokens)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t f_begin = (int64_t)blockIdx.x * ct * K;
   const int64_t f_end = min((int64_t)T * K, f_begin + (int64_t)ct * K);
@@ -237,7 +238,10 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(const RouteScatter a
         a.dest[f] = d;
         a.dropped[f] = keep ? 0 : 1;
         if (keep) a.row_src[d] = (int32_t)f;
-        if (K == 1) dropl[f - f_begin] = keep ? 0 : 1;
+        if (K == 1) {
+          dropl[f - f_begin] = keep ? 0 : 1;
+          keptd[f - f_begin] = d;
+        }
       } else if constexpr (MODE == kAffinity) {
         if (valid && a.counts[e] > cap) {
           a.seg[a.dem_off[e] + pos] = affinity_key(a.aff[f], f);
@@ -270,6 +274,27 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(const RouteScatter a
     __syncthreads();
   }
   if constexpr (MODE == kFirstCome) {
+    if (a.disp_xp && K == 1) {
+      // one wave per kept token: its x row, k-block kb (64 bytes = 4 lanes)
+      // to row keptd of xp's k-block kb
+      const int n = (int)(f_end - f_begin), nkb = a.disp_n_kb;
+      const int64_t kb_stride = a.disp_blk_rows * 4;
+      const int c = lane & 3;
+      for (int i = wave; i < n; i += 4) {
+        if (dropl[i]) continue;
+        const uint4* src = a.disp_x + (f_begin + i) * (int64_t)nkb * 4 + c;
+        uint4* dst = a.disp_xp + (int64_t)keptd[i] * 4 + c;
+        for (int kb0 = 0; kb0 < nkb; kb0 += 32) {
+          // 32 k-blocks per pass: two loads per lane in flight before the stores
+          const int kb1 = kb0 + (lane >> 2), kb2 = kb1 + 16;
+          uint4 v1 = make_uint4(0, 0, 0, 0), v2 = v1;
+          if (kb1 < nkb) v1 = src[kb1 * 4];
+          if (kb2 < nkb) v2 = src[kb2 * 4];
+          if (kb1 < nkb) dst[kb1 * kb_stride] = v1;
+          if (kb2 < nkb) dst[kb2 * kb_stride] = v2;
+        }
+      }
+    }
     if (a.drop_y && K == 1) {
       // one wave per dropped token of the chunk (token t = assignment f),
       // 8 elements per lane and step (bf16 layers: d is a multiple of 64)
