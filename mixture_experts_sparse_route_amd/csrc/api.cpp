@@ -233,12 +233,16 @@ moe_status check_routing(const moe_routing* r, bool need_logits, bool need_stats
 // when drop_x is null) and *drop_done says it did.
 // disp_xp non-null (same layers, bf16): the scatter also copies the kept
 // tokens' rows of x to the k-blocked xp (disp_rows rows per k-block), the
-// dispatch's work, under the same *drop_done.
+// dispatch's work, under the same *drop_done.  tiles non-null: the scatter
+// that runs on the final offsets also writes those GEMM tile tables, and
+// *tiles_done says whether it did (expert-choice routing has no scatter).
 moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const void* x, const float* Wg,
                     const float* logit_bias, const float* sel_bias, const moe_routing& r, void* ws, hipStream_t st,
                     void* drop_y = nullptr, const void* drop_x = nullptr, bool* drop_done = nullptr,
-                    void* disp_xp = nullptr, int64_t disp_rows = 0) {
+                    void* disp_xp = nullptr, int64_t disp_rows = 0, const TileJob* tiles = nullptr,
+                    bool* tiles_done = nullptr) {
   if (drop_done) *drop_done = false;
+  if (tiles_done) *tiles_done = false;
   int32_t* blk_count = at<int32_t>(ws, L.blk_count);
   int32_t* blk_base = at<int32_t>(ws, L.blk_base);
   const bool topk_in = c->flags & MOE_F_TOPK_IN;
@@ -285,6 +289,7 @@ moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const 
   if (aff) {
     uint64_t* seg = at<uint64_t>(ws, L.seg);
     sc.mode = kAffinity;
+    if (tiles) sc.tiles = *tiles;
     sc.counts = r.counts;
     sc.dem_off = dem_off;
     sc.aff = r.topk_w;
@@ -307,6 +312,7 @@ moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const 
     MOE_HIP(launch_route_scan(blk_count2, blk_base2, at<int32_t>(ws, L.counts2), r.offsets, s.n_chunks, s.E, s.cap,
                               nullptr, nullptr, nullptr, s.T, s.K, r.counts, nullptr, st));
     sc.mode = kReroute2;
+    if (tiles) sc.tiles = *tiles;
     sc.idx = sc.cand;
     sc.blk_base = blk_base2;
     sc.first_counts = r.counts;
@@ -315,6 +321,7 @@ moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const 
     MOE_HIP(launch_route_scatter(sc, s.T, s.K, s.E, s.cap, st));
   } else {
     sc.mode = kFirstCome;
+    if (tiles) sc.tiles = *tiles;
     if (drop_y && s.K == 1 && s.S == 0 && s.bf16 && s.d % 8 == 0) {
       sc.drop_y = drop_y;
       sc.drop_x = (const uint16_t*)drop_x;
@@ -330,19 +337,23 @@ moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const 
     MOE_HIP(launch_route_scatter(sc, s.T, s.K, s.E, s.cap, st));
     if (drop_done) *drop_done = sc.drop_y != nullptr;
   }
+  if (tiles_done) *tiles_done = tiles != nullptr;
   return MOE_OK;
 }
 
 // s1 / s3 / s2: row scales of E4M3 weights (s.w8), else unused.
 // group_max: bound of any group's rows; a_blocked: A is k-blocked with
 // max_rows rows (the fused path's own dispatch output), else row-major.
+// plan_in: the plan (else computed here); tiles_ready: its tile tables are
+// already written (by the routing scatter).
 moe_status do_ffn(const Shape& s, const void* A, bool a_blocked, const int32_t* offsets, int64_t n_groups,
                   int64_t max_rows, int64_t group_max,
                   const void* W1, const void* W3, const void* W2, const float* s1, const float* s3, const float* s2,
                   void* h, float* yp, int4* tab_up, int4* tab_down, int32_t* counts, int64_t F, hipStream_t st,
-                  const CombineFuse* fuse = nullptr) {
-  const FfnPlan plan = ffn_plan(s.bf16, s.w8, max_rows, group_max, n_groups, F, s.d);
-  MOE_HIP(launch_ffn_tiles(plan, offsets, n_groups, max_rows, F, s.d, tab_up, tab_down, counts, st));
+                  const CombineFuse* fuse = nullptr, const FfnPlan* plan_in = nullptr, bool tiles_ready = false) {
+  const FfnPlan plan = plan_in ? *plan_in : ffn_plan(s.bf16, s.w8, max_rows, group_max, n_groups, F, s.d);
+  if (!tiles_ready)
+    MOE_HIP(launch_ffn_tiles(plan, offsets, n_groups, max_rows, F, s.d, tab_up, tab_down, counts, st));
   MOE_HIP(launch_gemm_gate_up(s.bf16, plan, A, a_blocked, tab_up, counts, n_groups, max_rows, W1, W3, s1, s3, h, F, s.d,
                               st));
   MOE_HIP(launch_gemm_down(s.bf16, plan, h, tab_down, counts + 1, n_groups, max_rows, W2, s2, yp, fuse, F, s.d, st));
@@ -614,9 +625,18 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, co
   const bool fused = s.bf16 && s.K == 1 && s.S == 0 && !s.ec;
   bool drop_done = false;
   void* xp = at<void>(ws, L.xp);
+  // the routed FFN's plan is known before routing: the scatter that runs on
+  // the final offsets writes its tile tables (one launch fewer); an expert
+  // holds at most one row per token, and at most its capacity
+  const int64_t group_max = s.cap >= 0 ? std::min(s.T, s.cap) : s.T;
+  const FfnPlan plan = ffn_plan(s.bf16, s.w8, s.max_rows, group_max, s.E, s.F, s.d);
+  const TileJob tj = tile_job(plan, s.F, s.d, at<int4>(ws, L.tab_up), at<int4>(ws, L.tab_down),
+                              at<int32_t>(ws, L.counts));
+  bool tiles_done = false;
   // on the fused path the scatter also does the dispatch (one row per kept token)
   if ((st = do_route(cfg, s, L, x, Wg, logit_bias, sel_bias, rr, ws, hs, fused ? y : nullptr,
-                     residual ? x : nullptr, &drop_done, fused && s.max_rows > 0 ? xp : nullptr, s.max_rows)) != MOE_OK)
+                     residual ? x : nullptr, &drop_done, fused && s.max_rows > 0 ? xp : nullptr, s.max_rows,
+                     s.max_rows > 0 ? &tj : nullptr, &tiles_done)) != MOE_OK)
     return st;
   float* yp = at<float>(ws, L.yp);
   const CombineFuse fuse{rr.row_src, rr.topk_w, residual ? x : nullptr, y, s.bf16, s.out_bf16};
@@ -625,11 +645,9 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, co
     // GEMM1 tile then reads one contiguous run)
     if (!drop_done)
       MOE_HIP(launch_dispatch(x, rr.row_src, rr.offsets + s.E, xp, s.max_rows, s.K, s.d * (int64_t)s.esz, s.bf16, hs));
-    // an expert holds at most one row per token, and at most its capacity
-    const int64_t group_max = s.cap >= 0 ? std::min(s.T, s.cap) : s.T;
     if ((st = do_ffn(s, xp, s.bf16, rr.offsets, s.E, s.max_rows, group_max, W1, W3, W2, sc.w1, sc.w3, sc.w2, at<void>(ws, L.h), yp,
                      at<int4>(ws, L.tab_up), at<int4>(ws, L.tab_down), at<int32_t>(ws, L.counts), s.F, hs,
-                     fused ? &fuse : nullptr)) != MOE_OK)
+                     fused ? &fuse : nullptr, &plan, tiles_done)) != MOE_OK)
       return st;
   }
   if (s.S && !sd && (st = shared_ffn(hs)) != MOE_OK) return st;

@@ -61,6 +61,16 @@ hipError_t launch_route_scan(const int32_t* blk_count, int32_t* blk_base, int32_
                              double* stats, int64_t T, int64_t K, const int32_t* first_counts, int32_t* dem_off,
                              hipStream_t s);
 
+// Tile tables of one FFN's two GEMMs (as launch_ffn_tiles writes them), for
+// a routing kernel to write once the final offsets exist.  tab_up ==
+// nullptr: none.
+struct TileJob {
+  int bm_up, nt_up, bn_up, bm_down, nt_down, bn_down;
+  int4* tab_up;
+  int4* tab_down;
+  int32_t* counts;
+};
+
 // Capacity drop policy of the scatter (kernel comments give each mode).
 enum ScatterMode { kFirstCome = 0, kAffinity = 1, kReroute1 = 2, kReroute2 = 3 };
 
@@ -103,6 +113,9 @@ struct RouteScatter {
   const uint4* disp_x;
   int disp_n_kb;
   int64_t disp_blk_rows;
+  // a scatter that runs on the final offsets (kFirstCome, kAffinity,
+  // kReroute2) may also write the GEMM tile tables
+  TileJob tiles;
 };
 hipError_t launch_route_scatter(const RouteScatter& r, int64_t T, int64_t K, int64_t E, int64_t cap, hipStream_t s);
 hipError_t launch_route_affinity(const uint64_t* seg, const int32_t* counts, const int32_t* dem_off,
@@ -155,6 +168,8 @@ int64_t ffn_table_entries(bool bf16, int64_t max_rows, int64_t n_groups, int64_t
 // Builds both GEMMs' tile tables (int4 {group, first row, rows, first column};
 // m-tiles of p.bm rows for gate_up, p.bm_down for down)
 // and their entry counts counts[0] (gate_up) and counts[1] (down).
+// The tile-table job of plan p (F: GEMM1 output columns, d: GEMM2's).
+TileJob tile_job(const FfnPlan& p, int64_t F, int64_t d, int4* tab_up, int4* tab_down, int32_t* counts);
 hipError_t launch_ffn_tiles(const FfnPlan& p, const int32_t* offsets, int64_t n_groups, int64_t max_rows, int64_t F,
                             int64_t d, int4* tab_up, int4* tab_down, int32_t* counts, hipStream_t s);
 // Combine fused into GEMM2 for one assignment per token (K == 1, no shared

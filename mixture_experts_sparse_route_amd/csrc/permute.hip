@@ -190,6 +190,80 @@ __device__ __forceinline__ uint64_t affinity_key(float a, int64_t f) {
   return ((uint64_t)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)f);
 }
 
+// The GEMM tile tables (the entries ffn_tiles_kernel writes) from the final
+// offsets, by a grid of 256-thread workgroups: every workgroup scans the
+// m-tile counts of the G <= 1024 groups in LDS (thread t owns groups 4t ..
+// 4t+3), then one wave per group writes that group's contiguous range of
+// entries [mstart[g] * nt, mstart[g+1] * nt) with coalesced stores.
+__device__ void scatter_tiles(const int32_t* __restrict__ offsets, int G, const TileJob& j) {
+  __shared__ int mst[2][1025];
+  __shared__ int2 wtot[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int2 m[4];
+  int2 tot = make_int2(0, 0);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int g = 4 * tid + u;
+    const int rows = g < G ? offsets[g + 1] - offsets[g] : 0;
+    m[u] = rows > 0 ? make_int2((rows + j.bm_up - 1) / j.bm_up, (rows + j.bm_down - 1) / j.bm_down) : make_int2(0, 0);
+    tot.x += m[u].x;
+    tot.y += m[u].y;
+  }
+  // inclusive scan of the per-thread totals: within the wave, then over waves
+  int2 v = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int ux = __shfl_up(v.x, o), uy = __shfl_up(v.y, o);
+    if (lane >= o) {
+      v.x += ux;
+      v.y += uy;
+    }
+  }
+  if (lane == 63) wtot[wave] = v;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) {
+    v.x += wtot[w].x;
+    v.y += wtot[w].y;
+  }
+  int2 run = make_int2(v.x - tot.x, v.y - tot.y);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int g = 4 * tid + u;
+    if (g < G) {
+      mst[0][g] = run.x;
+      mst[1][g] = run.y;
+    }
+    run.x += m[u].x;
+    run.y += m[u].y;
+  }
+  if (tid == 255) {  // threads past G add nothing: the last inclusive value is the total
+    mst[0][G] = v.x;
+    mst[1][G] = v.y;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0 && tid == 0) {
+    j.counts[0] = mst[0][G] * j.nt_up;
+    j.counts[1] = mst[1][G] * j.nt_down;
+  }
+  for (int pass = 0; pass < 2; ++pass) {
+    const int nt = pass == 0 ? j.nt_up : j.nt_down;
+    const int bn = pass == 0 ? j.bn_up : j.bn_down;
+    const int bm = pass == 0 ? j.bm_up : j.bm_down;
+    const int* ms = mst[pass];
+    int4* tab = pass == 0 ? j.tab_up : j.tab_down;
+    for (int gg = blockIdx.x * 4 + wave; gg < G; gg += gridDim.x * 4) {
+      const int mtiles = ms[gg + 1] - ms[gg];
+      const int cnt = mtiles * nt, base = ms[gg] * nt;
+      const int g0 = offsets[gg], g1 = offsets[gg + 1];
+      for (int r = lane; r < cnt; r += 64) {
+        const int n = r / mtiles, mm = r % mtiles;
+        const int row0 = g0 + mm * bm;
+        tab[base + r] = make_int4(gg, row0, min(bm, g1 - row0), n * bn);
+      }
+    }
+  }
+}
+
 template <int MODE>
 __global__ __launch_bounds__(256) void route_scatter_kernel(const RouteScatter a, const int T, const int K,
                                                             const int E, const int nbits, const int cap, const int ct) {
@@ -329,6 +403,9 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(const RouteScatter a
         }
       }
     }
+  }
+  if constexpr (MODE != kReroute1) {
+    if (a.tiles.tab_up) scatter_tiles(a.offsets, E, a.tiles);
   }
   if constexpr (MODE == kReroute1) {
     // the j-th overflowing choice of token t (in k order) is offered to the
@@ -586,6 +663,20 @@ hipError_t launch_dispatch(const void* x, const int32_t* row_src, const int32_t*
                                                  (int)(row_bytes / 2), rpb);
   prof_end(K_DISPATCH, s);
   return hipGetLastError();
+}
+
+TileJob tile_job(const FfnPlan& p, int64_t F, int64_t d, int4* tab_up, int4* tab_down, int32_t* counts) {
+  TileJob j{};
+  j.bm_up = p.bm;
+  j.nt_up = (int)((F + p.bn_out_up - 1) / p.bn_out_up);
+  j.bn_up = p.bn_out_up;
+  j.bm_down = p.bm_down;
+  j.nt_down = (int)((d + p.bn_out_down - 1) / p.bn_out_down);
+  j.bn_down = p.bn_out_down;
+  j.tab_up = tab_up;
+  j.tab_down = tab_down;
+  j.counts = counts;
+  return j;
 }
 
 hipError_t launch_ffn_tiles(const FfnPlan& p, const int32_t* offsets, int64_t n_groups, int64_t max_rows, int64_t F,
