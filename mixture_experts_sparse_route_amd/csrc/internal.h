@@ -66,6 +66,7 @@ hipError_t launch_route_scan(const int32_t* blk_count, int32_t* blk_base, int32_
 // nullptr: none.
 struct TileJob {
   int bm_up, nt_up, bn_up, bm_down, nt_down, bn_down;
+  int even_up;  // GEMM1 m-tiles split evenly (FfnPlan::even_up)
   int4* tab_up;
   int4* tab_down;
   int32_t* counts;
@@ -146,6 +147,10 @@ struct FfnPlan {
   int bm_down;      // rows per m-tile of GEMM2 (bm: GEMM1)
   bool k64_up;      // GEMM1 in stages of 64 k (else 32)
   bool k64_down;    // GEMM2 in stages of 64 k (else 32)
+  // GEMM1 m-tiles of a group split evenly in 32-row units instead of full
+  // bm-row tiles and a remainder, so the m-tiles that share a weight tile
+  // stay in step (MFMA-bound groups of 512 rows or more on average)
+  bool even_up = false;
 };
 // Compute units of the current device (queried once).
 int device_cus();

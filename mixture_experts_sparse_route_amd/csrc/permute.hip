@@ -190,6 +190,27 @@ __device__ __forceinline__ uint64_t affinity_key(float a, int64_t f) {
   return ((uint64_t)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)f);
 }
 
+// Rows of m-tile mm of a group of `rows` rows that is cut into `mtiles`
+// tiles of at most bm rows (mtiles = ceil(rows / bm), bm a multiple of 32):
+// the group's 32-row units (one 16-row MFMA block for each of a tile's two
+// M-waves) are dealt out as evenly as possible (the first u % mtiles tiles
+// take one unit more), so the m-tiles of one weight tile take about equally
+// long and stay in step through k, sharing the weight tile's k-slices in L2.
+// u / mtiles <= bm / 32, so no tile exceeds bm rows; every tile holds at
+// least one unit, and only the last can be part-filled.
+// Returns {first row relative to the group, rows}.
+__device__ __forceinline__ int2 mtile_span(int rows, int mtiles, int mm) {
+  const int u = (rows + 31) >> 5;
+  const int q = u / mtiles, extra = u % mtiles;
+  const int r0 = 32 * (mm * q + min(mm, extra));
+  return make_int2(r0, min(32 * (q + (mm < extra ? 1 : 0)), rows - r0));
+}
+
+// m-tile mm of a group: evenly split (mtile_span) or bm rows from row mm * bm
+__device__ __forceinline__ int2 mtile_rows(int rows, int mtiles, int mm, int bm, bool even) {
+  return even ? mtile_span(rows, mtiles, mm) : make_int2(mm * bm, min(bm, rows - mm * bm));
+}
+
 // The GEMM tile tables (the entries ffn_tiles_kernel writes) from the final
 // offsets, by a grid of 256-thread workgroups: every workgroup scans the
 // m-tile counts of the G <= 1024 groups in LDS (thread t owns groups 4t ..
@@ -249,6 +270,7 @@ __device__ void scatter_tiles(const int32_t* __restrict__ offsets, int G, const 
     const int nt = pass == 0 ? j.nt_up : j.nt_down;
     const int bn = pass == 0 ? j.bn_up : j.bn_down;
     const int bm = pass == 0 ? j.bm_up : j.bm_down;
+    const bool even = pass == 0 && j.even_up;
     const int* ms = mst[pass];
     int4* tab = pass == 0 ? j.tab_up : j.tab_down;
     for (int gg = blockIdx.x * 4 + wave; gg < G; gg += gridDim.x * 4) {
@@ -257,8 +279,8 @@ __device__ void scatter_tiles(const int32_t* __restrict__ offsets, int G, const 
       const int g0 = offsets[gg], g1 = offsets[gg + 1];
       for (int r = lane; r < cnt; r += 64) {
         const int n = r / mtiles, mm = r % mtiles;
-        const int row0 = g0 + mm * bm;
-        tab[base + r] = make_int4(gg, row0, min(bm, g1 - row0), n * bn);
+        const int2 sp = mtile_rows(g1 - g0, mtiles, mm, bm, even);
+        tab[base + r] = make_int4(gg, g0 + sp.x, sp.y, n * bn);
       }
     }
   }
@@ -523,14 +545,15 @@ __global__ __launch_bounds__(256) void dispatch_blocked_kernel(const uint4* __re
 // ------------------------------------------------------------ FFN tiles
 // Tile list of both expert GEMMs (each workgroup scans the m-tile counts and
 // writes its share of the entries): for group g with rows(g) rows,
-// ceil(rows(g) / bm) m-tiles (bm of that GEMM) times its n-tiles, in the order
+// ceil(rows(g) / bm) m-tiles (bm of that GEMM; GEMM1's split by mtile_span
+// when even_up is set) times its n-tiles, in the order
 // (group, n-tile, m-tile) with the m-tile fastest, so the m-tiles of one
 // weight tile are neighbours.  Entry L = {group, first row, rows, first
 // column}; counts[0] / counts[1] = entries of the gate_up / down tables.
 __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t* __restrict__ offsets, int G, int bm_up,
                                                          int nt_up, int bn_up, int bm_down, int nt_down, int bn_down,
-                                                         int4* __restrict__ tab_up, int4* __restrict__ tab_down,
-                                                         int32_t* __restrict__ counts) {
+                                                         int even_up, int4* __restrict__ tab_up,
+                                                         int4* __restrict__ tab_down, int32_t* __restrict__ counts) {
   __shared__ int mstart[2][1025];  // exclusive scans of m-tiles per group (G <= 1024), per GEMM
   __shared__ int2 wsum[16];
   const int g = threadIdx.x, lane = g & 63, wave = g >> 6;
@@ -573,6 +596,7 @@ __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t* __restri
     const int bn = pass == 0 ? bn_up : bn_down;
     const int tot = pass == 0 ? tot_up : tot_down;
     const int bm = pass == 0 ? bm_up : bm_down;
+    const bool even = pass == 0 && even_up;
     const int* ms = mstart[pass];
     int4* tab = pass == 0 ? tab_up : tab_down;
     for (int L = blockIdx.x * 1024 + threadIdx.x; L < tot; L += gridDim.x * 1024) {
@@ -585,8 +609,8 @@ __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t* __restri
       const int mtiles = ms[lo + 1] - ms[lo];
       const int r = L - ms[lo] * nt;
       const int n = r / mtiles, m = r % mtiles;
-      const int row0 = offsets[lo] + m * bm;
-      tab[L] = make_int4(lo, row0, min(bm, offsets[lo + 1] - row0), n * bn);
+      const int2 sp = mtile_rows(offsets[lo + 1] - offsets[lo], mtiles, m, bm, even);
+      tab[L] = make_int4(lo, offsets[lo] + sp.x, sp.y, n * bn);
     }
   }
 }
@@ -673,6 +697,7 @@ TileJob tile_job(const FfnPlan& p, int64_t F, int64_t d, int4* tab_up, int4* tab
   j.bm_down = p.bm_down;
   j.nt_down = (int)((d + p.bn_out_down - 1) / p.bn_out_down);
   j.bn_down = p.bn_out_down;
+  j.even_up = p.even_up ? 1 : 0;
   j.tab_up = tab_up;
   j.tab_down = tab_down;
   j.counts = counts;
@@ -689,7 +714,7 @@ hipError_t launch_ffn_tiles(const FfnPlan& p, const int32_t* offsets, int64_t n_
   const unsigned grid = (unsigned)std::min<int64_t>(32, std::max<int64_t>(1, (most + 1023) / 1024));
   prof_begin(K_FFN_TILES, s);
   ffn_tiles_kernel<<<grid, 1024, 0, s>>>(offsets, (int)n_groups, p.bm, nt_up, p.bn_out_up, p.bm_down, nt_down,
-                                         p.bn_out_down, tab_up, tab_down, counts);
+                                         p.bn_out_down, p.even_up ? 1 : 0, tab_up, tab_down, counts);
   prof_end(K_FFN_TILES, s);
   return hipGetLastError();
 }

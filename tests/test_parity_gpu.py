@@ -143,6 +143,16 @@ def test_small_case(name):
     print(name, rep)
 
 
+# GEMM1's m-tiles split evenly in 32-row units (the plan does so when groups
+# average 512 rows or more); forced here on groups that the even split cuts
+# differently from full tiles plus a remainder (275 rows: 160 + 115 instead of
+# 192 + 83; 160 rows: 96 + 64 instead of 128 + 32)
+@pytest.mark.parametrize("name", ["mixtral_two_mtiles", "switch_capacity_160", "deepseek_small"])
+def test_even_m_tiles(name, monkeypatch):
+    monkeypatch.setenv("MOE_GEMM_EVEN_UP", "1")
+    print(name, check_case(Case(SMALL[name])))
+
+
 def test_residual_pass_through_with_capacity():
     rep = check_case(Case(SMALL["switch_capacity_small"]), residual=True)
     print(rep)
@@ -219,6 +229,12 @@ def test_entry_points_in_isolation():
     ref_c = oracle.combine(oracle.layer_of(wl), ypr, orc["w"].astype(np.float32).astype(np.float64), orc["dest"])
     # fp32 accumulation of K terms in the same order: a few fp32 ulps
     assert np.max(np.abs(host_f64(y) - ref_c) / np.maximum(np.abs(ref_c), np.sqrt(np.mean(ref_c ** 2)))) <= 1e-5
+
+
+def test_entry_points_in_isolation_even_m_tiles(monkeypatch):
+    """The same, with moe_expert_ffn's GEMM1 m-tiles split evenly."""
+    monkeypatch.setenv("MOE_GEMM_EVEN_UP", "1")
+    test_entry_points_in_isolation()
 
 
 # -------------------------------------------------------- full-size cases --
