@@ -126,7 +126,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+        print(f"bench.py: the layer runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
               "expert parallelism across GPUs is not part of it.", file=sys.stderr)
         sys.exit(2)
 

@@ -51,7 +51,7 @@ typedef struct ihipStream_t* moe_stream_t;
 typedef enum moe_status {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1, /* a size, pointer or enum is out of range */
-  MOE_ERR_UNSUPPORTED = 2, /* valid, but this build does not implement it */
+  MOE_ERR_UNSUPPORTED = 2, /* valid, but this library does not implement it */
   MOE_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than moe_workspace_size */
   MOE_ERR_HIP = 4          /* a HIP launch or runtime call failed */
 } moe_status;
