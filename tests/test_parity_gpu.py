@@ -169,6 +169,32 @@ def test_everything_dropped():
     assert torch.equal(y2.view(torch.int16), case.d["x"].view(torch.int16))
 
 
+# Exact ties: logits on a coarse grid (a handful of values, +0.0 and -0.0
+# among them) given to both sides; equal keys go to the lower expert and -0.0
+# equals +0.0, so indices, weights, counts, offsets, dest and the outputs are
+# fixed exactly (no near-tie exclusions).
+@pytest.mark.parametrize("name,wl", [
+    ("softmax_top2", workload("mixtral_prefill", T=300, d=128, F=64)),
+    ("switch_capacity", workload("switch_top1_capacity", T=500, d=128, F=64, E=16, logit_bias=None)),
+    ("sigmoid_top8", workload("deepseek_v3_fine", T=200, d=128, F=64, E=64, Fs=64, sel_bias=None)),
+])
+def test_exact_ties(name, wl):
+    case = Case(wl)
+    r = np.random.default_rng(7)
+    lg = (r.integers(-2, 3, size=(wl.T, wl.E)) * 0.5).astype(np.float32)
+    lg[lg == 0] = np.where(r.random(int((lg == 0).sum())) < 0.5, np.float32(-0.0), np.float32(0.0))
+    assert np.signbit(lg[lg == 0]).any() and (~np.signbit(lg[lg == 0])).any()
+    orc = oracle.route(case.L, None, None, sel_bias=case.h["sel_bias"], lg=lg)
+    y, rr = case.gpu_forward(logits_in=lg, out_dtype="f32")
+    g = routing_host(rr)
+    assert np.array_equal(g["idx"], orc["idx"]), "tied keys resolved differently"
+    assert_weights_close(g["w"], orc["w"], name)
+    assert_permutation_equal(g, orc, name)
+    live = kept_tokens(orc["dest"], wl.K, wl.n_shared)
+    y_ref = case.oracle_y(orc["idx"], orc["w"], orc["dest"])
+    print(name, assert_y_close(host_f64(y), y_ref, wl.dtype, rows=live, label=name))
+
+
 def test_single_token():
     rep = check_case(Case(workload("deepseek_v3_fine", T=1, d=256, F=128, E=16, K=3, Fs=128)))
     print(rep)
