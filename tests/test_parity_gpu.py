@@ -195,6 +195,29 @@ def test_exact_ties(name, wl):
     print(name, assert_y_close(host_f64(y), y_ref, wl.dtype, rows=live, label=name))
 
 
+# Logits far outside exp's fp32 range (|l| up to 3000): the softmax weights
+# must come from max-shifted exponentials on both sides (no inf / NaN).
+@pytest.mark.parametrize("name,wl", [
+    ("softmax_top2_renorm", workload("mixtral_prefill", T=300, d=128, F=64)),
+    ("switch_raw", workload("switch_top1_capacity", T=500, d=128, F=64, E=16, logit_bias=None)),
+])
+def test_extreme_logits(name, wl):
+    case = Case(wl)
+    r = np.random.default_rng(11)
+    lg = r.uniform(-3000.0, 3000.0, size=(wl.T, wl.E)).astype(np.float32)
+    lg[::7] *= np.float32(1e-3)  # some tokens with ordinary logits
+    orc = oracle.route(case.L, None, None, sel_bias=case.h["sel_bias"], lg=lg)
+    y, rr = case.gpu_forward(logits_in=lg, out_dtype="f32")
+    g = routing_host(rr)
+    assert np.all(np.isfinite(g["w"])) and np.all(np.isfinite(host_f64(y)))
+    assert np.array_equal(g["idx"], orc["idx"])
+    assert_weights_close(g["w"], orc["w"], name)
+    assert_permutation_equal(g, orc, name)
+    live = kept_tokens(orc["dest"], wl.K, wl.n_shared)
+    y_ref = case.oracle_y(orc["idx"], orc["w"], orc["dest"])
+    print(name, assert_y_close(host_f64(y), y_ref, wl.dtype, rows=live, label=name))
+
+
 def test_single_token():
     rep = check_case(Case(workload("deepseek_v3_fine", T=1, d=256, F=128, E=16, K=3, Fs=128)))
     print(rep)
