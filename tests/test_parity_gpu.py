@@ -218,6 +218,25 @@ def test_extreme_logits(name, wl):
     print(name, assert_y_close(host_f64(y), y_ref, wl.dtype, rows=live, label=name))
 
 
+# Tile plans (shapes, stage widths, persistent grids, even m-tiles) leave
+# every output bit unchanged: each output sums its k-steps in k order.
+PLAN_OVERRIDES = {
+    "even_m_tiles": {"MOE_GEMM_EVEN_UP": "1"},
+    "k32_128x256": {"MOE_GEMM_K64": "0", "MOE_GEMM_BM": "128", "MOE_GEMM_BNB_UP": "256", "MOE_GEMM_NS_UP": "3"},
+    "persistent": {"MOE_GEMM_WGS": "1"},
+}
+
+
+@pytest.mark.parametrize("over", list(PLAN_OVERRIDES))
+def test_plan_overrides_bitwise_identical(over, monkeypatch):
+    case = Case(SMALL["mixtral_two_mtiles"])
+    y0, _ = case.gpu_forward(out_dtype="f32")
+    for k, v in PLAN_OVERRIDES[over].items():
+        monkeypatch.setenv(k, v)
+    y1, _ = case.gpu_forward(out_dtype="f32")
+    assert torch.equal(y0.view(torch.int32), y1.view(torch.int32)), f"plan override {over} changed the output"
+
+
 def test_single_token():
     rep = check_case(Case(workload("deepseek_v3_fine", T=1, d=256, F=128, E=16, K=3, Fs=128)))
     print(rep)
