@@ -248,3 +248,15 @@ def test_misaligned_arrays_are_rejected_without_launching(lib):
     assert lib.moe_forward(ctypes.byref(c), 256, 256, None, None, 256, 256 + 8, 256, None, None, None, None, 256, None,
                            256, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
     assert b"16-byte aligned" in lib.moe_last_error()
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; asked for several it exits with status 2
+    and says so, before touching a device."""
+    import subprocess
+    import sys
+    for args, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "4"})):
+        p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], capture_output=True, text=True,
+                           timeout=120, env={**os.environ, **env}, cwd=ROOT)
+        assert p.returncode == 2, (args, env, p.returncode, p.stderr[-500:])
+        assert "one GPU only" in p.stderr and p.stdout == ""
