@@ -91,15 +91,16 @@ def _p(a):
 
 
 def layer(T, d, F, E, K, gate=GATE_SOFTMAX, renorm=True, residual=False, bf16=False, capacity_factor=0.0,
-          n_shared=0, Fs=0, round_h=None, w_fp8=False) -> OrcLayer:
-    """round_h: store the SwiGLU output h in bf16 (default: for bf16 layers).
+          n_shared=0, Fs=0, round_h=False, w_fp8=False) -> OrcLayer:
+    """round_h: False (the definition) keeps the SwiGLU output h in double;
+    True stores it in bf16 (ties to even) before the down projection, as a
+    bf16 kernel does -- a tighter second reference, never the definition.
     w_fp8: expert weights are FP8 E4M3 codes with per-row scales."""
-    rh = bf16 if round_h is None else round_h
     return OrcLayer(T, d, F, E, K, gate, int(renorm), int(residual), int(bf16), float(capacity_factor),
-                    n_shared, Fs, int(rh), int(w_fp8))
+                    n_shared, Fs, int(bool(round_h)), int(w_fp8))
 
 
-def layer_of(wl, residual=False, round_h=None) -> OrcLayer:
+def layer_of(wl, residual=False, round_h=False) -> OrcLayer:
     """OrcLayer for a ``moe_synth`` workload."""
     return layer(wl.T, wl.d, wl.F, wl.E, wl.K, gate=wl.gate, renorm=wl.renorm, residual=residual,
                  bf16=(wl.dtype == "bf16"), capacity_factor=wl.capacity_factor, n_shared=wl.n_shared, Fs=wl.Fs,

@@ -299,10 +299,12 @@ void orc_permute_reroute(const orc_layer* L, const int32_t* idx, const double* w
    * their new expert has left after the first pass */
   for (int64_t f = 0; f < N; ++f)
     if (cand[f] >= 0) pos[f] = second[cand[f]]++;
+  /* with no capacity limit nothing overflows and nothing is re-routed: the
+   * result is the first-come permutation */
   offsets[0] = 0;
   for (int64_t e = 0; e < E; ++e) {
-    int64_t room = cap - first[e];
-    int64_t extra = second[e] < room ? second[e] : room;
+    const int64_t room = cap < 0 ? 0 : cap - first[e];
+    const int64_t extra = second[e] < room ? second[e] : room;
     offsets[e + 1] = offsets[e] + (int32_t)(first[e] + extra);
   }
   /* rows of an expert: its first-pass assignments, then its re-routed ones,

@@ -54,9 +54,10 @@ typedef struct orc_layer {
   double capacity_factor; /* <= 0: no capacity limit */
   int64_t n_shared; /* always-active shared experts */
   int64_t Fs;       /* shared expert d_ff */
-  /* 1: the SwiGLU output h is stored in bf16 (rounded to nearest even) before
-   * the down projection, as a bf16 layer stores its activations; 0: h stays
-   * in double */
+  /* 0 (the definition): h stays in double.  1: the SwiGLU output h is
+   * stored in bf16 (rounded to nearest even) before the down projection, the
+   * way a bf16 layer stores its activations; a tighter second reference for
+   * kernels that do so, never the definition */
   int32_t round_h;
   /* 1: the expert weights (routed and shared) are OCP FP8 E4M3 codes, each
    * row with an fp32 scale (weight = decoded code * scale of its row); x

@@ -682,6 +682,24 @@ def test_reroute_invariants_and_special_cases():
         assert np.array_equal(a[k], b[k]), k
 
 
+def test_reroute_without_capacity_is_first_come():
+    """With no capacity limit (capacity factor <= 0) nothing overflows, so
+    re-routing moves nothing: the routing equals the first-come one [LN
+    §3.2 re-routes only an expert's excess over its capacity], with offsets
+    the exclusive scan of the demand and every assignment kept."""
+    r = rng(25)
+    for T, E, K, cf in ((6, 3, 1, 0.0), (300, 8, 2, 0.0), (120, 16, 3, -1.0), (64, 4, 4, 0.0)):
+        L = oracle.layer(T, 4, 4, E, K, renorm=(K > 1), capacity_factor=cf)
+        assert oracle.capacity(L) == -1
+        lg = r.standard_normal((T, E)).astype(np.float32)
+        a, b = oracle.route(L, None, None, policy="reroute", lg=lg), oracle.route(L, None, None, lg=lg)
+        for k in ("idx", "w", "counts", "offsets", "dest", "row_src", "dropped"):
+            assert np.array_equal(a[k], b[k]), (T, E, K, k)
+        assert np.array_equal(a["offsets"], np.concatenate([[0], np.cumsum(np.bincount(b["idx"].reshape(-1),
+                                                                                          minlength=E))]))
+        assert not a["dropped"].any() and np.array_equal(np.sort(a["dest"]), np.arange(T * K))
+
+
 def test_expert_choice_route_and_forward():
     """Expert choice in the K = E form: every expert holds exactly cap rows,
     rows list the chosen tokens in ascending order, and the layer output
