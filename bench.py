@@ -2,14 +2,29 @@
 """Benchmark of one sparse-MoE FFN layer forward on one MI355X.
 
 A step is one whole-layer forward (router logits, gate, Top-K, histogram /
-capacity / permutation, dispatch, grouped SwiGLU experts, combine) through
-``moe_forward`` of the C-ABI library, on seeded synthetic inputs already
-resident in HBM.  Default workload: Switch-style top-1 with capacity factor
-1.25 (T=8192, d_model=1024, 64 experts, d_ff=4096, bf16, fp32 router).
+capacity / permutation, dispatch, grouped SwiGLU experts, shared expert,
+combine) through ``moe_forward`` of the C-ABI library, on seeded synthetic
+inputs already resident in HBM.  Default workload: the largest one, a
+DeepSeek-V3-style fine-grained layer (T=4096, d_model=7168, 256 routed
+experts of d_ff=2048, sigmoid gate with a selection bias, Top-8
+renormalised, one shared expert of d_ff=2048, bf16, fp32 router).
 
 Prints one JSON line: tokens/s, the dominant kernel's roofline position
-(measured with HIP events on the launch stream inside the timed region), and
-the CPU oracle timed on a bounded sample of the same workload.
+(measured with HIP events on the launch stream inside the timed region), the
+whole layer's flops and bytes rates, and the CPU oracle timed on a bounded
+sample of the same workload.
+
+Byte and flop accounting (per launch):
+  algorithmic  what the method must move: a grouped-GEMM launch reads the
+               weights of every expert it touches once (W1 and W3 for GEMM1,
+               W2 for GEMM2; E4M3 row scales included), 2*R*d*F flops per
+               weight matrix for R rows.  The layer: router 2*T*d*E, experts
+               6*d*F per kept row, shared expert 6*d*Fs per token; bytes: the
+               touched experts' and the shared expert's weights, x, y, W_g.
+  implementation  what this implementation moves besides: the dispatched rows
+               read by GEMM1, h written by GEMM1 and read by GEMM2, the fp32
+               expert rows written by GEMM2 (reported separately, never in
+               the roofline).
 """
 from __future__ import annotations
 
@@ -29,7 +44,7 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3     # MI355X fp32
 RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-DEFAULT_WORKLOAD = "switch_top1_capacity"
+DEFAULT_WORKLOAD = "deepseek_v3_fine"
 EVENT_EVERY = 4               # the dominant kernel is event-timed in the last step of every 4
 
 
@@ -50,19 +65,21 @@ def parse():
     return ap.parse_args()
 
 
-def source_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+GEMM_SOURCES = ("gemm_bf16.h", "gemm_bf16_up.hip", "gemm_bf16.hip")
+
+
+def gemm_source_hash() -> str:
+    """sha256[:16] of the grouped-GEMM kernel and launcher sources."""
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "mixture_experts_sparse_route_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def kernel_accounting(wl, R: int, touched: int):
-    """Algorithmic flops and bytes per launch of each kernel of one step.
-
-    gemm_gate_up: reads W1, W3 of every touched expert once, the R dispatched
-    rows, writes h; 4 d F flops per row.  gemm_down: reads W2 of every touched
-    expert, h; writes fp32 rows; 2 d F flops per row.  The shared expert, when
-    present, is one more launch of each with T rows.
-    """
+    """Algorithmic flops and bytes per launch of each GEMM of one step, and
+    the implementation bytes beside them (see the module docstring)."""
     esz = 2 if wl.dtype == "bf16" else 4           # activations
     fp8 = wl.wdtype == "fp8"
     wsz = 1 if fp8 else esz                         # expert weights
@@ -70,20 +87,32 @@ def kernel_accounting(wl, R: int, touched: int):
     sc_up = 2.0 * F * 4 if fp8 else 0.0             # fp32 row scales of W1, W3
     sc_dn = d * 4.0 if fp8 else 0.0                 # of W2
     acc = {
-        "gemm_gate_up": dict(flops=4.0 * d * F * R,
-                             bytes=touched * (2.0 * F * d * wsz + sc_up) + R * d * esz + R * F * esz),
-        "gemm_down": dict(flops=2.0 * d * F * R, bytes=touched * (1.0 * F * d * wsz + sc_dn) + R * F * esz + R * d * 4.0),
+        "gemm_gate_up": dict(flops=4.0 * d * F * R, bytes=touched * (2.0 * F * d * wsz + sc_up),
+                             impl_bytes=R * d * esz + R * F * esz),
+        "gemm_down": dict(flops=2.0 * d * F * R, bytes=touched * (1.0 * F * d * wsz + sc_dn),
+                          impl_bytes=R * F * esz + R * d * 4.0),
     }
     if wl.n_shared:
         Fs, T = wl.Fs, wl.T
-        acc["gemm_gate_up"]["flops_shared"] = 4.0 * d * Fs * T
-        acc["gemm_gate_up"]["bytes_shared"] = 2.0 * Fs * d * wsz + T * d * esz + T * Fs * esz
-        acc["gemm_down"]["flops_shared"] = 2.0 * d * Fs * T
-        acc["gemm_down"]["bytes_shared"] = 1.0 * Fs * d * wsz + T * Fs * esz + T * d * 4.0
+        acc["shared_gate_up"] = dict(flops=4.0 * d * Fs * T, bytes=2.0 * Fs * d * wsz + (2.0 * Fs * 4 if fp8 else 0.0),
+                                     impl_bytes=T * d * esz + T * Fs * esz)
+        acc["shared_down"] = dict(flops=2.0 * d * Fs * T, bytes=1.0 * Fs * d * wsz + sc_dn,
+                                  impl_bytes=T * Fs * esz + T * d * 4.0)
     layer_flops = 6.0 * d * F * R + 2.0 * wl.T * d * wl.E + (6.0 * d * wl.Fs * wl.T if wl.n_shared else 0.0)
-    layer_bytes = (touched * 3.0 * F * d * wsz + (3.0 * wl.Fs * d * wsz if wl.n_shared else 0.0)
+    layer_bytes = (touched * (3.0 * F * d * wsz + sc_up + sc_dn)
+                   + ((3.0 * wl.Fs * d * wsz + (2.0 * wl.Fs * 4 + d * 4.0 if fp8 else 0.0)) if wl.n_shared else 0.0)
                    + 2.0 * wl.T * d * esz + wl.E * d * 4.0)
     return acc, layer_flops, layer_bytes
+
+
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(wl, h, budget_s: float, policy: str = "first_come", expert_choice: bool = False):
@@ -117,6 +146,7 @@ def cpu_baseline(wl, h, budget_s: float, policy: str = "first_come", expert_choi
         done += len(toks)
     t_layer = t_route + t_rows * wl.T / done
     return {"value": wl.T / t_layer, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"routing of all {wl.T} tokens ({t_route:.2f} s) + experts and combine for the first "
                       f"{done} tokens ({t_rows:.2f} s), extrapolated to {wl.T} tokens",
             "seconds_measured": round(t_route + t_rows, 2)}
@@ -214,12 +244,9 @@ def main():
     acc, layer_flops, layer_bytes = kernel_accounting(wl, R, touched)
     a = acc[dominant]
     timed_steps = sum(timed)
-    n_dom_per_step = dom_n / timed_steps  # routed (+ shared) launches per step
-    dom_bytes = a["bytes"] + (a.get("bytes_shared", 0.0) if n_dom_per_step > 1 else 0.0)
-    dom_flops = a["flops"] + (a.get("flops_shared", 0.0) if n_dom_per_step > 1 else 0.0)
-    # bytes and flops per launch (routed and shared launches averaged)
-    per_launch_bytes = dom_bytes / n_dom_per_step
-    per_launch_flops = dom_flops / n_dom_per_step
+    assert dom_n == timed_steps, f"{dominant}: {dom_n} launches timed in {timed_steps} steps"
+    per_launch_bytes = a["bytes"]
+    per_launch_flops = a["flops"]
     intensity = per_launch_flops / per_launch_bytes
     if intensity < RIDGE:
         achieved = per_launch_bytes / (dom_avg_ms * 1e-3) / 1e9
@@ -234,18 +261,20 @@ def main():
     roof["event_timed_launches"] = int(dom_n)  # in the last of every EVENT_EVERY timed steps
     roof["algorithmic_bytes_per_launch"] = per_launch_bytes
     roof["algorithmic_flops_per_launch"] = per_launch_flops
+    roof["implementation_bytes_per_launch"] = a["impl_bytes"]
+    roof["mfma_frac"] = round(per_launch_flops / (dom_avg_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+    roof["hbm_frac"] = round(per_launch_bytes / (dom_avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     # HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     # summary, valid only for the kernel source the counters were taken on
     roof["traffic"] = None
-    tpath = os.path.join(ROOT, "profiles", f"traffic__{dominant}__{wl.name}.txt")
+    tpath = os.path.join(ROOT, "profiles", f"traffic__{dominant}__{wl.name}{'__fp8_weights' if args.fp8 else ''}.txt")
     if os.path.exists(tpath):
         kv = {}
         for ln in open(tpath):
             if "=" in ln and not ln.lstrip().startswith("#"):
                 k, v = ln.split("=", 1)
                 kv[k.strip()] = v.strip()
-        src = os.path.join(ROOT, "mixture_experts_sparse_route_amd", "csrc", "gemm_bf16.hip")
-        if kv.get("source_sha256_16") == source_hash(src):
+        if kv.get("source_sha256_16") == gemm_source_hash():
             roof["traffic"] = float(kv["bytes_per_launch"])
 
     line = {
@@ -273,6 +302,10 @@ def main():
                   "algorithmic_gbps": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                   "mfma_frac": round(layer_flops / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                   "hbm_frac": round(layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  # max(flops / MFMA peak, bytes / HBM peak) / step time
+                  "roofline_frac": round(max(layer_flops / (BF16_PEAK_TFLOPS * 1e12),
+                                             layer_bytes / (HBM_PEAK_GBS * 1e9)) / (ms_per_step * 1e-3), 4),
+                  "algorithmic_flops": layer_flops, "algorithmic_bytes": layer_bytes,
                   "kept_rows": R, "touched_experts": touched, "host_wall_s": round(wall, 3)},
     }
     if breakdown:

@@ -34,13 +34,14 @@
  *   - Calls are stateless; calls sharing a workspace must be stream-ordered.
  *   - Results are deterministic: no floating-point atomics; every reduction
  *     has a fixed order.  Behaviour on non-finite inputs is undefined.
- *   - Tile plans are chosen from the shapes.  Environment variables read at
- *     each call override them for tuning (MOE_GEMM_K64, MOE_GEMM_K64_DOWN,
- *     MOE_GEMM_BM, MOE_GEMM_BM_DOWN, MOE_GEMM_BNB_UP, MOE_GEMM_NS_UP,
- *     MOE_GEMM_BNB_DOWN, MOE_GEMM_NS_DOWN, MOE_GEMM_WGS, MOE_GEMM_EVEN_UP;
- *     MOE_ROUTER_WGS, read once); a set that names no compiled configuration
- *     is ignored.  Results do not depend on the plan: every output element
- *     sums its 32-wide MFMA k-steps in k order whatever the tile shape.
+ *   - Tile plans are chosen from the shapes.  For tuning only, and only when
+ *     MOE_TUNING=1 is set in the environment, environment variables read at
+ *     each call override them (MOE_GEMM_K64, MOE_GEMM_K64_DOWN, MOE_GEMM_BM,
+ *     MOE_GEMM_BM_DOWN, MOE_GEMM_BNB_UP, MOE_GEMM_NS_UP, MOE_GEMM_BNB_DOWN,
+ *     MOE_GEMM_NS_DOWN, MOE_GEMM_WGS, MOE_GEMM_EVEN_UP; MOE_ROUTER_WGS, read
+ *     once); a set that names no compiled configuration is ignored.  Results
+ *     do not depend on the plan: every output element sums its 32-wide MFMA
+ *     k-steps in k order whatever the tile shape.
  */
 #ifndef MOE_H
 #define MOE_H

@@ -30,7 +30,7 @@ DROP_POLICIES = {"first_come": 0, "affinity": 1, "reroute": 2}
 STAT_NAMES = ("balance", "z_loss", "lif", "cv", "entropy_p", "entropy_f")
 
 KERNEL_NAMES = ["router_logits", "router_topk", "route_scan", "route_scatter", "dispatch", "ffn_tiles",
-                "gemm_gate_up", "gemm_down", "combine"]
+                "gemm_gate_up", "gemm_down", "combine", "shared_gate_up", "shared_down"]
 
 
 class MoeError(RuntimeError):

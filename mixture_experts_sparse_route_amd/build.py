@@ -16,8 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["router.hip", "permute.hip", "expert_choice.hip", "gemm_bf16.hip", "gemm_f32.hip", "combine.hip",
-           "api.cpp"]
+SOURCES = ["gemm_bf16_up.hip", "gemm_bf16.hip", "router.hip", "permute.hip", "expert_choice.hip", "gemm_f32.hip",
+           "combine.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
@@ -37,7 +37,7 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 6) -> str:
+def build(jobs: int = 8) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))

@@ -56,6 +56,11 @@ struct Shape {
   int64_t max_rows;  // upper bound of kept rows R
   int64_t n_chunks;  // router_topk workgroups / histogram chunks
   size_t esz;
+  // moe_forward: one assignment per token and no shared expert (bf16): the
+  // routed rows are copied into a k-blocked xp and GEMM2 writes y itself;
+  // other bf16 layers read the routed rows from a k-blocked copy of x
+  // through the routing (no per-row copy)
+  bool fused;
 };
 
 moe_status validate(const moe_config* c, Shape* sh) {
@@ -134,6 +139,7 @@ moe_status validate(const moe_config* c, Shape* sh) {
   sh->ec = ec;
   sh->n_chunks = (T + chunk_tokens(E, K) - 1) / chunk_tokens(E, K);
   sh->esz = bf16 ? 2 : 4;
+  sh->fused = bf16 && K == 1 && c->n_shared == 0 && !ec;
   return MOE_OK;
 }
 
@@ -141,7 +147,7 @@ moe_status validate(const moe_config* c, Shape* sh) {
 struct Layout {
   size_t router_part, blk_count, blk_base, blk_P, blk_z, dem_off, seg, alt_idx, alt_w, pos1, cand, cand_w,
       blk_count2, blk_base2, counts2, tab_up, tab_down, counts, sh_range, sh_tab_up, sh_tab_down, sh_counts;
-  size_t h, xp, yp, sh_h, sh_out;
+  size_t h, xp, xkb, yp, sh_h, sh_out;
   size_t r_logits, r_idx, r_w, r_counts, r_offsets, r_dest, r_row_src, r_dropped;
   size_t total;
 };
@@ -180,7 +186,10 @@ Layout layout(const Shape& s) {
   L.sh_tab_down = take(s.S ? (size_t)ffn_table_entries(s.bf16, s.T, 1, s.d, false) * 16 : 0);
   L.sh_counts = take(2 * 4);
   L.h = take((size_t)s.max_rows * s.F * s.esz);
-  L.xp = take((size_t)s.max_rows * s.d * s.esz);
+  // xp: the routed rows (fp32 layers row-major; the fused bf16 path
+  // k-blocked); xkb: x k-blocked [d/32][T][32] (the other bf16 layers)
+  L.xp = take(!s.bf16 || s.fused ? (size_t)s.max_rows * s.d * s.esz : 0);
+  L.xkb = take(s.bf16 && !s.fused ? (size_t)s.T * s.d * s.esz : 0);
   L.yp = take((size_t)s.max_rows * s.d * 4);
   L.sh_h = take((size_t)(s.S ? s.T * s.Fs : 0) * s.esz);
   L.sh_out = take((size_t)(s.S ? s.T * s.d : 0) * 4);
@@ -342,21 +351,22 @@ moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const 
 }
 
 // s1 / s3 / s2: row scales of E4M3 weights (s.w8), else unused.
-// group_max: bound of any group's rows; a_blocked: A is k-blocked with
-// max_rows rows (the fused path's own dispatch output), else row-major.
-// plan_in: the plan (else computed here); tiles_ready: its tile tables are
-// already written (by the routing scatter).
-moe_status do_ffn(const Shape& s, const void* A, bool a_blocked, const int32_t* offsets, int64_t n_groups,
+// group_max: bound of any group's rows; A: GEMM1's A operand (fp32 layers:
+// row-major A.ptr).  plan_in: the plan (else computed here); tiles_ready:
+// its tile tables are already written (by the routing scatter).
+moe_status do_ffn(const Shape& s, const AOperand& A, const int32_t* offsets, int64_t n_groups,
                   int64_t max_rows, int64_t group_max,
                   const void* W1, const void* W3, const void* W2, const float* s1, const float* s3, const float* s2,
                   void* h, float* yp, int4* tab_up, int4* tab_down, int32_t* counts, int64_t F, hipStream_t st,
-                  const CombineFuse* fuse = nullptr, const FfnPlan* plan_in = nullptr, bool tiles_ready = false) {
+                  const CombineFuse* fuse = nullptr, const FfnPlan* plan_in = nullptr, bool tiles_ready = false,
+                  bool shared = false) {
   const FfnPlan plan = plan_in ? *plan_in : ffn_plan(s.bf16, s.w8, max_rows, group_max, n_groups, F, s.d);
   if (!tiles_ready)
     MOE_HIP(launch_ffn_tiles(plan, offsets, n_groups, max_rows, F, s.d, tab_up, tab_down, counts, st));
-  MOE_HIP(launch_gemm_gate_up(s.bf16, plan, A, a_blocked, tab_up, counts, n_groups, max_rows, W1, W3, s1, s3, h, F, s.d,
-                              st));
-  MOE_HIP(launch_gemm_down(s.bf16, plan, h, tab_down, counts + 1, n_groups, max_rows, W2, s2, yp, fuse, F, s.d, st));
+  MOE_HIP(launch_gemm_gate_up(s.bf16, plan, A, tab_up, counts, n_groups, max_rows, W1, W3, s1, s3, h, F, s.d,
+                              st, shared ? K_SHARED_GATE_UP : K_GEMM_GATE_UP));
+  MOE_HIP(launch_gemm_down(s.bf16, plan, h, tab_down, counts + 1, n_groups, max_rows, W2, s2, yp, fuse, F, s.d, st,
+                           shared ? K_SHARED_DOWN : K_GEMM_DOWN));
   return MOE_OK;
 }
 
@@ -431,8 +441,132 @@ moe_status side_of(int dev, Side** out) {
   return MOE_OK;
 }
 
-const char* const kNames[K_COUNT] = {"router_logits", "router_topk", "route_scan",    "route_scatter", "dispatch",
-                                     "ffn_tiles",     "gemm_gate_up", "gemm_down",    "combine"};
+// moe_forward after validation.  allow_side: the shared expert may run on
+// the device's side stream (created on first use); otherwise every launch is
+// in order on hs.
+moe_status forward_impl(const moe_config* cfg, const Shape& s, const void* x, const float* Wg,
+                        const float* logit_bias, const float* sel_bias, const void* W1, const void* W3, const void* W2,
+                        const void* Ws1, const void* Ws3, const void* Ws2, const moe_scales* scales, void* y,
+                        const moe_routing* r, void* ws, size_t ws_bytes, hipStream_t hs, bool allow_side) {
+  moe_status st;
+  const bool topk_in = cfg->flags & MOE_F_TOPK_IN;
+  const bool logits_in = cfg->flags & MOE_F_LOGITS_IN;
+  if (!x || !y || !W1 || !W3 || !W2) return fail(MOE_ERR_INVALID_ARG, "x, y, W1, W3, W2 are required");
+  if (!topk_in && !logits_in && !Wg) return fail(MOE_ERR_INVALID_ARG, "Wg is required");
+  if (s.S && (!Ws1 || !Ws3 || !Ws2)) return fail(MOE_ERR_INVALID_ARG, "shared expert weights are required");
+  if (s.w8 && (!scales || !scales->w1 || !scales->w3 || !scales->w2 ||
+               (s.S && (!scales->ws1 || !scales->ws3 || !scales->ws2))))
+    return fail(MOE_ERR_INVALID_ARG, "MOE_FP8_E4M3 weights need their scales");
+  if ((st = check_aligned({x, Wg, W1, W3, W2, Ws1, Ws3, Ws2, y})) != MOE_OK) return st;
+  if (s.w8 && (st = check_aligned({scales->w1, scales->w3, scales->w2, scales->ws1, scales->ws3, scales->ws2})) != MOE_OK)
+    return st;
+  const moe_scales none{};
+  const moe_scales& sc = s.w8 ? *scales : none;
+  if ((topk_in || logits_in || s.stats) && !r)
+    return fail(MOE_ERR_INVALID_ARG, "MOE_F_*_IN and MOE_F_STATS need the routing arrays");
+  if (r && (st = check_routing(r, !topk_in, s.stats)) != MOE_OK) return st;
+  Layout L;
+  if ((st = check_ws(s, ws, ws_bytes, &L)) != MOE_OK) return st;
+  if (s.T == 0) return MOE_OK;
+  // the shared expert on the device's side stream when allowed and the
+  // caller's stream belongs to the current device (else in order on the
+  // caller's stream)
+  std::unique_lock<std::mutex> side_lk;
+  Side* sd = nullptr;
+  if (s.S && allow_side) {
+    int cur = -1, sdev = -2;
+    if (hipGetDevice(&cur) == hipSuccess && hipStreamGetDevice(hs, &sdev) == hipSuccess && sdev == cur) {
+      side_lk = std::unique_lock<std::mutex>(g_side_mu);
+      if ((st = side_of(cur, &sd)) != MOE_OK) return st;
+    }
+  }
+  moe_routing rr;
+  if (r) {
+    rr = *r;
+  } else {
+    rr.logits = at<float>(ws, L.r_logits);
+    rr.topk_idx = at<int32_t>(ws, L.r_idx);
+    rr.topk_w = at<float>(ws, L.r_w);
+    rr.counts = at<int32_t>(ws, L.r_counts);
+    rr.offsets = at<int32_t>(ws, L.r_offsets);
+    rr.dest = at<int32_t>(ws, L.r_dest);
+    rr.row_src = at<int32_t>(ws, L.r_row_src);
+    rr.dropped = at<uint8_t>(ws, L.r_dropped);
+    rr.stats = nullptr;
+  }
+  // x k-blocked once for the bf16 layers that read it through the routing
+  // (and for the shared expert), before the shared expert forks off
+  void* xkb = at<void>(ws, L.xkb);
+  if (s.bf16 && !s.fused) MOE_HIP(launch_kblock_copy(x, xkb, s.T, s.d * (int64_t)s.esz, hs));
+  // a8: the shared expert over all T rows of x
+  float* sh_out = s.S ? at<float>(ws, L.sh_out) : nullptr;
+  auto shared_ffn = [&](hipStream_t q) -> moe_status {
+    int32_t* range = at<int32_t>(ws, L.sh_range);
+    MOE_HIP(launch_set_range(range, s.T, q));
+    const AOperand xa = s.bf16 ? AOperand{xkb, s.T, nullptr, 1} : AOperand{x, 0, nullptr, 1};
+    return do_ffn(s, xa, range, 1, s.T, s.T, Ws1, Ws3, Ws2, sc.ws1, sc.ws3, sc.ws2, at<void>(ws, L.sh_h), sh_out,
+                  at<int4>(ws, L.sh_tab_up), at<int4>(ws, L.sh_tab_down), at<int32_t>(ws, L.sh_counts), s.Fs, q,
+                  nullptr, nullptr, false, true);
+  };
+  if (sd) {
+    MOE_HIP(hipEventRecord(sd->fork, hs));
+    MOE_HIP(hipStreamWaitEvent(sd->s, sd->fork, 0));
+    if ((st = shared_ffn(sd->s)) != MOE_OK) return st;
+    MOE_HIP(hipEventRecord(sd->join, sd->s));
+  }
+  const bool residual = cfg->flags & MOE_F_RESIDUAL;
+  // one assignment per token and no shared expert (bf16): GEMM2 writes the
+  // kept tokens' outputs itself, and the dropped tokens' rows are written by
+  // the capacity scatter (first-come drops) or else by the combine
+  const bool fused = s.fused;
+  bool drop_done = false;
+  void* xp = at<void>(ws, L.xp);
+  // the routed FFN's plan is known before routing: the scatter that runs on
+  // the final offsets writes its tile tables (one launch fewer); an expert
+  // holds at most one row per token, and at most its capacity
+  const int64_t group_max = s.cap >= 0 ? std::min(s.T, s.cap) : s.T;
+  const FfnPlan plan = ffn_plan(s.bf16, s.w8, s.max_rows, group_max, s.E, s.F, s.d);
+  const TileJob tj = tile_job(plan, s.F, s.d, at<int4>(ws, L.tab_up), at<int4>(ws, L.tab_down),
+                              at<int32_t>(ws, L.counts));
+  bool tiles_done = false;
+  // on the fused path the scatter also does the dispatch (one row per kept token)
+  if ((st = do_route(cfg, s, L, x, Wg, logit_bias, sel_bias, rr, ws, hs, fused ? y : nullptr,
+                     residual ? x : nullptr, &drop_done, fused && s.max_rows > 0 ? xp : nullptr, s.max_rows,
+                     s.max_rows > 0 ? &tj : nullptr, &tiles_done)) != MOE_OK)
+    return st;
+  float* yp = at<float>(ws, L.yp);
+  const CombineFuse fuse{rr.row_src, rr.topk_w, residual ? x : nullptr, y, s.bf16, s.out_bf16};
+  if (s.max_rows > 0) {
+    // A of the routed GEMM1: the fused path's xp (k-blocked, each k-step of a
+    // tile one contiguous run), written by the scatter or the dispatch; the
+    // other bf16 layers read x k-blocked through row_src (the a5 gather is
+    // folded into GEMM1's loads); fp32 layers dispatch row-major rows
+    AOperand xa{xp, 0, nullptr, 1};
+    if (s.bf16 && !fused) {
+      xa = AOperand{xkb, s.T, rr.row_src, (int)s.K};
+    } else {
+      if (!drop_done)
+        MOE_HIP(launch_dispatch(x, rr.row_src, rr.offsets + s.E, xp, s.max_rows, s.K, s.d * (int64_t)s.esz, s.bf16,
+                                hs));
+      if (s.bf16) xa.blk_rows = s.max_rows;
+    }
+    if ((st = do_ffn(s, xa, rr.offsets, s.E, s.max_rows, group_max, W1, W3, W2, sc.w1, sc.w3, sc.w2, at<void>(ws, L.h), yp,
+                     at<int4>(ws, L.tab_up), at<int4>(ws, L.tab_down), at<int32_t>(ws, L.counts), s.F, hs,
+                     fused ? &fuse : nullptr, &plan, tiles_done)) != MOE_OK)
+      return st;
+  }
+  if (s.S && !sd && (st = shared_ffn(hs)) != MOE_OK) return st;
+  if (sd) MOE_HIP(hipStreamWaitEvent(hs, sd->join, 0));
+  if (!drop_done)
+    MOE_HIP(launch_combine(s.bf16, s.out_bf16, yp, rr.topk_w, rr.dest, sh_out, residual ? x : nullptr, y, s.T, s.d,
+                           s.K, fused, hs));
+  return MOE_OK;
+}
+
+
+const char* const kNames[K_COUNT] = {"router_logits", "router_topk",  "route_scan", "route_scatter",
+                                     "dispatch",      "ffn_tiles",    "gemm_gate_up", "gemm_down",
+                                     "combine",       "shared_gate_up", "shared_down"};
 
 }  // namespace
 
@@ -531,7 +665,8 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* xp, const int32_t* 
   const moe_scales& sc = s.w8 ? *scales : none;
   // the plan assumes the routed bound of a group's rows (any rows stay correct)
   const int64_t group_max = s.cap >= 0 ? std::min(s.T, s.cap) : s.T;
-  return do_ffn(s, xp, false, offsets, n_groups, max_rows, group_max, W1, W3, W2, sc.w1, sc.w3, sc.w2, at<void>(ws, L.h), yp,
+  return do_ffn(s, AOperand{xp, 0, nullptr, 1}, offsets, n_groups, max_rows, group_max, W1, W3, W2, sc.w1, sc.w3, sc.w2,
+                at<void>(ws, L.h), yp,
                 at<int4>(ws, L.tab_up), at<int4>(ws, L.tab_down), at<int32_t>(ws, L.counts), s.F,
                 (hipStream_t)stream);
 }
@@ -559,103 +694,8 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, co
   Shape s;
   moe_status st = validate(cfg, &s);
   if (st != MOE_OK) return st;
-  const bool topk_in = cfg->flags & MOE_F_TOPK_IN;
-  const bool logits_in = cfg->flags & MOE_F_LOGITS_IN;
-  if (!x || !y || !W1 || !W3 || !W2) return fail(MOE_ERR_INVALID_ARG, "x, y, W1, W3, W2 are required");
-  if (!topk_in && !logits_in && !Wg) return fail(MOE_ERR_INVALID_ARG, "Wg is required");
-  if (s.S && (!Ws1 || !Ws3 || !Ws2)) return fail(MOE_ERR_INVALID_ARG, "shared expert weights are required");
-  if (s.w8 && (!scales || !scales->w1 || !scales->w3 || !scales->w2 ||
-               (s.S && (!scales->ws1 || !scales->ws3 || !scales->ws2))))
-    return fail(MOE_ERR_INVALID_ARG, "MOE_FP8_E4M3 weights need their scales");
-  if ((st = check_aligned({x, Wg, W1, W3, W2, Ws1, Ws3, Ws2, y})) != MOE_OK) return st;
-  if (s.w8 && (st = check_aligned({scales->w1, scales->w3, scales->w2, scales->ws1, scales->ws3, scales->ws2})) != MOE_OK)
-    return st;
-  const moe_scales none{};
-  const moe_scales& sc = s.w8 ? *scales : none;
-  if ((topk_in || logits_in || s.stats) && !r)
-    return fail(MOE_ERR_INVALID_ARG, "MOE_F_*_IN and MOE_F_STATS need the routing arrays");
-  if (r && (st = check_routing(r, !topk_in, s.stats)) != MOE_OK) return st;
-  Layout L;
-  if ((st = check_ws(s, ws, ws_bytes, &L)) != MOE_OK) return st;
-  if (s.T == 0) return MOE_OK;
-  hipStream_t hs = (hipStream_t)stream;
-  // the shared expert on the device's side stream when the caller's stream
-  // belongs to the current device (else in order on the caller's stream)
-  std::unique_lock<std::mutex> side_lk;
-  Side* sd = nullptr;
-  if (s.S) {
-    int cur = -1, sdev = -2;
-    if (hipGetDevice(&cur) == hipSuccess && hipStreamGetDevice(hs, &sdev) == hipSuccess && sdev == cur) {
-      side_lk = std::unique_lock<std::mutex>(g_side_mu);
-      if ((st = side_of(cur, &sd)) != MOE_OK) return st;
-    }
-  }
-  moe_routing rr;
-  if (r) {
-    rr = *r;
-  } else {
-    rr.logits = at<float>(ws, L.r_logits);
-    rr.topk_idx = at<int32_t>(ws, L.r_idx);
-    rr.topk_w = at<float>(ws, L.r_w);
-    rr.counts = at<int32_t>(ws, L.r_counts);
-    rr.offsets = at<int32_t>(ws, L.r_offsets);
-    rr.dest = at<int32_t>(ws, L.r_dest);
-    rr.row_src = at<int32_t>(ws, L.r_row_src);
-    rr.dropped = at<uint8_t>(ws, L.r_dropped);
-    rr.stats = nullptr;
-  }
-  // a8: the shared expert over all T rows of x
-  float* sh_out = s.S ? at<float>(ws, L.sh_out) : nullptr;
-  auto shared_ffn = [&](hipStream_t q) -> moe_status {
-    int32_t* range = at<int32_t>(ws, L.sh_range);
-    MOE_HIP(launch_set_range(range, s.T, q));
-    return do_ffn(s, x, false, range, 1, s.T, s.T, Ws1, Ws3, Ws2, sc.ws1, sc.ws3, sc.ws2, at<void>(ws, L.sh_h), sh_out,
-                  at<int4>(ws, L.sh_tab_up), at<int4>(ws, L.sh_tab_down), at<int32_t>(ws, L.sh_counts), s.Fs, q);
-  };
-  if (sd) {
-    MOE_HIP(hipEventRecord(sd->fork, hs));
-    MOE_HIP(hipStreamWaitEvent(sd->s, sd->fork, 0));
-    if ((st = shared_ffn(sd->s)) != MOE_OK) return st;
-    MOE_HIP(hipEventRecord(sd->join, sd->s));
-  }
-  const bool residual = cfg->flags & MOE_F_RESIDUAL;
-  // one assignment per token and no shared expert (bf16): GEMM2 writes the
-  // kept tokens' outputs itself, and the dropped tokens' rows are written by
-  // the capacity scatter (first-come drops) or else by the combine
-  const bool fused = s.bf16 && s.K == 1 && s.S == 0 && !s.ec;
-  bool drop_done = false;
-  void* xp = at<void>(ws, L.xp);
-  // the routed FFN's plan is known before routing: the scatter that runs on
-  // the final offsets writes its tile tables (one launch fewer); an expert
-  // holds at most one row per token, and at most its capacity
-  const int64_t group_max = s.cap >= 0 ? std::min(s.T, s.cap) : s.T;
-  const FfnPlan plan = ffn_plan(s.bf16, s.w8, s.max_rows, group_max, s.E, s.F, s.d);
-  const TileJob tj = tile_job(plan, s.F, s.d, at<int4>(ws, L.tab_up), at<int4>(ws, L.tab_down),
-                              at<int32_t>(ws, L.counts));
-  bool tiles_done = false;
-  // on the fused path the scatter also does the dispatch (one row per kept token)
-  if ((st = do_route(cfg, s, L, x, Wg, logit_bias, sel_bias, rr, ws, hs, fused ? y : nullptr,
-                     residual ? x : nullptr, &drop_done, fused && s.max_rows > 0 ? xp : nullptr, s.max_rows,
-                     s.max_rows > 0 ? &tj : nullptr, &tiles_done)) != MOE_OK)
-    return st;
-  float* yp = at<float>(ws, L.yp);
-  const CombineFuse fuse{rr.row_src, rr.topk_w, residual ? x : nullptr, y, s.bf16, s.out_bf16};
-  if (s.max_rows > 0) {
-    // the fused path's xp is internal: k-blocked for bf16 (each k-step of a
-    // GEMM1 tile then reads one contiguous run)
-    if (!drop_done)
-      MOE_HIP(launch_dispatch(x, rr.row_src, rr.offsets + s.E, xp, s.max_rows, s.K, s.d * (int64_t)s.esz, s.bf16, hs));
-    if ((st = do_ffn(s, xp, s.bf16, rr.offsets, s.E, s.max_rows, group_max, W1, W3, W2, sc.w1, sc.w3, sc.w2, at<void>(ws, L.h), yp,
-                     at<int4>(ws, L.tab_up), at<int4>(ws, L.tab_down), at<int32_t>(ws, L.counts), s.F, hs,
-                     fused ? &fuse : nullptr, &plan, tiles_done)) != MOE_OK)
-      return st;
-  }
-  if (s.S && !sd && (st = shared_ffn(hs)) != MOE_OK) return st;
-  if (sd) MOE_HIP(hipStreamWaitEvent(hs, sd->join, 0));
-  if (!drop_done)
-    MOE_HIP(launch_combine(s.bf16, s.out_bf16, yp, rr.topk_w, rr.dest, sh_out, residual ? x : nullptr, y, s.T, s.d,
-                           s.K, fused, hs));
-  return MOE_OK;
+  return forward_impl(cfg, s, x, Wg, logit_bias, sel_bias, W1, W3, W2, Ws1, Ws3, Ws2, scales, y, r, ws, ws_bytes,
+                      (hipStream_t)stream, true);
 }
 
 const char* moe_status_string(moe_status s) {

@@ -96,8 +96,14 @@ int device_cus() {
   return n_cu;
 }
 
+bool tuning_enabled() {
+  const char* e = getenv("MOE_TUNING");
+  return e && e[0] == '1' && e[1] == 0;
+}
+
+// a tuning override, or `def` when none is set or tuning is off
 static int env_int(const char* name, int def) {
-  const char* e = getenv(name);
+  const char* e = tuning_enabled() ? getenv(name) : nullptr;
   return e ? atoi(e) : def;
 }
 
@@ -198,8 +204,8 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_
   };
   shallow(d, p.k64_up, p.ns_up, p.bnb_up);
   shallow(F, p.k64_down, p.ns_down, p.bnb_down);
-  // overrides for tuning: MOE_GEMM_K64 (both GEMMs in stages of 64 k, 0 or
-  // 1), MOE_GEMM_K64_DOWN, MOE_GEMM_BM, MOE_GEMM_BM_DOWN,
+  // overrides for tuning, honoured with MOE_TUNING=1 only: MOE_GEMM_K64
+  // (both GEMMs in stages of 64 k, 0 or 1), MOE_GEMM_K64_DOWN, MOE_GEMM_BM, MOE_GEMM_BM_DOWN,
   // MOE_GEMM_{BNB,NS}_{UP,DOWN}, MOE_GEMM_WGS, MOE_GEMM_EVEN_UP; a set that names no compiled
   // configuration leaves the plan as it was
   const FfnPlan def = p;
@@ -240,31 +246,32 @@ static int64_t grid_of(int bm, int64_t max_rows, int64_t n_groups, int64_t n_col
   return (tiles + kXcds - 1) / kXcds * kXcds;
 }
 
-hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const void* A, bool a_blocked, const int4* tab,
+hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const AOperand& A, const int4* tab,
                                const int32_t* count, int64_t n_groups, int64_t max_rows, const void* W1, const void* W3,
-                               const float* s1, const float* s3, void* h, int64_t F, int64_t d, hipStream_t s) {
+                               const float* s1, const float* s3, void* h, int64_t F, int64_t d, hipStream_t s,
+                               int prof_id) {
   const int64_t grid = grid_of(p.bm, max_rows, n_groups, F, p.bn_out_up);
   if (grid == 0) return hipSuccess;
-  prof_begin(K_GEMM_GATE_UP, s);
+  prof_begin(prof_id, s);
   hipError_t err;
   if (bf16) {
-    err = gemm_bf16_gate_up(p, A, a_blocked ? max_rows : 0, tab, count, grid, W1, W3, s1, s3, h, max_rows, F, d, s);
+    err = gemm_bf16_gate_up(p, A, tab, count, grid, W1, W3, s1, s3, h, max_rows, F, d, s);
   } else {
-    F32Args a{(const float*)A, (const float*)W1, (const float*)W3, (float*)h, tab, count, (int)F, (int)d};
+    F32Args a{(const float*)A.ptr, (const float*)W1, (const float*)W3, (float*)h, tab, count, (int)F, (int)d};
     gemm_f32_kernel<true><<<(unsigned)grid, 256, 0, s>>>(a);
     err = hipGetLastError();
   }
-  prof_end(K_GEMM_GATE_UP, s);
+  prof_end(prof_id, s);
   return err;
 }
 
 hipError_t launch_gemm_down(bool bf16, const FfnPlan& p, const void* h, const int4* tab, const int32_t* count,
                             int64_t n_groups, int64_t max_rows, const void* W2, const float* s2, float* yp,
-                            const CombineFuse* fuse, int64_t F, int64_t d, hipStream_t s) {
+                            const CombineFuse* fuse, int64_t F, int64_t d, hipStream_t s, int prof_id) {
   if (fuse && !bf16) return hipErrorInvalidValue;
   const int64_t grid = grid_of(p.bm_down, max_rows, n_groups, d, p.bn_out_down);
   if (grid == 0) return hipSuccess;
-  prof_begin(K_GEMM_DOWN, s);
+  prof_begin(prof_id, s);
   hipError_t err;
   if (bf16) {
     err = gemm_bf16_down(p, h, max_rows, tab, count, grid, W2, s2, yp, fuse, F, d, s);
@@ -273,7 +280,7 @@ hipError_t launch_gemm_down(bool bf16, const FfnPlan& p, const void* h, const in
     gemm_f32_kernel<false><<<(unsigned)grid, 256, 0, s>>>(a);
     err = hipGetLastError();
   }
-  prof_end(K_GEMM_DOWN, s);
+  prof_end(prof_id, s);
   return err;
 }
 

@@ -17,6 +17,8 @@ enum KernelId {
   K_GEMM_GATE_UP,    // grouped GEMM1 + SiLU*gate epilogue
   K_GEMM_DOWN,       // grouped GEMM2
   K_COMBINE,
+  K_SHARED_GATE_UP,  // the shared expert's GEMM1 (+ SiLU*gate) and GEMM2
+  K_SHARED_DOWN,
   K_COUNT
 };
 const char* kernel_name(int id);
@@ -132,6 +134,8 @@ hipError_t launch_expert_choice(float* logits, const float* part, int S, const f
 // row-major.
 hipError_t launch_dispatch(const void* x, const int32_t* row_src, const int32_t* R_ptr, void* xp, int64_t max_rows,
                            int64_t K, int64_t row_bytes, bool blocked, hipStream_t s);
+// x [T, d] bf16 -> k-blocked [d/32][T][32] (row_bytes = 2 d, a multiple of 64).
+hipError_t launch_kblock_copy(const void* x, void* xkb, int64_t T, int64_t row_bytes, hipStream_t s);
 
 // ---- grouped expert FFN (a6-a7) ----
 struct FfnPlan {
@@ -154,6 +158,10 @@ struct FfnPlan {
 };
 // Compute units of the current device (queried once).
 int device_cus();
+// Tile-plan overrides from the environment (MOE_GEMM_*, MOE_ROUTER_WGS) are
+// honoured only when MOE_TUNING=1 is set, so an inherited variable cannot
+// change what a production caller launches.
+bool tuning_enabled();
 // group_max: upper bound of any group's rows (the expert capacity when there
 // is one); max_rows: of all groups together.
 FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_t n_groups, int64_t F, int64_t d);
@@ -189,25 +197,41 @@ struct CombineFuse {
   bool x_bf16, y_bf16;
 };
 
+// The A operand of GEMM1: row-major [rows, Kdim] (blk_rows = 0) or k-blocked
+// [Kdim/32][blk_rows][32] (the 32 columns of a k-step of all rows are one
+// contiguous run).  gather non-null (k-blocked only): GEMM row r reads A row
+// gather[r] / gather_div -- the routed rows read the k-blocked x through the
+// routing's row_src (gather_div = K), so no per-row copy of x is made.
+struct AOperand {
+  const void* ptr;
+  int64_t blk_rows;
+  const int32_t* gather;
+  int gather_div;
+};
+
 // bf16 MFMA path (gemm_bf16.hip); called through the launchers below.
 // s1 / s3 / s2: [groups, N] row scales of E4M3 weights (p.w8), else unused.
 // a_blk / h_blk: the row count R of a k-blocked operand ([cols/32][R][32]:
 // the 32 columns of a k-step of R rows are one contiguous run), 0 = row-major.
-hipError_t gemm_bf16_gate_up(const FfnPlan& p, const void* A, int64_t a_blk, const int4* tab, const int32_t* count,
+hipError_t gemm_bf16_gate_up(const FfnPlan& p, const AOperand& A, const int4* tab, const int32_t* count,
                              int64_t grid, const void* W1, const void* W3, const float* s1, const float* s3, void* h,
                              int64_t h_blk, int64_t F, int64_t d, hipStream_t s);
 hipError_t gemm_bf16_down(const FfnPlan& p, const void* h, int64_t h_blk, const int4* tab, const int32_t* count,
                           int64_t grid, const void* W2, const float* s2, float* yp, const CombineFuse* fuse, int64_t F,
                           int64_t d, hipStream_t s);
-// bf16: h is k-blocked with max_rows rows, and so is A when a_blocked (else
-// row-major); fp32: everything row-major.
-hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const void* A, bool a_blocked, const int4* tab,
+// bf16: h is k-blocked with max_rows rows; A as AOperand says; fp32:
+// everything row-major (A.ptr only).
+// prof_id: the timing facility's kernel id of the launch (the routed or the
+// shared expert's GEMM).
+hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const AOperand& A, const int4* tab,
                                const int32_t* count, int64_t n_groups, int64_t max_rows, const void* W1, const void* W3,
-                               const float* s1, const float* s3, void* h, int64_t F, int64_t d, hipStream_t s);
+                               const float* s1, const float* s3, void* h, int64_t F, int64_t d, hipStream_t s,
+                               int prof_id = K_GEMM_GATE_UP);
 // fuse (bf16 only, nullable): write y instead of yp.
 hipError_t launch_gemm_down(bool bf16, const FfnPlan& p, const void* h, const int4* tab, const int32_t* count,
                             int64_t n_groups, int64_t max_rows, const void* W2, const float* s2, float* yp,
-                            const CombineFuse* fuse, int64_t F, int64_t d, hipStream_t s);
+                            const CombineFuse* fuse, int64_t F, int64_t d, hipStream_t s,
+                            int prof_id = K_GEMM_DOWN);
 
 // dst[0] = 0, dst[1] = n (row range of the shared expert).
 hipError_t launch_set_range(int32_t* dst, int64_t n, hipStream_t s);

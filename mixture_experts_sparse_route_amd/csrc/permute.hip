@@ -517,18 +517,19 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const V* __restrict__ x, 
 // The same into a k-blocked xp (bf16, [d/32][blk_rows][32]): workgroup b
 // moves rows 16b .. 16b+15; in each instruction a wave writes one 64-byte
 // k-block of those 16 rows, 1 KB contiguous (lane: row lane/4, 16-byte chunk
-// lane%4), reading 64 bytes of each row's token.
+// lane%4), reading 64 bytes of each row's token.  row_src == nullptr: row r
+// is x's row r and R_ptr == nullptr: R = R_host (x itself k-blocked).
 __global__ __launch_bounds__(256) void dispatch_blocked_kernel(const uint4* __restrict__ x,
                                                                const int32_t* __restrict__ row_src,
                                                                const int32_t* __restrict__ R_ptr,
                                                                uint4* __restrict__ xp, int K, int n_kb,
-                                                               int64_t blk_rows) {
-  const int R = *R_ptr;
+                                                               int64_t blk_rows, int R_host) {
+  const int R = R_ptr ? *R_ptr : R_host;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = blockIdx.x * 16 + (lane >> 2), c = lane & 3;
   if (blockIdx.x * 16 >= R) return;
   if (r >= R) return;
-  const uint4* src = x + (int64_t)(row_src[r] / K) * n_kb * 4 + c;
+  const uint4* src = x + (int64_t)(row_src ? row_src[r] / K : r) * n_kb * 4 + c;
   uint4* dst = xp + (int64_t)r * 4 + c;
   const int64_t kb_stride = blk_rows * 4;
   int kb = wave;
@@ -667,7 +668,7 @@ hipError_t launch_dispatch(const void* x, const int32_t* row_src, const int32_t*
     if (nb == 0) return hipSuccess;
     prof_begin(K_DISPATCH, s);
     dispatch_blocked_kernel<<<nb, 256, 0, s>>>((const uint4*)x, row_src, R_ptr, (uint4*)xp, (int)K,
-                                               (int)(row_bytes / 64), max_rows);
+                                               (int)(row_bytes / 64), max_rows, 0);
     prof_end(K_DISPATCH, s);
     return hipGetLastError();
   }
@@ -702,6 +703,17 @@ TileJob tile_job(const FfnPlan& p, int64_t F, int64_t d, int4* tab_up, int4* tab
   j.tab_down = tab_down;
   j.counts = counts;
   return j;
+}
+
+hipError_t launch_kblock_copy(const void* x, void* xkb, int64_t T, int64_t row_bytes, hipStream_t s) {
+  if (row_bytes % 64 || T > INT32_MAX) return hipErrorInvalidValue;
+  const unsigned nb = (unsigned)((T + 15) / 16);
+  if (nb == 0) return hipSuccess;
+  prof_begin(K_DISPATCH, s);
+  dispatch_blocked_kernel<<<nb, 256, 0, s>>>((const uint4*)x, nullptr, nullptr, (uint4*)xkb, 1, (int)(row_bytes / 64),
+                                             T, (int)T);
+  prof_end(K_DISPATCH, s);
+  return hipGetLastError();
 }
 
 hipError_t launch_ffn_tiles(const FfnPlan& p, const int32_t* offsets, int64_t n_groups, int64_t max_rows, int64_t F,

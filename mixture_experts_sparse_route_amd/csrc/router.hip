@@ -558,10 +558,11 @@ int router_splits(int64_t T, int64_t d, int64_t E, bool bf16) {
   const int64_t tiles = ((T + LG_T - 1) / LG_T) * ((E + ew - 1) / ew);
   // split d until there is a workgroup per CU and no slice is longer than
   // 4096 (a slice is one workgroup's serial chain of 32-wide k-steps; more
-  // slices cost the Top-K kernel their partial sums).  Tuning override:
-  // MOE_ROUTER_WGS, a workgroup count to reach instead.
+  // slices cost the Top-K kernel their partial sums).  Tuning override
+  // (read once, with MOE_TUNING=1 only): MOE_ROUTER_WGS, a workgroup count to
+  // reach instead.
   static const int64_t want_env = [] {
-    const char* v = getenv("MOE_ROUTER_WGS");
+    const char* v = tuning_enabled() ? getenv("MOE_ROUTER_WGS") : nullptr;
     const long n = v ? atol(v) : 0;
     return n > 0 ? (int64_t)n : (int64_t)0;
   }();

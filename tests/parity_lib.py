@@ -3,13 +3,27 @@ HIP library on them through the C-ABI binding, run the CPU oracle on the same
 inputs, and compare.
 
 Tolerances (one place, used by every parity test):
-  fp32 layer:  max_i |y_i - r_i| / max(|r_i|, RMS(r)) <= 1e-4
-  bf16 layer:  max_i |y_i - r_i| <= 2e-2 * RMS(r), RMS over the rows of tokens
-               that are neither dropped nor excluded as near-ties, measured on
-               the layer's fp32 result before its final rounding; the bf16
-               output must then equal the round-to-nearest-even image of that
-               result bit for bit.  (Rounding the exact result to bf16 alone
-               can already cost 2e-2 x RMS when max|y| / RMS exceeds about 5.)
+  fp32 layer:  max_i |y_i - r_i| / max(|r_i|, RMS(r)) <= 1e-4 against the
+               oracle's definition (h in double).
+  bf16 layer:  max_i |y_i - r_i| <= 2e-2 * RMS(r) against the oracle's
+               definition (h kept in double), RMS over the rows of tokens that
+               are neither dropped nor excluded as near-ties, measured on the
+               layer's fp32 result before its final rounding; the bf16 output
+               must then equal the round-to-nearest-even image of that result
+               bit for bit.  (Rounding the exact result to bf16 alone can
+               already cost 2e-2 x RMS when max|y| / RMS exceeds about 5.)
+               Second, tighter check of the kernels: against the oracle that
+               stores h in bf16 as the layer does, <= 5e-3 * RMS (bf16
+               weights) or 1e-2 * RMS (E4M3 weights, whose fp32 sums put more
+               h values on the other side of a bf16 rounding boundary than the
+               double sums do).
+               Where storing h in bf16 by itself (the oracle's two modes
+               compared) leaves less than that second tolerance below 2e-2 --
+               a few small test shapes, listed with their numbers in the
+               design notes -- the bound against the definition is the
+               triangle-inequality one, cost_h + tolerance; such cases are
+               reported as "h-storage limited".  The five full-size workloads
+               are held to 2e-2 against the definition without exception.
   router logits: |l_gpu - l_ref| <= (3d + 2) * 2^-24 * sum_i |x_i w_i| + 2^-24 |l_ref|
                (the forward-error bound of an fp32 sum of 3d exact products:
                the bf16 path splits each fp32 router weight into three bf16
@@ -32,12 +46,14 @@ import mixture_experts_sparse_route_amd as moe
 
 NEAR_TIE = 1e-4
 F32_TOL = 1e-4
-# bf16 layers: max |y - r| <= 2e-2 * RMS(r) is the stated bound; against the
-# oracle that stores h in bf16 as the layer does, the remaining differences
-# are fp32 accumulation and rare one-ulp differences in h's rounding, so the
-# tests hold the tighter 5e-3.
+# bf16 layers: max |y - r| <= 2e-2 * RMS(r) against the definition is the
+# stated bound; against the oracle that stores h in bf16 as the layer does,
+# the remaining differences are fp32 accumulation and rare one-ulp
+# differences in h's rounding, so the tests also hold the tighter 5e-3
+# (1e-2 with E4M3 weights).
 BF16_TOL = 2e-2
 BF16_H_TOL = 5e-3
+FP8_H_TOL = 1e-2
 
 
 def scales_of(h: dict) -> dict:
@@ -118,12 +134,13 @@ class Case:
             self._route = oracle.route(self.L, h["x"], h["Wg"], h["logit_bias"], h["sel_bias"])
         return self._route
 
-    def oracle_y(self, idx, w, dest, tokens=None, residual=False, round_h=None):
-        """round_h=False: h kept in double (no bf16 storage of the SwiGLU output)."""
-        h = self.h
-        L = oracle.layer_of(self.wl, residual=residual, round_h=round_h)
-        return oracle.forward_rows(L, h["x"], idx, w, dest, h["W1"], h["W3"], h["W2"], h["Ws1"], h["Ws3"], h["Ws2"],
-                                   tokens=tokens, **scales_of(h))
+    def oracle_y(self, idx, w, dest, tokens=None, residual=False, L=None) -> "Ref":
+        """The oracle's outputs for the listed tokens (all if None): the
+        definition (h in double) and, for a bf16 layer, the bf16-h mode.
+        L: the oracle layer (default: the workload's, with `residual`)."""
+        if L is None:
+            L = oracle.layer_of(self.wl, residual=residual)
+        return oracle_refs(L, self.h, idx, w, dest, tokens)
 
     def logit_bound(self):
         x = self.h["x"]
@@ -155,23 +172,63 @@ def assert_weights_close(wg: np.ndarray, wo: np.ndarray, label=""):
     assert np.all(err <= bound), f"{label}: top-k weight error {err.max():.3g}"
 
 
-def y_error(y_gpu: np.ndarray, y_ref: np.ndarray, dtype: str, rows=None):
-    """-> (error measure, limit) on the given rows."""
-    if rows is not None:
-        y_gpu, y_ref = y_gpu[rows], y_ref[rows]
-    if y_ref.size == 0:
-        return 0.0, 1.0
+class Ref:
+    """Oracle outputs [n, d] (float64) of one set of tokens: y_def, the
+    definition (h in double); y_h, h stored in bf16 (bf16 layers only)."""
+
+    def __init__(self, y_def: np.ndarray, y_h: np.ndarray | None, fp8: bool):
+        self.y_def, self.y_h, self.fp8 = y_def, y_h, fp8
+
+
+def oracle_refs(L, h: dict, idx, w, dest, tokens=None) -> Ref:
+    """Ref of oracle layer L (its round_h is ignored) on the inputs h."""
+    def run(rh):
+        Lr = oracle.OrcLayer(L.T, L.d, L.F, L.E, L.K, L.gate, L.renorm, L.residual, L.bf16, L.capacity_factor,
+                             L.n_shared, L.Fs, rh, L.w_fp8)
+        return oracle.forward_rows(Lr, h["x"], idx, w, dest, h["W1"], h["W3"], h["W2"], h["Ws1"], h["Ws3"],
+                                   h["Ws2"], tokens=tokens, **scales_of(h))
+    return Ref(run(0), run(1) if L.bf16 else None, bool(L.w_fp8))
+
+
+def _max_err(y_gpu: np.ndarray, y_ref: np.ndarray, f32: bool) -> float:
     rms = float(np.sqrt(np.mean(y_ref ** 2)))
-    if dtype == "f32":
-        den = np.maximum(np.abs(y_ref), rms)
-        return float(np.max(np.abs(y_gpu - y_ref) / den)), F32_TOL
-    return float(np.max(np.abs(y_gpu - y_ref))) / rms, min(BF16_TOL, BF16_H_TOL)
+    if f32:
+        return float(np.max(np.abs(y_gpu - y_ref) / np.maximum(np.abs(y_ref), rms)))
+    return float(np.max(np.abs(y_gpu - y_ref))) / rms
 
 
-def assert_y_close(y_gpu: np.ndarray, y_ref: np.ndarray, dtype: str, rows=None, label=""):
-    err, lim = y_error(y_gpu, y_ref, dtype, rows)
-    assert err <= lim, f"{label}: output error {err:.4g} > {lim}"
-    return err
+def y_errors(y_gpu: np.ndarray, ref: Ref, rows=None) -> dict:
+    """{'def': error against the definition, 'h': against the bf16-h mode,
+    'cost_h': the bf16-h mode against the definition} on the given rows
+    (fp32 layers: 'def' only)."""
+    yd, yh = ref.y_def, ref.y_h
+    if rows is not None:
+        y_gpu, yd = y_gpu[rows], yd[rows]
+        yh = None if yh is None else yh[rows]
+    if yd.size == 0:
+        return {"def": 0.0}
+    if yh is None:
+        return {"def": _max_err(y_gpu, yd, True)}
+    return {"def": _max_err(y_gpu, yd, False), "h": _max_err(y_gpu, yh, False), "cost_h": _max_err(yh, yd, False)}
+
+
+def assert_y_close(y_gpu: np.ndarray, ref: Ref, rows=None, label="", strict=False) -> dict:
+    """Asserts the layer tolerance (module docstring) and returns the errors.
+    strict: the stated bound against the definition with no h-storage
+    allowance (the full-size workloads)."""
+    e = y_errors(y_gpu, ref, rows)
+    if "h" not in e:
+        assert e["def"] <= F32_TOL, f"{label}: output error {e['def']:.4g} > {F32_TOL}"
+        return e
+    htol = FP8_H_TOL if ref.fp8 else BF16_H_TOL
+    assert e["h"] <= htol, f"{label}: output error against bf16-h oracle {e['h']:.4g} > {htol}"
+    lim = BF16_TOL if strict else max(BF16_TOL, e["cost_h"] + htol)
+    if lim > BF16_TOL:
+        e["h_storage_limited"] = True
+        print(f"{label}: h-storage limited (bf16 h alone costs {e['cost_h']:.4g} x RMS); "
+              f"error against the definition {e['def']:.4g} <= {lim:.4g}")
+    assert e["def"] <= lim, f"{label}: output error against the definition {e['def']:.4g} > {lim:.4g}"
+    return e
 
 
 def kept_tokens(dest: np.ndarray, K: int, n_shared: int) -> np.ndarray:
@@ -180,3 +237,22 @@ def kept_tokens(dest: np.ndarray, K: int, n_shared: int) -> np.ndarray:
     if n_shared:
         return np.ones(T, bool)
     return (dest.reshape(T, K) >= 0).any(1)
+
+
+def tile_sample_tokens(orc: dict, K: int, T: int, extra=()) -> np.ndarray:
+    """Tokens whose rows cover every m-tile of both grouped GEMMs under any
+    tile plan: every m-tile starts 32 * j rows into its expert's group (tiles
+    are 64, 128 or 192 rows, or a group split evenly in 32-row units), so the
+    rows at multiples of 32 within each group, and each group's last row,
+    hold a checked output; every column tile of those rows is checked with
+    them."""
+    off, rs = orc["offsets"], orc["row_src"]
+    rows = []
+    for e in range(len(off) - 1):
+        a, b = int(off[e]), int(off[e + 1])
+        if b > a:
+            rows.extend(range(a, b, 32))
+            rows.append(b - 1)
+    toks = set((rs[np.array(rows, dtype=np.int64)] // K).tolist()) if rows else set()
+    toks |= {0, T - 1} | set(int(t) for t in extra)
+    return np.array(sorted(toks), dtype=np.int64)

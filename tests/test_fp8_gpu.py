@@ -5,15 +5,17 @@ article, §4.2: E4M3).
 The kernels stage the E4M3 bytes, convert them exactly to bf16 for the bf16
 MFMA and multiply the fp32 sums by the row scale; the oracle decodes each
 code by the format's definition, multiplies by the row scale and computes
-in double (storing h in bf16, as the bf16 layer does).  Outputs are held to
-the stated bf16 bound, max |y - r| <= 2e-2 RMS(r) on the fp32 result: the
-E4M3 test weights are heavier-tailed than the bf16 ones, so an fp32 sum that
-lands on the other side of a bf16 rounding boundary of h than the double sum
-moves y by up to about 5e-3 RMS (a CPU emulation with fp32 sums gives 0.0043
-on the two-m-tile case), above the 5e-3 the bf16-weight tests hold.  The
-kernel itself is pinned bit for bit: with power-of-two scales the FP8 layer
-must equal the bf16 layer given the dequantised weights.  Every case also
-checks that the bf16 output is the rounded fp32 one.
+in double.  Outputs are held to the layer tolerance of parity_lib: the stated
+bf16 bound, max |y - r| <= 2e-2 RMS(r) on the fp32 result against the
+definition (h in double), and 1e-2 RMS against the oracle that stores h in
+bf16 as the kernels do.  The E4M3 test weights are heavier-tailed than the
+bf16 ones, so storing h in bf16 costs more here (the oracle's two modes
+differ by up to about 0.04 RMS on the smallest shapes, which are reported as
+h-storage limited), and an fp32 sum that lands on the other side of a bf16
+rounding boundary of h than the double sum moves y by up to about 5e-3 RMS.
+The kernel itself is pinned bit for bit: with power-of-two scales the FP8
+layer must equal the bf16 layer given the dequantised weights.  Every case
+also checks that the bf16 output is the rounded fp32 one.
 """
 import numpy as np
 import pytest
@@ -23,7 +25,8 @@ import moe_synth
 import oracle
 import mixture_experts_sparse_route_amd as moe
 from moe_synth import workload
-from parity_lib import BF16_TOL, Case, assert_permutation_equal, host_f64, kept_tokens, routing_host, y_error
+from parity_lib import (Case, assert_permutation_equal, assert_y_close, host_f64, kept_tokens, oracle_refs,
+                        routing_host, tile_sample_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -47,7 +50,7 @@ CASES = {
 }
 
 
-def check_fp8(case: Case, tokens=None, expert_choice=False):
+def check_fp8(case: Case, tokens=None, expert_choice=False, strict=False):
     wl = case.wl
     T, K = wl.T, wl.K
     orc = case.oracle_route()
@@ -64,12 +67,8 @@ def check_fp8(case: Case, tokens=None, expert_choice=False):
         live = kept_tokens(orc["dest"], K, wl.n_shared)
     assert_permutation_equal(g, orc, "fp8")
     rows = np.arange(T) if tokens is None else tokens
-    h = case.h
-    y_ref = oracle.forward_rows(L, h["x"], orc["idx"], w, orc["dest"], h["W1"], h["W3"], h["W2"], h["Ws1"], h["Ws3"],
-                                h["Ws2"], tokens=rows,
-                                **{k: h[k] for k in ("S1", "S3", "S2", "Ss1", "Ss3", "Ss2")})
-    err, _ = y_error(host_f64(y)[rows], y_ref, "bf16", rows=live[rows])
-    assert err <= BF16_TOL, f"fp8: output error {err:.4g} > {BF16_TOL}"
+    y_ref = oracle_refs(L, case.h, orc["idx"], w, orc["dest"], tokens=rows)
+    err = assert_y_close(host_f64(y)[rows], y_ref, rows=live[rows], label="fp8", strict=strict)
     yb, _ = case.gpu_forward(logits_in=lg, out_dtype="bf16", expert_choice=expert_choice)
     assert torch.equal(yb.view(torch.int16), y.to(torch.bfloat16).view(torch.int16)), "bf16 output != rounded fp32"
     return err
@@ -113,18 +112,19 @@ def test_fp8_matches_dequantised_bf16_weights():
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["mixtral_decode", "switch_top1_capacity"])
+@pytest.mark.parametrize("name", ["mixtral_decode", "switch_top1_capacity", "mixtral_prefill", "deepseek_v3_fine"])
 def test_fp8_full_size(name):
+    """Routing over all tokens; outputs on tokens covering every (expert,
+    m-tile) of both GEMMs (all tokens of the decode step)."""
     case = Case(workload(name, wdtype="fp8"))
     T = case.wl.T
-    r = np.random.default_rng(0)
-    toks = None if T <= 64 else np.array(sorted({0, T - 1} | set(r.choice(T, 24, replace=False).tolist())))
-    print(name, check_fp8(case, tokens=toks))
+    toks = None if T <= 64 else tile_sample_tokens(case.oracle_route(), case.wl.K, T)
+    print(name, "tokens checked", T if toks is None else len(toks), check_fp8(case, tokens=toks))
 
 
 # E4M3 weights in stages of 32 k (the plans take stages of 64 k; the tuning
 # overrides select the 32-k kernels: 128 x 256 and 128 x 128 tiles)
-K32_ENV = {"MOE_GEMM_K64": "0", "MOE_GEMM_BM": "128", "MOE_GEMM_BM_DOWN": "128", "MOE_GEMM_BNB_UP": "256",
+K32_ENV = {"MOE_TUNING": "1", "MOE_GEMM_K64": "0", "MOE_GEMM_BM": "128", "MOE_GEMM_BM_DOWN": "128", "MOE_GEMM_BNB_UP": "256",
            "MOE_GEMM_NS_UP": "5", "MOE_GEMM_BNB_DOWN": "128", "MOE_GEMM_NS_DOWN": "6"}
 
 
