@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -186,9 +187,10 @@ Layout layout(const Shape& s) {
   L.sh_tab_down = take(s.S ? (size_t)ffn_table_entries(s.bf16, s.T, 1, s.d, false) * 16 : 0);
   L.sh_counts = take(2 * 4);
   L.h = take((size_t)s.max_rows * s.F * s.esz);
-  // xp: the routed rows (fp32 layers row-major; the fused bf16 path
-  // k-blocked); xkb: x k-blocked [d/32][T][32] (the other bf16 layers)
-  L.xp = take(!s.bf16 || s.fused ? (size_t)s.max_rows * s.d * s.esz : 0);
+  // xp: the routed rows (fp32 layers row-major; bf16 k-blocked: the fused
+  // path, or the dispatch when the gather is turned off for tuning); xkb: x
+  // k-blocked [d/kbw][T][kbw] (the other bf16 layers)
+  L.xp = take((size_t)s.max_rows * s.d * s.esz);
   L.xkb = take(s.bf16 && !s.fused ? (size_t)s.T * s.d * s.esz : 0);
   L.yp = take((size_t)s.max_rows * s.d * 4);
   L.sh_h = take((size_t)(s.S ? s.T * s.Fs : 0) * s.esz);
@@ -495,15 +497,27 @@ moe_status forward_impl(const moe_config* cfg, const Shape& s, const void* x, co
     rr.stats = nullptr;
   }
   // x k-blocked once for the bf16 layers that read it through the routing
-  // (and for the shared expert), before the shared expert forks off
+  // (and for the shared expert), before the shared expert forks off: in
+  // blocks of 64 k when every GEMM1 reading it takes stages of 64 k (a
+  // gathered row's piece of a stage is then one whole 128-byte line), else 32
+  const int64_t group_max = s.cap >= 0 ? std::min(s.T, s.cap) : s.T;
+  const FfnPlan plan = ffn_plan(s.bf16, s.w8, s.max_rows, group_max, s.E, s.F, s.d);
+  const bool gather = s.bf16 && !s.fused && !(tuning_enabled() && getenv("MOE_GATHER") &&
+                                             atoi(getenv("MOE_GATHER")) == 0);
+  int kbw = 0;  // 0: x is not k-blocked (fp32 layers, the fused path)
+  if (s.bf16 && !s.fused) {
+    const bool sh64 = !s.S || ffn_plan(s.bf16, s.w8, s.T, s.T, 1, s.Fs, s.d).k64_up;
+    kbw = (plan.k64_up || !gather) && sh64 && s.d % 64 == 0 ? 64 : 32;
+    if (!gather && !s.S) kbw = 0;  // nothing reads x k-blocked
+  }
   void* xkb = at<void>(ws, L.xkb);
-  if (s.bf16 && !s.fused) MOE_HIP(launch_kblock_copy(x, xkb, s.T, s.d * (int64_t)s.esz, hs));
+  if (kbw) MOE_HIP(launch_kblock_copy(x, xkb, s.T, s.d * (int64_t)s.esz, kbw, hs));
   // a8: the shared expert over all T rows of x
   float* sh_out = s.S ? at<float>(ws, L.sh_out) : nullptr;
   auto shared_ffn = [&](hipStream_t q) -> moe_status {
     int32_t* range = at<int32_t>(ws, L.sh_range);
     MOE_HIP(launch_set_range(range, s.T, q));
-    const AOperand xa = s.bf16 ? AOperand{xkb, s.T, nullptr, 1} : AOperand{x, 0, nullptr, 1};
+    const AOperand xa = kbw ? AOperand{xkb, s.T, nullptr, 1, kbw} : AOperand{x, 0, nullptr, 1, 32};
     return do_ffn(s, xa, range, 1, s.T, s.T, Ws1, Ws3, Ws2, sc.ws1, sc.ws3, sc.ws2, at<void>(ws, L.sh_h), sh_out,
                   at<int4>(ws, L.sh_tab_up), at<int4>(ws, L.sh_tab_down), at<int32_t>(ws, L.sh_counts), s.Fs, q,
                   nullptr, nullptr, false, true);
@@ -521,11 +535,9 @@ moe_status forward_impl(const moe_config* cfg, const Shape& s, const void* x, co
   const bool fused = s.fused;
   bool drop_done = false;
   void* xp = at<void>(ws, L.xp);
-  // the routed FFN's plan is known before routing: the scatter that runs on
-  // the final offsets writes its tile tables (one launch fewer); an expert
-  // holds at most one row per token, and at most its capacity
-  const int64_t group_max = s.cap >= 0 ? std::min(s.T, s.cap) : s.T;
-  const FfnPlan plan = ffn_plan(s.bf16, s.w8, s.max_rows, group_max, s.E, s.F, s.d);
+  // the routed FFN's plan (above) is known before routing: the scatter that
+  // runs on the final offsets writes its tile tables (one launch fewer); an
+  // expert holds at most one row per token, and at most its capacity
   const TileJob tj = tile_job(plan, s.F, s.d, at<int4>(ws, L.tab_up), at<int4>(ws, L.tab_down),
                               at<int32_t>(ws, L.counts));
   bool tiles_done = false;
@@ -541,9 +553,9 @@ moe_status forward_impl(const moe_config* cfg, const Shape& s, const void* x, co
     // tile one contiguous run), written by the scatter or the dispatch; the
     // other bf16 layers read x k-blocked through row_src (the a5 gather is
     // folded into GEMM1's loads); fp32 layers dispatch row-major rows
-    AOperand xa{xp, 0, nullptr, 1};
-    if (s.bf16 && !fused) {
-      xa = AOperand{xkb, s.T, rr.row_src, (int)s.K};
+    AOperand xa{xp, 0, nullptr, 1, 32};
+    if (gather) {
+      xa = AOperand{xkb, s.T, rr.row_src, (int)s.K, kbw};
     } else {
       if (!drop_done)
         MOE_HIP(launch_dispatch(x, rr.row_src, rr.offsets + s.E, xp, s.max_rows, s.K, s.d * (int64_t)s.esz, s.bf16,
@@ -665,7 +677,7 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* xp, const int32_t* 
   const moe_scales& sc = s.w8 ? *scales : none;
   // the plan assumes the routed bound of a group's rows (any rows stay correct)
   const int64_t group_max = s.cap >= 0 ? std::min(s.T, s.cap) : s.T;
-  return do_ffn(s, AOperand{xp, 0, nullptr, 1}, offsets, n_groups, max_rows, group_max, W1, W3, W2, sc.w1, sc.w3, sc.w2,
+  return do_ffn(s, AOperand{xp, 0, nullptr, 1, 32}, offsets, n_groups, max_rows, group_max, W1, W3, W2, sc.w1, sc.w3, sc.w2,
                 at<void>(ws, L.h), yp,
                 at<int4>(ws, L.tab_up), at<int4>(ws, L.tab_down), at<int32_t>(ws, L.counts), s.F,
                 (hipStream_t)stream);

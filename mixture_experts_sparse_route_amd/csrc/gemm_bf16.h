@@ -80,9 +80,12 @@ struct GemmArgs {
   CombineFuse fuse;        // down: y written through it when fuse.y is set
 };
 
-// A operand modes: row-major; k-blocked [Kdim/32][rows][32]; k-blocked with
-// the GEMM's rows gathered from A's rows through GemmArgs::gather.
-enum { AM_ROW = 0, AM_KB = 1, AM_GATHER = 2 };
+// A operand modes: row-major; k-blocked in blocks of 32 k ([Kdim/32][rows][32])
+// or 64 k ([Kdim/64][rows][64]); either k-blocked layout with the GEMM's rows
+// gathered from A's rows through GemmArgs::gather.  With 64-k blocks a
+// gathered row's piece of a 64-k stage is one whole 128-byte line (with
+// 32-k blocks it is two half lines in blocks far apart).
+enum { AM_ROW = 0, AM_KB = 1, AM_GATHER = 2, AM_KB64 = 3, AM_GATHER64 = 4 };
 
 __device__ __forceinline__ int lds_pos(int row, int chunk) { return row * RB + ((chunk ^ ((row >> 1) & 3)) << 4); }
 
@@ -205,12 +208,15 @@ struct Issuer {
   // weight bytes per stage and row
   static constexpr int WKS = WK == WK_BF16_64 ? 2 * RB : (WK == WK_E4M3_32 ? 32 : RB);
 
-  // A row stride: 32 for a k-blocked A (known at compile time), else the
-  // caller's
-  __device__ __forceinline__ static int64_t a_rs(const GemmArgs& p) { return AM != AM_ROW ? (int64_t)BKS : p.a_rs; }
+  static constexpr bool KB64 = AM == AM_KB64 || AM == AM_GATHER64;  // A in blocks of 64 k
+  // A row stride: the block width for a k-blocked A (known at compile time),
+  // else the caller's
+  __device__ __forceinline__ static int64_t a_rs(const GemmArgs& p) {
+    return AM == AM_ROW ? p.a_rs : (int64_t)(KB64 ? 2 * BKS : BKS);
+  }
   // the A row that GEMM row r reads
   __device__ __forceinline__ static int64_t a_row(const GemmArgs& p, int r) {
-    if constexpr (AM == AM_GATHER) return (int64_t)(p.gather[r] / p.gather_div);
+    if constexpr (AM == AM_GATHER || AM == AM_GATHER64) return (int64_t)(p.gather[r] / p.gather_div);
     return (int64_t)r;
   }
 
@@ -240,6 +246,8 @@ struct Issuer {
   __device__ __forceinline__ void setup(const GemmArgs& p, int wave, int lane) {
     const int rows = cur.rows, row_first = cur.row_first;
     if constexpr (!K64) {
+      // 32 k per stage; with 64-k blocks a stage is the half (kt & 1) of
+      // block kt >> 1 (issue adds the half's 64 bytes)
       const int r_l = lane >> 2, c_l = (lane & 3) ^ ((r_l >> 1) & 3);
       aks = p.a_ks * 2;
 #pragma unroll
@@ -249,11 +257,12 @@ struct Issuer {
       }
     } else {
       const int r8 = lane >> 3, ch = (lane & 7) ^ r8;
-      aks = p.a_ks * 4;
+      aks = KB64 ? p.a_ks * 2 : p.a_ks * 4;
 #pragma unroll
       for (int j = 0; j < NA; ++j) {
         const int row = min((wave + 4 * j) * 8 + r8, rows - 1);
-        ab[j] = (const char*)(p.A + a_row(p, row_first + row) * a_rs(p) + (int64_t)(ch >> 2) * p.a_ks + (ch & 3) * 8);
+        const int64_t kofs = KB64 ? (int64_t)ch * 8 : (int64_t)(ch >> 2) * p.a_ks + (ch & 3) * 8;
+        ab[j] = (const char*)(p.A + a_row(p, row_first + row) * a_rs(p) + kofs);
       }
     }
     if constexpr (WK == WK_BF16_64) {
@@ -281,7 +290,8 @@ struct Issuer {
       setup(p, wave, lane);
     }
     char* const st = lds + (s % NS) * STAGE;
-    const int64_t ao = (int64_t)kt * aks, wo = (int64_t)kt * WKS;
+    const int64_t ao = (!K64 && KB64) ? (int64_t)(kt >> 1) * aks + (kt & 1) * 2 * BKS : (int64_t)kt * aks;
+    const int64_t wo = (int64_t)kt * WKS;
 #pragma unroll
     for (int j = 0; j < NA; ++j)
       __builtin_amdgcn_global_load_lds(ab[j] + ao, (lds_ptr_t)(st + (wave + 4 * j) * (K64 ? 8 * 2 * RB : 16 * RB)), 16,
@@ -553,10 +563,11 @@ static inline int64_t launch_grid(const FfnPlan& pl, int64_t grid) {
   return pg < grid ? pg : grid;
 }
 
-// a_blk / c_blk: rows of a k-blocked A / h ([cols/32][rows][32]), 0 = row-major.
-static inline void set_layout(GemmArgs& a, int64_t a_blk, int64_t c_blk) {
-  a.a_rs = a_blk ? BKS : a.Kdim;
-  a.a_ks = a_blk ? BKS * a_blk : BKS;
+// a_blk / c_blk: rows of a k-blocked A / h ([cols/kbw][rows][kbw], kbw = 32
+// or 64 for A, 32 for h), 0 = row-major.
+static inline void set_layout(GemmArgs& a, int64_t a_blk, int64_t c_blk, int kbw = BKS) {
+  a.a_rs = a_blk ? kbw : a.Kdim;
+  a.a_ks = a_blk ? kbw * a_blk : BKS;
   a.c_rs = c_blk ? 32 : a.N;
   a.c_bs = c_blk ? 32 * c_blk : 32;
 }

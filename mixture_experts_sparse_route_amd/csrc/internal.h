@@ -134,8 +134,9 @@ hipError_t launch_expert_choice(float* logits, const float* part, int S, const f
 // row-major.
 hipError_t launch_dispatch(const void* x, const int32_t* row_src, const int32_t* R_ptr, void* xp, int64_t max_rows,
                            int64_t K, int64_t row_bytes, bool blocked, hipStream_t s);
-// x [T, d] bf16 -> k-blocked [d/32][T][32] (row_bytes = 2 d, a multiple of 64).
-hipError_t launch_kblock_copy(const void* x, void* xkb, int64_t T, int64_t row_bytes, hipStream_t s);
+// x [T, d] bf16 -> k-blocked [d/kbw][T][kbw], kbw = 32 or 64 (row_bytes = 2 d,
+// a multiple of 2 kbw).
+hipError_t launch_kblock_copy(const void* x, void* xkb, int64_t T, int64_t row_bytes, int kbw, hipStream_t s);
 
 // ---- grouped expert FFN (a6-a7) ----
 struct FfnPlan {
@@ -198,15 +199,17 @@ struct CombineFuse {
 };
 
 // The A operand of GEMM1: row-major [rows, Kdim] (blk_rows = 0) or k-blocked
-// [Kdim/32][blk_rows][32] (the 32 columns of a k-step of all rows are one
-// contiguous run).  gather non-null (k-blocked only): GEMM row r reads A row
-// gather[r] / gather_div -- the routed rows read the k-blocked x through the
-// routing's row_src (gather_div = K), so no per-row copy of x is made.
+// [Kdim/kbw][blk_rows][kbw] with kbw = 32 or 64 (the kbw columns of all rows
+// are one contiguous run).  gather non-null (k-blocked only): GEMM row r
+// reads A row gather[r] / gather_div -- the routed rows read the k-blocked x
+// through the routing's row_src (gather_div = K), so no per-row copy of x is
+// made.
 struct AOperand {
   const void* ptr;
   int64_t blk_rows;
   const int32_t* gather;
   int gather_div;
+  int kbw;
 };
 
 // bf16 MFMA path (gemm_bf16.hip); called through the launchers below.

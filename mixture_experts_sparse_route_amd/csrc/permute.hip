@@ -517,19 +517,18 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const V* __restrict__ x, 
 // The same into a k-blocked xp (bf16, [d/32][blk_rows][32]): workgroup b
 // moves rows 16b .. 16b+15; in each instruction a wave writes one 64-byte
 // k-block of those 16 rows, 1 KB contiguous (lane: row lane/4, 16-byte chunk
-// lane%4), reading 64 bytes of each row's token.  row_src == nullptr: row r
-// is x's row r and R_ptr == nullptr: R = R_host (x itself k-blocked).
+// lane%4), reading 64 bytes of each row's token.
 __global__ __launch_bounds__(256) void dispatch_blocked_kernel(const uint4* __restrict__ x,
                                                                const int32_t* __restrict__ row_src,
                                                                const int32_t* __restrict__ R_ptr,
                                                                uint4* __restrict__ xp, int K, int n_kb,
-                                                               int64_t blk_rows, int R_host) {
-  const int R = R_ptr ? *R_ptr : R_host;
+                                                               int64_t blk_rows) {
+  const int R = *R_ptr;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = blockIdx.x * 16 + (lane >> 2), c = lane & 3;
   if (blockIdx.x * 16 >= R) return;
   if (r >= R) return;
-  const uint4* src = x + (int64_t)(row_src ? row_src[r] / K : r) * n_kb * 4 + c;
+  const uint4* src = x + (int64_t)(row_src[r] / K) * n_kb * 4 + c;
   uint4* dst = xp + (int64_t)r * 4 + c;
   const int64_t kb_stride = blk_rows * 4;
   int kb = wave;
@@ -541,6 +540,31 @@ __global__ __launch_bounds__(256) void dispatch_blocked_kernel(const uint4* __re
     dst[(kb + 12) * kb_stride] = v3;
   }
   for (; kb < n_kb; kb += 4) dst[kb * kb_stride] = src[kb * 4];
+}
+
+// x itself k-blocked: [T, d] -> [d/kbw][T][kbw] with CPB = kbw / 8 16-byte
+// chunks per row and block.  Workgroup b takes rows 64/CPB * b onward; in each
+// instruction a wave writes one block of those rows, 1 KB contiguous (lane:
+// row lane / CPB, chunk lane % CPB), reading 2 kbw bytes of each row.
+template <int CPB>
+__global__ __launch_bounds__(256) void kblock_copy_kernel(const uint4* __restrict__ x, uint4* __restrict__ xkb, int T,
+                                                          int n_kb) {
+  constexpr int RPW = 64 / CPB;  // rows per workgroup
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = blockIdx.x * RPW + lane / CPB, c = lane % CPB;
+  if (r >= T) return;
+  const uint4* src = x + (int64_t)r * n_kb * CPB + c;
+  uint4* dst = xkb + (int64_t)r * CPB + c;
+  const int64_t kb_stride = (int64_t)T * CPB;
+  int kb = wave;
+  for (; kb + 12 < n_kb; kb += 16) {  // four blocks in flight per lane
+    const uint4 v0 = src[kb * CPB], v1 = src[(kb + 4) * CPB], v2 = src[(kb + 8) * CPB], v3 = src[(kb + 12) * CPB];
+    dst[kb * kb_stride] = v0;
+    dst[(kb + 4) * kb_stride] = v1;
+    dst[(kb + 8) * kb_stride] = v2;
+    dst[(kb + 12) * kb_stride] = v3;
+  }
+  for (; kb < n_kb; kb += 4) dst[kb * kb_stride] = src[kb * CPB];
 }
 
 // ------------------------------------------------------------ FFN tiles
@@ -668,7 +692,7 @@ hipError_t launch_dispatch(const void* x, const int32_t* row_src, const int32_t*
     if (nb == 0) return hipSuccess;
     prof_begin(K_DISPATCH, s);
     dispatch_blocked_kernel<<<nb, 256, 0, s>>>((const uint4*)x, row_src, R_ptr, (uint4*)xp, (int)K,
-                                               (int)(row_bytes / 64), max_rows, 0);
+                                               (int)(row_bytes / 64), max_rows);
     prof_end(K_DISPATCH, s);
     return hipGetLastError();
   }
@@ -705,13 +729,17 @@ TileJob tile_job(const FfnPlan& p, int64_t F, int64_t d, int4* tab_up, int4* tab
   return j;
 }
 
-hipError_t launch_kblock_copy(const void* x, void* xkb, int64_t T, int64_t row_bytes, hipStream_t s) {
-  if (row_bytes % 64 || T > INT32_MAX) return hipErrorInvalidValue;
-  const unsigned nb = (unsigned)((T + 15) / 16);
+hipError_t launch_kblock_copy(const void* x, void* xkb, int64_t T, int64_t row_bytes, int kbw, hipStream_t s) {
+  if ((kbw != 32 && kbw != 64) || row_bytes % (2 * kbw) || T > INT32_MAX) return hipErrorInvalidValue;
+  const int rpw = kbw == 64 ? 8 : 16;
+  const unsigned nb = (unsigned)((T + rpw - 1) / rpw);
   if (nb == 0) return hipSuccess;
+  const int n_kb = (int)(row_bytes / (2 * kbw));
   prof_begin(K_DISPATCH, s);
-  dispatch_blocked_kernel<<<nb, 256, 0, s>>>((const uint4*)x, nullptr, nullptr, (uint4*)xkb, 1, (int)(row_bytes / 64),
-                                             T, (int)T);
+  if (kbw == 64)
+    kblock_copy_kernel<8><<<nb, 256, 0, s>>>((const uint4*)x, (uint4*)xkb, (int)T, n_kb);
+  else
+    kblock_copy_kernel<4><<<nb, 256, 0, s>>>((const uint4*)x, (uint4*)xkb, (int)T, n_kb);
   prof_end(K_DISPATCH, s);
   return hipGetLastError();
 }

@@ -96,8 +96,13 @@ class Case:
 
     def __init__(self, wl):
         self.wl = wl
+        big = wl.E * wl.F * wl.d > 1e9
+        if big:
+            print(f"  inputs of {wl.name}: generating ...", flush=True)
         self.h = wl.gen_all()
         self.d = {k: dev(v) for k, v in self.h.items()}
+        if big:
+            print("  inputs on the device", flush=True)
         self.L = oracle.layer_of(wl)
         self._route = None
 
@@ -182,9 +187,14 @@ class Ref:
 
 def oracle_refs(L, h: dict, idx, w, dest, tokens=None) -> Ref:
     """Ref of oracle layer L (its round_h is ignored) on the inputs h."""
+    n = L.T if tokens is None else len(tokens)
+    big = n * L.d * max(L.F, 1) * min(L.K, 8) > 2e10   # minutes of oracle work: say so as it goes
+
     def run(rh):
         Lr = oracle.OrcLayer(L.T, L.d, L.F, L.E, L.K, L.gate, L.renorm, L.residual, L.bf16, L.capacity_factor,
                              L.n_shared, L.Fs, rh, L.w_fp8)
+        if big:
+            print(f"  oracle: {n} tokens, h {'in bf16' if rh else 'in double'} ...", flush=True)
         return oracle.forward_rows(Lr, h["x"], idx, w, dest, h["W1"], h["W3"], h["W2"], h["Ws1"], h["Ws3"],
                                    h["Ws2"], tokens=tokens, **scales_of(h))
     return Ref(run(0), run(1) if L.bf16 else None, bool(L.w_fp8))
@@ -240,19 +250,46 @@ def kept_tokens(dest: np.ndarray, K: int, n_shared: int) -> np.ndarray:
 
 
 def tile_sample_tokens(orc: dict, K: int, T: int, extra=()) -> np.ndarray:
-    """Tokens whose rows cover every m-tile of both grouped GEMMs under any
-    tile plan: every m-tile starts 32 * j rows into its expert's group (tiles
-    are 64, 128 or 192 rows, or a group split evenly in 32-row units), so the
-    rows at multiples of 32 within each group, and each group's last row,
-    hold a checked output; every column tile of those rows is checked with
-    them."""
+    """A small set of tokens whose rows cover every m-tile of both grouped
+    GEMMs under any tile plan.  Every m-tile starts 32 * j rows into its
+    expert's group (tiles are 64, 128, 192 or 256 rows, or a group split
+    evenly in 32-row units), so a checked row in every 32-row unit of every
+    group, and in each group's last row, puts one in every m-tile; every
+    column tile of those rows is checked with them.  A token's K rows lie in
+    K different groups, so the units are covered greedily: each pick is the
+    token that covers the most units still uncovered (ties: lower token)."""
     off, rs = orc["offsets"], orc["row_src"]
-    rows = []
-    for e in range(len(off) - 1):
-        a, b = int(off[e]), int(off[e + 1])
-        if b > a:
-            rows.extend(range(a, b, 32))
-            rows.append(b - 1)
-    toks = set((rs[np.array(rows, dtype=np.int64)] // K).tolist()) if rows else set()
-    toks |= {0, T - 1} | set(int(t) for t in extra)
-    return np.array(sorted(toks), dtype=np.int64)
+    R = int(off[-1])
+    if R == 0:
+        return np.array(sorted({0, T - 1} | set(int(t) for t in extra)), dtype=np.int64)
+    grp = np.searchsorted(off, np.arange(R), side="right") - 1
+    pos = np.arange(R) - off[grp]
+    last = np.arange(R) == off[grp + 1] - 1
+    # unit ids: (group, 32-row unit) and, separately, each group's last row
+    base = np.concatenate([[0], np.cumsum((np.diff(off) + 31) // 32)])
+    unit = base[grp] + pos // 32
+    n_units = int(base[-1])
+    units = [unit, np.where(last, n_units + grp, -1)]
+    tok = rs[:R] // K
+    covered = np.zeros(n_units + len(off) - 1, bool)
+    covered[n_units:] = True
+    covered[n_units + grp[last]] = False
+    picks = {0, T - 1} | set(int(t) for t in extra)
+
+    def cover(t):
+        for u in units:
+            uu = u[tok == t]
+            covered[uu[uu >= 0]] = True
+
+    for t in sorted(picks):
+        cover(t)
+    while not covered.all():
+        gain = np.zeros(T, np.int64)
+        for u in units:
+            ok = u >= 0
+            ok[ok] = ~covered[u[ok]]
+            np.add.at(gain, tok[ok], 1)
+        t = int(np.argmax(gain))
+        picks.add(t)
+        cover(t)
+    return np.array(sorted(picks), dtype=np.int64)
