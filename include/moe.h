@@ -289,6 +289,27 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* Wg, co
                        const void* Ws3, const void* Ws2, const moe_scales* scales, void* y, const moe_routing* r,
                        void* ws, size_t ws_bytes, moe_stream_t stream);
 
+/* ---- The same forward without any allocation -----------------------------
+ * For callers that cannot allocate device memory or create streams or events
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * it): moe_forward with the same arguments and results, minus the workspace.
+ * Its scratch is a built-in device array of MOE_NOALLOC_SCRATCH_BYTES per
+ * GPU (held from the library's load on that GPU until the process ends); a
+ * layer whose moe_workspace_size exceeds it returns MOE_ERR_WORKSPACE before
+ * any launch.  The call allocates nothing (no hipMalloc / hipFree, no stream
+ * or event creation): the shared expert runs in order on `stream`, and the
+ * per-kernel timing facility is not applied.  `stream` must belong to the
+ * current device (else MOE_ERR_INVALID_ARG).  Every call on one GPU uses that
+ * GPU's one array and leaves its contents behind (no part of it needs to
+ * start at zero): calls that overlap on one GPU -- on different streams
+ * without ordering, or from different threads -- race and corrupt each
+ * other's results; order them on one stream. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_forward_noalloc(const moe_config* cfg, const void* x, const float* Wg, const float* logit_bias,
+                               const float* sel_bias, const void* W1, const void* W3, const void* W2, const void* Ws1,
+                               const void* Ws3, const void* Ws2, const moe_scales* scales, void* y,
+                               const moe_routing* r, moe_stream_t stream);
+
 /* Static string for a status code. */
 const char* moe_status_string(moe_status s);
 

@@ -80,6 +80,7 @@ def load_library(path: str = LIB_PATH):
         "moe_expert_ffn": [C, vp, vp, i64, i64, vp, vp, vp, ctypes.POINTER(MoeScales), vp, vp, sz, vp],
         "moe_combine": [C, vp, R, vp, vp, vp, vp],
         "moe_forward": [C, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(MoeScales), vp, R, vp, sz, vp],
+        "moe_forward_noalloc": [C, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(MoeScales), vp, R, vp],
         "moe_profile_enable": [ctypes.c_uint32],
         "moe_profile_reset": [],
         "moe_profile_read": [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)],
@@ -279,6 +280,22 @@ def moe_forward(spec, x, Wg, logit_bias, sel_bias, W1, W3, W2, Ws1, Ws3, Ws2, y,
                                       _scales(scales), _ptr(y),
                                       ctypes.byref(r) if r is not None else None, _ws_ptr(ws), _ws_bytes(ws),
                                       _stream(stream)), "moe_forward")
+
+
+# Bytes of the built-in scratch array of moe_forward_noalloc (per GPU).
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_forward_noalloc(spec, x, Wg, logit_bias, sel_bias, W1, W3, W2, Ws1, Ws3, Ws2, y,
+                        routing: Optional[Routing], stream=None, scales=None):
+    """moe_forward without a workspace: the library's built-in scratch array
+    of NOALLOC_SCRATCH_BYTES per GPU (see moe.h); allocates nothing."""
+    r = routing.struct() if routing is not None else None
+    _check(load_library().moe_forward_noalloc(ctypes.byref(_cfg(spec)), _ptr(x), _ptr(Wg), _ptr(logit_bias),
+                                              _ptr(sel_bias), _ptr(W1), _ptr(W3), _ptr(W2), _ptr(Ws1), _ptr(Ws3),
+                                              _ptr(Ws2), _scales(scales), _ptr(y),
+                                              ctypes.byref(r) if r is not None else None, _stream(stream)),
+           "moe_forward_noalloc")
 
 
 # ---------------------------------------------------------------- profiling --

@@ -12,6 +12,7 @@
 #include <string>
 #include <vector>
 
+#include "api_internal.h"
 #include "internal.h"
 #include "moe.h"
 
@@ -584,15 +585,19 @@ const char* const kNames[K_COUNT] = {"router_logits", "router_topk",  "route_sca
 
 const char* kernel_name(int id) { return (id >= 0 && id < K_COUNT) ? kNames[id] : nullptr; }
 
+// Set while the calling thread is inside moe_forward_noalloc: the timing
+// facility creates events on demand, which that entry point must not do.
+thread_local bool g_no_timing = false;
+
 void prof_begin(int id, hipStream_t s) {
-  if (!(g_prof >> id & 1u)) return;
+  if (!(g_prof >> id & 1u) || g_no_timing) return;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_open = get_event();
   if (g_open) (void)hipEventRecord(g_open, s);
 }
 
 void prof_end(int id, hipStream_t s) {
-  if (!(g_prof >> id & 1u)) return;
+  if (!(g_prof >> id & 1u) || g_no_timing) return;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   if (!g_open) return;
   hipEvent_t b = get_event();
@@ -601,6 +606,26 @@ void prof_end(int id, hipStream_t s) {
   g_recs.push_back(ProfRec{id, g_open, b});
   g_open = nullptr;
 }
+
+moe_status forward_in_scratch(const moe_config* cfg, const void* x, const float* Wg, const float* logit_bias,
+                              const float* sel_bias, const void* W1, const void* W3, const void* W2,
+                              const void* Ws1, const void* Ws3, const void* Ws2, const moe_scales* scales, void* y,
+                              const moe_routing* r, void* ws, size_t ws_bytes, hipStream_t hs) {
+  Shape s;
+  moe_status st = validate(cfg, &s);
+  if (st != MOE_OK) return st;
+  const size_t need = layout(s).total;
+  if (need > ws_bytes)
+    return fail(MOE_ERR_WORKSPACE, "this layer needs %zu bytes of scratch, more than the %zu available; call "
+                "moe_forward with a workspace", need, ws_bytes);
+  g_no_timing = true;
+  st = forward_impl(cfg, s, x, Wg, logit_bias, sel_bias, W1, W3, W2, Ws1, Ws3, Ws2, scales, y, r, ws, ws_bytes, hs,
+                    false);
+  g_no_timing = false;
+  return st;
+}
+
+moe_status fail_detail(moe_status s, const char* msg) { return fail(s, "%s", msg); }
 
 }  // namespace moe
 

@@ -260,3 +260,13 @@ def test_bench_refuses_more_than_one_gpu():
                            timeout=120, env={**os.environ, **env}, cwd=ROOT)
         assert p.returncode == 2, (args, env, p.returncode, p.stderr[-500:])
         assert "one GPU only" in p.stderr and p.stdout == ""
+
+
+def test_noalloc_rejects_a_layer_larger_than_its_scratch(lib):
+    """moe_forward_noalloc checks the layer's scratch need against its
+    built-in array on the host, before any HIP call (this machine has no
+    GPU: a call that got further would fail with MOE_ERR_HIP)."""
+    sp = spec(tokens=4096, d_model=4096, d_ff=14336, n_experts=8, top_k=2)
+    assert moe.workspace_size(sp) > moe.NOALLOC_SCRATCH_BYTES
+    st = lib.moe_forward_noalloc(ctypes.byref(moe._cfg(sp)), *([None] * 10), None, None, None, None)
+    assert st == moe.MOE_ERR_WORKSPACE and b"built-in" in lib.moe_last_error()
