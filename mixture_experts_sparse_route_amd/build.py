@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["gemm_bf16_up.hip", "gemm_bf16.hip", "router.hip", "permute.hip", "expert_choice.hip", "gemm_f32.hip",
+SOURCES = ["gemm_bf16_up.hip", "gemm_bf16.hip", "gemm_stream.hip", "router.hip", "permute.hip", "expert_choice.hip", "gemm_f32.hip",
            "combine.hip", "api.cpp", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",

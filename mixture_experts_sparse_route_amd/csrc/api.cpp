@@ -364,12 +364,12 @@ moe_status do_ffn(const Shape& s, const AOperand& A, const int32_t* offsets, int
                   const CombineFuse* fuse = nullptr, const FfnPlan* plan_in = nullptr, bool tiles_ready = false,
                   bool shared = false) {
   const FfnPlan plan = plan_in ? *plan_in : ffn_plan(s.bf16, s.w8, max_rows, group_max, n_groups, F, s.d);
-  if (!tiles_ready)
+  if (!tiles_ready && !(s.bf16 && plan.stream_up && plan.stream_down))
     MOE_HIP(launch_ffn_tiles(plan, offsets, n_groups, max_rows, F, s.d, tab_up, tab_down, counts, st));
-  MOE_HIP(launch_gemm_gate_up(s.bf16, plan, A, tab_up, counts, n_groups, max_rows, W1, W3, s1, s3, h, F, s.d,
+  MOE_HIP(launch_gemm_gate_up(s.bf16, plan, A, tab_up, counts, offsets, n_groups, max_rows, W1, W3, s1, s3, h, F, s.d,
                               st, shared ? K_SHARED_GATE_UP : K_GEMM_GATE_UP));
-  MOE_HIP(launch_gemm_down(s.bf16, plan, h, tab_down, counts + 1, n_groups, max_rows, W2, s2, yp, fuse, F, s.d, st,
-                           shared ? K_SHARED_DOWN : K_GEMM_DOWN));
+  MOE_HIP(launch_gemm_down(s.bf16, plan, h, tab_down, counts + 1, offsets, n_groups, max_rows, W2, s2, yp, fuse, F,
+                           s.d, st, shared ? K_SHARED_DOWN : K_GEMM_DOWN));
   return MOE_OK;
 }
 
@@ -502,13 +502,16 @@ moe_status forward_impl(const moe_config* cfg, const Shape& s, const void* x, co
   // blocks of 64 k when every GEMM1 reading it takes stages of 64 k (a
   // gathered row's piece of a stage is then one whole 128-byte line), else 32
   const int64_t group_max = s.cap >= 0 ? std::min(s.T, s.cap) : s.T;
-  const FfnPlan plan = ffn_plan(s.bf16, s.w8, s.max_rows, group_max, s.E, s.F, s.d);
+  FfnPlan plan = ffn_plan(s.bf16, s.w8, s.max_rows, group_max, s.E, s.F, s.d);
+  if (s.fused) plan.stream_down = false;  // the fused GEMM2 epilogue is the tile kernel's
   const bool gather = s.bf16 && !s.fused && !(tuning_enabled() && getenv("MOE_GATHER") &&
                                              atoi(getenv("MOE_GATHER")) == 0);
   int kbw = 0;  // 0: x is not k-blocked (fp32 layers, the fused path)
   if (s.bf16 && !s.fused) {
-    const bool sh64 = !s.S || ffn_plan(s.bf16, s.w8, s.T, s.T, 1, s.Fs, s.d).k64_up;
-    kbw = (plan.k64_up || !gather) && sh64 && s.d % 64 == 0 ? 64 : 32;
+    // the weight-streaming kernels read A in blocks of 32 k
+    auto wants64 = [](const FfnPlan& q) { return q.k64_up && !q.stream_up; };
+    const bool sh64 = !s.S || wants64(ffn_plan(s.bf16, s.w8, s.T, s.T, 1, s.Fs, s.d));
+    kbw = (wants64(plan) || !gather) && sh64 && s.d % 64 == 0 ? 64 : 32;
     if (!gather && !s.S) kbw = 0;  // nothing reads x k-blocked
   }
   void* xkb = at<void>(ws, L.xkb);
@@ -545,7 +548,7 @@ moe_status forward_impl(const moe_config* cfg, const Shape& s, const void* x, co
   // on the fused path the scatter also does the dispatch (one row per kept token)
   if ((st = do_route(cfg, s, L, x, Wg, logit_bias, sel_bias, rr, ws, hs, fused ? y : nullptr,
                      residual ? x : nullptr, &drop_done, fused && s.max_rows > 0 ? xp : nullptr, s.max_rows,
-                     s.max_rows > 0 ? &tj : nullptr, &tiles_done)) != MOE_OK)
+                     s.max_rows > 0 && !(plan.stream_up && plan.stream_down) ? &tj : nullptr, &tiles_done)) != MOE_OK)
     return st;
   float* yp = at<float>(ws, L.yp);
   const CombineFuse fuse{rr.row_src, rr.topk_w, residual ? x : nullptr, y, s.bf16, s.out_bf16};

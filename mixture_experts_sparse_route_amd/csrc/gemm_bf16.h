@@ -544,7 +544,8 @@ __global__ __launch_bounds__(256, NS* stage_bytes<WK>(BM, BNB) <= LDS_BYTES / 2 
 #define MOE_GEMM8K64_CONFIGS(X) X(64, 256, 3) X(128, 128, 3) X(128, 128, 2) X(64, 128, 5) X(64, 128, 4) X(64, 128, 2) \
   X(192, 128, 2) X(192, 128, 3)
 #define MOE_GEMM16K64_CONFIGS(X) X(192, 128, 3) X(192, 128, 2) X(128, 128, 3) X(128, 128, 2) X(64, 128, 3) \
-  X(64, 128, 2) X(64, 256, 3) X(128, 256, 2) X(64, 128, 5) X(64, 256, 2) X(256, 128, 2)
+  X(64, 128, 2) X(64, 256, 3) X(128, 256, 2) X(64, 128, 5) X(64, 256, 2) X(256, 128, 2) X(192, 128, 4) \
+  X(128, 256, 3) X(96, 128, 5)
 
 // every configuration fits the tile tables' sizing
 #define MOE_FITS_TABLES(B, W, N) \

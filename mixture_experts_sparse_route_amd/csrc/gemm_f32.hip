@@ -204,6 +204,14 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_
   };
   shallow(d, p.k64_up, p.ns_up, p.bnb_up);
   shallow(F, p.k64_down, p.ns_down, p.bnb_down);
+  // bf16 weights and at most 32 rows in any group (decode-sized batches):
+  // GEMM2 is the weight-streaming kernel, which reads 512 bytes of each
+  // weight row per load batch instead of 128 per LDS stage (same box, Mixtral
+  // decode: down 196-197 -> 179-182 us on its 28 KB rows; 185-189 with
+  // 256-byte batches); GEMM1 keeps the tile kernel (its 8 KB rows stream at
+  // 6.1-6.4 TB/s there; the streaming GEMM1 measured 351-370 against
+  // 307-317 us on the same box)
+  if (!w8 && n_groups > 0 && group_max <= 32) p.stream_down = true;
   // overrides for tuning, honoured with MOE_TUNING=1 only: MOE_GEMM_K64
   // (both GEMMs in stages of 64 k, 0 or 1), MOE_GEMM_K64_DOWN, MOE_GEMM_BM, MOE_GEMM_BM_DOWN,
   // MOE_GEMM_{BNB,NS}_{UP,DOWN}, MOE_GEMM_WGS, MOE_GEMM_EVEN_UP; a set that names no compiled
@@ -220,6 +228,11 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_
   p.ns_down = env_int("MOE_GEMM_NS_DOWN", p.ns_down);
   p.wg_per_cu = env_int("MOE_GEMM_WGS", p.wg_per_cu);
   p.even_up = env_int("MOE_GEMM_EVEN_UP", p.even_up ? 1 : 0) != 0;
+  const int st_env = env_int("MOE_GEMM_STREAM", -1);  // both GEMMs
+  if (st_env >= 0) p.stream_up = p.stream_down = st_env != 0;
+  p.stream_up = env_int("MOE_GEMM_STREAM_UP", p.stream_up ? 1 : 0) != 0 && !w8;
+  p.stream_down = env_int("MOE_GEMM_STREAM_DOWN", p.stream_down ? 1 : 0) != 0 && !w8;
+  p.stream_u = env_int("MOE_GEMM_STREAM_U", p.stream_u);
   if (!gemm_bf16_has_config(w8, p.k64_up, p.bm, p.bnb_up, p.ns_up) ||
       !gemm_bf16_has_config(w8, p.k64_down, p.bm_down, p.bnb_down, p.ns_down) ||
       d / (p.k64_up ? 64 : 32) < p.ns_up - 1 || F / (p.k64_down ? 64 : 32) < p.ns_down - 1)
@@ -247,14 +260,17 @@ static int64_t grid_of(int bm, int64_t max_rows, int64_t n_groups, int64_t n_col
 }
 
 hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const AOperand& A, const int4* tab,
-                               const int32_t* count, int64_t n_groups, int64_t max_rows, const void* W1, const void* W3,
+                               const int32_t* count, const int32_t* offsets, int64_t n_groups, int64_t max_rows,
+                               const void* W1, const void* W3,
                                const float* s1, const float* s3, void* h, int64_t F, int64_t d, hipStream_t s,
                                int prof_id) {
   const int64_t grid = grid_of(p.bm, max_rows, n_groups, F, p.bn_out_up);
   if (grid == 0) return hipSuccess;
   prof_begin(prof_id, s);
   hipError_t err;
-  if (bf16) {
+  if (bf16 && p.stream_up) {
+    err = stream_gate_up(A, offsets, n_groups, W1, W3, h, max_rows, F, d, s);
+  } else if (bf16) {
     err = gemm_bf16_gate_up(p, A, tab, count, grid, W1, W3, s1, s3, h, max_rows, F, d, s);
   } else {
     F32Args a{(const float*)A.ptr, (const float*)W1, (const float*)W3, (float*)h, tab, count, (int)F, (int)d};
@@ -266,14 +282,16 @@ hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const AOperand& A, c
 }
 
 hipError_t launch_gemm_down(bool bf16, const FfnPlan& p, const void* h, const int4* tab, const int32_t* count,
-                            int64_t n_groups, int64_t max_rows, const void* W2, const float* s2, float* yp,
-                            const CombineFuse* fuse, int64_t F, int64_t d, hipStream_t s, int prof_id) {
-  if (fuse && !bf16) return hipErrorInvalidValue;
+                            const int32_t* offsets, int64_t n_groups, int64_t max_rows, const void* W2, const float* s2,
+                            float* yp, const CombineFuse* fuse, int64_t F, int64_t d, hipStream_t s, int prof_id) {
+  if ((fuse && !bf16) || (fuse && p.stream_down)) return hipErrorInvalidValue;
   const int64_t grid = grid_of(p.bm_down, max_rows, n_groups, d, p.bn_out_down);
   if (grid == 0) return hipSuccess;
   prof_begin(prof_id, s);
   hipError_t err;
-  if (bf16) {
+  if (bf16 && p.stream_down) {
+    err = stream_down(h, max_rows, offsets, n_groups, W2, yp, F, d, p.stream_u, s);
+  } else if (bf16) {
     err = gemm_bf16_down(p, h, max_rows, tab, count, grid, W2, s2, yp, fuse, F, d, s);
   } else {
     F32Args a{(const float*)h, (const float*)W2, nullptr, yp, tab, count, (int)d, (int)F};

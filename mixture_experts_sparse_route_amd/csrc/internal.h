@@ -156,6 +156,11 @@ struct FfnPlan {
   // bm-row tiles and a remainder, so the m-tiles that share a weight tile
   // stay in step (MFMA-bound groups of 512 rows or more on average)
   bool even_up = false;
+  // bf16 weights, at most 32 rows in any group: GEMM1 / GEMM2 are the
+  // weight-streaming kernels (gemm_stream.hip; they need no tile table)
+  bool stream_up = false;
+  bool stream_down = false;
+  int stream_u = 8;  // GEMM2's 32-k steps per load batch (8 or 4)
 };
 // Compute units of the current device (queried once).
 int device_cus();
@@ -212,6 +217,16 @@ struct AOperand {
   int kbw;
 };
 
+// Weight-streaming GEMMs (gemm_stream.hip) for plans with p.stream_*: groups
+// from offsets directly; A k-blocked in blocks of 32 k or row-major; h
+// k-blocked with h_blk rows; yp row-major fp32.
+hipError_t stream_gate_up(const AOperand& A, const int32_t* offsets, int64_t n_groups, const void* W1, const void* W3,
+                          void* h, int64_t h_blk, int64_t F, int64_t d, hipStream_t s);
+// u_max: 32-k steps per load batch of GEMM2 (8 or 4; fewer when K / 32 is
+// not a multiple).
+hipError_t stream_down(const void* h, int64_t h_blk, const int32_t* offsets, int64_t n_groups, const void* W2,
+                       float* yp, int64_t F, int64_t d, int u_max, hipStream_t s);
+
 // bf16 MFMA path (gemm_bf16.hip); called through the launchers below.
 // s1 / s3 / s2: [groups, N] row scales of E4M3 weights (p.w8), else unused.
 // a_blk / h_blk: the row count R of a k-blocked operand ([cols/32][R][32]:
@@ -227,12 +242,14 @@ hipError_t gemm_bf16_down(const FfnPlan& p, const void* h, int64_t h_blk, const 
 // prof_id: the timing facility's kernel id of the launch (the routed or the
 // shared expert's GEMM).
 hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const AOperand& A, const int4* tab,
-                               const int32_t* count, int64_t n_groups, int64_t max_rows, const void* W1, const void* W3,
+                               const int32_t* count, const int32_t* offsets, int64_t n_groups, int64_t max_rows,
+                               const void* W1, const void* W3,
                                const float* s1, const float* s3, void* h, int64_t F, int64_t d, hipStream_t s,
                                int prof_id = K_GEMM_GATE_UP);
 // fuse (bf16 only, nullable): write y instead of yp.
 hipError_t launch_gemm_down(bool bf16, const FfnPlan& p, const void* h, const int4* tab, const int32_t* count,
-                            int64_t n_groups, int64_t max_rows, const void* W2, const float* s2, float* yp,
+                            const int32_t* offsets, int64_t n_groups, int64_t max_rows, const void* W2, const float* s2,
+                            float* yp,
                             const CombineFuse* fuse, int64_t F, int64_t d, hipStream_t s,
                             int prof_id = K_GEMM_DOWN);
 

@@ -238,6 +238,59 @@ def test_plan_overrides_bitwise_identical(over, monkeypatch):
     assert torch.equal(y0.view(torch.int32), y1.view(torch.int32)), f"plan override {over} changed the output"
 
 
+# Decode-sized groups (at most 32 rows per expert) take the weight-streaming
+# GEMM2 (and, forced with MOE_GEMM_STREAM=1, GEMM1); they must give the tile
+# kernels' outputs (MOE_GEMM_STREAM=0) bit for bit: same MFMAs, fragments
+# and k order.
+STREAM_CASES = {
+    "decode_small": workload("mixtral_decode", T=5, d=512, F=1024),
+    "two_row_blocks": workload("mixtral_decode", T=30, d=256, F=384, E=2, K=2),   # groups of 30 rows
+    "shared_expert": workload("deepseek_v3_fine", T=24, d=256, F=128, E=16, K=4, Fs=192),
+    "short_reduction": workload("mixtral_decode", T=6, d=64, F=64),
+}
+
+
+@pytest.mark.parametrize("name", list(STREAM_CASES))
+def test_stream_plan_bitwise_identical(name, monkeypatch):
+    case = Case(STREAM_CASES[name])
+    y_default, _ = case.gpu_forward(out_dtype="f32")
+    monkeypatch.setenv("MOE_TUNING", "1")
+    for both in ("1", "0"):
+        monkeypatch.setenv("MOE_GEMM_STREAM", both)
+        y, _ = case.gpu_forward(out_dtype="f32")
+        assert torch.equal(y_default.view(torch.int32), y.view(torch.int32)), f"MOE_GEMM_STREAM={both} differs"
+    monkeypatch.delenv("MOE_GEMM_STREAM")
+    print(name, check_case(case))
+
+
+def test_stream_group_over_32_rows(monkeypatch):
+    """moe_expert_ffn with a caller's group of 40 rows under a decode-sized
+    config (the plan streams): the kernel walks the rows in chunks of 32; the
+    output equals the tile kernels' bit for bit."""
+    wl = workload("mixtral_decode", T=32, d=256, F=256, E=4, K=2)
+    case = Case(wl)
+    spec = spec_of(wl)
+    mr = moe.max_rows(spec)
+    rows = 40
+    xp = case.d["x"].repeat(2, 1)[:mr].contiguous()
+    offs = torch.tensor([0, rows], dtype=torch.int32, device="cuda")
+    out = []
+    for stream in ("1", "0"):
+        monkeypatch.setenv("MOE_TUNING", "1")
+        monkeypatch.setenv("MOE_GEMM_STREAM", stream)
+        ws, _ = moe.alloc_workspace(spec)
+        yp = torch.full((mr, wl.d), float("nan"), dtype=torch.float32, device="cuda")
+        moe.moe_expert_ffn(spec, xp, offs, 1, rows, case.d["W1"], case.d["W3"], case.d["W2"], yp, ws)
+        torch.cuda.synchronize()
+        out.append(yp[:rows].clone())
+    assert torch.equal(out[0].view(torch.int32), out[1].view(torch.int32))
+    ref = np.stack([oracle.swiglu(case.h["W1"][0], case.h["W3"][0], case.h["W2"][0],
+                                  moe_synth.bf16_to_f32(case.h["x"][i % wl.T]).astype(np.float64), bf16=True)
+                    for i in range(rows)])
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert np.max(np.abs(host_f64(out[0]) - ref)) <= 2e-2 * rms
+
+
 def test_single_token():
     rep = check_case(Case(workload("deepseek_v3_fine", T=1, d=256, F=128, E=16, K=3, Fs=128)))
     print(rep)
