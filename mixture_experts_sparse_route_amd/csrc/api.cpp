@@ -289,8 +289,12 @@ moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const 
                                nullptr, nullptr, nullptr, 0, s.T, s.E, s.K, c->gate, false, true, st));
   }
   int32_t* dem_off = aff ? at<int32_t>(ws, L.dem_off) : nullptr;
-  MOE_HIP(launch_route_scan(blk_count, blk_base, r.counts, r.offsets, s.n_chunks, s.E, s.cap, blk_P, blk_z,
-                            s.stats ? r.stats : nullptr, s.T, s.K, nullptr, dem_off, st));
+  // one chunk with first-come drops and no statistics (decode-sized batches):
+  // the scatter does the capacity scan itself, one launch fewer
+  const bool one = s.n_chunks == 1 && !aff && !rr && !s.stats;
+  if (!one)
+    MOE_HIP(launch_route_scan(blk_count, blk_base, r.counts, r.offsets, s.n_chunks, s.E, s.cap, blk_P, blk_z,
+                              s.stats ? r.stats : nullptr, s.T, s.K, nullptr, dem_off, st));
   RouteScatter sc{};
   sc.idx = r.topk_idx;
   sc.blk_base = blk_base;
@@ -334,6 +338,11 @@ moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const 
   } else {
     sc.mode = kFirstCome;
     if (tiles) sc.tiles = *tiles;
+    if (one) {
+      sc.one_count = blk_count;
+      sc.one_counts = r.counts;
+      sc.one_offsets = r.offsets;
+    }
     if (drop_y && s.K == 1 && s.S == 0 && s.bf16 && s.d % 8 == 0) {
       sc.drop_y = drop_y;
       sc.drop_x = (const uint16_t*)drop_x;
@@ -504,15 +513,21 @@ moe_status forward_impl(const moe_config* cfg, const Shape& s, const void* x, co
   const int64_t group_max = s.cap >= 0 ? std::min(s.T, s.cap) : s.T;
   FfnPlan plan = ffn_plan(s.bf16, s.w8, s.max_rows, group_max, s.E, s.F, s.d);
   if (s.fused) plan.stream_down = false;  // the fused GEMM2 epilogue is the tile kernel's
-  const bool gather = s.bf16 && !s.fused && !(tuning_enabled() && getenv("MOE_GATHER") &&
-                                             atoi(getenv("MOE_GATHER")) == 0);
+  // decode-sized batches (at most 64 tokens) read the rows from x itself,
+  // row-major (x is then a few hundred KB and stays in L2; the copy would
+  // cost a launch); tuning: MOE_GATHER=0 dispatches a per-row copy instead,
+  // =1 always copies, =2 always reads x row-major
+  const int gather_env = tuning_enabled() && getenv("MOE_GATHER") ? atoi(getenv("MOE_GATHER")) : -1;
+  const bool gather = s.bf16 && !s.fused && gather_env != 0;
+  const bool gather_row = gather && (gather_env == 2 || (gather_env == -1 && s.T <= 64));
   int kbw = 0;  // 0: x is not k-blocked (fp32 layers, the fused path)
   if (s.bf16 && !s.fused) {
     // the weight-streaming kernels read A in blocks of 32 k
     auto wants64 = [](const FfnPlan& q) { return q.k64_up && !q.stream_up; };
     const bool sh64 = !s.S || wants64(ffn_plan(s.bf16, s.w8, s.T, s.T, 1, s.Fs, s.d));
     kbw = (wants64(plan) || !gather) && sh64 && s.d % 64 == 0 ? 64 : 32;
-    if (!gather && !s.S) kbw = 0;  // nothing reads x k-blocked
+    if ((!gather || gather_row) && !s.S) kbw = 0;  // nothing reads x k-blocked
+    if (gather_row) kbw = 0;
   }
   void* xkb = at<void>(ws, L.xkb);
   if (kbw) MOE_HIP(launch_kblock_copy(x, xkb, s.T, s.d * (int64_t)s.esz, kbw, hs));
@@ -558,7 +573,9 @@ moe_status forward_impl(const moe_config* cfg, const Shape& s, const void* x, co
     // other bf16 layers read x k-blocked through row_src (the a5 gather is
     // folded into GEMM1's loads); fp32 layers dispatch row-major rows
     AOperand xa{xp, 0, nullptr, 1, 32};
-    if (gather) {
+    if (gather_row) {
+      xa = AOperand{x, 0, rr.row_src, (int)s.K, 32};
+    } else if (gather) {
       xa = AOperand{xkb, s.T, rr.row_src, (int)s.K, kbw};
     } else {
       if (!drop_done)

@@ -84,8 +84,9 @@ struct GemmArgs {
 // or 64 k ([Kdim/64][rows][64]); either k-blocked layout with the GEMM's rows
 // gathered from A's rows through GemmArgs::gather.  With 64-k blocks a
 // gathered row's piece of a 64-k stage is one whole 128-byte line (with
-// 32-k blocks it is two half lines in blocks far apart).
-enum { AM_ROW = 0, AM_KB = 1, AM_GATHER = 2, AM_KB64 = 3, AM_GATHER64 = 4 };
+// 32-k blocks it is two half lines in blocks far apart); or row-major with
+// the rows gathered (a 64-k stage's piece of a row is then also one line).
+enum { AM_ROW = 0, AM_KB = 1, AM_GATHER = 2, AM_KB64 = 3, AM_GATHER64 = 4, AM_GATHER_ROW = 5 };
 
 __device__ __forceinline__ int lds_pos(int row, int chunk) { return row * RB + ((chunk ^ ((row >> 1) & 3)) << 4); }
 
@@ -212,11 +213,12 @@ struct Issuer {
   // A row stride: the block width for a k-blocked A (known at compile time),
   // else the caller's
   __device__ __forceinline__ static int64_t a_rs(const GemmArgs& p) {
-    return AM == AM_ROW ? p.a_rs : (int64_t)(KB64 ? 2 * BKS : BKS);
+    return (AM == AM_ROW || AM == AM_GATHER_ROW) ? p.a_rs : (int64_t)(KB64 ? 2 * BKS : BKS);
   }
   // the A row that GEMM row r reads
   __device__ __forceinline__ static int64_t a_row(const GemmArgs& p, int r) {
-    if constexpr (AM == AM_GATHER || AM == AM_GATHER64) return (int64_t)(p.gather[r] / p.gather_div);
+    if constexpr (AM == AM_GATHER || AM == AM_GATHER64 || AM == AM_GATHER_ROW)
+      return (int64_t)(p.gather[r] / p.gather_div);
     return (int64_t)r;
   }
 

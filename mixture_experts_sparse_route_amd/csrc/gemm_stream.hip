@@ -162,7 +162,7 @@ hipError_t launch_stream(const StreamArgs& a, int64_t n_groups, int u_max, hipSt
 hipError_t stream_gate_up(const AOperand& A, const int32_t* offsets, int64_t n_groups, const void* W1, const void* W3,
                           void* h, int64_t h_blk, int64_t F, int64_t d, hipStream_t s) {
   if (A.blk_rows && A.kbw != 32) return hipErrorInvalidValue;
-  if (A.gather && (!A.blk_rows || A.gather_div < 1)) return hipErrorInvalidValue;
+  if (A.gather && A.gather_div < 1) return hipErrorInvalidValue;
   StreamArgs a{};
   a.A = (const uint16_t*)A.ptr;
   a.a_rs = A.blk_rows ? 32 : d;

@@ -119,6 +119,13 @@ struct RouteScatter {
   // a scatter that runs on the final offsets (kFirstCome, kAffinity,
   // kReroute2) may also write the GEMM tile tables
   TileJob tiles;
+  // kFirstCome with a single chunk (decode-sized batches): the scatter first
+  // does the capacity scan itself from the chunk's histogram one_count [E],
+  // writing one_counts (= counts) and one_offsets (= offsets), and the scan
+  // launch is skipped.  one_count == nullptr: not done here.
+  const int32_t* one_count;
+  int32_t* one_counts;
+  int32_t* one_offsets;
 };
 hipError_t launch_route_scatter(const RouteScatter& r, int64_t T, int64_t K, int64_t E, int64_t cap, hipStream_t s);
 hipError_t launch_route_affinity(const uint64_t* seg, const int32_t* counts, const int32_t* dem_off,
@@ -205,8 +212,8 @@ struct CombineFuse {
 
 // The A operand of GEMM1: row-major [rows, Kdim] (blk_rows = 0) or k-blocked
 // [Kdim/kbw][blk_rows][kbw] with kbw = 32 or 64 (the kbw columns of all rows
-// are one contiguous run).  gather non-null (k-blocked only): GEMM row r
-// reads A row gather[r] / gather_div -- the routed rows read the k-blocked x
+// are one contiguous run).  gather non-null: GEMM row r reads A row
+// gather[r] / gather_div -- the routed rows read x (k-blocked or row-major)
 // through the routing's row_src (gather_div = K), so no per-row copy of x is
 // made.
 struct AOperand {

@@ -286,6 +286,41 @@ __device__ void scatter_tiles(const int32_t* __restrict__ offsets, int G, const 
   }
 }
 
+// The capacity scan of one chunk (route_scan_kernel with a single chunk and
+// no statistics) by one 256-thread workgroup: thread t owns experts 4t ..
+// 4t+3; counts[e] = the demand, offsets = exclusive scan of min(demand, cap),
+// offsets[E] = R.
+__device__ void one_chunk_scan(const int32_t* __restrict__ hist, int32_t* counts, int32_t* offsets, int E, int cap) {
+  __shared__ int wtot[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int kept[4], tot = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = 4 * tid + u;
+    const int c = e < E ? hist[e] : 0;
+    if (e < E) counts[e] = c;
+    kept[u] = min(c, cap);
+    tot += kept[u];
+  }
+  int v = tot;  // inclusive scan: within the wave, then over the waves
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) wtot[wave] = v;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) v += wtot[w];
+  int run = v - tot;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = 4 * tid + u;
+    if (e < E) offsets[e] = run;
+    run += kept[u];
+  }
+  if (tid == 255) offsets[E] = v;  // threads past E add nothing: the last inclusive value is R
+}
+
 template <int MODE>
 __global__ __launch_bounds__(256) void route_scatter_kernel(const RouteScatter a, const int T, const int K,
                                                             const int E, const int nbits, const int cap, const int ct) {
@@ -298,9 +333,16 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(const RouteScatter a
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t f_begin = (int64_t)blockIdx.x * ct * K;
   const int64_t f_end = min((int64_t)T * K, f_begin + (int64_t)ct * K);
-  for (int e = threadIdx.x; e < E; e += 256) {
-    running[e] = a.blk_base[(int64_t)blockIdx.x * E + e];
-    if constexpr (MODE == kReroute1) hist2[e] = 0;
+  if (MODE == kFirstCome && a.one_count) {
+    // a single chunk: the capacity scan here (every chunk base is 0); the
+    // offsets it writes are read back below after a barrier
+    one_chunk_scan(a.one_count, a.one_counts, a.one_offsets, E, cap);
+    for (int e = threadIdx.x; e < E; e += 256) running[e] = 0;
+  } else {
+    for (int e = threadIdx.x; e < E; e += 256) {
+      running[e] = a.blk_base[(int64_t)blockIdx.x * E + e];
+      if constexpr (MODE == kReroute1) hist2[e] = 0;
+    }
   }
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int64_t pass = f_begin; pass < f_end; pass += 256) {
@@ -663,6 +705,7 @@ hipError_t launch_route_scatter(const RouteScatter& r, int64_t T, int64_t K, int
   const int ct = chunk_tokens(E, K);
   const unsigned nb = (unsigned)((T + ct - 1) / ct);
   const int Ti = (int)T, Ki = (int)K, Ei = (int)E;
+  if (r.one_count && (r.mode != kFirstCome || nb != 1 || E > 1024)) return hipErrorInvalidValue;
   prof_begin(K_ROUTE_SCATTER, s);
   switch (r.mode) {
     case kFirstCome: route_scatter_kernel<kFirstCome><<<nb, 256, 0, s>>>(r, Ti, Ki, Ei, nbits, capi, ct); break;
