@@ -54,6 +54,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--tokens", type=int, default=0, help="override the workload's token count (a size sweep)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel in an untimed extra pass")
@@ -166,7 +167,7 @@ def main():
     import mixture_experts_sparse_route_amd as moe
     from moe_synth import workload
 
-    wl = workload(args.workload, **({"wdtype": "fp8"} if args.fp8 else {}))
+    wl = workload(args.workload, **({"wdtype": "fp8"} if args.fp8 else {}), **({"T": args.tokens} if args.tokens else {}))
     lib = moe.load_library()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
