@@ -64,6 +64,25 @@ def near_tie_experts(o_idx, aff32, cap, E):
     return amb
 
 
+def assert_near_ties_valid(g, orc, amb, aff32, cap, E):
+    """At a near-tie cut several kept sets are correct: bound how many experts
+    have one, and check that the GPU's is valid there: `cap` kept, none
+    below a dropped one by more than the tie width, and the kept rows in flat
+    order at the expert's rows (the stable permutation)."""
+    assert len(amb) <= max(1, E // 16), f"{len(amb)} near-tie experts"
+    fi, a = orc["idx"].reshape(-1), aff32.reshape(-1).astype(np.float64)
+    gd, off, rs = g["dest"].reshape(-1), g["offsets"], g["row_src"]
+    for e in amb:
+        sel = np.nonzero(fi == e)[0]
+        kept, drop = sel[gd[sel] >= 0], sel[gd[sel] < 0]
+        assert len(kept) == cap, (e, len(kept), cap)
+        if len(drop):
+            lo = a[kept].min()
+            assert lo >= a[drop].max() - 1e-5 * abs(lo), f"expert {e}: a kept affinity below a dropped one"
+        assert np.array_equal(gd[kept], np.arange(off[e], off[e] + cap)), f"expert {e}: kept rows out of order"
+        assert np.array_equal(rs[gd[kept]], kept), f"expert {e}: row_src disagrees with dest"
+
+
 def check_policy(case: Case, policy: str):
     wl = case.wl
     T, K, E = wl.T, wl.K, wl.E
@@ -86,6 +105,7 @@ def check_policy(case: Case, policy: str):
         ok = ~np.isin(orc["idx"].reshape(-1), amb)
         assert np.array_equal(g["counts"], orc["counts"]) and np.array_equal(g["offsets"], orc["offsets"])
         assert np.array_equal(g["dest"][ok], orc["dest"][ok]), "affinity drop differs"
+        assert_near_ties_valid(g, orc, amb, orc["w"].astype(np.float32), cap, E)
         if amb:
             rows = ~np.isin(np.arange(T), np.nonzero(~ok)[0] // K)   # compare tokens away from the near-ties
     live = kept_tokens(orc["dest"], K, wl.n_shared)
@@ -197,6 +217,7 @@ def test_policy_full_size_switch(policy):
         amb = near_tie_experts(orc["idx"], orc["w"].astype(np.float32), cap, wl.E)
         ok = ~np.isin(orc["idx"].reshape(-1), amb)
         assert np.array_equal(g["dest"][ok], orc["dest"][ok])
+        assert_near_ties_valid(g, orc, amb, orc["w"].astype(np.float32), cap, wl.E)
         print("near-tie experts", len(amb))
     # outputs on tokens covering every (expert, m-tile) of both GEMMs, held
     # to the layer tolerance (the stated bound against the definition where
