@@ -78,6 +78,10 @@ struct GemmArgs {
   const int32_t* gather;
   int gather_div;
   CombineFuse fuse;        // down: y written through it when fuse.y is set
+  // > 0: tiles go to the XCDs in chunks of xcd_chunk consecutive tiles,
+  // round-robin (one tile per workgroup), instead of one contiguous range
+  // per XCD
+  int xcd_chunk;
 };
 
 // A operand modes: row-major; k-blocked in blocks of 32 k ([Kdim/32][rows][32])
@@ -493,12 +497,23 @@ __global__ __launch_bounds__(256, NS* stage_bytes<WK>(BM, BNB) <= LDS_BYTES / 2 
   const int per_xcd = (total + kXcds - 1) / kXcds;
   const int g8 = gridDim.x / kXcds;
   const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
-  const int begin = xcd * per_xcd, end = min(total, begin + per_xcd);
-  if (begin + j >= end) return;
   Seq q;
-  q.lbase = begin + j;
-  q.lstride = g8;
-  q.n_tiles = (end - begin - j + g8 - 1) / g8;
+  if (p.xcd_chunk > 0) {
+    // chunk k of XCD x is the table's chunk 8 k + x (the launcher sizes the
+    // grid to a multiple of 8 chunks covering every tile)
+    const int C = p.xcd_chunk;
+    const int t = ((j / C) * kXcds + xcd) * C + j % C;
+    if (t >= total) return;
+    q.lbase = t;
+    q.lstride = 1;
+    q.n_tiles = 1;
+  } else {
+    const int begin = xcd * per_xcd, end = min(total, begin + per_xcd);
+    if (begin + j >= end) return;
+    q.lbase = begin + j;
+    q.lstride = g8;
+    q.n_tiles = (end - begin - j + g8 - 1) / g8;
+  }
   q.nk = p.Kdim / k_per_stage<WK>();
   q.total_steps = q.n_tiles * q.nk;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -560,7 +575,11 @@ MOE_GEMM16K64_CONFIGS(MOE_FITS_TABLES)
 
 // Workgroups to launch: one per tile (upper bound `grid`), or with
 // pl.wg_per_cu > 0 a persistent grid of wg_per_cu workgroups per CU.
-static inline int64_t launch_grid(const FfnPlan& pl, int64_t grid) {
+static inline int64_t launch_grid(const FfnPlan& pl, int64_t grid, int xcd_chunk) {
+  if (xcd_chunk > 0 && pl.wg_per_cu <= 0) {
+    const int64_t c8 = (int64_t)kXcds * xcd_chunk;
+    return (grid + c8 - 1) / c8 * c8;
+  }
   if (pl.wg_per_cu <= 0) return grid;
   const int64_t pg = (int64_t)device_cus() * pl.wg_per_cu / kXcds * kXcds;
   return pg < grid ? pg : grid;

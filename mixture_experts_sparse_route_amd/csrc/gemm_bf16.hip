@@ -27,7 +27,8 @@ hipError_t gemm_bf16_down(const FfnPlan& pl, const void* h, int64_t h_blk, const
   set_layout(a, h_blk, 0);
   if (fuse) a.fuse = *fuse;
   if (F / (pl.k64_down ? 2 * BKS : BKS) < pl.ns_down - 1) return hipErrorInvalidValue;
-  const unsigned g = (unsigned)launch_grid(pl, grid);
+  a.xcd_chunk = pl.wg_per_cu > 0 ? 0 : pl.xcd_chunk_down;
+  const unsigned g = (unsigned)launch_grid(pl, grid, a.xcd_chunk);
 #define MOE_LAUNCH(B, W, N)                                     \
   if (pl.bm_down == B && pl.bnb_down == W && pl.ns_down == N) { \
     gemm_bf16_kernel<B, W, N, false, WKV, AM_KB><<<g, 256, 0, s>>>(a); \

@@ -14,7 +14,8 @@ hipError_t gemm_bf16_gate_up(const FfnPlan& pl, const AOperand& A, const int4* t
   a.gather = A.gather;
   a.gather_div = A.gather_div;
   if (d / (pl.k64_up ? 2 * BKS : BKS) < pl.ns_up - 1) return hipErrorInvalidValue;
-  const unsigned g = (unsigned)launch_grid(pl, grid);
+  a.xcd_chunk = pl.wg_per_cu > 0 ? 0 : pl.xcd_chunk_up;
+  const unsigned g = (unsigned)launch_grid(pl, grid, a.xcd_chunk);
 // A row-major (x itself, or a caller's xp), k-blocked (the layer's own
 // dispatch output, or x k-blocked), or x (k-blocked or row-major) with the
 // rows gathered through the routing: separate instantiations, so the row

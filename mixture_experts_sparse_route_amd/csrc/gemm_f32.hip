@@ -212,6 +212,18 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_
   // 6.1-6.4 TB/s there; the streaming GEMM1 measured 351-370 against
   // 307-317 us on the same box)
   if (!w8 && n_groups > 0 && group_max <= 32) p.stream_down = true;
+  // bf16 tile plans other than the decode-sized one deal their tiles to the
+  // XCDs in chunks of 16 consecutive tiles, round-robin, instead of one
+  // contiguous range per XCD, so every XCD works through every expert's
+  // tiles (m-tiles of one weight tile stay together).  Same box, same
+  // process: Switch 0.420-0.440 -> 0.403-0.410 ms, prefill 2.82-2.97 ->
+  // 2.78-2.80 ms; GEMM2 with 256-row weight tiles (the DeepSeek-style
+  // layer's) was slower (1.91 -> 1.96-1.98 ms) and keeps the ranges, and
+  // decode's GEMM1 was slower (292-297 -> 322-329 us).
+  if (!w8 && !small) {
+    p.xcd_chunk_up = 16;
+    p.xcd_chunk_down = p.bnb_down == 128 ? 16 : 0;
+  }
   // overrides for tuning, honoured with MOE_TUNING=1 only: MOE_GEMM_K64
   // (both GEMMs in stages of 64 k, 0 or 1), MOE_GEMM_K64_DOWN, MOE_GEMM_BM, MOE_GEMM_BM_DOWN,
   // MOE_GEMM_{BNB,NS}_{UP,DOWN}, MOE_GEMM_WGS, MOE_GEMM_EVEN_UP; a set that names no compiled
@@ -233,6 +245,10 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_
   p.stream_up = env_int("MOE_GEMM_STREAM_UP", p.stream_up ? 1 : 0) != 0 && !w8;
   p.stream_down = env_int("MOE_GEMM_STREAM_DOWN", p.stream_down ? 1 : 0) != 0 && !w8;
   p.stream_u = env_int("MOE_GEMM_STREAM_U", p.stream_u);
+  const int xc_env = env_int("MOE_GEMM_XCD_CHUNK", -1);  // both GEMMs
+  if (xc_env >= 0) p.xcd_chunk_up = p.xcd_chunk_down = xc_env;
+  p.xcd_chunk_up = env_int("MOE_GEMM_XCD_CHUNK_UP", p.xcd_chunk_up);
+  p.xcd_chunk_down = env_int("MOE_GEMM_XCD_CHUNK_DOWN", p.xcd_chunk_down);
   if (!gemm_bf16_has_config(w8, p.k64_up, p.bm, p.bnb_up, p.ns_up) ||
       !gemm_bf16_has_config(w8, p.k64_down, p.bm_down, p.bnb_down, p.ns_down) ||
       d / (p.k64_up ? 64 : 32) < p.ns_up - 1 || F / (p.k64_down ? 64 : 32) < p.ns_down - 1)

@@ -168,6 +168,10 @@ struct FfnPlan {
   bool stream_up = false;
   bool stream_down = false;
   int stream_u = 8;  // GEMM2's 32-k steps per load batch (8 or 4)
+  // tile kernels: > 0 deals tiles to the XCDs in chunks of this many
+  // consecutive tiles, round-robin (one tile per workgroup)
+  int xcd_chunk_up = 0;
+  int xcd_chunk_down = 0;
 };
 // Compute units of the current device (queried once).
 int device_cus();

@@ -224,6 +224,9 @@ PLAN_OVERRIDES = {
     "even_m_tiles": {"MOE_GEMM_EVEN_UP": "1"},
     "k32_128x256": {"MOE_GEMM_K64": "0", "MOE_GEMM_BM": "128", "MOE_GEMM_BNB_UP": "256", "MOE_GEMM_NS_UP": "3"},
     "persistent": {"MOE_GEMM_WGS": "1"},
+    "xcd_ranges": {"MOE_GEMM_XCD_CHUNK": "0"},
+    "xcd_chunks_of_1": {"MOE_GEMM_XCD_CHUNK": "1"},
+    "xcd_chunks_of_3": {"MOE_GEMM_XCD_CHUNK_UP": "3", "MOE_GEMM_XCD_CHUNK_DOWN": "5"},
 }
 
 
