@@ -38,10 +38,13 @@
  *     MOE_TUNING=1 is set in the environment, environment variables read at
  *     each call override them (MOE_GEMM_K64, MOE_GEMM_K64_DOWN, MOE_GEMM_BM,
  *     MOE_GEMM_BM_DOWN, MOE_GEMM_BNB_UP, MOE_GEMM_NS_UP, MOE_GEMM_BNB_DOWN,
- *     MOE_GEMM_NS_DOWN, MOE_GEMM_WGS, MOE_GEMM_EVEN_UP; MOE_ROUTER_WGS, read
- *     once); a set that names no compiled configuration is ignored.  Results
- *     do not depend on the plan: every output element sums its 32-wide MFMA
- *     k-steps in k order whatever the tile shape.
+ *     MOE_GEMM_NS_DOWN, MOE_GEMM_WGS, MOE_GEMM_EVEN_UP, MOE_GEMM_STREAM,
+ *     MOE_GEMM_STREAM_UP, MOE_GEMM_STREAM_DOWN, MOE_GEMM_STREAM_U,
+ *     MOE_GEMM_XCD_CHUNK, MOE_GEMM_XCD_CHUNK_UP, MOE_GEMM_XCD_CHUNK_DOWN,
+ *     MOE_GATHER; MOE_ROUTER_WGS, read once); a set that names no compiled
+ *     configuration is ignored.  Results do not depend on the plan: every
+ *     output element sums its 32-wide MFMA k-steps in k order whatever the
+ *     tile shape, tile order or kernel.
  */
 #ifndef MOE_H
 #define MOE_H

@@ -226,7 +226,8 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_
   }
   // overrides for tuning, honoured with MOE_TUNING=1 only: MOE_GEMM_K64
   // (both GEMMs in stages of 64 k, 0 or 1), MOE_GEMM_K64_DOWN, MOE_GEMM_BM, MOE_GEMM_BM_DOWN,
-  // MOE_GEMM_{BNB,NS}_{UP,DOWN}, MOE_GEMM_WGS, MOE_GEMM_EVEN_UP; a set that names no compiled
+  // MOE_GEMM_{BNB,NS}_{UP,DOWN}, MOE_GEMM_WGS, MOE_GEMM_EVEN_UP, MOE_GEMM_STREAM{,_UP,_DOWN},
+  // MOE_GEMM_STREAM_U, MOE_GEMM_XCD_CHUNK{,_UP,_DOWN}; a set that names no compiled
   // configuration leaves the plan as it was
   const FfnPlan def = p;
   const int k64_env = env_int("MOE_GEMM_K64", -1);
