@@ -46,6 +46,12 @@ FP32_PEAK_TFLOPS = 157.3     # MI355X fp32
 RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 DEFAULT_WORKLOAD = "deepseek_v3_fine"
 EVENT_EVERY = 4               # the dominant kernel is event-timed in the last step of every 4
+# Which GEMMs' weights a bf16 workload's weights are packed for (moe_pack_weights), by default: the
+# layout its GEMMs stream fastest (same box, alternating runs, against row-major weights):
+# DeepSeek-style GEMM1 3.62 -> 3.46 ms, GEMM2 unchanged; prefill GEMM1 1.80 -> 1.76 ms, GEMM2 908 -> 889 us;
+# Switch GEMM2 132 -> 118 us, GEMM1 235 -> 242 us; decode GEMM2 178 -> 169 us, GEMM1 294 -> 313 us.
+DEFAULT_PACKING = {"deepseek_v3_fine": "up", "mixtral_prefill": "both", "switch_top1_capacity": "down",
+                   "mixtral_decode": "down"}
 
 
 def parse():
@@ -63,6 +69,9 @@ def parse():
                     help="which assignments an expert over capacity drops")
     ap.add_argument("--expert-choice", action="store_true", help="expert-choice routing instead of token choice")
     ap.add_argument("--fp8", action="store_true", help="FP8 E4M3 expert weights with per-row scales")
+    ap.add_argument("--packed", default="auto", choices=["auto", "none", "up", "down", "both"],
+                    help="which GEMMs' expert weights moe_pack_weights packs once before timing (bf16 layers); "
+                         "auto: the layout measured fastest for the workload")
     return ap.parse_args()
 
 
@@ -168,6 +177,9 @@ def main():
     from moe_synth import workload
 
     wl = workload(args.workload, **({"wdtype": "fp8"} if args.fp8 else {}), **({"T": args.tokens} if args.tokens else {}))
+    packing = args.packed
+    if packing == "auto":
+        packing = DEFAULT_PACKING.get(wl.name, "none") if wl.dtype == "bf16" and wl.wdtype != "fp8" else "none"
     lib = moe.load_library()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
@@ -188,7 +200,19 @@ def main():
                          capacity_factor=wl.capacity_factor, n_shared=wl.n_shared,
                          d_ff_shared=wl.Fs, dtype=wl.dtype, stats=args.stats, drop_policy=args.drop_policy,
                          expert_choice=args.expert_choice, renorm=wl.renorm and not args.expert_choice,
-                         wdtype=wl.wdtype)
+                         wdtype=wl.wdtype, packed=packing)
+    # the weight layout is chosen once, when the weights are loaded: outside the timed region
+    pack_names = {"none": (), "up": ("W1", "W3", "Ws1", "Ws3"), "down": ("W2", "Ws2")}
+    pack_names["both"] = pack_names["up"] + pack_names["down"]
+    torch.cuda.synchronize()
+    t_pack = time.perf_counter()
+    for k in pack_names[packing]:
+        if d.get(k) is not None:
+            packed = torch.empty_like(d[k])
+            moe.moe_pack_weights(d[k], packed)
+            d[k] = packed
+    torch.cuda.synchronize()
+    t_pack = time.perf_counter() - t_pack
     scales = None
     if args.fp8:
         scales = dict(w1=d["S1"], w3=d["S3"], w2=d["S2"], ws1=d["Ss1"], ws3=d["Ss3"], ws2=d["Ss2"])
@@ -295,6 +319,7 @@ def main():
                    "top_k": wl.K, "gate": "sigmoid" if wl.gate else "softmax", "renorm": wl.renorm,
                    "capacity_factor": wl.capacity_factor, "n_shared": wl.n_shared, "d_ff_shared": wl.Fs,
                    "expert_weights": "fp8_e4m3" if args.fp8 else wl.dtype,
+                   "packed_weights": packing, "weight_pack_ms": round(t_pack * 1e3, 2),
                    "router_stats": args.stats, "drop_policy": args.drop_policy,
                    "routing": "expert_choice" if args.expert_choice else "token_choice",
                    "parallelism": "single GPU"},

@@ -139,7 +139,16 @@ enum {
    * ascending t) or -1; counts[e] = cap, offsets[e] = e * cap; every other
    * entry point then takes K = E.  Softmax gate only; not with
    * MOE_F_TOPK_IN, MOE_F_STATS or MOE_F_RENORM. */
-  MOE_F_EXPERT_CHOICE = 32u
+  MOE_F_EXPERT_CHOICE = 32u,
+  /* Expert weights in the packed layout that moe_pack_weights writes
+   * instead of the nn.Linear row-major one, per GEMM: W1 and W3 (and the
+   * shared expert's Ws1, Ws3) with MOE_F_PACKED_UP, W2 (and Ws2) with
+   * MOE_F_PACKED_DOWN.  The same values, so every result is bit for bit that
+   * of the row-major weights; which layout streams faster depends on the
+   * GEMM's tile plan, so a caller chooses per matrix once, when it loads
+   * the weights.  bf16 weights only (MOE_ERR_UNSUPPORTED otherwise). */
+  MOE_F_PACKED_UP = 64u,
+  MOE_F_PACKED_DOWN = 128u
 };
 
 /* Router statistics, written to routing->stats (E + MOE_N_STATS doubles)
@@ -261,6 +270,24 @@ moe_status moe_dispatch(const moe_config* cfg, const void* x, const moe_routing*
 moe_status moe_expert_ffn(const moe_config* cfg, const void* xp, const int32_t* offsets, int64_t n_groups,
                           int64_t max_rows, const void* W1, const void* W3, const void* W2, const moe_scales* scales,
                           float* yp, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Weight packing, done once when a layer's weights are loaded (not part of
+ * the forward).  The expert GEMMs [LN §2.2; TD §7.4] reduce every weight row
+ * along its length (d for W1 / W3, F for W2) in steps of 64 elements, and a
+ * workgroup reads one step of 64-row blocks of rows at a time; in the
+ * row-major layout those are 128-byte pieces of rows 2 d or 2 F bytes apart.
+ * The packed layout cuts each group's rows into panels of 64 rows and stores
+ * a panel's 64-element steps one after the other, each as one 8 KB run:
+ *   src: device [groups, N, K] bf16 row-major (nn.Linear out x in)
+ *   dst: device [groups, N/64, K/64, 64, 64] bf16: element (g, n, k) of src
+ *        at dst[(((g * (N/64) + n/64) * (K/64) + k/64) * 64 + n % 64) * 64 + k % 64]
+ * W1 / W3 are packed with (N, K) = (F, d) and W2 with (d, F) (the shared
+ * expert's likewise with Fs); the result is then passed with
+ * MOE_F_PACKED_UP / MOE_F_PACKED_DOWN.  groups >= 1; N and K positive multiples of 64 (as
+ * every bf16 layer's d, F and Fs are); src and dst 16-byte aligned and not
+ * overlapping, owned by the caller.  Enqueued on `stream`;
+ * MOE_ERR_INVALID_ARG on a bad size or pointer, before any launch. */
+moe_status moe_pack_weights(const void* src, void* dst, int64_t groups, int64_t N, int64_t K, moe_stream_t stream);
 
 /* a9: weighted combine [TD §3.1 step 4; BD §4 step 5]:
  *   y[t] = sum_{k ascending, dest[t*K+k] >= 0} topk_w[t][k] * yp[dest[t*K+k]]

@@ -24,6 +24,9 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_GATE_SOFTMAX, MOE_GATE_SIGMOID = 0, 1
 MOE_F_RENORM, MOE_F_RESIDUAL, MOE_F_LOGITS_IN, MOE_F_TOPK_IN, MOE_F_STATS = 1, 2, 4, 8, 16
 MOE_F_EXPERT_CHOICE = 32
+MOE_F_PACKED_UP, MOE_F_PACKED_DOWN = 64, 128
+# expert-weight layouts: which GEMMs' weights are packed by moe_pack_weights
+PACKINGS = {"none": 0, "up": MOE_F_PACKED_UP, "down": MOE_F_PACKED_DOWN, "both": MOE_F_PACKED_UP | MOE_F_PACKED_DOWN}
 # moe_drop_policy: which assignments an expert over capacity drops
 DROP_POLICIES = {"first_come": 0, "affinity": 1, "reroute": 2}
 # router statistics after the E per-expert mean probabilities (moe.h, MOE_STAT_*)
@@ -81,6 +84,7 @@ def load_library(path: str = LIB_PATH):
         "moe_combine": [C, vp, R, vp, vp, vp, vp],
         "moe_forward": [C, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(MoeScales), vp, R, vp, sz, vp],
         "moe_forward_noalloc": [C, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(MoeScales), vp, R, vp],
+        "moe_pack_weights": [vp, vp, i64, i64, i64, vp],
         "moe_profile_enable": [ctypes.c_uint32],
         "moe_profile_reset": [],
         "moe_profile_read": [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)],
@@ -135,11 +139,13 @@ class LayerSpec:
     stats: bool = False
     drop_policy: str = "first_come"   # a key of DROP_POLICIES
     expert_choice: bool = False       # expert-choice routing (routing arrays in the K = E form)
+    packed: str = "none"              # a key of PACKINGS: weights in moe_pack_weights' layout (bf16)
 
     def config(self) -> MoeConfig:
         flags = ((MOE_F_RENORM if self.renorm else 0) | (MOE_F_RESIDUAL if self.residual else 0)
                  | (MOE_F_LOGITS_IN if self.logits_in else 0) | (MOE_F_TOPK_IN if self.topk_in else 0)
-                 | (MOE_F_STATS if self.stats else 0) | (MOE_F_EXPERT_CHOICE if self.expert_choice else 0))
+                 | (MOE_F_STATS if self.stats else 0) | (MOE_F_EXPERT_CHOICE if self.expert_choice else 0)
+                 | PACKINGS[self.packed])
         dt = MOE_BF16 if self.dtype == "bf16" else MOE_F32
         ot = dt if self.out_dtype is None else (MOE_BF16 if self.out_dtype == "bf16" else MOE_F32)
         return MoeConfig(self.tokens, self.d_model, self.d_ff, self.n_experts, self.top_k, self.gate, flags,
@@ -263,6 +269,14 @@ def moe_expert_ffn(spec, xp, offsets, n_groups, max_rows_, W1, W3, W2, yp, ws, s
     _check(load_library().moe_expert_ffn(ctypes.byref(_cfg(spec)), _ptr(xp), _ptr(offsets), n_groups, max_rows_,
                                          _ptr(W1), _ptr(W3), _ptr(W2), _scales(scales), _ptr(yp), _ws_ptr(ws),
                                          _ws_bytes(ws), _stream(stream)), "moe_expert_ffn")
+
+
+def moe_pack_weights(src, dst, stream=None):
+    """dst <- src [groups, N, K] bf16 in the packed layout
+    [groups, N/64, K/64, 64, 64] (moe.h); src is 3-D, dst any device tensor
+    of the same size."""
+    G, N, K = src.shape
+    _check(load_library().moe_pack_weights(_ptr(src), _ptr(dst), G, N, K, _stream(stream)), "moe_pack_weights")
 
 
 def moe_combine(spec, yp, routing: Routing, shared_out, x_residual, y, stream=None):

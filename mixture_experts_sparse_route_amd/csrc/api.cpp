@@ -42,7 +42,8 @@ moe_status hip_fail(hipError_t e, const char* where) {
   } while (0)
 
 constexpr uint32_t kKnownFlags =
-    MOE_F_RENORM | MOE_F_RESIDUAL | MOE_F_LOGITS_IN | MOE_F_TOPK_IN | MOE_F_STATS | MOE_F_EXPERT_CHOICE;
+    MOE_F_RENORM | MOE_F_RESIDUAL | MOE_F_LOGITS_IN | MOE_F_TOPK_IN | MOE_F_STATS | MOE_F_EXPERT_CHOICE |
+    MOE_F_PACKED_UP | MOE_F_PACKED_DOWN;
 
 // Everything the launches need, derived from a validated config.
 struct Shape {
@@ -50,6 +51,7 @@ struct Shape {
   bool out_bf16;
   bool stats;  // router statistics requested
   bool w8;     // expert weights are E4M3 bytes with per-row scales
+  bool packed_up, packed_down;  // W1 / W3 and W2 in the packed layout (moe_pack_weights)
   int policy;  // moe_drop_policy in effect (first-come when there is no capacity)
   int64_t K2;  // re-routing alternates per token
   bool ec;     // expert-choice routing: K is E (the K = E form), cap the tokens per expert
@@ -100,6 +102,8 @@ moe_status validate(const moe_config* c, Shape* sh) {
     return fail(MOE_ERR_INVALID_ARG, "unknown out_dtype %d", (int)c->out_dtype);
   if (c->act_dtype == MOE_F32 && c->out_dtype != MOE_F32)
     return fail(MOE_ERR_UNSUPPORTED, "an fp32 layer has an fp32 output");
+  if ((c->flags & (MOE_F_PACKED_UP | MOE_F_PACKED_DOWN)) && c->w_dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "packed weights (MOE_F_PACKED_UP / _DOWN) are implemented for bf16 weights");
   const bool bf16 = c->act_dtype == MOE_BF16;
   if (bf16) {
     if (c->d_model % 64 || c->d_ff % 64 || (c->n_shared && c->d_ff_shared % 64))
@@ -127,6 +131,8 @@ moe_status validate(const moe_config* c, Shape* sh) {
   sh->out_bf16 = c->out_dtype == MOE_BF16;
   sh->stats = c->flags & MOE_F_STATS;
   sh->w8 = c->w_dtype == MOE_FP8_E4M3;
+  sh->packed_up = c->flags & MOE_F_PACKED_UP;
+  sh->packed_down = c->flags & MOE_F_PACKED_DOWN;
   sh->policy = cap >= 0 ? c->drop_policy : MOE_DROP_FIRST_COME;
   sh->K2 = sh->policy == MOE_DROP_REROUTE ? std::min(K, E - K) : 0;
   sh->T = T;
@@ -362,6 +368,14 @@ moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const 
   return MOE_OK;
 }
 
+// The GEMM plan of an FFN of the layer, with its weights' layout.
+FfnPlan plan_of(const Shape& s, int64_t max_rows, int64_t group_max, int64_t n_groups, int64_t F) {
+  FfnPlan p = ffn_plan(s.bf16, s.w8, max_rows, group_max, n_groups, F, s.d);
+  p.packed_up = s.packed_up;
+  p.packed_down = s.packed_down;
+  return p;
+}
+
 // s1 / s3 / s2: row scales of E4M3 weights (s.w8), else unused.
 // group_max: bound of any group's rows; A: GEMM1's A operand (fp32 layers:
 // row-major A.ptr).  plan_in: the plan (else computed here); tiles_ready:
@@ -372,7 +386,7 @@ moe_status do_ffn(const Shape& s, const AOperand& A, const int32_t* offsets, int
                   void* h, float* yp, int4* tab_up, int4* tab_down, int32_t* counts, int64_t F, hipStream_t st,
                   const CombineFuse* fuse = nullptr, const FfnPlan* plan_in = nullptr, bool tiles_ready = false,
                   bool shared = false) {
-  const FfnPlan plan = plan_in ? *plan_in : ffn_plan(s.bf16, s.w8, max_rows, group_max, n_groups, F, s.d);
+  const FfnPlan plan = plan_in ? *plan_in : plan_of(s, max_rows, group_max, n_groups, F);
   if (!tiles_ready && !(s.bf16 && plan.stream_up && plan.stream_down))
     MOE_HIP(launch_ffn_tiles(plan, offsets, n_groups, max_rows, F, s.d, tab_up, tab_down, counts, st));
   MOE_HIP(launch_gemm_gate_up(s.bf16, plan, A, tab_up, counts, offsets, n_groups, max_rows, W1, W3, s1, s3, h, F, s.d,
@@ -511,7 +525,7 @@ moe_status forward_impl(const moe_config* cfg, const Shape& s, const void* x, co
   // blocks of 64 k when every GEMM1 reading it takes stages of 64 k (a
   // gathered row's piece of a stage is then one whole 128-byte line), else 32
   const int64_t group_max = s.cap >= 0 ? std::min(s.T, s.cap) : s.T;
-  FfnPlan plan = ffn_plan(s.bf16, s.w8, s.max_rows, group_max, s.E, s.F, s.d);
+  FfnPlan plan = plan_of(s, s.max_rows, group_max, s.E, s.F);
   if (s.fused) plan.stream_down = false;  // the fused GEMM2 epilogue is the tile kernel's
   // decode-sized batches (at most 64 tokens) read the rows from x itself,
   // row-major (x is then a few hundred KB and stays in L2; the copy would
@@ -524,7 +538,7 @@ moe_status forward_impl(const moe_config* cfg, const Shape& s, const void* x, co
   if (s.bf16 && !s.fused) {
     // the weight-streaming kernels read A in blocks of 32 k
     auto wants64 = [](const FfnPlan& q) { return q.k64_up && !q.stream_up; };
-    const bool sh64 = !s.S || wants64(ffn_plan(s.bf16, s.w8, s.T, s.T, 1, s.Fs, s.d));
+    const bool sh64 = !s.S || wants64(plan_of(s, s.T, s.T, 1, s.Fs));
     kbw = (wants64(plan) || !gather) && sh64 && s.d % 64 == 0 ? 64 : 32;
     if ((!gather || gather_row) && !s.S) kbw = 0;  // nothing reads x k-blocked
     if (gather_row) kbw = 0;
@@ -726,6 +740,22 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* xp, const int32_t* 
                 at<void>(ws, L.h), yp,
                 at<int4>(ws, L.tab_up), at<int4>(ws, L.tab_down), at<int32_t>(ws, L.counts), s.F,
                 (hipStream_t)stream);
+}
+
+moe_status moe_pack_weights(const void* src, void* dst, int64_t groups, int64_t N, int64_t K, moe_stream_t stream) {
+  if (!src || !dst) return fail(MOE_ERR_INVALID_ARG, "src and dst are required");
+  if (groups < 1 || N < 64 || N % 64 || K < 64 || K % 64)
+    return fail(MOE_ERR_INVALID_ARG, "groups = %lld must be >= 1, N = %lld and K = %lld positive multiples of 64",
+                (long long)groups, (long long)N, (long long)K);
+  if (N > (int64_t)INT32_MAX || groups > (int64_t)INT32_MAX / N || K > (int64_t)INT32_MAX / 8)
+    return fail(MOE_ERR_UNSUPPORTED, "groups * N or K exceeds the supported range");
+  moe_status st;
+  if ((st = check_aligned({src, dst})) != MOE_OK) return st;
+  const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst, n = (uintptr_t)(groups * N * K * 2);
+  if (a < b + n && b < a + n) return fail(MOE_ERR_INVALID_ARG, "src and dst overlap");
+  // N is a multiple of 64, so the panels of all groups' rows are the groups' panels
+  MOE_HIP(launch_pack_weights(src, dst, groups * N, K, (hipStream_t)stream));
+  return MOE_OK;
 }
 
 moe_status moe_combine(const moe_config* cfg, const float* yp, const moe_routing* r, const float* shared_out,

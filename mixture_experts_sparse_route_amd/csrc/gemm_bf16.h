@@ -82,6 +82,15 @@ struct GemmArgs {
   // round-robin (one tile per workgroup), instead of one contiguous range
   // per XCD
   int xcd_chunk;
+  // bf16 weights row-major [groups][N][Kdim], or packed (w_packed) in
+  // panels of 64 rows [groups][N/64][Kdim/64][64][64]: element (g, n, k) at
+  // byte g N Kdim 2 + (n / 64) Kdim 128 + (k / 64) 8192 + (n % 64) 128 +
+  // (k % 64) 2, so the 64-k steps of a panel follow each other in memory and
+  // a stage reads whole 8 KB runs.  w_bs = bytes between a row's
+  // consecutive 64-k steps (128 row-major, 8192 packed).  E4M3 weights are
+  // row-major.
+  int w_packed;
+  int64_t w_bs;
 };
 
 // A operand modes: row-major; k-blocked in blocks of 32 k ([Kdim/32][rows][32])
@@ -246,6 +255,8 @@ struct Issuer {
       col = cur.n0 + rt;
     }
     col = min(col, p.N - 1);
+    if ((WK == WK_BF16 || WK == WK_BF16_64) && p.w_packed)
+      return base + (int64_t)cur.g * p.N * p.Kdim * 2 + (int64_t)(col >> 6) * p.Kdim * 128 + (col & 63) * 128 + off;
     return base + (((int64_t)cur.g * p.N + col) * p.Kdim) * esz + off;
   }
 
@@ -297,7 +308,11 @@ struct Issuer {
     }
     char* const st = lds + (s % NS) * STAGE;
     const int64_t ao = (!K64 && KB64) ? (int64_t)(kt >> 1) * aks + (kt & 1) * 2 * BKS : (int64_t)kt * aks;
-    const int64_t wo = (int64_t)kt * WKS;
+    // weight offset of k-step kt: 64-k stage kt is block kt; a 32-k stage
+    // is the half (kt & 1) of block kt >> 1
+    const int64_t wo = WK == WK_BF16_64 ? (int64_t)kt * p.w_bs
+                       : WK == WK_BF16  ? (int64_t)(kt >> 1) * p.w_bs + (kt & 1) * RB
+                                        : (int64_t)kt * WKS;
 #pragma unroll
     for (int j = 0; j < NA; ++j)
       __builtin_amdgcn_global_load_lds(ab[j] + ao, (lds_ptr_t)(st + (wave + 4 * j) * (K64 ? 8 * 2 * RB : 16 * RB)), 16,
@@ -592,6 +607,13 @@ static inline void set_layout(GemmArgs& a, int64_t a_blk, int64_t c_blk, int kbw
   a.a_ks = a_blk ? kbw * a_blk : BKS;
   a.c_rs = c_blk ? 32 : a.N;
   a.c_bs = c_blk ? 32 * c_blk : 32;
+}
+
+// bf16 weights row-major [groups][N][Kdim] or packed in 64-row panels
+// [groups][N/64][Kdim/64][64][64]
+static inline void set_weight_layout(GemmArgs& a, bool packed) {
+  a.w_packed = packed ? 1 : 0;
+  a.w_bs = packed ? 64 * 2 * RB : 2 * RB;
 }
 
 // the configuration list of the weight kind (pl.w8, k64), each entry expanded by LAUNCH

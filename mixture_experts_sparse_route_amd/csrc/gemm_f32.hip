@@ -285,8 +285,9 @@ hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const AOperand& A, c
   if (grid == 0) return hipSuccess;
   prof_begin(prof_id, s);
   hipError_t err;
+  if (p.packed_up && !bf16) return hipErrorInvalidValue;  // packed weights are bf16
   if (bf16 && p.stream_up) {
-    err = stream_gate_up(A, offsets, n_groups, W1, W3, h, max_rows, F, d, s);
+    err = stream_gate_up(A, offsets, n_groups, W1, W3, h, max_rows, F, d, p.packed_up, s);
   } else if (bf16) {
     err = gemm_bf16_gate_up(p, A, tab, count, grid, W1, W3, s1, s3, h, max_rows, F, d, s);
   } else {
@@ -306,8 +307,9 @@ hipError_t launch_gemm_down(bool bf16, const FfnPlan& p, const void* h, const in
   if (grid == 0) return hipSuccess;
   prof_begin(prof_id, s);
   hipError_t err;
+  if (p.packed_down && !bf16) return hipErrorInvalidValue;
   if (bf16 && p.stream_down) {
-    err = stream_down(h, max_rows, offsets, n_groups, W2, yp, F, d, p.stream_u, s);
+    err = stream_down(h, max_rows, offsets, n_groups, W2, yp, F, d, p.stream_u, p.packed_down, s);
   } else if (bf16) {
     err = gemm_bf16_down(p, h, max_rows, tab, count, grid, W2, s2, yp, fuse, F, d, s);
   } else {

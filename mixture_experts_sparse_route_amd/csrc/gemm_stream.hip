@@ -35,6 +35,9 @@ struct StreamArgs {
                             // down: fp32 yp, the same addressing
   int64_t c_rs, c_bs;
   int N, K;
+  // weights packed in 64-row panels [groups][N/64][K/64][64][64] (the tile
+  // kernels' packed layout), else row-major
+  int w_packed;
 };
 
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
@@ -56,9 +59,15 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(const StreamArgs p) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lk = lane >> 4;
   const int n0 = (blockIdx.x * 4 + wave) * 16;
   if (n0 >= p.N) return;
-  const int64_t wrow = (int64_t)g * p.N + min(n0 + lr, p.N - 1);
-  const uint16_t* b0 = p.B0 + wrow * p.K + lk * 8;
-  const uint16_t* b1 = GATE_UP ? p.B1 + wrow * p.K + lk * 8 : nullptr;
+  // weight element (n, k) of group g: row-major at (g N + n) K + k; packed at
+  // g N K + (n / 64) 64 K + (k / 64) 4096 + (n % 64) 64 + k % 64, so 32-k
+  // step kt of a row is at (kt / 2) * w_bs + (kt % 2) * 32 from its start
+  const int n = min(n0 + lr, p.N - 1);
+  const int64_t wofs = p.w_packed ? (int64_t)g * p.N * p.K + (int64_t)(n >> 6) * 64 * p.K + (n & 63) * 64
+                                  : ((int64_t)g * p.N + n) * p.K;
+  const int64_t w_bs = p.w_packed ? 4096 : 64;
+  const uint16_t* b0 = p.B0 + wofs + lk * 8;
+  const uint16_t* b1 = GATE_UP ? p.B1 + wofs + lk * 8 : nullptr;
   // A rows past the group's end are loaded clamped to its last row (their
   // results are never stored)
   auto arow = [&](int r) -> int64_t {
@@ -87,8 +96,9 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(const StreamArgs p) {
     auto load = [&](Batch& bt, int kt) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        bt.w[0][u] = *(const bf16x8_t*)(b0 + (int64_t)(kt + u) * 32);
-        if constexpr (GATE_UP) bt.w[1][u] = *(const bf16x8_t*)(b1 + (int64_t)(kt + u) * 32);
+        const int64_t wk = (int64_t)((kt + u) >> 1) * w_bs + ((kt + u) & 1) * 32;
+        bt.w[0][u] = *(const bf16x8_t*)(b0 + wk);
+        if constexpr (GATE_UP) bt.w[1][u] = *(const bf16x8_t*)(b1 + wk);
         bt.a[0][u] = *(const bf16x8_t*)(a0 + (int64_t)(kt + u) * p.a_ks);
       }
       if (two) {
@@ -160,7 +170,7 @@ hipError_t launch_stream(const StreamArgs& a, int64_t n_groups, int u_max, hipSt
 }  // namespace
 
 hipError_t stream_gate_up(const AOperand& A, const int32_t* offsets, int64_t n_groups, const void* W1, const void* W3,
-                          void* h, int64_t h_blk, int64_t F, int64_t d, hipStream_t s) {
+                          void* h, int64_t h_blk, int64_t F, int64_t d, bool packed, hipStream_t s) {
   if (A.blk_rows && A.kbw != 32) return hipErrorInvalidValue;
   if (A.gather && A.gather_div < 1) return hipErrorInvalidValue;
   StreamArgs a{};
@@ -177,11 +187,12 @@ hipError_t stream_gate_up(const AOperand& A, const int32_t* offsets, int64_t n_g
   a.c_bs = 32 * h_blk;
   a.N = (int)F;
   a.K = (int)d;
+  a.w_packed = packed ? 1 : 0;
   return launch_stream<true>(a, n_groups, 4, s);
 }
 
 hipError_t stream_down(const void* h, int64_t h_blk, const int32_t* offsets, int64_t n_groups, const void* W2,
-                       float* yp, int64_t F, int64_t d, int u_max, hipStream_t s) {
+                       float* yp, int64_t F, int64_t d, int u_max, bool packed, hipStream_t s) {
   StreamArgs a{};
   a.A = (const uint16_t*)h;
   a.a_rs = 32;
@@ -196,6 +207,7 @@ hipError_t stream_down(const void* h, int64_t h_blk, const int32_t* offsets, int
   a.c_bs = 32;
   a.N = (int)d;
   a.K = (int)F;
+  a.w_packed = packed ? 1 : 0;
   return launch_stream<false>(a, n_groups, u_max, s);
 }
 

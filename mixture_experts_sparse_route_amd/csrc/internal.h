@@ -144,6 +144,9 @@ hipError_t launch_dispatch(const void* x, const int32_t* row_src, const int32_t*
 // x [T, d] bf16 -> k-blocked [d/kbw][T][kbw], kbw = 32 or 64 (row_bytes = 2 d,
 // a multiple of 2 kbw).
 hipError_t launch_kblock_copy(const void* x, void* xkb, int64_t T, int64_t row_bytes, int kbw, hipStream_t s);
+// moe_pack_weights: rows [rows, K] bf16 (rows a multiple of 64) into panels
+// [rows/64][K/64][64][64].
+hipError_t launch_pack_weights(const void* src, void* dst, int64_t rows, int64_t K, hipStream_t s);
 
 // ---- grouped expert FFN (a6-a7) ----
 struct FfnPlan {
@@ -172,6 +175,10 @@ struct FfnPlan {
   // consecutive tiles, round-robin (one tile per workgroup)
   int xcd_chunk_up = 0;
   int xcd_chunk_down = 0;
+  // bf16 weights of GEMM1 / GEMM2 packed in 64-row panels
+  // [groups][N/64][K/64][64][64] (moe_pack_weights), else row-major
+  bool packed_up = false;
+  bool packed_down = false;
 };
 // Compute units of the current device (queried once).
 int device_cus();
@@ -230,13 +237,14 @@ struct AOperand {
 
 // Weight-streaming GEMMs (gemm_stream.hip) for plans with p.stream_*: groups
 // from offsets directly; A k-blocked in blocks of 32 k or row-major; h
-// k-blocked with h_blk rows; yp row-major fp32.
+// k-blocked with h_blk rows; yp row-major fp32.  packed: the weights are in
+// the packed layout of moe_pack_weights, else row-major.
 hipError_t stream_gate_up(const AOperand& A, const int32_t* offsets, int64_t n_groups, const void* W1, const void* W3,
-                          void* h, int64_t h_blk, int64_t F, int64_t d, hipStream_t s);
+                          void* h, int64_t h_blk, int64_t F, int64_t d, bool packed, hipStream_t s);
 // u_max: 32-k steps per load batch of GEMM2 (8 or 4; fewer when K / 32 is
 // not a multiple).
 hipError_t stream_down(const void* h, int64_t h_blk, const int32_t* offsets, int64_t n_groups, const void* W2,
-                       float* yp, int64_t F, int64_t d, int u_max, hipStream_t s);
+                       float* yp, int64_t F, int64_t d, int u_max, bool packed, hipStream_t s);
 
 // bf16 MFMA path (gemm_bf16.hip); called through the launchers below.
 // s1 / s3 / s2: [groups, N] row scales of E4M3 weights (p.w8), else unused.

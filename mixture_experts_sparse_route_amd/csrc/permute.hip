@@ -609,6 +609,21 @@ __global__ __launch_bounds__(256) void kblock_copy_kernel(const uint4* __restric
   for (; kb < n_kb; kb += 4) dst[kb * kb_stride] = src[kb * CPB];
 }
 
+// Weight packing (moe_pack_weights): rows [rows, K] of bf16 into panels of
+// 64 rows, [rows/64][K/64][64][64].  A workgroup moves 8 rows (lane: row
+// lane / 8, 16-byte chunk lane % 8 of a 128-byte step); wave w copies the
+// 64-k steps w, w + 4, ...
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                           int64_t rows, int n_kb) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t r = (int64_t)blockIdx.x * 8 + (lane >> 3);
+  const int c = lane & 7;
+  if (r >= rows) return;
+  const uint4* s = src + r * n_kb * 8 + c;
+  uint4* d = dst + (r >> 6) * (int64_t)n_kb * 512 + (r & 63) * 8 + c;  // a panel step: 64 rows x 8 chunks
+  for (int kb = wave; kb < n_kb; kb += 4) d[(int64_t)kb * 512] = s[(int64_t)kb * 8];
+}
+
 // ------------------------------------------------------------ FFN tiles
 // Tile list of both expert GEMMs (each workgroup scans the m-tile counts and
 // writes its share of the entries): for group g with rows(g) rows,
@@ -784,6 +799,12 @@ hipError_t launch_kblock_copy(const void* x, void* xkb, int64_t T, int64_t row_b
   else
     kblock_copy_kernel<4><<<nb, 256, 0, s>>>((const uint4*)x, (uint4*)xkb, (int)T, n_kb);
   prof_end(K_DISPATCH, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_weights(const void* src, void* dst, int64_t rows, int64_t K, hipStream_t s) {
+  if (rows % 64 || K % 64 || rows < 64 || K < 64) return hipErrorInvalidValue;
+  pack_weights_kernel<<<(unsigned)(rows / 8), 256, 0, s>>>((const uint4*)src, (uint4*)dst, rows, (int)(K / 64));
   return hipGetLastError();
 }
 

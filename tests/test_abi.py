@@ -270,3 +270,27 @@ def test_noalloc_rejects_a_layer_larger_than_its_scratch(lib):
     assert moe.workspace_size(sp) > moe.NOALLOC_SCRATCH_BYTES
     st = lib.moe_forward_noalloc(ctypes.byref(moe._cfg(sp)), *([None] * 10), None, None, None, None)
     assert st == moe.MOE_ERR_WORKSPACE and b"built-in" in lib.moe_last_error()
+
+
+def test_packed_weight_validation(lib):
+    """MOE_F_PACKED_UP / _DOWN only with bf16 weights; moe_pack_weights checks
+    sizes, alignment and overlap on the host before any launch."""
+    n = ctypes.c_size_t()
+    assert (moe.MOE_F_PACKED_UP, moe.MOE_F_PACKED_DOWN) == (64, 128)
+    for packed, bits in (("up", 64), ("down", 128), ("both", 192)):
+        c = spec(packed=packed).config()
+        assert c.flags & 192 == bits
+        assert lib.moe_workspace_size(ctypes.byref(c), ctypes.byref(n)) == moe.MOE_OK
+        for bad in (spec(packed=packed, dtype="f32"), spec(packed=packed, wdtype="fp8")):
+            c = bad.config()
+            assert lib.moe_workspace_size(ctypes.byref(c), ctypes.byref(n)) == moe.MOE_ERR_UNSUPPORTED
+    pack = lib.moe_pack_weights
+    big = 1 << 40
+    assert pack(None, big, 2, 64, 64, None) == moe.MOE_ERR_INVALID_ARG
+    assert pack(256, big, 2, 64, 96, None) == moe.MOE_ERR_INVALID_ARG       # K not a multiple of 64
+    assert pack(256, big, 2, 72, 64, None) == moe.MOE_ERR_INVALID_ARG       # N not a multiple of 64
+    assert pack(256, big, 0, 64, 64, None) == moe.MOE_ERR_INVALID_ARG       # no groups
+    assert pack(256, big, 2, 0, 64, None) == moe.MOE_ERR_INVALID_ARG        # no rows
+    assert pack(256 + 8, big, 2, 64, 64, None) == moe.MOE_ERR_INVALID_ARG   # misaligned
+    assert pack(4096, 4096 + 1024, 2, 64, 64, None) == moe.MOE_ERR_INVALID_ARG  # overlapping
+    assert b"overlap" in lib.moe_last_error()
