@@ -47,10 +47,11 @@ RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 DEFAULT_WORKLOAD = "deepseek_v3_fine"
 EVENT_EVERY = 4               # the dominant kernel is event-timed in the last step of every 4
 # Which GEMMs' weights a bf16 workload's weights are packed for (moe_pack_weights), by default: the
-# layout its GEMMs stream fastest (same box, alternating runs, against row-major weights):
-# DeepSeek-style GEMM1 3.62 -> 3.46 ms, GEMM2 unchanged; prefill GEMM1 1.80 -> 1.76 ms, GEMM2 908 -> 889 us;
-# Switch GEMM2 132 -> 118 us, GEMM1 235 -> 242 us; decode GEMM2 178 -> 169 us, GEMM1 294 -> 313 us.
-DEFAULT_PACKING = {"deepseek_v3_fine": "up", "mixtral_prefill": "both", "switch_top1_capacity": "down",
+# layout its GEMMs stream fastest with the plans the library takes for each (same box, alternating runs,
+# against row-major weights): DeepSeek-style GEMM1 3.62 -> 3.46 ms, GEMM2 1.93 -> 1.89 ms; prefill GEMM1
+# 1.80 -> 1.76 ms, GEMM2 908 -> 889 us; Switch GEMM1 235 -> 228 us, GEMM2 132 -> 118 us; decode GEMM2
+# 178 -> 169 us, GEMM1 294 -> 313 us (so decode keeps W1 / W3 row-major).
+DEFAULT_PACKING = {"deepseek_v3_fine": "both", "mixtral_prefill": "both", "switch_top1_capacity": "both",
                    "mixtral_decode": "down"}
 
 

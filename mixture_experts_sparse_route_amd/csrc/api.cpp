@@ -370,7 +370,7 @@ moe_status do_route(const moe_config* c, const Shape& s, const Layout& L, const 
 
 // The GEMM plan of an FFN of the layer, with its weights' layout.
 FfnPlan plan_of(const Shape& s, int64_t max_rows, int64_t group_max, int64_t n_groups, int64_t F) {
-  FfnPlan p = ffn_plan(s.bf16, s.w8, max_rows, group_max, n_groups, F, s.d);
+  FfnPlan p = ffn_plan(s.bf16, s.w8, max_rows, group_max, n_groups, F, s.d, s.packed_up, s.packed_down);
   p.packed_up = s.packed_up;
   p.packed_down = s.packed_down;
   return p;

@@ -53,6 +53,7 @@ namespace moe {
 namespace {
 
 constexpr int BKS = 32;   // k per stage
+constexpr int kCpolNT = 2;  // cache-policy operand of a load: the nt (non-temporal) bit
 constexpr int RB = 64;    // LDS bytes per tile row
 constexpr int LDS_BYTES = 160 * 1024;
 
@@ -91,6 +92,9 @@ struct GemmArgs {
   // row-major.
   int w_packed;
   int64_t w_bs;
+  // nonzero: the weight DMA loads carry the non-temporal cache policy (for
+  // plans whose weight tiles are each read by one m-tile)
+  int w_nt;
 };
 
 // A operand modes: row-major; k-blocked in blocks of 32 k ([Kdim/32][rows][32])
@@ -319,9 +323,15 @@ struct Issuer {
                                        0, 0);
     constexpr int WOFF = BM * (K64 ? 2 * RB : RB);  // weight tile offset in the stage
     constexpr int WLOAD = WK == WK_BF16_64 ? 8 * 2 * RB : (WK == WK_E4M3_32 ? 32 * 32 : 16 * RB);  // bytes per load
+    if (p.w_nt) {
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
-      __builtin_amdgcn_global_load_lds(wb[j] + wo, (lds_ptr_t)(st + WOFF + (wave + 4 * j) * WLOAD), 16, 0, 0);
+      for (int j = 0; j < NB; ++j)
+        __builtin_amdgcn_global_load_lds(wb[j] + wo, (lds_ptr_t)(st + WOFF + (wave + 4 * j) * WLOAD), 16, 0, kCpolNT);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        __builtin_amdgcn_global_load_lds(wb[j] + wo, (lds_ptr_t)(st + WOFF + (wave + 4 * j) * WLOAD), 16, 0, 0);
+    }
   }
 };
 
@@ -611,7 +621,8 @@ static inline void set_layout(GemmArgs& a, int64_t a_blk, int64_t c_blk, int kbw
 
 // bf16 weights row-major [groups][N][Kdim] or packed in 64-row panels
 // [groups][N/64][Kdim/64][64][64]
-static inline void set_weight_layout(GemmArgs& a, bool packed) {
+static inline void set_weight_layout(GemmArgs& a, bool packed, bool nt) {
+  a.w_nt = nt ? 1 : 0;
   a.w_packed = packed ? 1 : 0;
   a.w_bs = packed ? 64 * 2 * RB : 2 * RB;
 }

@@ -26,7 +26,7 @@ hipError_t gemm_bf16_down(const FfnPlan& pl, const void* h, int64_t h_blk, const
   GemmArgs a{(const uint16_t*)h, W2, nullptr, s2, nullptr, yp, tab, count, (int)d, (int)F};
   set_layout(a, h_blk, 0);
   if (pl.packed_down && pl.w8) return hipErrorInvalidValue;
-  set_weight_layout(a, pl.packed_down);
+  set_weight_layout(a, pl.packed_down, pl.nt_down);
   if (fuse) a.fuse = *fuse;
   if (F / (pl.k64_down ? 2 * BKS : BKS) < pl.ns_down - 1) return hipErrorInvalidValue;
   a.xcd_chunk = pl.wg_per_cu > 0 ? 0 : pl.xcd_chunk_down;

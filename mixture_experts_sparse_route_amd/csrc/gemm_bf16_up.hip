@@ -12,7 +12,7 @@ hipError_t gemm_bf16_gate_up(const FfnPlan& pl, const AOperand& A, const int4* t
     return hipErrorInvalidValue;
   set_layout(a, A.blk_rows, h_blk, A.blk_rows ? A.kbw : BKS);
   if (pl.packed_up && pl.w8) return hipErrorInvalidValue;
-  set_weight_layout(a, pl.packed_up);
+  set_weight_layout(a, pl.packed_up, pl.nt_up);
   a.gather = A.gather;
   a.gather_div = A.gather_div;
   if (d / (pl.k64_up ? 2 * BKS : BKS) < pl.ns_up - 1) return hipErrorInvalidValue;

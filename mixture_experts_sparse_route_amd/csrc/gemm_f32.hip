@@ -107,7 +107,8 @@ static int env_int(const char* name, int def) {
   return e ? atoi(e) : def;
 }
 
-FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_t n_groups, int64_t F, int64_t d) {
+FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_t n_groups, int64_t F, int64_t d,
+                 bool packed_up, bool packed_down) {
   if (!bf16) return FfnPlan{FB, 0, 1, 0, 1, 0, FB, FB, false, FB, false, false};
   // Fields: bm, bnb_up, ns_up, bnb_down, ns_down, wg_per_cu, bn_out_up,
   // bn_out_down, w8, bm_down, k64_up, k64_down.
@@ -133,6 +134,14 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_
     // decode 0.532 -> 0.523 ms against 3 stages at two workgroups per CU
     p = w8 ? FfnPlan{64, 128, 5, 128, 5, 0, 64, 128, true, 64, true, true}
            : FfnPlan{64, 128, 5, 128, 5, 0, 64, 128, false, 64, true, true};
+    // every weight tile is read by one m-tile: bf16 W1 / W3 stream faster
+    // with the non-temporal load policy (same box: Mixtral-shaped decode
+    // gate_up 290-293 -> 270-273 us; the DeepSeek-style layer at 512 tokens
+    // 2171-2176 -> 1934-1949 us on packed weights); E4M3 weights (225 ->
+    // 236 us), the streaming GEMM2 (no change) and the plans whose weight
+    // tiles several m-tiles share (DeepSeek-style, prefill, Switch: 5-40%
+    // slower) keep the default policy
+    p.nt_up = !w8;
   } else if (w8k64) {
     p = FfnPlan{64, 256, 3, 256, 3, 0, 128, 256, true, 64, true, true};
   } else if (w8) {
@@ -168,12 +177,30 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_
       p.bm_down = 192;
       p.bnb_down = 128;
       p.ns_down = 4;
+      // packed W1 / W3: GEMM1 in 192 x 128 tiles, 2 stages of 64 k, as for
+      // unbounded groups (same box, Switch: gate_up 235 us on row-major
+      // weights in 128 x 256 x 3 of 32 k, 243 packed, 228 packed in these)
+      if (packed_up) {
+        p.bm = 192;
+        p.bnb_up = 128;
+        p.ns_up = 2;
+        p.k64_up = true;
+      }
     } else {
       p.bm_down = p.bm;
       p.bm = 192;
       p.bnb_up = 128;
       p.ns_up = 2;
       p.k64_up = true;
+      // packed W2: GEMM2 in 192 x 128 tiles, 2 stages of 64 k (same box,
+      // DeepSeek-style: down 1.93 ms on row-major weights in 128 x 256 x 3 of
+      // 32 k, 1.94 packed, 1.89 packed in these)
+      if (packed_down) {
+        p.bm_down = 192;
+        p.bnb_down = 128;
+        p.ns_down = 2;
+        p.k64_down = true;
+      }
       if (avg >= 512) {
         // GEMM1's m-tiles split evenly (same box: prefill gate_up
         // 1.83 -> 1.80 ms; the same split of GEMM2's measured 0.94 -> 0.95)
@@ -227,7 +254,7 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_
   // overrides for tuning, honoured with MOE_TUNING=1 only: MOE_GEMM_K64
   // (both GEMMs in stages of 64 k, 0 or 1), MOE_GEMM_K64_DOWN, MOE_GEMM_BM, MOE_GEMM_BM_DOWN,
   // MOE_GEMM_{BNB,NS}_{UP,DOWN}, MOE_GEMM_WGS, MOE_GEMM_EVEN_UP, MOE_GEMM_STREAM{,_UP,_DOWN},
-  // MOE_GEMM_STREAM_U, MOE_GEMM_XCD_CHUNK{,_UP,_DOWN}; a set that names no compiled
+  // MOE_GEMM_STREAM_U, MOE_GEMM_XCD_CHUNK{,_UP,_DOWN}, MOE_GEMM_NT_{UP,DOWN}; a set that names no compiled
   // configuration leaves the plan as it was
   const FfnPlan def = p;
   const int k64_env = env_int("MOE_GEMM_K64", -1);
@@ -250,6 +277,8 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_
   if (xc_env >= 0) p.xcd_chunk_up = p.xcd_chunk_down = xc_env;
   p.xcd_chunk_up = env_int("MOE_GEMM_XCD_CHUNK_UP", p.xcd_chunk_up);
   p.xcd_chunk_down = env_int("MOE_GEMM_XCD_CHUNK_DOWN", p.xcd_chunk_down);
+  p.nt_up = env_int("MOE_GEMM_NT_UP", p.nt_up ? 1 : 0) != 0;
+  p.nt_down = env_int("MOE_GEMM_NT_DOWN", p.nt_down ? 1 : 0) != 0;
   if (!gemm_bf16_has_config(w8, p.k64_up, p.bm, p.bnb_up, p.ns_up) ||
       !gemm_bf16_has_config(w8, p.k64_down, p.bm_down, p.bnb_down, p.ns_down) ||
       d / (p.k64_up ? 64 : 32) < p.ns_up - 1 || F / (p.k64_down ? 64 : 32) < p.ns_down - 1)
@@ -287,7 +316,7 @@ hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const AOperand& A, c
   hipError_t err;
   if (p.packed_up && !bf16) return hipErrorInvalidValue;  // packed weights are bf16
   if (bf16 && p.stream_up) {
-    err = stream_gate_up(A, offsets, n_groups, W1, W3, h, max_rows, F, d, p.packed_up, s);
+    err = stream_gate_up(A, offsets, n_groups, W1, W3, h, max_rows, F, d, p.packed_up, p.nt_up, s);
   } else if (bf16) {
     err = gemm_bf16_gate_up(p, A, tab, count, grid, W1, W3, s1, s3, h, max_rows, F, d, s);
   } else {
@@ -309,7 +338,7 @@ hipError_t launch_gemm_down(bool bf16, const FfnPlan& p, const void* h, const in
   hipError_t err;
   if (p.packed_down && !bf16) return hipErrorInvalidValue;
   if (bf16 && p.stream_down) {
-    err = stream_down(h, max_rows, offsets, n_groups, W2, yp, F, d, p.stream_u, p.packed_down, s);
+    err = stream_down(h, max_rows, offsets, n_groups, W2, yp, F, d, p.stream_u, p.packed_down, p.nt_down, s);
   } else if (bf16) {
     err = gemm_bf16_down(p, h, max_rows, tab, count, grid, W2, s2, yp, fuse, F, d, s);
   } else {

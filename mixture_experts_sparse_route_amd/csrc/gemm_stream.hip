@@ -38,6 +38,7 @@ struct StreamArgs {
   // weights packed in 64-row panels [groups][N/64][K/64][64][64] (the tile
   // kernels' packed layout), else row-major
   int w_packed;
+  int w_nt;  // weight loads non-temporal
 };
 
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
@@ -97,8 +98,13 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(const StreamArgs p) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int64_t wk = (int64_t)((kt + u) >> 1) * w_bs + ((kt + u) & 1) * 32;
-        bt.w[0][u] = *(const bf16x8_t*)(b0 + wk);
-        if constexpr (GATE_UP) bt.w[1][u] = *(const bf16x8_t*)(b1 + wk);
+        if (p.w_nt) {
+          bt.w[0][u] = __builtin_nontemporal_load((const bf16x8_t*)(b0 + wk));
+          if constexpr (GATE_UP) bt.w[1][u] = __builtin_nontemporal_load((const bf16x8_t*)(b1 + wk));
+        } else {
+          bt.w[0][u] = *(const bf16x8_t*)(b0 + wk);
+          if constexpr (GATE_UP) bt.w[1][u] = *(const bf16x8_t*)(b1 + wk);
+        }
         bt.a[0][u] = *(const bf16x8_t*)(a0 + (int64_t)(kt + u) * p.a_ks);
       }
       if (two) {
@@ -170,7 +176,7 @@ hipError_t launch_stream(const StreamArgs& a, int64_t n_groups, int u_max, hipSt
 }  // namespace
 
 hipError_t stream_gate_up(const AOperand& A, const int32_t* offsets, int64_t n_groups, const void* W1, const void* W3,
-                          void* h, int64_t h_blk, int64_t F, int64_t d, bool packed, hipStream_t s) {
+                          void* h, int64_t h_blk, int64_t F, int64_t d, bool packed, bool nt, hipStream_t s) {
   if (A.blk_rows && A.kbw != 32) return hipErrorInvalidValue;
   if (A.gather && A.gather_div < 1) return hipErrorInvalidValue;
   StreamArgs a{};
@@ -188,11 +194,12 @@ hipError_t stream_gate_up(const AOperand& A, const int32_t* offsets, int64_t n_g
   a.N = (int)F;
   a.K = (int)d;
   a.w_packed = packed ? 1 : 0;
+  a.w_nt = nt ? 1 : 0;
   return launch_stream<true>(a, n_groups, 4, s);
 }
 
 hipError_t stream_down(const void* h, int64_t h_blk, const int32_t* offsets, int64_t n_groups, const void* W2,
-                       float* yp, int64_t F, int64_t d, int u_max, bool packed, hipStream_t s) {
+                       float* yp, int64_t F, int64_t d, int u_max, bool packed, bool nt, hipStream_t s) {
   StreamArgs a{};
   a.A = (const uint16_t*)h;
   a.a_rs = 32;
@@ -208,6 +215,7 @@ hipError_t stream_down(const void* h, int64_t h_blk, const int32_t* offsets, int
   a.N = (int)d;
   a.K = (int)F;
   a.w_packed = packed ? 1 : 0;
+  a.w_nt = nt ? 1 : 0;
   return launch_stream<false>(a, n_groups, u_max, s);
 }
 

@@ -179,6 +179,9 @@ struct FfnPlan {
   // [groups][N/64][K/64][64][64] (moe_pack_weights), else row-major
   bool packed_up = false;
   bool packed_down = false;
+  // GEMM1 / GEMM2 weight loads with the non-temporal cache policy
+  bool nt_up = false;
+  bool nt_down = false;
 };
 // Compute units of the current device (queried once).
 int device_cus();
@@ -188,7 +191,10 @@ int device_cus();
 bool tuning_enabled();
 // group_max: upper bound of any group's rows (the expert capacity when there
 // is one); max_rows: of all groups together.
-FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_t n_groups, int64_t F, int64_t d);
+// packed_up / packed_down: W1, W3 / W2 in moe_pack_weights' layout, which
+// some plans stream faster.
+FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_t n_groups, int64_t F, int64_t d,
+                 bool packed_up = false, bool packed_down = false);
 // Whether the bf16-activation GEMM is compiled for (m-tile rows, weight-tile
 // rows, stages), with bf16 (w8 false) or E4M3 (w8 true) weights in stages of
 // 32 k or (k64) 64 k.
@@ -240,11 +246,11 @@ struct AOperand {
 // k-blocked with h_blk rows; yp row-major fp32.  packed: the weights are in
 // the packed layout of moe_pack_weights, else row-major.
 hipError_t stream_gate_up(const AOperand& A, const int32_t* offsets, int64_t n_groups, const void* W1, const void* W3,
-                          void* h, int64_t h_blk, int64_t F, int64_t d, bool packed, hipStream_t s);
+                          void* h, int64_t h_blk, int64_t F, int64_t d, bool packed, bool nt, hipStream_t s);
 // u_max: 32-k steps per load batch of GEMM2 (8 or 4; fewer when K / 32 is
 // not a multiple).
 hipError_t stream_down(const void* h, int64_t h_blk, const int32_t* offsets, int64_t n_groups, const void* W2,
-                       float* yp, int64_t F, int64_t d, int u_max, bool packed, hipStream_t s);
+                       float* yp, int64_t F, int64_t d, int u_max, bool packed, bool nt, hipStream_t s);
 
 // bf16 MFMA path (gemm_bf16.hip); called through the launchers below.
 // s1 / s3 / s2: [groups, N] row scales of E4M3 weights (p.w8), else unused.

@@ -77,7 +77,10 @@ CASES = {
     "deepseek_small": workload("deepseek_v3_fine", T=300, d=512, F=256, E=64, Fs=256),
     "mixtral_two_mtiles": workload("mixtral_prefill", T=1100, d=256, F=384),
     "mixtral_550_rows": workload("mixtral_prefill", T=2200, d=256, F=384),
-    "switch_small": workload("switch_top1_capacity", T=1024, d=256, F=512, E=16),
+    # uncapped groups averaging 250 rows: GEMM2 on packed W2 takes 192 x 128 tiles of 64 k
+    "deepseek_mid": workload("deepseek_v3_fine", T=2000, d=256, F=256, E=64, Fs=256),
+    # capacity 160: GEMM1 on packed W1 / W3 takes 192 x 128 tiles of 64 k
+    "switch_capacity_160": workload("switch_top1_capacity", T=2048, d=256, F=512, E=16),
     "decode_small": workload("mixtral_decode", T=8, d=256, F=512),
     "short_reduction": workload("mixtral_prefill", T=700, d=64, F=128),
 }
