@@ -125,3 +125,20 @@ def test_packed_needs_bf16_weights():
     spec = spec_of(wl, packed="both")
     with pytest.raises(moe.MoeError):
         moe.workspace_size(spec)
+
+
+def test_packed_noalloc_matches_forward():
+    """moe_forward_noalloc on packed weights gives moe_forward's output on
+    the same packed weights bit for bit (same kernels and plans)."""
+    case = Case(CASES["deepseek_mid"])
+    wl = case.wl
+    y0, _ = forward(case, "both")
+    spec = spec_of(wl, out_dtype="f32", packed="both")
+    d = dict(case.d)
+    for k in UP + DOWN:
+        d[k] = packed_of(d[k])
+    y1 = torch.full((wl.T, wl.d), float("nan"), dtype=torch.float32, device="cuda")
+    moe.moe_forward_noalloc(spec, d["x"], d["Wg"], d["logit_bias"], d["sel_bias"], d["W1"], d["W3"], d["W2"],
+                            d["Ws1"], d["Ws3"], d["Ws2"], y1, None)
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int32), y1.view(torch.int32)), "noalloc output on packed weights differs"
