@@ -41,8 +41,9 @@
  *     MOE_GEMM_NS_DOWN, MOE_GEMM_WGS, MOE_GEMM_EVEN_UP, MOE_GEMM_STREAM,
  *     MOE_GEMM_STREAM_UP, MOE_GEMM_STREAM_DOWN, MOE_GEMM_STREAM_U,
  *     MOE_GEMM_XCD_CHUNK, MOE_GEMM_XCD_CHUNK_UP, MOE_GEMM_XCD_CHUNK_DOWN,
- *     MOE_GEMM_NT_UP, MOE_GEMM_NT_DOWN, MOE_GATHER; MOE_ROUTER_WGS, read
- *     once); a set that names no compiled
+ *     MOE_GEMM_NT_UP, MOE_GEMM_NT_DOWN, MOE_GEMM_NT_ROWS_UP,
+ *     MOE_GEMM_NT_ROWS_DOWN, MOE_GATHER; MOE_ROUTER_WGS, read once); a set
+ *     that names no compiled
  *     configuration is ignored.  Results do not depend on the plan: every
  *     output element sums its 32-wide MFMA k-steps in k order whatever the
  *     tile shape, tile order or kernel.

@@ -95,6 +95,10 @@ struct GemmArgs {
   // nonzero: the weight DMA loads carry the non-temporal cache policy (for
   // plans whose weight tiles are each read by one m-tile)
   int w_nt;
+  // > 0: also for the tiles that hold a whole group of at most w_nt_rows
+  // rows (groups from offsets), whose weight tiles no other m-tile reads
+  int w_nt_rows;
+  const int32_t* offsets;
 };
 
 // A operand modes: row-major; k-blocked in blocks of 32 k ([Kdim/32][rows][32])
@@ -240,6 +244,7 @@ struct Issuer {
   }
 
   TileRef cur;   // tile whose k-steps are being issued
+  int nt;        // cur's weight loads take the non-temporal policy
   TileRef next;  // the following tile
   int tile;      // position of `cur` in this workgroup's tile sequence
   int64_t aks;   // A bytes per stage along k
@@ -265,6 +270,9 @@ struct Issuer {
   }
 
   __device__ __forceinline__ void setup(const GemmArgs& p, int wave, int lane) {
+    nt = p.w_nt;
+    if (!nt && p.w_nt_rows > 0 && cur.rows <= p.w_nt_rows)
+      nt = cur.row_first == p.offsets[cur.g] && cur.row_first + cur.rows == p.offsets[cur.g + 1];
     const int rows = cur.rows, row_first = cur.row_first;
     if constexpr (!K64) {
       // 32 k per stage; with 64-k blocks a stage is the half (kt & 1) of
@@ -323,7 +331,7 @@ struct Issuer {
                                        0, 0);
     constexpr int WOFF = BM * (K64 ? 2 * RB : RB);  // weight tile offset in the stage
     constexpr int WLOAD = WK == WK_BF16_64 ? 8 * 2 * RB : (WK == WK_E4M3_32 ? 32 * 32 : 16 * RB);  // bytes per load
-    if (p.w_nt) {
+    if (nt) {
 #pragma unroll
       for (int j = 0; j < NB; ++j)
         __builtin_amdgcn_global_load_lds(wb[j] + wo, (lds_ptr_t)(st + WOFF + (wave + 4 * j) * WLOAD), 16, 0, kCpolNT);

@@ -21,12 +21,14 @@ bool gemm_bf16_has_config(bool w8, bool k64, int bm, int bnb, int ns) {
 }
 
 hipError_t gemm_bf16_down(const FfnPlan& pl, const void* h, int64_t h_blk, const int4* tab, const int32_t* count,
-                          int64_t grid, const void* W2, const float* s2, float* yp, const CombineFuse* fuse, int64_t F,
-                          int64_t d, hipStream_t s) {
+                          const int32_t* offsets, int64_t grid, const void* W2, const float* s2, float* yp,
+                          const CombineFuse* fuse, int64_t F, int64_t d, hipStream_t s) {
   GemmArgs a{(const uint16_t*)h, W2, nullptr, s2, nullptr, yp, tab, count, (int)d, (int)F};
   set_layout(a, h_blk, 0);
   if (pl.packed_down && pl.w8) return hipErrorInvalidValue;
   set_weight_layout(a, pl.packed_down, pl.nt_down);
+  a.w_nt_rows = pl.nt_rows_down;
+  a.offsets = offsets;
   if (fuse) a.fuse = *fuse;
   if (F / (pl.k64_down ? 2 * BKS : BKS) < pl.ns_down - 1) return hipErrorInvalidValue;
   a.xcd_chunk = pl.wg_per_cu > 0 ? 0 : pl.xcd_chunk_down;

@@ -5,14 +5,16 @@
 namespace moe {
 
 hipError_t gemm_bf16_gate_up(const FfnPlan& pl, const AOperand& A, const int4* tab, const int32_t* count,
-                             int64_t grid, const void* W1, const void* W3, const float* s1, const float* s3, void* h,
-                             int64_t h_blk, int64_t F, int64_t d, hipStream_t s) {
+                             const int32_t* offsets, int64_t grid, const void* W1, const void* W3, const float* s1,
+                             const float* s3, void* h, int64_t h_blk, int64_t F, int64_t d, hipStream_t s) {
   GemmArgs a{(const uint16_t*)A.ptr, W1, W3, s1, s3, h, tab, count, (int)F, (int)d};
   if ((A.gather && A.gather_div < 1) || (A.blk_rows && A.kbw != 32 && A.kbw != 64) || (A.blk_rows && d % A.kbw))
     return hipErrorInvalidValue;
   set_layout(a, A.blk_rows, h_blk, A.blk_rows ? A.kbw : BKS);
   if (pl.packed_up && pl.w8) return hipErrorInvalidValue;
   set_weight_layout(a, pl.packed_up, pl.nt_up);
+  a.w_nt_rows = pl.nt_rows_up;
+  a.offsets = offsets;
   a.gather = A.gather;
   a.gather_div = A.gather_div;
   if (d / (pl.k64_up ? 2 * BKS : BKS) < pl.ns_up - 1) return hipErrorInvalidValue;

@@ -192,6 +192,12 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_
       p.bnb_up = 128;
       p.ns_up = 2;
       p.k64_up = true;
+      // the tiles that hold a whole expert read weight tiles that no other
+      // m-tile reads: their weight loads take the non-temporal policy (same
+      // box, DeepSeek-style gate_up 3.46-3.47 -> 3.41-3.42 ms; GEMM2 and the
+      // plans in stages of 32 k, which read each 128-byte line in two
+      // stages, gain nothing or lose: Switch down 135 -> 180 us)
+      p.nt_rows_up = p.bm;
       // packed W2: GEMM2 in 192 x 128 tiles, 2 stages of 64 k (same box,
       // DeepSeek-style: down 1.93 ms on row-major weights in 128 x 256 x 3 of
       // 32 k, 1.94 packed, 1.89 packed in these)
@@ -205,6 +211,7 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_
         // GEMM1's m-tiles split evenly (same box: prefill gate_up
         // 1.83 -> 1.80 ms; the same split of GEMM2's measured 0.94 -> 0.95)
         p.even_up = true;
+        p.nt_rows_up = 0;  // groups of 512 rows and more share every weight tile
         p.bm_down = 192;
         p.bnb_down = 128;
         p.ns_down = 2;
@@ -231,6 +238,8 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_
   };
   shallow(d, p.k64_up, p.ns_up, p.bnb_up);
   shallow(F, p.k64_down, p.ns_down, p.bnb_down);
+  if (!p.k64_up) p.nt_rows_up = 0;  // stages of 32 k read a line in two halves
+  if (!p.k64_down) p.nt_rows_down = 0;
   // bf16 weights and at most 32 rows in any group (decode-sized batches):
   // GEMM2 is the weight-streaming kernel, which reads 512 bytes of each
   // weight row per load batch instead of 128 per LDS stage (same box, Mixtral
@@ -254,7 +263,8 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_
   // overrides for tuning, honoured with MOE_TUNING=1 only: MOE_GEMM_K64
   // (both GEMMs in stages of 64 k, 0 or 1), MOE_GEMM_K64_DOWN, MOE_GEMM_BM, MOE_GEMM_BM_DOWN,
   // MOE_GEMM_{BNB,NS}_{UP,DOWN}, MOE_GEMM_WGS, MOE_GEMM_EVEN_UP, MOE_GEMM_STREAM{,_UP,_DOWN},
-  // MOE_GEMM_STREAM_U, MOE_GEMM_XCD_CHUNK{,_UP,_DOWN}, MOE_GEMM_NT_{UP,DOWN}; a set that names no compiled
+  // MOE_GEMM_STREAM_U, MOE_GEMM_XCD_CHUNK{,_UP,_DOWN}, MOE_GEMM_NT_{UP,DOWN}, MOE_GEMM_NT_ROWS_{UP,DOWN};
+  // a set that names no compiled
   // configuration leaves the plan as it was
   const FfnPlan def = p;
   const int k64_env = env_int("MOE_GEMM_K64", -1);
@@ -278,6 +288,8 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_
   p.xcd_chunk_up = env_int("MOE_GEMM_XCD_CHUNK_UP", p.xcd_chunk_up);
   p.xcd_chunk_down = env_int("MOE_GEMM_XCD_CHUNK_DOWN", p.xcd_chunk_down);
   p.nt_up = env_int("MOE_GEMM_NT_UP", p.nt_up ? 1 : 0) != 0;
+  p.nt_rows_up = env_int("MOE_GEMM_NT_ROWS_UP", p.nt_rows_up);
+  p.nt_rows_down = env_int("MOE_GEMM_NT_ROWS_DOWN", p.nt_rows_down);
   p.nt_down = env_int("MOE_GEMM_NT_DOWN", p.nt_down ? 1 : 0) != 0;
   if (!gemm_bf16_has_config(w8, p.k64_up, p.bm, p.bnb_up, p.ns_up) ||
       !gemm_bf16_has_config(w8, p.k64_down, p.bm_down, p.bnb_down, p.ns_down) ||
@@ -318,7 +330,7 @@ hipError_t launch_gemm_gate_up(bool bf16, const FfnPlan& p, const AOperand& A, c
   if (bf16 && p.stream_up) {
     err = stream_gate_up(A, offsets, n_groups, W1, W3, h, max_rows, F, d, p.packed_up, p.nt_up, s);
   } else if (bf16) {
-    err = gemm_bf16_gate_up(p, A, tab, count, grid, W1, W3, s1, s3, h, max_rows, F, d, s);
+    err = gemm_bf16_gate_up(p, A, tab, count, offsets, grid, W1, W3, s1, s3, h, max_rows, F, d, s);
   } else {
     F32Args a{(const float*)A.ptr, (const float*)W1, (const float*)W3, (float*)h, tab, count, (int)F, (int)d};
     gemm_f32_kernel<true><<<(unsigned)grid, 256, 0, s>>>(a);
@@ -340,7 +352,7 @@ hipError_t launch_gemm_down(bool bf16, const FfnPlan& p, const void* h, const in
   if (bf16 && p.stream_down) {
     err = stream_down(h, max_rows, offsets, n_groups, W2, yp, F, d, p.stream_u, p.packed_down, p.nt_down, s);
   } else if (bf16) {
-    err = gemm_bf16_down(p, h, max_rows, tab, count, grid, W2, s2, yp, fuse, F, d, s);
+    err = gemm_bf16_down(p, h, max_rows, tab, count, offsets, grid, W2, s2, yp, fuse, F, d, s);
   } else {
     F32Args a{(const float*)h, (const float*)W2, nullptr, yp, tab, count, (int)d, (int)F};
     gemm_f32_kernel<false><<<(unsigned)grid, 256, 0, s>>>(a);

@@ -182,6 +182,10 @@ struct FfnPlan {
   // GEMM1 / GEMM2 weight loads with the non-temporal cache policy
   bool nt_up = false;
   bool nt_down = false;
+  // > 0: the tiles that hold a whole group of at most this many rows also
+  // load their weights non-temporally (no other m-tile reads them)
+  int nt_rows_up = 0;
+  int nt_rows_down = 0;
 };
 // Compute units of the current device (queried once).
 int device_cus();
@@ -257,11 +261,11 @@ hipError_t stream_down(const void* h, int64_t h_blk, const int32_t* offsets, int
 // a_blk / h_blk: the row count R of a k-blocked operand ([cols/32][R][32]:
 // the 32 columns of a k-step of R rows are one contiguous run), 0 = row-major.
 hipError_t gemm_bf16_gate_up(const FfnPlan& p, const AOperand& A, const int4* tab, const int32_t* count,
-                             int64_t grid, const void* W1, const void* W3, const float* s1, const float* s3, void* h,
-                             int64_t h_blk, int64_t F, int64_t d, hipStream_t s);
+                             const int32_t* offsets, int64_t grid, const void* W1, const void* W3, const float* s1,
+                             const float* s3, void* h, int64_t h_blk, int64_t F, int64_t d, hipStream_t s);
 hipError_t gemm_bf16_down(const FfnPlan& p, const void* h, int64_t h_blk, const int4* tab, const int32_t* count,
-                          int64_t grid, const void* W2, const float* s2, float* yp, const CombineFuse* fuse, int64_t F,
-                          int64_t d, hipStream_t s);
+                          const int32_t* offsets, int64_t grid, const void* W2, const float* s2, float* yp,
+                          const CombineFuse* fuse, int64_t F, int64_t d, hipStream_t s);
 // bf16: h is k-blocked with max_rows rows; A as AOperand says; fp32:
 // everything row-major (A.ptr only).
 // prof_id: the timing facility's kernel id of the launch (the routed or the

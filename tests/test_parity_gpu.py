@@ -227,6 +227,9 @@ PLAN_OVERRIDES = {
     "xcd_ranges": {"MOE_GEMM_XCD_CHUNK": "0"},
     "xcd_chunks_of_1": {"MOE_GEMM_XCD_CHUNK": "1"},
     "xcd_chunks_of_3": {"MOE_GEMM_XCD_CHUNK_UP": "3", "MOE_GEMM_XCD_CHUNK_DOWN": "5"},
+    # cache policy only: non-temporal weight loads everywhere, or for whole-group tiles
+    "nt_everywhere": {"MOE_GEMM_NT_UP": "1", "MOE_GEMM_NT_DOWN": "1"},
+    "nt_whole_groups": {"MOE_GEMM_NT_ROWS_UP": "100000", "MOE_GEMM_NT_ROWS_DOWN": "100000"},
 }
 
 
