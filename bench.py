@@ -9,6 +9,11 @@ DeepSeek-V3-style fine-grained layer (T=4096, d_model=7168, 256 routed
 experts of d_ff=2048, sigmoid gate with a selection bias, Top-8
 renormalised, one shared expert of d_ff=2048, bf16, fp32 router).
 
+Expert weights are packed once by ``moe_pack_weights`` before anything is
+timed, for the GEMMs the workload's default names (``--packed``; the line's
+``config.packed_weights`` and ``weight_pack_ms`` report the choice and its
+one-time cost).
+
 Prints one JSON line: tokens/s, the dominant kernel's roofline position
 (measured with HIP events on the launch stream inside the timed region), the
 whole layer's flops and bytes rates, and the CPU oracle timed on a bounded
