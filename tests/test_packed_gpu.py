@@ -142,3 +142,44 @@ def test_packed_noalloc_matches_forward():
                             d["Ws1"], d["Ws3"], d["Ws2"], y1, None)
     torch.cuda.synchronize()
     assert torch.equal(y0.view(torch.int32), y1.view(torch.int32)), "noalloc output on packed weights differs"
+
+
+def forward_variant(case: Case, packed: str, **spec_kw):
+    """moe_forward with the routing variants of spec_kw (expert choice, drop
+    policy, statistics, residual) on packed or row-major weights."""
+    wl = case.wl
+    spec = spec_of(wl, out_dtype="f32", packed=packed, **spec_kw)
+    if spec_kw.get("expert_choice"):
+        spec.renorm = False
+    d = dict(case.d)
+    names = {"none": (), "up": UP, "down": DOWN, "both": UP + DOWN}[packed]
+    for k in names:
+        if d.get(k) is not None:
+            d[k] = packed_of(d[k])
+    r = moe.Routing(spec)
+    ws, _ = moe.alloc_workspace(spec)
+    y = torch.full((wl.T, wl.d), float("nan"), dtype=torch.float32, device="cuda")
+    moe.moe_forward(spec, d["x"], d["Wg"], d["logit_bias"], d["sel_bias"], d["W1"], d["W3"], d["W2"], d["Ws1"],
+                    d["Ws3"], d["Ws2"], y, r, ws, scales=device_scales(d))
+    torch.cuda.synchronize()
+    return y
+
+
+VARIANTS = {
+    "expert_choice": dict(expert_choice=True),
+    "drop_affinity": dict(drop_policy="affinity"),
+    "drop_reroute": dict(drop_policy="reroute"),
+    "stats_residual": dict(stats=True, residual=True),
+}
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_packed_routing_variants_bit_identical(variant):
+    """The routing variants feed the same grouped GEMMs: packed weights give
+    the row-major outputs bit for bit (Switch shape with capacity 160)."""
+    case = Case(CASES["switch_capacity_160"])
+    print(variant, flush=True)
+    y0 = forward_variant(case, "none", **VARIANTS[variant])
+    for packed in ("up", "down", "both"):
+        y1 = forward_variant(case, packed, **VARIANTS[variant])
+        assert torch.equal(y0.view(torch.int32), y1.view(torch.int32)), f"{variant} with {packed} packed differs"
