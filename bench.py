@@ -58,6 +58,11 @@ EVENT_EVERY = 4               # the dominant kernel is event-timed in the last s
 # 178 -> 169 us, GEMM1 294 -> 313 us (so decode keeps W1 / W3 row-major).
 DEFAULT_PACKING = {"deepseek_v3_fine": "both", "mixtral_prefill": "both", "switch_top1_capacity": "both",
                    "mixtral_decode": "down"}
+# E4M3 expert weights likewise (same box, alternating runs, layer ms row-major -> packed): DeepSeek-style
+# 5.11-5.12 -> 5.01 (W1 / W3; all: 5.05), prefill 2.83 -> 2.71-2.73 (all), decode 0.414-0.416 -> 0.396-0.399
+# (W1 / W3), Switch 0.366-0.375 -> 0.345 (all).
+DEFAULT_PACKING_FP8 = {"deepseek_v3_fine": "up", "mixtral_prefill": "both", "switch_top1_capacity": "both",
+                       "mixtral_decode": "up"}
 
 
 def parse():
@@ -76,7 +81,7 @@ def parse():
     ap.add_argument("--expert-choice", action="store_true", help="expert-choice routing instead of token choice")
     ap.add_argument("--fp8", action="store_true", help="FP8 E4M3 expert weights with per-row scales")
     ap.add_argument("--packed", default="auto", choices=["auto", "none", "up", "down", "both"],
-                    help="which GEMMs' expert weights moe_pack_weights packs once before timing (bf16 layers); "
+                    help="which GEMMs' expert weights moe_pack_weights packs once before timing (bf16 or E4M3); "
                          "auto: the layout measured fastest for the workload")
     return ap.parse_args()
 
@@ -185,7 +190,8 @@ def main():
     wl = workload(args.workload, **({"wdtype": "fp8"} if args.fp8 else {}), **({"T": args.tokens} if args.tokens else {}))
     packing = args.packed
     if packing == "auto":
-        packing = DEFAULT_PACKING.get(wl.name, "none") if wl.dtype == "bf16" and wl.wdtype != "fp8" else "none"
+        table = DEFAULT_PACKING_FP8 if wl.wdtype == "fp8" else DEFAULT_PACKING
+        packing = table.get(wl.name, "none") if wl.dtype == "bf16" else "none"
     lib = moe.load_library()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)

@@ -148,7 +148,8 @@ enum {
    * MOE_F_PACKED_DOWN.  The same values, so every result is bit for bit that
    * of the row-major weights; which layout streams faster depends on the
    * GEMM's tile plan, so a caller chooses per matrix once, when it loads
-   * the weights.  bf16 weights only (MOE_ERR_UNSUPPORTED otherwise). */
+   * the weights.  bf16 or E4M3 weights (MOE_ERR_UNSUPPORTED for fp32); the
+   * E4M3 row scales stay [groups, N]. */
   MOE_F_PACKED_UP = 64u,
   MOE_F_PACKED_DOWN = 128u
 };
@@ -279,17 +280,21 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* xp, const int32_t* 
  * workgroup reads one step of 64-row blocks of rows at a time; in the
  * row-major layout those are 128-byte pieces of rows 2 d or 2 F bytes apart.
  * The packed layout cuts each group's rows into panels of 64 rows and stores
- * a panel's 64-element steps one after the other, each as one 8 KB run:
- *   src: device [groups, N, K] bf16 row-major (nn.Linear out x in)
- *   dst: device [groups, N/64, K/64, 64, 64] bf16: element (g, n, k) of src
- *        at dst[(((g * (N/64) + n/64) * (K/64) + k/64) * 64 + n % 64) * 64 + k % 64]
+ * a panel's 64-element steps one after the other, each as one run of
+ * 64 x 64 elements (8 KB of bf16, 4 KB of E4M3):
+ *   src: device [groups, N, K] row-major (nn.Linear out x in), elements of
+ *        w_dtype (MOE_BF16 or MOE_FP8_E4M3)
+ *   dst: device [groups, N/64, K/64, 64, 64], same elements: element
+ *        (g, n, k) of src at
+ *        dst[(((g * (N/64) + n/64) * (K/64) + k/64) * 64 + n % 64) * 64 + k % 64]
  * W1 / W3 are packed with (N, K) = (F, d) and W2 with (d, F) (the shared
  * expert's likewise with Fs); the result is then passed with
  * MOE_F_PACKED_UP / MOE_F_PACKED_DOWN.  groups >= 1; N and K positive multiples of 64 (as
  * every bf16 layer's d, F and Fs are); src and dst 16-byte aligned and not
  * overlapping, owned by the caller.  Enqueued on `stream`;
  * MOE_ERR_INVALID_ARG on a bad size or pointer, before any launch. */
-moe_status moe_pack_weights(const void* src, void* dst, int64_t groups, int64_t N, int64_t K, moe_stream_t stream);
+moe_status moe_pack_weights(const void* src, void* dst, int64_t groups, int64_t N, int64_t K, int32_t w_dtype,
+                            moe_stream_t stream);
 
 /* a9: weighted combine [TD §3.1 step 4; BD §4 step 5]:
  *   y[t] = sum_{k ascending, dest[t*K+k] >= 0} topk_w[t][k] * yp[dest[t*K+k]]

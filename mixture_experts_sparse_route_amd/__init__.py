@@ -84,7 +84,7 @@ def load_library(path: str = LIB_PATH):
         "moe_combine": [C, vp, R, vp, vp, vp, vp],
         "moe_forward": [C, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(MoeScales), vp, R, vp, sz, vp],
         "moe_forward_noalloc": [C, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(MoeScales), vp, R, vp],
-        "moe_pack_weights": [vp, vp, i64, i64, i64, vp],
+        "moe_pack_weights": [vp, vp, i64, i64, i64, i32, vp],
         "moe_profile_enable": [ctypes.c_uint32],
         "moe_profile_reset": [],
         "moe_profile_read": [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)],
@@ -272,11 +272,12 @@ def moe_expert_ffn(spec, xp, offsets, n_groups, max_rows_, W1, W3, W2, yp, ws, s
 
 
 def moe_pack_weights(src, dst, stream=None):
-    """dst <- src [groups, N, K] bf16 in the packed layout
-    [groups, N/64, K/64, 64, 64] (moe.h); src is 3-D, dst any device tensor
-    of the same size."""
+    """dst <- src [groups, N, K] (bf16, or uint8 E4M3 codes) in the packed
+    layout [groups, N/64, K/64, 64, 64] (moe.h); src is 3-D, dst any device
+    tensor of the same size."""
     G, N, K = src.shape
-    _check(load_library().moe_pack_weights(_ptr(src), _ptr(dst), G, N, K, _stream(stream)), "moe_pack_weights")
+    wd = MOE_FP8_E4M3 if src.element_size() == 1 else MOE_BF16
+    _check(load_library().moe_pack_weights(_ptr(src), _ptr(dst), G, N, K, wd, _stream(stream)), "moe_pack_weights")
 
 
 def moe_combine(spec, yp, routing: Routing, shared_out, x_residual, y, stream=None):

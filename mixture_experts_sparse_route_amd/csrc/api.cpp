@@ -102,8 +102,8 @@ moe_status validate(const moe_config* c, Shape* sh) {
     return fail(MOE_ERR_INVALID_ARG, "unknown out_dtype %d", (int)c->out_dtype);
   if (c->act_dtype == MOE_F32 && c->out_dtype != MOE_F32)
     return fail(MOE_ERR_UNSUPPORTED, "an fp32 layer has an fp32 output");
-  if ((c->flags & (MOE_F_PACKED_UP | MOE_F_PACKED_DOWN)) && c->w_dtype != MOE_BF16)
-    return fail(MOE_ERR_UNSUPPORTED, "packed weights (MOE_F_PACKED_UP / _DOWN) are implemented for bf16 weights");
+  if ((c->flags & (MOE_F_PACKED_UP | MOE_F_PACKED_DOWN)) && c->w_dtype == MOE_F32)
+    return fail(MOE_ERR_UNSUPPORTED, "packed weights (MOE_F_PACKED_UP / _DOWN) are bf16 or E4M3");
   const bool bf16 = c->act_dtype == MOE_BF16;
   if (bf16) {
     if (c->d_model % 64 || c->d_ff % 64 || (c->n_shared && c->d_ff_shared % 64))
@@ -742,8 +742,12 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* xp, const int32_t* 
                 (hipStream_t)stream);
 }
 
-moe_status moe_pack_weights(const void* src, void* dst, int64_t groups, int64_t N, int64_t K, moe_stream_t stream) {
+moe_status moe_pack_weights(const void* src, void* dst, int64_t groups, int64_t N, int64_t K, int32_t w_dtype,
+                            moe_stream_t stream) {
   if (!src || !dst) return fail(MOE_ERR_INVALID_ARG, "src and dst are required");
+  if (w_dtype != MOE_BF16 && w_dtype != MOE_FP8_E4M3)
+    return fail(MOE_ERR_INVALID_ARG, "w_dtype %d: packing takes MOE_BF16 or MOE_FP8_E4M3 weights", (int)w_dtype);
+  const int64_t esz = w_dtype == MOE_BF16 ? 2 : 1;
   if (groups < 1 || N < 64 || N % 64 || K < 64 || K % 64)
     return fail(MOE_ERR_INVALID_ARG, "groups = %lld must be >= 1, N = %lld and K = %lld positive multiples of 64",
                 (long long)groups, (long long)N, (long long)K);
@@ -751,10 +755,10 @@ moe_status moe_pack_weights(const void* src, void* dst, int64_t groups, int64_t 
     return fail(MOE_ERR_UNSUPPORTED, "groups * N or K exceeds the supported range");
   moe_status st;
   if ((st = check_aligned({src, dst})) != MOE_OK) return st;
-  const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst, n = (uintptr_t)(groups * N * K * 2);
+  const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst, n = (uintptr_t)(groups * N * K * esz);
   if (a < b + n && b < a + n) return fail(MOE_ERR_INVALID_ARG, "src and dst overlap");
   // N is a multiple of 64, so the panels of all groups' rows are the groups' panels
-  MOE_HIP(launch_pack_weights(src, dst, groups * N, K, (hipStream_t)stream));
+  MOE_HIP(launch_pack_weights(src, dst, groups * N, K, (int)esz, (hipStream_t)stream));
   return MOE_OK;
 }
 

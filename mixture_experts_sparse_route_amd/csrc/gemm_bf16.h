@@ -83,13 +83,13 @@ struct GemmArgs {
   // round-robin (one tile per workgroup), instead of one contiguous range
   // per XCD
   int xcd_chunk;
-  // bf16 weights row-major [groups][N][Kdim], or packed (w_packed) in
-  // panels of 64 rows [groups][N/64][Kdim/64][64][64]: element (g, n, k) at
-  // byte g N Kdim 2 + (n / 64) Kdim 128 + (k / 64) 8192 + (n % 64) 128 +
-  // (k % 64) 2, so the 64-k steps of a panel follow each other in memory and
-  // a stage reads whole 8 KB runs.  w_bs = bytes between a row's
-  // consecutive 64-k steps (128 row-major, 8192 packed).  E4M3 weights are
-  // row-major.
+  // weights (elements of e = 2 bytes for bf16, 1 for E4M3) row-major
+  // [groups][N][Kdim], or packed (w_packed) in panels of 64 rows
+  // [groups][N/64][Kdim/64][64][64]: element (g, n, k) at byte
+  // e (g N Kdim + (n / 64) 64 Kdim + (k / 64) 4096 + (n % 64) 64 + k % 64),
+  // so the 64-k steps of a panel follow each other in memory and a stage
+  // reads whole runs of 4096 e bytes.  w_bs = bytes between a row's
+  // consecutive 64-k steps (64 e row-major, 4096 e packed).
   int w_packed;
   int64_t w_bs;
   // nonzero: the weight DMA loads carry the non-temporal cache policy (for
@@ -227,8 +227,6 @@ struct Issuer {
   static constexpr int NB = WK == WK_BF16_64 ? BNB / 32 : (WK == WK_E4M3_32 ? BNB / 32 / 4 : BNB / 16 / 4);
   static constexpr int HALF = BNB / 4;  // gate_up: rows of one matrix in each quarter of the weight tile
   static constexpr int STAGE = stage_bytes<WK>(BM, BNB);
-  // weight bytes per stage and row
-  static constexpr int WKS = WK == WK_BF16_64 ? 2 * RB : (WK == WK_E4M3_32 ? 32 : RB);
 
   static constexpr bool KB64 = AM == AM_KB64 || AM == AM_GATHER64;  // A in blocks of 64 k
   // A row stride: the block width for a k-blocked A (known at compile time),
@@ -264,8 +262,8 @@ struct Issuer {
       col = cur.n0 + rt;
     }
     col = min(col, p.N - 1);
-    if ((WK == WK_BF16 || WK == WK_BF16_64) && p.w_packed)
-      return base + (int64_t)cur.g * p.N * p.Kdim * 2 + (int64_t)(col >> 6) * p.Kdim * 128 + (col & 63) * 128 + off;
+    if (p.w_packed)
+      return base + ((int64_t)cur.g * p.N * p.Kdim + (int64_t)(col >> 6) * 64 * p.Kdim + (col & 63) * 64) * esz + off;
     return base + (((int64_t)cur.g * p.N + col) * p.Kdim) * esz + off;
   }
 
@@ -322,9 +320,8 @@ struct Issuer {
     const int64_t ao = (!K64 && KB64) ? (int64_t)(kt >> 1) * aks + (kt & 1) * 2 * BKS : (int64_t)kt * aks;
     // weight offset of k-step kt: 64-k stage kt is block kt; a 32-k stage
     // is the half (kt & 1) of block kt >> 1
-    const int64_t wo = WK == WK_BF16_64 ? (int64_t)kt * p.w_bs
-                       : WK == WK_BF16  ? (int64_t)(kt >> 1) * p.w_bs + (kt & 1) * RB
-                                        : (int64_t)kt * WKS;
+    constexpr int E = (WK == WK_BF16 || WK == WK_BF16_64) ? 2 : 1;  // weight element bytes
+    const int64_t wo = K64 ? (int64_t)kt * p.w_bs : (int64_t)(kt >> 1) * p.w_bs + (kt & 1) * 32 * E;
 #pragma unroll
     for (int j = 0; j < NA; ++j)
       __builtin_amdgcn_global_load_lds(ab[j] + ao, (lds_ptr_t)(st + (wave + 4 * j) * (K64 ? 8 * 2 * RB : 16 * RB)), 16,
@@ -627,12 +624,12 @@ static inline void set_layout(GemmArgs& a, int64_t a_blk, int64_t c_blk, int kbw
   a.c_bs = c_blk ? 32 * c_blk : 32;
 }
 
-// bf16 weights row-major [groups][N][Kdim] or packed in 64-row panels
-// [groups][N/64][Kdim/64][64][64]
-static inline void set_weight_layout(GemmArgs& a, bool packed, bool nt) {
+// weights of esz-byte elements row-major [groups][N][Kdim] or packed in
+// 64-row panels [groups][N/64][Kdim/64][64][64]
+static inline void set_weight_layout(GemmArgs& a, bool packed, bool nt, int esz) {
   a.w_nt = nt ? 1 : 0;
   a.w_packed = packed ? 1 : 0;
-  a.w_bs = packed ? 64 * 2 * RB : 2 * RB;
+  a.w_bs = (packed ? 64 * 64 : 64) * (int64_t)esz;
 }
 
 // the configuration list of the weight kind (pl.w8, k64), each entry expanded by LAUNCH

@@ -25,8 +25,7 @@ hipError_t gemm_bf16_down(const FfnPlan& pl, const void* h, int64_t h_blk, const
                           const CombineFuse* fuse, int64_t F, int64_t d, hipStream_t s) {
   GemmArgs a{(const uint16_t*)h, W2, nullptr, s2, nullptr, yp, tab, count, (int)d, (int)F};
   set_layout(a, h_blk, 0);
-  if (pl.packed_down && pl.w8) return hipErrorInvalidValue;
-  set_weight_layout(a, pl.packed_down, pl.nt_down);
+  set_weight_layout(a, pl.packed_down, pl.nt_down, pl.w8 ? 1 : 2);
   a.w_nt_rows = pl.nt_rows_down;
   a.offsets = offsets;
   if (fuse) a.fuse = *fuse;

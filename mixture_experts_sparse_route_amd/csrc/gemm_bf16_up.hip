@@ -11,8 +11,7 @@ hipError_t gemm_bf16_gate_up(const FfnPlan& pl, const AOperand& A, const int4* t
   if ((A.gather && A.gather_div < 1) || (A.blk_rows && A.kbw != 32 && A.kbw != 64) || (A.blk_rows && d % A.kbw))
     return hipErrorInvalidValue;
   set_layout(a, A.blk_rows, h_blk, A.blk_rows ? A.kbw : BKS);
-  if (pl.packed_up && pl.w8) return hipErrorInvalidValue;
-  set_weight_layout(a, pl.packed_up, pl.nt_up);
+  set_weight_layout(a, pl.packed_up, pl.nt_up, pl.w8 ? 1 : 2);
   a.w_nt_rows = pl.nt_rows_up;
   a.offsets = offsets;
   a.gather = A.gather;

@@ -144,9 +144,9 @@ hipError_t launch_dispatch(const void* x, const int32_t* row_src, const int32_t*
 // x [T, d] bf16 -> k-blocked [d/kbw][T][kbw], kbw = 32 or 64 (row_bytes = 2 d,
 // a multiple of 2 kbw).
 hipError_t launch_kblock_copy(const void* x, void* xkb, int64_t T, int64_t row_bytes, int kbw, hipStream_t s);
-// moe_pack_weights: rows [rows, K] bf16 (rows a multiple of 64) into panels
-// [rows/64][K/64][64][64].
-hipError_t launch_pack_weights(const void* src, void* dst, int64_t rows, int64_t K, hipStream_t s);
+// moe_pack_weights: rows [rows, K] of esz-byte elements (bf16: 2, E4M3: 1;
+// rows a multiple of 64) into panels [rows/64][K/64][64][64].
+hipError_t launch_pack_weights(const void* src, void* dst, int64_t rows, int64_t K, int esz, hipStream_t s);
 
 // ---- grouped expert FFN (a6-a7) ----
 struct FfnPlan {

@@ -609,19 +609,21 @@ __global__ __launch_bounds__(256) void kblock_copy_kernel(const uint4* __restric
   for (; kb < n_kb; kb += 4) dst[kb * kb_stride] = src[kb * CPB];
 }
 
-// Weight packing (moe_pack_weights): rows [rows, K] of bf16 into panels of
-// 64 rows, [rows/64][K/64][64][64].  A workgroup moves 8 rows (lane: row
-// lane / 8, 16-byte chunk lane % 8 of a 128-byte step); wave w copies the
-// 64-k steps w, w + 4, ...
+// Weight packing (moe_pack_weights): rows [rows, K] into panels of 64
+// rows, [rows/64][K/64][64][64] elements.  CPS = 16-byte chunks in a 64-element
+// step of a row (8 for bf16, 4 for E4M3).  A workgroup moves 64 / CPS rows
+// (lane: row lane / CPS, chunk lane % CPS); wave w copies the 64-k steps w,
+// w + 4, ...
+template <int CPS>
 __global__ __launch_bounds__(256) void pack_weights_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                            int64_t rows, int n_kb) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t r = (int64_t)blockIdx.x * 8 + (lane >> 3);
-  const int c = lane & 7;
+  const int64_t r = (int64_t)blockIdx.x * (64 / CPS) + lane / CPS;
+  const int c = lane % CPS;
   if (r >= rows) return;
-  const uint4* s = src + r * n_kb * 8 + c;
-  uint4* d = dst + (r >> 6) * (int64_t)n_kb * 512 + (r & 63) * 8 + c;  // a panel step: 64 rows x 8 chunks
-  for (int kb = wave; kb < n_kb; kb += 4) d[(int64_t)kb * 512] = s[(int64_t)kb * 8];
+  const uint4* s = src + r * n_kb * CPS + c;
+  uint4* d = dst + (r >> 6) * (int64_t)n_kb * 64 * CPS + (r & 63) * CPS + c;  // a panel step: 64 rows x CPS chunks
+  for (int kb = wave; kb < n_kb; kb += 4) d[(int64_t)kb * 64 * CPS] = s[(int64_t)kb * CPS];
 }
 
 // ------------------------------------------------------------ FFN tiles
@@ -802,9 +804,12 @@ hipError_t launch_kblock_copy(const void* x, void* xkb, int64_t T, int64_t row_b
   return hipGetLastError();
 }
 
-hipError_t launch_pack_weights(const void* src, void* dst, int64_t rows, int64_t K, hipStream_t s) {
-  if (rows % 64 || K % 64 || rows < 64 || K < 64) return hipErrorInvalidValue;
-  pack_weights_kernel<<<(unsigned)(rows / 8), 256, 0, s>>>((const uint4*)src, (uint4*)dst, rows, (int)(K / 64));
+hipError_t launch_pack_weights(const void* src, void* dst, int64_t rows, int64_t K, int esz, hipStream_t s) {
+  if (rows % 64 || K % 64 || rows < 64 || K < 64 || (esz != 1 && esz != 2)) return hipErrorInvalidValue;
+  if (esz == 2)
+    pack_weights_kernel<8><<<(unsigned)(rows / 8), 256, 0, s>>>((const uint4*)src, (uint4*)dst, rows, (int)(K / 64));
+  else
+    pack_weights_kernel<4><<<(unsigned)(rows / 16), 256, 0, s>>>((const uint4*)src, (uint4*)dst, rows, (int)(K / 64));
   return hipGetLastError();
 }
 

@@ -278,19 +278,22 @@ def test_packed_weight_validation(lib):
     n = ctypes.c_size_t()
     assert (moe.MOE_F_PACKED_UP, moe.MOE_F_PACKED_DOWN) == (64, 128)
     for packed, bits in (("up", 64), ("down", 128), ("both", 192)):
-        c = spec(packed=packed).config()
-        assert c.flags & 192 == bits
-        assert lib.moe_workspace_size(ctypes.byref(c), ctypes.byref(n)) == moe.MOE_OK
-        for bad in (spec(packed=packed, dtype="f32"), spec(packed=packed, wdtype="fp8")):
-            c = bad.config()
-            assert lib.moe_workspace_size(ctypes.byref(c), ctypes.byref(n)) == moe.MOE_ERR_UNSUPPORTED
-    pack = lib.moe_pack_weights
+        for ok in (spec(packed=packed), spec(packed=packed, wdtype="fp8")):
+            c = ok.config()
+            assert c.flags & 192 == bits
+            assert lib.moe_workspace_size(ctypes.byref(c), ctypes.byref(n)) == moe.MOE_OK
+        c = spec(packed=packed, dtype="f32").config()
+        assert lib.moe_workspace_size(ctypes.byref(c), ctypes.byref(n)) == moe.MOE_ERR_UNSUPPORTED
+    def pack(src, dst, g, n, k, wd=moe.MOE_BF16):
+        return lib.moe_pack_weights(src, dst, g, n, k, wd, None)
     big = 1 << 40
-    assert pack(None, big, 2, 64, 64, None) == moe.MOE_ERR_INVALID_ARG
-    assert pack(256, big, 2, 64, 96, None) == moe.MOE_ERR_INVALID_ARG       # K not a multiple of 64
-    assert pack(256, big, 2, 72, 64, None) == moe.MOE_ERR_INVALID_ARG       # N not a multiple of 64
-    assert pack(256, big, 0, 64, 64, None) == moe.MOE_ERR_INVALID_ARG       # no groups
-    assert pack(256, big, 2, 0, 64, None) == moe.MOE_ERR_INVALID_ARG        # no rows
-    assert pack(256 + 8, big, 2, 64, 64, None) == moe.MOE_ERR_INVALID_ARG   # misaligned
-    assert pack(4096, 4096 + 1024, 2, 64, 64, None) == moe.MOE_ERR_INVALID_ARG  # overlapping
+    assert pack(None, big, 2, 64, 64) == moe.MOE_ERR_INVALID_ARG
+    assert pack(256, big, 2, 64, 96) == moe.MOE_ERR_INVALID_ARG       # K not a multiple of 64
+    assert pack(256, big, 2, 72, 64) == moe.MOE_ERR_INVALID_ARG       # N not a multiple of 64
+    assert pack(256, big, 0, 64, 64) == moe.MOE_ERR_INVALID_ARG       # no groups
+    assert pack(256, big, 2, 0, 64) == moe.MOE_ERR_INVALID_ARG        # no rows
+    assert pack(256 + 8, big, 2, 64, 64) == moe.MOE_ERR_INVALID_ARG   # misaligned
+    assert pack(256, big, 2, 64, 64, moe.MOE_F32) == moe.MOE_ERR_INVALID_ARG   # fp32 weights are not packed
+    assert pack(4096, 4096 + 1024, 2, 64, 64) == moe.MOE_ERR_INVALID_ARG  # overlapping (2 x 64 x 64 x 2 bytes)
+    assert pack(4096, 4096 + 4096, 2, 64, 64, moe.MOE_FP8_E4M3) == moe.MOE_ERR_INVALID_ARG  # 8 KB of E4M3: overlapping
     assert b"overlap" in lib.moe_last_error()

@@ -120,7 +120,7 @@ def test_packed_full_size(name):
     print(assert_y_close(host_f64(y1)[toks], ref, rows=live[toks], label=f"{name} packed", strict=True))
 
 
-def test_packed_needs_bf16_weights():
+def test_packed_needs_bf16_or_e4m3_weights():
     wl = workload("tiny_top2_fp32")
     spec = spec_of(wl, packed="both")
     with pytest.raises(moe.MoeError):
@@ -183,3 +183,50 @@ def test_packed_routing_variants_bit_identical(variant):
     for packed in ("up", "down", "both"):
         y1 = forward_variant(case, packed, **VARIANTS[variant])
         assert torch.equal(y0.view(torch.int32), y1.view(torch.int32)), f"{variant} with {packed} packed differs"
+
+
+# ---------------------------------------------------------------- E4M3 weights
+
+def test_pack_e4m3_equals_reshape():
+    G, N, K = 3, 128, 192
+    g = torch.Generator().manual_seed(7)
+    src = torch.randint(0, 256, (G, N, K), dtype=torch.uint8, generator=g).cuda()
+    dst = packed_of(src)
+    torch.cuda.synchronize()
+    ref = src.cpu().reshape(G, N // 64, 64, K // 64, 64).permute(0, 1, 3, 2, 4).contiguous()
+    assert torch.equal(dst.cpu().reshape(G, N // 64, K // 64, 64, 64), ref)
+
+
+FP8_CASES = {
+    "mixtral_small": workload("mixtral_prefill", T=300, d=512, F=1024, wdtype="fp8"),
+    "deepseek_shared": workload("deepseek_v3_fine", T=200, d=512, F=256, E=64, Fs=256, wdtype="fp8"),
+    "deepseek_mid": workload("deepseek_v3_fine", T=2000, d=256, F=256, E=64, Fs=256, wdtype="fp8"),
+    "decode_small": workload("mixtral_decode", T=8, d=256, F=512, wdtype="fp8"),
+    "switch_capacity_160": workload("switch_top1_capacity", T=2048, d=256, F=512, E=16, wdtype="fp8"),
+}
+
+
+@pytest.mark.parametrize("name", list(FP8_CASES))
+def test_packed_e4m3_bit_identical(name, monkeypatch):
+    """E4M3 weights packed: every GEMM's and both, in the plans' stages of 64 k
+    and, forced, in stages of 32 k: the row-major layer's output bit for bit."""
+    case = Case(FP8_CASES[name])
+    print(name, flush=True)
+    y0, _ = forward(case, "none")
+    for packed in ("up", "down", "both"):
+        y1, _ = forward(case, packed)
+        assert torch.equal(y0.view(torch.int32), y1.view(torch.int32)), f"E4M3 with {packed} packed differs"
+    monkeypatch.setenv("MOE_TUNING", "1")
+    for k, v in {"MOE_GEMM_K64": "0", "MOE_GEMM_BM": "128", "MOE_GEMM_BM_DOWN": "128", "MOE_GEMM_BNB_UP": "128",
+                 "MOE_GEMM_NS_UP": "3", "MOE_GEMM_BNB_DOWN": "128", "MOE_GEMM_NS_DOWN": "3"}.items():
+        monkeypatch.setenv(k, v)   # E4M3 in stages of 32 k, 128 x 128 tiles
+    y2, _ = forward(case, "both")
+    assert torch.equal(y0.view(torch.int32), y2.view(torch.int32)), "E4M3 packed in stages of 32 k differs"
+
+
+def test_packed_e4m3_full_size():
+    case = Case(workload("deepseek_v3_fine", wdtype="fp8"))
+    print("deepseek_v3_fine fp8 full size", flush=True)
+    y0, _ = forward(case, "none")
+    y1, _ = forward(case, "both")
+    assert torch.equal(y0.view(torch.int32), y1.view(torch.int32)), "E4M3 packed output differs"
