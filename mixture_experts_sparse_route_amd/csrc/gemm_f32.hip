@@ -137,11 +137,13 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_
     // every weight tile is read by one m-tile: bf16 W1 / W3 stream faster
     // with the non-temporal load policy (same box: Mixtral-shaped decode
     // gate_up 290-293 -> 270-273 us; the DeepSeek-style layer at 512 tokens
-    // 2171-2176 -> 1934-1949 us on packed weights); E4M3 weights (225 ->
-    // 236 us), the streaming GEMM2 (no change) and the plans whose weight
-    // tiles several m-tiles share (DeepSeek-style, prefill, Switch: 5-40%
-    // slower) keep the default policy
-    p.nt_up = !w8;
+    // 2171-2176 -> 1934-1949 us on packed weights), and so do packed E4M3
+    // ones (decode 0.396-0.399 -> 0.381-0.385 ms), whose stages then read
+    // whole lines; row-major E4M3 weights (225 -> 236 us), the streaming
+    // GEMM2 (no change) and the plans whose weight tiles several m-tiles
+    // share (DeepSeek-style, prefill, Switch: 5-40% slower) keep the
+    // default policy
+    p.nt_up = !w8 || packed_up;
   } else if (w8k64) {
     p = FfnPlan{64, 256, 3, 256, 3, 0, 128, 256, true, 64, true, true};
   } else if (w8) {
@@ -149,6 +151,10 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_
     // GEMMs (same box: FP8 prefill 3.27 -> 2.84 ms, DeepSeek 5.54 -> 5.46 ms
     // against stages of 32 k)
     p = FfnPlan{192, 128, 2, 128, 2, 0, 64, 128, true, 192, true, true};
+    // packed W1 / W3: the tiles that hold a whole expert load them
+    // non-temporally (same box, DeepSeek-style FP8 layer 4.99-5.02 ->
+    // 4.94-4.95 ms)
+    if (packed_up) p.nt_rows_up = p.bm;
   } else {
     const int ns_narrow = w8 ? 6 : 4;
     const int64_t mtiles = max_rows / 128 > n_groups ? max_rows / 128 : n_groups;  // rough m-tile count
@@ -238,8 +244,8 @@ FfnPlan ffn_plan(bool bf16, bool w8, int64_t max_rows, int64_t group_max, int64_
   };
   shallow(d, p.k64_up, p.ns_up, p.bnb_up);
   shallow(F, p.k64_down, p.ns_down, p.bnb_down);
-  if (!p.k64_up) p.nt_rows_up = 0;  // stages of 32 k read a line in two halves
-  if (!p.k64_down) p.nt_rows_down = 0;
+  if (!p.k64_up) p.nt_rows_up = 0, p.nt_up = false;  // stages of 32 k read a line in two halves
+  if (!p.k64_down) p.nt_rows_down = 0, p.nt_down = false;
   // bf16 weights and at most 32 rows in any group (decode-sized batches):
   // GEMM2 is the weight-streaming kernel, which reads 512 bytes of each
   // weight row per load batch instead of 128 per LDS stage (same box, Mixtral
